@@ -1,0 +1,230 @@
+"""fp64 CPU oracle for causal kernelized linear attention (fast-weight form).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+CPU-baseline leg of the benchmark.  The product path never imports it.
+
+The arithmetic lives in ``la_oracle.c`` (plain C, double precision, one token
+at a time).  This module compiles it with gcc, loads it with ctypes and splits
+independent (batch, head) rows over a thread pool (ctypes releases the GIL
+during the foreign call, so the C loops run in parallel).
+
+All public functions take numpy arrays in the [B, H, N, d] layout (any float
+dtype; values are widened exactly to float64) and return float64 arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "la_oracle.c")
+_LIB = os.path.join(_HERE, "liborc.so")
+PHI_KINDS = {"elu1": 0, "trig_rf": 1}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile la_oracle.c into liborc.so (plain gcc, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.POINTER(ctypes.c_double)
+    L, I, D = ctypes.c_long, ctypes.c_int, ctypes.c_double
+    lib.orc_phi.argtypes = [I, P, I, I, P, D, P]
+    lib.orc_phi.restype = None
+    lib.orc_causal.argtypes = [P, P, P, L, L, I, I, I, I, P, D, P, D, P, P, P, P, P, P]
+    lib.orc_causal.restype = None
+    lib.orc_noncausal.argtypes = [P, P, P, L, L, I, I, I, I, P, D, D, P]
+    lib.orc_noncausal.restype = None
+    lib.orc_decode_step.argtypes = [P, P, P, L, I, I, I, I, P, D, P, D, P, P, P]
+    lib.orc_decode_step.restype = None
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a, offset_elems=0):
+    if a is None:
+        return None
+    base = a.ctypes.data + 8 * int(offset_elems)
+    return ctypes.cast(base, ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def feature_dim(phi: str, dk: int, omega) -> int:
+    return dk if phi == "elu1" else 2 * int(np.asarray(omega).shape[0])
+
+
+def phi_map(x, phi: str = "elu1", omega=None, scale: float = 1.0):
+    """Feature map applied to the last axis of x; returns float64 [..., F]."""
+    lib = _load()
+    x = _f64(x)
+    dk = x.shape[-1]
+    om = _f64(omega)
+    m = 0 if om is None else om.shape[0]
+    F = feature_dim(phi, dk, om)
+    flat = x.reshape(-1, dk)
+    out = np.empty((flat.shape[0], F), dtype=np.float64)
+    for r in range(flat.shape[0]):
+        lib.orc_phi(PHI_KINDS[phi], _ptr(flat, r * dk), dk, m, _ptr(om), float(scale),
+                    _ptr(out, r * F))
+    return out.reshape(x.shape[:-1] + (F,))
+
+
+def _lam_rows(lam, B, H):
+    if lam is None:
+        lam = np.ones(H)
+    lam = np.asarray(lam, dtype=np.float64).reshape(-1)
+    if lam.size == 1:
+        lam = np.full(H, lam[0])
+    assert lam.size == H, "lambda must have one value per head"
+    return np.ascontiguousarray(np.tile(lam, B))
+
+
+def _split(nbh, threads):
+    threads = max(1, min(threads, nbh))
+    edges = np.linspace(0, nbh, threads + 1).astype(int)
+    return [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+def causal(q, k, v, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
+           S0=None, z0=None, want_state=False, want_kappa=False, threads=None):
+    """Causal forward, per (b,h) one token at a time (update, then query).
+
+    q, k: [B,H,N,dk]; v: [B,H,N,dv]; lam: [H] (None = 1); S0: [B,H,F,dv],
+    z0: [B,H,F] or None (zero state).  Returns y [B,H,N,dv] and, if asked,
+    the final (S, z) and the cancellation factor kappa [B,H,N].
+    """
+    lib = _load()
+    q, k, v, om = _f64(q), _f64(k), _f64(v), _f64(omega)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    m = 0 if om is None else om.shape[0]
+    F = feature_dim(phi, dk, om)
+    nbh = B * H
+    lam_r = _lam_rows(lam, B, H)
+    S0, z0 = _f64(S0), _f64(z0)
+    y = np.empty((B, H, N, dv), dtype=np.float64)
+    S = np.empty((B, H, F, dv), dtype=np.float64) if want_state else None
+    z = np.empty((B, H, F), dtype=np.float64) if want_state else None
+    kap = np.empty((B, H, N), dtype=np.float64) if want_kappa else None
+
+    def run(rng):
+        a, b = rng
+        lib.orc_causal(_ptr(q, a * N * dk), _ptr(k, a * N * dk), _ptr(v, a * N * dv),
+                       b - a, N, dk, dv, PHI_KINDS[phi], m, _ptr(om), float(scale),
+                       _ptr(lam_r, a), float(eps),
+                       _ptr(S0, a * F * dv), _ptr(z0, a * F),
+                       _ptr(y, a * N * dv), _ptr(S, a * F * dv), _ptr(z, a * F),
+                       _ptr(kap, a * N))
+
+    parts = _split(nbh, threads or default_threads())
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    out = [y]
+    if want_state:
+        out += [S, z]
+    if want_kappa:
+        out.append(kap)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def noncausal(q, k, v, eps=1e-6, phi="elu1", omega=None, scale=1.0, threads=None):
+    """Non-causal forward: one state summed over the whole sequence, no decay."""
+    lib = _load()
+    q, k, v, om = _f64(q), _f64(k), _f64(v), _f64(omega)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    m = 0 if om is None else om.shape[0]
+    y = np.empty((B, H, N, dv), dtype=np.float64)
+
+    def run(rng):
+        a, b = rng
+        lib.orc_noncausal(_ptr(q, a * N * dk), _ptr(k, a * N * dk), _ptr(v, a * N * dv),
+                          b - a, N, dk, dv, PHI_KINDS[phi], m, _ptr(om), float(scale),
+                          float(eps), _ptr(y, a * N * dv))
+
+    parts = _split(B * H, threads or default_threads())
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return y
+
+
+def decode_step(q, k, v, S, z, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
+                threads=None):
+    """One decode step.  q,k: [B,H,1,dk] (or [B,H,dk]); v: [B,H,1,dv];
+    S [B,H,F,dv], z [B,H,F].  Returns (y [B,H,1,dv], S_new, z_new); the inputs
+    are not modified."""
+    lib = _load()
+    q, k, v, om = _f64(q), _f64(k), _f64(v), _f64(omega)
+    B, H = q.shape[0], q.shape[1]
+    dk, dv = q.shape[-1], v.shape[-1]
+    m = 0 if om is None else om.shape[0]
+    F = feature_dim(phi, dk, om)
+    S = np.array(S, dtype=np.float64, copy=True, order="C")
+    z = np.array(z, dtype=np.float64, copy=True, order="C")
+    y = np.empty((B, H, 1, dv), dtype=np.float64)
+    lam_r = _lam_rows(lam, B, H)
+
+    def run(rng):
+        a, b = rng
+        lib.orc_decode_step(_ptr(q, a * dk), _ptr(k, a * dk), _ptr(v, a * dv), b - a, dk,
+                            dv, PHI_KINDS[phi], m, _ptr(om), float(scale), _ptr(lam_r, a),
+                            float(eps), _ptr(S, a * F * dv), _ptr(z, a * F),
+                            _ptr(y, a * dv))
+
+    parts = _split(B * H, threads or default_threads())
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return y, S, z
+
+
+def rowwise_rel_err(y, y_ref):
+    """max over rows r=(b,h,i) of max_c |y - y_ref| / max_c |y_ref|.
+
+    Elementwise relative error is unusable here (outputs cross zero), so each
+    row is normalised by its own largest reference magnitude.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    num = np.max(np.abs(y - y_ref), axis=-1)
+    den = np.max(np.abs(y_ref), axis=-1)
+    den = np.where(den == 0, 1.0, den)
+    r = num / den
+    return float(np.max(r)) if r.size else 0.0

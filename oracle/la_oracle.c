@@ -1,0 +1,198 @@
+/*
+ * la_oracle.c -- slow, plain fp64 CPU reference for causal kernelized linear
+ * attention in fast-weight form.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this file; only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no header, helper or constant with
+ * the GPU path.
+ *
+ * Every function is the plain definition written out, one token at a time,
+ * in double precision.  Inputs are widened exactly from the stored fp32 /
+ * bf16 values by the caller.
+ *
+ * Sources (pages, by title and section):
+ *  - "Attention is also an FFN" (kwkr.cn/news/587576):
+ *      sec. 2.1  kernel factorisation, state S_i = sum_{j<=i} phi(k_j) v_j^T and
+ *                its outer-product recurrence; query y_i = phi(q_i)^T S_i
+ *      sec. 3.2  decayed recurrence S_t = lambda S_{t-1} + phi(k_t) v_t^T
+ *      sec. 4.1  elu+1 feature map; single-token step updates the state first
+ *                and then queries it; the state starts at zero
+ *      sec. 4.2  normaliser z_i = z_{i-1} + phi(k_i), output divided by
+ *                phi(q_i)^T z_i plus a small eps; the decay may also be put on z
+ *  - "From standard attention to linear attention" (tqpw.cn/news/561043):
+ *      sec. 3    non-causal closed form with S = sum phi(k) v^T, Z = sum phi(k)
+ *      sec. 4.1  elu(x)+1 with alpha = 1
+ *      sec. 4.2  random cos/sin features of omega . x scaled by 1/sqrt(m)
+ *      sec. 6    autoregressive step: S += k v^T, Z += k, then query
+ *
+ * Readings where the pages leave a step open (each also listed in the design
+ * notes): update-then-query (inclusive state); the decay multiplies z as well
+ * as S; the denominator is (phi(q)^T z + eps); the random-feature map is
+ * phi(x) = exp(-|x'|^2/2)/sqrt(m) [cos(omega x'), sin(omega x')] with
+ * x' = s x, cosine block first.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_PHI_ELU1 = 0, ORC_PHI_TRIG_RF = 1 };
+
+/* Feature map of one vector x[dk] -> out[F].
+ * ELU1: F = dk, phi(x)_f = x_f + 1 if x_f > 0 else exp(x_f)   (elu, alpha=1, plus 1)
+ * TRIG_RF: F = 2m, x' = scale * x, u_r = omega_r . x',
+ *          phi = exp(-|x'|^2 / 2) / sqrt(m) * [cos u_1..cos u_m, sin u_1..sin u_m] */
+void orc_phi(int kind, const double* x, int dk, int m, const double* omega,
+             double scale, double* out)
+{
+    if (kind == ORC_PHI_ELU1) {
+        for (int f = 0; f < dk; ++f)
+            out[f] = x[f] > 0.0 ? x[f] + 1.0 : exp(x[f]);
+        return;
+    }
+    double* xs = (double*)malloc(sizeof(double) * (size_t)dk);
+    double nrm2 = 0.0;
+    for (int f = 0; f < dk; ++f) {
+        xs[f] = scale * x[f];
+        nrm2 += xs[f] * xs[f];
+    }
+    double c = exp(-0.5 * nrm2) / sqrt((double)m);
+    for (int r = 0; r < m; ++r) {
+        double u = 0.0;
+        for (int f = 0; f < dk; ++f) u += omega[(size_t)r * dk + f] * xs[f];
+        out[r] = c * cos(u);
+        out[m + r] = c * sin(u);
+    }
+    free(xs);
+}
+
+static int feat_dim(int kind, int dk, int m) { return kind == ORC_PHI_ELU1 ? dk : 2 * m; }
+
+/* Causal forward over nbh independent (batch, head) rows.
+ *   q,k [nbh][N][dk], v [nbh][N][dv], lam [nbh], S0 [nbh][F][dv] / z0 [nbh][F]
+ *   (NULL = zero state), y [nbh][N][dv], S_out / z_out (NULL = not written),
+ *   kappa [nbh][N] (NULL = not computed): the cancellation factor
+ *   |phi q|^T zbar / |phi(q)^T z + eps| with zbar the same recurrence on |phi(k)|.
+ * Per token: S <- lam S + phi(k) v^T ; z <- lam z + phi(k) ;
+ *            y = phi(q)^T S / (phi(q)^T z + eps). */
+void orc_causal(const double* q, const double* k, const double* v,
+                long nbh, long N, int dk, int dv, int kind, int m,
+                const double* omega, double scale, const double* lam, double eps,
+                const double* S0, const double* z0,
+                double* y, double* S_out, double* z_out, double* kappa)
+{
+    const int F = feat_dim(kind, dk, m);
+    double* S = (double*)malloc(sizeof(double) * (size_t)F * dv);
+    double* z = (double*)malloc(sizeof(double) * (size_t)F);
+    double* zb = (double*)malloc(sizeof(double) * (size_t)F);
+    double* pk = (double*)malloc(sizeof(double) * (size_t)F);
+    double* pq = (double*)malloc(sizeof(double) * (size_t)F);
+    for (long bh = 0; bh < nbh; ++bh) {
+        const double L = lam[bh];
+        if (S0) memcpy(S, S0 + (size_t)bh * F * dv, sizeof(double) * (size_t)F * dv);
+        else memset(S, 0, sizeof(double) * (size_t)F * dv);
+        if (z0) memcpy(z, z0 + (size_t)bh * F, sizeof(double) * (size_t)F);
+        else memset(z, 0, sizeof(double) * (size_t)F);
+        for (int f = 0; f < F; ++f) zb[f] = fabs(z[f]);
+        for (long i = 0; i < N; ++i) {
+            const double* ki = k + ((size_t)bh * N + i) * dk;
+            const double* qi = q + ((size_t)bh * N + i) * dk;
+            const double* vi = v + ((size_t)bh * N + i) * dv;
+            orc_phi(kind, ki, dk, m, omega, scale, pk);
+            orc_phi(kind, qi, dk, m, omega, scale, pq);
+            for (int f = 0; f < F; ++f) {
+                double* Sf = S + (size_t)f * dv;
+                for (int d = 0; d < dv; ++d) Sf[d] = L * Sf[d] + pk[f] * vi[d];
+                z[f] = L * z[f] + pk[f];
+                zb[f] = L * zb[f] + fabs(pk[f]);
+            }
+            double den = 0.0, denb = 0.0;
+            for (int f = 0; f < F; ++f) {
+                den += pq[f] * z[f];
+                denb += fabs(pq[f]) * zb[f];
+            }
+            double* yi = y + ((size_t)bh * N + i) * dv;
+            for (int d = 0; d < dv; ++d) {
+                double num = 0.0;
+                for (int f = 0; f < F; ++f) num += pq[f] * S[(size_t)f * dv + d];
+                yi[d] = num / (den + eps);
+            }
+            if (kappa) kappa[(size_t)bh * N + i] = denb / fabs(den + eps);
+        }
+        if (S_out) memcpy(S_out + (size_t)bh * F * dv, S, sizeof(double) * (size_t)F * dv);
+        if (z_out) memcpy(z_out + (size_t)bh * F, z, sizeof(double) * (size_t)F);
+    }
+    free(S); free(z); free(zb); free(pk); free(pq);
+}
+
+/* Non-causal forward: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j) over the
+ * whole sequence (no decay), then y_i = phi(q_i)^T S / (phi(q_i)^T z + eps). */
+void orc_noncausal(const double* q, const double* k, const double* v,
+                   long nbh, long N, int dk, int dv, int kind, int m,
+                   const double* omega, double scale, double eps, double* y)
+{
+    const int F = feat_dim(kind, dk, m);
+    double* S = (double*)malloc(sizeof(double) * (size_t)F * dv);
+    double* z = (double*)malloc(sizeof(double) * (size_t)F);
+    double* p = (double*)malloc(sizeof(double) * (size_t)F);
+    for (long bh = 0; bh < nbh; ++bh) {
+        memset(S, 0, sizeof(double) * (size_t)F * dv);
+        memset(z, 0, sizeof(double) * (size_t)F);
+        for (long j = 0; j < N; ++j) {
+            const double* kj = k + ((size_t)bh * N + j) * dk;
+            const double* vj = v + ((size_t)bh * N + j) * dv;
+            orc_phi(kind, kj, dk, m, omega, scale, p);
+            for (int f = 0; f < F; ++f) {
+                for (int d = 0; d < dv; ++d) S[(size_t)f * dv + d] += p[f] * vj[d];
+                z[f] += p[f];
+            }
+        }
+        for (long i = 0; i < N; ++i) {
+            const double* qi = q + ((size_t)bh * N + i) * dk;
+            orc_phi(kind, qi, dk, m, omega, scale, p);
+            double den = 0.0;
+            for (int f = 0; f < F; ++f) den += p[f] * z[f];
+            double* yi = y + ((size_t)bh * N + i) * dv;
+            for (int d = 0; d < dv; ++d) {
+                double num = 0.0;
+                for (int f = 0; f < F; ++f) num += p[f] * S[(size_t)f * dv + d];
+                yi[d] = num / (den + eps);
+            }
+        }
+    }
+    free(S); free(z); free(p);
+}
+
+/* One recurrent decode step on nbh head-states, in place:
+ *   q,k [nbh][dk], v [nbh][dv], S [nbh][F][dv], z [nbh][F], y [nbh][dv].
+ * S <- lam S + phi(k) v^T ; z <- lam z + phi(k) ; y = phi(q)^T S / (phi(q)^T z + eps). */
+void orc_decode_step(const double* q, const double* k, const double* v,
+                     long nbh, int dk, int dv, int kind, int m,
+                     const double* omega, double scale, const double* lam, double eps,
+                     double* S, double* z, double* y)
+{
+    const int F = feat_dim(kind, dk, m);
+    double* pk = (double*)malloc(sizeof(double) * (size_t)F);
+    double* pq = (double*)malloc(sizeof(double) * (size_t)F);
+    for (long bh = 0; bh < nbh; ++bh) {
+        const double L = lam[bh];
+        double* Sb = S + (size_t)bh * F * dv;
+        double* zb = z + (size_t)bh * F;
+        orc_phi(kind, k + (size_t)bh * dk, dk, m, omega, scale, pk);
+        orc_phi(kind, q + (size_t)bh * dk, dk, m, omega, scale, pq);
+        const double* vb = v + (size_t)bh * dv;
+        for (int f = 0; f < F; ++f) {
+            for (int d = 0; d < dv; ++d)
+                Sb[(size_t)f * dv + d] = L * Sb[(size_t)f * dv + d] + pk[f] * vb[d];
+            zb[f] = L * zb[f] + pk[f];
+        }
+        double den = 0.0;
+        for (int f = 0; f < F; ++f) den += pq[f] * zb[f];
+        for (int d = 0; d < dv; ++d) {
+            double num = 0.0;
+            for (int f = 0; f < F; ++f) num += pq[f] * Sb[(size_t)f * dv + d];
+            y[(size_t)bh * dv + d] = num / (den + eps);
+        }
+    }
+    free(pk); free(pq);
+}

@@ -1,0 +1,237 @@
+"""Seeded synthetic inputs for the linear-attention workloads.
+
+This module is shared by the CPU oracle tests and the GPU path.  It holds no
+arithmetic of the method itself: only random draws, round-to-nearest-even
+conversion to bfloat16, and shape bookkeeping.  Every array it returns is a
+plain numpy array; the same bytes are handed to both sides.
+
+Workloads (synthetic stand-ins; the pages measure on no public benchmark):
+
+  1  causal, elu+1, lambda=1, eps=1e-6: B=1 H=1 N=256 d=64, fp32 N(0,1)
+  2  causal, elu+1, lambda=1: B=4 H=8 N=4096 d=64, bf16 0.5*N(0,1)
+  3  causal, elu+1, per-head lambda ~ U[0.9,0.999]: B=2 H=16 N=32768 d=128, bf16
+  4  decode: 256 sequences x 32 heads, d=128, 512-token prefix then 1024
+     single-token steps, lambda=0.999, bf16 0.5*N(0,1)
+  5  causal, trigonometric random features m=128 (F=256): B=1 H=16 N=65536
+     d=64, q/k scaled by d^-1/4 inside the feature map, bf16 0.5*N(0,1)
+
+Each workload index is also its seed.  Independent sub-streams (q, k, v,
+lambda, omega, prefix, steps) are spawned from numpy's SeedSequence so that
+changing one tensor's size never changes another tensor's values.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "workload", "bf16_bits_rne", "bf16_bits_to_f32",
+    "round_to_bf16", "make_qkv", "make_lambda", "make_omega", "make_inputs",
+    "make_decode_step", "make_decode_prefix",
+]
+
+STREAMS = ("q", "k", "v", "lam", "omega", "prefix", "steps")
+
+
+# --------------------------------------------------------------------------
+# bfloat16 rounding (explicit bit operations, independent of any torch version)
+# --------------------------------------------------------------------------
+def bf16_bits_rne(x) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    NaN inputs map to a quiet NaN; infinities are preserved; values that
+    round past the largest finite bf16 become infinity (IEEE behaviour).
+    """
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    nan = np.isnan(a)
+    if nan.any():
+        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> the exactly equal fp32 values."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_bf16(x):
+    """Return (bits uint16, values float32) of x rounded to bf16 (RNE)."""
+    bits = bf16_bits_rne(x)
+    return bits, bf16_bits_to_f32(bits)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    kind: str            # "causal" | "decode"
+    B: int
+    H: int
+    N: int               # sequence length (decode: prefix length)
+    dk: int
+    dv: int
+    dtype: str           # "f32" | "bf16"
+    scale: float         # standard deviation of q, k, v
+    phi: str             # "elu1" | "trig_rf"
+    m: int = 0           # random features (F = 2m) for trig_rf
+    lam: str = "one"     # "one" | "per_head" | "const"
+    lam_value: float = 1.0
+    lam_lo: float = 0.9
+    lam_hi: float = 0.999
+    eps: float = 1e-6
+    steps: int = 0       # decode steps after the prefix
+
+    @property
+    def F(self) -> int:
+        return 2 * self.m if self.phi == "trig_rf" else self.dk
+
+    @property
+    def qk_scale(self) -> float:
+        return float(self.dk) ** -0.25 if self.phi == "trig_rf" else 1.0
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    1: Workload(1, "elu1_causal_B1_H1_N256_d64_f32", "causal", 1, 1, 256, 64, 64,
+                "f32", 1.0, "elu1"),
+    2: Workload(2, "elu1_causal_B4_H8_N4096_d64_bf16", "causal", 4, 8, 4096, 64, 64,
+                "bf16", 0.5, "elu1"),
+    3: Workload(3, "elu1_decay_causal_B2_H16_N32768_d128_bf16", "causal", 2, 16, 32768,
+                128, 128, "bf16", 0.5, "elu1", lam="per_head"),
+    4: Workload(4, "elu1_decode_B256_H32_d128_prefix512_steps1024_bf16", "decode", 256,
+                32, 512, 128, 128, "bf16", 0.5, "elu1", lam="const", lam_value=0.999,
+                steps=1024),
+    5: Workload(5, "trigrf_m128_causal_B1_H16_N65536_d64_bf16", "causal", 1, 16, 65536,
+                64, 64, "bf16", 0.5, "trig_rf", m=128),
+}
+
+
+def workload(index: int) -> Workload:
+    return WORKLOADS[index]
+
+
+def _streams(seed: int) -> dict:
+    children = np.random.SeedSequence(seed).spawn(len(STREAMS))
+    return {name: child for name, child in zip(STREAMS, children)}
+
+
+def _rng(seed: int, stream: str, *extra: int) -> np.random.Generator:
+    ss = _streams(seed)[stream]
+    if extra:
+        ss = np.random.SeedSequence(entropy=ss.entropy, spawn_key=ss.spawn_key + tuple(extra))
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def _normal(rng, shape, scale, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        x = (x * np.float32(scale)).astype(np.float32)
+    if dtype == "bf16":
+        bits, vals = round_to_bf16(x)
+        return bits, vals
+    return None, x
+
+
+def make_qkv(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None):
+    """q, k, v of shape [B,H,N,d] for a workload (sizes may be overridden).
+
+    Returns a dict with float32 'q','k','v' (exact values) and, for bf16
+    workloads, the uint16 bit patterns 'q_bits','k_bits','v_bits'.
+    """
+    seed = wl.index if seed is None else seed
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    N = wl.N if N is None else N
+    out = {}
+    for name, d in (("q", wl.dk), ("k", wl.dk), ("v", wl.dv)):
+        bits, vals = _normal(_rng(seed, name), (B, H, N, d), wl.scale, wl.dtype)
+        out[name] = vals
+        if bits is not None:
+            out[name + "_bits"] = bits
+    return out
+
+
+def make_lambda(wl: Workload, seed: Optional[int] = None, H=None) -> np.ndarray:
+    """Per-head decay as float32 [H]."""
+    seed = wl.index if seed is None else seed
+    H = wl.H if H is None else H
+    if wl.lam == "one":
+        return np.ones(H, dtype=np.float32)
+    if wl.lam == "const":
+        return np.full(H, wl.lam_value, dtype=np.float32)
+    rng = _rng(seed, "lam")
+    return rng.uniform(wl.lam_lo, wl.lam_hi, size=H).astype(np.float32)
+
+
+def make_omega(m: int, dk: int, seed: int) -> np.ndarray:
+    """Random-feature directions omega [m, dk] float32.
+
+    Rows are drawn from N(0, I) and orthogonalised in independent blocks of
+    dk rows: each block is the Q factor of a dk x dk Gaussian matrix
+    (sign-fixed by the diagonal of R so the factorisation is unique), and each
+    row is then rescaled to the norm of a fresh N(0, I_dk) draw, so that rows
+    keep the marginal distribution of N(0, I) while being exactly orthogonal
+    within a block.
+    """
+    rng = _rng(seed, "omega")
+    blocks = []
+    remaining = m
+    while remaining > 0:
+        g = rng.standard_normal((dk, dk))
+        qm, rm = np.linalg.qr(g)
+        qm = qm * np.sign(np.diag(rm))[None, :]
+        rows = qm.T                                   # orthonormal rows
+        norms = np.linalg.norm(rng.standard_normal((dk, dk)), axis=1)
+        blocks.append(rows * norms[:, None])
+        remaining -= dk
+    return np.concatenate(blocks, axis=0)[:m].astype(np.float32)
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None):
+    """Everything a forward call needs: q, k, v, lambda [H], omega or None."""
+    seed = wl.index if seed is None else seed
+    d = make_qkv(wl, seed, B, H, N)
+    d["lam"] = make_lambda(wl, seed, H)
+    d["omega"] = make_omega(wl.m, wl.dk, seed) if wl.phi == "trig_rf" else None
+    return d
+
+
+def make_decode_prefix(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None):
+    """The prefix tokens that initialise the decode state: [B,H,N,d]."""
+    seed = wl.index if seed is None else seed
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    N = wl.N if N is None else N
+    out = {}
+    for j, (name, d) in enumerate((("q", wl.dk), ("k", wl.dk), ("v", wl.dv))):
+        bits, vals = _normal(_rng(seed, "prefix", j), (B, H, N, d), wl.scale, wl.dtype)
+        out[name] = vals
+        if bits is not None:
+            out[name + "_bits"] = bits
+    return out
+
+
+def make_decode_step(wl: Workload, step: int, seed: Optional[int] = None, B=None, H=None):
+    """Single-token inputs of one decode step, [B,H,1,d]; regenerated from
+    (seed, step) so that no trajectory needs to be stored."""
+    seed = wl.index if seed is None else seed
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    out = {}
+    for j, (name, d) in enumerate((("q", wl.dk), ("k", wl.dk), ("v", wl.dv))):
+        bits, vals = _normal(_rng(seed, "steps", step, j), (B, H, 1, d), wl.scale, wl.dtype)
+        out[name] = vals
+        if bits is not None:
+            out[name + "_bits"] = bits
+    return out

@@ -1,0 +1,289 @@
+"""Pins of the fp64 CPU oracle against facts the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every expected value comes from
+a different formulation (the O(N^2) masked quadratic form, the cumulative-sum
+form at lambda = 1, the non-causal closed form with library matmuls), a closed
+form, an exact identity, or a hand derivation stored under tests/golden/.
+"""
+import json
+import math
+import os
+import zlib
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from seeded_inputs import make_omega
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- feature maps
+def test_phi_elu1_closed_values(orc):
+    # elu with alpha = 1, plus one ("From standard attention to linear attention", sec. 4.1)
+    x = np.array([[0.0, 1.0, -1.0, 2.5, -3.0, 1e-12, -1e-12, -40.0]])
+    got = orc.phi_map(x, "elu1")[0]
+    want = [1.0, 2.0, math.exp(-1.0), 3.5, math.exp(-3.0), 1.0 + 1e-12,
+            math.exp(-1e-12), math.exp(-40.0)]
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=0)
+    assert np.all(got > 0)  # strictly positive features
+
+
+def test_phi_rf_identity_omega_closed_form(orc):
+    # omega = identity rows, so u = x' exactly: phi = exp(-|x'|^2/2)/sqrt(m) [cos x', sin x']
+    rng = np.random.default_rng(0)
+    dk = m = 4
+    s = 0.7
+    x = _rand(rng, 3, dk)
+    got = orc.phi_map(x, "trig_rf", omega=np.eye(m), scale=s)
+    xs = s * x
+    c = np.exp(-0.5 * np.sum(xs * xs, axis=1, keepdims=True)) / math.sqrt(m)
+    want = np.concatenate([c * np.cos(xs), c * np.sin(xs)], axis=1)
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-16)
+
+
+def test_phi_rf_norm_identity_and_zero(orc):
+    rng = np.random.default_rng(1)
+    dk, m = 16, 32
+    om = make_omega(m, dk, seed=11)
+    s = dk ** -0.25
+    x = _rand(rng, 20, dk)
+    p = orc.phi_map(x, "trig_rf", omega=om, scale=s)
+    # cos^2 + sin^2 = 1  =>  |phi(x)|^2 = exp(-|x'|^2)
+    np.testing.assert_allclose(np.sum(p * p, axis=1), np.exp(-np.sum((s * x) ** 2, axis=1)),
+                               rtol=1e-13)
+    p0 = orc.phi_map(np.zeros((1, dk)), "trig_rf", omega=om, scale=s)[0]
+    want0 = np.concatenate([np.full(m, m ** -0.5), np.zeros(m)])
+    np.testing.assert_allclose(p0, want0, rtol=1e-15, atol=0)
+
+
+def test_phi_rf_kernel_monte_carlo(orc):
+    # E[phi(x).phi(y)] = exp(-|x'|^2/2 - |y'|^2/2 - |x'-y'|^2/2) for omega ~ N(0, I)
+    rng = np.random.default_rng(2)
+    dk, m = 8, 8192
+    om = make_omega(m, dk, seed=12)
+    s = 0.8
+    x = _rand(rng, 6, dk, scale=0.6)
+    y = _rand(rng, 6, dk, scale=0.6)
+    px = orc.phi_map(x, "trig_rf", omega=om, scale=s)
+    py = orc.phi_map(y, "trig_rf", omega=om, scale=s)
+    got = np.sum(px * py, axis=1)
+    xs, ys = s * x, s * y
+    want = np.exp(-0.5 * np.sum(xs ** 2, 1) - 0.5 * np.sum(ys ** 2, 1)
+                  - 0.5 * np.sum((xs - ys) ** 2, 1))
+    bound = 4.0 * math.sqrt(0.5 / m) * np.exp(-0.5 * (np.sum(xs ** 2, 1) + np.sum(ys ** 2, 1)))
+    assert np.all(np.abs(got - want) < bound), (got, want, bound)
+
+
+# ---------------------------------------------------------------- recurrence
+def _brute_force(pq, pk, v, lam, eps):
+    """O(N^2) masked quadratic form, one (b,h) row:
+    y_i = sum_{j<=i} lam^(i-j) (pq_i . pk_j) v_j / (sum_{j<=i} lam^(i-j) pq_i . pk_j + eps)."""
+    N = pq.shape[0]
+    y = np.zeros((N, v.shape[1]))
+    for i in range(N):
+        num = np.zeros(v.shape[1])
+        den = 0.0
+        for j in range(i + 1):
+            w = 1.0 if i == j else lam ** (i - j)
+            a = w * float(pq[i] @ pk[j])
+            num += a * v[j]
+            den += a
+        y[i] = num / (den + eps)
+    return y
+
+
+CASES = [
+    # phi, dk, m, lam, eps
+    ("elu1", 2, 0, 1.0, 1e-6),
+    ("elu1", 4, 0, 0.0, 1e-6),
+    ("elu1", 4, 0, 0.3, 1e-6),
+    ("elu1", 8, 0, 0.9, 1e-6),
+    ("elu1", 8, 0, 0.999, 0.0),
+    ("trig_rf", 4, 6, 1.0, 1e-6),
+    ("trig_rf", 8, 4, 0.95, 1e-6),
+]
+
+
+@pytest.mark.parametrize("phi,dk,m,lam,eps", CASES)
+def test_causal_matches_bruteforce(orc, phi, dk, m, lam, eps):
+    rng = np.random.default_rng(zlib.crc32(repr((phi, dk, m, lam)).encode()))
+    B, H, N, dv = 2, 2, 37, 3
+    q, k = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk)
+    v = _rand(rng, B, H, N, dv)
+    om = make_omega(m, dk, seed=5) if phi == "trig_rf" else None
+    s = dk ** -0.25 if phi == "trig_rf" else 1.0
+    lam_h = np.array([lam, lam])
+    y = orc.causal(q, k, v, lam_h, eps, phi, om, s)
+    pq = orc.phi_map(q, phi, om, s)
+    pk = orc.phi_map(k, phi, om, s)
+    for b in range(B):
+        for h in range(H):
+            want = _brute_force(pq[b, h], pk[b, h], v[b, h], lam, eps)
+            np.testing.assert_allclose(y[b, h], want, rtol=1e-10, atol=1e-12)
+
+
+def test_per_head_lambda_bruteforce(orc):
+    rng = np.random.default_rng(7)
+    B, H, N, dk, dv = 1, 3, 25, 4, 2
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    lam_h = np.array([0.5, 0.9, 1.0])
+    y = orc.causal(q, k, v, lam_h, 1e-6)
+    pq, pk = orc.phi_map(q), orc.phi_map(k)
+    for h in range(H):
+        np.testing.assert_allclose(y[0, h], _brute_force(pq[0, h], pk[0, h], v[0, h],
+                                                          lam_h[h], 1e-6), rtol=1e-10)
+
+
+def test_lambda_one_cumsum_identity(orc):
+    # lambda = 1: S_i = cumsum_j phi(k_j) v_j^T, z_i = cumsum_j phi(k_j)
+    rng = np.random.default_rng(3)
+    B, H, N, dk, dv = 1, 2, 50, 6, 5
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    y, S, z = orc.causal(q, k, v, None, 1e-6, want_state=True)
+    pq, pk = orc.phi_map(q), orc.phi_map(k)
+    outer = pk[..., :, None] * v[..., None, :]            # [B,H,N,F,dv]
+    Sc = np.cumsum(outer, axis=2)
+    zc = np.cumsum(pk, axis=2)
+    num = np.einsum("bhnf,bhnfd->bhnd", pq, Sc)
+    den = np.einsum("bhnf,bhnf->bhn", pq, zc)
+    np.testing.assert_allclose(y, num / (den[..., None] + 1e-6), rtol=1e-11)
+    np.testing.assert_allclose(S, Sc[:, :, -1], rtol=1e-12)
+    np.testing.assert_allclose(z, zc[:, :, -1], rtol=1e-12)
+
+
+def test_noncausal_closed_form(orc):
+    # phi(Q) (phi(K)^T V) / (phi(Q) . sum_j phi(k_j) + eps), two library matmuls
+    rng = np.random.default_rng(4)
+    B, H, N, dk, dv = 2, 2, 33, 8, 4
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    for phi, om, s in (("elu1", None, 1.0), ("trig_rf", make_omega(16, dk, 9), dk ** -0.25)):
+        y = orc.noncausal(q, k, v, 1e-6, phi, om, s)
+        pq, pk = orc.phi_map(q, phi, om, s), orc.phi_map(k, phi, om, s)
+        KV = np.swapaxes(pk, -1, -2) @ v
+        num = pq @ KV
+        den = pq @ pk.sum(axis=2)[..., None]
+        np.testing.assert_allclose(y, num / (den + 1e-6), rtol=1e-11, atol=1e-14)
+
+
+def test_golden_handcheck(orc):
+    with open(os.path.join(GOLDEN, "handcheck_elu1_N2_d4.json")) as fh:
+        g = json.load(fh)
+    q = np.array(g["q"], dtype=float)[None, None]
+    k = np.array(g["k"], dtype=float)[None, None]
+    v = np.array(g["v"], dtype=float)[None, None]
+    num = np.array([[float(Fraction(x)) for x in row] for row in g["num"]])
+    den = np.array([float(Fraction(x)) for x in g["den"]])
+    for eps in (0.0, 1e-6):
+        y, S, z = orc.causal(q, k, v, [g["lambda"]], eps, want_state=True)
+        np.testing.assert_allclose(y[0, 0], num / (den[:, None] + eps), rtol=1e-15)
+    Sf = np.array([[float(Fraction(x)) for x in row] for row in g["S_final"]])
+    zf = np.array([float(Fraction(x)) for x in g["z_final"]])
+    np.testing.assert_array_equal(S[0, 0], Sf)
+    np.testing.assert_array_equal(z[0, 0], zf)
+
+
+# ---------------------------------------------------------------- invariants
+def test_invariants_single_token_and_constant_v(orc):
+    rng = np.random.default_rng(5)
+    B, H, dk, dv = 1, 2, 4, 3
+    eps = 1e-6
+    # N = 1: y_0 = v_0 a / (a + eps), a = phi(q_0).phi(k_0)
+    q, k, v = _rand(rng, B, H, 1, dk), _rand(rng, B, H, 1, dk), _rand(rng, B, H, 1, dv)
+    y = orc.causal(q, k, v, [0.7, 0.2], eps)
+    a = np.sum(orc.phi_map(q) * orc.phi_map(k), axis=-1)
+    np.testing.assert_allclose(y, v * (a / (a + eps))[..., None], rtol=1e-14)
+    # constant v_j = c: y_i = c den_i / (den_i + eps)
+    N = 20
+    q, k = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk)
+    c = np.array([1.5, -2.0, 0.25])
+    v = np.broadcast_to(c, (B, H, N, dv)).copy()
+    y = orc.causal(q, k, v, [0.9, 1.0], eps)
+    ratio = y / c
+    np.testing.assert_allclose(ratio, ratio[..., :1].repeat(dv, -1), rtol=1e-12)
+    assert np.all(ratio < 1.0) and np.all(ratio > 0.999)
+
+
+def test_lambda_zero_is_diagonal(orc):
+    # lambda = 0 (with 0^0 = 1): only the current token survives
+    rng = np.random.default_rng(6)
+    q, k, v = _rand(rng, 1, 1, 9, 4), _rand(rng, 1, 1, 9, 4), _rand(rng, 1, 1, 9, 2)
+    y = orc.causal(q, k, v, [0.0], 1e-6)
+    a = np.sum(orc.phi_map(q) * orc.phi_map(k), axis=-1)
+    np.testing.assert_allclose(y, v * (a / (a + 1e-6))[..., None], rtol=1e-14)
+
+
+def test_linearity_in_v_and_permutation(orc):
+    rng = np.random.default_rng(8)
+    B, H, N, dk, dv = 2, 3, 15, 4, 2
+    q, k = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk)
+    v1, v2 = _rand(rng, B, H, N, dv), _rand(rng, B, H, N, dv)
+    lam = [0.8, 0.95, 1.0]
+    y1 = orc.causal(q, k, v1, lam)
+    y2 = orc.causal(q, k, v2, lam)
+    y12 = orc.causal(q, k, 2.0 * v1 - 0.5 * v2, lam)
+    np.testing.assert_allclose(y12, 2.0 * y1 - 0.5 * y2, rtol=1e-10, atol=1e-12)
+    # permuting batch rows permutes outputs (each (b,h) is independent)
+    perm = [1, 0]
+    yp = orc.causal(q[perm], k[perm], v1[perm], lam)
+    np.testing.assert_allclose(yp, y1[perm], rtol=0, atol=0)
+
+
+def test_split_resume_and_last_row_noncausal(orc):
+    rng = np.random.default_rng(9)
+    B, H, N, dk, dv = 1, 2, 40, 4, 3
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    lam = [0.9, 1.0]
+    y, S, z = orc.causal(q, k, v, lam, want_state=True)
+    n1 = 17
+    ya, Sa, za = orc.causal(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], lam, want_state=True)
+    yb, Sb, zb = orc.causal(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], lam, S0=Sa, z0=za,
+                            want_state=True)
+    np.testing.assert_allclose(np.concatenate([ya, yb], axis=2), y, rtol=1e-12)
+    np.testing.assert_allclose(Sb, S, rtol=1e-12)
+    np.testing.assert_allclose(zb, z, rtol=1e-12)
+    # lambda = 1: the causal last row equals the non-causal row N-1
+    y1 = orc.causal(q, k, v, [1.0, 1.0])
+    yn = orc.noncausal(q, k, v)
+    np.testing.assert_allclose(y1[:, :, -1], yn[:, :, -1], rtol=1e-12)
+
+
+def test_decode_steps_match_bruteforce(orc):
+    # N decode steps from the zero state equal the quadratic form row by row
+    rng = np.random.default_rng(10)
+    B, H, N, dk, dv = 2, 2, 12, 4, 3
+    lam = np.array([0.85, 1.0])
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    F = dk
+    S = np.zeros((B, H, F, dv))
+    z = np.zeros((B, H, F))
+    ys = []
+    for t in range(N):
+        yt, S, z = orc.decode_step(q[:, :, t:t + 1], k[:, :, t:t + 1], v[:, :, t:t + 1],
+                                   S, z, lam, 1e-6)
+        ys.append(yt)
+    y = np.concatenate(ys, axis=2)
+    pq, pk = orc.phi_map(q), orc.phi_map(k)
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_allclose(y[b, h], _brute_force(pq[b, h], pk[b, h], v[b, h],
+                                                             lam[h], 1e-6), rtol=1e-10)
+
+
+def test_kappa_is_one_for_positive_features(orc):
+    rng = np.random.default_rng(12)
+    q, k, v = _rand(rng, 1, 1, 30, 4), _rand(rng, 1, 1, 30, 4), _rand(rng, 1, 1, 30, 2)
+    # with eps = 0 the companion denominator equals |den| exactly for positive features
+    _, kap = orc.causal(q, k, v, [0.9], 0.0, want_kappa=True)
+    np.testing.assert_allclose(kap, 1.0, rtol=1e-12)
+
+
+def test_rowwise_rel_err_definition(orc):
+    ref = np.array([[1.0, -2.0, 0.0], [0.0, 0.0, 0.0]])
+    y = np.array([[1.1, -2.0, 0.05], [0.0, 0.0, 0.0]])
+    assert abs(orc.rowwise_rel_err(y, ref) - 0.05) < 1e-15
