@@ -1,0 +1,155 @@
+/*
+ * la.h -- C ABI of liblinattn: causal kernelized linear attention in
+ * fast-weight form on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, tokens i = 0..N-1):
+ *
+ *   S_i = lambda_h * S_{i-1} + phi(k_i) v_i^T          state,      [F x d_v]
+ *   z_i = lambda_h * z_{i-1} + phi(k_i)                normaliser, [F]
+ *   y_i = phi(q_i)^T S_i / (phi(q_i)^T z_i + eps)
+ *
+ * The state is updated with token i before it is queried by token i.
+ * Sources: "Attention is also an FFN" (kwkr.cn/news/587576) sec. 2.1 (fast
+ * weight state and its outer-product recurrence), sec. 3.2 (decay lambda),
+ * sec. 4.2 (normaliser z, eps, decay applied to z as well); "From standard
+ * attention to linear attention" (tqpw.cn/news/561043) sec. 3 (S and Z,
+ * non-causal form), sec. 4.1 (elu+1), sec. 4.2 (random cos/sin features),
+ * sec. 6 (state layout, autoregressive step).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are row-major and contiguous: q, k [B,H,N,d_k]; v, y [B,H,N,d_v];
+ *    state S [B,H,F,d_v] fp32 and z [B,H,F] fp32.  F = d_k for LA_PHI_ELU1 and
+ *    F = 2m for LA_PHI_TRIG_RF.  Every device pointer must be 16-byte aligned.
+ *  - The caller owns and allocates every device buffer, including the
+ *    workspace sized by la_workspace_size().  The library never allocates,
+ *    frees or synchronises.  Descriptors and lambda_h are host memory, read
+ *    only during the call.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  For fixed shapes the result is bitwise deterministic.
+ *  - Validation happens on the host before anything is enqueued.  On failure
+ *    a non-zero la_status is returned, la_last_error() describes it, and
+ *    nothing is enqueued.  A failed launch returns LA_ERR_HIP.  Device faults
+ *    surface at the caller's next synchronisation.
+ *  - Support matrix: d_k, d_v in {64, 128}; LA_PHI_TRIG_RF with m in {32, 64,
+ *    128} (F = 2m) and d_k * m <= 8192; in_dtype LA_BF16 or LA_F32; out_dtype
+ *    equal to in_dtype or LA_F32.  Other valid shapes return LA_ERR_UNSUPPORTED.
+ *  - H <= LA_MAX_HEADS; lambda_h values must lie in [0, 1] (0^0 is taken as 1);
+ *    eps must be finite and >= 0.
+ */
+#ifndef LA_H_
+#define LA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream handle (hipStream_t); NULL selects the null stream. */
+typedef struct ihipStream_t* la_stream_t;
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARGUMENT = 1,  /* malformed call: null pointer, bad size, lambda or eps */
+    LA_ERR_UNSUPPORTED = 2,       /* valid but outside the support matrix                */
+    LA_ERR_WORKSPACE = 3,         /* workspace missing or smaller than la_workspace_size */
+    LA_ERR_HIP = 4                /* a HIP launch failed; la_last_error() has the text   */
+} la_status;
+
+enum { LA_F32 = 0, LA_BF16 = 1 };             /* element types of q, k, v, y */
+enum { LA_PHI_ELU1 = 0, LA_PHI_TRIG_RF = 1 }; /* feature maps                */
+
+#define LA_MAX_HEADS 256
+
+/* Feature map descriptor.
+ *  LA_PHI_ELU1   : phi(x)_f = x_f + 1 if x_f > 0, else exp(x_f)  ("From standard
+ *                  attention to linear attention" sec. 4.1: elu with alpha 1, plus
+ *                  one).  m = 0, omega = NULL, qk_scale must be 1.
+ *  LA_PHI_TRIG_RF: x' = qk_scale * x, u = omega x',
+ *                  phi(x) = exp(-|x'|^2 / 2) / sqrt(m) [cos u_1..u_m, sin u_1..u_m]
+ *                  (same page, sec. 4.2).  omega is a device pointer to an fp32
+ *                  [m, d_k] row-major matrix supplied by the caller (the random
+ *                  directions are an input: draw them once from a fixed seed and
+ *                  share them).  qk_scale is typically d_k^(-1/4).             */
+typedef struct {
+    int32_t kind;
+    int32_t m;
+    const float* omega;
+    float qk_scale;
+} la_phi;
+
+/* Problem shape and element types.  For la_decode_step N must be 1. */
+typedef struct {
+    int64_t B, H, N;
+    int32_t d_k, d_v;
+    int32_t in_dtype, out_dtype;
+} la_shape;
+
+/* Zero the state: S[B,H,F,d_v] = 0 and z[B,H,F] = 0 (fp32, device memory).
+ * "Attention is also an FFN" sec. 4.1 and "From standard attention to linear
+ * attention" sec. 6: the recurrent state starts at zero.  Implemented with a
+ * fill kernel (no hipMemset node), so it may be recorded into a HIP graph.
+ * Either pointer may be NULL to skip that buffer. */
+la_status la_init_state(float* S, float* z, int64_t B, int64_t H, int32_t F, int32_t d_v,
+                        la_stream_t stream);
+
+/* Bytes of device workspace that la_forward_causal (causal != 0) or
+ * la_forward_noncausal (causal == 0) needs for this shape; 0 when none is
+ * needed.  Returns 0 for shapes that fail validation as well. */
+size_t la_workspace_size(const la_shape* shape, const la_phi* phi, int32_t causal);
+
+/* Causal forward over [B,H,N,d].
+ * q, k, v: device inputs of shape->in_dtype; y: device output [B,H,N,d_v] of
+ * shape->out_dtype, must not alias q, k or v.  lambda_h: host array [H] of
+ * per-head decays, NULL means lambda = 1 for every head.  S_in [B,H,F,d_v] /
+ * z_in [B,H,F]: optional initial state (both NULL = zero state; both or none).
+ * S_out / z_out: optional final state (both or none); S_out may equal S_in and
+ * z_out may equal z_in for an in-place carry.  N = 0 copies S_in to S_out (or
+ * zeroes S_out) and returns LA_OK.
+ * Method ("Attention is also an FFN" sec. 4.1 and sec. 5.2: cut the sequence
+ * into chunks, parallel inside a chunk, carried across chunks): the sequence
+ * is cut into chunks of C tokens; inside a chunk the decayed, masked scores
+ * phi(Q) phi(K)^T and their product with V run on matrix cores, the chunk
+ * reads the carried state, and the state is carried forward as
+ * S <- lambda^n S + sum_j lambda^(n-1-j) phi(k_j) v_j^T.  Long sequences are
+ * additionally split into segments whose states are combined by a scan. */
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* y,
+                            const la_shape* shape, const la_phi* phi,
+                            const float* lambda_h, float eps,
+                            const float* S_in, const float* z_in,
+                            float* S_out, float* z_out,
+                            void* workspace, size_t workspace_bytes, la_stream_t stream);
+
+/* Non-causal forward ("From standard attention to linear attention" sec. 3
+ * and sec. 6): S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j) over the whole
+ * sequence (no decay), then y_i = phi(q_i)^T S / (phi(q_i)^T z + eps).
+ * Arguments as for la_forward_causal.  N must be >= 1. */
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* y,
+                               const la_shape* shape, const la_phi* phi, float eps,
+                               void* workspace, size_t workspace_bytes, la_stream_t stream);
+
+/* One recurrent decode step, in place ("From standard attention to linear
+ * attention" sec. 6 autoregressive step, with the decay of "Attention is also
+ * an FFN" sec. 3.2): per (b,h)
+ *   S <- lambda_h S + phi(k) v^T,  z <- lambda_h z + phi(k),
+ *   y  = phi(q)^T S / (phi(q)^T z + eps).
+ * q, k: [B,H,1,d_k]; v: [B,H,1,d_v]; y: [B,H,1,d_v]; S [B,H,F,d_v] and
+ * z [B,H,F] fp32 are read and overwritten.  shape->N must be 1. */
+la_status la_decode_step(const void* q, const void* k, const void* v, void* y,
+                         float* S, float* z, const la_shape* shape, const la_phi* phi,
+                         const float* lambda_h, float eps, la_stream_t stream);
+
+/* Static description of a status code. */
+const char* la_status_string(la_status status);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * ("" when none).  The pointer stays valid until the next call on the thread. */
+const char* la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H_ */

@@ -1,0 +1,70 @@
+"""Helpers for the GPU parity tests: seeded inputs to device tensors, calls
+through the C ABI binding, and the oracle comparison metric."""
+import numpy as np
+import torch
+
+import oracle
+import seeded_inputs as si
+import weight_sequence_mixing_amd as la
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = torch.device("cuda:0")
+
+
+def to_dev(inp, name, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(inp[name])).to(DEV)
+
+
+def tdtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def phi_for(wl, omega_np):
+    if wl.phi == "trig_rf":
+        return la.Phi("trig_rf", torch.from_numpy(omega_np).to(DEV), wl.qk_scale)
+    return la.Phi()
+
+
+def run_causal(wl, inp, lam=None, out_f32=False, S_in=None, z_in=None, want_state=False, eps=None):
+    q, k, v = (to_dev(inp, n, wl.dtype) for n in ("q", "k", "v"))
+    B, H, N, _ = q.shape
+    ydt = torch.float32 if out_f32 else tdtype(wl.dtype)
+    y = torch.full((B, H, N, wl.dv), float("nan"), dtype=ydt, device=DEV)
+    phi = phi_for(wl, inp.get("omega"))
+    F = wl.F
+    S_out = z_out = None
+    if want_state:
+        S_out = torch.full((B, H, F, wl.dv), float("nan"), dtype=torch.float32, device=DEV)
+        z_out = torch.full((B, H, F), float("nan"), dtype=torch.float32, device=DEV)
+    lam = inp["lam"] if lam is None else lam
+    la.la_forward_causal(q, k, v, y, phi=phi, lambda_h=list(map(float, lam)),
+                         eps=wl.eps if eps is None else eps, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
+    torch.cuda.synchronize()
+    if want_state:
+        return y, S_out, z_out
+    return y
+
+
+def oracle_causal(wl, inp, lam=None, heads=None, **kw):
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    lam = inp["lam"] if lam is None else lam
+    if heads is not None:
+        b, h = heads
+        q, k, v = q[b][:, h], k[b][:, h], v[b][:, h]
+        lam = np.asarray(lam)[h]
+    return oracle.causal(q, k, v, lam, kw.pop("eps", wl.eps), wl.phi, inp.get("omega"), wl.qk_scale, **kw)
+
+
+def rel_err(y_gpu, y_ref):
+    y = y_gpu.float().cpu().numpy() if isinstance(y_gpu, torch.Tensor) else y_gpu
+    return oracle.rowwise_rel_err(y, y_ref)
+
+
+def inputs(index, **over):
+    wl = si.workload(index)
+    sizes = {k: over.pop(k) for k in ("B", "H", "N") if k in over}
+    if over:
+        wl = wl.with_(**over)
+    return wl, si.make_inputs(wl, **sizes)

@@ -1,0 +1,119 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects malformed calls during host-side validation (nothing is enqueued, so
+no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_sequence_mixing_amd as la
+from weight_sequence_mixing_amd.binding import LaPhiC, LaShapeC
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la.load_library()
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "la.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"^\s*(?:la_status|size_t|const char\*)\s+(la_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = _declared()
+    assert set(names) == set(la.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED",
+                                 "LA_ERR_WORKSPACE", "LA_ERR_HIP"]):
+        assert la.la_status_string(code) == name
+
+
+def _shape(B=1, H=2, N=64, dk=64, dv=64, it=la.LA_BF16, ot=None):
+    return LaShapeC(B, H, N, dk, dv, it, it if ot is None else ot)
+
+
+ELU = LaPhiC(la.LA_PHI_ELU1, 0, None, 1.0)
+
+
+GAP = 1 << 32
+
+
+def _causal(lib, shape, phi=ELU, lam=None, eps=1e-6, q=FAKE, k=FAKE + GAP, v=FAKE + 2 * GAP,
+            y=FAKE + 3 * GAP, S_in=None, z_in=None, S_out=None, z_out=None, ws=None, ws_bytes=0):
+    lam_arr = None
+    if lam is not None:
+        lam_arr = (ctypes.c_float * len(lam))(*lam)
+    return lib.la_forward_causal(q, k, v, y, ctypes.byref(shape), ctypes.byref(phi),
+                                 ctypes.cast(lam_arr, ctypes.c_void_p) if lam_arr else None, eps,
+                                 S_in, z_in, S_out, z_out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(shape=_shape(dk=96)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(dv=32)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(B=0)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(N=-1)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(H=300)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(it=7)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(it=la.LA_F32, ot=la.LA_BF16)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(), lam=[1.5, 1.0]), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), lam=[-0.1, 1.0]), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), lam=[float("nan"), 1.0]), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), eps=-1.0), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), eps=float("inf")), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), S_in=FAKE), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), S_out=FAKE, z_out=None), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), q=None), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), q=FAKE + 8), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), y=FAKE), la.binding.LA_ERR_INVALID_ARGUMENT),          # y aliases q
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_ELU1, 4, None, 1.0)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_TRIG_RF, 64, None, 0.35)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_TRIG_RF, 48, FAKE, 0.35)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(dk=128), phi=LaPhiC(la.LA_PHI_TRIG_RF, 128, FAKE, 0.35)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(), phi=LaPhiC(9, 0, None, 1.0)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(B=4, H=8, N=4096)), la.binding.LA_ERR_WORKSPACE),        # needs a workspace
+    (dict(shape=_shape(B=4, H=8, N=4096), ws=FAKE + 5 * (1 << 32), ws_bytes=16), la.binding.LA_ERR_WORKSPACE),
+])
+def test_causal_validation(lib, kw, status):
+    st = _causal(lib, **kw)
+    assert st == status, (st, la.la_last_error())
+    assert la.la_last_error()
+
+
+def test_workspace_size_queries(lib):
+    s = _shape(B=4, H=8, N=4096)
+    assert lib.la_workspace_size(ctypes.byref(s), ctypes.byref(ELU), 1) > 0
+    assert lib.la_workspace_size(ctypes.byref(s), ctypes.byref(ELU), 0) > 0
+    bad = _shape(dk=96)
+    assert lib.la_workspace_size(ctypes.byref(bad), ctypes.byref(ELU), 1) == 0
+    # a long single head splits into segments: the workspace holds their states
+    one = _shape(B=1, H=1, N=1 << 16, dk=128, dv=128)
+    ws = lib.la_workspace_size(ctypes.byref(one), ctypes.byref(ELU), 1)
+    assert ws >= 2 * (128 * 128 + 128) * 4
+
+
+def test_noncausal_and_decode_validation(lib):
+    s = _shape(N=0)
+    st = lib.la_forward_noncausal(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, ctypes.byref(s),
+                                  ctypes.byref(ELU), 1e-6, None, 0, None)
+    assert st == la.binding.LA_ERR_INVALID_ARGUMENT
+    s = _shape(N=2)
+    st = lib.la_decode_step(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                            FAKE + 0x500000, ctypes.byref(s), ctypes.byref(ELU), None, 1e-6, None)
+    assert st == la.binding.LA_ERR_INVALID_ARGUMENT
+    s = _shape(N=1)
+    st = lib.la_decode_step(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, None,
+                            FAKE + 0x500000, ctypes.byref(s), ctypes.byref(ELU), None, 1e-6, None)
+    assert st == la.binding.LA_ERR_INVALID_ARGUMENT
+    st = lib.la_init_state(FAKE, FAKE, 0, 1, 64, 64, None)
+    assert st == la.binding.LA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,224 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Metric: max over rows (b,h,i) of max_c |y - y_ref| / max_c |y_ref|.
+Bars: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (fp32 state).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import weight_sequence_mixing_amd as la
+from gpu_util import DEV, TOL, inputs, oracle_causal, phi_for, rel_err, run_causal, tdtype, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_single_hip_runtime_loaded():
+    la.load_library()
+    torch.zeros(1, device=DEV)
+    with open("/proc/self/maps") as fh:
+        libs = {line.split()[-1] for line in fh if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+
+
+def test_workload1_fp32_full():
+    wl, inp = inputs(1)
+    y = run_causal(wl, inp)
+    err = rel_err(y, oracle_causal(wl, inp))
+    assert err < TOL["f32"], err
+
+
+@pytest.mark.parametrize("N", [1, 31, 64, 65, 300])
+def test_workload2_small_ragged(N):
+    wl, inp = inputs(2, B=1, H=2, N=N)
+    lam = [0.9, 1.0]
+    y = run_causal(wl, inp, lam=lam)
+    err = rel_err(y, oracle_causal(wl, inp, lam=lam))
+    assert err < TOL["bf16"], err
+
+
+def test_workload2_full():
+    wl, inp = inputs(2)
+    y = run_causal(wl, inp)
+    err = rel_err(y, oracle_causal(wl, inp))
+    assert err < TOL["bf16"], err
+
+
+def test_bf16_inputs_fp32_output():
+    wl, inp = inputs(2, B=2, H=2, N=500)
+    y = run_causal(wl, inp, out_f32=True)
+    assert y.dtype == torch.float32
+    err = rel_err(y, oracle_causal(wl, inp))
+    assert err < TOL["bf16"], err
+
+
+def test_workload3_reduced_per_head_decay():
+    wl, inp = inputs(3, B=1, H=4, N=2000)
+    y = run_causal(wl, inp)
+    err = rel_err(y, oracle_causal(wl, inp))
+    assert err < TOL["bf16"], err
+
+
+def test_workload3_full_sampled_heads():
+    wl, inp = inputs(3)
+    y = run_causal(wl, inp)
+    for b, h in ((0, 0), (1, 15)):
+        ref = oracle.causal(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
+                            inp["v"][b:b + 1, h:h + 1], [inp["lam"][h]], wl.eps)
+        err = rel_err(y[b:b + 1, h:h + 1], ref)
+        assert err < TOL["bf16"], (b, h, err)
+    assert torch.isfinite(y.float()).all()
+
+
+def test_workload5_reduced_random_features():
+    wl, inp = inputs(5, H=2, N=1000)
+    y = run_causal(wl, inp)
+    ref, kap = oracle_causal(wl, inp, want_kappa=True)
+    err = rel_err(y, ref)
+    assert err < TOL["bf16"], (err, float(kap.max()))
+
+
+def test_workload5_full_sampled_head():
+    wl, inp = inputs(5)
+    y = run_causal(wl, inp)
+    h = 3
+    ref = oracle.causal(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1], [1.0], wl.eps,
+                        "trig_rf", inp["omega"], wl.qk_scale)
+    err = rel_err(y[:, h:h + 1], ref)
+    assert err < TOL["bf16"], err
+    assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("dk,m,dv", [(64, 64, 128), (128, 32, 64)])
+def test_random_features_other_shapes(dk, m, dv):
+    wl = si.workload(5).with_(dk=dk, m=m, dv=dv)
+    inp = si.make_inputs(wl, B=1, H=2, N=333)
+    y = run_causal(wl, inp, lam=[0.97, 1.0])
+    err = rel_err(y, oracle_causal(wl, inp, lam=[0.97, 1.0]))
+    assert err < TOL["bf16"], err
+
+
+@pytest.mark.parametrize("phi", ["elu1", "trig_rf"])
+def test_fp32_inputs_small(phi):
+    wl = si.workload(1).with_(phi=phi, m=32 if phi == "trig_rf" else 0)
+    inp = si.make_inputs(wl, B=1, H=2, N=200)
+    y = run_causal(wl, inp, lam=[0.95, 1.0])
+    err = rel_err(y, oracle_causal(wl, inp, lam=[0.95, 1.0]))
+    assert err < TOL["f32"], err
+
+
+def test_lambda_zero_and_one():
+    wl, inp = inputs(2, B=1, H=2, N=130)
+    y = run_causal(wl, inp, lam=[0.0, 1.0])
+    err = rel_err(y, oracle_causal(wl, inp, lam=[0.0, 1.0]))
+    assert err < TOL["bf16"], err
+
+
+def test_state_out_and_split_resume():
+    wl, inp = inputs(3, B=1, H=2, N=700)
+    y, S, z = run_causal(wl, inp, want_state=True)
+    ref, Sr, zr = oracle_causal(wl, inp, want_state=True)
+    assert rel_err(y, ref) < TOL["bf16"]
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=2e-2)
+    # resume: first 257 tokens, then the rest from the carried state
+    n1 = 257
+    first = {k: (v[:, :, :n1] if isinstance(v, np.ndarray) and v.ndim == 4 else v) for k, v in inp.items()}
+    rest = {k: (v[:, :, n1:] if isinstance(v, np.ndarray) and v.ndim == 4 else v) for k, v in inp.items()}
+    ya, Sa, za = run_causal(wl, first, want_state=True)
+    yb = run_causal(wl, rest, S_in=Sa, z_in=za)
+    y2 = torch.cat([ya, yb], dim=2)
+    assert rel_err(y2, ref) < TOL["bf16"]
+    # in place: S_out aliases S_in
+    q, k, v = (to_dev(rest, n, wl.dtype) for n in ("q", "k", "v"))
+    yc = torch.empty_like(yb)
+    la.la_forward_causal(q, k, v, yc, lambda_h=list(map(float, inp["lam"])), eps=wl.eps,
+                         S_in=Sa, z_in=za, S_out=Sa, z_out=za)
+    torch.cuda.synchronize()
+    assert torch.equal(yc, yb)
+    np.testing.assert_allclose(Sa.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+
+
+@pytest.mark.parametrize("segs,wins", [(1, 1), (3, 1), (7, 1), (1, 3), (4, 2)])
+def test_segment_and_window_invariance(monkeypatch, segs, wins):
+    wl, inp = inputs(3, B=1, H=2, N=1500)
+    monkeypatch.setenv("LA_SEGMENTS", str(segs))
+    monkeypatch.setenv("LA_WINDOWS", str(wins))
+    y, S, z = run_causal(wl, inp, want_state=True)
+    ref, Sr, zr = oracle_causal(wl, inp, want_state=True)
+    assert rel_err(y, ref) < TOL["bf16"]
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
+
+
+def test_deterministic_repeat():
+    wl, inp = inputs(2, B=2, H=4, N=1000)
+    y1 = run_causal(wl, inp)
+    y2 = run_causal(wl, inp)
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("index,over", [(2, dict(B=2, H=4, N=777)), (5, dict(H=2, N=900)), (1, {})])
+def test_noncausal(index, over):
+    wl, inp = inputs(index, **over)
+    q, k, v = (to_dev(inp, n, wl.dtype) for n in ("q", "k", "v"))
+    B, H, N, _ = q.shape
+    y = torch.empty(B, H, N, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_noncausal(q, k, v, y, phi=phi_for(wl, inp["omega"]), eps=wl.eps)
+    torch.cuda.synchronize()
+    ref = oracle.noncausal(inp["q"], inp["k"], inp["v"], wl.eps, wl.phi, inp["omega"], wl.qk_scale)
+    err = rel_err(y, ref)
+    assert err < TOL[wl.dtype], err
+
+
+def _decode_run(wl, B, H, steps):
+    pre = si.make_decode_prefix(wl, B=B, H=H)
+    lam = si.make_lambda(wl, H=H)
+    q, k, v = (to_dev(pre, n, wl.dtype) for n in ("q", "k", "v"))
+    F = wl.F
+    S = torch.empty(B, H, F, wl.dv, dtype=torch.float32, device=DEV)
+    z = torch.empty(B, H, F, dtype=torch.float32, device=DEV)
+    yp = torch.empty(B, H, wl.N, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_causal(q, k, v, yp, lambda_h=list(map(float, lam)), eps=wl.eps, S_out=S, z_out=z)
+    ys, step_inp = [], []
+    for t in range(steps):
+        st = si.make_decode_step(wl, t, B=B, H=H)
+        step_inp.append(st)
+        qs, ks, vs = (to_dev(st, n, wl.dtype) for n in ("q", "k", "v"))
+        y = torch.empty(B, H, 1, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+        la.la_decode_step(qs, ks, vs, y, S, z, lambda_h=list(map(float, lam)), eps=wl.eps)
+        ys.append(y)
+    torch.cuda.synchronize()
+    return pre, lam, step_inp, torch.cat(ys, dim=2), S, z
+
+
+def test_decode_reduced_matches_forward_trajectory():
+    wl = si.workload(4)
+    B, H, steps = 2, 4, 16
+    pre, lam, step_inp, y, S, z = _decode_run(wl, B, H, steps)
+    cat = {n: np.concatenate([pre[n]] + [s[n] for s in step_inp], axis=2) for n in ("q", "k", "v")}
+    ref, Sr, zr = oracle.causal(cat["q"], cat["k"], cat["v"], lam, wl.eps, want_state=True)
+    assert rel_err(y, ref[:, :, wl.N:]) < TOL["bf16"]
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+
+
+def test_decode_full_size_sampled():
+    wl = si.workload(4)
+    steps = 4
+    pre, lam, step_inp, y, S, z = _decode_run(wl, wl.B, wl.H, steps)
+    rng = np.random.default_rng(0)
+    for b, h in zip(rng.integers(0, wl.B, 6), rng.integers(0, wl.H, 6)):
+        cat = {n: np.concatenate([pre[n][b:b + 1, h:h + 1]] + [s[n][b:b + 1, h:h + 1] for s in step_inp], axis=2)
+               for n in ("q", "k", "v")}
+        ref = oracle.causal(cat["q"], cat["k"], cat["v"], [lam[h]], wl.eps)
+        assert rel_err(y[b:b + 1, h:h + 1], ref[:, :, wl.N:]) < TOL["bf16"], (b, h)
+
+
+def test_init_state_zeroes():
+    S = torch.full((2, 3, 64, 128), 7.0, device=DEV)
+    z = torch.full((2, 3, 64), 7.0, device=DEV)
+    la.la_init_state(S, z)
+    torch.cuda.synchronize()
+    assert float(S.abs().max()) == 0.0 and float(z.abs().max()) == 0.0

@@ -1,0 +1,13 @@
+"""weight_sequence_mixing_amd -- causal kernelized linear attention in
+fast-weight form for AMD Instinct MI355X (gfx950).
+
+The computation lives in liblinattn.so (hand-written HIP kernels behind the C
+ABI declared in include/la.h).  This package is its thin Python binding: the
+functions below carry the C names and only marshal torch tensors, shapes and
+the current HIP stream.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, LA_BF16, LA_F32, LA_MAX_HEADS, LA_PHI_ELU1, LA_PHI_TRIG_RF, LaError, Phi,
+    la_decode_step, la_forward_causal, la_forward_noncausal, la_init_state, la_last_error,
+    la_status_string, la_workspace_size, load_library, rf_scale,
+)

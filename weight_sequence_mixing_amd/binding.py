@@ -1,0 +1,227 @@
+"""Thin ctypes binding of liblinattn (include/la.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors supply device pointers, shapes and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if the library is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_OK, LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_F32, LA_BF16 = 0, 1
+LA_PHI_ELU1, LA_PHI_TRIG_RF = 0, 1
+LA_MAX_HEADS = 256
+
+# names declared in include/la.h
+EXPORTS = ("la_init_state", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
+           "la_decode_step", "la_status_string", "la_last_error")
+
+
+class LaPhiC(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("omega", ctypes.c_void_p), ("qk_scale", ctypes.c_float)]
+
+
+class LaShapeC(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class LaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (_status_name(status), detail))
+        self.status = status
+
+
+_lib = None
+
+
+def _status_name(s):
+    return {0: "LA_OK", 1: "LA_ERR_INVALID_ARGUMENT", 2: "LA_ERR_UNSUPPORTED",
+            3: "LA_ERR_WORKSPACE", 4: "LA_ERR_HIP"}.get(int(s), "LA_ERR_UNKNOWN")
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load liblinattn.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("liblinattn.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m weight_sequence_mixing_amd.build" % p)
+    lib = ctypes.CDLL(p)
+    vp, sz, f, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_int32, ctypes.c_int64
+    SP, PP = ctypes.POINTER(LaShapeC), ctypes.POINTER(LaPhiC)
+    lib.la_init_state.argtypes = [vp, vp, i64, i64, i32, i32, vp]
+    lib.la_init_state.restype = ctypes.c_int
+    lib.la_workspace_size.argtypes = [SP, PP, i32]
+    lib.la_workspace_size.restype = sz
+    lib.la_forward_causal.argtypes = [vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_forward_causal.restype = ctypes.c_int
+    lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, SP, PP, f, vp, sz, vp]
+    lib.la_forward_noncausal.restype = ctypes.c_int
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp]
+    lib.la_decode_step.restype = ctypes.c_int
+    lib.la_status_string.argtypes = [ctypes.c_int]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_last_error.argtypes = []
+    lib.la_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != LA_OK:
+        raise LaError(status, _lib.la_last_error().decode())
+
+
+@dataclass
+class Phi:
+    """Feature map: 'elu1' (elu(x)+1) or 'trig_rf' (cos/sin random features).
+
+    For 'trig_rf', omega is a device fp32 tensor [m, d_k] and qk_scale the
+    factor applied to q and k before the map (typically d_k ** -0.25)."""
+    kind: str = "elu1"
+    omega: Optional[torch.Tensor] = None
+    qk_scale: float = 1.0
+
+    def c(self) -> LaPhiC:
+        if self.kind == "elu1":
+            return LaPhiC(LA_PHI_ELU1, 0, None, 1.0)
+        om = self.omega
+        if om is None:
+            return LaPhiC(LA_PHI_TRIG_RF, 0, None, float(self.qk_scale))
+        if om.dtype != torch.float32 or not om.is_contiguous():
+            raise ValueError("omega must be a contiguous float32 tensor")
+        return LaPhiC(LA_PHI_TRIG_RF, int(om.shape[0]), om.data_ptr(), float(self.qk_scale))
+
+    def F(self, d_k: int) -> int:
+        return d_k if self.kind == "elu1" else 2 * int(self.omega.shape[0])
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise ValueError("unsupported dtype %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shape(q: torch.Tensor, v: torch.Tensor, y: torch.Tensor) -> LaShapeC:
+    B, H, N, dk = q.shape
+    return LaShapeC(B, H, N, dk, v.shape[-1], _dt(q), _dt(y))
+
+
+def _lam(lambda_h, H):
+    if lambda_h is None:
+        return None, None
+    if isinstance(lambda_h, torch.Tensor):
+        lambda_h = lambda_h.detach().to("cpu", torch.float32).reshape(-1).tolist()
+    arr = (ctypes.c_float * H)(*[float(x) for x in lambda_h])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def la_status_string(status: int) -> str:
+    return load_library().la_status_string(int(status)).decode()
+
+
+def la_last_error() -> str:
+    return load_library().la_last_error().decode()
+
+
+def la_init_state(S: torch.Tensor, z: torch.Tensor, stream=None) -> None:
+    """S [B,H,F,d_v] = 0, z [B,H,F] = 0 (fp32 device tensors)."""
+    load_library()
+    B, H, F, dv = S.shape
+    _check(_lib.la_init_state(_ptr(S), _ptr(z), B, H, F, dv, _stream(stream)))
+
+
+def la_workspace_size(B, H, N, d_k, d_v, in_dtype=LA_BF16, out_dtype=None, phi: Optional[Phi] = None,
+                      causal: bool = True) -> int:
+    load_library()
+    phi = phi or Phi()
+    shape = LaShapeC(B, H, N, d_k, d_v, in_dtype, in_dtype if out_dtype is None else out_dtype)
+    pc = phi.c()
+    return int(_lib.la_workspace_size(ctypes.byref(shape), ctypes.byref(pc), 1 if causal else 0))
+
+
+def _workspace(shape: LaShapeC, pc: LaPhiC, causal: bool, workspace, device):
+    need = int(_lib.la_workspace_size(ctypes.byref(shape), ctypes.byref(pc), 1 if causal else 0))
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def la_forward_causal(q, k, v, y, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6,
+                      S_in=None, z_in=None, S_out=None, z_out=None, workspace=None, stream=None):
+    """Causal forward; writes y [B,H,N,d_v] (and S_out, z_out when given)."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    pc = phi.c()
+    ws, ws_bytes = _workspace(shape, pc, True, workspace, q.device)
+    lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    _check(_lib.la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
+                                  lam_ptr, float(eps), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                  _ptr(ws), ws_bytes, _stream(stream)))
+    del lam_keep
+    return y
+
+
+def la_forward_noncausal(q, k, v, y, phi: Optional[Phi] = None, eps: float = 1e-6, workspace=None, stream=None):
+    """Non-causal forward; writes y [B,H,N,d_v]."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    pc = phi.c()
+    ws, ws_bytes = _workspace(shape, pc, False, workspace, q.device)
+    _check(_lib.la_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
+                                     float(eps), _ptr(ws), ws_bytes, _stream(stream)))
+    return y
+
+
+def la_decode_step(q, k, v, y, S, z, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6, stream=None):
+    """One decode step on [B,H,1,d] inputs; updates S [B,H,F,d_v] and z [B,H,F] in place."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    pc = phi.c()
+    lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    _check(_lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S), _ptr(z), ctypes.byref(shape),
+                               ctypes.byref(pc), lam_ptr, float(eps), _stream(stream)))
+    del lam_keep
+    return y
+
+
+def rf_scale(d_k: int) -> float:
+    return float(d_k) ** -0.25 if d_k > 0 else 1.0
+

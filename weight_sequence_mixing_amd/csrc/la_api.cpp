@@ -1,0 +1,484 @@
+// la_api.cpp -- the C ABI of liblinattn: host-side validation, work planning
+// (chunks, segments, windows, workspace) and kernel dispatch.
+//
+// Every argument is checked on the host before anything is enqueued; no call
+// allocates, frees or synchronises.  See include/la.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "la_internal.h"
+
+using namespace la;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+la_status fail(la_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+la_status ok()
+{
+    return LA_OK;
+}
+
+la_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+const KernelEntry* find_entry(int in_dtype, int phi, int dk, int F, int dv)
+{
+    const KernelEntry* tables[] = {kEntriesBf16Elu, kEntriesBf16Rf, kEntriesF32};
+    const int counts[] = {kNumEntriesBf16Elu, kNumEntriesBf16Rf, kNumEntriesF32};
+    for (int t = 0; t < 3; ++t)
+        for (int i = 0; i < counts[t]; ++i) {
+            const KernelEntry& e = tables[t][i];
+            if (e.in_dtype == in_dtype && e.phi == phi && e.dk == dk && e.F == F && e.dv == dv) return &e;
+        }
+    return nullptr;
+}
+
+bool aligned16(const void* p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+size_t elem_size(int dtype)
+{
+    return dtype == LA_BF16 ? 2 : 4;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shape and feature-map checks shared by every entry point.  On success sets
+// F and the kernel table entry.
+la_status check_shape(const la_shape* s, const la_phi* phi, int64_t min_n, int64_t max_n,
+                      int* F_out, const KernelEntry** entry_out)
+{
+    if (!s) return fail(LA_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (!phi) return fail(LA_ERR_INVALID_ARGUMENT, "phi is NULL");
+    if (s->B < 1 || s->H < 1) return fail(LA_ERR_INVALID_ARGUMENT, "B and H must be >= 1 (got B=%lld H=%lld)",
+                                          (long long)s->B, (long long)s->H);
+    if (s->N < min_n || s->N > max_n)
+        return fail(LA_ERR_INVALID_ARGUMENT, "N=%lld outside [%lld, %lld]", (long long)s->N, (long long)min_n,
+                    (long long)max_n);
+    if (s->H > LA_MAX_HEADS) return fail(LA_ERR_UNSUPPORTED, "H=%lld exceeds LA_MAX_HEADS=%d", (long long)s->H, LA_MAX_HEADS);
+    if (s->d_k < 1 || s->d_v < 1) return fail(LA_ERR_INVALID_ARGUMENT, "d_k and d_v must be >= 1");
+    if (s->in_dtype != LA_F32 && s->in_dtype != LA_BF16) return fail(LA_ERR_INVALID_ARGUMENT, "unknown in_dtype %d", s->in_dtype);
+    if (s->out_dtype != LA_F32 && s->out_dtype != LA_BF16) return fail(LA_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", s->out_dtype);
+    if (s->out_dtype != s->in_dtype && s->out_dtype != LA_F32)
+        return fail(LA_ERR_UNSUPPORTED, "out_dtype must equal in_dtype or be LA_F32");
+    if ((s->d_k != 64 && s->d_k != 128) || (s->d_v != 64 && s->d_v != 128))
+        return fail(LA_ERR_UNSUPPORTED, "d_k=%d d_v=%d: supported head sizes are 64 and 128", s->d_k, s->d_v);
+    int F = 0;
+    if (phi->kind == LA_PHI_ELU1) {
+        if (phi->m != 0 || phi->omega != nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "elu+1 takes m = 0 and omega = NULL");
+        if (phi->qk_scale != 1.0f) return fail(LA_ERR_INVALID_ARGUMENT, "elu+1 takes qk_scale = 1");
+        F = s->d_k;
+    } else if (phi->kind == LA_PHI_TRIG_RF) {
+        if (phi->m < 1) return fail(LA_ERR_INVALID_ARGUMENT, "random features need m >= 1 (got %d)", phi->m);
+        if (!phi->omega) return fail(LA_ERR_INVALID_ARGUMENT, "random features need omega");
+        if (!aligned16(phi->omega)) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be 16-byte aligned");
+        if (!std::isfinite(phi->qk_scale) || phi->qk_scale <= 0.f)
+            return fail(LA_ERR_INVALID_ARGUMENT, "qk_scale must be finite and > 0");
+        if (phi->m != 32 && phi->m != 64 && phi->m != 128)
+            return fail(LA_ERR_UNSUPPORTED, "m=%d: supported random-feature counts are 32, 64, 128", phi->m);
+        if ((int64_t)s->d_k * phi->m > 8192) return fail(LA_ERR_UNSUPPORTED, "d_k * m must be <= 8192");
+        F = 2 * phi->m;
+    } else {
+        return fail(LA_ERR_INVALID_ARGUMENT, "unknown feature map kind %d", phi->kind);
+    }
+    const KernelEntry* e = find_entry(s->in_dtype, phi->kind, s->d_k, F, s->d_v);
+    if (!e) return fail(LA_ERR_UNSUPPORTED, "no kernel for dtype=%d phi=%d d_k=%d F=%d d_v=%d", s->in_dtype, phi->kind,
+                        s->d_k, F, s->d_v);
+    *F_out = F;
+    *entry_out = e;
+    return LA_OK;
+}
+
+la_status make_lam(const float* lambda_h, int64_t H, LamTable* t)
+{
+    std::memset(t, 0, sizeof(*t));
+    for (int64_t h = 0; h < H; ++h) {
+        const float l = lambda_h ? lambda_h[h] : 1.0f;
+        if (!std::isfinite(l) || l < 0.f || l > 1.f)
+            return fail(LA_ERR_INVALID_ARGUMENT, "lambda_h[%lld]=%g outside [0, 1]", (long long)h, (double)l);
+        t->lam[h] = l;
+        t->log2lam[h] = (l == 0.f) ? -INFINITY : (float)std::log2((double)l);
+    }
+    return LA_OK;
+}
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+// Work plan of one forward call.
+struct Plan {
+    int C;          // chunk length
+    int P;          // segments per window (upper bound over windows)
+    int W;          // windows
+    int64_t SZ;     // floats per state slot: F*d_v + F
+    size_t ws_bytes;
+};
+
+// Number of workgroups per pass the planner aims for: two per compute unit of
+// an MI355X (256 CUs).
+constexpr int kTargetWorkgroups = 512;
+
+int segments_for(int64_t n_len, int C, int64_t BH)
+{
+    const int64_t NC = (n_len + C - 1) / C;
+    int64_t P = (kTargetWorkgroups + BH - 1) / BH;
+    const int forced = env_int("LA_SEGMENTS", 0);
+    if (forced > 0) P = forced;
+    if (P > NC) P = NC;
+    if (P < 1) P = 1;
+    return (int)P;
+}
+
+Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal)
+{
+    Plan p;
+    p.C = e->C;
+    p.SZ = (int64_t)F * s->d_v + F;
+    const int64_t BH = s->B * s->H;
+    const int64_t NC = (s->N + p.C - 1) / p.C;
+    int W = causal ? env_int("LA_WINDOWS", 1) : 1;
+    if (W < 1) W = 1;
+    if (W > NC) W = (int)(NC > 0 ? NC : 1);
+    p.W = W;
+    // the first window is the longest (windows are cut on chunk boundaries)
+    const int64_t len0 = std::min<int64_t>(s->N, ((NC + W - 1) / W) * p.C);
+    p.P = segments_for(len0 > 0 ? len0 : 1, p.C, BH);
+    size_t floats = 0;
+    if (causal) {
+        if (p.P > 1) floats += (size_t)p.P * BH * p.SZ;
+        if (p.W > 1) floats += (size_t)BH * p.SZ;
+    } else {
+        floats += (size_t)p.P * BH * p.SZ;
+    }
+    p.ws_bytes = floats ? ((floats * sizeof(float) + 255) & ~size_t(255)) : 0;
+    return p;
+}
+
+la_status check_ws(const Plan& p, void* ws, size_t ws_bytes)
+{
+    if (p.ws_bytes == 0) return LA_OK;
+    if (!ws) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", p.ws_bytes);
+    if (ws_bytes < p.ws_bytes) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", p.ws_bytes, ws_bytes);
+    if (!aligned16(ws)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    return LA_OK;
+}
+
+la_status check_io(const void* q, const void* k, const void* v, const void* y, const la_shape* s)
+{
+    if (!q || !k || !v || !y) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and y must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+        return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, y must be 16-byte aligned");
+    const size_t rows = (size_t)s->B * s->H * s->N;
+    const size_t nq = rows * s->d_k * elem_size(s->in_dtype), nv = rows * s->d_v * elem_size(s->in_dtype);
+    const size_t ny = rows * s->d_v * elem_size(s->out_dtype);
+    if (overlaps(y, ny, q, nq) || overlaps(y, ny, k, nq) || overlaps(y, ny, v, nv))
+        return fail(LA_ERR_INVALID_ARGUMENT, "y must not alias q, k or v");
+    return LA_OK;
+}
+
+la_status check_eps(float eps)
+{
+    if (!std::isfinite(eps) || eps < 0.f) return fail(LA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0 (got %g)", (double)eps);
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(la_status s)
+{
+    switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARGUMENT: return "LA_ERR_INVALID_ARGUMENT";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+    }
+    return "LA_ERR_UNKNOWN";
+}
+
+const char* la_last_error(void)
+{
+    return g_last_error.c_str();
+}
+
+la_status la_init_state(float* S, float* z, int64_t B, int64_t H, int32_t F, int32_t d_v, la_stream_t stream)
+{
+    if (B < 1 || H < 1 || F < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARGUMENT, "B, H, F, d_v must be >= 1");
+    if ((S && !aligned16(S)) || (z && !aligned16(z))) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be 16-byte aligned");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (S) e = launch_fill_zero(S, B * H * (int64_t)F * d_v, st);
+    if (e == hipSuccess && z) e = launch_fill_zero(z, B * H * (int64_t)F, st);
+    if (e != hipSuccess) return hip_fail(e, "la_init_state launch");
+    return ok();
+}
+
+size_t la_workspace_size(const la_shape* shape, const la_phi* phi, int32_t causal)
+{
+    int F = 0;
+    const KernelEntry* e = nullptr;
+    const std::string saved = g_last_error;
+    const la_status st = check_shape(shape, phi, causal ? 0 : 1, INT64_MAX / 4, &F, &e);
+    g_last_error = saved;
+    if (st != LA_OK || shape->N == 0) return 0;
+    return make_plan(shape, F, e, causal != 0).ws_bytes;
+}
+
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                            const la_phi* phi, const float* lambda_h, float eps, const float* S_in,
+                            const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                            la_stream_t stream)
+{
+    int F = 0;
+    const KernelEntry* ent = nullptr;
+    la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &ent);
+    if (st != LA_OK) return st;
+    if ((S_in == nullptr) != (z_in == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_in and z_in must be given together");
+    if ((S_out == nullptr) != (z_out == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_out and z_out must be given together");
+    if ((S_in && (!aligned16(S_in) || !aligned16(z_in))) || (S_out && (!aligned16(S_out) || !aligned16(z_out))))
+        return fail(LA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
+    if ((st = check_eps(eps)) != LA_OK) return st;
+    LamTable lam;
+    if ((st = make_lam(lambda_h, shape->H, &lam)) != LA_OK) return st;
+    const int64_t BH = shape->B * shape->H;
+    if (BH > 65535) return fail(LA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)BH);
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    const int64_t nS = BH * F * (int64_t)shape->d_v, nz = BH * F;
+
+    if (shape->N == 0) {
+        hipError_t e = hipSuccess;
+        if (S_out) {
+            if (S_in) {
+                e = launch_copy(S_out, S_in, nS, strm);
+                if (e == hipSuccess) e = launch_copy(z_out, z_in, nz, strm);
+            } else {
+                e = launch_fill_zero(S_out, nS, strm);
+                if (e == hipSuccess) e = launch_fill_zero(z_out, nz, strm);
+            }
+        }
+        if (e != hipSuccess) return hip_fail(e, "la_forward_causal (N=0)");
+        return ok();
+    }
+    if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
+    const Plan plan = make_plan(shape, F, ent, true);
+    if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
+
+    float* ws = static_cast<float*>(workspace);
+    float* segs = ws;                                                     // [P][BH][SZ]
+    float* carry = ws ? ws + (plan.P > 1 ? (size_t)plan.P * BH * plan.SZ : 0) : nullptr;  // [BH][SZ]
+    const int64_t NC = (shape->N + plan.C - 1) / plan.C;
+
+    FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.N = shape->N;
+    a.BH = (int32_t)BH;
+    a.H = (int32_t)shape->H;
+    a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
+    a.eps = eps;
+    a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
+    a.omega = phi->omega;
+    a.lam = lam;
+
+    for (int w = 0; w < plan.W; ++w) {
+        const int64_t c0 = (int64_t)w * NC / plan.W, c1 = (int64_t)(w + 1) * NC / plan.W;
+        const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, shape->N) - n0;
+        const int P = segments_for(n_len, plan.C, BH) <= plan.P ? segments_for(n_len, plan.C, BH) : plan.P;
+        // state entering and leaving this window
+        const float* Si = nullptr;
+        const float* zi = nullptr;
+        int64_t si_stride = 0, zi_stride = 0;
+        if (w == 0) {
+            Si = S_in; zi = z_in; si_stride = (int64_t)F * shape->d_v; zi_stride = F;
+        } else {
+            Si = carry; zi = carry + (int64_t)F * shape->d_v; si_stride = plan.SZ; zi_stride = plan.SZ;
+        }
+        float* So = nullptr;
+        float* zo = nullptr;
+        int64_t so_stride = 0, zo_stride = 0;
+        if (w == plan.W - 1) {
+            So = S_out; zo = z_out; so_stride = (int64_t)F * shape->d_v; zo_stride = F;
+        } else {
+            So = carry; zo = carry + (int64_t)F * shape->d_v; so_stride = plan.SZ; zo_stride = plan.SZ;
+        }
+        a.n0 = n0;
+        a.n_len = n_len;
+        a.P = P;
+        hipError_t e;
+        if (P > 1) {
+            // pass 1: segment-local states
+            FwdArgs l = a;
+            l.S_dst = segs;
+            l.z_dst = segs + (int64_t)F * shape->d_v;
+            l.dst_stride = plan.SZ;
+            l.dst_zstride = plan.SZ;
+            if ((e = ent->fwd(l, MODE_LOCAL, strm)) != hipSuccess) return hip_fail(e, "segment state launch");
+            // pass 2: decayed exclusive scan over segments
+            ScanArgs sa;
+            std::memset(&sa, 0, sizeof(sa));
+            sa.ws = segs;
+            sa.P = P;
+            sa.BH = (int32_t)BH;
+            sa.H = (int32_t)shape->H;
+            sa.F = F;
+            sa.DV = shape->d_v;
+            sa.n_len = n_len;
+            sa.C = plan.C;
+            sa.causal = 1;
+            sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
+            sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
+            sa.lam = lam;
+            if ((e = launch_scan(sa, strm)) != hipSuccess) return hip_fail(e, "segment scan launch");
+            // pass 3: outputs from the carried-in state of each segment
+            FwdArgs c = a;
+            c.S_src = segs;
+            c.z_src = segs + (int64_t)F * shape->d_v;
+            c.src_stride = plan.SZ;
+            c.src_zstride = plan.SZ;
+            c.src_seg_stride = BH * plan.SZ;
+            if ((e = ent->fwd(c, MODE_CAUSAL, strm)) != hipSuccess) return hip_fail(e, "causal output launch");
+        } else {
+            FwdArgs c = a;
+            c.S_src = Si; c.z_src = zi; c.src_stride = si_stride; c.src_zstride = zi_stride;
+            c.src_seg_stride = 0;
+            c.S_dst = So; c.z_dst = zo; c.dst_stride = so_stride; c.dst_zstride = zo_stride;
+            if ((e = ent->fwd(c, MODE_CAUSAL, strm)) != hipSuccess) return hip_fail(e, "causal launch");
+        }
+    }
+    return ok();
+}
+
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                               const la_phi* phi, float eps, void* workspace, size_t workspace_bytes, la_stream_t stream)
+{
+    int F = 0;
+    const KernelEntry* ent = nullptr;
+    la_status st = check_shape(shape, phi, 1, INT64_MAX / 4, &F, &ent);
+    if (st != LA_OK) return st;
+    if ((st = check_eps(eps)) != LA_OK) return st;
+    const int64_t BH = shape->B * shape->H;
+    if (BH > 65535) return fail(LA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)BH);
+    if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
+    const Plan plan = make_plan(shape, F, ent, false);
+    if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+
+    FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.N = shape->N;
+    a.n0 = 0;
+    a.n_len = shape->N;
+    a.BH = (int32_t)BH;
+    a.H = (int32_t)shape->H;
+    a.P = plan.P;
+    a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
+    a.eps = eps;
+    a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
+    a.omega = phi->omega;
+    make_lam(nullptr, shape->H, &a.lam);  // no decay in the non-causal form
+
+    hipError_t e;
+    FwdArgs l = a;
+    l.S_dst = ws;
+    l.z_dst = ws + (int64_t)F * shape->d_v;
+    l.dst_stride = plan.SZ;
+    l.dst_zstride = plan.SZ;
+    if ((e = ent->fwd(l, MODE_LOCAL, strm)) != hipSuccess) return hip_fail(e, "state sum launch");
+    if (plan.P > 1) {
+        ScanArgs sa;
+        std::memset(&sa, 0, sizeof(sa));
+        sa.ws = ws;
+        sa.P = plan.P;
+        sa.BH = (int32_t)BH;
+        sa.H = (int32_t)shape->H;
+        sa.F = F;
+        sa.DV = shape->d_v;
+        sa.n_len = shape->N;
+        sa.C = plan.C;
+        sa.causal = 0;
+        if ((e = launch_scan(sa, strm)) != hipSuccess) return hip_fail(e, "state reduction launch");
+    }
+    FwdArgs qa = a;
+    qa.S_src = ws;
+    qa.z_src = ws + (int64_t)F * shape->d_v;
+    qa.src_stride = plan.SZ;
+    qa.src_zstride = plan.SZ;
+    qa.src_seg_stride = 0;
+    if ((e = ent->fwd(qa, MODE_QUERY, strm)) != hipSuccess) return hip_fail(e, "query launch");
+    return ok();
+}
+
+la_status la_decode_step(const void* q, const void* k, const void* v, void* y, float* S, float* z,
+                         const la_shape* shape, const la_phi* phi, const float* lambda_h, float eps, la_stream_t stream)
+{
+    int F = 0;
+    const KernelEntry* ent = nullptr;
+    la_status st = check_shape(shape, phi, 1, 1, &F, &ent);
+    if (st != LA_OK) return st;
+    if (!S || !z) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be non-NULL");
+    if (!aligned16(S) || !aligned16(z)) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be 16-byte aligned");
+    if ((st = check_eps(eps)) != LA_OK) return st;
+    if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
+    const int64_t BH = shape->B * shape->H;
+    if (BH > 0x7fffffff) return fail(LA_ERR_UNSUPPORTED, "B*H too large");
+    DecArgs a;
+    std::memset(&a, 0, sizeof(a));
+    if ((st = make_lam(lambda_h, shape->H, &a.lam)) != LA_OK) return st;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.S = S;
+    a.z = z;
+    a.BH = (int32_t)BH;
+    a.H = (int32_t)shape->H;
+    a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
+    a.eps = eps;
+    a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
+    a.omega = phi->omega;
+    hipError_t e = ent->dec(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// la_decode.h -- recurrent decode step (gfx950): one token per (batch, head),
+// the fp32 state read and written once.
+//
+// Per head-state ("From standard attention to linear attention",
+// tqpw.cn/news/561043, sec. 6 autoregressive step; decay from "Attention is
+// also an FFN", kwkr.cn/news/587576, sec. 3.2; normaliser sec. 4.2):
+//   S <- lambda S + phi(k) v^T,  z <- lambda z + phi(k),
+//   y  = phi(q)^T S / (phi(q)^T z + eps)          (update, then query)
+//
+// The step is bound by HBM: 8 bytes of state traffic per state element
+// against 4 flops.  One 256-thread workgroup streams one head-state: each
+// thread owns a 4-column quad of F/RG rows, issues all of its 16-byte loads
+// before the first use so that many bytes are in flight, updates them in
+// registers, writes them back and accumulates phi(q)^T S for its columns.
+// Partial sums over rows are reduced across lanes and then across waves
+// through LDS.
+#pragma once
+
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+template <class T, int PHI, int DK, int F, int DV>
+__global__ void __launch_bounds__(256)
+la_decode_kernel(const DecArgs a)
+{
+    constexpr int NT = 256;
+    constexpr bool RF = PHI == LA_PHI_TRIG_RF;
+    constexpr int M = RF ? F / 2 : 0;
+    constexpr int CQ = DV / 4;      // column quads
+    constexpr int RG = NT / CQ;     // row groups
+    constexpr int RPT = F / RG;     // rows per thread
+    static_assert(F <= NT && DV <= NT && F % RG == 0, "decode thread mapping");
+
+    __shared__ float sPq[F], sPk[F], sV[DV];
+    __shared__ float sX[RF ? 2 * DK : 1];
+    __shared__ f32x4 sRed[NT / 64][CQ];
+    __shared__ float sDen[NT / 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x, h = bh % a.H;
+    const float lam = a.lam.lam[h];
+    const T* q = (const T*)a.q + (int64_t)bh * DK;
+    const T* k = (const T*)a.k + (int64_t)bh * DK;
+    const T* v = (const T*)a.v + (int64_t)bh * DV;
+    float* Sb = a.S + (int64_t)bh * F * DV;
+    float* zb = a.z + (int64_t)bh * F;
+
+    const int cq = tid % CQ, rg = tid / CQ;
+    // issue the state loads first: they are the whole cost of the step
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = *(const f32x4*)(Sb + (rg + RG * i) * DV + 4 * cq);
+    float zf = (tid < F) ? zb[tid] : 0.f;
+
+    // feature maps of this token
+    if constexpr (RF) {
+        if (tid < DK) {
+            sX[tid] = to_f32(q[tid]);
+            sX[DK + tid] = to_f32(k[tid]);
+        }
+        if (tid < DV) sV[tid] = to_f32(v[tid]);
+        __syncthreads();
+        if (tid < 2 * M) {
+            const int which = tid / M, r = tid % M;
+            const float* x = sX + which * DK;
+            const float* om = a.omega + (int64_t)r * DK;
+            float u = 0.f, n2 = 0.f;
+            for (int d = 0; d < DK; ++d) {
+                u += om[d] * x[d];
+                n2 += x[d] * x[d];
+            }
+            const float qs = a.qk_scale;
+            const float c = exp_rf<T>(-0.5f * qs * qs * n2) * rsqrtf((float)M);
+            float sn, cs;
+            sincos_rf<T>(qs * u, &sn, &cs);
+            float* dst = which ? sPk : sPq;
+            dst[r] = c * cs;
+            dst[M + r] = c * sn;
+        }
+    } else {
+        if (tid < DK) {
+            sPq[tid] = phi_elu1<T>(to_f32(q[tid]));
+            sPk[tid] = phi_elu1<T>(to_f32(k[tid]));
+        }
+        if (tid < DV) sV[tid] = to_f32(v[tid]);
+    }
+    __syncthreads();
+
+    // S <- lambda S + phi(k) v^T ; partial phi(q)^T S
+    const f32x4 v4 = {sV[4 * cq], sV[4 * cq + 1], sV[4 * cq + 2], sV[4 * cq + 3]};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int f = rg + RG * i;
+        const f32x4 sn = lam * s[i] + sPk[f] * v4;
+        *(f32x4*)(Sb + f * DV + 4 * cq) = sn;
+        acc += sPq[f] * sn;
+    }
+    // z <- lambda z + phi(k) ; partial phi(q)^T z
+    float dz = 0.f;
+    if (tid < F) {
+        zf = lam * zf + sPk[tid];
+        zb[tid] = zf;
+        dz = sPq[tid] * zf;
+    }
+    // reduce over row groups: lanes of one wave first, then waves
+#pragma unroll
+    for (int m = CQ; m < 64; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
+    }
+    dz = wave_sum_xor(dz, 1, 32);
+    if (lane < CQ) sRed[wave][lane] = acc;
+    if (lane == 0) sDen[wave] = dz;
+    __syncthreads();
+    if (tid < CQ) {
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            num += sRed[w][tid];
+            den += sDen[w];
+        }
+        const float inv = 1.0f / (den + a.eps);
+        const int64_t yo = (int64_t)bh * DV + 4 * tid;
+        if (a.out_f32) {
+            *(f32x4*)((float*)a.y + yo) = num * inv;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ((T*)a.y)[yo + e] = from_f32<T>(num[e] * inv);
+        }
+    }
+}
+
+template <class T, int PHI, int DK, int F, int DV>
+hipError_t dec_launch(const DecArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((la_decode_kernel<T, PHI, DK, F, DV>), dim3((unsigned)a.BH), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

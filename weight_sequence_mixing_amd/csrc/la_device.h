@@ -1,0 +1,143 @@
+// la_device.h -- device helpers for the gfx950 kernels: element types, MFMA
+// fragments, feature maps and decay powers.
+//
+// Matrix-core fragments.  Every product in this library is built from the
+// 16x16 output tile of v_mfma_f32_16x16x32_bf16 (bf16 operands) or of eight
+// chained v_mfma_f32_16x16x4_f32 (fp32 operands).  In the 16x16 fp32
+// accumulator, lane l holds rows 4*(l/16)+r (r = 0..3) of column l%16.
+//
+// A contraction over a 32-wide block of the k index is fed as one "fragment"
+// per lane: 8 values for the lane's row (A operand) or column (B operand), at
+// the k positions
+//     K(g) = { 4g, 4g+1, 4g+2, 4g+3, 16+4g, 16+4g+1, 16+4g+2, 16+4g+3 },
+// g = l/16.  Both operands use the same K(g), so the product is the full
+// contraction whatever order the hardware assigns to the 8 slots.  K(g) is
+// exactly the set of rows a lane holds in two vertically adjacent accumulator
+// tiles, so an accumulator pair converts into the next product's operand with
+// no data movement between lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <class T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <class T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Four consecutive elements at p (p must be 4-element aligned).
+__device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *(const bf16x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+    bf16x4 t = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *(bf16x4*)p = t;
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+    f32x4 t = {a, b, c, d};
+    *(f32x4*)p = t;
+}
+
+// Fragment from two 4-element groups (k = 4g.. and k = 16+4g..).
+__device__ __forceinline__ Frag<bf16> frag2(const bf16* lo, const bf16* hi) {
+    Frag<bf16> f;
+    f.v = __builtin_shufflevector(ld4(lo), ld4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+}
+__device__ __forceinline__ Frag<float> frag2(const float* lo, const float* hi) {
+    Frag<float> f;
+    f.lo = ld4(lo);
+    f.hi = ld4(hi);
+    return f;
+}
+
+// Fragment of a row-major [rows][ld] buffer: row `row`, k block starting at k0.
+template <class T>
+__device__ __forceinline__ Frag<T> frag_rm(const T* base, int ld, int row, int k0, int g) {
+    const T* p = base + row * ld + k0 + 4 * g;
+    return frag2(p, p + 16);
+}
+
+// Fragment from two accumulator tiles (rows 0..15 then 16..31 of the k block).
+template <class T> __device__ __forceinline__ Frag<T> frag_acc(const f32x4& a, const f32x4& b);
+template <> __device__ __forceinline__ Frag<bf16> frag_acc<bf16>(const f32x4& a, const f32x4& b) {
+    Frag<bf16> f;
+    f.v = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                 (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_acc<float>(const f32x4& a, const f32x4& b) {
+    Frag<float> f;
+    f.lo = a;
+    f.hi = b;
+    return f;
+}
+
+// acc += A(16 x 32) * B(32 x 16) for one 32-wide k block.
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
+}
+
+// lambda^k from log2(lambda), with lambda^0 = 1 also for lambda = 0.
+__device__ __forceinline__ float lam_pow(float log2lam, int k) {
+    return k == 0 ? 1.0f : exp2f((float)k * log2lam);
+}
+
+// elu(x) + 1 ("From standard attention to linear attention" sec. 4.1).
+template <class T> __device__ __forceinline__ float phi_elu1(float x);
+template <> __device__ __forceinline__ float phi_elu1<bf16>(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+template <> __device__ __forceinline__ float phi_elu1<float>(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+template <class T> __device__ __forceinline__ void sincos_rf(float u, float* s, float* c);
+template <> __device__ __forceinline__ void sincos_rf<bf16>(float u, float* s, float* c) {
+    *s = __sinf(u);
+    *c = __cosf(u);
+}
+template <> __device__ __forceinline__ void sincos_rf<float>(float u, float* s, float* c) {
+    sincosf(u, s, c);
+}
+template <class T> __device__ __forceinline__ float exp_rf(float x);
+template <> __device__ __forceinline__ float exp_rf<bf16>(float x) { return __expf(x); }
+template <> __device__ __forceinline__ float exp_rf<float>(float x) { return expf(x); }
+
+// Unpack a 16-byte vector of VEC elements into floats (bit operations only,
+// so the vector never leaves registers).
+__device__ __forceinline__ void unpack16(const uint4& u, float* out, const bf16*) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        out[2 * e] = __uint_as_float(w[e] << 16);
+        out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack16(const uint4& u, float* out, const float*) {
+    out[0] = __uint_as_float(u.x);
+    out[1] = __uint_as_float(u.y);
+    out[2] = __uint_as_float(u.z);
+    out[3] = __uint_as_float(u.w);
+}
+
+__device__ __forceinline__ float wave_sum_xor(float v, int mask_lo, int mask_hi) {
+    for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+}  // namespace la

@@ -1,0 +1,115 @@
+// la_internal.h -- host/device interface between the C ABI (la_api.cpp) and
+// the HIP kernels.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/la.h"
+
+namespace la {
+
+// Per-head decay, passed by value in the kernel arguments so that a launch
+// never needs a host-to-device copy (and can be recorded into a graph).
+struct LamTable {
+    float lam[LA_MAX_HEADS];
+    float log2lam[LA_MAX_HEADS];  // log2(lambda); -inf for lambda == 0
+};
+
+enum FwdMode : int {
+    MODE_LOCAL = 0,   // segment-local state  sum_j lambda^(L-1-j) phi(k_j) [v_j, 1]^T
+    MODE_CAUSAL = 1,  // chunked causal output with a carried state
+    MODE_QUERY = 2,   // non-causal output phi(Q) S / (phi(Q) z + eps) for a fixed state
+};
+
+// One launch of the forward kernel covers tokens [n0, n0 + n_len) of every
+// (batch, head) row, cut into P segments of whole chunks (blockIdx.x = segment,
+// blockIdx.y = batch*head).
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* y;
+    int64_t N;        // full sequence length (token stride of q, k, v, y)
+    int64_t n0;       // first token of this launch
+    int64_t n_len;    // tokens in this launch
+    int32_t BH;       // batch * heads
+    int32_t H;
+    int32_t P;        // segments
+    int32_t out_f32;  // 1: y is fp32, 0: y has the input type
+    float eps;
+    float qk_scale;
+    const float* omega;  // [m, d_k] fp32 (random features) or null
+    // initial state (MODE_CAUSAL, MODE_QUERY): S at
+    // S_src + seg*src_seg_stride + bh*src_stride as [F][d_v], z at
+    // z_src + seg*src_seg_stride + bh*src_zstride as [F]; null S_src = zero state.
+    const float* S_src;
+    const float* z_src;
+    int64_t src_stride;
+    int64_t src_zstride;
+    int64_t src_seg_stride;
+    // final state (MODE_CAUSAL, optional) or segment-local state (MODE_LOCAL):
+    // written at S_dst + (seg*BH + bh)*dst_stride (MODE_LOCAL) or
+    // S_dst + bh*dst_stride (MODE_CAUSAL), z likewise.
+    float* S_dst;
+    float* z_dst;
+    int64_t dst_stride;
+    int64_t dst_zstride;
+    LamTable lam;
+};
+
+struct ScanArgs {
+    float* ws;               // slots [P][BH][F*d_v + F]
+    int32_t P, BH, H, F, DV;
+    int64_t n_len;           // tokens covered by the P segments
+    int32_t C;               // chunk size used to cut segments
+    int32_t causal;          // 1: exclusive decayed scan; 0: plain sum into slot 0
+    const float* S_init;     // initial state (causal), user layout or carry slot
+    const float* z_init;
+    int64_t init_stride, init_zstride;
+    float* S_fin;            // final state (causal) or null
+    float* z_fin;
+    int64_t fin_stride, fin_zstride;
+    LamTable lam;
+};
+
+struct DecArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* y;
+    float* S;
+    float* z;
+    int32_t BH, H;
+    int32_t out_f32;
+    float eps;
+    float qk_scale;
+    const float* omega;
+    LamTable lam;
+};
+
+typedef hipError_t (*fwd_launch_fn)(const FwdArgs&, int mode, hipStream_t);
+typedef hipError_t (*dec_launch_fn)(const DecArgs&, hipStream_t);
+
+struct KernelEntry {
+    int in_dtype;   // LA_F32 / LA_BF16
+    int phi;        // LA_PHI_*
+    int dk, F, dv;
+    int C;          // chunk length used by the forward kernels
+    fwd_launch_fn fwd;
+    dec_launch_fn dec;
+};
+
+// Tables defined by the instantiation units.
+extern KernelEntry kEntriesBf16Elu[];
+extern int kNumEntriesBf16Elu;
+extern KernelEntry kEntriesBf16Rf[];
+extern int kNumEntriesBf16Rf;
+extern KernelEntry kEntriesF32[];
+extern int kNumEntriesF32;
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+}  // namespace la

@@ -1,0 +1,90 @@
+// la_scan.hip -- combination of per-segment states, and small fill/copy
+// kernels.
+//
+// A sequence cut into P segments of lengths L_0..L_{P-1} has segment-local
+// states S_loc(s) = sum over the segment of lambda^(L_s-1-j) phi(k_j)[v_j,1]^T.
+// The state entering segment s is the decayed prefix
+//   S_in(0) = S_init,  S_in(s) = lambda^(L_{s-1}) S_in(s-1) + S_loc(s-1),
+// the same carry the chunked method applies between chunks ("Attention is
+// also an FFN", kwkr.cn/news/587576, sec. 5.2: parallel inside a block,
+// carried between blocks), applied once more between segments.  Each thread
+// owns one element of the [F x (d_v + 1)] state of one (batch, head) row and
+// walks the P segments in order, in place.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+__global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
+{
+    const int SZ = a.F * a.DV + a.F;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= SZ) return;
+    const bool isz = e >= a.F * a.DV;
+    const int ez = e - a.F * a.DV;
+    float* base = a.ws + (int64_t)bh * SZ + e;
+    const int64_t slot = (int64_t)a.BH * SZ;
+    if (!a.causal) {
+        float acc = 0.f;
+        for (int s = 0; s < a.P; ++s) acc += base[s * slot];
+        base[0] = acc;
+        return;
+    }
+    const float l2l = a.lam.log2lam[bh % a.H];
+    float carry = 0.f;
+    if (a.S_init) carry = isz ? a.z_init[bh * a.init_zstride + ez] : a.S_init[bh * a.init_stride + e];
+    const int64_t NC = (a.n_len + a.C - 1) / a.C;
+    for (int s = 0; s < a.P; ++s) {
+        const int64_t c0 = (int64_t)s * NC / a.P, c1 = (int64_t)(s + 1) * NC / a.P;
+        const int64_t L = min(c1 * a.C, a.n_len) - c0 * a.C;
+        const float loc = base[s * slot];
+        base[s * slot] = carry;
+        carry = lam_pow(l2l, (int)L) * carry + loc;
+    }
+    if (a.S_fin) {
+        if (isz) a.z_fin[bh * a.fin_zstride + ez] = carry;
+        else a.S_fin[bh * a.fin_stride + e] = carry;
+    }
+}
+
+__global__ void __launch_bounds__(256) la_fill_zero_kernel(float* p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+__global__ void __launch_bounds__(256) la_copy_kernel(float* dst, const float* src, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream)
+{
+    const int SZ = a.F * a.DV + a.F;
+    hipLaunchKernelGGL(la_scan_kernel, dim3((SZ + 255) / 256, a.BH), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+static unsigned grid_for(int64_t n)
+{
+    int64_t b = (n + 255) / 256;
+    if (b > 4096) b = 4096;
+    if (b < 1) b = 1;
+    return (unsigned)b;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(la_fill_zero_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream)
+{
+    if (n <= 0 || dst == src) return hipSuccess;
+    hipLaunchKernelGGL(la_copy_kernel, dim3(grid_for(n)), dim3(256), 0, stream, dst, src, n);
+    return hipGetLastError();
+}
+
+}  // namespace la
