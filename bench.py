@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal kernelized linear attention hot path on one MI355X.
+
+One step = one la_forward_causal call over the whole batch of the headline
+workload (elu+1, B=4, H=8, N=4096, d_k=d_v=64, bf16 inputs, fp32 state): the
+segment-state pass, the segment scan and the chunked output pass.  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Printed: ONE JSON line with the throughput (Mtokens/s, tokens = B*N), the
+roofline of the dominant kernel (algorithmic bytes per launch over its mean
+device time, from HIP events the library records around each of its launches
+on the launch stream), the secondary workloads (decode step on 256x32 state,
+long causal forwards with per-head decay and with random features) each with
+its own roofline, and the fp64 CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+                       [--no-cpu-baseline] [--only NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["la_forward.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "weight_sequence_mixing_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """Counter-measured HBM bytes per launch, if taken on the current kernels."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("per_launch_bytes", {}).get("%s/%s" % (workload, kernel))
+
+
+class Ctx:
+    def __init__(self, steps, warmup):
+        import torch
+        import weight_sequence_mixing_amd as la
+        self.torch, self.la = torch, la
+        self.dev = torch.device("cuda:0")
+        self.steps, self.warmup = steps, warmup
+
+    def time_steps(self, fn, steps=None, warmup=None):
+        torch = self.torch
+        steps = self.steps if steps is None else steps
+        warmup = self.warmup if warmup is None else warmup
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def kernel_times(self, fn, steps=None, launches_per_step=8):
+        """Mean device ms per launch, by kernel id, from the library's event brackets."""
+        la = self.la
+        steps = self.steps if steps is None else steps
+        self.torch.cuda.synchronize()
+        la.la_profile_begin(steps * launches_per_step)
+        for _ in range(steps):
+            fn()
+        rec = la.la_profile_end(steps * launches_per_step)
+        out = {}
+        for kid, ms in rec:
+            out.setdefault(kid, []).append(ms)
+        return {kid: (float(np.mean(v)), len(v) // steps) for kid, v in out.items()}
+
+
+def roofline(achieved_gbs, traffic):
+    return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def causal_bytes(B, H, N, dk, dv, in_bytes, out_bytes):
+    """Algorithmic bytes of the causal forward: q, k, v read once, y written once."""
+    return B * H * N * ((2 * dk + dv) * in_bytes + dv * out_bytes)
+
+
+def kernel_alg_bytes(kid, la, B, H, N, dk, dv, F, P, in_bytes=2, out_bytes=2):
+    ids = la.KERNEL_IDS
+    rows = B * H * N
+    SZ = F * dv + F
+    if kid == ids["fwd_causal"]:
+        return rows * ((2 * dk + dv) * in_bytes + dv * out_bytes)
+    if kid == ids["fwd_local"]:
+        return rows * (dk + dv) * in_bytes + P * B * H * SZ * 4
+    if kid == ids["fwd_query"]:
+        return rows * (dk * in_bytes + dv * out_bytes)
+    if kid == ids["scan"]:
+        return 2 * P * B * H * SZ * 4
+    return None
+
+
+def bench_causal(ctx, name, B, H, N, dk, dv, lam, phi, gen, steps=None, planned_P=None):
+    """Time one causal workload; returns a result dict."""
+    torch, la = ctx.torch, ctx.la
+    q, k, v = gen
+    y = torch.empty(B, H, N, dv, dtype=torch.bfloat16, device=ctx.dev)
+    F = phi.F(dk)
+    ws_n = la.la_workspace_size(B, H, N, dk, dv, phi=phi)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=ctx.dev)
+    lam_l = list(map(float, lam))
+
+    def step():
+        la.la_forward_causal(q, k, v, y, phi=phi, lambda_h=lam_l, eps=1e-6, workspace=ws)
+
+    ms = ctx.time_steps(step, steps=steps)
+    kt = ctx.kernel_times(step, steps=steps)
+    tokens = B * N
+    P = planned_P if planned_P is not None else max(1, -(-512 // (B * H)))
+    # dominant kernel by total device time per step
+    dom = max(kt.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
+    dom_ms = kt[dom][0]
+    # segments actually used: infer from the workspace (states of P segments)
+    if ws_n:
+        P = max(1, int(round(ws_n / (B * H * (F * dv + F) * 4))))
+    alg = kernel_alg_bytes(dom, la, B, H, N, dk, dv, F, P)
+    achieved = alg / (dom_ms * 1e-3) / 1e9
+    step_bytes = causal_bytes(B, H, N, dk, dv, 2, 2)
+    flops_min = 4.0 * F * dv * B * H * N
+    res = {
+        "workload": name, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 2),
+        "head_tokens_per_s": round(B * H * N / (ms * 1e-3), 1),
+        "step_alg_bytes": step_bytes, "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "recurrent_TFLOPs": round(flops_min / (ms * 1e-3) / 1e12, 2),
+        "recurrent_mfma_frac": round(flops_min / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "segments": P,
+        "kernels": {la.la_kernel_name(kid): {"mean_ms": round(t, 4), "launches_per_step": n}
+                    for kid, (t, n) in kt.items()},
+        "dominant_kernel": la.la_kernel_name(dom),
+        "roofline": roofline(achieved, load_traffic(name, la.la_kernel_name(dom))),
+        "roofline_alg_bytes_per_launch": alg,
+        "dominant_mean_ms": round(dom_ms, 4),
+    }
+    return res
+
+
+def device_normal(torch, gen, shape, scale, dev):
+    return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * scale).to(torch.bfloat16)
+
+
+def workload2(ctx):
+    import seeded_inputs as si
+    torch = ctx.torch
+    wl = si.workload(2)
+    inp = si.make_inputs(wl)
+
+    def t(name):
+        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(ctx.dev)
+
+    gen = (t("q"), t("k"), t("v"))
+    res = bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, inp["lam"], ctx.la.Phi(), gen)
+    return wl, inp, res
+
+
+def workload3(ctx):
+    import seeded_inputs as si
+    torch = ctx.torch
+    wl = si.workload(3)
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(3)
+    shape = (wl.B, wl.H, wl.N, wl.dk)
+    gen = tuple(device_normal(torch, g, shape, wl.scale, ctx.dev) for _ in range(3))
+    lam = si.make_lambda(wl)
+    return bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, lam, ctx.la.Phi(), gen,
+                        steps=max(3, ctx.steps // 2))
+
+
+def workload5(ctx):
+    import seeded_inputs as si
+    torch = ctx.torch
+    wl = si.workload(5)
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(5)
+    shape = (wl.B, wl.H, wl.N, wl.dk)
+    gen = tuple(device_normal(torch, g, shape, wl.scale, ctx.dev) for _ in range(3))
+    omega = torch.from_numpy(si.make_omega(wl.m, wl.dk, wl.index)).to(ctx.dev)
+    phi = ctx.la.Phi("trig_rf", omega, wl.qk_scale)
+    return bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, si.make_lambda(wl), phi, gen,
+                        steps=max(3, ctx.steps // 2))
+
+
+def workload4_decode(ctx, steps=1024):
+    """Decode: prefix of 512 tokens through the causal forward, then `steps`
+    single-token steps timed back to back.  Bytes per step: state read and
+    written once, plus q, k, v, y."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    wl = si.workload(4)
+    B, H, d = wl.B, wl.H, wl.dk
+    F = wl.F
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(4)
+    lam = list(map(float, si.make_lambda(wl)))
+    pq, pk, pv = (device_normal(torch, g, (B, H, wl.N, d), wl.scale, ctx.dev) for _ in range(3))
+    S = torch.empty(B, H, F, d, dtype=torch.float32, device=ctx.dev)
+    z = torch.empty(B, H, F, dtype=torch.float32, device=ctx.dev)
+    yp = torch.empty_like(pq)
+    la.la_forward_causal(pq, pk, pv, yp, lambda_h=lam, eps=wl.eps, S_out=S, z_out=z)
+    del pq, pk, pv, yp
+    sq, sk, sv = (device_normal(torch, g, (steps, B, H, 1, d), wl.scale, ctx.dev) for _ in range(3))
+    y = torch.empty(B, H, 1, d, dtype=torch.bfloat16, device=ctx.dev)
+    counter = [0]
+
+    def step():
+        i = counter[0] % steps
+        counter[0] += 1
+        la.la_decode_step(sq[i], sk[i], sv[i], y, S, z, lambda_h=lam, eps=wl.eps)
+
+    ms = ctx.time_steps(step, steps=steps, warmup=8)
+    kt = ctx.kernel_times(step, steps=min(steps, 256), launches_per_step=1)
+    dec_ms = kt[la.KERNEL_IDS["decode"]][0]
+    state_bytes = 2 * B * H * (F * d + F) * 4
+    io_bytes = B * H * (3 * d * 2 + d * 2)
+    per_step = state_bytes + io_bytes
+    achieved = per_step / (dec_ms * 1e-3) / 1e9
+    return {
+        "workload": wl.name, "ms_per_step": round(ms, 4), "steps_timed": steps,
+        "state_GBps": round(per_step / (ms * 1e-3) / 1e9, 1),
+        "Mtokens_per_s": round(B / (ms * 1e-3) / 1e6, 4),
+        "head_tokens_per_s": round(B * H / (ms * 1e-3), 1),
+        "alg_bytes_per_step": per_step,
+        "kernels": {la.la_kernel_name(k): {"mean_ms": round(t, 4), "launches_per_step": n} for k, (t, n) in kt.items()},
+        "dominant_kernel": la.la_kernel_name(la.KERNEL_IDS["decode"]),
+        "roofline": roofline(achieved, load_traffic(wl.name, la.la_kernel_name(la.KERNEL_IDS["decode"]))),
+        "dominant_mean_ms": round(dec_ms, 4),
+    }
+
+
+def cpu_baseline(wl, inp):
+    """The fp64 oracle, as it stands, on the host: the whole headline workload."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.causal(inp["q"], inp["k"], inp["v"], inp["lam"], wl.eps, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(wl.B * wl.N / dt / 1e6, 5), "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload (B=%d H=%d N=%d d=%d, fp64 recurrence) in %.2f s" % (wl.B, wl.H, wl.N, wl.dk, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w5"], help="run one workload (profiling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path "
+            "(each GPU would run its own heads; see the sharding notes in DESIGN.md).")
+        sys.exit(2)
+
+    ctx = Ctx(args.steps, args.warmup)
+    import seeded_inputs as si
+    if args.only and args.only != "w2":
+        fn = {"w3": workload3, "w4": workload4_decode, "w5": workload5}[args.only]
+        log("running", args.only)
+        print(json.dumps({"only": args.only, "result": fn(ctx)}), flush=True)
+        return
+
+    log("workload 2 (headline) ...")
+    wl, inp, res = workload2(ctx)
+    log(json.dumps(res))
+    extra = {}
+    if not args.no_extra:
+        for key, fn in (("decode_w4", workload4_decode), ("causal_w3", workload3), ("causal_w5", workload5)):
+            log(key, "...")
+            extra[key] = fn(ctx)
+            log(json.dumps(extra[key]))
+            ctx.torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl, inp)
+    line = {
+        "metric": "causal linear-attn fwd Mtokens/s + MFMA util; decode-step state GB/s vs HBM",
+        "value": res["Mtokens_per_s"],
+        "unit": "Mtokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5, rounded to bf16)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,
+                   "phi": wl.phi, "lambda": 1.0, "eps": wl.eps, "state": "fp32", "segments": res["segments"]},
+        "roofline": res["roofline"],
+        "dominant_kernel": res["dominant_kernel"],
+        "kernels": res["kernels"],
+        "step_hbm_frac": res["step_hbm_frac"],
+        "recurrent_mfma_frac": res["recurrent_mfma_frac"],
+        "cpu_baseline": cpu,
+        "secondary": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -141,6 +141,30 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y,
                          float* S, float* z, const la_shape* shape, const la_phi* phi,
                          const float* lambda_h, float eps, la_stream_t stream);
 
+/* Measurement hooks (for benchmarks; not needed to compute anything).
+ * Between la_profile_begin() and la_profile_end(), every kernel this library
+ * launches from the calling thread is bracketed by two HIP events recorded on
+ * the launch's own stream, so each launch's device time can be read back.
+ * la_profile_begin creates 2*max_launches events (host-side runtime objects;
+ * no device memory); launches beyond max_launches are not recorded.
+ * la_profile_end waits for the last recorded event, writes up to `capacity`
+ * (kernel id, milliseconds) pairs in launch order, sets *count to the number
+ * recorded, destroys the events and turns recording off.  Calling
+ * la_profile_begin twice without la_profile_end is LA_ERR_INVALID_ARGUMENT. */
+enum {
+    LA_KERNEL_FWD_LOCAL = 0,   /* segment-local state pass of a forward        */
+    LA_KERNEL_FWD_CAUSAL = 1,  /* chunked causal output pass                   */
+    LA_KERNEL_FWD_QUERY = 2,   /* non-causal output pass                       */
+    LA_KERNEL_SCAN = 3,        /* segment state scan / reduction               */
+    LA_KERNEL_DECODE = 4,      /* recurrent decode step                        */
+    LA_KERNEL_FILL = 5,        /* zero fill (la_init_state, empty forward)     */
+    LA_KERNEL_COPY = 6         /* state copy (empty forward)                   */
+};
+la_status la_profile_begin(int32_t max_launches);
+la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);
+/* Name of a kernel id: the prefix of the device function's symbol. */
+const char* la_kernel_name(int32_t kernel_id);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status status);
 

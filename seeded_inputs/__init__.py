@@ -195,7 +195,7 @@ def make_omega(m: int, dk: int, seed: int) -> np.ndarray:
         norms = np.linalg.norm(rng.standard_normal((dk, dk)), axis=1)
         blocks.append(rows * norms[:, None])
         remaining -= dk
-    return np.concatenate(blocks, axis=0)[:m].astype(np.float32)
+    return np.ascontiguousarray(np.concatenate(blocks, axis=0)[:m], dtype=np.float32)
 
 
 def make_inputs(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None):

@@ -1,5 +1,8 @@
 """Helpers for the GPU parity tests: seeded inputs to device tensors, calls
 through the C ABI binding, and the oracle comparison metric."""
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -23,7 +26,7 @@ def tdtype(dtype):
 
 def phi_for(wl, omega_np):
     if wl.phi == "trig_rf":
-        return la.Phi("trig_rf", torch.from_numpy(omega_np).to(DEV), wl.qk_scale)
+        return la.Phi("trig_rf", torch.from_numpy(np.ascontiguousarray(omega_np)).to(DEV), wl.qk_scale)
     return la.Phi()
 
 
@@ -59,7 +62,19 @@ def oracle_causal(wl, inp, lam=None, heads=None, **kw):
 
 def rel_err(y_gpu, y_ref):
     y = y_gpu.float().cpu().numpy() if isinstance(y_gpu, torch.Tensor) else y_gpu
-    return oracle.rowwise_rel_err(y, y_ref)
+    err = oracle.rowwise_rel_err(y, y_ref)
+    _record(err)
+    return err
+
+
+def _record(err):
+    """Append the error to $LA_PARITY_LOG (one JSON line per comparison)."""
+    path = os.environ.get("LA_PARITY_LOG")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    with open(path, "a") as fh:
+        fh.write(json.dumps({"test": test, "max_row_rel_err": err}) + "\n")
 
 
 def inputs(index, **over):

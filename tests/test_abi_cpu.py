@@ -25,6 +25,16 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:la_status|size_t|const char\*)\s+(la_\w+)\s*\(", text, re.M)))
 
 
+def test_profile_hooks_host_side(lib):
+    # ending without a begin is rejected on the host (creating events needs a GPU)
+    with pytest.raises(la.LaError):
+        la.la_profile_end()
+    with pytest.raises(la.LaError):
+        la.la_profile_begin(0)
+    assert la.la_kernel_name(1).startswith("la_fwd_kernel")
+    assert la.la_kernel_name(4) == "la_decode_kernel"
+
+
 def test_header_declarations_are_exported(lib):
     names = _declared()
     assert set(names) == set(la.EXPORTS), names

@@ -216,6 +216,18 @@ def test_decode_full_size_sampled():
         assert rel_err(y[b:b + 1, h:h + 1], ref[:, :, wl.N:]) < TOL["bf16"], (b, h)
 
 
+def test_profile_hooks_record_launches():
+    wl, inp = inputs(2, B=1, H=2, N=4096)
+    la.la_profile_begin(8)
+    with pytest.raises(la.LaError):
+        la.la_profile_begin(8)
+    run_causal(wl, inp)
+    rec = la.la_profile_end()
+    ids = [k for k, _ in rec]
+    assert ids == [la.KERNEL_IDS["fwd_local"], la.KERNEL_IDS["scan"], la.KERNEL_IDS["fwd_causal"]], rec
+    assert all(ms > 0 for _, ms in rec)
+
+
 def test_init_state_zeroes():
     S = torch.full((2, 3, 64, 128), 7.0, device=DEV)
     z = torch.full((2, 3, 64), 7.0, device=DEV)

@@ -24,7 +24,9 @@ LA_MAX_HEADS = 256
 
 # names declared in include/la.h
 EXPORTS = ("la_init_state", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
-           "la_decode_step", "la_status_string", "la_last_error")
+           "la_decode_step", "la_status_string", "la_last_error", "la_profile_begin", "la_profile_end",
+           "la_kernel_name")
+KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6}
 
 
 class LaPhiC(ctypes.Structure):
@@ -78,6 +80,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_last_error.argtypes = []
     lib.la_last_error.restype = ctypes.c_char_p
+    lib.la_profile_begin.argtypes = [i32]
+    lib.la_profile_begin.restype = ctypes.c_int
+    lib.la_profile_end.argtypes = [vp, vp, i32, vp]
+    lib.la_profile_end.restype = ctypes.c_int
+    lib.la_kernel_name.argtypes = [i32]
+    lib.la_kernel_name.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -154,6 +162,27 @@ def la_status_string(status: int) -> str:
 
 def la_last_error() -> str:
     return load_library().la_last_error().decode()
+
+
+def la_profile_begin(max_launches: int) -> None:
+    """Start bracketing every library launch on this thread with HIP events."""
+    load_library()
+    _check(_lib.la_profile_begin(int(max_launches)))
+
+
+def la_profile_end(capacity: int = 100000):
+    """Stop recording; returns a list of (kernel_id, milliseconds) in launch order."""
+    load_library()
+    ids = (ctypes.c_int32 * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    n = ctypes.c_int32(0)
+    _check(_lib.la_profile_end(ctypes.cast(ids, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p),
+                               capacity, ctypes.cast(ctypes.pointer(n), ctypes.c_void_p)))
+    return [(int(ids[i]), float(ms[i])) for i in range(n.value)]
+
+
+def la_kernel_name(kernel_id: int) -> str:
+    return load_library().la_kernel_name(int(kernel_id)).decode()
 
 
 def la_init_state(S: torch.Tensor, z: torch.Tensor, stream=None) -> None:

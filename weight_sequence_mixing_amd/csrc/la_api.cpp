@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "la_internal.h"
 
@@ -39,6 +40,40 @@ la_status ok()
 la_status hip_fail(hipError_t e, const char* what)
 {
     return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- per-launch event brackets for la_profile_begin / la_profile_end
+struct Profiler {
+    bool on = false;
+    int max = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;  // 2 per launch
+    std::vector<int> ids;
+};
+thread_local Profiler g_prof;
+
+void prof_before(int id, hipStream_t s)
+{
+    if (!g_prof.on || g_prof.used >= g_prof.max) return;
+    hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+    g_prof.ids[g_prof.used] = id;
+}
+
+void prof_after(hipStream_t s)
+{
+    if (!g_prof.on || g_prof.used >= g_prof.max) return;
+    hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+    ++g_prof.used;
+}
+
+// Launch through `fn` bracketed by profiling events when recording is on.
+template <class Fn>
+hipError_t launch(int id, hipStream_t s, Fn&& fn)
+{
+    prof_before(id, s);
+    const hipError_t e = fn();
+    prof_after(s);
+    return e;
 }
 
 const KernelEntry* find_entry(int in_dtype, int phi, int dk, int F, int dv)
@@ -233,14 +268,77 @@ const char* la_last_error(void)
     return g_last_error.c_str();
 }
 
+la_status la_profile_begin(int32_t max_launches)
+{
+    if (g_prof.on) return fail(LA_ERR_INVALID_ARGUMENT, "profiling already on");
+    if (max_launches < 1) return fail(LA_ERR_INVALID_ARGUMENT, "max_launches must be >= 1");
+    g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+    g_prof.ids.assign((size_t)max_launches, -1);
+    for (size_t i = 0; i < g_prof.ev.size(); ++i) {
+        const hipError_t e = hipEventCreate(&g_prof.ev[i]);
+        if (e != hipSuccess) {
+            for (size_t j = 0; j < i; ++j) hipEventDestroy(g_prof.ev[j]);
+            g_prof.ev.clear();
+            return hip_fail(e, "hipEventCreate");
+        }
+    }
+    g_prof.max = max_launches;
+    g_prof.used = 0;
+    g_prof.on = true;
+    return ok();
+}
+
+la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count)
+{
+    if (!g_prof.on) return fail(LA_ERR_INVALID_ARGUMENT, "profiling is not on");
+    la_status st = LA_OK;
+    int n = 0;
+    if (g_prof.used > 0) {
+        const hipError_t e = hipEventSynchronize(g_prof.ev[2 * g_prof.used - 1]);
+        if (e != hipSuccess) st = hip_fail(e, "hipEventSynchronize");
+    }
+    for (int i = 0; st == LA_OK && i < g_prof.used && i < capacity; ++i) {
+        float t = 0.f;
+        const hipError_t e = hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (e != hipSuccess) {
+            st = hip_fail(e, "hipEventElapsedTime");
+            break;
+        }
+        if (kernel_ids) kernel_ids[i] = g_prof.ids[i];
+        if (ms) ms[i] = t;
+        n = i + 1;
+    }
+    if (count) *count = n;
+    for (hipEvent_t ev : g_prof.ev) hipEventDestroy(ev);
+    g_prof.ev.clear();
+    g_prof.ids.clear();
+    g_prof.on = false;
+    g_prof.used = 0;
+    return st;
+}
+
+const char* la_kernel_name(int32_t id)
+{
+    switch (id) {
+    case LA_KERNEL_FWD_LOCAL: return "la_fwd_kernel (segment state)";
+    case LA_KERNEL_FWD_CAUSAL: return "la_fwd_kernel (causal output)";
+    case LA_KERNEL_FWD_QUERY: return "la_fwd_kernel (non-causal output)";
+    case LA_KERNEL_SCAN: return "la_scan_kernel";
+    case LA_KERNEL_DECODE: return "la_decode_kernel";
+    case LA_KERNEL_FILL: return "la_fill_zero_kernel";
+    case LA_KERNEL_COPY: return "la_copy_kernel";
+    }
+    return "unknown";
+}
+
 la_status la_init_state(float* S, float* z, int64_t B, int64_t H, int32_t F, int32_t d_v, la_stream_t stream)
 {
     if (B < 1 || H < 1 || F < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARGUMENT, "B, H, F, d_v must be >= 1");
     if ((S && !aligned16(S)) || (z && !aligned16(z))) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be 16-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    if (S) e = launch_fill_zero(S, B * H * (int64_t)F * d_v, st);
-    if (e == hipSuccess && z) e = launch_fill_zero(z, B * H * (int64_t)F, st);
+    if (S) e = launch(LA_KERNEL_FILL, st, [&] { return launch_fill_zero(S, B * H * (int64_t)F * d_v, st); });
+    if (e == hipSuccess && z) e = launch(LA_KERNEL_FILL, st, [&] { return launch_fill_zero(z, B * H * (int64_t)F, st); });
     if (e != hipSuccess) return hip_fail(e, "la_init_state launch");
     return ok();
 }
@@ -281,11 +379,11 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
         hipError_t e = hipSuccess;
         if (S_out) {
             if (S_in) {
-                e = launch_copy(S_out, S_in, nS, strm);
-                if (e == hipSuccess) e = launch_copy(z_out, z_in, nz, strm);
+                e = launch(LA_KERNEL_COPY, strm, [&] { return launch_copy(S_out, S_in, nS, strm); });
+                if (e == hipSuccess) e = launch(LA_KERNEL_COPY, strm, [&] { return launch_copy(z_out, z_in, nz, strm); });
             } else {
-                e = launch_fill_zero(S_out, nS, strm);
-                if (e == hipSuccess) e = launch_fill_zero(z_out, nz, strm);
+                e = launch(LA_KERNEL_FILL, strm, [&] { return launch_fill_zero(S_out, nS, strm); });
+                if (e == hipSuccess) e = launch(LA_KERNEL_FILL, strm, [&] { return launch_fill_zero(z_out, nz, strm); });
             }
         }
         if (e != hipSuccess) return hip_fail(e, "la_forward_causal (N=0)");
@@ -347,7 +445,8 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             l.z_dst = segs + (int64_t)F * shape->d_v;
             l.dst_stride = plan.SZ;
             l.dst_zstride = plan.SZ;
-            if ((e = ent->fwd(l, MODE_LOCAL, strm)) != hipSuccess) return hip_fail(e, "segment state launch");
+            if ((e = launch(LA_KERNEL_FWD_LOCAL, strm, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
+                return hip_fail(e, "segment state launch");
             // pass 2: decayed exclusive scan over segments
             ScanArgs sa;
             std::memset(&sa, 0, sizeof(sa));
@@ -363,7 +462,8 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
             sa.lam = lam;
-            if ((e = launch_scan(sa, strm)) != hipSuccess) return hip_fail(e, "segment scan launch");
+            if ((e = launch(LA_KERNEL_SCAN, strm, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+                return hip_fail(e, "segment scan launch");
             // pass 3: outputs from the carried-in state of each segment
             FwdArgs c = a;
             c.S_src = segs;
@@ -371,13 +471,15 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             c.src_stride = plan.SZ;
             c.src_zstride = plan.SZ;
             c.src_seg_stride = BH * plan.SZ;
-            if ((e = ent->fwd(c, MODE_CAUSAL, strm)) != hipSuccess) return hip_fail(e, "causal output launch");
+            if ((e = launch(LA_KERNEL_FWD_CAUSAL, strm, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
+                return hip_fail(e, "causal output launch");
         } else {
             FwdArgs c = a;
             c.S_src = Si; c.z_src = zi; c.src_stride = si_stride; c.src_zstride = zi_stride;
             c.src_seg_stride = 0;
             c.S_dst = So; c.z_dst = zo; c.dst_stride = so_stride; c.dst_zstride = zo_stride;
-            if ((e = ent->fwd(c, MODE_CAUSAL, strm)) != hipSuccess) return hip_fail(e, "causal launch");
+            if ((e = launch(LA_KERNEL_FWD_CAUSAL, strm, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
+                return hip_fail(e, "causal launch");
         }
     }
     return ok();
@@ -423,7 +525,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     l.z_dst = ws + (int64_t)F * shape->d_v;
     l.dst_stride = plan.SZ;
     l.dst_zstride = plan.SZ;
-    if ((e = ent->fwd(l, MODE_LOCAL, strm)) != hipSuccess) return hip_fail(e, "state sum launch");
+    if ((e = launch(LA_KERNEL_FWD_LOCAL, strm, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
+        return hip_fail(e, "state sum launch");
     if (plan.P > 1) {
         ScanArgs sa;
         std::memset(&sa, 0, sizeof(sa));
@@ -436,7 +539,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
         sa.n_len = shape->N;
         sa.C = plan.C;
         sa.causal = 0;
-        if ((e = launch_scan(sa, strm)) != hipSuccess) return hip_fail(e, "state reduction launch");
+        if ((e = launch(LA_KERNEL_SCAN, strm, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+            return hip_fail(e, "state reduction launch");
     }
     FwdArgs qa = a;
     qa.S_src = ws;
@@ -444,7 +548,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     qa.src_stride = plan.SZ;
     qa.src_zstride = plan.SZ;
     qa.src_seg_stride = 0;
-    if ((e = ent->fwd(qa, MODE_QUERY, strm)) != hipSuccess) return hip_fail(e, "query launch");
+    if ((e = launch(LA_KERNEL_FWD_QUERY, strm, [&] { return ent->fwd(qa, MODE_QUERY, strm); })) != hipSuccess)
+        return hip_fail(e, "query launch");
     return ok();
 }
 
@@ -476,7 +581,8 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     a.eps = eps;
     a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
     a.omega = phi->omega;
-    hipError_t e = ent->dec(a, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch(LA_KERNEL_DECODE, strm, [&] { return ent->dec(a, strm); });
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
 }
