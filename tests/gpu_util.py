@@ -67,6 +67,14 @@ def rel_err(y_gpu, y_ref):
     return err
 
 
+def row_errors(y_gpu, y_ref):
+    """Per-row errors max_c |y - y_ref| / max_c |y_ref|, shape [B,H,N]."""
+    y = y_gpu.float().cpu().numpy() if isinstance(y_gpu, torch.Tensor) else np.asarray(y_gpu)
+    num = np.max(np.abs(y - y_ref), axis=-1)
+    den = np.max(np.abs(y_ref), axis=-1)
+    return num / np.where(den == 0, 1.0, den)
+
+
 def _record(err):
     """Append the error to $LA_PARITY_LOG (one JSON line per comparison)."""
     path = os.environ.get("LA_PARITY_LOG")
