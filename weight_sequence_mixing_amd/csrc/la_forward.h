@@ -85,7 +85,11 @@ struct FwdCfg {
     static constexpr size_t SZ_XK = (RF && NEED_K) ? size_t(C) * XLD * sizeof(T) : 0;
     static constexpr size_t OFF_XN = al(OFF_XK + SZ_XK);
     static constexpr size_t SZ_XN = RF ? size_t(2) * C * sizeof(float) : 0;
-    static constexpr size_t OFF_OM = al(OFF_XN + SZ_XN);
+    // partial sums over token groups of the weighted key features (for z)
+    static constexpr int ZR = NW > QB ? NW : QB;
+    static constexpr size_t OFF_ZP = al(OFF_XN + SZ_XN);
+    static constexpr size_t SZ_ZP = NEED_K ? size_t(ZR) * F * sizeof(float) : 0;
+    static constexpr size_t OFF_OM = al(OFF_ZP + SZ_ZP);
     // omega in LDS: bf16 high and low parts (bf16 inputs) or fp32 (fp32 inputs)
     static constexpr size_t SZ_OM = RF ? (sizeof(T) == 2 ? size_t(2) * M * XLD * 2 : size_t(M) * XLD * 4) : 0;
     static constexpr size_t TOTAL = al(OFF_OM + SZ_OM);
@@ -123,6 +127,7 @@ la_fwd_kernel(const FwdArgs a)
     T* sXq = (T*)(smem + Cfg::OFF_XQ);
     T* sXk = (T*)(smem + Cfg::OFF_XK);
     float* sXn = (float*)(smem + Cfg::OFF_XN);
+    float* sZp = (float*)(smem + Cfg::OFF_ZP);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
@@ -237,6 +242,10 @@ la_fwd_kernel(const FwdArgs a)
             }
         }
         if constexpr (Cfg::NEED_K) {
+            // every r visits the same feature group cg = tid % VPRQ
+            float zacc[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) zacc[e] = 0.f;
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
@@ -263,8 +272,20 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
                         const int f = cg * VEC + e;
-                        sKT[f * C + tsw(f, j)] = from_f32<T>(w * p[e]);
+                        const T wp = from_f32<T>(w * p[e]);
+                        sKT[f * C + tsw(f, j)] = wp;
+                        zacc[e] += to_f32(wp);
                     }
+                }
+            }
+            if constexpr (!RF) {
+                // sum over the lanes of this wave that hold the same feature group
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    for (int m = VPRQ; m < 64; m <<= 1) zacc[e] += __shfl_xor(zacc[e], m, 64);
+                if (lane < VPRQ) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) sZp[wave * F + lane * VEC + e] = zacc[e];
                 }
             }
 #pragma unroll
@@ -318,10 +339,21 @@ la_fwd_kernel(const FwdArgs a)
                 }
                 if (dst_t) {
                     const float w = (i < n) ? lam_pow(l2l, n - 1 - i) : 0.f;
+                    float zc[4], zs[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        dst_t[(f0 + r) * C + tsw(f0 + r, i)] = from_f32<T>(w * cs[r]);
-                        dst_t[(M + f0 + r) * C + tsw(M + f0 + r, i)] = from_f32<T>(w * sn[r]);
+                        const T wc = from_f32<T>(w * cs[r]), ws = from_f32<T>(w * sn[r]);
+                        dst_t[(f0 + r) * C + tsw(f0 + r, i)] = wc;
+                        dst_t[(M + f0 + r) * C + tsw(M + f0 + r, i)] = ws;
+                        zc[r] = wave_sum_xor(to_f32(wc), 1, 8);
+                        zs[r] = wave_sum_xor(to_f32(ws), 1, 8);
+                    }
+                    if (l16 == 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            sZp[ib * F + f0 + r] = zc[r];
+                            sZp[ib * F + M + f0 + r] = zs[r];
+                        }
                     }
                 }
             }
@@ -380,8 +412,10 @@ la_fwd_kernel(const FwdArgs a)
         float znew = zreg;
         if constexpr (Cfg::NEED_K) {
             if (tid < F) {
+                constexpr int NZP = RF ? QB : NW;  // row groups that wrote partial sums
                 float zs = 0.f;
-                for (int j = 0; j < C; ++j) zs += to_f32(sKT[tid * C + j]);
+#pragma unroll
+                for (int w = 0; w < NZP; ++w) zs += sZp[w * F + tid];
                 znew = lam_pow(l2l, n) * zreg + zs;
             }
         }

@@ -25,9 +25,18 @@ __global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
     const int ez = e - a.F * a.DV;
     float* base = a.ws + (int64_t)bh * SZ + e;
     const int64_t slot = (int64_t)a.BH * SZ;
+    // Segments are visited in batches whose loads are all issued before the
+    // first store, so a batch costs one memory round trip, not one per segment.
+    constexpr int BATCH = 8;
+    float loc[BATCH];
     if (!a.causal) {
         float acc = 0.f;
-        for (int s = 0; s < a.P; ++s) acc += base[s * slot];
+        for (int s0 = 0; s0 < a.P; s0 += BATCH) {
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : 0.f;
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) acc += loc[b];
+        }
         base[0] = acc;
         return;
     }
@@ -35,12 +44,19 @@ __global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
     float carry = 0.f;
     if (a.S_init) carry = isz ? a.z_init[bh * a.init_zstride + ez] : a.S_init[bh * a.init_stride + e];
     const int64_t NC = (a.n_len + a.C - 1) / a.C;
-    for (int s = 0; s < a.P; ++s) {
-        const int64_t c0 = (int64_t)s * NC / a.P, c1 = (int64_t)(s + 1) * NC / a.P;
-        const int64_t L = min(c1 * a.C, a.n_len) - c0 * a.C;
-        const float loc = base[s * slot];
-        base[s * slot] = carry;
-        carry = lam_pow(l2l, (int)L) * carry + loc;
+    for (int s0 = 0; s0 < a.P; s0 += BATCH) {
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : 0.f;
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int s = s0 + b;
+            if (s < a.P) {
+                const int64_t c0 = (int64_t)s * NC / a.P, c1 = (int64_t)(s + 1) * NC / a.P;
+                const int64_t L = min(c1 * a.C, a.n_len) - c0 * a.C;
+                base[s * slot] = carry;
+                carry = lam_pow(l2l, (int)L) * carry + loc[b];
+            }
+        }
     }
     if (a.S_fin) {
         if (isz) a.z_fin[bh * a.fin_zstride + ez] = carry;
