@@ -173,7 +173,7 @@ int env_int(const char* name, int dflt)
 // Work plan of one forward call.
 struct Plan {
     int C;          // chunk length
-    int P;          // segments per window (upper bound over windows)
+    int Pmax;       // upper bound of segments per window (sizes the workspace)
     int W;          // windows
     int64_t SZ;     // floats per state slot: F*d_v + F
     size_t ws_bytes;
@@ -183,15 +183,23 @@ struct Plan {
 // an MI355X (256 CUs).
 constexpr int kTargetWorkgroups = 512;
 
-int segments_for(int64_t n_len, int C, int64_t BH)
+// Segments wanted for a row of NC chunks (before rounding to whole chunks).
+int64_t target_segments(int64_t NC, int64_t BH)
 {
-    const int64_t NC = (n_len + C - 1) / C;
     int64_t P = (kTargetWorkgroups + BH - 1) / BH;
     const int forced = env_int("LA_SEGMENTS", 0);
     if (forced > 0) P = forced;
     if (P > NC) P = NC;
     if (P < 1) P = 1;
-    return (int)P;
+    return P;
+}
+
+// Cut NC chunks into segments of cps chunks: every segment but the last is full.
+void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps)
+{
+    const int64_t Pt = target_segments(NC, BH);
+    *cps = (NC + Pt - 1) / Pt;
+    *P = (int)((NC + *cps - 1) / *cps);
 }
 
 Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal)
@@ -205,15 +213,14 @@ Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal)
     if (W < 1) W = 1;
     if (W > NC) W = (int)(NC > 0 ? NC : 1);
     p.W = W;
-    // the first window is the longest (windows are cut on chunk boundaries)
-    const int64_t len0 = std::min<int64_t>(s->N, ((NC + W - 1) / W) * p.C);
-    p.P = segments_for(len0 > 0 ? len0 : 1, p.C, BH);
+    // every window has at most NC chunks, so it is cut into at most this many segments
+    p.Pmax = (int)target_segments(NC > 0 ? NC : 1, BH);
     size_t floats = 0;
     if (causal) {
-        if (p.P > 1) floats += (size_t)p.P * BH * p.SZ;
+        if (p.Pmax > 1) floats += (size_t)p.Pmax * BH * p.SZ;
         if (p.W > 1) floats += (size_t)BH * p.SZ;
     } else {
-        floats += (size_t)p.P * BH * p.SZ;
+        floats += (size_t)p.Pmax * BH * p.SZ;
     }
     p.ws_bytes = floats ? ((floats * sizeof(float) + 255) & ~size_t(255)) : 0;
     return p;
@@ -395,7 +402,7 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
 
     float* ws = static_cast<float*>(workspace);
     float* segs = ws;                                                     // [P][BH][SZ]
-    float* carry = ws ? ws + (plan.P > 1 ? (size_t)plan.P * BH * plan.SZ : 0) : nullptr;  // [BH][SZ]
+    float* carry = ws ? ws + (plan.Pmax > 1 ? (size_t)plan.Pmax * BH * plan.SZ : 0) : nullptr;  // [BH][SZ]
     const int64_t NC = (shape->N + plan.C - 1) / plan.C;
 
     FwdArgs a;
@@ -416,7 +423,9 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
     for (int w = 0; w < plan.W; ++w) {
         const int64_t c0 = (int64_t)w * NC / plan.W, c1 = (int64_t)(w + 1) * NC / plan.W;
         const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, shape->N) - n0;
-        const int P = segments_for(n_len, plan.C, BH) <= plan.P ? segments_for(n_len, plan.C, BH) : plan.P;
+        int P = 1;
+        int64_t cps = 1;
+        cut_segments(c1 - c0, BH, &P, &cps);
         // state entering and leaving this window
         const float* Si = nullptr;
         const float* zi = nullptr;
@@ -437,6 +446,7 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
         a.n0 = n0;
         a.n_len = n_len;
         a.P = P;
+        a.cps = cps;
         hipError_t e;
         if (P > 1) {
             // pass 1: segment-local states
@@ -457,7 +467,7 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             sa.F = F;
             sa.DV = shape->d_v;
             sa.n_len = n_len;
-            sa.C = plan.C;
+            sa.seg_len = cps * plan.C;
             sa.causal = 1;
             sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
@@ -512,7 +522,11 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     a.n_len = shape->N;
     a.BH = (int32_t)BH;
     a.H = (int32_t)shape->H;
-    a.P = plan.P;
+    int P = 1;
+    int64_t cps = 1;
+    cut_segments((shape->N + plan.C - 1) / plan.C, BH, &P, &cps);
+    a.P = P;
+    a.cps = cps;
     a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
     a.eps = eps;
     a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
@@ -527,17 +541,17 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     l.dst_zstride = plan.SZ;
     if ((e = launch(LA_KERNEL_FWD_LOCAL, strm, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
         return hip_fail(e, "state sum launch");
-    if (plan.P > 1) {
+    if (P > 1) {
         ScanArgs sa;
         std::memset(&sa, 0, sizeof(sa));
         sa.ws = ws;
-        sa.P = plan.P;
+        sa.P = P;
         sa.BH = (int32_t)BH;
         sa.H = (int32_t)shape->H;
         sa.F = F;
         sa.DV = shape->d_v;
         sa.n_len = shape->N;
-        sa.C = plan.C;
+        sa.seg_len = cps * plan.C;
         sa.causal = 0;
         if ((e = launch(LA_KERNEL_SCAN, strm, [&] { return launch_scan(sa, strm); })) != hipSuccess)
             return hip_fail(e, "state reduction launch");

@@ -96,6 +96,74 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
     for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
 }
 
+// ---- LDS tiles ----------------------------------------------------------
+// A per-chunk operand tile holds `rows` tokens of W elements each, row-major.
+// bf16 tiles have no padding; their 8-byte units (4 elements) are XOR-swizzled
+// inside each aligned group of 16 units by swz(row).  With that permutation a
+// row-fragment read (16 consecutive rows, one unit each) and a transposing
+// read (4 consecutive rows x 4 consecutive units per 16 lanes) both touch 32
+// distinct banks.  fp32 tiles are padded by 4 elements per row instead.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+template <class T, int W> struct TileL;
+template <int W> struct TileL<bf16, W> {
+    static_assert(W % 64 == 0, "bf16 tiles need at least 16 units per row");
+    static constexpr int STRIDE = W;
+    // element offset of the 4-element unit holding column col (col % 4 == 0)
+    __device__ static __forceinline__ int off(int row, int col) {
+        return row * W + ((((col >> 2) ^ swz(row))) << 2);
+    }
+};
+template <int W> struct TileL<float, W> {
+    static constexpr int STRIDE = W + 4;
+    __device__ static __forceinline__ int off(int row, int col) { return row * (W + 4) + col; }
+};
+
+// Row fragment: lane (row, g) holds columns {32kb+4g..+3, 32kb+16+4g..+3}.
+template <class T, int W>
+__device__ __forceinline__ Frag<T> lds_frag_row(const T* t, int row, int kb, int g) {
+    return frag2(t + TileL<T, W>::off(row, 32 * kb + 4 * g), t + TileL<T, W>::off(row, 32 * kb + 16 + 4 * g));
+}
+
+// Column fragment of rows j0..j0+31 and columns m0..m0+15 (j0 % 32 == 0,
+// m0 % 16 == 0): lane l holds X[j0+4g+e][m0+l%16] in slot e and
+// X[j0+16+4g+e][m0+l%16] in slot 4+e, g = l/16 -- the same k positions as a
+// row fragment, so it pairs with row fragments and accumulator fragments.
+// bf16: two ds_read_b64_tr_b16.  Within each group of 16 lanes that
+// instruction returns to lane i, slot e, element i%4 of the 8 bytes addressed
+// by lane 4e+i/4; lane 16g+l' therefore addresses row j0+4g+l'/4 at column
+// m0+4(l'%4).  fp32: eight scalar reads.
+template <class T, int W> struct ColRead;
+template <int W> struct ColRead<bf16, W> {
+    __device__ static __forceinline__ Frag<bf16> get(const bf16* t, int j0, int m0, int lane) {
+        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+        const int g = lane >> 4, lp = lane & 15;
+        const int row = j0 + 4 * g + (lp >> 2), col = m0 + 4 * (lp & 3);
+        const bf16* p = t + TileL<bf16, W>::off(row, col);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * W));
+        Frag<bf16> f;
+        f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return f;
+    }
+};
+template <int W> struct ColRead<float, W> {
+    __device__ static __forceinline__ Frag<float> get(const float* t, int j0, int m0, int lane) {
+        const int g = lane >> 4, m = m0 + (lane & 15);
+        constexpr int S = TileL<float, W>::STRIDE;
+        Frag<float> f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f.lo[e] = t[(j0 + 4 * g + e) * S + m];
+            f.hi[e] = t[(j0 + 16 + 4 * g + e) * S + m];
+        }
+        return f;
+    }
+};
+
+// 1/x on the transcendental unit (1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // lambda^k from log2(lambda), with lambda^0 = 1 also for lambda = 0.
 __device__ __forceinline__ float lam_pow(float log2lam, int k) {
     return k == 0 ? 1.0f : exp2f((float)k * log2lam);

@@ -2,7 +2,7 @@
 // kernelized linear attention, templated on element type, feature map and
 // head sizes.  Instantiated by the la_inst_*.hip units.
 //
-// Method ("Attention is also an FFN", kwkr.cn/news/587576, sec. 4.1 and
+// Method ("Attention is also an FFN", kwkr.cn/news/587576, sec. 4.1 notes and
 // sec. 5.2: cut the sequence into chunks, compute in parallel inside a chunk
 // and carry a state across chunks; decay from sec. 3.2, normaliser from
 // sec. 4.2).  For a chunk of n tokens starting after state (S, z), with local
@@ -15,14 +15,23 @@
 //
 // which equals the token-by-token recurrence exactly up to rounding order.
 //
-// One workgroup of 4 waves owns one segment (a run of whole chunks) of one
-// (batch, head) row.  The fp32 state lives in the waves' accumulator
-// registers, split by value column: wave w owns d_v columns
-// [16*DBW*w, 16*DBW*(w+1)) of S for all F feature rows, so the product
-// phi(Q) S reads its B operand straight from the accumulators (see the
-// fragment note in la_device.h) and the state never goes through LDS.
-// The chunk's scores phi(K) phi(Q)^T are computed once, cooperatively, and
-// shared through LDS as the masked, decayed matrix P (row-major, bf16).
+// Work split.  One workgroup of NW waves owns one segment (a run of whole
+// chunks) of one (batch, head) row.  The fp32 state S lives in accumulator
+// registers, split by value column: wave w owns columns
+// [16*DBW*w, 16*DBW*(w+1)) for all F feature rows.  Outputs are computed
+// transposed, O^T = S^T phi(Q)^T + V^T P^T, so that
+//   - S^T is an A operand read straight from the accumulators,
+//   - the transposed score tile phi(K) phi(Q)^T that a wave holds is already
+//     the B operand P^T (no LDS round trip for P), and
+//   - each lane ends up with 4 consecutive output columns of one token, which
+//     it stores with one 8-byte (bf16) or 16-byte (fp32) write.
+// Every wave computes the (small) score tiles it needs itself.
+//
+// Per chunk, the tiles phi(Q), phi(K), lambda-weighted phi(K) and V are staged
+// row-major in LDS (see TileL in la_device.h); products that contract over
+// the token axis read them with transposing LDS reads.  The tiles are double
+// buffered so that a chunk needs one barrier; the next chunk's q, k, v are
+// loaded into registers while the current one is computed.
 //
 // Modes: MODE_LOCAL   segment-local state from a zero start (pass 1),
 //        MODE_CAUSAL  outputs of a segment from its carried-in state (pass 3),
@@ -34,14 +43,9 @@
 
 namespace la {
 
-// Transposed [rows][C] buffers are XOR-swizzled in groups of 4 columns so that
-// the scattered 2-byte staging writes spread over the LDS banks while every
-// 4-element group stays contiguous (and 8-byte aligned) for fragment reads.
-__device__ __forceinline__ int tsw(int r, int j) { return j ^ (((r >> 3) & 7) << 2); }
-
 template <class T, int PHI>
 constexpr int chunk_len(int F) {
-    return (sizeof(T) == 4) ? 32 : (F > 128 ? 32 : 64);
+    return (sizeof(T) == 4 || F > 128) ? 32 : 64;
 }
 
 template <class T, int PHI, int DK, int F, int DV, int C, int NW, int MODE>
@@ -54,50 +58,47 @@ struct FwdCfg {
     static constexpr int FB = F / 16;
     static constexpr int DB = DV / 16;
     static constexpr int DBW = DB / NW;
-    static constexpr int PAD = 4;
-    static constexpr int QLD = F + PAD;
-    static constexpr int PLD = C + PAD;
-    static constexpr int XLD = DK + PAD;
+    static constexpr int XLD = DK + 4;  // raw q/k rows of the random-feature prologue
     static constexpr bool NEED_Q = MODE != MODE_LOCAL;
     static constexpr bool NEED_K = MODE != MODE_QUERY;
     static constexpr bool NEED_KROW = MODE == MODE_CAUSAL;
-    static constexpr bool NEED_P = MODE == MODE_CAUSAL;
+    // feature tiles are double buffered for elu+1; the random-feature prologue
+    // has a barrier of its own before it writes them, so one buffer suffices
+    static constexpr int NBF = RF ? 1 : 2;
+    static constexpr int TQ = C * TileL<T, F>::STRIDE;   // elements of a feature tile
+    static constexpr int TV = C * TileL<T, DV>::STRIDE;  // elements of a value tile
+    static constexpr int ZR = NW > QB ? NW : QB;         // rows of partial key-feature sums
+    static constexpr int DQR = RF ? M / 16 : 1;          // rows of partial phi(q).z sums
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t OFF_Q = 0;
-    static constexpr size_t SZ_Q = NEED_Q ? size_t(C) * QLD * sizeof(T) : 0;
+    static constexpr size_t SZ_Q = NEED_Q ? size_t(NBF) * TQ * sizeof(T) : 0;
     static constexpr size_t OFF_K = al(OFF_Q + SZ_Q);
-    static constexpr size_t SZ_K = NEED_KROW ? size_t(C) * QLD * sizeof(T) : 0;
-    static constexpr size_t OFF_KT = al(OFF_K + SZ_K);
-    static constexpr size_t SZ_KT = NEED_K ? size_t(F) * C * sizeof(T) : 0;
-    static constexpr size_t OFF_VT = al(OFF_KT + SZ_KT);
-    static constexpr size_t SZ_VT = NEED_K ? size_t(DV) * C * sizeof(T) : 0;
-    static constexpr size_t OFF_P = al(OFF_VT + SZ_VT);
-    static constexpr size_t SZ_P = NEED_P ? size_t(C) * PLD * sizeof(T) : 0;
-    static constexpr size_t OFF_Z = al(OFF_P + SZ_P);
-    static constexpr size_t SZ_Z = size_t(F) * sizeof(float);
-    static constexpr size_t OFF_DEN = al(OFF_Z + SZ_Z);
-    static constexpr size_t SZ_DEN = size_t(C) * sizeof(float);
-    static constexpr size_t OFF_ROW = al(OFF_DEN + SZ_DEN);
-    static constexpr size_t SZ_ROW = NEED_P ? size_t(QB) * C * sizeof(float) : 0;
-    static constexpr size_t OFF_XQ = al(OFF_ROW + SZ_ROW);
+    static constexpr size_t SZ_K = NEED_KROW ? size_t(NBF) * TQ * sizeof(T) : 0;
+    static constexpr size_t OFF_KW = al(OFF_K + SZ_K);
+    static constexpr size_t SZ_KW = NEED_K ? size_t(NBF) * TQ * sizeof(T) : 0;
+    static constexpr size_t OFF_V = al(OFF_KW + SZ_KW);
+    static constexpr size_t SZ_V = NEED_K ? size_t(2) * TV * sizeof(T) : 0;
+    static constexpr size_t OFF_DQ = al(OFF_V + SZ_V);
+    static constexpr size_t SZ_DQ = NEED_Q ? size_t(2) * DQR * C * sizeof(float) : 0;
+    static constexpr size_t OFF_ZP = al(OFF_DQ + SZ_DQ);
+    static constexpr size_t SZ_ZP = NEED_K ? size_t(2) * ZR * F * sizeof(float) : 0;
+    static constexpr size_t OFF_Z = al(OFF_ZP + SZ_ZP);
+    static constexpr size_t SZ_Z = RF ? size_t(F) * sizeof(float) : 0;
+    static constexpr size_t OFF_XQ = al(OFF_Z + SZ_Z);
     static constexpr size_t SZ_XQ = (RF && NEED_Q) ? size_t(C) * XLD * sizeof(T) : 0;
     static constexpr size_t OFF_XK = al(OFF_XQ + SZ_XQ);
     static constexpr size_t SZ_XK = (RF && NEED_K) ? size_t(C) * XLD * sizeof(T) : 0;
     static constexpr size_t OFF_XN = al(OFF_XK + SZ_XK);
     static constexpr size_t SZ_XN = RF ? size_t(2) * C * sizeof(float) : 0;
-    // partial sums over token groups of the weighted key features (for z)
-    static constexpr int ZR = NW > QB ? NW : QB;
-    static constexpr size_t OFF_ZP = al(OFF_XN + SZ_XN);
-    static constexpr size_t SZ_ZP = NEED_K ? size_t(ZR) * F * sizeof(float) : 0;
-    static constexpr size_t OFF_OM = al(OFF_ZP + SZ_ZP);
+    static constexpr size_t OFF_OM = al(OFF_XN + SZ_XN);
     // omega in LDS: bf16 high and low parts (bf16 inputs) or fp32 (fp32 inputs)
     static constexpr size_t SZ_OM = RF ? (sizeof(T) == 2 ? size_t(2) * M * XLD * 2 : size_t(M) * XLD * 4) : 0;
     static constexpr size_t TOTAL = al(OFF_OM + SZ_OM);
 
     static_assert(C % 32 == 0 && C >= 32, "chunk must be a multiple of 32");
-    static_assert(F % 32 == 0 && DV % 16 == 0 && DK % 32 == 0, "head sizes");
+    static_assert(F % 64 == 0 && DV % 64 == 0 && DK % 32 == 0, "head sizes");
     static_assert(DBW >= 1 && DB % NW == 0, "value columns must split over the waves");
-    static_assert(F <= NT && C <= NT && NT % C == 0, "thread mapping");
+    static_assert(F <= NT && C <= NT, "thread mapping");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -107,38 +108,59 @@ la_fwd_kernel(const FwdArgs a)
 {
     using Cfg = FwdCfg<T, PHI, DK, F, DV, C, NW, MODE>;
     constexpr int NT = Cfg::NT, VEC = Cfg::VEC, M = Cfg::M, QB = Cfg::QB, FB = Cfg::FB;
-    constexpr int DBW = Cfg::DBW, QLD = Cfg::QLD, PLD = Cfg::PLD, XLD = Cfg::XLD;
+    constexpr int DBW = Cfg::DBW, XLD = Cfg::XLD, NBF = Cfg::NBF, TQ = Cfg::TQ, TV = Cfg::TV;
+    constexpr int ZR = Cfg::ZR, DQR = Cfg::DQR;
     constexpr bool RF = Cfg::RF;
+    constexpr int KB = F / 32;                  // 32-wide feature blocks
+    constexpr int CB = C / 32;                  // 32-wide token blocks
     constexpr int VPRQ = DK / VEC;              // 16-byte vectors per q/k row
     constexpr int VPRV = DV / VEC;              // 16-byte vectors per v row
     constexpr int VQ = C * VPRQ, VV = C * VPRV; // vectors per tile
     constexpr int RQ = (VQ + NT - 1) / NT, RV = (VV + NT - 1) / NT;
     static_assert(VQ % NT == 0 && VV % NT == 0, "tiles must split evenly over threads");
+    using TF = TileL<T, F>;
+    using TVL = TileL<T, DV>;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
-    T* sQ = (T*)(smem + Cfg::OFF_Q);
-    T* sK = (T*)(smem + Cfg::OFF_K);
-    T* sKT = (T*)(smem + Cfg::OFF_KT);
-    T* sVT = (T*)(smem + Cfg::OFF_VT);
-    T* sP = (T*)(smem + Cfg::OFF_P);
-    float* sZ = (float*)(smem + Cfg::OFF_Z);
-    float* sDen = (float*)(smem + Cfg::OFF_DEN);
-    float* sRow = (float*)(smem + Cfg::OFF_ROW);
-    T* sXq = (T*)(smem + Cfg::OFF_XQ);
-    T* sXk = (T*)(smem + Cfg::OFF_XK);
-    float* sXn = (float*)(smem + Cfg::OFF_XN);
-    float* sZp = (float*)(smem + Cfg::OFF_ZP);
+    T* const sQ0 = (T*)(smem + Cfg::OFF_Q);
+    T* const sK0 = (T*)(smem + Cfg::OFF_K);
+    T* const sKw0 = (T*)(smem + Cfg::OFF_KW);
+    T* const sV0 = (T*)(smem + Cfg::OFF_V);
+    float* const sDq0 = (float*)(smem + Cfg::OFF_DQ);
+    float* const sZp0 = (float*)(smem + Cfg::OFF_ZP);
+    float* const sZ = (float*)(smem + Cfg::OFF_Z);
+    T* const sXq = (T*)(smem + Cfg::OFF_XQ);
+    T* const sXk = (T*)(smem + Cfg::OFF_XK);
+    float* const sXn = (float*)(smem + Cfg::OFF_XN);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
     const float l2l = (MODE == MODE_QUERY) ? 0.f : a.lam.log2lam[h];
+    const bool decay = l2l != 0.f;  // uniform over the workgroup
     const int64_t NC = (a.n_len + C - 1) / C;
-    const int64_t c_beg = (int64_t)seg * NC / a.P, c_end = (int64_t)(seg + 1) * NC / a.P;
+    const int64_t c_beg = (int64_t)seg * a.cps, c_end = min(NC, c_beg + a.cps);
     const T* qg = (const T*)a.q + ((int64_t)bh * a.N + a.n0) * DK;
     const T* kg = (const T*)a.k + ((int64_t)bh * a.N + a.n0) * DK;
     const T* vg = (const T*)a.v + ((int64_t)bh * a.N + a.n0) * DV;
     const float qs = a.qk_scale;
+    const float lamC = lam_pow(l2l, C);
+    const int cg = tid % VPRQ;       // this thread's feature group in the staging loops
+
+    // ---- decay tables of this lane (lambda is fixed per workgroup)
+    // mt[d][r]: mask and decay of score element (i = 16(jb+d) + l16, j = 16 jb + 4g + r)
+    float mt[QB][4];
+    // lq[ib]: lambda^(i+1) for the lane's query row i = 16 ib + l16
+    float lq[QB];
+#pragma unroll
+    for (int d = 0; d < QB; ++d) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 16 * d + l16 - 4 * g - r;
+            mt[d][r] = e < 0 ? 0.f : (decay ? lam_pow(l2l, e) : 1.f);
+        }
+        lq[d] = decay ? lam_pow(l2l, 16 * d + l16 + 1) : 1.f;
+    }
 
     // ---- random-feature directions into LDS (once per workgroup)
     if constexpr (RF) {
@@ -157,16 +179,21 @@ la_fwd_kernel(const FwdArgs a)
         }
     }
 
-    // ---- carried state: accumulator tiles (fb, this wave's d-blocks)
+    // ---- carried state: accumulator tiles (fb, this wave's d-blocks); z
     f32x4 accS[FB][DBW];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
         for (int t = 0; t < DBW; ++t) accS[fb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float zreg = 0.f;  // z[tid] (tid < F)
+    // elu+1: every thread tracks z for its own VEC features cg*VEC.. (all the
+    // staging needs); random features keep z in LDS.
+    float zreg[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) zreg[e] = 0.f;
     if constexpr (MODE != MODE_LOCAL) {
         if (a.S_src) {
             const float* Sb = a.S_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_stride;
+            const float* zb = a.z_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_zstride;
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -175,13 +202,27 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) accS[fb][t][r] = Sb[(16 * fb + 4 * g + r) * DV + d];
                 }
-            if (tid < F) zreg = a.z_src[(int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_zstride + tid];
+            if constexpr (RF) {
+                if (tid < F) sZ[tid] = zb[tid];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) zreg[e] = zb[cg * VEC + e];
+            }
+        } else if constexpr (RF) {
+            if (tid < F) sZ[tid] = 0.f;
         }
-        if (tid < F) sZ[tid] = zreg;
+    } else if constexpr (RF) {
+        if (tid < F) sZ[tid] = 0.f;
     }
-    if constexpr (Cfg::NEED_P) {
-        for (int idx = tid; idx < C * PLD; idx += NT) sP[idx] = from_f32<T>(0.f);
-    }
+    // S as bf16 / fp32 operand fragments (A operand of O^T = S^T phi(Q)^T)
+    Frag<T> sf[KB][DBW];
+    auto convert_state = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < DBW; ++t) sf[kb][t] = frag_acc<T>(accS[2 * kb][t], accS[2 * kb + 1][t]);
+    };
+    if constexpr (Cfg::NEED_Q) convert_state();
 
     // ---- global -> register prefetch of one chunk.  Rows past the end of the
     // sequence re-read the last valid row (always in bounds) and are replaced
@@ -194,33 +235,81 @@ la_fwd_kernel(const FwdArgs a)
         if constexpr (Cfg::NEED_Q) {
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
-                const uint4 val = *(const uint4*)(qg + (t0 + min(j, n - 1)) * DK + cg * VEC);
+                const int idx = tid + r * NT, j = idx / VPRQ, c4 = idx % VPRQ;
+                const uint4 val = *(const uint4*)(qg + (t0 + min(j, n - 1)) * DK + c4 * VEC);
                 rq[r] = (j < n) ? val : zero;
             }
         }
         if constexpr (Cfg::NEED_K) {
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
-                const uint4 val = *(const uint4*)(kg + (t0 + min(j, n - 1)) * DK + cg * VEC);
+                const int idx = tid + r * NT, j = idx / VPRQ, c4 = idx % VPRQ;
+                const uint4 val = *(const uint4*)(kg + (t0 + min(j, n - 1)) * DK + c4 * VEC);
                 rk[r] = (j < n) ? val : zero;
             }
 #pragma unroll
             for (int r = 0; r < RV; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRV, cg = idx % VPRV;
-                const uint4 val = *(const uint4*)(vg + (t0 + min(j, n - 1)) * DV + cg * VEC);
+                const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
+                const uint4 val = *(const uint4*)(vg + (t0 + min(j, n - 1)) * DV + c4 * VEC);
                 rv[r] = (j < n) ? val : zero;
             }
         }
     };
 
-    // ---- register -> LDS staging (feature map for elu+1; raw tiles for RF)
-    auto stage = [&](int n) {
+    // raw 16-byte vector -> row-major tile (no conversion)
+    auto put_raw = [&](T* tile, int stride_w, int row, int col, const uint4& u) {
+        if constexpr (sizeof(T) == 2) {
+            (void)stride_w;
+            *(uint2*)(tile + TVL::off(row, col)) = uint2{u.x, u.y};
+            *(uint2*)(tile + TVL::off(row, col + 4)) = uint2{u.z, u.w};
+        } else {
+            *(uint4*)(tile + row * stride_w + col) = u;
+        }
+    };
+    // VEC floats -> row-major feature tile (rounded to T); returns the rounded values
+    auto put_feat = [&](T* tile, int row, int col, float* p) {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            st4(tile + TF::off(row, col + e), p[e], p[e + 1], p[e + 2], p[e + 3]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) p[e + u] = to_f32(from_f32<T>(p[e + u]));
+        }
+    };
+
+    // ---- staging of one chunk from registers.  elu+1: feature map, phi(q).z,
+    // weighted keys and their column sums; random features: raw rows and norms.
+    auto stage = [&](int buf, int n, bool first) {
+        T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
+        T* const sK = sK0 + (RF ? 0 : buf * TQ);
+        T* const sKw = sKw0 + (RF ? 0 : buf * TQ);
+        T* const sV = sV0 + buf * TV;
+        if constexpr (Cfg::NEED_K) {
+            // fold the previous chunk's key-feature sums into z
+            const float* zp = sZp0 + (buf ^ 1) * ZR * F;
+            if constexpr (RF) {
+                if (!first && tid < F) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int w = 0; w < QB; ++w) s += zp[w * F + tid];
+                    sZ[tid] = lamC * sZ[tid] + s;
+                }
+            } else {
+                if (!first) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        float s = 0.f;
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) s += zp[w * F + cg * VEC + e];
+                        zreg[e] = lamC * zreg[e] + s;
+                    }
+                }
+            }
+        }
         if constexpr (Cfg::NEED_Q) {
+            float* const sDq = sDq0 + buf * DQR * C;
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
+                const int idx = tid + r * NT, j = idx / VPRQ;
                 float x[VEC];
                 unpack16(rq[r], x, (const T*)nullptr);
                 if constexpr (RF) {
@@ -236,19 +325,22 @@ la_fwd_kernel(const FwdArgs a)
                     float p[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) p[e] = (j < n) ? phi_elu1<T>(x[e]) : 0.f;
+                    put_feat(sQ, j, cg * VEC, p);
+                    float dq = 0.f;
 #pragma unroll
-                    for (int e = 0; e < VEC; e += 4) st4(sQ + j * QLD + cg * VEC + e, p[e], p[e + 1], p[e + 2], p[e + 3]);
+                    for (int e = 0; e < VEC; ++e) dq += p[e] * zreg[e];
+                    dq = wave_sum_xor(dq, 1, VPRQ / 2);
+                    if (cg == 0) sDq[j] = dq;
                 }
             }
         }
         if constexpr (Cfg::NEED_K) {
-            // every r visits the same feature group cg = tid % VPRQ
             float zacc[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) zacc[e] = 0.f;
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
+                const int idx = tid + r * NT, j = idx / VPRQ;
                 float x[VEC];
                 unpack16(rk[r], x, (const T*)nullptr);
                 if constexpr (RF) {
@@ -261,262 +353,237 @@ la_fwd_kernel(const FwdArgs a)
                     s2 = wave_sum_xor(s2, 1, VPRQ / 2);
                     if (cg == 0) sXn[C + j] = s2;
                 } else {
-                    const float w = (j < n) ? lam_pow(l2l, n - 1 - j) : 0.f;
                     float p[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) p[e] = (j < n) ? phi_elu1<T>(x[e]) : 0.f;
-                    if constexpr (Cfg::NEED_KROW) {
+                    if (!decay) {
+                        // unweighted keys serve the scores and the state update
+                        put_feat(Cfg::NEED_KROW ? sK : sKw, j, cg * VEC, p);
+                    } else {
+                        const float w = (j < n) ? lam_pow(l2l, n - 1 - j) : 0.f;
+                        if constexpr (Cfg::NEED_KROW) {
+                            float pk[VEC];
 #pragma unroll
-                        for (int e = 0; e < VEC; e += 4) st4(sK + j * QLD + cg * VEC + e, p[e], p[e + 1], p[e + 2], p[e + 3]);
+                            for (int e = 0; e < VEC; ++e) pk[e] = p[e];
+                            put_feat(sK, j, cg * VEC, pk);
+                        }
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) p[e] *= w;
+                        put_feat(sKw, j, cg * VEC, p);
                     }
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const int f = cg * VEC + e;
-                        const T wp = from_f32<T>(w * p[e]);
-                        sKT[f * C + tsw(f, j)] = wp;
-                        zacc[e] += to_f32(wp);
-                    }
+                    for (int e = 0; e < VEC; ++e) zacc[e] += p[e];
                 }
             }
             if constexpr (!RF) {
-                // sum over the lanes of this wave that hold the same feature group
+                // column sums over the rows this wave staged; lanes < VPRQ hold them
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     for (int m = VPRQ; m < 64; m <<= 1) zacc[e] += __shfl_xor(zacc[e], m, 64);
                 if (lane < VPRQ) {
+                    float* zp = sZp0 + buf * ZR * F + wave * F + cg * VEC;
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) sZp[wave * F + lane * VEC + e] = zacc[e];
+                    for (int e = 0; e < VEC; e += 4) *(f32x4*)(zp + e) = f32x4{zacc[e], zacc[e + 1], zacc[e + 2], zacc[e + 3]};
                 }
             }
 #pragma unroll
             for (int r = 0; r < RV; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRV, cg = idx % VPRV;
-                float x[VEC];
-                unpack16(rv[r], x, (const T*)nullptr);
+                const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
+                put_raw(sV, TVL::STRIDE, j, c4 * VEC, rv[r]);
+            }
+        }
+    };
+
+    // ---- random features on the matrix cores: U^T = omega x^T, then cos/sin,
+    // written row-major into the feature tiles
+    auto rf_features = [&](int buf, int n) {
+        if constexpr (RF) {
+            constexpr int TILES = (M / 16) * QB;
+            const float cnorm = rsqrtf((float)M);
+            float* const sDq = sDq0 + buf * DQR * C;
+            float* const zp = sZp0 + buf * ZR * F;
+            constexpr int NPASS = (Cfg::NEED_Q ? 1 : 0) + (Cfg::NEED_K ? 1 : 0);
+            for (int pass = 0; pass < NPASS; ++pass) {
+                const bool isq = Cfg::NEED_Q && pass == 0;
+                const T* sX = isq ? sXq : sXk;
+                const float* xn = sXn + (isq ? 0 : C);
+                for (int t = wave; t < TILES; t += NW) {
+                    const int rb = t / QB, ib = t % QB;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const int d = cg * VEC + e;
-                    sVT[d * C + tsw(d, j)] = from_f32<T>(x[e]);
+                    for (int kb = 0; kb < DK / 32; ++kb) {
+                        const Frag<T> b = frag_rm(sX, XLD, 16 * ib + l16, 32 * kb, g);
+                        if constexpr (sizeof(T) == 2) {
+                            const bf16* hi = (const bf16*)(smem + Cfg::OFF_OM);
+                            const bf16* lo = hi + M * XLD;
+                            mma(acc, frag_rm(hi, XLD, 16 * rb + l16, 32 * kb, g), b);
+                            mma(acc, frag_rm(lo, XLD, 16 * rb + l16, 32 * kb, g), b);
+                        } else {
+                            const float* om = (const float*)(smem + Cfg::OFF_OM);
+                            mma(acc, frag_rm(om, XLD, 16 * rb + l16, 32 * kb, g), b);
+                        }
+                    }
+                    // acc[r] = u_{f0+r}(x_i) / qs with f0 = 16 rb + 4 g, token i = 16 ib + l16
+                    const int i = 16 * ib + l16, f0 = 16 * rb + 4 * g;
+                    const float cfac = (i < n) ? exp_rf<T>(-0.5f * qs * qs * xn[i]) * cnorm : 0.f;
+                    float cs[4], sn[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        sincos_rf<T>(qs * acc[r], &sn[r], &cs[r]);
+                        cs[r] *= cfac;
+                        sn[r] *= cfac;
+                    }
+                    if (isq) {
+                        st4(sQ0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
+                        st4(sQ0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
+                        // phi(q_i).z over these 8 features, summed over the 4 lane groups
+                        const f32x4 zc = *(const f32x4*)(sZ + f0), zs = *(const f32x4*)(sZ + M + f0);
+                        float dq = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            dq += to_f32(from_f32<T>(cs[r])) * zc[r] + to_f32(from_f32<T>(sn[r])) * zs[r];
+                        dq += __shfl_xor(dq, 16, 64);
+                        dq += __shfl_xor(dq, 32, 64);
+                        if (g == 0) sDq[rb * C + i] = dq;
+                    } else {
+                        if constexpr (Cfg::NEED_KROW) {
+                            st4(sK0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
+                            st4(sK0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
+                        }
+                        const float w = (i < n) ? (decay ? lam_pow(l2l, n - 1 - i) : 1.f) : 0.f;
+                        float wc[4], ws[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            wc[r] = to_f32(from_f32<T>(w * cs[r]));
+                            ws[r] = to_f32(from_f32<T>(w * sn[r]));
+                        }
+                        st4(sKw0 + TF::off(i, f0), wc[0], wc[1], wc[2], wc[3]);
+                        st4(sKw0 + TF::off(i, M + f0), ws[0], ws[1], ws[2], ws[3]);
+                        // column sums over the 16 tokens of this tile
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            wc[r] = wave_sum_xor(wc[r], 1, 8);
+                            ws[r] = wave_sum_xor(ws[r], 1, 8);
+                        }
+                        if (l16 == 0) {
+                            *(f32x4*)(zp + ib * F + f0) = f32x4{wc[0], wc[1], wc[2], wc[3]};
+                            *(f32x4*)(zp + ib * F + M + f0) = f32x4{ws[0], ws[1], ws[2], ws[3]};
+                        }
+                    }
                 }
             }
         }
     };
 
-    // ---- random features on the matrix cores: U^T = omega x^T, then cos/sin
-    auto rf_features = [&](const T* sX, const float* xn, T* dst_row, T* dst_t, int n) {
-        if constexpr (RF) {
-            constexpr int TILES = (M / 16) * QB;
-            const float cnorm = rsqrtf((float)M);
-            for (int t = wave; t < TILES; t += NW) {
-                const int rb = t / QB, ib = t % QB;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- outputs and state update of one staged chunk
+    auto compute = [&](int buf, int n, int64_t t0) {
+        const T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
+        const T* const sK = sK0 + (RF ? 0 : buf * TQ);
+        const T* const sKw = (Cfg::NEED_KROW && !decay && !RF) ? sK : sKw0 + (RF ? 0 : buf * TQ);
+        const T* const sV = sV0 + buf * TV;
+        const float* const sDq = sDq0 + buf * DQR * C;
+        // V column fragments: A operand of V^T P^T and B operand of the state update
+        Frag<T> vf[Cfg::NEED_K ? CB : 1][DBW];
+        if constexpr (Cfg::NEED_K) {
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb) {
-                    const Frag<T> b = frag_rm(sX, XLD, 16 * ib + l16, 32 * kb, g);
-                    if constexpr (sizeof(T) == 2) {
-                        const bf16* hi = (const bf16*)(smem + Cfg::OFF_OM);
-                        const bf16* lo = hi + M * XLD;
-                        mma(acc, frag_rm(hi, XLD, 16 * rb + l16, 32 * kb, g), b);
-                        mma(acc, frag_rm(lo, XLD, 16 * rb + l16, 32 * kb, g), b);
-                    } else {
-                        const float* om = (const float*)(smem + Cfg::OFF_OM);
-                        mma(acc, frag_rm(om, XLD, 16 * rb + l16, 32 * kb, g), b);
-                    }
-                }
+            for (int kb = 0; kb < CB; ++kb)
+#pragma unroll
+                for (int t = 0; t < DBW; ++t) vf[kb][t] = ColRead<T, DV>::get(sV, 32 * kb, 16 * (wave * DBW + t), lane);
+        }
+        if constexpr (Cfg::NEED_Q) {
+            const float eps = a.eps;
+#pragma unroll
+            for (int ib = 0; ib < QB; ++ib) {
                 const int i = 16 * ib + l16;
-                const float cfac = (i < n) ? exp_rf<T>(-0.5f * qs * qs * xn[i]) * cnorm : 0.f;
-                float cs[4], sn[4];
+                Frag<T> qf[KB];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sincos_rf<T>(qs * acc[r], &sn[r], &cs[r]);
-                    cs[r] *= cfac;
-                    sn[r] *= cfac;
-                }
-                const int f0 = 16 * rb + 4 * g;
-                if (dst_row) {
-                    st4(dst_row + i * QLD + f0, cs[0], cs[1], cs[2], cs[3]);
-                    st4(dst_row + i * QLD + M + f0, sn[0], sn[1], sn[2], sn[3]);
-                }
-                if (dst_t) {
-                    const float w = (i < n) ? lam_pow(l2l, n - 1 - i) : 0.f;
-                    float zc[4], zs[4];
+                for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F>(sQ, i, kb, g);
+                // scores of query block ib against key blocks jb <= ib, as P^T fragments
+                Frag<T> pf[CB];
+                float rs = 0.f;
+                if constexpr (MODE == MODE_CAUSAL) {
+                    f32x4 pt[QB];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const T wc = from_f32<T>(w * cs[r]), ws = from_f32<T>(w * sn[r]);
-                        dst_t[(f0 + r) * C + tsw(f0 + r, i)] = wc;
-                        dst_t[(M + f0 + r) * C + tsw(M + f0 + r, i)] = ws;
-                        zc[r] = wave_sum_xor(to_f32(wc), 1, 8);
-                        zs[r] = wave_sum_xor(to_f32(ws), 1, 8);
-                    }
-                    if (l16 == 0) {
+                    for (int jb = 0; jb < QB; ++jb) {
+                        pt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (jb <= ib) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            sZp[ib * F + f0 + r] = zc[r];
-                            sZp[ib * F + M + f0 + r] = zs[r];
+                            for (int kb = 0; kb < KB; ++kb)
+                                mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                pt[jb][r] = to_f32(from_f32<T>(pt[jb][r] * mt[ib - jb][r]));
+                                rs += pt[jb][r];
+                            }
                         }
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < CB; ++kb) pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
+                    rs += __shfl_xor(rs, 16, 64);
+                    rs += __shfl_xor(rs, 32, 64);
+                }
+                float dq = 0.f;
+#pragma unroll
+                for (int q = 0; q < DQR; ++q) dq += sDq[q * C + i];
+                const float den = (MODE == MODE_CAUSAL) ? rs + lq[ib] * dq : dq;
+                const float inv = fast_rcp(den + eps);
+                const int64_t yrow = (int64_t)bh * a.N + a.n0 + t0 + i;
+#pragma unroll
+                for (int t = 0; t < DBW; ++t) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) mma(o, sf[kb][t], qf[kb]);
+                    if constexpr (MODE == MODE_CAUSAL) {
+                        o *= lq[ib];
+#pragma unroll
+                        for (int kb = 0; kb < CB; ++kb)
+                            if (2 * kb <= ib) mma(o, vf[kb][t], pf[kb]);
+                    }
+                    if (i < n) {
+                        const int64_t yo = yrow * DV + 16 * (wave * DBW + t) + 4 * g;
+                        if (a.out_f32) st4((float*)a.y + yo, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+                        else st4((T*)a.y + yo, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
                     }
                 }
             }
+        }
+        // state carry: S <- lambda^n S + (w phi(K))^T V
+        if constexpr (Cfg::NEED_K) {
+            if (decay) {
+                const float dec = lam_pow(l2l, n);
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                    for (int t = 0; t < DBW; ++t) accS[fb][t] *= dec;
+            }
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) {
+                    const Frag<T> kf = ColRead<T, F>::get(sKw, 32 * kb, 16 * fb, lane);
+#pragma unroll
+                    for (int t = 0; t < DBW; ++t) mma(accS[fb][t], kf, vf[kb][t]);
+                }
+            }
+            if constexpr (Cfg::NEED_Q) convert_state();
         }
     };
 
     // ---- main loop over the segment's chunks
     if (c_beg < c_end) load_chunk(c_beg);
-    __syncthreads();  // LDS initialisation complete
+    if constexpr (RF) __syncthreads();  // omega and z in LDS
     for (int64_t c = c_beg; c < c_end; ++c) {
+        const int buf = (int)((c - c_beg) & 1);
         const int64_t t0 = c * C;
         const int n = (int)min((int64_t)C, a.n_len - t0);
-        stage(n);
-        __syncthreads();
+        stage(buf, n, c == c_beg);
         if (c + 1 < c_end) load_chunk(c + 1);
+        __syncthreads();
         if constexpr (RF) {
-            if constexpr (Cfg::NEED_Q) rf_features(sXq, sXn, sQ, (T*)nullptr, n);
-            if constexpr (Cfg::NEED_K) rf_features(sXk, sXn + C, Cfg::NEED_KROW ? sK : (T*)nullptr, sKT, n);
+            rf_features(buf, n);
             __syncthreads();
         }
-
-        // -- scores P = mask(lambda^(i-j) phi(q_i).phi(k_j)), row sums
-        if constexpr (MODE == MODE_CAUSAL) {
-            constexpr int NSC = QB * (QB + 1) / 2;
-            for (int t = wave; t < NSC; t += NW) {
-                int ib = 0, jb = t;
-                while (jb > ib) { jb -= ib + 1; ++ib; }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < F / 32; ++kb)
-                    mma(acc, frag_rm(sK, QLD, 16 * jb + l16, 32 * kb, g), frag_rm(sQ, QLD, 16 * ib + l16, 32 * kb, g));
-                const int i = 16 * ib + l16;
-                float pv[4], rs = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * jb + 4 * g + r;
-                    const float x = (j <= i) ? acc[r] * lam_pow(l2l, i - j) : 0.f;
-                    pv[r] = to_f32(from_f32<T>(x));
-                    rs += pv[r];
-                }
-                st4(sP + i * PLD + 16 * jb + 4 * g, pv[0], pv[1], pv[2], pv[3]);
-                rs += __shfl_xor(rs, 16, 64);
-                rs += __shfl_xor(rs, 32, 64);
-                if (g == 0) sRow[jb * C + i] = rs;
-            }
-        }
-
-        // -- phi(q_i).z for the denominator, and the next z
-        constexpr int TPR = NT / C;
-        const int row = tid / TPR, sub = tid % TPR;
-        float dqz = 0.f;
-        if constexpr (Cfg::NEED_Q) {
-            for (int f = sub; f < F; f += TPR) dqz += to_f32(sQ[row * QLD + f]) * sZ[f];
-            dqz = wave_sum_xor(dqz, 1, TPR / 2);
-        }
-        float znew = zreg;
-        if constexpr (Cfg::NEED_K) {
-            if (tid < F) {
-                constexpr int NZP = RF ? QB : NW;  // row groups that wrote partial sums
-                float zs = 0.f;
-#pragma unroll
-                for (int w = 0; w < NZP; ++w) zs += sZp[w * F + tid];
-                znew = lam_pow(l2l, n) * zreg + zs;
-            }
-        }
-
-        if constexpr (Cfg::NEED_Q) {
-            if constexpr (MODE == MODE_CAUSAL) __syncthreads();  // sRow complete
-            if (sub == 0) {
-                float den = dqz;
-                if constexpr (MODE == MODE_CAUSAL) {
-                    float rsum = 0.f;
-                    for (int jb = 0; jb <= row / 16; ++jb) rsum += sRow[jb * C + row];
-                    den = rsum + lam_pow(l2l, row + 1) * dqz;
-                }
-                sDen[row] = den;
-            }
-            __syncthreads();  // sDen complete
-
-            // -- outputs: O = lambda^(i+1) phi(Q) S  (+ P V), normalised
-            Frag<T> sfr[F / 32][DBW];
-#pragma unroll
-            for (int kb = 0; kb < F / 32; ++kb)
-#pragma unroll
-                for (int t = 0; t < DBW; ++t) sfr[kb][t] = frag_acc<T>(accS[2 * kb][t], accS[2 * kb + 1][t]);
-            const float eps = a.eps;
-#pragma unroll
-            for (int ib = 0; ib < QB; ++ib) {
-                f32x4 o[DBW];
-#pragma unroll
-                for (int t = 0; t < DBW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < F / 32; ++kb) {
-                    const Frag<T> fa = frag_rm(sQ, QLD, 16 * ib + l16, 32 * kb, g);
-#pragma unroll
-                    for (int t = 0; t < DBW; ++t) mma(o[t], fa, sfr[kb][t]);
-                }
-                if constexpr (MODE == MODE_CAUSAL) {
-#pragma unroll
-                    for (int t = 0; t < DBW; ++t)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) o[t][r] *= lam_pow(l2l, 16 * ib + 4 * g + r + 1);
-#pragma unroll
-                    for (int kb2 = 0; kb2 <= ib / 2; ++kb2) {
-                        const Frag<T> fp = frag_rm(sP, PLD, 16 * ib + l16, 32 * kb2, g);
-#pragma unroll
-                        for (int t = 0; t < DBW; ++t) {
-                            const int rr = 16 * (wave * DBW + t) + l16;
-                            const T* vrow = sVT + rr * C;
-                            mma(o[t], fp, frag2(vrow + tsw(rr, 32 * kb2 + 4 * g), vrow + tsw(rr, 32 * kb2 + 16 + 4 * g)));
-                        }
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * ib + 4 * g + r;
-                    if (i < n) {
-                        const float inv = 1.0f / (sDen[i] + eps);
-                        const int64_t yo = ((int64_t)bh * a.N + a.n0 + t0 + i) * DV;
-#pragma unroll
-                        for (int t = 0; t < DBW; ++t) {
-                            const int d = 16 * (wave * DBW + t) + l16;
-                            if (a.out_f32) ((float*)a.y)[yo + d] = o[t][r] * inv;
-                            else ((T*)a.y)[yo + d] = from_f32<T>(o[t][r] * inv);
-                        }
-                    }
-                }
-            }
-        }
-
-        // -- state carry: S <- lambda^n S + (w phi(K))^T V
-        if constexpr (Cfg::NEED_K) {
-            const float dec = lam_pow(l2l, n);
-            Frag<T> vfr[C / 32][DBW];
-#pragma unroll
-            for (int kb = 0; kb < C / 32; ++kb)
-#pragma unroll
-                for (int t = 0; t < DBW; ++t) {
-                    const int rr = 16 * (wave * DBW + t) + l16;
-                    const T* vrow = sVT + rr * C;
-                    vfr[kb][t] = frag2(vrow + tsw(rr, 32 * kb + 4 * g), vrow + tsw(rr, 32 * kb + 16 + 4 * g));
-                }
-#pragma unroll
-            for (int fb = 0; fb < FB; ++fb) {
-#pragma unroll
-                for (int t = 0; t < DBW; ++t) accS[fb][t] *= dec;
-                const int rr = 16 * fb + l16;
-                const T* krow = sKT + rr * C;
-#pragma unroll
-                for (int kb = 0; kb < C / 32; ++kb) {
-                    const Frag<T> fk = frag2(krow + tsw(rr, 32 * kb + 4 * g), krow + tsw(rr, 32 * kb + 16 + 4 * g));
-#pragma unroll
-                    for (int t = 0; t < DBW; ++t) mma(accS[fb][t], fk, vfr[kb][t]);
-                }
-            }
-        }
-        __syncthreads();  // every read of this chunk's LDS tiles is done
-        if constexpr (Cfg::NEED_K) {
-            zreg = znew;
-            if constexpr (MODE == MODE_CAUSAL) {
-                if (tid < F) sZ[tid] = znew;
-            }
-        }
+        compute(buf, n, t0);
     }
 
     // ---- state out
@@ -539,7 +606,40 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Sd[(16 * fb + 4 * g + r) * DV + d] = accS[fb][t][r];
                 }
-            if (tid < F) zd[tid] = zreg;
+            // fold the last chunk's key-feature sums (visible since its barrier)
+            if (c_beg < c_end) {
+                const int lb = (int)((c_end - 1 - c_beg) & 1);
+                const int n_last = (int)min((int64_t)C, a.n_len - (c_end - 1) * C);
+                const float dec = lam_pow(l2l, n_last);
+                const float* zp = sZp0 + lb * ZR * F;
+                if constexpr (RF) {
+                    if (tid < F) {
+                        float s = 0.f;
+#pragma unroll
+                        for (int w = 0; w < QB; ++w) s += zp[w * F + tid];
+                        zd[tid] = dec * sZ[tid] + s;
+                    }
+                } else {
+                    if (tid < VPRQ) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            float s = 0.f;
+#pragma unroll
+                            for (int w = 0; w < NW; ++w) s += zp[w * F + cg * VEC + e];
+                            zd[cg * VEC + e] = dec * zreg[e] + s;
+                        }
+                    }
+                }
+            } else {
+                if constexpr (RF) {
+                    if (tid < F) zd[tid] = sZ[tid];
+                } else {
+                    if (tid < VPRQ) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) zd[cg * VEC + e] = zreg[e];
+                    }
+                }
+            }
         }
     }
 }

@@ -23,8 +23,8 @@ enum FwdMode : int {
 };
 
 // One launch of the forward kernel covers tokens [n0, n0 + n_len) of every
-// (batch, head) row, cut into P segments of whole chunks (blockIdx.x = segment,
-// blockIdx.y = batch*head).
+// (batch, head) row, cut into P segments of cps whole chunks each (the last
+// may be shorter; blockIdx.x = segment, blockIdx.y = batch*head).
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -36,6 +36,7 @@ struct FwdArgs {
     int32_t BH;       // batch * heads
     int32_t H;
     int32_t P;        // segments
+    int64_t cps;      // chunks per segment
     int32_t out_f32;  // 1: y is fp32, 0: y has the input type
     float eps;
     float qk_scale;
@@ -62,7 +63,7 @@ struct ScanArgs {
     float* ws;               // slots [P][BH][F*d_v + F]
     int32_t P, BH, H, F, DV;
     int64_t n_len;           // tokens covered by the P segments
-    int32_t C;               // chunk size used to cut segments
+    int64_t seg_len;         // tokens per segment (cps * C); the last may be shorter
     int32_t causal;          // 1: exclusive decayed scan; 0: plain sum into slot 0
     const float* S_init;     // initial state (causal), user layout or carry slot
     const float* z_init;

@@ -43,7 +43,6 @@ __global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
     const float l2l = a.lam.log2lam[bh % a.H];
     float carry = 0.f;
     if (a.S_init) carry = isz ? a.z_init[bh * a.init_zstride + ez] : a.S_init[bh * a.init_stride + e];
-    const int64_t NC = (a.n_len + a.C - 1) / a.C;
     for (int s0 = 0; s0 < a.P; s0 += BATCH) {
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : 0.f;
@@ -51,8 +50,7 @@ __global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
         for (int b = 0; b < BATCH; ++b) {
             const int s = s0 + b;
             if (s < a.P) {
-                const int64_t c0 = (int64_t)s * NC / a.P, c1 = (int64_t)(s + 1) * NC / a.P;
-                const int64_t L = min(c1 * a.C, a.n_len) - c0 * a.C;
+                const int64_t L = min((int64_t)(s + 1) * a.seg_len, a.n_len) - (int64_t)s * a.seg_len;
                 base[s * slot] = carry;
                 carry = lam_pow(l2l, (int)L) * carry + loc[b];
             }
