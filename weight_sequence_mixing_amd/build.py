@@ -36,6 +36,9 @@ HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the kernels scale and mask
+    # them with vector ALU code, which cannot read AGPRs directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

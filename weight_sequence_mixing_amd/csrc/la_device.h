@@ -85,6 +85,23 @@ template <> __device__ __forceinline__ Frag<float> frag_acc<float>(const f32x4& 
     return f;
 }
 
+// A fragment whose every slot is 1: as the A operand it turns a product into
+// column sums of B over the k block (rows of the result all equal), as the B
+// operand into row sums of A.
+template <class T> __device__ __forceinline__ Frag<T> frag_ones();
+template <> __device__ __forceinline__ Frag<bf16> frag_ones<bf16>() {
+    Frag<bf16> f;
+    const bf16 one = (bf16)1.0f;
+    f.v = bf16x8{one, one, one, one, one, one, one, one};
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_ones<float>() {
+    Frag<float> f;
+    f.lo = f32x4{1.f, 1.f, 1.f, 1.f};
+    f.hi = f.lo;
+    return f;
+}
+
 // acc += A(16 x 32) * B(32 x 16) for one 32-wide k block.
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
@@ -166,7 +183,7 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 // lambda^k from log2(lambda), with lambda^0 = 1 also for lambda = 0.
 __device__ __forceinline__ float lam_pow(float log2lam, int k) {
-    return k == 0 ? 1.0f : exp2f((float)k * log2lam);
+    return k == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)k * log2lam);
 }
 
 // elu(x) + 1 ("From standard attention to linear attention" sec. 4.1).

@@ -27,6 +27,18 @@
 //     it stores with one 8-byte (bf16) or 16-byte (fp32) write.
 // Every wave computes the (small) score tiles it needs itself.
 //
+// The normaliser runs on the matrix cores too: z is an accumulator tile set
+// updated with an all-ones B operand (every column holds z), phi(Q) z is a
+// product with z broadcast as the A operand, and the row sums of P are a
+// product with an all-ones A operand -- so numerator and denominator see the
+// same bf16-rounded operands.
+//
+// Decay without a per-chunk multiply of the state: the true state is D * S^
+// with a scalar D that is the same in every thread.  A chunk multiplies D by
+// lambda^n and adds its keys with weights lambda^(n-1-j) / D; S^ (and z^) are
+// rescaled only when D would fall below 2^-60, which for lambda = 0 is every
+// chunk (then the weights are lambda^(n-1-j) themselves and 0^0 = 1).
+//
 // Per chunk, the tiles phi(Q), phi(K), lambda-weighted phi(K) and V are staged
 // row-major in LDS (see TileL in la_device.h); products that contract over
 // the token axis read them with transposing LDS reads.  The tiles are double
@@ -48,6 +60,9 @@ constexpr int chunk_len(int F) {
     return (sizeof(T) == 4 || F > 128) ? 32 : 64;
 }
 
+// log2 of the smallest pending decay factor before the state is rescaled
+constexpr float kLog2MinScale = -60.f;
+
 template <class T, int PHI, int DK, int F, int DV, int C, int NW, int MODE>
 struct FwdCfg {
     static constexpr int NT = NW * 64;
@@ -67,8 +82,6 @@ struct FwdCfg {
     static constexpr int NBF = RF ? 1 : 2;
     static constexpr int TQ = C * TileL<T, F>::STRIDE;   // elements of a feature tile
     static constexpr int TV = C * TileL<T, DV>::STRIDE;  // elements of a value tile
-    static constexpr int ZR = NW > QB ? NW : QB;         // rows of partial key-feature sums
-    static constexpr int DQR = RF ? M / 16 : 1;          // rows of partial phi(q).z sums
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t SZ_Q = NEED_Q ? size_t(NBF) * TQ * sizeof(T) : 0;
@@ -78,13 +91,7 @@ struct FwdCfg {
     static constexpr size_t SZ_KW = NEED_K ? size_t(NBF) * TQ * sizeof(T) : 0;
     static constexpr size_t OFF_V = al(OFF_KW + SZ_KW);
     static constexpr size_t SZ_V = NEED_K ? size_t(2) * TV * sizeof(T) : 0;
-    static constexpr size_t OFF_DQ = al(OFF_V + SZ_V);
-    static constexpr size_t SZ_DQ = NEED_Q ? size_t(2) * DQR * C * sizeof(float) : 0;
-    static constexpr size_t OFF_ZP = al(OFF_DQ + SZ_DQ);
-    static constexpr size_t SZ_ZP = NEED_K ? size_t(2) * ZR * F * sizeof(float) : 0;
-    static constexpr size_t OFF_Z = al(OFF_ZP + SZ_ZP);
-    static constexpr size_t SZ_Z = RF ? size_t(F) * sizeof(float) : 0;
-    static constexpr size_t OFF_XQ = al(OFF_Z + SZ_Z);
+    static constexpr size_t OFF_XQ = al(OFF_V + SZ_V);
     static constexpr size_t SZ_XQ = (RF && NEED_Q) ? size_t(C) * XLD * sizeof(T) : 0;
     static constexpr size_t OFF_XK = al(OFF_XQ + SZ_XQ);
     static constexpr size_t SZ_XK = (RF && NEED_K) ? size_t(C) * XLD * sizeof(T) : 0;
@@ -98,7 +105,6 @@ struct FwdCfg {
     static_assert(C % 32 == 0 && C >= 32, "chunk must be a multiple of 32");
     static_assert(F % 64 == 0 && DV % 64 == 0 && DK % 32 == 0, "head sizes");
     static_assert(DBW >= 1 && DB % NW == 0, "value columns must split over the waves");
-    static_assert(F <= NT && C <= NT, "thread mapping");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -108,8 +114,7 @@ la_fwd_kernel(const FwdArgs a)
 {
     using Cfg = FwdCfg<T, PHI, DK, F, DV, C, NW, MODE>;
     constexpr int NT = Cfg::NT, VEC = Cfg::VEC, M = Cfg::M, QB = Cfg::QB, FB = Cfg::FB;
-    constexpr int DBW = Cfg::DBW, XLD = Cfg::XLD, NBF = Cfg::NBF, TQ = Cfg::TQ, TV = Cfg::TV;
-    constexpr int ZR = Cfg::ZR, DQR = Cfg::DQR;
+    constexpr int DBW = Cfg::DBW, XLD = Cfg::XLD, TQ = Cfg::TQ, TV = Cfg::TV;
     constexpr bool RF = Cfg::RF;
     constexpr int KB = F / 32;                  // 32-wide feature blocks
     constexpr int CB = C / 32;                  // 32-wide token blocks
@@ -126,9 +131,6 @@ la_fwd_kernel(const FwdArgs a)
     T* const sK0 = (T*)(smem + Cfg::OFF_K);
     T* const sKw0 = (T*)(smem + Cfg::OFF_KW);
     T* const sV0 = (T*)(smem + Cfg::OFF_V);
-    float* const sDq0 = (float*)(smem + Cfg::OFF_DQ);
-    float* const sZp0 = (float*)(smem + Cfg::OFF_ZP);
-    float* const sZ = (float*)(smem + Cfg::OFF_Z);
     T* const sXq = (T*)(smem + Cfg::OFF_XQ);
     T* const sXk = (T*)(smem + Cfg::OFF_XK);
     float* const sXn = (float*)(smem + Cfg::OFF_XN);
@@ -144,23 +146,22 @@ la_fwd_kernel(const FwdArgs a)
     const T* kg = (const T*)a.k + ((int64_t)bh * a.N + a.n0) * DK;
     const T* vg = (const T*)a.v + ((int64_t)bh * a.N + a.n0) * DV;
     const float qs = a.qk_scale;
-    const float lamC = lam_pow(l2l, C);
-    const int cg = tid % VPRQ;       // this thread's feature group in the staging loops
+    const Frag<T> ones = frag_ones<T>();
 
-    // ---- decay tables of this lane (lambda is fixed per workgroup)
-    // mt[d][r]: mask and decay of score element (i = 16(jb+d) + l16, j = 16 jb + 4g + r)
-    float mt[QB][4];
-    // lq[ib]: lambda^(i+1) for the lane's query row i = 16 ib + l16
-    float lq[QB];
+    // ---- decay tables of this lane (lambda is fixed per workgroup).  Score
+    // element (i = 16 ib + l16, j = 16 jb + 4 g + r) is weighted by lambda^(i-j):
+    //   jb == ib: m0[r] = lambda^(l16-4g-r), or 0 above the diagonal;
+    //   jb <  ib: m1[r] * lambda^(16 (ib-jb-1)), m1[r] = lambda^(16+l16-4g-r)
+    // (every exponent is >= 0, so nothing overflows for small lambda).
+    // Query row i reads the carried state with lambda^(i+1) = lq1 * lambda^(16 ib).
+    float m0[4], m1[4];
 #pragma unroll
-    for (int d = 0; d < QB; ++d) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int e = 16 * d + l16 - 4 * g - r;
-            mt[d][r] = e < 0 ? 0.f : (decay ? lam_pow(l2l, e) : 1.f);
-        }
-        lq[d] = decay ? lam_pow(l2l, 16 * d + l16 + 1) : 1.f;
+    for (int r = 0; r < 4; ++r) {
+        const int e = l16 - 4 * g - r;
+        m0[r] = e < 0 ? 0.f : (decay ? lam_pow(l2l, e) : 1.f);
+        m1[r] = decay ? lam_pow(l2l, 16 + e) : 1.f;
     }
+    const float lq1 = decay ? lam_pow(l2l, l16 + 1) : 1.f;
 
     // ---- random-feature directions into LDS (once per workgroup)
     if constexpr (RF) {
@@ -179,50 +180,43 @@ la_fwd_kernel(const FwdArgs a)
         }
     }
 
-    // ---- carried state: accumulator tiles (fb, this wave's d-blocks); z
-    f32x4 accS[FB][DBW];
+    // ---- carried state: S tiles (fb, this wave's d-blocks) and z tiles
+    // (lane (g, l16) of z tile fb holds z[16 fb + 4 g + r] in every column)
+    f32x4 accS[FB][DBW], accZ[FB];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+    for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
         for (int t = 0; t < DBW; ++t) accS[fb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // elu+1: every thread tracks z for its own VEC features cg*VEC.. (all the
-    // staging needs); random features keep z in LDS.
-    float zreg[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) zreg[e] = 0.f;
+        accZ[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if constexpr (MODE != MODE_LOCAL) {
         if (a.S_src) {
             const float* Sb = a.S_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_stride;
             const float* zb = a.z_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_zstride;
 #pragma unroll
-            for (int fb = 0; fb < FB; ++fb)
+            for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
                 for (int t = 0; t < DBW; ++t) {
                     const int d = 16 * (wave * DBW + t) + l16;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) accS[fb][t][r] = Sb[(16 * fb + 4 * g + r) * DV + d];
                 }
-            if constexpr (RF) {
-                if (tid < F) sZ[tid] = zb[tid];
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) zreg[e] = zb[cg * VEC + e];
+                accZ[fb] = *(const f32x4*)(zb + 16 * fb + 4 * g);
             }
-        } else if constexpr (RF) {
-            if (tid < F) sZ[tid] = 0.f;
         }
-    } else if constexpr (RF) {
-        if (tid < F) sZ[tid] = 0.f;
     }
-    // S as bf16 / fp32 operand fragments (A operand of O^T = S^T phi(Q)^T)
-    Frag<T> sf[KB][DBW];
+    // S and z as operand fragments (A operands of S^T phi(Q)^T and z phi(Q)^T)
+    Frag<T> sf[KB][DBW], zf[KB];
     auto convert_state = [&]() {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int t = 0; t < DBW; ++t) sf[kb][t] = frag_acc<T>(accS[2 * kb][t], accS[2 * kb + 1][t]);
+            zf[kb] = frag_acc<T>(accZ[2 * kb], accZ[2 * kb + 1]);
+        }
     };
     if constexpr (Cfg::NEED_Q) convert_state();
+    float log2D = 0.f;  // the true state is 2^log2D times the accumulators
 
     // ---- global -> register prefetch of one chunk.  Rows past the end of the
     // sequence re-read the last valid row (always in bounds) and are replaced
@@ -256,57 +250,38 @@ la_fwd_kernel(const FwdArgs a)
         }
     };
 
-    // raw 16-byte vector -> row-major tile (no conversion)
-    auto put_raw = [&](T* tile, int stride_w, int row, int col, const uint4& u) {
+    // raw 16-byte vector -> row-major value tile (no conversion)
+    auto put_raw = [&](T* tile, int row, int col, const uint4& u) {
         if constexpr (sizeof(T) == 2) {
-            (void)stride_w;
             *(uint2*)(tile + TVL::off(row, col)) = uint2{u.x, u.y};
             *(uint2*)(tile + TVL::off(row, col + 4)) = uint2{u.z, u.w};
         } else {
-            *(uint4*)(tile + row * stride_w + col) = u;
+            *(uint4*)(tile + TVL::off(row, col)) = u;
         }
     };
-    // VEC floats -> row-major feature tile (rounded to T); returns the rounded values
-    auto put_feat = [&](T* tile, int row, int col, float* p) {
+    // VEC floats -> row-major feature tile (rounded to T)
+    auto put_feat = [&](T* tile, int row, int col, const float* p) {
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-            st4(tile + TF::off(row, col + e), p[e], p[e + 1], p[e + 2], p[e + 3]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) p[e + u] = to_f32(from_f32<T>(p[e + u]));
-        }
+        for (int e = 0; e < VEC; e += 4) st4(tile + TF::off(row, col + e), p[e], p[e + 1], p[e + 2], p[e + 3]);
     };
 
-    // ---- staging of one chunk from registers.  elu+1: feature map, phi(q).z,
-    // weighted keys and their column sums; random features: raw rows and norms.
-    auto stage = [&](int buf, int n, bool first) {
+    // lambda^k / 2^kw_l2 with lambda^0 = 1 also for lambda = 0
+    auto key_weight = [&](int k, float kw_l2) {
+        return k == 0 ? __builtin_amdgcn_exp2f(-kw_l2) : __builtin_amdgcn_exp2f((float)k * l2l - kw_l2);
+    };
+
+    // ---- staging of one chunk from registers.  elu+1: the feature map and
+    // the weighted keys; random features: raw rows and their squared norms.
+    // kw_l2: log2 of the key weight of token 0 relative to lambda^(n-1-j),
+    // i.e. weight_j = 2^((n-1-j) log2 lambda - kw_l2) (kw_l2 = 0 after a rescale).
+    auto stage = [&](int buf, int n, float kw_l2) {
         T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         T* const sK = sK0 + (RF ? 0 : buf * TQ);
         T* const sKw = sKw0 + (RF ? 0 : buf * TQ);
         T* const sV = sV0 + buf * TV;
-        if constexpr (Cfg::NEED_K) {
-            // fold the previous chunk's key-feature sums into z
-            const float* zp = sZp0 + (buf ^ 1) * ZR * F;
-            if constexpr (RF) {
-                if (!first && tid < F) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int w = 0; w < QB; ++w) s += zp[w * F + tid];
-                    sZ[tid] = lamC * sZ[tid] + s;
-                }
-            } else {
-                if (!first) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        float s = 0.f;
-#pragma unroll
-                        for (int w = 0; w < NW; ++w) s += zp[w * F + cg * VEC + e];
-                        zreg[e] = lamC * zreg[e] + s;
-                    }
-                }
-            }
-        }
+        const bool tail = n < C;
+        const int cg = tid % VPRQ;
         if constexpr (Cfg::NEED_Q) {
-            float* const sDq = sDq0 + buf * DQR * C;
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRQ;
@@ -324,20 +299,16 @@ la_fwd_kernel(const FwdArgs a)
                 } else {
                     float p[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) p[e] = (j < n) ? phi_elu1<T>(x[e]) : 0.f;
-                    put_feat(sQ, j, cg * VEC, p);
-                    float dq = 0.f;
+                    for (int e = 0; e < VEC; ++e) p[e] = phi_elu1<T>(x[e]);
+                    if (tail && j >= n) {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) dq += p[e] * zreg[e];
-                    dq = wave_sum_xor(dq, 1, VPRQ / 2);
-                    if (cg == 0) sDq[j] = dq;
+                        for (int e = 0; e < VEC; ++e) p[e] = 0.f;
+                    }
+                    put_feat(sQ, j, cg * VEC, p);
                 }
             }
         }
         if constexpr (Cfg::NEED_K) {
-            float zacc[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) zacc[e] = 0.f;
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRQ;
@@ -355,53 +326,38 @@ la_fwd_kernel(const FwdArgs a)
                 } else {
                     float p[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) p[e] = (j < n) ? phi_elu1<T>(x[e]) : 0.f;
+                    for (int e = 0; e < VEC; ++e) p[e] = phi_elu1<T>(x[e]);
+                    if (tail && j >= n) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) p[e] = 0.f;
+                    }
                     if (!decay) {
                         // unweighted keys serve the scores and the state update
                         put_feat(Cfg::NEED_KROW ? sK : sKw, j, cg * VEC, p);
                     } else {
-                        const float w = (j < n) ? lam_pow(l2l, n - 1 - j) : 0.f;
-                        if constexpr (Cfg::NEED_KROW) {
-                            float pk[VEC];
+                        if constexpr (Cfg::NEED_KROW) put_feat(sK, j, cg * VEC, p);
+                        const float w = (j < n) ? key_weight(n - 1 - j, kw_l2) : 0.f;
+                        float pw[VEC];
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e) pk[e] = p[e];
-                            put_feat(sK, j, cg * VEC, pk);
-                        }
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) p[e] *= w;
-                        put_feat(sKw, j, cg * VEC, p);
+                        for (int e = 0; e < VEC; ++e) pw[e] = p[e] * w;
+                        put_feat(sKw, j, cg * VEC, pw);
                     }
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) zacc[e] += p[e];
-                }
-            }
-            if constexpr (!RF) {
-                // column sums over the rows this wave staged; lanes < VPRQ hold them
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    for (int m = VPRQ; m < 64; m <<= 1) zacc[e] += __shfl_xor(zacc[e], m, 64);
-                if (lane < VPRQ) {
-                    float* zp = sZp0 + buf * ZR * F + wave * F + cg * VEC;
-#pragma unroll
-                    for (int e = 0; e < VEC; e += 4) *(f32x4*)(zp + e) = f32x4{zacc[e], zacc[e + 1], zacc[e + 2], zacc[e + 3]};
                 }
             }
 #pragma unroll
             for (int r = 0; r < RV; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
-                put_raw(sV, TVL::STRIDE, j, c4 * VEC, rv[r]);
+                put_raw(sV, j, c4 * VEC, rv[r]);
             }
         }
     };
 
     // ---- random features on the matrix cores: U^T = omega x^T, then cos/sin,
     // written row-major into the feature tiles
-    auto rf_features = [&](int buf, int n) {
+    auto rf_features = [&](int n, float kw_l2) {
         if constexpr (RF) {
             constexpr int TILES = (M / 16) * QB;
             const float cnorm = rsqrtf((float)M);
-            float* const sDq = sDq0 + buf * DQR * C;
-            float* const zp = sZp0 + buf * ZR * F;
             constexpr int NPASS = (Cfg::NEED_Q ? 1 : 0) + (Cfg::NEED_K ? 1 : 0);
             for (int pass = 0; pass < NPASS; ++pass) {
                 const bool isq = Cfg::NEED_Q && pass == 0;
@@ -423,7 +379,7 @@ la_fwd_kernel(const FwdArgs a)
                             mma(acc, frag_rm(om, XLD, 16 * rb + l16, 32 * kb, g), b);
                         }
                     }
-                    // acc[r] = u_{f0+r}(x_i) / qs with f0 = 16 rb + 4 g, token i = 16 ib + l16
+                    // acc[r] = (omega x_i)_{f0+r} with f0 = 16 rb + 4 g, token i = 16 ib + l16
                     const int i = 16 * ib + l16, f0 = 16 * rb + 4 * g;
                     const float cfac = (i < n) ? exp_rf<T>(-0.5f * qs * qs * xn[i]) * cnorm : 0.f;
                     float cs[4], sn[4];
@@ -436,52 +392,28 @@ la_fwd_kernel(const FwdArgs a)
                     if (isq) {
                         st4(sQ0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
                         st4(sQ0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
-                        // phi(q_i).z over these 8 features, summed over the 4 lane groups
-                        const f32x4 zc = *(const f32x4*)(sZ + f0), zs = *(const f32x4*)(sZ + M + f0);
-                        float dq = 0.f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            dq += to_f32(from_f32<T>(cs[r])) * zc[r] + to_f32(from_f32<T>(sn[r])) * zs[r];
-                        dq += __shfl_xor(dq, 16, 64);
-                        dq += __shfl_xor(dq, 32, 64);
-                        if (g == 0) sDq[rb * C + i] = dq;
                     } else {
                         if constexpr (Cfg::NEED_KROW) {
                             st4(sK0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
                             st4(sK0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
                         }
-                        const float w = (i < n) ? (decay ? lam_pow(l2l, n - 1 - i) : 1.f) : 0.f;
-                        float wc[4], ws[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            wc[r] = to_f32(from_f32<T>(w * cs[r]));
-                            ws[r] = to_f32(from_f32<T>(w * sn[r]));
-                        }
-                        st4(sKw0 + TF::off(i, f0), wc[0], wc[1], wc[2], wc[3]);
-                        st4(sKw0 + TF::off(i, M + f0), ws[0], ws[1], ws[2], ws[3]);
-                        // column sums over the 16 tokens of this tile
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            wc[r] = wave_sum_xor(wc[r], 1, 8);
-                            ws[r] = wave_sum_xor(ws[r], 1, 8);
-                        }
-                        if (l16 == 0) {
-                            *(f32x4*)(zp + ib * F + f0) = f32x4{wc[0], wc[1], wc[2], wc[3]};
-                            *(f32x4*)(zp + ib * F + M + f0) = f32x4{ws[0], ws[1], ws[2], ws[3]};
-                        }
+                        const float w = (i < n) ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
+                        st4(sKw0 + TF::off(i, f0), w * cs[0], w * cs[1], w * cs[2], w * cs[3]);
+                        st4(sKw0 + TF::off(i, M + f0), w * sn[0], w * sn[1], w * sn[2], w * sn[3]);
                     }
                 }
             }
         }
     };
 
-    // ---- outputs and state update of one staged chunk
-    auto compute = [&](int buf, int n, int64_t t0) {
+    // ---- outputs and state update of one staged chunk.  dscale: 2^log2D of
+    // the state the chunk reads; rescale: factor applied to the accumulators
+    // before this chunk's keys are added (1 when none).
+    auto compute = [&](int buf, int n, int64_t t0, float dscale, bool do_rescale, float rescale) {
         const T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         const T* const sK = sK0 + (RF ? 0 : buf * TQ);
         const T* const sKw = (Cfg::NEED_KROW && !decay && !RF) ? sK : sKw0 + (RF ? 0 : buf * TQ);
         const T* const sV = sV0 + buf * TV;
-        const float* const sDq = sDq0 + buf * DQR * C;
         // V column fragments: A operand of V^T P^T and B operand of the state update
         Frag<T> vf[Cfg::NEED_K ? CB : 1][DBW];
         if constexpr (Cfg::NEED_K) {
@@ -495,38 +427,46 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int ib = 0; ib < QB; ++ib) {
                 const int i = 16 * ib + l16;
+                const float lqi = decay ? lq1 * lam_pow(l2l, 16 * ib) : 1.f;
                 Frag<T> qf[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F>(sQ, i, kb, g);
-                // scores of query block ib against key blocks jb <= ib, as P^T fragments
-                Frag<T> pf[CB];
-                float rs = 0.f;
-                if constexpr (MODE == MODE_CAUSAL) {
-                    f32x4 pt[QB];
+                // phi(q_i).z (every row of the tile holds it)
+                f32x4 dq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int jb = 0; jb < QB; ++jb) {
+                for (int kb = 0; kb < KB; ++kb) mma(dq, zf[kb], qf[kb]);
+                float den = dq[0];
+                Frag<T> pf[CB];
+                if constexpr (MODE == MODE_CAUSAL) {
+                    // scores of query block ib against key blocks jb <= ib, as P^T fragments
+                    f32x4 pt[2 * CB];
+#pragma unroll
+                    for (int jb = 0; jb < 2 * CB; ++jb) {
                         pt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
                         if (jb <= ib) {
 #pragma unroll
                             for (int kb = 0; kb < KB; ++kb)
                                 mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                            if (jb == ib) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                pt[jb][r] = to_f32(from_f32<T>(pt[jb][r] * mt[ib - jb][r]));
-                                rs += pt[jb][r];
+                                for (int r = 0; r < 4; ++r) pt[jb][r] *= m0[r];
+                            } else if (decay) {
+                                const float dj = lam_pow(l2l, 16 * (ib - jb - 1));
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) pt[jb][r] *= m1[r] * dj;
                             }
                         }
                     }
+                    f32x4 rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kb = 0; kb < CB; ++kb) pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
-                    rs += __shfl_xor(rs, 16, 64);
-                    rs += __shfl_xor(rs, 32, 64);
+                    for (int kb = 0; kb < CB; ++kb) {
+                        pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
+                        if (2 * kb <= ib) mma(rs, ones, pf[kb]);
+                    }
+                    den = rs[0] + lqi * dscale * den;
                 }
-                float dq = 0.f;
-#pragma unroll
-                for (int q = 0; q < DQR; ++q) dq += sDq[q * C + i];
-                const float den = (MODE == MODE_CAUSAL) ? rs + lq[ib] * dq : dq;
                 const float inv = fast_rcp(den + eps);
+                const float sc = (MODE == MODE_CAUSAL) ? lqi * dscale * inv : inv;
                 const int64_t yrow = (int64_t)bh * a.N + a.n0 + t0 + i;
 #pragma unroll
                 for (int t = 0; t < DBW; ++t) {
@@ -534,27 +474,33 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) mma(o, sf[kb][t], qf[kb]);
                     if constexpr (MODE == MODE_CAUSAL) {
-                        o *= lq[ib];
+                        // o = (lambda^(i+1) D S^T phi(q) + V^T P^T) / den
+                        o *= sc;
+                        f32x4 oi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int kb = 0; kb < CB; ++kb)
-                            if (2 * kb <= ib) mma(o, vf[kb][t], pf[kb]);
+                            if (2 * kb <= ib) mma(oi, vf[kb][t], pf[kb]);
+                        o += oi * inv;
+                    } else {
+                        o *= sc;
                     }
                     if (i < n) {
                         const int64_t yo = yrow * DV + 16 * (wave * DBW + t) + 4 * g;
-                        if (a.out_f32) st4((float*)a.y + yo, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-                        else st4((T*)a.y + yo, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+                        if (a.out_f32) st4((float*)a.y + yo, o[0], o[1], o[2], o[3]);
+                        else st4((T*)a.y + yo, o[0], o[1], o[2], o[3]);
                     }
                 }
             }
         }
-        // state carry: S <- lambda^n S + (w phi(K))^T V
+        // state carry: S^ <- S^ + (w phi(K))^T V, z^ <- z^ + (w phi(K))^T 1
         if constexpr (Cfg::NEED_K) {
-            if (decay) {
-                const float dec = lam_pow(l2l, n);
+            if (do_rescale) {
 #pragma unroll
-                for (int fb = 0; fb < FB; ++fb)
+                for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
-                    for (int t = 0; t < DBW; ++t) accS[fb][t] *= dec;
+                    for (int t = 0; t < DBW; ++t) accS[fb][t] *= rescale;
+                    accZ[fb] *= rescale;
+                }
             }
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb) {
@@ -563,6 +509,7 @@ la_fwd_kernel(const FwdArgs a)
                     const Frag<T> kf = ColRead<T, F>::get(sKw, 32 * kb, 16 * fb, lane);
 #pragma unroll
                     for (int t = 0; t < DBW; ++t) mma(accS[fb][t], kf, vf[kb][t]);
+                    mma(accZ[fb], kf, ones);
                 }
             }
             if constexpr (Cfg::NEED_Q) convert_state();
@@ -571,22 +518,37 @@ la_fwd_kernel(const FwdArgs a)
 
     // ---- main loop over the segment's chunks
     if (c_beg < c_end) load_chunk(c_beg);
-    if constexpr (RF) __syncthreads();  // omega and z in LDS
+    if constexpr (RF) __syncthreads();  // omega in LDS
     for (int64_t c = c_beg; c < c_end; ++c) {
         const int buf = (int)((c - c_beg) & 1);
         const int64_t t0 = c * C;
         const int n = (int)min((int64_t)C, a.n_len - t0);
-        stage(buf, n, c == c_beg);
+        // decay bookkeeping (uniform): pending factor 2^log2D * lambda^n
+        const float dscale = decay ? exp2f(log2D) : 1.f;
+        bool do_rescale = false;
+        float rescale = 1.f, kw_l2 = 0.f;
+        if (decay) {
+            const float cand = log2D + (float)n * l2l;
+            if (cand >= kLog2MinScale) {
+                kw_l2 = cand;
+                log2D = cand;
+            } else {
+                do_rescale = true;
+                rescale = exp2f(cand);  // 0 for lambda = 0
+                log2D = 0.f;
+            }
+        }
+        stage(buf, n, kw_l2);
         if (c + 1 < c_end) load_chunk(c + 1);
         __syncthreads();
         if constexpr (RF) {
-            rf_features(buf, n);
+            rf_features(n, kw_l2);
             __syncthreads();
         }
-        compute(buf, n, t0);
+        compute(buf, n, t0, dscale, do_rescale, rescale);
     }
 
-    // ---- state out
+    // ---- state out (true scale)
     if constexpr (MODE != MODE_QUERY) {
         float* Sd = nullptr;
         float* zd = nullptr;
@@ -598,47 +560,16 @@ la_fwd_kernel(const FwdArgs a)
             zd = a.z_dst + (int64_t)bh * a.dst_zstride;
         }
         if (Sd) {
+            const float ds = decay ? exp2f(log2D) : 1.f;
 #pragma unroll
-            for (int fb = 0; fb < FB; ++fb)
+            for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
                 for (int t = 0; t < DBW; ++t) {
                     const int d = 16 * (wave * DBW + t) + l16;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Sd[(16 * fb + 4 * g + r) * DV + d] = accS[fb][t][r];
+                    for (int r = 0; r < 4; ++r) Sd[(16 * fb + 4 * g + r) * DV + d] = ds * accS[fb][t][r];
                 }
-            // fold the last chunk's key-feature sums (visible since its barrier)
-            if (c_beg < c_end) {
-                const int lb = (int)((c_end - 1 - c_beg) & 1);
-                const int n_last = (int)min((int64_t)C, a.n_len - (c_end - 1) * C);
-                const float dec = lam_pow(l2l, n_last);
-                const float* zp = sZp0 + lb * ZR * F;
-                if constexpr (RF) {
-                    if (tid < F) {
-                        float s = 0.f;
-#pragma unroll
-                        for (int w = 0; w < QB; ++w) s += zp[w * F + tid];
-                        zd[tid] = dec * sZ[tid] + s;
-                    }
-                } else {
-                    if (tid < VPRQ) {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) {
-                            float s = 0.f;
-#pragma unroll
-                            for (int w = 0; w < NW; ++w) s += zp[w * F + cg * VEC + e];
-                            zd[cg * VEC + e] = dec * zreg[e] + s;
-                        }
-                    }
-                }
-            } else {
-                if constexpr (RF) {
-                    if (tid < F) zd[tid] = sZ[tid];
-                } else {
-                    if (tid < VPRQ) {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) zd[cg * VEC + e] = zreg[e];
-                    }
-                }
+                if (wave == 0 && l16 == 0) *(f32x4*)(zd + 16 * fb + 4 * g) = accZ[fb] * ds;
             }
         }
     }
