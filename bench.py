@@ -258,6 +258,31 @@ def workload4_decode(ctx, steps=1024):
     }
 
 
+def state_copy(ctx, B=256, H=32, F=128, D=128, steps=50):
+    """Reference stream: the library's state copy (la_forward_causal with N=0
+    and S_in -> S_out) over a decode-sized fp32 state; bytes = read + write."""
+    torch, la = ctx.torch, ctx.la
+    S_in = torch.randn(B, H, F, D, device=ctx.dev)
+    z_in = torch.rand(B, H, F, device=ctx.dev)
+    S_out, z_out = torch.empty_like(S_in), torch.empty_like(z_in)
+    q = torch.empty(B, H, 0, D, dtype=torch.bfloat16, device=ctx.dev)
+    y = torch.empty_like(q)
+
+    def step():
+        la.la_forward_causal(q, q, q, y, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
+
+    ms = ctx.time_steps(step, steps=steps, warmup=5)
+    kt = ctx.kernel_times(step, steps=steps, launches_per_step=2)
+    assert torch.equal(S_out, S_in) and torch.equal(z_out, z_in)
+    cid = la.KERNEL_IDS["copy"]
+    dev_ms = kt[cid][0] * kt[cid][1]
+    nbytes = 2 * 4 * (B * H * F * D + B * H * F)
+    return {"workload": "state copy fp32 %dx%dx%dx%d" % (B, H, F, D), "bytes_per_step": nbytes,
+            "ms_per_step": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "device_GBps": round(nbytes / (dev_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, inp, min_seconds=10.0, max_passes=400):
     """The fp64 oracle, as it stands, on the host cores: whole passes over the
     headline workload, repeated until at least `min_seconds` of CPU work."""
@@ -283,7 +308,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["w2", "w3", "w4", "w5"], help="run one workload (profiling)")
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w5", "copy"], help="run one workload (profiling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -294,7 +319,7 @@ def main():
     ctx = Ctx(args.steps, args.warmup)
     import seeded_inputs as si
     if args.only and args.only != "w2":
-        fn = {"w3": workload3, "w4": workload4_decode, "w5": workload5}[args.only]
+        fn = {"w3": workload3, "w4": workload4_decode, "w5": workload5, "copy": state_copy}[args.only]
         log("running", args.only)
         print(json.dumps({"only": args.only, "result": fn(ctx)}), flush=True)
         return

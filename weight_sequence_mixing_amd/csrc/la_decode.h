@@ -8,18 +8,31 @@
 //   y  = phi(q)^T S / (phi(q)^T z + eps)          (update, then query)
 //
 // The step is bound by HBM: 8 bytes of state traffic per state element
-// against 4 flops.  One 256-thread workgroup streams one head-state: each
-// thread owns a 4-column quad of F/RG rows, issues all of its 16-byte loads
-// before the first use so that many bytes are in flight, updates them in
-// registers, writes them back and accumulates phi(q)^T S for its columns.
-// Partial sums over rows are reduced across lanes and then across waves
-// through LDS.
+// against 4 flops.  The value columns of a head-state may be split over DS
+// workgroups of 256 threads (see decode_split).  Each thread owns a 4-column
+// quad of F/RG rows, issues all of its 16-byte loads before the first use so
+// that many bytes are in flight, updates them in registers, writes them back
+// and accumulates phi(q)^T S for its columns; partial sums over rows are reduced across lanes
+// and then across waves through LDS.  Every workgroup recomputes the new z
+// for its denominator; the first column slice writes it back.
+//
+// Head-states are visited in ascending order on even calls and descending
+// order on odd ones (DecArgs::reverse): when back-to-back steps run over a
+// state larger than the last-level cache, the part written last by one step
+// is read first by the next, while it may still be cached.  The order does
+// not change any result.
 #pragma once
 
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace la {
+
+// Column slices per head-state.  Two 32 KB slices per d_v = 128 head-state
+// measured slower than one 64 KB workgroup (the per-workgroup feature map and
+// reductions are paid twice), so every head-state is one workgroup.
+template <int DV>
+constexpr int decode_split() { return 1; }
 
 template <class T, int PHI, int DK, int F, int DV>
 __global__ void __launch_bounds__(256)
@@ -28,23 +41,27 @@ la_decode_kernel(const DecArgs a)
     constexpr int NT = 256;
     constexpr bool RF = PHI == LA_PHI_TRIG_RF;
     constexpr int M = RF ? F / 2 : 0;
-    constexpr int CQ = DV / 4;      // column quads
+    constexpr int DS = decode_split<DV>();
+    constexpr int DW = DV / DS;     // value columns of this workgroup
+    constexpr int CQ = DW / 4;      // column quads
     constexpr int RG = NT / CQ;     // row groups
     constexpr int RPT = F / RG;     // rows per thread
-    static_assert(F <= NT && DV <= NT && F % RG == 0, "decode thread mapping");
+    static_assert(F <= NT && DV <= NT && F % RG == 0 && NT % CQ == 0, "decode thread mapping");
 
-    __shared__ float sPq[F], sPk[F], sV[DV];
+    __shared__ float sPq[F], sPk[F], sV[DW];
     __shared__ float sX[RF ? 2 * DK : 1];
     __shared__ f32x4 sRed[NT / 64][CQ];
     __shared__ float sDen[NT / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bh = blockIdx.x, h = bh % a.H;
+    const int blk = a.reverse ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int bh = blk / DS, part = blk % DS, h = bh % a.H;
+    const int d0 = part * DW;
     const float lam = a.lam.lam[h];
     const T* q = (const T*)a.q + (int64_t)bh * DK;
     const T* k = (const T*)a.k + (int64_t)bh * DK;
     const T* v = (const T*)a.v + (int64_t)bh * DV;
-    float* Sb = a.S + (int64_t)bh * F * DV;
+    float* Sb = a.S + (int64_t)bh * F * DV + d0;
     float* zb = a.z + (int64_t)bh * F;
 
     const int cq = tid % CQ, rg = tid / CQ;
@@ -60,7 +77,7 @@ la_decode_kernel(const DecArgs a)
             sX[tid] = to_f32(q[tid]);
             sX[DK + tid] = to_f32(k[tid]);
         }
-        if (tid < DV) sV[tid] = to_f32(v[tid]);
+        if (tid < DW) sV[tid] = to_f32(v[d0 + tid]);
         __syncthreads();
         if (tid < 2 * M) {
             const int which = tid / M, r = tid % M;
@@ -84,7 +101,7 @@ la_decode_kernel(const DecArgs a)
             sPq[tid] = phi_elu1<T>(to_f32(q[tid]));
             sPk[tid] = phi_elu1<T>(to_f32(k[tid]));
         }
-        if (tid < DV) sV[tid] = to_f32(v[tid]);
+        if (tid < DW) sV[tid] = to_f32(v[d0 + tid]);
     }
     __syncthreads();
 
@@ -102,7 +119,7 @@ la_decode_kernel(const DecArgs a)
     float dz = 0.f;
     if (tid < F) {
         zf = lam * zf + sPk[tid];
-        zb[tid] = zf;
+        if (part == 0) zb[tid] = zf;
         dz = sPq[tid] * zf;
     }
     // reduce over row groups: lanes of one wave first, then waves
@@ -124,7 +141,7 @@ la_decode_kernel(const DecArgs a)
             den += sDen[w];
         }
         const float inv = 1.0f / (den + a.eps);
-        const int64_t yo = (int64_t)bh * DV + 4 * tid;
+        const int64_t yo = (int64_t)bh * DV + d0 + 4 * tid;
         if (a.out_f32) {
             *(f32x4*)((float*)a.y + yo) = num * inv;
         } else {
@@ -137,7 +154,8 @@ la_decode_kernel(const DecArgs a)
 template <class T, int PHI, int DK, int F, int DV>
 hipError_t dec_launch(const DecArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((la_decode_kernel<T, PHI, DK, F, DV>), dim3((unsigned)a.BH), dim3(256), 0, stream, a);
+    const unsigned blocks = (unsigned)a.BH * (unsigned)decode_split<DV>();
+    hipLaunchKernelGGL((la_decode_kernel<T, PHI, DK, F, DV>), dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -86,6 +86,7 @@ struct DecArgs {
     float eps;
     float qk_scale;
     const float* omega;
+    int32_t reverse;   // 1: visit head-states in descending order
     LamTable lam;
 };
 
