@@ -283,6 +283,76 @@ def state_copy(ctx, B=256, H=32, F=128, D=128, steps=50):
             "hbm_frac": round(nbytes / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+# ---- HBM traffic from rocprofv3 counter runs -------------------------------
+# rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) runs of `bench.py --only TAG`
+# write <dir>/<counter>_<tag>/**/*_counter_collection.csv.  The counters are
+# scaled by what they read for the library's state copy, whose bytes are known.
+COUNTER_TAGS = {"copy": None, "w2": 2, "w3": 3, "w4": 4, "w5": 5}
+
+
+def _kernel_label(mangled):
+    if "la_copy_kernel" in mangled:
+        return "la_copy_kernel"
+    if "la_decode_kernel" in mangled:
+        return "la_decode_kernel"
+    if "la_scan_kernel" in mangled:
+        return "la_scan_kernel"
+    if "la_fwd_kernel" in mangled:
+        # the mode is the last template argument, mangled (...ELi1EEEvNS_7FwdArgsE)
+        # or demangled (..., 4, 1>(la::FwdArgs))
+        if "EEEvNS_7FwdArgsE" in mangled:
+            mode = mangled.split("EEEvNS_7FwdArgsE")[0].rsplit("ELi", 1)[-1]
+        else:
+            mode = mangled.split(">(")[0].rsplit(",", 1)[-1].strip()
+        return {"0": "la_fwd_kernel (segment state)", "1": "la_fwd_kernel (causal output)",
+                "2": "la_fwd_kernel (non-causal output)"}.get(mode, "la_fwd_kernel")
+    return None
+
+
+def _counter_means(root, counter, tag):
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(root, "%s_%s" % (counter.lower(), tag), "**", "*_counter_collection.csv"),
+                          recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                label = _kernel_label(row["Kernel_Name"])
+                if label:
+                    vals.setdefault(label, []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def traffic_from(root):
+    """Write profiles/traffic_counters.json from counter runs under `root`."""
+    import seeded_inputs as si
+    fetch = {t: _counter_means(root, "FETCH_SIZE", t) for t in COUNTER_TAGS}
+    write = {t: _counter_means(root, "WRITE_SIZE", t) for t in COUNTER_TAGS}
+    # calibration: the largest copy dispatch moves the fp32 state 256x32x128x128
+    state_bytes = 4 * 256 * 32 * 128 * 128
+    f_copy = max(fetch["copy"]["la_copy_kernel"]) * 1024.0
+    w_copy = max(write["copy"]["la_copy_kernel"]) * 1024.0
+    cal = {"read_factor": state_bytes / f_copy, "write_factor": state_bytes / w_copy,
+           "copy_fetch_KiB": f_copy / 1024, "copy_write_KiB": w_copy / 1024, "copy_bytes_each_way": state_bytes}
+    out = {"source_hash": source_hash(), "calibration": cal, "per_launch_bytes": {}, "raw_KiB": {}}
+    for tag, idx in COUNTER_TAGS.items():
+        if idx is None:
+            continue
+        name = si.workload(idx).name
+        for label in sorted(set(fetch[tag]) & set(write[tag])):
+            fr = float(np.mean(fetch[tag][label]))
+            wr = float(np.mean(write[tag][label]))
+            key = "%s/%s" % (name, label)
+            out["per_launch_bytes"][key] = int(fr * 1024 * cal["read_factor"] + wr * 1024 * cal["write_factor"])
+            out["raw_KiB"][key] = {"FETCH_SIZE": fr, "WRITE_SIZE": wr}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    return out
+
+
 def cpu_baseline(wl, inp, min_seconds=10.0, max_passes=400):
     """The fp64 oracle, as it stands, on the host cores: whole passes over the
     headline workload, repeated until at least `min_seconds` of CPU work."""
@@ -309,7 +379,13 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["w2", "w3", "w4", "w5", "copy"], help="run one workload (profiling)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="host only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR into "
+                         "profiles/traffic_counters.json and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from(args.traffic_from), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         log("bench.py measures one GPU: this build has no multi-GPU path "

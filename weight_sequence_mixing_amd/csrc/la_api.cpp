@@ -43,7 +43,7 @@ la_status hip_fail(hipError_t e, const char* what)
     return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// ---- per-launch event brackets for la_profile_begin / la_profile_end
+// ---- per-launch timing for la_profile_begin / la_profile_end
 struct Profiler {
     bool on = false;
     int max = 0;
@@ -52,30 +52,41 @@ struct Profiler {
     std::vector<int> ids;
 };
 thread_local Profiler g_prof;
+thread_local LaunchEvents g_launch_ev = {nullptr, nullptr, false};
 
-void prof_before(int id, hipStream_t s)
+void prof_before(int id)
 {
     if (!g_prof.on || g_prof.used >= g_prof.max) return;
-    hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+    g_launch_ev = {g_prof.ev[2 * g_prof.used], g_prof.ev[2 * g_prof.used + 1], false};
     g_prof.ids[g_prof.used] = id;
 }
 
-void prof_after(hipStream_t s)
+void prof_after()
 {
-    if (!g_prof.on || g_prof.used >= g_prof.max) return;
-    hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
-    ++g_prof.used;
+    // a call that launched nothing (empty copy, say) leaves no record
+    if (g_launch_ev.fired) ++g_prof.used;
+    g_launch_ev = {nullptr, nullptr, false};
 }
 
-// Launch through `fn` bracketed by profiling events when recording is on.
+// Launch through `fn`; while recording is on, the kernel it launches stores
+// its own start and end timestamps in the next pair of events.
 template <class Fn>
-hipError_t launch(int id, hipStream_t s, Fn&& fn)
+hipError_t launch(int id, Fn&& fn)
 {
-    prof_before(id, s);
+    prof_before(id);
     const hipError_t e = fn();
-    prof_after(s);
+    prof_after();
     return e;
 }
+
+}  // namespace
+
+LaunchEvents& la::launch_events()
+{
+    return g_launch_ev;
+}
+
+namespace {
 
 const KernelEntry* find_entry(int in_dtype, int phi, int dk, int F, int dv)
 {
@@ -345,8 +356,8 @@ la_status la_init_state(float* S, float* z, int64_t B, int64_t H, int32_t F, int
     if ((S && !aligned16(S)) || (z && !aligned16(z))) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be 16-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    if (S) e = launch(LA_KERNEL_FILL, st, [&] { return launch_fill_zero(S, B * H * (int64_t)F * d_v, st); });
-    if (e == hipSuccess && z) e = launch(LA_KERNEL_FILL, st, [&] { return launch_fill_zero(z, B * H * (int64_t)F, st); });
+    if (S) e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(S, B * H * (int64_t)F * d_v, st); });
+    if (e == hipSuccess && z) e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(z, B * H * (int64_t)F, st); });
     if (e != hipSuccess) return hip_fail(e, "la_init_state launch");
     return ok();
 }
@@ -387,11 +398,11 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
         hipError_t e = hipSuccess;
         if (S_out) {
             if (S_in) {
-                e = launch(LA_KERNEL_COPY, strm, [&] { return launch_copy(S_out, S_in, nS, strm); });
-                if (e == hipSuccess) e = launch(LA_KERNEL_COPY, strm, [&] { return launch_copy(z_out, z_in, nz, strm); });
+                e = launch(LA_KERNEL_COPY, [&] { return launch_copy(S_out, S_in, nS, strm); });
+                if (e == hipSuccess) e = launch(LA_KERNEL_COPY, [&] { return launch_copy(z_out, z_in, nz, strm); });
             } else {
-                e = launch(LA_KERNEL_FILL, strm, [&] { return launch_fill_zero(S_out, nS, strm); });
-                if (e == hipSuccess) e = launch(LA_KERNEL_FILL, strm, [&] { return launch_fill_zero(z_out, nz, strm); });
+                e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(S_out, nS, strm); });
+                if (e == hipSuccess) e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(z_out, nz, strm); });
             }
         }
         if (e != hipSuccess) return hip_fail(e, "la_forward_causal (N=0)");
@@ -456,7 +467,7 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             l.z_dst = segs + (int64_t)F * shape->d_v;
             l.dst_stride = plan.SZ;
             l.dst_zstride = plan.SZ;
-            if ((e = launch(LA_KERNEL_FWD_LOCAL, strm, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
+            if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
                 return hip_fail(e, "segment state launch");
             // pass 2: decayed exclusive scan over segments
             ScanArgs sa;
@@ -473,7 +484,7 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
             sa.lam = lam;
-            if ((e = launch(LA_KERNEL_SCAN, strm, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+            if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
                 return hip_fail(e, "segment scan launch");
             // pass 3: outputs from the carried-in state of each segment
             FwdArgs c = a;
@@ -482,14 +493,14 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             c.src_stride = plan.SZ;
             c.src_zstride = plan.SZ;
             c.src_seg_stride = BH * plan.SZ;
-            if ((e = launch(LA_KERNEL_FWD_CAUSAL, strm, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
+            if ((e = launch(LA_KERNEL_FWD_CAUSAL, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
                 return hip_fail(e, "causal output launch");
         } else {
             FwdArgs c = a;
             c.S_src = Si; c.z_src = zi; c.src_stride = si_stride; c.src_zstride = zi_stride;
             c.src_seg_stride = 0;
             c.S_dst = So; c.z_dst = zo; c.dst_stride = so_stride; c.dst_zstride = zo_stride;
-            if ((e = launch(LA_KERNEL_FWD_CAUSAL, strm, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
+            if ((e = launch(LA_KERNEL_FWD_CAUSAL, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
                 return hip_fail(e, "causal launch");
         }
     }
@@ -540,7 +551,7 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     l.z_dst = ws + (int64_t)F * shape->d_v;
     l.dst_stride = plan.SZ;
     l.dst_zstride = plan.SZ;
-    if ((e = launch(LA_KERNEL_FWD_LOCAL, strm, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
+    if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
         return hip_fail(e, "state sum launch");
     if (P > 1) {
         ScanArgs sa;
@@ -554,7 +565,7 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
         sa.n_len = shape->N;
         sa.seg_len = cps * plan.C;
         sa.causal = 0;
-        if ((e = launch(LA_KERNEL_SCAN, strm, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+        if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
             return hip_fail(e, "state reduction launch");
     }
     FwdArgs qa = a;
@@ -563,7 +574,7 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     qa.src_stride = plan.SZ;
     qa.src_zstride = plan.SZ;
     qa.src_seg_stride = 0;
-    if ((e = launch(LA_KERNEL_FWD_QUERY, strm, [&] { return ent->fwd(qa, MODE_QUERY, strm); })) != hipSuccess)
+    if ((e = launch(LA_KERNEL_FWD_QUERY, [&] { return ent->fwd(qa, MODE_QUERY, strm); })) != hipSuccess)
         return hip_fail(e, "query launch");
     return ok();
 }
@@ -605,7 +616,7 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     }();
     a.reverse = plain ? 0 : (int)(calls.fetch_add(1, std::memory_order_relaxed) & 1);
     hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = launch(LA_KERNEL_DECODE, strm, [&] { return ent->dec(a, strm); });
+    hipError_t e = launch(LA_KERNEL_DECODE, [&] { return ent->dec(a, strm); });
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
 }

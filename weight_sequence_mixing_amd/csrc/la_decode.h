@@ -155,8 +155,7 @@ template <class T, int PHI, int DK, int F, int DV>
 hipError_t dec_launch(const DecArgs& a, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)a.BH * (unsigned)decode_split<DV>();
-    hipLaunchKernelGGL((la_decode_kernel<T, PHI, DK, F, DV>), dim3(blocks), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(la_decode_kernel<T, PHI, DK, F, DV>, dim3(blocks), dim3(256), stream, a);
 }
 
 }  // namespace la

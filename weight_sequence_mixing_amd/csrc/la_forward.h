@@ -583,16 +583,12 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
     const dim3 grid((unsigned)a.P, (unsigned)a.BH), block(NW * 64);
     switch (mode) {
     case MODE_LOCAL:
-        hipLaunchKernelGGL((la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL>), grid, block, 0, stream, a);
-        break;
+        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL>, grid, block, stream, a);
     case MODE_CAUSAL:
-        hipLaunchKernelGGL((la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL>), grid, block, 0, stream, a);
-        break;
+        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL>, grid, block, stream, a);
     default:
-        hipLaunchKernelGGL((la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_QUERY>), grid, block, 0, stream, a);
-        break;
+        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_QUERY>, grid, block, stream, a);
     }
-    return hipGetLastError();
 }
 
 }  // namespace la

@@ -2,6 +2,7 @@
 // the HIP kernels.  Not installed; not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,6 +110,26 @@ extern KernelEntry kEntriesBf16Rf[];
 extern int kNumEntriesBf16Rf;
 extern KernelEntry kEntriesF32[];
 extern int kNumEntriesF32;
+
+// Per-launch timing: while `start` is set, the next kernel launched through
+// launch_kernel records the dispatch's own begin and end timestamps into
+// start/stop (the interval a kernel trace reports, without the queueing gap
+// that a separate event record before the launch would add) and sets `fired`.
+struct LaunchEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+    bool fired;
+};
+LaunchEvents& launch_events();
+
+template <class K, class... Args>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args)
+{
+    LaunchEvents& ev = launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+    if (ev.start) ev.fired = true;
+    return hipGetLastError();
+}
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);

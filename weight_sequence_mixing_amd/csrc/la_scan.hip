@@ -67,21 +67,22 @@ __global__ void __launch_bounds__(256) la_fill_zero_kernel(float* p, int64_t n)
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-// dst[0..n) = src[0..n): 16-byte accesses, four in flight per thread
+// dst[0..n) = src[0..n): 16-byte accesses, eight in flight per thread
 // (pointers are 16-byte aligned; a scalar loop finishes a ragged tail).
 __global__ void __launch_bounds__(256) la_copy_kernel(float* dst, const float* src, int64_t n)
 {
+    constexpr int U = 8;
     const int64_t n4 = n / 4;
     const f32x4* s4 = (const f32x4*)src;
     f32x4* d4 = (f32x4*)dst;
     const int64_t stride = (int64_t)gridDim.x * 256;
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n4; i += 4 * stride) {
-        const f32x4 a = s4[i], b = s4[i + stride], c = s4[i + 2 * stride], d = s4[i + 3 * stride];
-        d4[i] = a;
-        d4[i + stride] = b;
-        d4[i + 2 * stride] = c;
-        d4[i + 3 * stride] = d;
+    for (; i + (U - 1) * stride < n4; i += U * stride) {
+        f32x4 t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) t[u] = s4[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) d4[i + u * stride] = t[u];
     }
     for (; i < n4; i += stride) d4[i] = s4[i];
     for (int64_t t = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x; t < n; t += stride) dst[t] = src[t];
@@ -90,8 +91,7 @@ __global__ void __launch_bounds__(256) la_copy_kernel(float* dst, const float* s
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream)
 {
     const int SZ = a.F * a.DV + a.F;
-    hipLaunchKernelGGL(la_scan_kernel, dim3((SZ + 255) / 256, a.BH), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(la_scan_kernel, dim3((SZ + 255) / 256, a.BH), dim3(256), stream, a);
 }
 
 static unsigned grid_for(int64_t n)
@@ -105,18 +105,16 @@ static unsigned grid_for(int64_t n)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream)
 {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(la_fill_zero_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n);
-    return hipGetLastError();
+    return launch_kernel(la_fill_zero_kernel, dim3(grid_for(n)), dim3(256), stream, p, n);
 }
 
 hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream)
 {
     if (n <= 0 || dst == src) return hipSuccess;
-    int64_t b = (n / 4 + 1023) / 1024;  // about four 16-byte vectors per thread
-    if (b > 8192) b = 8192;
+    int64_t b = (n / 4 + 2047) / 2048;  // about eight 16-byte vectors per thread
+    if (b > 16384) b = 16384;
     if (b < 1) b = 1;
-    hipLaunchKernelGGL(la_copy_kernel, dim3((unsigned)b), dim3(256), 0, stream, dst, src, n);
-    return hipGetLastError();
+    return launch_kernel(la_copy_kernel, dim3((unsigned)b), dim3(256), stream, dst, src, n);
 }
 
 }  // namespace la
