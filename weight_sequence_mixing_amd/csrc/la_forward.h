@@ -50,6 +50,8 @@
 //        MODE_QUERY   non-causal outputs for a fixed state.
 #pragma once
 
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -180,6 +182,43 @@ la_fwd_kernel(const FwdArgs a)
         }
     }
 
+    // ---- global -> register prefetch of one chunk.  A full chunk is read at
+    // fixed per-thread offsets from a uniform base.  In a ragged last chunk,
+    // rows past the end re-read the last valid row (always in bounds) and are
+    // replaced by zeros in registers, so the loads stay unconditional.
+    uint4 rq[Cfg::NEED_Q ? RQ : 1], rk[Cfg::NEED_K ? RQ : 1], rv[Cfg::NEED_K ? RV : 1];
+    auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) {
+        constexpr bool TAIL = decltype(tail_c)::value;
+        const uint4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int r = 0; r < nreg; ++r) {
+            const int idx = tid + r * NT, j = idx / vpr, c4 = idx % vpr;
+            if constexpr (!TAIL) {
+                dst[r] = *(const uint4*)(base + j * ld + c4 * VEC);
+            } else {
+                const uint4 val = *(const uint4*)(base + min(j, n - 1) * ld + c4 * VEC);
+                dst[r] = (j < n) ? val : zero;
+            }
+        }
+    };
+    auto load_chunk_as = [&](int64_t t0, int n, auto tail_c) {
+        if constexpr (Cfg::NEED_Q) load_rows(rq, qg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
+        if constexpr (Cfg::NEED_K) {
+            load_rows(rk, kg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
+            load_rows(rv, vg + t0 * DV, VPRV, DV, RV, n, tail_c);
+        }
+    };
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = c * C;
+        const int n = (int)min((int64_t)C, a.n_len - t0);
+        if (n == C) load_chunk_as(t0, n, std::false_type{});
+        else load_chunk_as(t0, n, std::true_type{});
+    };
+
+    // the first chunk's loads go out before the carried state is read, so
+    // that the two memory latencies overlap
+    if (c_beg < c_end) load_chunk(c_beg);
+
     // ---- carried state: S tiles (fb, this wave's d-blocks) and z tiles
     // (lane (g, l16) of z tile fb holds z[16 fb + 4 g + r] in every column)
     f32x4 accS[FB][DBW], accZ[FB];
@@ -218,38 +257,6 @@ la_fwd_kernel(const FwdArgs a)
     if constexpr (Cfg::NEED_Q) convert_state();
     float log2D = 0.f;  // the true state is 2^log2D times the accumulators
 
-    // ---- global -> register prefetch of one chunk.  Rows past the end of the
-    // sequence re-read the last valid row (always in bounds) and are replaced
-    // by zeros in registers, so the loads stay unconditional global loads.
-    uint4 rq[Cfg::NEED_Q ? RQ : 1], rk[Cfg::NEED_K ? RQ : 1], rv[Cfg::NEED_K ? RV : 1];
-    auto load_chunk = [&](int64_t c) {
-        const int64_t t0 = c * C;
-        const int n = (int)min((int64_t)C, a.n_len - t0);
-        const uint4 zero = {0u, 0u, 0u, 0u};
-        if constexpr (Cfg::NEED_Q) {
-#pragma unroll
-            for (int r = 0; r < RQ; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRQ, c4 = idx % VPRQ;
-                const uint4 val = *(const uint4*)(qg + (t0 + min(j, n - 1)) * DK + c4 * VEC);
-                rq[r] = (j < n) ? val : zero;
-            }
-        }
-        if constexpr (Cfg::NEED_K) {
-#pragma unroll
-            for (int r = 0; r < RQ; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRQ, c4 = idx % VPRQ;
-                const uint4 val = *(const uint4*)(kg + (t0 + min(j, n - 1)) * DK + c4 * VEC);
-                rk[r] = (j < n) ? val : zero;
-            }
-#pragma unroll
-            for (int r = 0; r < RV; ++r) {
-                const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
-                const uint4 val = *(const uint4*)(vg + (t0 + min(j, n - 1)) * DV + c4 * VEC);
-                rv[r] = (j < n) ? val : zero;
-            }
-        }
-    };
-
     // raw 16-byte vector -> row-major value tile (no conversion)
     auto put_raw = [&](T* tile, int row, int col, const uint4& u) {
         if constexpr (sizeof(T) == 2) {
@@ -274,12 +281,15 @@ la_fwd_kernel(const FwdArgs a)
     // the weighted keys; random features: raw rows and their squared norms.
     // kw_l2: log2 of the key weight of token 0 relative to lambda^(n-1-j),
     // i.e. weight_j = 2^((n-1-j) log2 lambda - kw_l2) (kw_l2 = 0 after a rescale).
-    auto stage = [&](int buf, int n, float kw_l2) {
+    // TAIL (a std::bool_constant): the chunk is a ragged last chunk.  Query
+    // rows past its end need no masking: each feeds only its own output row,
+    // which is never stored.  Key rows past the end must not reach the state.
+    auto stage = [&](int buf, int n, float kw_l2, auto tail_c) {
+        constexpr bool TAIL = decltype(tail_c)::value;
         T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         T* const sK = sK0 + (RF ? 0 : buf * TQ);
         T* const sKw = sKw0 + (RF ? 0 : buf * TQ);
         T* const sV = sV0 + buf * TV;
-        const bool tail = n < C;
         const int cg = tid % VPRQ;
         if constexpr (Cfg::NEED_Q) {
 #pragma unroll
@@ -300,10 +310,6 @@ la_fwd_kernel(const FwdArgs a)
                     float p[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) p[e] = phi_elu1<T>(x[e]);
-                    if (tail && j >= n) {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) p[e] = 0.f;
-                    }
                     put_feat(sQ, j, cg * VEC, p);
                 }
             }
@@ -327,7 +333,7 @@ la_fwd_kernel(const FwdArgs a)
                     float p[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) p[e] = phi_elu1<T>(x[e]);
-                    if (tail && j >= n) {
+                    if (TAIL && j >= n) {
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) p[e] = 0.f;
                     }
@@ -336,7 +342,7 @@ la_fwd_kernel(const FwdArgs a)
                         put_feat(Cfg::NEED_KROW ? sK : sKw, j, cg * VEC, p);
                     } else {
                         if constexpr (Cfg::NEED_KROW) put_feat(sK, j, cg * VEC, p);
-                        const float w = (j < n) ? key_weight(n - 1 - j, kw_l2) : 0.f;
+                        const float w = (TAIL && j >= n) ? 0.f : key_weight(n - 1 - j, kw_l2);
                         float pw[VEC];
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) pw[e] = p[e] * w;
@@ -517,7 +523,6 @@ la_fwd_kernel(const FwdArgs a)
     };
 
     // ---- main loop over the segment's chunks
-    if (c_beg < c_end) load_chunk(c_beg);
     if constexpr (RF) __syncthreads();  // omega in LDS
     for (int64_t c = c_beg; c < c_end; ++c) {
         const int buf = (int)((c - c_beg) & 1);
@@ -538,7 +543,8 @@ la_fwd_kernel(const FwdArgs a)
                 log2D = 0.f;
             }
         }
-        stage(buf, n, kw_l2);
+        if (n == C) stage(buf, n, kw_l2, std::false_type{});
+        else stage(buf, n, kw_l2, std::true_type{});
         if (c + 1 < c_end) load_chunk(c + 1);
         __syncthreads();
         if constexpr (RF) {
