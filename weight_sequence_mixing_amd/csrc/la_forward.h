@@ -75,6 +75,7 @@ struct FwdCfg {
     static constexpr int FB = F / 16;
     static constexpr int DB = DV / 16;
     static constexpr int DBW = DB / NW;
+    static constexpr int ZB = FB / NW;  // z tiles per wave
     static constexpr int XLD = DK + 4;  // raw q/k rows of the random-feature prologue
     static constexpr bool NEED_Q = MODE != MODE_LOCAL;
     static constexpr bool NEED_K = MODE != MODE_QUERY;
@@ -99,24 +100,34 @@ struct FwdCfg {
     static constexpr size_t SZ_XK = (RF && NEED_K) ? size_t(C) * XLD * sizeof(T) : 0;
     static constexpr size_t OFF_XN = al(OFF_XK + SZ_XK);
     static constexpr size_t SZ_XN = RF ? size_t(2) * C * sizeof(float) : 0;
-    static constexpr size_t OFF_OM = al(OFF_XN + SZ_XN);
+    // the normaliser z after each chunk, double buffered (fp32, MODE_CAUSAL)
+    static constexpr size_t OFF_Z = al(OFF_XN + SZ_XN);
+    static constexpr size_t SZ_Z = (NEED_Q && NEED_K) ? size_t(2) * F * sizeof(float) : 0;
+    static constexpr size_t OFF_OM = al(OFF_Z + SZ_Z);
     // omega in LDS: bf16 high and low parts (bf16 inputs) or fp32 (fp32 inputs)
     static constexpr size_t SZ_OM = RF ? (sizeof(T) == 2 ? size_t(2) * M * XLD * 2 : size_t(M) * XLD * 4) : 0;
     static constexpr size_t TOTAL = al(OFF_OM + SZ_OM);
+    // waves per SIMD the register allocation must allow: two where the state
+    // is small (d_k, d_v <= 64 and F <= 64), so that two workgroups share a CU
+    static constexpr int MIN_WAVES = (F <= 64 && DV <= 64) ? 2 : 1;
 
     static_assert(C % 32 == 0 && C >= 32, "chunk must be a multiple of 32");
     static_assert(F % 64 == 0 && DV % 64 == 0 && DK % 32 == 0, "head sizes");
     static_assert(DBW >= 1 && DB % NW == 0, "value columns must split over the waves");
+    static_assert(ZB >= 1 && FB % NW == 0, "z tiles must split over the waves");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-template <class T, int PHI, int DK, int F, int DV, int C, int NW, int MODE>
-__global__ void __launch_bounds__(NW * 64)
+// OUTF32: y is fp32 (bf16 inputs with fp32 outputs).  A template argument, not
+// a runtime branch: branches around the output stores make the compiler wait
+// for every earlier store before the next chunk's loaded data is used.
+template <class T, int PHI, int DK, int F, int DV, int C, int NW, int MODE, bool OUTF32>
+__global__ void __launch_bounds__(NW * 64, (FwdCfg<T, PHI, DK, F, DV, C, NW, MODE>::MIN_WAVES))
 la_fwd_kernel(const FwdArgs a)
 {
     using Cfg = FwdCfg<T, PHI, DK, F, DV, C, NW, MODE>;
     constexpr int NT = Cfg::NT, VEC = Cfg::VEC, M = Cfg::M, QB = Cfg::QB, FB = Cfg::FB;
-    constexpr int DBW = Cfg::DBW, XLD = Cfg::XLD, TQ = Cfg::TQ, TV = Cfg::TV;
+    constexpr int DBW = Cfg::DBW, XLD = Cfg::XLD, TQ = Cfg::TQ, TV = Cfg::TV, ZB = Cfg::ZB;
     constexpr bool RF = Cfg::RF;
     constexpr int KB = F / 32;                  // 32-wide feature blocks
     constexpr int CB = C / 32;                  // 32-wide token blocks
@@ -136,6 +147,7 @@ la_fwd_kernel(const FwdArgs a)
     T* const sXq = (T*)(smem + Cfg::OFF_XQ);
     T* const sXk = (T*)(smem + Cfg::OFF_XK);
     float* const sXn = (float*)(smem + Cfg::OFF_XN);
+    float* const sZ = (float*)(smem + Cfg::OFF_Z);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
@@ -186,6 +198,9 @@ la_fwd_kernel(const FwdArgs a)
     // fixed per-thread offsets from a uniform base.  In a ragged last chunk,
     // rows past the end re-read the last valid row (always in bounds) and are
     // replaced by zeros in registers, so the loads stay unconditional.
+    const bool ragged = c_end > c_beg && c_end * C > a.n_len;
+    const int64_t c_full = ragged ? c_end - 1 : c_end;
+    const int n_tail = ragged ? (int)(a.n_len - c_full * C) : C;
     uint4 rq[Cfg::NEED_Q ? RQ : 1], rk[Cfg::NEED_K ? RQ : 1], rv[Cfg::NEED_K ? RV : 1];
     auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) {
         constexpr bool TAIL = decltype(tail_c)::value;
@@ -201,33 +216,37 @@ la_fwd_kernel(const FwdArgs a)
             }
         }
     };
-    auto load_chunk_as = [&](int64_t t0, int n, auto tail_c) {
+    // chunk c: a full one (c < c_full) or, with TAIL, the ragged last one
+    auto load_chunk = [&](int64_t c, auto tail_c) {
+        const int64_t t0 = c * C;
+        const int n = decltype(tail_c)::value ? n_tail : C;
         if constexpr (Cfg::NEED_Q) load_rows(rq, qg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
         if constexpr (Cfg::NEED_K) {
             load_rows(rk, kg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
             load_rows(rv, vg + t0 * DV, VPRV, DV, RV, n, tail_c);
         }
     };
-    auto load_chunk = [&](int64_t c) {
-        const int64_t t0 = c * C;
-        const int n = (int)min((int64_t)C, a.n_len - t0);
-        if (n == C) load_chunk_as(t0, n, std::false_type{});
-        else load_chunk_as(t0, n, std::true_type{});
-    };
 
     // the first chunk's loads go out before the carried state is read, so
     // that the two memory latencies overlap
-    if (c_beg < c_end) load_chunk(c_beg);
+    if (c_beg < c_full) load_chunk(c_beg, std::false_type{});
+    else if (c_beg < c_end) load_chunk(c_beg, std::true_type{});
 
-    // ---- carried state: S tiles (fb, this wave's d-blocks) and z tiles
-    // (lane (g, l16) of z tile fb holds z[16 fb + 4 g + r] in every column)
-    f32x4 accS[FB][DBW], accZ[FB];
+    // ---- carried state: S tiles (fb, this wave's d-blocks) and this wave's z
+    // tiles fb = ZB * wave + u; lane (g, l16) of a z tile holds
+    // z[16 fb + 4 g + r] in every column
+    f32x4 accS[FB][DBW], accZ[ZB];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) {
+    for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
         for (int t = 0; t < DBW; ++t) accS[fb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accZ[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+#pragma unroll
+    for (int u = 0; u < ZB; ++u) accZ[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // z as an operand fragment (A operand of z phi(Q)^T, z in every row)
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    Frag<T> zf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) zf[kb] = frag_acc<T>(zero4, zero4);
     if constexpr (MODE != MODE_LOCAL) {
         if (a.S_src) {
             const float* Sb = a.S_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_stride;
@@ -240,19 +259,30 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) accS[fb][t][r] = Sb[(16 * fb + 4 * g + r) * DV + d];
                 }
-                accZ[fb] = *(const f32x4*)(zb + 16 * fb + 4 * g);
+            }
+#pragma unroll
+            for (int u = 0; u < ZB; ++u) accZ[u] = *(const f32x4*)(zb + 16 * (ZB * wave + u) + 4 * g);
+            if constexpr (Cfg::NEED_Q) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    zf[kb] = frag_acc<T>(*(const f32x4*)(zb + 32 * kb + 4 * g), *(const f32x4*)(zb + 32 * kb + 16 + 4 * g));
             }
         }
     }
-    // S and z as operand fragments (A operands of S^T phi(Q)^T and z phi(Q)^T)
-    Frag<T> sf[KB][DBW], zf[KB];
+    // S as operand fragments (A operands of S^T phi(Q)^T)
+    Frag<T> sf[KB][DBW];
     auto convert_state = [&]() {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int t = 0; t < DBW; ++t) sf[kb][t] = frag_acc<T>(accS[2 * kb][t], accS[2 * kb + 1][t]);
-            zf[kb] = frag_acc<T>(accZ[2 * kb], accZ[2 * kb + 1]);
-        }
+    };
+    // z after the previous chunk, published in LDS by the waves that own it
+    auto read_z = [&](int par) {
+        const float* zs = sZ + par * F;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            zf[kb] = frag_acc<T>(*(const f32x4*)(zs + 32 * kb + 4 * g), *(const f32x4*)(zs + 32 * kb + 16 + 4 * g));
     };
     if constexpr (Cfg::NEED_Q) convert_state();
     float log2D = 0.f;  // the true state is 2^log2D times the accumulators
@@ -415,7 +445,8 @@ la_fwd_kernel(const FwdArgs a)
     // ---- outputs and state update of one staged chunk.  dscale: 2^log2D of
     // the state the chunk reads; rescale: factor applied to the accumulators
     // before this chunk's keys are added (1 when none).
-    auto compute = [&](int buf, int n, int64_t t0, float dscale, bool do_rescale, float rescale) {
+    auto compute = [&](int buf, int n, int64_t t0, float dscale, bool do_rescale, float rescale, int zpar, auto tail_c) {
+        constexpr bool TAIL = decltype(tail_c)::value;
         const T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         const T* const sK = sK0 + (RF ? 0 : buf * TQ);
         const T* const sKw = (Cfg::NEED_KROW && !decay && !RF) ? sK : sKw0 + (RF ? 0 : buf * TQ);
@@ -490,9 +521,9 @@ la_fwd_kernel(const FwdArgs a)
                     } else {
                         o *= sc;
                     }
-                    if (i < n) {
+                    if (!TAIL || i < n) {
                         const int64_t yo = yrow * DV + 16 * (wave * DBW + t) + 4 * g;
-                        if (a.out_f32) st4((float*)a.y + yo, o[0], o[1], o[2], o[3]);
+                        if constexpr (OUTF32) st4((float*)a.y + yo, o[0], o[1], o[2], o[3]);
                         else st4((T*)a.y + yo, o[0], o[1], o[2], o[3]);
                     }
                 }
@@ -502,11 +533,11 @@ la_fwd_kernel(const FwdArgs a)
         if constexpr (Cfg::NEED_K) {
             if (do_rescale) {
 #pragma unroll
-                for (int fb = 0; fb < FB; ++fb) {
+                for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
                     for (int t = 0; t < DBW; ++t) accS[fb][t] *= rescale;
-                    accZ[fb] *= rescale;
-                }
+#pragma unroll
+                for (int u = 0; u < ZB; ++u) accZ[u] *= rescale;
             }
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb) {
@@ -515,43 +546,94 @@ la_fwd_kernel(const FwdArgs a)
                     const Frag<T> kf = ColRead<T, F>::get(sKw, 32 * kb, 16 * fb, lane);
 #pragma unroll
                     for (int t = 0; t < DBW; ++t) mma(accS[fb][t], kf, vf[kb][t]);
-                    mma(accZ[fb], kf, ones);
                 }
             }
-            if constexpr (Cfg::NEED_Q) convert_state();
+            // z: this wave's feature blocks only (a column offset, no branch)
+#pragma unroll
+            for (int u = 0; u < ZB; ++u)
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb)
+                    mma(accZ[u], ColRead<T, F>::get(sKw, 32 * kb, 16 * (ZB * wave + u), lane), ones);
+            if constexpr (Cfg::NEED_Q) {
+                convert_state();
+                // publish z for the next chunk (read after its barrier)
+                if (l16 == 0) {
+                    float* zs = sZ + zpar * F;
+#pragma unroll
+                    for (int u = 0; u < ZB; ++u) *(f32x4*)(zs + 16 * (ZB * wave + u) + 4 * g) = accZ[u];
+                }
+            }
         }
     };
 
-    // ---- main loop over the segment's chunks
+    // ---- main loop over the segment's chunks.  The loop is rotated: an
+    // iteration issues the next chunk's loads, computes the staged chunk and
+    // then stages the next one, so that every load is consumed in the
+    // iteration that issued it.  (A load consumed across the back edge, after
+    // the output stores, is waited for with vmcnt(0), i.e. after the stores.)
+    // The ragged last chunk of the sequence, if any, is loaded unprefetched and
+    // computed after the loop, so that the loop's stores are unconditional.
     if constexpr (RF) __syncthreads();  // omega in LDS
-    for (int64_t c = c_beg; c < c_end; ++c) {
-        const int buf = (int)((c - c_beg) & 1);
-        const int64_t t0 = c * C;
-        const int n = (int)min((int64_t)C, a.n_len - t0);
-        // decay bookkeeping (uniform): pending factor 2^log2D * lambda^n
-        const float dscale = decay ? exp2f(log2D) : 1.f;
-        bool do_rescale = false;
-        float rescale = 1.f, kw_l2 = 0.f;
+
+    // decay bookkeeping of the next chunk, in chunk order (uniform): the
+    // pending factor 2^log2D * lambda^n and the key-weight offset
+    struct Dec { float dscale, rescale, kw_l2; bool do_rescale; };
+    auto book = [&](int n) {
+        Dec d = {decay ? exp2f(log2D) : 1.f, 1.f, 0.f, false};
         if (decay) {
             const float cand = log2D + (float)n * l2l;
             if (cand >= kLog2MinScale) {
-                kw_l2 = cand;
+                d.kw_l2 = cand;
                 log2D = cand;
             } else {
-                do_rescale = true;
-                rescale = exp2f(cand);  // 0 for lambda = 0
+                d.do_rescale = true;
+                d.rescale = exp2f(cand);  // 0 for lambda = 0
                 log2D = 0.f;
             }
         }
-        if (n == C) stage(buf, n, kw_l2, std::false_type{});
-        else stage(buf, n, kw_l2, std::true_type{});
-        if (c + 1 < c_end) load_chunk(c + 1);
+        return d;
+    };
+    // barrier, features (random features), carried z, outputs and state
+    auto finish = [&](int64_t c, int n, const Dec& d, auto tail_c) {
+        const int buf = (int)((c - c_beg) & 1);
         __syncthreads();
         if constexpr (RF) {
-            rf_features(n, kw_l2);
+            rf_features(n, d.kw_l2);
             __syncthreads();
         }
-        compute(buf, n, t0, dscale, do_rescale, rescale);
+        if constexpr (Cfg::NEED_Q && Cfg::NEED_K) {
+            if (c > c_beg) read_z(buf ^ 1);
+        }
+        compute(buf, n, c * C, d.dscale, d.do_rescale, d.rescale, buf, tail_c);
+    };
+
+    if (c_beg < c_end) {
+        Dec d;
+        if (c_beg < c_full) {
+            d = book(C);
+            stage(0, C, d.kw_l2, std::false_type{});
+        } else {
+            d = book(n_tail);
+            stage(0, n_tail, d.kw_l2, std::true_type{});
+        }
+        for (int64_t c = c_beg; c < c_full; ++c) {
+            const int buf = (int)((c - c_beg) & 1);
+            const bool next_full = c + 1 < c_full;
+            if (next_full) load_chunk(c + 1, std::false_type{});
+            finish(c, C, d, std::false_type{});
+            if (next_full) {
+                d = book(C);
+                stage(buf ^ 1, C, d.kw_l2, std::false_type{});
+            }
+        }
+        if (ragged) {
+            if (c_full > c_beg) {
+                load_chunk(c_full, std::true_type{});
+                d = book(n_tail);
+                stage((int)((c_full - c_beg) & 1), n_tail, d.kw_l2, std::true_type{});
+            }
+            finish(c_full, n_tail, d, std::true_type{});
+        }
     }
 
     // ---- state out (true scale)
@@ -575,7 +657,10 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Sd[(16 * fb + 4 * g + r) * DV + d] = ds * accS[fb][t][r];
                 }
-                if (wave == 0 && l16 == 0) *(f32x4*)(zd + 16 * fb + 4 * g) = accZ[fb] * ds;
+            }
+            if (l16 == 0) {
+#pragma unroll
+                for (int u = 0; u < ZB; ++u) *(f32x4*)(zd + 16 * (ZB * wave + u) + 4 * g) = accZ[u] * ds;
             }
         }
     }
@@ -587,13 +672,17 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
     constexpr int C = chunk_len<T, PHI>(F);
     constexpr int NW = 4;
     const dim3 grid((unsigned)a.P, (unsigned)a.BH), block(NW * 64);
+    // fp32 inputs always write fp32 outputs, so only bf16 needs both variants
+    const bool o32 = sizeof(T) == 2 && a.out_f32;
     switch (mode) {
     case MODE_LOCAL:
-        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL>, grid, block, stream, a);
+        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL, false>, grid, block, stream, a);
     case MODE_CAUSAL:
-        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL>, grid, block, stream, a);
+        return o32 ? launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL, true>, grid, block, stream, a)
+                   : launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL, false>, grid, block, stream, a);
     default:
-        return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_QUERY>, grid, block, stream, a);
+        return o32 ? launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_QUERY, true>, grid, block, stream, a)
+                   : launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_QUERY, false>, grid, block, stream, a);
     }
 }
 
