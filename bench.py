@@ -298,12 +298,15 @@ def _kernel_label(mangled):
     if "la_scan_kernel" in mangled:
         return "la_scan_kernel"
     if "la_fwd_kernel" in mangled:
-        # the mode is the last template argument, mangled (...ELi1EEEvNS_7FwdArgsE)
-        # or demangled (..., 4, 1>(la::FwdArgs))
+        # the mode is the last int template argument (a bool, the output type,
+        # follows it), mangled (...ELi1ELb0EEEvNS_7FwdArgsE) or demangled
+        # (..., 4, 1, false>(la::FwdArgs))
         if "EEEvNS_7FwdArgsE" in mangled:
-            mode = mangled.split("EEEvNS_7FwdArgsE")[0].rsplit("ELi", 1)[-1]
+            mode = mangled.split("EEEvNS_7FwdArgsE")[0].rsplit("ELi", 1)[-1].split("E")[0]
         else:
-            mode = mangled.split(">(")[0].rsplit(",", 1)[-1].strip()
+            args = [x.strip() for x in mangled.split(">(")[0].split(",")]
+            ints = [x for x in args if x.lstrip("-").isdigit()]
+            mode = ints[-1] if ints else ""
         return {"0": "la_fwd_kernel (segment state)", "1": "la_fwd_kernel (causal output)",
                 "2": "la_fwd_kernel (non-causal output)"}.get(mode, "la_fwd_kernel")
     return None
