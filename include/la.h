@@ -143,8 +143,10 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y,
 
 /* Measurement hooks (for benchmarks; not needed to compute anything).
  * Between la_profile_begin() and la_profile_end(), every kernel this library
- * launches from the calling thread is bracketed by two HIP events recorded on
- * the launch's own stream, so each launch's device time can be read back.
+ * launches from the calling thread records its own dispatch start and end
+ * timestamps into a pair of HIP events (hipExtLaunchKernelGGL), so each
+ * launch's device time can be read back.  A call that launches nothing (an
+ * empty copy) records nothing.
  * la_profile_begin creates 2*max_launches events (host-side runtime objects;
  * no device memory); launches beyond max_launches are not recorded.
  * la_profile_end waits for the last recorded event, writes up to `capacity`
