@@ -57,9 +57,13 @@
 
 namespace la {
 
+// Tokens per chunk.  32 for every shape: against 64 it halves the LDS tiles
+// and the registers of the staged chunk (the d = 64 output kernel fits three
+// waves per SIMD), and the outputs of a chunk depend on fewer score tiles;
+// measured faster for d = 64 and d = 128.
 template <class T, int PHI>
 constexpr int chunk_len(int F) {
-    return (sizeof(T) == 4 || F > 128) ? 32 : 64;
+    return 32;
 }
 
 // log2 of the smallest pending decay factor before the state is rescaled
