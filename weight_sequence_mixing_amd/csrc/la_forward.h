@@ -57,6 +57,10 @@
 
 namespace la {
 
+// The kernel body is written as lambdas over the workgroup's registers; each
+// must be inlined (a call would move the captured arrays to scratch memory).
+#define LA_INLINE __attribute__((always_inline))
+
 // Tokens per chunk.  32 for every shape: against 64 it halves the LDS tiles
 // and the registers of the staged chunk (the d = 64 output kernel fits three
 // waves per SIMD), and the outputs of a chunk depend on fewer score tiles;
@@ -107,10 +111,12 @@ struct FwdCfg {
     // the normaliser z after each chunk, double buffered (fp32, MODE_CAUSAL)
     static constexpr size_t OFF_Z = al(OFF_XN + SZ_XN);
     static constexpr size_t SZ_Z = (NEED_Q && NEED_K) ? size_t(2) * F * sizeof(float) : 0;
-    static constexpr size_t OFF_OM = al(OFF_Z + SZ_Z);
-    // omega in LDS: bf16 high and low parts (bf16 inputs) or fp32 (fp32 inputs)
-    static constexpr size_t SZ_OM = RF ? (sizeof(T) == 2 ? size_t(2) * M * XLD * 2 : size_t(M) * XLD * 4) : 0;
-    static constexpr size_t TOTAL = al(OFF_OM + SZ_OM);
+    static constexpr size_t TOTAL = al(OFF_Z + SZ_Z);
+    // random features: each wave computes the feature blocks of one 16-token
+    // block (ib = wave % QB) for TPW 16-row blocks of omega, whose operand
+    // fragments it keeps in registers
+    static constexpr int KX = DK / 32;
+    static constexpr int TPW = RF ? (M / 16) * QB / NW : 1;
     // waves per SIMD the register allocation must allow: two where the state
     // is small (d_k, d_v <= 64 and F <= 64), so that two workgroups share a CU
     static constexpr int MIN_WAVES = (F <= 64 && DV <= 64) ? 2 : 1;
@@ -120,6 +126,7 @@ struct FwdCfg {
     static_assert(DBW >= 1 && DB % NW == 0, "value columns must split over the waves");
     static_assert(ZB >= 1 && FB % NW == 0, "z tiles must split over the waves");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(!RF || ((M / 16) * QB % NW == 0 && NW % QB == 0), "random-feature tiles must split over the waves");
 };
 
 // OUTF32: y is fp32 (bf16 inputs with fp32 outputs).  A template argument, not
@@ -181,19 +188,29 @@ la_fwd_kernel(const FwdArgs a)
     }
     const float lq1 = decay ? lam_pow(l2l, l16 + 1) : 1.f;
 
-    // ---- random-feature directions into LDS (once per workgroup)
+    // ---- random-feature directions as operand fragments, in registers for
+    // the whole workgroup: rows 16 rb.. of omega (rb = wave / QB + (NW / QB) u),
+    // as bf16 high and low parts for bf16 inputs (omega = hi + lo to 16 bits)
+    constexpr int TPW = Cfg::TPW, KX = Cfg::KX;
+    Frag<T> om_hi[TPW][KX], om_lo[sizeof(T) == 2 ? TPW : 1][KX];
     if constexpr (RF) {
-        for (int idx = tid; idx < M * DK; idx += NT) {
-            const int r = idx / DK, d = idx % DK;
-            const float w = a.omega[idx];
-            if constexpr (sizeof(T) == 2) {
-                bf16* hi = (bf16*)(smem + Cfg::OFF_OM);
-                bf16* lo = hi + M * XLD;
-                const bf16 wh = (bf16)w;
-                hi[r * XLD + d] = wh;
-                lo[r * XLD + d] = (bf16)(w - (float)wh);
-            } else {
-                ((float*)(smem + Cfg::OFF_OM))[r * XLD + d] = w;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int rb = wave / QB + (NW / QB) * u;
+#pragma unroll
+            for (int kb = 0; kb < KX; ++kb) {
+                const float* p = a.omega + (int64_t)(16 * rb + l16) * DK + 32 * kb + 4 * g;
+                const f32x4 w0 = *(const f32x4*)p, w1 = *(const f32x4*)(p + 16);
+                om_hi[u][kb] = frag_acc<T>(w0, w1);
+                if constexpr (sizeof(T) == 2) {
+                    f32x4 r0, r1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        r0[e] = w0[e] - (float)(bf16)w0[e];
+                        r1[e] = w1[e] - (float)(bf16)w1[e];
+                    }
+                    om_lo[u][kb] = frag_acc<T>(r0, r1);
+                }
             }
         }
     }
@@ -206,7 +223,7 @@ la_fwd_kernel(const FwdArgs a)
     const int64_t c_full = ragged ? c_end - 1 : c_end;
     const int n_tail = ragged ? (int)(a.n_len - c_full * C) : C;
     uint4 rq[Cfg::NEED_Q ? RQ : 1], rk[Cfg::NEED_K ? RQ : 1], rv[Cfg::NEED_K ? RV : 1];
-    auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) {
+    auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const uint4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -221,7 +238,7 @@ la_fwd_kernel(const FwdArgs a)
         }
     };
     // chunk c: a full one (c < c_full) or, with TAIL, the ragged last one
-    auto load_chunk = [&](int64_t c, auto tail_c) {
+    auto load_chunk = [&](int64_t c, auto tail_c) LA_INLINE {
         const int64_t t0 = c * C;
         const int n = decltype(tail_c)::value ? n_tail : C;
         if constexpr (Cfg::NEED_Q) load_rows(rq, qg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
@@ -275,14 +292,14 @@ la_fwd_kernel(const FwdArgs a)
     }
     // S as operand fragments (A operands of S^T phi(Q)^T)
     Frag<T> sf[KB][DBW];
-    auto convert_state = [&]() {
+    auto convert_state = [&]() LA_INLINE {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int t = 0; t < DBW; ++t) sf[kb][t] = frag_acc<T>(accS[2 * kb][t], accS[2 * kb + 1][t]);
     };
     // z after the previous chunk, published in LDS by the waves that own it
-    auto read_z = [&](int par) {
+    auto read_z = [&](int par) LA_INLINE {
         const float* zs = sZ + par * F;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -292,7 +309,7 @@ la_fwd_kernel(const FwdArgs a)
     float log2D = 0.f;  // the true state is 2^log2D times the accumulators
 
     // raw 16-byte vector -> row-major value tile (no conversion)
-    auto put_raw = [&](T* tile, int row, int col, const uint4& u) {
+    auto put_raw = [&](T* tile, int row, int col, const uint4& u) LA_INLINE {
         if constexpr (sizeof(T) == 2) {
             *(uint2*)(tile + TVL::off(row, col)) = uint2{u.x, u.y};
             *(uint2*)(tile + TVL::off(row, col + 4)) = uint2{u.z, u.w};
@@ -301,13 +318,13 @@ la_fwd_kernel(const FwdArgs a)
         }
     };
     // VEC floats -> row-major feature tile (rounded to T)
-    auto put_feat = [&](T* tile, int row, int col, const float* p) {
+    auto put_feat = [&](T* tile, int row, int col, const float* p) LA_INLINE {
 #pragma unroll
         for (int e = 0; e < VEC; e += 4) st4(tile + TF::off(row, col + e), p[e], p[e + 1], p[e + 2], p[e + 3]);
     };
 
     // lambda^k / 2^kw_l2 with lambda^0 = 1 also for lambda = 0
-    auto key_weight = [&](int k, float kw_l2) {
+    auto key_weight = [&](int k, float kw_l2) LA_INLINE {
         return k == 0 ? __builtin_amdgcn_exp2f(-kw_l2) : __builtin_amdgcn_exp2f((float)k * l2l - kw_l2);
     };
 
@@ -318,7 +335,7 @@ la_fwd_kernel(const FwdArgs a)
     // TAIL (a std::bool_constant): the chunk is a ragged last chunk.  Query
     // rows past its end need no masking: each feeds only its own output row,
     // which is never stored.  Key rows past the end must not reach the state.
-    auto stage = [&](int buf, int n, float kw_l2, auto tail_c) {
+    auto stage = [&](int buf, int n, float kw_l2, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         T* const sK = sK0 + (RF ? 0 : buf * TQ);
@@ -394,34 +411,31 @@ la_fwd_kernel(const FwdArgs a)
 
     // ---- random features on the matrix cores: U^T = omega x^T, then cos/sin,
     // written row-major into the feature tiles
-    auto rf_features = [&](int n, float kw_l2) {
+    auto rf_features = [&](int n, float kw_l2) LA_INLINE {
         if constexpr (RF) {
-            constexpr int TILES = (M / 16) * QB;
             const float cnorm = rsqrtf((float)M);
             constexpr int NPASS = (Cfg::NEED_Q ? 1 : 0) + (Cfg::NEED_K ? 1 : 0);
+            const int i = 16 * (wave % QB) + l16;  // this lane's token
+#pragma unroll
             for (int pass = 0; pass < NPASS; ++pass) {
                 const bool isq = Cfg::NEED_Q && pass == 0;
                 const T* sX = isq ? sXq : sXk;
                 const float* xn = sXn + (isq ? 0 : C);
-                for (int t = wave; t < TILES; t += NW) {
-                    const int rb = t / QB, ib = t % QB;
+                Frag<T> xf[KX];
+#pragma unroll
+                for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(sX, XLD, i, 32 * kb, g);
+                const float cfac = (i < n) ? exp_rf<T>(-0.5f * qs * qs * xn[i]) * cnorm : 0.f;
+                const float w = (i < n) ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb) {
-                        const Frag<T> b = frag_rm(sX, XLD, 16 * ib + l16, 32 * kb, g);
-                        if constexpr (sizeof(T) == 2) {
-                            const bf16* hi = (const bf16*)(smem + Cfg::OFF_OM);
-                            const bf16* lo = hi + M * XLD;
-                            mma(acc, frag_rm(hi, XLD, 16 * rb + l16, 32 * kb, g), b);
-                            mma(acc, frag_rm(lo, XLD, 16 * rb + l16, 32 * kb, g), b);
-                        } else {
-                            const float* om = (const float*)(smem + Cfg::OFF_OM);
-                            mma(acc, frag_rm(om, XLD, 16 * rb + l16, 32 * kb, g), b);
-                        }
+                    for (int kb = 0; kb < KX; ++kb) {
+                        mma(acc, om_hi[u][kb], xf[kb]);
+                        if constexpr (sizeof(T) == 2) mma(acc, om_lo[u][kb], xf[kb]);
                     }
-                    // acc[r] = (omega x_i)_{f0+r} with f0 = 16 rb + 4 g, token i = 16 ib + l16
-                    const int i = 16 * ib + l16, f0 = 16 * rb + 4 * g;
-                    const float cfac = (i < n) ? exp_rf<T>(-0.5f * qs * qs * xn[i]) * cnorm : 0.f;
+                    // acc[r] = (omega x_i)_{f0+r} with f0 = 16 rb + 4 g
+                    const int f0 = 16 * (wave / QB + (NW / QB) * u) + 4 * g;
                     float cs[4], sn[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -437,7 +451,6 @@ la_fwd_kernel(const FwdArgs a)
                             st4(sK0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
                             st4(sK0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
                         }
-                        const float w = (i < n) ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
                         st4(sKw0 + TF::off(i, f0), w * cs[0], w * cs[1], w * cs[2], w * cs[3]);
                         st4(sKw0 + TF::off(i, M + f0), w * sn[0], w * sn[1], w * sn[2], w * sn[3]);
                     }
@@ -449,7 +462,7 @@ la_fwd_kernel(const FwdArgs a)
     // ---- outputs and state update of one staged chunk.  dscale: 2^log2D of
     // the state the chunk reads; rescale: factor applied to the accumulators
     // before this chunk's keys are added (1 when none).
-    auto compute = [&](int buf, int n, int64_t t0, float dscale, bool do_rescale, float rescale, int zpar, auto tail_c) {
+    auto compute = [&](int buf, int n, int64_t t0, float dscale, bool do_rescale, float rescale, int zpar, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         const T* const sK = sK0 + (RF ? 0 : buf * TQ);
@@ -577,12 +590,11 @@ la_fwd_kernel(const FwdArgs a)
     // the output stores, is waited for with vmcnt(0), i.e. after the stores.)
     // The ragged last chunk of the sequence, if any, is loaded unprefetched and
     // computed after the loop, so that the loop's stores are unconditional.
-    if constexpr (RF) __syncthreads();  // omega in LDS
 
     // decay bookkeeping of the next chunk, in chunk order (uniform): the
     // pending factor 2^log2D * lambda^n and the key-weight offset
     struct Dec { float dscale, rescale, kw_l2; bool do_rescale; };
-    auto book = [&](int n) {
+    auto book = [&](int n) LA_INLINE {
         Dec d = {decay ? exp2f(log2D) : 1.f, 1.f, 0.f, false};
         if (decay) {
             const float cand = log2D + (float)n * l2l;
@@ -598,7 +610,7 @@ la_fwd_kernel(const FwdArgs a)
         return d;
     };
     // barrier, features (random features), carried z, outputs and state
-    auto finish = [&](int64_t c, int n, const Dec& d, auto tail_c) {
+    auto finish = [&](int64_t c, int n, const Dec& d, auto tail_c) LA_INLINE {
         const int buf = (int)((c - c_beg) & 1);
         __syncthreads();
         if constexpr (RF) {
