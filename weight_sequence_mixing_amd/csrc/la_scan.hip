@@ -8,46 +8,53 @@
 // the same carry the chunked method applies between chunks ("Attention is
 // also an FFN", kwkr.cn/news/587576, sec. 5.2: parallel inside a block,
 // carried between blocks), applied once more between segments.  Each thread
-// owns one element of the [F x (d_v + 1)] state of one (batch, head) row and
+// owns four elements of the [F x (d_v + 1)] state of one (batch, head) row and
 // walks the P segments in order, in place.
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace la {
 
-__global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
+// Threads per workgroup of the scan, and segments whose loads are in flight
+// together (one memory round trip per batch, not one per segment).
+constexpr int kScanThreads = 128;
+constexpr int kScanBatch = 16;
+
+__global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
 {
+    // each thread owns 4 consecutive elements (F*d_v and F are multiples of 4,
+    // so a group never straddles S and z; every base is 16-byte aligned)
     const int SZ = a.F * a.DV + a.F;
-    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int e = 4 * (blockIdx.x * kScanThreads + threadIdx.x);
     const int bh = blockIdx.y;
     if (e >= SZ) return;
     const bool isz = e >= a.F * a.DV;
     const int ez = e - a.F * a.DV;
-    float* base = a.ws + (int64_t)bh * SZ + e;
-    const int64_t slot = (int64_t)a.BH * SZ;
-    // Segments are visited in batches whose loads are all issued before the
-    // first store, so a batch costs one memory round trip, not one per segment.
-    constexpr int BATCH = 8;
-    float loc[BATCH];
+    f32x4* base = (f32x4*)(a.ws + (int64_t)bh * SZ + e);
+    const int64_t slot = (int64_t)a.BH * SZ / 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 loc[kScanBatch];
     if (!a.causal) {
-        float acc = 0.f;
-        for (int s0 = 0; s0 < a.P; s0 += BATCH) {
+        f32x4 acc = zero;
+        for (int s0 = 0; s0 < a.P; s0 += kScanBatch) {
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : 0.f;
+            for (int b = 0; b < kScanBatch; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : zero;
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b) acc += loc[b];
+            for (int b = 0; b < kScanBatch; ++b) acc += loc[b];
         }
         base[0] = acc;
         return;
     }
     const float l2l = a.lam.log2lam[bh % a.H];
-    float carry = 0.f;
-    if (a.S_init) carry = isz ? a.z_init[bh * a.init_zstride + ez] : a.S_init[bh * a.init_stride + e];
-    for (int s0 = 0; s0 < a.P; s0 += BATCH) {
+    f32x4 carry = zero;
+    if (a.S_init)
+        carry = isz ? *(const f32x4*)(a.z_init + bh * a.init_zstride + ez)
+                    : *(const f32x4*)(a.S_init + bh * a.init_stride + e);
+    for (int s0 = 0; s0 < a.P; s0 += kScanBatch) {
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : 0.f;
+        for (int b = 0; b < kScanBatch; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : zero;
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
+        for (int b = 0; b < kScanBatch; ++b) {
             const int s = s0 + b;
             if (s < a.P) {
                 const int64_t L = min((int64_t)(s + 1) * a.seg_len, a.n_len) - (int64_t)s * a.seg_len;
@@ -57,8 +64,8 @@ __global__ void __launch_bounds__(256) la_scan_kernel(const ScanArgs a)
         }
     }
     if (a.S_fin) {
-        if (isz) a.z_fin[bh * a.fin_zstride + ez] = carry;
-        else a.S_fin[bh * a.fin_stride + e] = carry;
+        if (isz) *(f32x4*)(a.z_fin + bh * a.fin_zstride + ez) = carry;
+        else *(f32x4*)(a.S_fin + bh * a.fin_stride + e) = carry;
     }
 }
 
@@ -90,8 +97,9 @@ __global__ void __launch_bounds__(256) la_copy_kernel(float* dst, const float* s
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream)
 {
-    const int SZ = a.F * a.DV + a.F;
-    return launch_kernel(la_scan_kernel, dim3((SZ + 255) / 256, a.BH), dim3(256), stream, a);
+    const int SZ4 = (a.F * a.DV + a.F) / 4;
+    return launch_kernel(la_scan_kernel, dim3((SZ4 + kScanThreads - 1) / kScanThreads, a.BH), dim3(kScanThreads),
+                         stream, a);
 }
 
 static unsigned grid_for(int64_t n)
