@@ -23,7 +23,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "la_oracle.c")
 _LIB = os.path.join(_HERE, "liborc.so")
-PHI_KINDS = {"elu1": 0, "trig_rf": 1}
+PHI_KINDS = {"elu1": 0, "trig_rf": 1, "relu": 2, "trig_rf_plain": 3, "trig_rf_softmax": 4}
+# feature maps with F = d_k (the others are random features with F = 2m)
+ELEMENTWISE = ("elu1", "relu")
 
 _lib = None
 
@@ -42,7 +44,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    # (re)build when the library is missing or older than its source
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build(force=True)
     lib = ctypes.CDLL(_LIB)
     P = ctypes.POINTER(ctypes.c_double)
@@ -79,7 +82,7 @@ def default_threads() -> int:
 
 
 def feature_dim(phi: str, dk: int, omega) -> int:
-    return dk if phi == "elu1" else 2 * int(np.asarray(omega).shape[0])
+    return dk if phi in ELEMENTWISE else 2 * int(np.asarray(omega).shape[0])
 
 
 def phi_map(x, phi: str = "elu1", omega=None, scale: float = 1.0):

@@ -20,28 +20,44 @@
  *                and then queries it; the state starts at zero
  *      sec. 4.2  normaliser z_i = z_{i-1} + phi(k_i), output divided by
  *                phi(q_i)^T z_i plus a small eps; the decay may also be put on z
+ *      sec. 5.1  ReLU named beside elu+1 as a feature map with a controlled
+ *                output range
  *  - "From standard attention to linear attention" (tqpw.cn/news/561043):
  *      sec. 3    non-causal closed form with S = sum phi(k) v^T, Z = sum phi(k)
  *      sec. 4.1  elu(x)+1 with alpha = 1
- *      sec. 4.2  random cos/sin features of omega . x scaled by 1/sqrt(m)
+ *      sec. 4.2  random cos/sin features of omega . x scaled by 1/sqrt(m),
+ *                with a prefactor exp(|x|^2/2) h(x) and an optional h such as
+ *                exp(-|x|^2/2)
  *      sec. 6    autoregressive step: S += k v^T, Z += k, then query
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): update-then-query (inclusive state); the decay multiplies z as well
  * as S; the denominator is (phi(q)^T z + eps); the random-feature map is
  * phi(x) = exp(-|x'|^2/2)/sqrt(m) [cos(omega x'), sin(omega x')] with
- * x' = s x, cosine block first.
+ * x' = s x, cosine block first; the two other prefactors the section's
+ * formula allows are 1/sqrt(m) (h = exp(-|x|^2/2) cancelling exp(|x|^2/2):
+ * the Gaussian kernel) and exp(+|x'|^2/2)/sqrt(m) (h = 1: the kernel
+ * exp(x'.y')).
  */
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_PHI_ELU1 = 0, ORC_PHI_TRIG_RF = 1 };
+enum {
+    ORC_PHI_ELU1 = 0,
+    ORC_PHI_TRIG_RF = 1,          /* prefactor exp(-|x'|^2/2) / sqrt(m) */
+    ORC_PHI_RELU = 2,
+    ORC_PHI_TRIG_RF_PLAIN = 3,    /* prefactor 1 / sqrt(m) */
+    ORC_PHI_TRIG_RF_SOFTMAX = 4   /* prefactor exp(+|x'|^2/2) / sqrt(m) */
+};
 
 /* Feature map of one vector x[dk] -> out[F].
  * ELU1: F = dk, phi(x)_f = x_f + 1 if x_f > 0 else exp(x_f)   (elu, alpha=1, plus 1)
- * TRIG_RF: F = 2m, x' = scale * x, u_r = omega_r . x',
- *          phi = exp(-|x'|^2 / 2) / sqrt(m) * [cos u_1..cos u_m, sin u_1..sin u_m] */
+ * RELU: F = dk, phi(x)_f = x_f if x_f > 0 else 0
+ * TRIG_RF*: F = 2m, x' = scale * x, u_r = omega_r . x',
+ *          phi = c(x') * [cos u_1..cos u_m, sin u_1..sin u_m] with
+ *          c = exp(-|x'|^2/2)/sqrt(m) (TRIG_RF), 1/sqrt(m) (PLAIN),
+ *          exp(+|x'|^2/2)/sqrt(m) (SOFTMAX) */
 void orc_phi(int kind, const double* x, int dk, int m, const double* omega,
              double scale, double* out)
 {
@@ -50,13 +66,21 @@ void orc_phi(int kind, const double* x, int dk, int m, const double* omega,
             out[f] = x[f] > 0.0 ? x[f] + 1.0 : exp(x[f]);
         return;
     }
+    if (kind == ORC_PHI_RELU) {
+        for (int f = 0; f < dk; ++f)
+            out[f] = x[f] > 0.0 ? x[f] : 0.0;
+        return;
+    }
     double* xs = (double*)malloc(sizeof(double) * (size_t)dk);
     double nrm2 = 0.0;
     for (int f = 0; f < dk; ++f) {
         xs[f] = scale * x[f];
         nrm2 += xs[f] * xs[f];
     }
-    double c = exp(-0.5 * nrm2) / sqrt((double)m);
+    double c;
+    if (kind == ORC_PHI_TRIG_RF) c = exp(-0.5 * nrm2) / sqrt((double)m);
+    else if (kind == ORC_PHI_TRIG_RF_SOFTMAX) c = exp(0.5 * nrm2) / sqrt((double)m);
+    else c = 1.0 / sqrt((double)m);
     for (int r = 0; r < m; ++r) {
         double u = 0.0;
         for (int f = 0; f < dk; ++f) u += omega[(size_t)r * dk + f] * xs[f];
@@ -66,7 +90,10 @@ void orc_phi(int kind, const double* x, int dk, int m, const double* omega,
     free(xs);
 }
 
-static int feat_dim(int kind, int dk, int m) { return kind == ORC_PHI_ELU1 ? dk : 2 * m; }
+static int feat_dim(int kind, int dk, int m)
+{
+    return (kind == ORC_PHI_ELU1 || kind == ORC_PHI_RELU) ? dk : 2 * m;
+}
 
 /* Causal forward over nbh independent (batch, head) rows.
  *   q,k [nbh][N][dk], v [nbh][N][dv], lam [nbh], S0 [nbh][F][dv] / z0 [nbh][F]

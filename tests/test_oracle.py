@@ -80,6 +80,65 @@ def test_phi_rf_kernel_monte_carlo(orc):
     assert np.all(np.abs(got - want) < bound), (got, want, bound)
 
 
+def test_phi_relu_closed_values(orc):
+    # ReLU feature map ("Attention is also an FFN", sec. 5.1): max(x, 0) elementwise
+    x = np.array([[0.0, 1.0, -1.0, 2.5, -3.0, 1e-12, -1e-12, -40.0]])
+    got = orc.phi_map(x, "relu")[0]
+    want = [0.0, 1.0, 0.0, 2.5, 0.0, 1e-12, 0.0, 0.0]
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("phi,sgn", [("trig_rf_plain", 0.0), ("trig_rf_softmax", 1.0)])
+def test_phi_rf_prefactor_variants_identity_omega(orc, phi, sgn):
+    # "From standard attention to linear attention", sec. 4.2: prefactor
+    # exp(|x|^2/2) h(x) / sqrt(m); h = exp(-|x|^2/2) gives 1/sqrt(m), h = 1 gives
+    # exp(+|x'|^2/2)/sqrt(m).  With omega = I, u = x' exactly.
+    rng = np.random.default_rng(3)
+    dk = m = 4
+    s = 0.7
+    x = _rand(rng, 3, dk)
+    got = orc.phi_map(x, phi, omega=np.eye(m), scale=s)
+    xs = s * x
+    c = np.exp(0.5 * sgn * np.sum(xs * xs, axis=1, keepdims=True)) / math.sqrt(m)
+    want = np.concatenate([c * np.cos(xs), c * np.sin(xs)], axis=1)
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-16)
+
+
+@pytest.mark.parametrize("phi,sgn", [("trig_rf_plain", 0.0), ("trig_rf_softmax", 1.0)])
+def test_phi_rf_prefactor_variants_norm(orc, phi, sgn):
+    # cos^2 + sin^2 = 1  =>  |phi(x)|^2 = exp(sgn |x'|^2): 1 (plain), exp(|x'|^2) (softmax)
+    rng = np.random.default_rng(4)
+    dk, m = 16, 32
+    om = make_omega(m, dk, seed=13)
+    s = dk ** -0.25
+    x = _rand(rng, 20, dk)
+    p = orc.phi_map(x, phi, omega=om, scale=s)
+    np.testing.assert_allclose(np.sum(p * p, axis=1), np.exp(sgn * np.sum((s * x) ** 2, axis=1)),
+                               rtol=1e-13)
+
+
+@pytest.mark.parametrize("phi", ["trig_rf_plain", "trig_rf_softmax"])
+def test_phi_rf_prefactor_variants_kernel_monte_carlo(orc, phi):
+    # omega ~ N(0, I): E[cos(w.x') cos(w.y') + sin sin] = exp(-|x'-y'|^2/2), so
+    # plain features estimate the Gaussian kernel and softmax ones exp(x'.y')
+    rng = np.random.default_rng(5)
+    dk, m = 8, 8192
+    om = make_omega(m, dk, seed=14)
+    s = 0.8
+    x = _rand(rng, 6, dk, scale=0.6)
+    y = _rand(rng, 6, dk, scale=0.6)
+    got = np.sum(orc.phi_map(x, phi, omega=om, scale=s) * orc.phi_map(y, phi, omega=om, scale=s), axis=1)
+    xs, ys = s * x, s * y
+    if phi == "trig_rf_plain":
+        want = np.exp(-0.5 * np.sum((xs - ys) ** 2, 1))
+        scale_xy = np.ones(len(x))
+    else:
+        want = np.exp(np.sum(xs * ys, 1))
+        scale_xy = np.exp(0.5 * (np.sum(xs ** 2, 1) + np.sum(ys ** 2, 1)))
+    bound = 4.0 * math.sqrt(0.5 / m) * scale_xy
+    assert np.all(np.abs(got - want) < bound), (got, want, bound)
+
+
 # ---------------------------------------------------------------- recurrence
 def _brute_force(pq, pk, v, lam, eps):
     """O(N^2) masked quadratic form, one (b,h) row:
@@ -107,6 +166,10 @@ CASES = [
     ("elu1", 8, 0, 0.999, 0.0),
     ("trig_rf", 4, 6, 1.0, 1e-6),
     ("trig_rf", 8, 4, 0.95, 1e-6),
+    ("relu", 4, 0, 0.9, 1e-6),
+    ("relu", 8, 0, 1.0, 1e-6),
+    ("trig_rf_plain", 4, 6, 1.0, 1e-6),
+    ("trig_rf_softmax", 8, 4, 0.95, 1e-6),
 ]
 
 
@@ -116,8 +179,9 @@ def test_causal_matches_bruteforce(orc, phi, dk, m, lam, eps):
     B, H, N, dv = 2, 2, 37, 3
     q, k = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk)
     v = _rand(rng, B, H, N, dv)
-    om = make_omega(m, dk, seed=5) if phi == "trig_rf" else None
-    s = dk ** -0.25 if phi == "trig_rf" else 1.0
+    rf = phi.startswith("trig_rf")
+    om = make_omega(m, dk, seed=5) if rf else None
+    s = dk ** -0.25 if rf else 1.0
     lam_h = np.array([lam, lam])
     y = orc.causal(q, k, v, lam_h, eps, phi, om, s)
     pq = orc.phi_map(q, phi, om, s)
@@ -162,7 +226,8 @@ def test_noncausal_closed_form(orc):
     rng = np.random.default_rng(4)
     B, H, N, dk, dv = 2, 2, 33, 8, 4
     q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
-    for phi, om, s in (("elu1", None, 1.0), ("trig_rf", make_omega(16, dk, 9), dk ** -0.25)):
+    for phi, om, s in (("elu1", None, 1.0), ("trig_rf", make_omega(16, dk, 9), dk ** -0.25),
+                       ("relu", None, 1.0), ("trig_rf_softmax", make_omega(16, dk, 9), dk ** -0.25)):
         y = orc.noncausal(q, k, v, 1e-6, phi, om, s)
         pq, pk = orc.phi_map(q, phi, om, s), orc.phi_map(k, phi, om, s)
         KV = np.swapaxes(pk, -1, -2) @ v
@@ -253,7 +318,8 @@ def test_split_resume_and_last_row_noncausal(orc):
     np.testing.assert_allclose(y1[:, :, -1], yn[:, :, -1], rtol=1e-12)
 
 
-def test_decode_steps_match_bruteforce(orc):
+@pytest.mark.parametrize("phi", ["elu1", "relu"])
+def test_decode_steps_match_bruteforce(orc, phi):
     # N decode steps from the zero state equal the quadratic form row by row
     rng = np.random.default_rng(10)
     B, H, N, dk, dv = 2, 2, 12, 4, 3
@@ -265,10 +331,10 @@ def test_decode_steps_match_bruteforce(orc):
     ys = []
     for t in range(N):
         yt, S, z = orc.decode_step(q[:, :, t:t + 1], k[:, :, t:t + 1], v[:, :, t:t + 1],
-                                   S, z, lam, 1e-6)
+                                   S, z, lam, 1e-6, phi)
         ys.append(yt)
     y = np.concatenate(ys, axis=2)
-    pq, pk = orc.phi_map(q), orc.phi_map(k)
+    pq, pk = orc.phi_map(q, phi), orc.phi_map(k, phi)
     for b in range(B):
         for h in range(H):
             np.testing.assert_allclose(y[b, h], _brute_force(pq[b, h], pk[b, h], v[b, h],
