@@ -20,7 +20,8 @@
  * --------------------------------
  *  - Tensors are row-major and contiguous: q, k [B,H,N,d_k]; v, y [B,H,N,d_v];
  *    state S [B,H,F,d_v] fp32 and z [B,H,F] fp32.  F = d_k for LA_PHI_ELU1 and
- *    F = 2m for LA_PHI_TRIG_RF.  Every device pointer must be 16-byte aligned.
+ *    LA_PHI_RELU, F = 2m for the random-feature maps.  Every device pointer
+ *    must be 16-byte aligned.
  *  - The caller owns and allocates every device buffer, including the
  *    workspace sized by la_workspace_size().  The library never allocates,
  *    frees or synchronises.  Descriptors and lambda_h are host memory, read
@@ -31,7 +32,7 @@
  *    a non-zero la_status is returned, la_last_error() describes it, and
  *    nothing is enqueued.  A failed launch returns LA_ERR_HIP.  Device faults
  *    surface at the caller's next synchronisation.
- *  - Support matrix: d_k, d_v in {64, 128}; LA_PHI_TRIG_RF with m in {32, 64,
+ *  - Support matrix: d_k, d_v in {64, 128}; random features with m in {32, 64,
  *    128} (F = 2m) and d_k * m <= 8192; in_dtype LA_BF16 or LA_F32; out_dtype
  *    equal to in_dtype or LA_F32.  Other valid shapes return LA_ERR_UNSUPPORTED.
  *  - H <= LA_MAX_HEADS; lambda_h values must lie in [0, 1] (0^0 is taken as 1);
@@ -59,7 +60,14 @@ typedef enum {
 } la_status;
 
 enum { LA_F32 = 0, LA_BF16 = 1 };             /* element types of q, k, v, y */
-enum { LA_PHI_ELU1 = 0, LA_PHI_TRIG_RF = 1 }; /* feature maps                */
+/* feature maps */
+enum {
+    LA_PHI_ELU1 = 0,
+    LA_PHI_TRIG_RF = 1,
+    LA_PHI_RELU = 2,
+    LA_PHI_TRIG_RF_PLAIN = 3,
+    LA_PHI_TRIG_RF_SOFTMAX = 4
+};
 
 #define LA_MAX_HEADS 256
 
@@ -72,7 +80,15 @@ enum { LA_PHI_ELU1 = 0, LA_PHI_TRIG_RF = 1 }; /* feature maps                */
  *                  (same page, sec. 4.2).  omega is a device pointer to an fp32
  *                  [m, d_k] row-major matrix supplied by the caller (the random
  *                  directions are an input: draw them once from a fixed seed and
- *                  share them).  qk_scale is typically d_k^(-1/4).             */
+ *                  share them).  qk_scale is typically d_k^(-1/4).
+ *  LA_PHI_RELU   : phi(x)_f = max(x_f, 0)  ("Attention is also an FFN", sec. 5.1,
+ *                  beside elu+1 as a map with a controlled range).  m = 0,
+ *                  omega = NULL, qk_scale must be 1.  A query whose features are
+ *                  all zero has output 0 (numerator 0, denominator eps).
+ *  LA_PHI_TRIG_RF_PLAIN, LA_PHI_TRIG_RF_SOFTMAX: as LA_PHI_TRIG_RF with the
+ *                  prefactor 1/sqrt(m) (the section's exp(|x|^2/2) h(x) with
+ *                  h = exp(-|x|^2/2): a Gaussian-kernel estimate) or
+ *                  exp(+|x'|^2/2)/sqrt(m) (h = 1: an estimate of exp(x'.y')).  */
 typedef struct {
     int32_t kind;
     int32_t m;

@@ -81,22 +81,27 @@ class Workload:
     dv: int
     dtype: str           # "f32" | "bf16"
     scale: float         # standard deviation of q, k, v
-    phi: str             # "elu1" | "trig_rf"
-    m: int = 0           # random features (F = 2m) for trig_rf
+    phi: str             # "elu1" | "relu" | "trig_rf" | "trig_rf_plain" | "trig_rf_softmax"
+    m: int = 0           # random features (F = 2m) for the trig_rf kinds
     lam: str = "one"     # "one" | "per_head" | "const"
     lam_value: float = 1.0
     lam_lo: float = 0.9
     lam_hi: float = 0.999
     eps: float = 1e-6
     steps: int = 0       # decode steps after the prefix
+    omega: str = "orthogonal"  # random directions: "orthogonal" blocks or plain "gaussian"
+
+    @property
+    def random_features(self) -> bool:
+        return self.phi.startswith("trig_rf")
 
     @property
     def F(self) -> int:
-        return 2 * self.m if self.phi == "trig_rf" else self.dk
+        return 2 * self.m if self.random_features else self.dk
 
     @property
     def qk_scale(self) -> float:
-        return float(self.dk) ** -0.25 if self.phi == "trig_rf" else 1.0
+        return float(self.dk) ** -0.25 if self.random_features else 1.0
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -174,8 +179,10 @@ def make_lambda(wl: Workload, seed: Optional[int] = None, H=None) -> np.ndarray:
     return rng.uniform(wl.lam_lo, wl.lam_hi, size=H).astype(np.float32)
 
 
-def make_omega(m: int, dk: int, seed: int) -> np.ndarray:
+def make_omega(m: int, dk: int, seed: int, orthogonal: bool = True) -> np.ndarray:
     """Random-feature directions omega [m, dk] float32.
+
+    orthogonal=False: rows drawn independently from N(0, I).
 
     Rows are drawn from N(0, I) and orthogonalised in independent blocks of
     dk rows: each block is the Q factor of a dk x dk Gaussian matrix
@@ -185,6 +192,8 @@ def make_omega(m: int, dk: int, seed: int) -> np.ndarray:
     within a block.
     """
     rng = _rng(seed, "omega")
+    if not orthogonal:
+        return np.ascontiguousarray(rng.standard_normal((m, dk)), dtype=np.float32)
     blocks = []
     remaining = m
     while remaining > 0:
@@ -203,7 +212,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None
     seed = wl.index if seed is None else seed
     d = make_qkv(wl, seed, B, H, N)
     d["lam"] = make_lambda(wl, seed, H)
-    d["omega"] = make_omega(wl.m, wl.dk, seed) if wl.phi == "trig_rf" else None
+    d["omega"] = (make_omega(wl.m, wl.dk, seed, orthogonal=wl.omega == "orthogonal")
+                  if wl.random_features else None)
     return d
 
 

@@ -25,9 +25,9 @@ def tdtype(dtype):
 
 
 def phi_for(wl, omega_np):
-    if wl.phi == "trig_rf":
-        return la.Phi("trig_rf", torch.from_numpy(np.ascontiguousarray(omega_np)).to(DEV), wl.qk_scale)
-    return la.Phi()
+    if wl.random_features:
+        return la.Phi(wl.phi, torch.from_numpy(np.ascontiguousarray(omega_np)).to(DEV), wl.qk_scale)
+    return la.Phi(wl.phi)
 
 
 def run_causal(wl, inp, lam=None, out_f32=False, S_in=None, z_in=None, want_state=False, eps=None):

@@ -91,6 +91,11 @@ def _causal(lib, shape, phi=ELU, lam=None, eps=1e-6, q=FAKE, k=FAKE + GAP, v=FAK
     (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_TRIG_RF, 48, FAKE, 0.35)), la.binding.LA_ERR_UNSUPPORTED),
     (dict(shape=_shape(dk=128), phi=LaPhiC(la.LA_PHI_TRIG_RF, 128, FAKE, 0.35)), la.binding.LA_ERR_UNSUPPORTED),
     (dict(shape=_shape(), phi=LaPhiC(9, 0, None, 1.0)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_RELU, 4, None, 1.0)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_RELU, 0, None, 0.5)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_TRIG_RF_SOFTMAX, 64, None, 0.35)), la.binding.LA_ERR_INVALID_ARGUMENT),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_TRIG_RF_PLAIN, 48, FAKE, 0.35)), la.binding.LA_ERR_UNSUPPORTED),
+    (dict(shape=_shape(), phi=LaPhiC(la.LA_PHI_TRIG_RF_PLAIN, 64, FAKE, 0.0)), la.binding.LA_ERR_INVALID_ARGUMENT),
     (dict(shape=_shape(B=4, H=8, N=4096)), la.binding.LA_ERR_WORKSPACE),        # needs a workspace
     (dict(shape=_shape(B=4, H=8, N=4096), ws=FAKE + 5 * (1 << 32), ws_bytes=16), la.binding.LA_ERR_WORKSPACE),
 ])

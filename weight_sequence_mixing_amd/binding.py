@@ -19,7 +19,10 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
 LA_F32, LA_BF16 = 0, 1
-LA_PHI_ELU1, LA_PHI_TRIG_RF = 0, 1
+LA_PHI_ELU1, LA_PHI_TRIG_RF, LA_PHI_RELU, LA_PHI_TRIG_RF_PLAIN, LA_PHI_TRIG_RF_SOFTMAX = 0, 1, 2, 3, 4
+PHI_KINDS = {"elu1": LA_PHI_ELU1, "trig_rf": LA_PHI_TRIG_RF, "relu": LA_PHI_RELU,
+             "trig_rf_plain": LA_PHI_TRIG_RF_PLAIN, "trig_rf_softmax": LA_PHI_TRIG_RF_SOFTMAX}
+ELEMENTWISE = ("elu1", "relu")
 LA_MAX_HEADS = 256
 
 # names declared in include/la.h
@@ -98,26 +101,31 @@ def _check(status: int):
 
 @dataclass
 class Phi:
-    """Feature map: 'elu1' (elu(x)+1) or 'trig_rf' (cos/sin random features).
+    """Feature map: 'elu1' (elu(x)+1), 'relu' (max(x, 0)), or cos/sin random
+    features with the prefactor exp(-|x'|^2/2)/sqrt(m) ('trig_rf'), 1/sqrt(m)
+    ('trig_rf_plain') or exp(+|x'|^2/2)/sqrt(m) ('trig_rf_softmax').
 
-    For 'trig_rf', omega is a device fp32 tensor [m, d_k] and qk_scale the
+    For random features, omega is a device fp32 tensor [m, d_k] and qk_scale the
     factor applied to q and k before the map (typically d_k ** -0.25)."""
     kind: str = "elu1"
     omega: Optional[torch.Tensor] = None
     qk_scale: float = 1.0
 
     def c(self) -> LaPhiC:
-        if self.kind == "elu1":
-            return LaPhiC(LA_PHI_ELU1, 0, None, 1.0)
+        if self.kind not in PHI_KINDS:
+            raise ValueError("unknown feature map %r" % (self.kind,))
+        code = PHI_KINDS[self.kind]
+        if self.kind in ELEMENTWISE:
+            return LaPhiC(code, 0, None, 1.0)
         om = self.omega
         if om is None:
-            return LaPhiC(LA_PHI_TRIG_RF, 0, None, float(self.qk_scale))
+            return LaPhiC(code, 0, None, float(self.qk_scale))
         if om.dtype != torch.float32 or not om.is_contiguous():
             raise ValueError("omega must be a contiguous float32 tensor")
-        return LaPhiC(LA_PHI_TRIG_RF, int(om.shape[0]), om.data_ptr(), float(self.qk_scale))
+        return LaPhiC(code, int(om.shape[0]), om.data_ptr(), float(self.qk_scale))
 
     def F(self, d_k: int) -> int:
-        return d_k if self.kind == "elu1" else 2 * int(self.omega.shape[0])
+        return d_k if self.kind in ELEMENTWISE else 2 * int(self.omega.shape[0])
 
 
 def _dt(t: torch.Tensor) -> int:

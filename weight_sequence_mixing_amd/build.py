@@ -28,6 +28,8 @@ SOURCES = [
     "la_inst_bf16_elu.hip",
     "la_inst_bf16_rf.hip",
     "la_inst_f32.hip",
+    "la_inst_bf16_relu.hip",
+    "la_inst_f32_relu.hip",
     "la_scan.hip",
     "la_api.cpp",
 ]

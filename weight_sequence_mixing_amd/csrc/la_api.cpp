@@ -88,11 +88,30 @@ LaunchEvents& la::launch_events()
 
 namespace {
 
+bool is_rf(int kind)
+{
+    return kind == LA_PHI_TRIG_RF || kind == LA_PHI_TRIG_RF_PLAIN || kind == LA_PHI_TRIG_RF_SOFTMAX;
+}
+
+// The kernel family of a feature-map kind: the three random-feature kinds
+// share one kernel and differ only in the prefactor's sign.
+int kernel_phi(int kind)
+{
+    return is_rf(kind) ? LA_PHI_TRIG_RF : kind;
+}
+
+// s in the random-feature prefactor exp(s |x'|^2 / 2) / sqrt(m)
+float rf_sign(int kind)
+{
+    return kind == LA_PHI_TRIG_RF ? -1.f : (kind == LA_PHI_TRIG_RF_SOFTMAX ? 1.f : 0.f);
+}
+
 const KernelEntry* find_entry(int in_dtype, int phi, int dk, int F, int dv)
 {
-    const KernelEntry* tables[] = {kEntriesBf16Elu, kEntriesBf16Rf, kEntriesF32};
-    const int counts[] = {kNumEntriesBf16Elu, kNumEntriesBf16Rf, kNumEntriesF32};
-    for (int t = 0; t < 3; ++t)
+    const KernelEntry* tables[] = {kEntriesBf16Elu, kEntriesBf16Rf, kEntriesBf16Relu, kEntriesF32, kEntriesF32Relu};
+    const int counts[] = {kNumEntriesBf16Elu, kNumEntriesBf16Rf, kNumEntriesBf16Relu, kNumEntriesF32,
+                          kNumEntriesF32Relu};
+    for (int t = 0; t < 5; ++t)
         for (int i = 0; i < counts[t]; ++i) {
             const KernelEntry& e = tables[t][i];
             if (e.in_dtype == in_dtype && e.phi == phi && e.dk == dk && e.F == F && e.dv == dv) return &e;
@@ -137,11 +156,12 @@ la_status check_shape(const la_shape* s, const la_phi* phi, int64_t min_n, int64
     if ((s->d_k != 64 && s->d_k != 128) || (s->d_v != 64 && s->d_v != 128))
         return fail(LA_ERR_UNSUPPORTED, "d_k=%d d_v=%d: supported head sizes are 64 and 128", s->d_k, s->d_v);
     int F = 0;
-    if (phi->kind == LA_PHI_ELU1) {
-        if (phi->m != 0 || phi->omega != nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "elu+1 takes m = 0 and omega = NULL");
-        if (phi->qk_scale != 1.0f) return fail(LA_ERR_INVALID_ARGUMENT, "elu+1 takes qk_scale = 1");
+    if (phi->kind == LA_PHI_ELU1 || phi->kind == LA_PHI_RELU) {
+        if (phi->m != 0 || phi->omega != nullptr)
+            return fail(LA_ERR_INVALID_ARGUMENT, "elementwise feature maps take m = 0 and omega = NULL");
+        if (phi->qk_scale != 1.0f) return fail(LA_ERR_INVALID_ARGUMENT, "elementwise feature maps take qk_scale = 1");
         F = s->d_k;
-    } else if (phi->kind == LA_PHI_TRIG_RF) {
+    } else if (is_rf(phi->kind)) {
         if (phi->m < 1) return fail(LA_ERR_INVALID_ARGUMENT, "random features need m >= 1 (got %d)", phi->m);
         if (!phi->omega) return fail(LA_ERR_INVALID_ARGUMENT, "random features need omega");
         if (!aligned16(phi->omega)) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be 16-byte aligned");
@@ -154,7 +174,7 @@ la_status check_shape(const la_shape* s, const la_phi* phi, int64_t min_n, int64
     } else {
         return fail(LA_ERR_INVALID_ARGUMENT, "unknown feature map kind %d", phi->kind);
     }
-    const KernelEntry* e = find_entry(s->in_dtype, phi->kind, s->d_k, F, s->d_v);
+    const KernelEntry* e = find_entry(s->in_dtype, kernel_phi(phi->kind), s->d_k, F, s->d_v);
     if (!e) return fail(LA_ERR_UNSUPPORTED, "no kernel for dtype=%d phi=%d d_k=%d F=%d d_v=%d", s->in_dtype, phi->kind,
                         s->d_k, F, s->d_v);
     *F_out = F;
@@ -428,7 +448,8 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
     a.H = (int32_t)shape->H;
     a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
     a.eps = eps;
-    a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
+    a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
+    a.rf_sign = rf_sign(phi->kind);
     a.omega = phi->omega;
     a.lam = lam;
 
@@ -541,7 +562,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     a.cps = cps;
     a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
     a.eps = eps;
-    a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
+    a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
+    a.rf_sign = rf_sign(phi->kind);
     a.omega = phi->omega;
     make_lam(nullptr, shape->H, &a.lam);  // no decay in the non-causal form
 
@@ -605,7 +627,8 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     a.H = (int32_t)shape->H;
     a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
     a.eps = eps;
-    a.qk_scale = phi->kind == LA_PHI_TRIG_RF ? phi->qk_scale : 1.0f;
+    a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
+    a.rf_sign = rf_sign(phi->kind);
     a.omega = phi->omega;
     // alternate the visiting order between calls (no effect on results; see
     // la_decode.h); LA_DECODE_ORDER=plain keeps it ascending for measurements

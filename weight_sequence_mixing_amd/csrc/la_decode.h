@@ -89,7 +89,7 @@ la_decode_kernel(const DecArgs a)
                 n2 += x[d] * x[d];
             }
             const float qs = a.qk_scale;
-            const float c = exp_rf<T>(-0.5f * qs * qs * n2) * rsqrtf((float)M);
+            const float c = exp_rf<T>(a.rf_sign * 0.5f * qs * qs * n2) * rsqrtf((float)M);
             float sn, cs;
             sincos_rf<T>(qs * u, &sn, &cs);
             float* dst = which ? sPk : sPq;
@@ -98,8 +98,8 @@ la_decode_kernel(const DecArgs a)
         }
     } else {
         if (tid < DK) {
-            sPq[tid] = phi_elu1<T>(to_f32(q[tid]));
-            sPk[tid] = phi_elu1<T>(to_f32(k[tid]));
+            sPq[tid] = phi_elem<T, PHI>(to_f32(q[tid]));
+            sPk[tid] = phi_elem<T, PHI>(to_f32(k[tid]));
         }
         if (tid < DW) sV[tid] = to_f32(v[d0 + tid]);
     }

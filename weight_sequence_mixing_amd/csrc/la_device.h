@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/la.h"
+
 namespace la {
 
 typedef __bf16 bf16;
@@ -190,6 +192,15 @@ __device__ __forceinline__ float lam_pow(float log2lam, int k) {
 template <class T> __device__ __forceinline__ float phi_elu1(float x);
 template <> __device__ __forceinline__ float phi_elu1<bf16>(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 template <> __device__ __forceinline__ float phi_elu1<float>(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+// max(x, 0) ("Attention is also an FFN" sec. 5.1 names ReLU beside elu+1).
+__device__ __forceinline__ float phi_relu(float x) { return x > 0.f ? x : 0.f; }
+
+// The elementwise feature maps (F = d_k) by kind.
+template <class T, int PHI> __device__ __forceinline__ float phi_elem(float x) {
+    if constexpr (PHI == LA_PHI_RELU) return phi_relu(x);
+    else return phi_elu1<T>(x);
+}
 
 template <class T> __device__ __forceinline__ void sincos_rf(float u, float* s, float* c);
 template <> __device__ __forceinline__ void sincos_rf<bf16>(float u, float* s, float* c) {

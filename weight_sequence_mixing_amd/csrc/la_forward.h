@@ -360,7 +360,7 @@ la_fwd_kernel(const FwdArgs a)
                 } else {
                     float p[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) p[e] = phi_elu1<T>(x[e]);
+                    for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
                     put_feat(sQ, j, cg * VEC, p);
                 }
             }
@@ -383,7 +383,7 @@ la_fwd_kernel(const FwdArgs a)
                 } else {
                     float p[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) p[e] = phi_elu1<T>(x[e]);
+                    for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
                     if (TAIL && j >= n) {
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) p[e] = 0.f;
@@ -424,7 +424,7 @@ la_fwd_kernel(const FwdArgs a)
                 Frag<T> xf[KX];
 #pragma unroll
                 for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(sX, XLD, i, 32 * kb, g);
-                const float cfac = (i < n) ? exp_rf<T>(-0.5f * qs * qs * xn[i]) * cnorm : 0.f;
+                const float cfac = (i < n) ? exp_rf<T>(a.rf_sign * 0.5f * qs * qs * xn[i]) * cnorm : 0.f;
                 const float w = (i < n) ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
 #pragma unroll
                 for (int u = 0; u < TPW; ++u) {

@@ -41,6 +41,8 @@ struct FwdArgs {
     int32_t out_f32;  // 1: y is fp32, 0: y has the input type
     float eps;
     float qk_scale;
+    // random features: sign s of the prefactor exp(s |x'|^2 / 2) / sqrt(m)
+    float rf_sign;
     const float* omega;  // [m, d_k] fp32 (random features) or null
     // initial state (MODE_CAUSAL, MODE_QUERY): S at
     // S_src + seg*src_seg_stride + bh*src_stride as [F][d_v], z at
@@ -86,6 +88,7 @@ struct DecArgs {
     int32_t out_f32;
     float eps;
     float qk_scale;
+    float rf_sign;  // random features: sign of the prefactor's exponent
     const float* omega;
     int32_t reverse;   // 1: visit head-states in descending order
     LamTable lam;
@@ -110,6 +113,10 @@ extern KernelEntry kEntriesBf16Rf[];
 extern int kNumEntriesBf16Rf;
 extern KernelEntry kEntriesF32[];
 extern int kNumEntriesF32;
+extern KernelEntry kEntriesBf16Relu[];
+extern int kNumEntriesBf16Relu;
+extern KernelEntry kEntriesF32Relu[];
+extern int kNumEntriesF32Relu;
 
 // Per-launch timing: while `start` is set, the next kernel launched through
 // launch_kernel records the dispatch's own begin and end timestamps into
