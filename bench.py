@@ -215,6 +215,34 @@ def workload5(ctx):
                         steps=SECONDARY_STEPS["w5"], warmup=max(ctx.warmup, 5))
 
 
+def feature_map_variant(ctx, base, phi, m=0, steps=20):
+    """A feature-map variant at the shape of workload `base` (2 or 5): the same
+    synthetic inputs and decay, another map (ReLU, a random-feature prefactor,
+    another m)."""
+    import seeded_inputs as si
+    torch = ctx.torch
+    wl = si.workload(base).with_(phi=phi, m=m)
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(base)
+    shape = (wl.B, wl.H, wl.N, wl.dk)
+    gen = tuple(device_normal(torch, g, shape, wl.scale, ctx.dev) for _ in range(3))
+    if wl.random_features:
+        omega = torch.from_numpy(si.make_omega(wl.m, wl.dk, wl.index)).to(ctx.dev)
+        phi_c = ctx.la.Phi(phi, omega, wl.qk_scale)
+    else:
+        phi_c = ctx.la.Phi(phi)
+    name = "%s_causal_B%d_H%d_N%d_d%d_%s" % (phi.replace("_", "") + ("_m%d" % m if m else ""), wl.B, wl.H,
+                                             wl.N, wl.dk, wl.dtype)
+    res = bench_causal(ctx, name, wl.B, wl.H, wl.N, wl.dk, wl.dv, si.make_lambda(wl), phi_c, gen,
+                       steps=steps, warmup=max(ctx.warmup, 5), planned_P=max(1, -(-512 // (wl.B * wl.H))))
+    return res
+
+
+# Feature-map variants measured beside the main workloads: (key, base shape, map, m, steps)
+VARIANTS = (("relu_w2", 2, "relu", 0, 200), ("rf_softmax_w5", 5, "trig_rf_softmax", 128, 25),
+            ("rf_m64_w5", 5, "trig_rf", 64, 25), ("rf_m32_w5", 5, "trig_rf", 32, 25))
+
+
 def workload4_decode(ctx, steps=1024):
     """Decode: prefix of 512 tokens through the causal forward, then `steps`
     single-token steps timed back to back.  Bytes per step: state read and
@@ -385,7 +413,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["w2", "w3", "w4", "w5", "copy"], help="run one workload (profiling)")
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w5", "copy"] + [v[0] for v in VARIANTS],
+                    help="run one workload (profiling)")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="host only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR into "
                          "profiles/traffic_counters.json and exit")
@@ -402,7 +431,10 @@ def main():
     ctx = Ctx(args.steps, args.warmup)
     import seeded_inputs as si
     if args.only and args.only != "w2":
-        fn = {"w3": workload3, "w4": workload4_decode, "w5": workload5, "copy": state_copy}[args.only]
+        fns = {"w3": workload3, "w4": workload4_decode, "w5": workload5, "copy": state_copy}
+        for key, base, phi, m, steps in VARIANTS:
+            fns[key] = (lambda c, b=base, p=phi, mm=m, st=steps: feature_map_variant(c, b, p, mm, st))
+        fn = fns[args.only]
         log("running", args.only)
         print(json.dumps({"only": args.only, "result": fn(ctx)}), flush=True)
         return
@@ -414,6 +446,11 @@ def main():
         for key, fn in (("decode_w4", workload4_decode), ("causal_w3", workload3), ("causal_w5", workload5)):
             log(key, "...")
             extra[key] = fn(ctx)
+            log(json.dumps(extra[key]))
+            ctx.torch.cuda.empty_cache()
+        for key, base, phi, m, steps in VARIANTS:
+            log(key, "...")
+            extra[key] = feature_map_variant(ctx, base, phi, m, steps)
             log(json.dumps(extra[key]))
             ctx.torch.cuda.empty_cache()
     log("workload 2 (headline) ...")
