@@ -111,6 +111,17 @@ typedef struct {
 la_status la_init_state(float* S, float* z, int64_t B, int64_t H, int32_t F, int32_t d_v,
                         la_stream_t stream);
 
+/* Identity-initialised state ("Attention is also an FFN" sec. 6: start S at
+ * the identity or near it, a default history, rather than at zero):
+ * S[b,h,f,d] = alpha if f == d else 0 (a rectangular identity when F != d_v)
+ * and z[b,h,f] = alpha for f < min(F, d_v), else 0 -- the state left by
+ * min(F, d_v) virtual tokens with phi(k) = e_f and v = e_f at weight alpha, so
+ * that numerator and normaliser describe the same history.  alpha must be
+ * finite.  Fill kernel, no hipMemset node (graph-capturable).  Either pointer
+ * may be NULL to skip that buffer. */
+la_status la_init_state_identity(float* S, float* z, int64_t B, int64_t H, int32_t F, int32_t d_v,
+                                 float alpha, la_stream_t stream);
+
 /* Bytes of device workspace that la_forward_causal (causal != 0) or
  * la_forward_noncausal (causal == 0) needs for this shape; 0 when none is
  * needed.  Returns 0 for shapes that fail validation as well. */

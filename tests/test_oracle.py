@@ -341,6 +341,38 @@ def test_decode_steps_match_bruteforce(orc, phi):
                                                              lam[h], 1e-6), rtol=1e-10)
 
 
+@pytest.mark.parametrize("dv", [3, 4, 6])
+def test_identity_initial_state_is_virtual_history(orc, dv):
+    # "Attention is also an FFN", sec. 6: start S at the identity (a default
+    # history).  S0 = alpha I (rectangular), z0 = alpha on the first min(F, dv)
+    # features is the state of min(F, dv) virtual tokens phi(k) = e_f, v = e_f at
+    # time -1, so token i reads it with weight alpha lam^(i+1):
+    #   num_i = alpha lam^(i+1) phi(q_i)^T I + sum_{j<=i} lam^(i-j) (phi q_i . phi k_j) v_j
+    #   den_i = alpha lam^(i+1) sum_{f<min(F,dv)} phi(q_i)_f + sum_{j<=i} lam^(i-j) phi q_i . phi k_j + eps
+    rng = np.random.default_rng(40 + dv)
+    B, H, N, dk = 1, 2, 19, 4
+    alpha, eps = 0.7, 1e-6
+    lam = np.array([0.8, 1.0])
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    F = dk
+    eye = np.eye(F, dv)
+    S0 = np.broadcast_to(alpha * eye, (B, H, F, dv)).copy()
+    z0 = np.zeros((B, H, F))
+    z0[..., :min(F, dv)] = alpha
+    y = orc.causal(q, k, v, lam, eps, S0=S0, z0=z0)
+    pq, pk = orc.phi_map(q), orc.phi_map(k)
+    for h in range(H):
+        for i in range(N):
+            w0 = alpha * lam[h] ** (i + 1)
+            num = w0 * (pq[0, h, i] @ eye)
+            den = w0 * pq[0, h, i, :min(F, dv)].sum()
+            for j in range(i + 1):
+                a = lam[h] ** (i - j) * float(pq[0, h, i] @ pk[0, h, j])
+                num = num + a * v[0, h, j]
+                den += a
+            np.testing.assert_allclose(y[0, h, i], num / (den + eps), rtol=1e-11, atol=1e-14)
+
+
 def test_kappa_is_one_for_positive_features(orc):
     rng = np.random.default_rng(12)
     q, k, v = _rand(rng, 1, 1, 30, 4), _rand(rng, 1, 1, 30, 4), _rand(rng, 1, 1, 30, 2)

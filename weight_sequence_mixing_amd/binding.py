@@ -26,7 +26,7 @@ ELEMENTWISE = ("elu1", "relu")
 LA_MAX_HEADS = 256
 
 # names declared in include/la.h
-EXPORTS = ("la_init_state", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
+EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
            "la_decode_step", "la_status_string", "la_last_error", "la_profile_begin", "la_profile_end",
            "la_kernel_name")
 KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6}
@@ -71,6 +71,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     SP, PP = ctypes.POINTER(LaShapeC), ctypes.POINTER(LaPhiC)
     lib.la_init_state.argtypes = [vp, vp, i64, i64, i32, i32, vp]
     lib.la_init_state.restype = ctypes.c_int
+    lib.la_init_state_identity.argtypes = [vp, vp, i64, i64, i32, i32, f, vp]
+    lib.la_init_state_identity.restype = ctypes.c_int
     lib.la_workspace_size.argtypes = [SP, PP, i32]
     lib.la_workspace_size.restype = sz
     lib.la_forward_causal.argtypes = [vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, sz, vp]
@@ -198,6 +200,14 @@ def la_init_state(S: torch.Tensor, z: torch.Tensor, stream=None) -> None:
     load_library()
     B, H, F, dv = S.shape
     _check(_lib.la_init_state(_ptr(S), _ptr(z), B, H, F, dv, _stream(stream)))
+
+
+def la_init_state_identity(S: torch.Tensor, z: torch.Tensor, alpha: float = 1.0, stream=None) -> None:
+    """S [B,H,F,d_v] = alpha * I (rectangular), z [B,H,F] = alpha on the first
+    min(F, d_v) features, 0 elsewhere (fp32 device tensors)."""
+    load_library()
+    B, H, F, dv = S.shape
+    _check(_lib.la_init_state_identity(_ptr(S), _ptr(z), B, H, F, dv, float(alpha), _stream(stream)))
 
 
 def la_workspace_size(B, H, N, d_k, d_v, in_dtype=LA_BF16, out_dtype=None, phi: Optional[Phi] = None,

@@ -382,6 +382,18 @@ la_status la_init_state(float* S, float* z, int64_t B, int64_t H, int32_t F, int
     return ok();
 }
 
+la_status la_init_state_identity(float* S, float* z, int64_t B, int64_t H, int32_t F, int32_t d_v, float alpha,
+                                 la_stream_t stream)
+{
+    if (B < 1 || H < 1 || F < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARGUMENT, "B, H, F, d_v must be >= 1");
+    if ((S && !aligned16(S)) || (z && !aligned16(z))) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be 16-byte aligned");
+    if (!std::isfinite(alpha)) return fail(LA_ERR_INVALID_ARGUMENT, "alpha must be finite");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = launch(LA_KERNEL_FILL, [&] { return launch_fill_identity(S, z, B * H, F, d_v, alpha, st); });
+    if (e != hipSuccess) return hip_fail(e, "la_init_state_identity launch");
+    return ok();
+}
+
 size_t la_workspace_size(const la_shape* shape, const la_phi* phi, int32_t causal)
 {
     int F = 0;

@@ -664,6 +664,9 @@ la_fwd_kernel(const FwdArgs a)
             zd = a.z_dst + (int64_t)bh * a.dst_zstride;
         }
         if (Sd) {
+            // every wave has consumed its carried-in state (z is read by all
+            // waves) before any writes the final one: S_dst may alias S_src
+            if constexpr (MODE == MODE_CAUSAL) __syncthreads();
             const float ds = decay ? exp2f(log2D) : 1.f;
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb) {

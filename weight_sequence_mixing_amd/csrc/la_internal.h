@@ -140,6 +140,8 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Ar
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+// S[BH][F][DV] = alpha * I (f == d), z[BH][F] = alpha for f < min(F, DV)
+hipError_t launch_fill_identity(float* S, float* z, int64_t BH, int F, int DV, float alpha, hipStream_t stream);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream);
 
 }  // namespace la

@@ -110,6 +110,30 @@ static unsigned grid_for(int64_t n)
     return (unsigned)b;
 }
 
+// S = alpha * I per head-state (rectangular identity) and z = alpha on the
+// first min(F, DV) features; grid-stride over both buffers.
+__global__ void __launch_bounds__(256) la_fill_identity_kernel(float* S, float* z, int64_t BH, int F, int DV,
+                                                              float alpha)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t nS = S ? BH * F * (int64_t)DV : 0, nz = z ? BH * F : 0;
+    const int fz = F < DV ? F : DV;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nS; i += stride) {
+        const int64_t e = i % ((int64_t)F * DV);
+        S[i] = (e / DV == e % DV) ? alpha : 0.f;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nz; i += stride)
+        z[i] = (i % F < fz) ? alpha : 0.f;
+}
+
+hipError_t launch_fill_identity(float* S, float* z, int64_t BH, int F, int DV, float alpha, hipStream_t stream)
+{
+    const int64_t nS = S ? BH * F * (int64_t)DV : 0, nz = z ? BH * F : 0;
+    const int64_t n = nS > nz ? nS : nz;
+    if (n <= 0) return hipSuccess;
+    return launch_kernel(la_fill_identity_kernel, dim3(grid_for(n)), dim3(256), stream, S, z, BH, F, DV, alpha);
+}
+
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream)
 {
     if (n <= 0) return hipSuccess;
