@@ -290,6 +290,57 @@ def workload4_decode(ctx, steps=1024):
     }
 
 
+def workload4_multi(ctx, k_tok=4, calls=256):
+    """Fused multi-token decode at the decode workload's shape: the same
+    512-token prefix, then `calls` calls of la_decode_step with k_tok new tokens
+    per head-state (the state read once, kept on chip across the tokens, written
+    once).  Bytes per call: the state read and written once, plus k_tok tokens of
+    q, k, v, y."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    wl = si.workload(4)
+    B, H, d = wl.B, wl.H, wl.dk
+    F = wl.F
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(4)
+    lam = list(map(float, si.make_lambda(wl)))
+    pq, pk, pv = (device_normal(torch, g, (B, H, wl.N, d), wl.scale, ctx.dev) for _ in range(3))
+    S = torch.empty(B, H, F, d, dtype=torch.float32, device=ctx.dev)
+    z = torch.empty(B, H, F, dtype=torch.float32, device=ctx.dev)
+    yp = torch.empty_like(pq)
+    la.la_forward_causal(pq, pk, pv, yp, lambda_h=lam, eps=wl.eps, S_out=S, z_out=z)
+    del pq, pk, pv, yp
+    nbuf = 16
+    sq, sk, sv = (device_normal(torch, g, (nbuf, B, H, k_tok, d), wl.scale, ctx.dev) for _ in range(3))
+    y = torch.empty(B, H, k_tok, d, dtype=torch.bfloat16, device=ctx.dev)
+    counter = [0]
+
+    def call():
+        i = counter[0] % nbuf
+        counter[0] += 1
+        la.la_decode_step(sq[i], sk[i], sv[i], y, S, z, lambda_h=lam, eps=wl.eps)
+
+    ms = ctx.time_steps(call, steps=calls, warmup=8)
+    kt = ctx.kernel_times(call, steps=min(calls, 128), launches_per_step=4)
+    dom = max(kt.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
+    dom_ms = kt[dom][0]
+    state_bytes = 2 * B * H * (F * d + F) * 4
+    io_bytes = B * H * k_tok * (3 * d * 2 + d * 2)
+    per_call = state_bytes + io_bytes
+    name = "elu1_decode_multi%d_B%d_H%d_d%d_prefix%d_bf16" % (k_tok, B, H, d, wl.N)
+    return {
+        "workload": name, "ms_per_call": round(ms, 4), "tokens_per_call": k_tok, "calls_timed": calls,
+        "state_GBps": round(per_call / (ms * 1e-3) / 1e9, 1),
+        "Mtokens_per_s": round(B * k_tok / (ms * 1e-3) / 1e6, 4),
+        "head_tokens_per_s": round(B * H * k_tok / (ms * 1e-3), 1),
+        "alg_bytes_per_call": per_call,
+        "kernels": {la.la_kernel_name(k): {"mean_ms": round(t, 4), "launches_per_step": n} for k, (t, n) in kt.items()},
+        "dominant_kernel": la.la_kernel_name(dom),
+        "roofline": roofline(per_call / (dom_ms * 1e-3) / 1e9, load_traffic(name, la.la_kernel_name(dom))),
+        "dominant_mean_ms": round(dom_ms, 4),
+    }
+
+
 def state_copy(ctx, B=256, H=32, F=128, D=128, steps=50):
     """Reference stream: the library's state copy (la_forward_causal with N=0
     and S_in -> S_out) over a decode-sized fp32 state; bytes = read + write."""
@@ -413,7 +464,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["w2", "w3", "w4", "w5", "copy"] + [v[0] for v in VARIANTS],
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "copy"] + [v[0] for v in VARIANTS],
                     help="run one workload (profiling)")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="host only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR into "
@@ -431,7 +482,8 @@ def main():
     ctx = Ctx(args.steps, args.warmup)
     import seeded_inputs as si
     if args.only and args.only != "w2":
-        fns = {"w3": workload3, "w4": workload4_decode, "w5": workload5, "copy": state_copy}
+        fns = {"w3": workload3, "w4": workload4_decode, "w5": workload5, "copy": state_copy,
+               "w4multi": workload4_multi}
         for key, base, phi, m, steps in VARIANTS:
             fns[key] = (lambda c, b=base, p=phi, mm=m, st=steps: feature_map_variant(c, b, p, mm, st))
         fn = fns[args.only]
@@ -443,7 +495,9 @@ def main():
     # work also bring the GPU's clocks up before the headline is timed
     extra = {}
     if not args.no_extra:
-        for key, fn in (("decode_w4", workload4_decode), ("causal_w3", workload3), ("causal_w5", workload5)):
+        for key, fn in (("decode_w4", workload4_decode), ("decode_multi4_w4", workload4_multi),
+                        ("decode_multi16_w4", lambda c: workload4_multi(c, 16, 64)),
+                        ("causal_w3", workload3), ("causal_w5", workload5)):
             log(key, "...")
             extra[key] = fn(ctx)
             log(json.dumps(extra[key]))

@@ -96,7 +96,9 @@ typedef struct {
     float qk_scale;
 } la_phi;
 
-/* Problem shape and element types.  For la_decode_step N must be 1. */
+/* Problem shape and element types.  For la_decode_step N is the number of
+ * tokens per head-state, 1 <= N <= LA_DECODE_MAX_TOKENS. */
+#define LA_DECODE_MAX_TOKENS 64
 typedef struct {
     int64_t B, H, N;
     int32_t d_k, d_v;
@@ -157,13 +159,14 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
                                const la_shape* shape, const la_phi* phi, float eps,
                                void* workspace, size_t workspace_bytes, la_stream_t stream);
 
-/* One recurrent decode step, in place ("From standard attention to linear
+/* Recurrent decode steps, in place ("From standard attention to linear
  * attention" sec. 6 autoregressive step, with the decay of "Attention is also
- * an FFN" sec. 3.2): per (b,h)
+ * an FFN" sec. 3.2): per (b,h), for each of the N tokens in order
  *   S <- lambda_h S + phi(k) v^T,  z <- lambda_h z + phi(k),
  *   y  = phi(q)^T S / (phi(q)^T z + eps).
- * q, k: [B,H,1,d_k]; v: [B,H,1,d_v]; y: [B,H,1,d_v]; S [B,H,F,d_v] and
- * z [B,H,F] fp32 are read and overwritten.  shape->N must be 1. */
+ * q, k: [B,H,N,d_k]; v: [B,H,N,d_v]; y: [B,H,N,d_v]; S [B,H,F,d_v] and
+ * z [B,H,F] fp32 are read once and overwritten once.  1 <= shape->N <=
+ * LA_DECODE_MAX_TOKENS (longer runs: la_forward_causal with S_in = S_out). */
 la_status la_decode_step(const void* q, const void* k, const void* v, void* y,
                          float* S, float* z, const la_shape* shape, const la_phi* phi,
                          const float* lambda_h, float eps, la_stream_t stream);

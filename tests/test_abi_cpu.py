@@ -122,10 +122,11 @@ def test_noncausal_and_decode_validation(lib):
     st = lib.la_forward_noncausal(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, ctypes.byref(s),
                                   ctypes.byref(ELU), 1e-6, None, 0, None)
     assert st == la.binding.LA_ERR_INVALID_ARGUMENT
-    s = _shape(N=2)
-    st = lib.la_decode_step(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
-                            FAKE + 0x500000, ctypes.byref(s), ctypes.byref(ELU), None, 1e-6, None)
-    assert st == la.binding.LA_ERR_INVALID_ARGUMENT
+    for n in (0, la.binding.LA_DECODE_MAX_TOKENS + 1):  # tokens per call outside [1, 64]
+        s = _shape(N=n)
+        st = lib.la_decode_step(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                FAKE + 0x500000, ctypes.byref(s), ctypes.byref(ELU), None, 1e-6, None)
+        assert st == la.binding.LA_ERR_INVALID_ARGUMENT
     s = _shape(N=1)
     st = lib.la_decode_step(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, None,
                             FAKE + 0x500000, ctypes.byref(s), ctypes.byref(ELU), None, 1e-6, None)

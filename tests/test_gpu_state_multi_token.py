@@ -83,3 +83,46 @@ def test_multi_token_decode_in_place(k_tok):
     assert rel_err(torch.cat(ys, dim=2), ref[:, :, wl.N:]) < TOL["bf16"]
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=2e-2)
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+
+
+@pytest.mark.parametrize("phi,m,dk,k_tok", [("elu1", 0, 128, 3), ("elu1", 0, 128, 16), ("elu1", 0, 64, 64),
+                                            ("relu", 0, 128, 5), ("trig_rf", 32, 64, 7)])
+def test_decode_step_multi_token(phi, m, dk, k_tok):
+    # la_decode_step with k_tok tokens per head-state per call (state held on
+    # chip across them), three calls after a 96-token prefix
+    wl = si.workload(4).with_(N=96, phi=phi, m=m, dk=dk, dv=dk)
+    B, H, calls = 2, 4, 3
+    omega = si.make_omega(m, dk, 4) if m else None
+    phi_c = la.Phi(phi, torch.from_numpy(omega).to(DEV), wl.qk_scale) if m else la.Phi(phi)
+    pre = si.make_decode_prefix(wl, B=B, H=H)
+    lam = list(map(float, si.make_lambda(wl, H=H)))
+    S = torch.empty(B, H, wl.F, wl.dv, device=DEV)
+    z = torch.empty(B, H, wl.F, device=DEV)
+    q, k, v = (to_dev(pre, n, wl.dtype) for n in ("q", "k", "v"))
+    yp = torch.empty(B, H, wl.N, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_causal(q, k, v, yp, phi=phi_c, lambda_h=lam, eps=wl.eps, S_out=S, z_out=z)
+    rng = np.random.default_rng(100 + k_tok)
+    chunks, ys = [], []
+    for c in range(calls):
+        blk = {}
+        for n, d in (("q", wl.dk), ("k", wl.dk), ("v", wl.dv)):
+            bits, vals = si.round_to_bf16((rng.standard_normal((B, H, k_tok, d)) * wl.scale).astype(np.float32))
+            blk[n], blk[n + "_bits"] = vals, bits
+        chunks.append(blk)
+        qs, ks, vs = (to_dev(blk, n, wl.dtype) for n in ("q", "k", "v"))
+        y = torch.empty(B, H, k_tok, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+        la.la_decode_step(qs, ks, vs, y, S, z, phi=phi_c, lambda_h=lam, eps=wl.eps)
+        ys.append(y)
+    torch.cuda.synchronize()
+    cat = {n: np.concatenate([pre[n]] + [c[n] for c in chunks], axis=2) for n in ("q", "k", "v")}
+    ref, Sr, zr, kap = oracle.causal(cat["q"], cat["k"], cat["v"], np.array(lam), wl.eps, phi, omega, wl.qk_scale,
+                                     want_state=True, want_kappa=True)
+    y = torch.cat(ys, dim=2)
+    err = oracle.rowwise_rel_err(y.float().cpu().numpy(), ref[:, :, wl.N:]) if not m else None
+    if m:
+        from gpu_util import row_errors
+        e = row_errors(y, ref[:, :, wl.N:])
+        assert np.all(e <= TOL["bf16"] * np.maximum(1.0, kap[:, :, wl.N:]))
+    else:
+        assert err < TOL["bf16"], err
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())

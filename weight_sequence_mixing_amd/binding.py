@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
 LA_F32, LA_BF16 = 0, 1
+LA_DECODE_MAX_TOKENS = 64  # include/la.h
 LA_PHI_ELU1, LA_PHI_TRIG_RF, LA_PHI_RELU, LA_PHI_TRIG_RF_PLAIN, LA_PHI_TRIG_RF_SOFTMAX = 0, 1, 2, 3, 4
 PHI_KINDS = {"elu1": LA_PHI_ELU1, "trig_rf": LA_PHI_TRIG_RF, "relu": LA_PHI_RELU,
              "trig_rf_plain": LA_PHI_TRIG_RF_PLAIN, "trig_rf_softmax": LA_PHI_TRIG_RF_SOFTMAX}
@@ -257,7 +258,8 @@ def la_forward_noncausal(q, k, v, y, phi: Optional[Phi] = None, eps: float = 1e-
 
 
 def la_decode_step(q, k, v, y, S, z, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6, stream=None):
-    """One decode step on [B,H,1,d] inputs; updates S [B,H,F,d_v] and z [B,H,F] in place."""
+    """Decode steps on [B,H,N,d] inputs (N tokens per head-state, in order, N <= 64);
+    updates S [B,H,F,d_v] and z [B,H,F] in place."""
     load_library()
     phi = phi or Phi()
     shape = _shape(q, v, y)

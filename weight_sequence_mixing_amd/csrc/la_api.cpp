@@ -618,7 +618,7 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
 {
     int F = 0;
     const KernelEntry* ent = nullptr;
-    la_status st = check_shape(shape, phi, 1, 1, &F, &ent);
+    la_status st = check_shape(shape, phi, 1, LA_DECODE_MAX_TOKENS, &F, &ent);
     if (st != LA_OK) return st;
     if (!S || !z) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be non-NULL");
     if (!aligned16(S) || !aligned16(z)) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be 16-byte aligned");
@@ -637,6 +637,7 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     a.z = z;
     a.BH = (int32_t)BH;
     a.H = (int32_t)shape->H;
+    a.ntok = (int32_t)shape->N;
     a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
     a.eps = eps;
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
