@@ -52,10 +52,13 @@ def _load():
     L, I, D = ctypes.c_long, ctypes.c_int, ctypes.c_double
     lib.orc_phi.argtypes = [I, P, I, I, P, D, P]
     lib.orc_phi.restype = None
-    lib.orc_causal.argtypes = [P, P, P, L, L, I, I, I, I, P, D, P, D, P, P, P, P, P, P]
+    U = ctypes.POINTER(ctypes.c_ubyte)
+    lib.orc_causal.argtypes = [P, P, P, L, L, I, I, I, I, P, D, P, D, U, P, P, P, P, P, P]
     lib.orc_causal.restype = None
     lib.orc_noncausal.argtypes = [P, P, P, L, L, I, I, I, I, P, D, D, P]
     lib.orc_noncausal.restype = None
+    lib.orc_cross.argtypes = [P, P, P, L, L, L, I, I, I, I, P, D, D, U, P]
+    lib.orc_cross.restype = None
     lib.orc_decode_step.argtypes = [P, P, P, L, I, I, I, I, P, D, P, D, P, P, P]
     lib.orc_decode_step.restype = None
     _lib = lib
@@ -71,6 +74,22 @@ def _ptr(a, offset_elems=0):
         return None
     base = a.ctypes.data + 8 * int(offset_elems)
     return ctypes.cast(base, ctypes.POINTER(ctypes.c_double))
+
+
+def _mask_rows(mask, B, H, N):
+    """Key padding mask [B, N] (True / nonzero = the key is ignored) expanded
+    to one uint8 row per (batch, head), or None."""
+    if mask is None:
+        return None
+    mask = np.asarray(mask).astype(bool)
+    assert mask.shape == (B, N), "key padding mask must be [B, N_keys]"
+    return np.ascontiguousarray(np.repeat(mask, H, axis=0).astype(np.uint8))
+
+
+def _uptr(a, offset=0):
+    if a is None:
+        return None
+    return ctypes.cast(a.ctypes.data + int(offset), ctypes.POINTER(ctypes.c_ubyte))
 
 
 def default_threads() -> int:
@@ -118,12 +137,14 @@ def _split(nbh, threads):
 
 
 def causal(q, k, v, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
-           S0=None, z0=None, want_state=False, want_kappa=False, threads=None):
+           S0=None, z0=None, want_state=False, want_kappa=False, threads=None,
+           key_padding_mask=None):
     """Causal forward, per (b,h) one token at a time (update, then query).
 
     q, k: [B,H,N,dk]; v: [B,H,N,dv]; lam: [H] (None = 1); S0: [B,H,F,dv],
-    z0: [B,H,F] or None (zero state).  Returns y [B,H,N,dv] and, if asked,
-    the final (S, z) and the cancellation factor kappa [B,H,N].
+    z0: [B,H,F] or None (zero state); key_padding_mask: [B,N] bool (True =
+    the key adds no term) or None.  Returns y [B,H,N,dv] and, if asked, the
+    final (S, z) and the cancellation factor kappa [B,H,N].
     """
     lib = _load()
     q, k, v, om = _f64(q), _f64(k), _f64(v), _f64(omega)
@@ -138,12 +159,13 @@ def causal(q, k, v, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
     S = np.empty((B, H, F, dv), dtype=np.float64) if want_state else None
     z = np.empty((B, H, F), dtype=np.float64) if want_state else None
     kap = np.empty((B, H, N), dtype=np.float64) if want_kappa else None
+    kpm = _mask_rows(key_padding_mask, B, H, N)
 
     def run(rng):
         a, b = rng
         lib.orc_causal(_ptr(q, a * N * dk), _ptr(k, a * N * dk), _ptr(v, a * N * dv),
                        b - a, N, dk, dv, PHI_KINDS[phi], m, _ptr(om), float(scale),
-                       _ptr(lam_r, a), float(eps),
+                       _ptr(lam_r, a), float(eps), _uptr(kpm, a * N),
                        _ptr(S0, a * F * dv), _ptr(z0, a * F),
                        _ptr(y, a * N * dv), _ptr(S, a * F * dv), _ptr(z, a * F),
                        _ptr(kap, a * N))
@@ -184,6 +206,74 @@ def noncausal(q, k, v, eps=1e-6, phi="elu1", omega=None, scale=1.0, threads=None
         with ThreadPoolExecutor(len(parts)) as ex:
             list(ex.map(run, parts))
     return y
+
+
+def cross(q, k, v, eps=1e-6, phi="elu1", omega=None, scale=1.0, key_padding_mask=None,
+          threads=None):
+    """Non-causal cross attention: q [B,H,Nq,dk] against k [B,H,Nk,dk] and
+    v [B,H,Nk,dv]; key_padding_mask [B,Nk] bool (True = the key is ignored)
+    or None.  Returns y [B,H,Nq,dv]."""
+    lib = _load()
+    q, k, v, om = _f64(q), _f64(k), _f64(v), _f64(omega)
+    B, H, Nq, dk = q.shape
+    Nk = k.shape[2]
+    dv = v.shape[-1]
+    assert k.shape == (B, H, Nk, dk) and v.shape[:3] == (B, H, Nk)
+    m = 0 if om is None else om.shape[0]
+    kpm = _mask_rows(key_padding_mask, B, H, Nk)
+    y = np.empty((B, H, Nq, dv), dtype=np.float64)
+
+    def run(rng):
+        a, b = rng
+        lib.orc_cross(_ptr(q, a * Nq * dk), _ptr(k, a * Nk * dk), _ptr(v, a * Nk * dv),
+                      b - a, Nq, Nk, dk, dv, PHI_KINDS[phi], m, _ptr(om), float(scale),
+                      float(eps), _uptr(kpm, a * Nk), _ptr(y, a * Nq * dv))
+
+    parts = _split(B * H, threads or default_threads())
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return y
+
+
+def causal_varlen(q, k, v, cu_seqlens, lam=None, eps=1e-6, phi="elu1", omega=None,
+                  scale=1.0, S0=None, z0=None, threads=None):
+    """Causal forward over packed sequences of different lengths.
+
+    q, k: [1,H,T,dk], v: [1,H,T,dv]: sequence b holds tokens
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head's row; S0 [B,H,F,dv],
+    z0 [B,H,F] (None = zero) are the sequences' initial states.  Each sequence
+    is its own causal problem: this calls causal() on each slice.  Returns
+    y [1,H,T,dv] (tokens outside every sequence are 0) and the final S, z
+    [B,H,F,dv], [B,H,F].
+    """
+    q, k, v, om = _f64(q), _f64(k), _f64(v), _f64(omega)
+    _, H, T, dk = q.shape
+    dv = v.shape[-1]
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    B = len(cu) - 1
+    assert cu[0] == 0 and all(b >= a for a, b in zip(cu[:-1], cu[1:])) and cu[-1] <= T
+    F = feature_dim(phi, dk, om)
+    y = np.zeros((1, H, T, dv), dtype=np.float64)
+    S = np.empty((B, H, F, dv), dtype=np.float64)
+    z = np.empty((B, H, F), dtype=np.float64)
+    S0, z0 = _f64(S0), _f64(z0)
+    for b in range(B):
+        s0 = None if S0 is None else S0[b:b + 1]
+        zz0 = None if z0 is None else z0[b:b + 1]
+        lo, hi = cu[b], cu[b + 1]
+        if hi == lo:
+            S[b] = 0.0 if s0 is None else s0[0]
+            z[b] = 0.0 if zz0 is None else zz0[0]
+            continue
+        yb, Sb, zb = causal(q[:, :, lo:hi], k[:, :, lo:hi], v[:, :, lo:hi], lam=lam, eps=eps,
+                            phi=phi, omega=om, scale=scale, S0=s0, z0=zz0, want_state=True,
+                            threads=threads)
+        y[:, :, lo:hi] = yb
+        S[b], z[b] = Sb[0], zb[0]
+    return y, S, z
 
 
 def decode_step(q, k, v, S, z, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,

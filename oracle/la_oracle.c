@@ -28,7 +28,10 @@
  *      sec. 4.2  random cos/sin features of omega . x scaled by 1/sqrt(m),
  *                with a prefactor exp(|x|^2/2) h(x) and an optional h such as
  *                exp(-|x|^2/2)
- *      sec. 6    autoregressive step: S += k v^T, Z += k, then query
+ *      sec. 6    autoregressive step: S += k v^T, Z += k, then query; the
+ *                forward takes a key padding mask and a key sequence of its
+ *                own length (cross attention)
+ *      sec. 2    cross attention: N queries against M keys and values
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): update-then-query (inclusive state); the decay multiplies z as well
@@ -37,7 +40,9 @@
  * x' = s x, cosine block first; the two other prefactors the section's
  * formula allows are 1/sqrt(m) (h = exp(-|x|^2/2) cancelling exp(|x|^2/2):
  * the Gaussian kernel) and exp(+|x'|^2/2)/sqrt(m) (h = 1: the kernel
- * exp(x'.y')).
+ * exp(x'.y')).  A key padding mask removes a key's term phi(k_j) v_j^T and
+ * phi(k_j) from every sum; positions keep their indices, so the decay of the
+ * other keys is unchanged.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -97,7 +102,8 @@ static int feat_dim(int kind, int dk, int m)
 
 /* Causal forward over nbh independent (batch, head) rows.
  *   q,k [nbh][N][dk], v [nbh][N][dv], lam [nbh], S0 [nbh][F][dv] / z0 [nbh][F]
- *   (NULL = zero state), y [nbh][N][dv], S_out / z_out (NULL = not written),
+ *   (NULL = zero state), kpm [nbh][N] key padding mask (nonzero = the key
+ *   adds nothing; NULL = none), y [nbh][N][dv], S_out / z_out (NULL = not written),
  *   kappa [nbh][N] (NULL = not computed): the cancellation factor
  *   |phi q|^T zbar / |phi(q)^T z + eps| with zbar the same recurrence on |phi(k)|.
  * Per token: S <- lam S + phi(k) v^T ; z <- lam z + phi(k) ;
@@ -105,6 +111,7 @@ static int feat_dim(int kind, int dk, int m)
 void orc_causal(const double* q, const double* k, const double* v,
                 long nbh, long N, int dk, int dv, int kind, int m,
                 const double* omega, double scale, const double* lam, double eps,
+                const unsigned char* kpm,
                 const double* S0, const double* z0,
                 double* y, double* S_out, double* z_out, double* kappa)
 {
@@ -127,6 +134,8 @@ void orc_causal(const double* q, const double* k, const double* v,
             const double* vi = v + ((size_t)bh * N + i) * dv;
             orc_phi(kind, ki, dk, m, omega, scale, pk);
             orc_phi(kind, qi, dk, m, omega, scale, pq);
+            if (kpm && kpm[(size_t)bh * N + i])  /* padded key: no term */
+                for (int f = 0; f < F; ++f) pk[f] = 0.0;
             for (int f = 0; f < F; ++f) {
                 double* Sf = S + (size_t)f * dv;
                 for (int d = 0; d < dv; ++d) Sf[d] = L * Sf[d] + pk[f] * vi[d];
@@ -180,6 +189,48 @@ void orc_noncausal(const double* q, const double* k, const double* v,
             double den = 0.0;
             for (int f = 0; f < F; ++f) den += p[f] * z[f];
             double* yi = y + ((size_t)bh * N + i) * dv;
+            for (int d = 0; d < dv; ++d) {
+                double num = 0.0;
+                for (int f = 0; f < F; ++f) num += p[f] * S[(size_t)f * dv + d];
+                yi[d] = num / (den + eps);
+            }
+        }
+    }
+    free(S); free(z); free(p);
+}
+
+/* Cross attention, non-causal: Nq queries against Nk keys and values of the
+ * same (batch, head) row.  S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j)
+ * over the keys j that kpm (per row, Nk bytes; NULL = none) does not mark,
+ * then y_i = phi(q_i)^T S / (phi(q_i)^T z + eps) for every query. */
+void orc_cross(const double* q, const double* k, const double* v,
+               long nbh, long Nq, long Nk, int dk, int dv, int kind, int m,
+               const double* omega, double scale, double eps,
+               const unsigned char* kpm, double* y)
+{
+    const int F = feat_dim(kind, dk, m);
+    double* S = (double*)malloc(sizeof(double) * (size_t)F * dv);
+    double* z = (double*)malloc(sizeof(double) * (size_t)F);
+    double* p = (double*)malloc(sizeof(double) * (size_t)F);
+    for (long bh = 0; bh < nbh; ++bh) {
+        memset(S, 0, sizeof(double) * (size_t)F * dv);
+        memset(z, 0, sizeof(double) * (size_t)F);
+        for (long j = 0; j < Nk; ++j) {
+            if (kpm && kpm[(size_t)bh * Nk + j]) continue;
+            const double* kj = k + ((size_t)bh * Nk + j) * dk;
+            const double* vj = v + ((size_t)bh * Nk + j) * dv;
+            orc_phi(kind, kj, dk, m, omega, scale, p);
+            for (int f = 0; f < F; ++f) {
+                for (int d = 0; d < dv; ++d) S[(size_t)f * dv + d] += p[f] * vj[d];
+                z[f] += p[f];
+            }
+        }
+        for (long i = 0; i < Nq; ++i) {
+            const double* qi = q + ((size_t)bh * Nq + i) * dk;
+            orc_phi(kind, qi, dk, m, omega, scale, p);
+            double den = 0.0;
+            for (int f = 0; f < F; ++f) den += p[f] * z[f];
+            double* yi = y + ((size_t)bh * Nq + i) * dv;
             for (int d = 0; d < dv; ++d) {
                 double num = 0.0;
                 for (int f = 0; f < F; ++f) num += p[f] * S[(size_t)f * dv + d];

@@ -385,3 +385,153 @@ def test_rowwise_rel_err_definition(orc):
     ref = np.array([[1.0, -2.0, 0.0], [0.0, 0.0, 0.0]])
     y = np.array([[1.1, -2.0, 0.05], [0.0, 0.0, 0.0]])
     assert abs(orc.rowwise_rel_err(y, ref) - 0.05) < 1e-15
+
+
+# ------------------------------------------------ masks, cross attention, var-len
+def _brute_force_masked(pq, pk, v, lam, eps, keep):
+    """O(N^2) quadratic form of one row with a key padding mask: a key with
+    keep[j] == False is left out of numerator and denominator."""
+    N = pq.shape[0]
+    y = np.zeros((N, v.shape[1]))
+    for i in range(N):
+        num = np.zeros(v.shape[1])
+        den = 0.0
+        for j in range(i + 1):
+            if not keep[j]:
+                continue
+            a = (1.0 if i == j else lam ** (i - j)) * float(pq[i] @ pk[j])
+            num += a * v[j]
+            den += a
+        y[i] = num / (den + eps)
+    return y
+
+
+@pytest.mark.parametrize("phi,dk,m,lam", [("elu1", 4, 0, 0.9), ("elu1", 6, 0, 1.0),
+                                          ("trig_rf", 4, 6, 0.95), ("relu", 4, 0, 0.8)])
+def test_causal_key_padding_mask_bruteforce(orc, phi, dk, m, lam):
+    rng = np.random.default_rng(zlib.crc32(repr(("kpm", phi, dk, lam)).encode()))
+    B, H, N, dv = 2, 2, 29, 3
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    rf = phi.startswith("trig_rf")
+    om = make_omega(m, dk, seed=5) if rf else None
+    s = dk ** -0.25 if rf else 1.0
+    mask = rng.random((B, N)) < 0.3
+    mask[1, :4] = True  # leading padded keys: outputs 0 until the first kept key
+    y, S, z = orc.causal(q, k, v, np.array([lam, lam]), 1e-6, phi, om, s,
+                         want_state=True, key_padding_mask=mask)
+    pq, pk = orc.phi_map(q, phi, om, s), orc.phi_map(k, phi, om, s)
+    for b in range(B):
+        for h in range(H):
+            want = _brute_force_masked(pq[b, h], pk[b, h], v[b, h], lam, 1e-6, ~mask[b])
+            np.testing.assert_allclose(y[b, h], want, rtol=1e-10, atol=1e-12)
+            # final state: sum over kept keys of lam^(N-1-j) phi(k_j) [v_j, 1]^T
+            w = np.where(mask[b], 0.0, lam ** (N - 1 - np.arange(N)))
+            np.testing.assert_allclose(S[b, h], (pk[b, h] * w[:, None]).T @ v[b, h], rtol=1e-11)
+            np.testing.assert_allclose(z[b, h], (pk[b, h] * w[:, None]).sum(0), rtol=1e-11)
+    np.testing.assert_array_equal(y[1, :, :4], 0.0)
+
+
+def test_causal_mask_none_and_all(orc):
+    rng = np.random.default_rng(21)
+    B, H, N, dk, dv = 2, 1, 17, 4, 3
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    S0, z0 = rng.standard_normal((B, H, dk, dv)), rng.random((B, H, dk)) + 0.5
+    none = np.zeros((B, N), bool)
+    a = orc.causal(q, k, v, [0.9], 1e-6, S0=S0, z0=z0, want_state=True)
+    b = orc.causal(q, k, v, [0.9], 1e-6, S0=S0, z0=z0, want_state=True, key_padding_mask=none)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # every key padded: the initial state decays untouched, y_i reads it
+    y, S, z = orc.causal(q, k, v, [0.9], 1e-6, S0=S0, z0=z0, want_state=True,
+                         key_padding_mask=~none)
+    np.testing.assert_allclose(S, S0 * 0.9 ** N, rtol=1e-12)
+    np.testing.assert_allclose(z, z0 * 0.9 ** N, rtol=1e-12)
+    pq = orc.phi_map(q)
+    li = 0.9 ** (np.arange(N) + 1)
+    num = np.einsum("bhnf,bhfd->bhnd", pq, S0) * li[:, None]
+    den = np.einsum("bhnf,bhf->bhn", pq, z0) * li
+    np.testing.assert_allclose(y, num / (den[..., None] + 1e-6), rtol=1e-11)
+
+
+@pytest.mark.parametrize("phi,m", [("elu1", 0), ("trig_rf", 8), ("relu", 0)])
+def test_cross_closed_form_and_mask(orc, phi, m):
+    # y = phi(Q) (phi(K)^T diag(keep) V) / (phi(Q) phi(K)^T keep + eps) with
+    # two library matmuls; Nq != Nk
+    rng = np.random.default_rng(zlib.crc32(repr(("cross", phi)).encode()))
+    B, H, Nq, Nk, dk, dv = 2, 3, 11, 23, 8, 5
+    q, k, v = _rand(rng, B, H, Nq, dk), _rand(rng, B, H, Nk, dk), _rand(rng, B, H, Nk, dv)
+    rf = phi.startswith("trig_rf")
+    om = make_omega(m, dk, seed=3) if rf else None
+    s = dk ** -0.25 if rf else 1.0
+    mask = rng.random((B, Nk)) < 0.4
+    pq, pk = orc.phi_map(q, phi, om, s), orc.phi_map(k, phi, om, s)
+    for kpm in (None, mask):
+        keep = np.ones((B, Nk)) if kpm is None else (~kpm).astype(float)
+        y = orc.cross(q, k, v, 1e-6, phi, om, s, key_padding_mask=kpm)
+        pkk = pk * keep[:, None, :, None]
+        num = pq @ (np.swapaxes(pkk, -1, -2) @ v)
+        den = pq @ pkk.sum(axis=2)[..., None]
+        np.testing.assert_allclose(y, num / (den + 1e-6), rtol=1e-11, atol=1e-14)
+
+
+def test_cross_reduces_to_noncausal_and_to_key_subset(orc):
+    rng = np.random.default_rng(22)
+    B, H, N, dk, dv = 1, 2, 19, 4, 3
+    q, k, v = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dv)
+    # Nq == Nk and no mask: the self-attention non-causal form (its own C loop)
+    np.testing.assert_allclose(orc.cross(q, k, v, 1e-6), orc.noncausal(q, k, v, 1e-6),
+                               rtol=1e-13)
+    # a mask equals dropping the masked keys and values
+    mask = np.zeros((B, N), bool)
+    mask[0, [0, 3, 4, 11, 18]] = True
+    keep = ~mask[0]
+    np.testing.assert_allclose(orc.cross(q, k, v, 1e-6, key_padding_mask=mask),
+                               orc.cross(q, k[:, :, keep], v[:, :, keep], 1e-6), rtol=1e-13)
+    # a single key: every query returns that key's value (up to eps)
+    y1 = orc.cross(q, k[:, :, :1], v[:, :, :1], 0.0)
+    np.testing.assert_allclose(y1, np.broadcast_to(v[:, :, :1], y1.shape), rtol=1e-12)
+
+
+def test_varlen_per_sequence_bruteforce(orc):
+    rng = np.random.default_rng(23)
+    H, dk, dv, lam = 2, 4, 3, 0.85
+    lens = [5, 0, 13, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1]) + 3  # three trailing tokens belong to no sequence
+    q, k, v = _rand(rng, 1, H, T, dk), _rand(rng, 1, H, T, dk), _rand(rng, 1, H, T, dv)
+    B = len(lens)
+    S0, z0 = rng.standard_normal((B, H, dk, dv)), rng.random((B, H, dk)) + 0.5
+    y, S, z = orc.causal_varlen(q, k, v, cu, lam=[lam, 0.5], S0=S0, z0=z0)
+    pq, pk = orc.phi_map(q), orc.phi_map(k)
+    for h, lh in enumerate([lam, 0.5]):
+        for b in range(B):
+            lo, hi = cu[b], cu[b + 1]
+            St, zt = S0[b, h].copy(), z0[b, h].copy()
+            for i in range(lo, hi):  # the recurrence restarted at each sequence
+                St = lh * St + np.outer(pk[0, h, i], v[0, h, i])
+                zt = lh * zt + pk[0, h, i]
+                want = pq[0, h, i] @ St / (pq[0, h, i] @ zt + 1e-6)
+                np.testing.assert_allclose(y[0, h, i], want, rtol=1e-11)
+            np.testing.assert_allclose(S[b, h], St, rtol=1e-12)
+            np.testing.assert_allclose(z[b, h], zt, rtol=1e-12)
+    np.testing.assert_array_equal(y[:, :, cu[-1]:], 0.0)
+
+
+def test_varlen_single_sequence_and_reordering(orc):
+    rng = np.random.default_rng(24)
+    H, T, dk, dv = 2, 31, 4, 3
+    q, k, v = _rand(rng, 1, H, T, dk), _rand(rng, 1, H, T, dk), _rand(rng, 1, H, T, dv)
+    y1, S1, z1 = orc.causal_varlen(q, k, v, [0, T], lam=[0.9, 1.0])
+    y, S, z = orc.causal(q, k, v, [0.9, 1.0], want_state=True)
+    np.testing.assert_array_equal(y1, y)
+    np.testing.assert_array_equal(S1, S)
+    # swapping two packed sequences swaps their outputs and states
+    a, b = 12, T - 12
+    perm = np.r_[a:T, 0:a]
+    yp, Sp, zp = orc.causal_varlen(q[:, :, perm], k[:, :, perm], v[:, :, perm], [0, b, T],
+                                   lam=[0.9, 1.0])
+    ys, Ss, zs = orc.causal_varlen(q, k, v, [0, a, T], lam=[0.9, 1.0])
+    np.testing.assert_allclose(yp[:, :, :b], ys[:, :, a:], rtol=1e-13)
+    np.testing.assert_allclose(yp[:, :, b:], ys[:, :, :a], rtol=1e-13)
+    np.testing.assert_allclose(Sp[[1, 0]], Ss, rtol=1e-13)
+    np.testing.assert_allclose(zp[[1, 0]], zs, rtol=1e-13)
