@@ -159,6 +159,60 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
                                const la_shape* shape, const la_phi* phi, float eps,
                                void* workspace, size_t workspace_bytes, la_stream_t stream);
 
+/* Causal forward with a key padding mask ("From standard attention to linear
+ * attention" sec. 6 gives the forward a key padding mask).  As
+ * la_forward_causal, plus key_padding_mask: device bytes [B,N]; a nonzero
+ * byte drops key n of batch b from every sum -- its term phi(k_n) v_n^T and
+ * phi(k_n) never enter S or z, in the outputs or the final state.  Positions
+ * keep their indices: the decay between two kept keys is still
+ * lambda^(distance).  A query whose kept history is empty reads only the
+ * initial state (y = 0 from a zero state).  Workspace: la_workspace_size with
+ * causal = 1.  A NULL mask is LA_ERR_INVALID_ARGUMENT (use la_forward_causal). */
+la_status la_forward_causal_masked(const void* q, const void* k, const void* v, void* y,
+                                   const la_shape* shape, const la_phi* phi,
+                                   const float* lambda_h, float eps,
+                                   const uint8_t* key_padding_mask,
+                                   const float* S_in, const float* z_in,
+                                   float* S_out, float* z_out,
+                                   void* workspace, size_t workspace_bytes, la_stream_t stream);
+
+/* Causal forward over packed sequences of different lengths.
+ * shape->B is the number of sequences, shape->N the packed token count T:
+ * q, k: [H,T,d_k], v: [H,T,d_v], y: [H,T,d_v] (one row of T tokens per head),
+ * and sequence b holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of every
+ * head's row.  cu_seqlens: device int32 [B+1], non-decreasing from 0 and at
+ * most T (the kernels clamp every offset to [0, T], so other values cannot
+ * address memory outside the rows, but their results are unspecified).  Each
+ * sequence is an independent causal problem (the recurrence of
+ * la_forward_causal restarted at its first token) with its own initial state
+ * S_in[b] / z_in[b] and final state S_out[b] / z_out[b] ([B,H,F,d_v] and
+ * [B,H,F]; same rules as la_forward_causal).  Output rows outside every
+ * sequence are not written.  max_seqlen (host, 0 <= max_seqlen <= T): the
+ * longest sequence; it sizes the segment split and the workspace
+ * (la_workspace_size_varlen) -- results do not depend on it, only speed. */
+size_t la_workspace_size_varlen(const la_shape* shape, int64_t max_seqlen, const la_phi* phi);
+la_status la_forward_causal_varlen(const void* q, const void* k, const void* v, void* y,
+                                   const int32_t* cu_seqlens, int64_t max_seqlen,
+                                   const la_shape* shape, const la_phi* phi,
+                                   const float* lambda_h, float eps,
+                                   const float* S_in, const float* z_in,
+                                   float* S_out, float* z_out,
+                                   void* workspace, size_t workspace_bytes, la_stream_t stream);
+
+/* Cross attention, non-causal ("From standard attention to linear attention"
+ * sec. 2: N queries against M keys and values; sec. 3 and sec. 6 for the
+ * form): per (b,h), S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j) over the
+ * n_kv keys that key_padding_mask keeps, then y_i = phi(q_i)^T S /
+ * (phi(q_i)^T z + eps) for the shape->N queries.  q: [B,H,N,d_k], k:
+ * [B,H,n_kv,d_k], v: [B,H,n_kv,d_v], y: [B,H,N,d_v]; key_padding_mask: NULL or
+ * device bytes [B,n_kv], nonzero = the key is ignored.  N >= 1, n_kv >= 1.
+ * Workspace: la_workspace_size_cross (sized by n_kv). */
+size_t la_workspace_size_cross(const la_shape* shape, int64_t n_kv, const la_phi* phi);
+la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
+                           const la_shape* shape, int64_t n_kv,
+                           const uint8_t* key_padding_mask, const la_phi* phi, float eps,
+                           void* workspace, size_t workspace_bytes, la_stream_t stream);
+
 /* Recurrent decode steps, in place ("From standard attention to linear
  * attention" sec. 6 autoregressive step, with the decay of "Attention is also
  * an FFN" sec. 3.2): per (b,h), for each of the N tokens in order

@@ -29,10 +29,12 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "bf16_bits_rne", "bf16_bits_to_f32",
     "round_to_bf16", "make_qkv", "make_lambda", "make_omega", "make_inputs",
-    "make_decode_step", "make_decode_prefix",
+    "make_decode_step", "make_decode_prefix", "make_kv", "make_key_padding_mask",
+    "make_varlen_lengths", "cu_seqlens", "pack_heads",
 ]
 
-STREAMS = ("q", "k", "v", "lam", "omega", "prefix", "steps")
+# appended streams keep the earlier ones' values (child i of the seed's spawn)
+STREAMS = ("q", "k", "v", "lam", "omega", "prefix", "steps", "mask", "lens", "kv")
 
 
 # --------------------------------------------------------------------------
@@ -245,3 +247,65 @@ def make_decode_step(wl: Workload, step: int, seed: Optional[int] = None, B=None
         if bits is not None:
             out[name + "_bits"] = bits
     return out
+
+
+# --------------------------------------------------------------------------
+# masks, cross attention and packed sequences
+# --------------------------------------------------------------------------
+def make_kv(wl: Workload, n_kv: int, seed: Optional[int] = None, B=None, H=None):
+    """Keys and values of their own length n_kv (cross attention): 'k', 'v'
+    [B,H,n_kv,d] (and '_bits' for bf16), from a stream of their own."""
+    seed = wl.index if seed is None else seed
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    out = {}
+    for i, (name, d) in enumerate((("k", wl.dk), ("v", wl.dv))):
+        bits, vals = _normal(_rng(seed, "kv", i), (B, H, n_kv, d), wl.scale, wl.dtype)
+        out[name] = vals
+        if bits is not None:
+            out[name + "_bits"] = bits
+    return out
+
+
+def make_key_padding_mask(B: int, N: int, kind: str = "right", seed: int = 0, p: float = 0.25) -> np.ndarray:
+    """Key padding mask [B,N] bool, True = padded (ignored) key.
+
+    kind "right": a padded batch -- batch b keeps its first L_b keys, L_0 = N
+    and the others uniform in [1, N]; "random": each key padded independently
+    with probability p; "none" / "all": no key / every key padded."""
+    if kind == "none":
+        return np.zeros((B, N), dtype=bool)
+    if kind == "all":
+        return np.ones((B, N), dtype=bool)
+    rng = _rng(seed, "mask")
+    if kind == "random":
+        return rng.random((B, N)) < p
+    if kind == "right":
+        lens = rng.integers(1, N + 1, size=B)
+        lens[0] = N
+        return np.arange(N)[None, :] >= lens[:, None]
+    raise ValueError(kind)
+
+
+def make_varlen_lengths(n_seq: int, max_len: int, seed: int = 0, empty: int = 0) -> np.ndarray:
+    """Lengths of n_seq packed sequences: log-uniform in [1, max_len] (many
+    short, some long), one of exactly max_len, and `empty` zero-length ones
+    placed at random positions."""
+    rng = _rng(seed, "lens")
+    lens = np.exp(rng.uniform(0.0, np.log(max_len), size=n_seq)).astype(np.int64)
+    lens = np.clip(lens, 1, max_len)
+    lens[rng.integers(n_seq)] = max_len
+    if empty:
+        lens[rng.choice(n_seq, size=empty, replace=False)] = 0
+    return lens
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Offsets [n_seq + 1] int32 of sequences packed back to back."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def pack_heads(wl: Workload, T: int, seed: Optional[int] = None, H=None):
+    """q, k, v for T packed tokens per head: [1,H,T,d] (the packed layout is
+    one row of T tokens per head)."""
+    return make_qkv(wl, seed=seed, B=1, H=H, N=T)

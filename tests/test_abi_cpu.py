@@ -133,3 +133,46 @@ def test_noncausal_and_decode_validation(lib):
     assert st == la.binding.LA_ERR_INVALID_ARGUMENT
     st = lib.la_init_state(FAKE, FAKE, 0, 1, 64, 64, None)
     assert st == la.binding.LA_ERR_INVALID_ARGUMENT
+
+
+def test_masked_cross_varlen_validation(lib):
+    """Argument errors of the mask, cross-attention and packed entry points are
+    caught on the host (no launch)."""
+    E = la.binding.LA_ERR_INVALID_ARGUMENT
+    s = _shape()
+    q, k, v, y = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    # masked causal without a mask
+    st = lib.la_forward_causal_masked(q, k, v, y, ctypes.byref(s), ctypes.byref(ELU), None, 1e-6, None,
+                                      None, None, None, None, None, 0, None)
+    assert st == E and "key_padding_mask" in la.la_last_error()
+    # cross: no keys; y overlapping the (longer) key rows
+    st = lib.la_forward_cross(q, k, v, y, ctypes.byref(s), 0, None, ctypes.byref(ELU), 1e-6, None, 0, None)
+    assert st == E and "n_kv" in la.la_last_error()
+    st = lib.la_forward_cross(q, k, v, k + 64 * 64 * 2 * 2 * 4, ctypes.byref(s), 1024, None, ctypes.byref(ELU),
+                              1e-6, None, 0, None)
+    assert st == E and "alias" in la.la_last_error()
+    # packed sequences: no offsets, misaligned offsets, max_seqlen beyond T
+    sv = _shape(B=3, H=2, N=100)
+    for cu, mx in ((None, 50), (FAKE + 2, 50), (FAKE, 101), (FAKE, -1)):
+        st = lib.la_forward_causal_varlen(q, k, v, y, cu, mx, ctypes.byref(sv), ctypes.byref(ELU), None, 1e-6,
+                                          None, None, None, None, None, 0, None)
+        assert st == E, (cu, mx, st)
+    # y overlapping q's H x T rows
+    st = lib.la_forward_causal_varlen(q, k, v, q + 2 * 100 * 64, FAKE, 50, ctypes.byref(sv), ctypes.byref(ELU),
+                                      None, 1e-6, None, None, None, None, None, 0, None)
+    assert st == E and "alias" in la.la_last_error()
+
+
+def test_cross_and_varlen_workspace_queries(lib):
+    s = _shape(B=1, H=1, N=64, dk=128, dv=128)
+    # sized by the key count, not the query count
+    small = lib.la_workspace_size_cross(ctypes.byref(s), 64, ctypes.byref(ELU))
+    big = lib.la_workspace_size_cross(ctypes.byref(s), 1 << 16, ctypes.byref(ELU))
+    assert big >= 2 * (128 * 128 + 128) * 4 and big > small
+    assert lib.la_workspace_size_cross(ctypes.byref(s), 0, ctypes.byref(ELU)) == 0
+    # packed: sized by the longest sequence; many head-sequences need no segments
+    sv = _shape(B=2, H=1, N=1 << 16, dk=128, dv=128)
+    assert lib.la_workspace_size_varlen(ctypes.byref(sv), 1 << 15, ctypes.byref(ELU)) >= 2 * (128 * 128 + 128) * 4
+    assert lib.la_workspace_size_varlen(ctypes.byref(sv), (1 << 16) + 1, ctypes.byref(ELU)) == 0
+    wide = _shape(B=64, H=16, N=1 << 16)
+    assert lib.la_workspace_size_varlen(ctypes.byref(wide), 1024, ctypes.byref(ELU)) == 0

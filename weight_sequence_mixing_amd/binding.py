@@ -28,6 +28,8 @@ LA_MAX_HEADS = 256
 
 # names declared in include/la.h
 EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
+           "la_forward_causal_masked", "la_workspace_size_varlen", "la_forward_causal_varlen",
+           "la_workspace_size_cross", "la_forward_cross",
            "la_decode_step", "la_status_string", "la_last_error", "la_profile_begin", "la_profile_end",
            "la_kernel_name")
 KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6}
@@ -80,6 +82,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.la_forward_causal.restype = ctypes.c_int
     lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, SP, PP, f, vp, sz, vp]
     lib.la_forward_noncausal.restype = ctypes.c_int
+    lib.la_forward_causal_masked.argtypes = [vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_forward_causal_masked.restype = ctypes.c_int
+    lib.la_workspace_size_varlen.argtypes = [SP, i64, PP]
+    lib.la_workspace_size_varlen.restype = sz
+    lib.la_forward_causal_varlen.argtypes = [vp, vp, vp, vp, vp, i64, SP, PP, vp, f, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_forward_causal_varlen.restype = ctypes.c_int
+    lib.la_workspace_size_cross.argtypes = [SP, i64, PP]
+    lib.la_workspace_size_cross.restype = sz
+    lib.la_forward_cross.argtypes = [vp, vp, vp, vp, SP, i64, vp, PP, f, vp, sz, vp]
+    lib.la_forward_cross.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp]
     lib.la_decode_step.restype = ctypes.c_int
     lib.la_status_string.argtypes = [ctypes.c_int]
@@ -254,6 +266,100 @@ def la_forward_noncausal(q, k, v, y, phi: Optional[Phi] = None, eps: float = 1e-
     ws, ws_bytes = _workspace(shape, pc, False, workspace, q.device)
     _check(_lib.la_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
                                      float(eps), _ptr(ws), ws_bytes, _stream(stream)))
+    return y
+
+
+def _mask_ptr(mask: Optional[torch.Tensor]):
+    if mask is None:
+        return None
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("key_padding_mask must be bool or uint8")
+    return _ptr(mask)  # bool is stored as one byte per element, 0 or 1
+
+
+def _alloc_ws(need: int, workspace, device):
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def la_forward_causal_masked(q, k, v, y, key_padding_mask, phi: Optional[Phi] = None, lambda_h=None,
+                             eps: float = 1e-6, S_in=None, z_in=None, S_out=None, z_out=None, workspace=None,
+                             stream=None):
+    """Causal forward with a key padding mask [B,N] (bool / uint8 on the device,
+    True = the key adds nothing)."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    pc = phi.c()
+    ws, ws_bytes = _workspace(shape, pc, True, workspace, q.device)
+    lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    _check(_lib.la_forward_causal_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape),
+                                         ctypes.byref(pc), lam_ptr, float(eps), _mask_ptr(key_padding_mask),
+                                         _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
+    del lam_keep
+    return y
+
+
+def la_workspace_size_varlen(B, H, T, max_seqlen, d_k, d_v, in_dtype=LA_BF16, out_dtype=None,
+                             phi: Optional[Phi] = None) -> int:
+    load_library()
+    phi = phi or Phi()
+    shape = LaShapeC(B, H, T, d_k, d_v, in_dtype, in_dtype if out_dtype is None else out_dtype)
+    pc = phi.c()
+    return int(_lib.la_workspace_size_varlen(ctypes.byref(shape), int(max_seqlen), ctypes.byref(pc)))
+
+
+def la_forward_causal_varlen(q, k, v, y, cu_seqlens, max_seqlen: int, phi: Optional[Phi] = None, lambda_h=None,
+                             eps: float = 1e-6, S_in=None, z_in=None, S_out=None, z_out=None, workspace=None,
+                             stream=None):
+    """Causal forward over packed sequences: q, k [H,T,d_k], v, y [H,T,d_v];
+    cu_seqlens: int32 device tensor [B+1]; states [B,H,F,d_v] / [B,H,F]."""
+    load_library()
+    phi = phi or Phi()
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    H, T, dk = q.shape
+    B = cu_seqlens.numel() - 1
+    shape = LaShapeC(B, H, T, dk, v.shape[-1], _dt(q), _dt(y))
+    pc = phi.c()
+    need = int(_lib.la_workspace_size_varlen(ctypes.byref(shape), int(max_seqlen), ctypes.byref(pc)))
+    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
+    lam_keep, lam_ptr = _lam(lambda_h, H)
+    _check(_lib.la_forward_causal_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(cu_seqlens), int(max_seqlen),
+                                         ctypes.byref(shape), ctypes.byref(pc), lam_ptr, float(eps), _ptr(S_in),
+                                         _ptr(z_in), _ptr(S_out), _ptr(z_out), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
+    del lam_keep
+    return y
+
+
+def la_workspace_size_cross(B, H, N, n_kv, d_k, d_v, in_dtype=LA_BF16, out_dtype=None,
+                            phi: Optional[Phi] = None) -> int:
+    load_library()
+    phi = phi or Phi()
+    shape = LaShapeC(B, H, N, d_k, d_v, in_dtype, in_dtype if out_dtype is None else out_dtype)
+    pc = phi.c()
+    return int(_lib.la_workspace_size_cross(ctypes.byref(shape), int(n_kv), ctypes.byref(pc)))
+
+
+def la_forward_cross(q, k, v, y, key_padding_mask=None, phi: Optional[Phi] = None, eps: float = 1e-6,
+                     workspace=None, stream=None):
+    """Non-causal cross attention: q [B,H,N,d_k] against k [B,H,M,d_k] and
+    v [B,H,M,d_v]; optional key_padding_mask [B,M]; writes y [B,H,N,d_v]."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    n_kv = int(k.shape[2])
+    pc = phi.c()
+    need = int(_lib.la_workspace_size_cross(ctypes.byref(shape), n_kv, ctypes.byref(pc)))
+    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
+    _check(_lib.la_forward_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), n_kv,
+                                 _mask_ptr(key_padding_mask), ctypes.byref(pc), float(eps), _ptr(ws), ws_bytes,
+                                 _stream(stream)))
     return y
 
 

@@ -234,14 +234,16 @@ void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps)
     *P = (int)((NC + *cps - 1) / *cps);
 }
 
-Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal)
+// Plan of a forward over rows of N tokens (causal: may be cut into windows;
+// packed variable-length rows: N is the longest sequence, one window).
+Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, bool windows = true)
 {
     Plan p;
     p.C = e->C;
     p.SZ = (int64_t)F * s->d_v + F;
     const int64_t BH = s->B * s->H;
     const int64_t NC = (s->N + p.C - 1) / p.C;
-    int W = causal ? env_int("LA_WINDOWS", 1) : 1;
+    int W = (causal && windows) ? env_int("LA_WINDOWS", 1) : 1;
     if (W < 1) W = 1;
     if (W > NC) W = (int)(NC > 0 ? NC : 1);
     p.W = W;
@@ -267,17 +269,25 @@ la_status check_ws(const Plan& p, void* ws, size_t ws_bytes)
     return LA_OK;
 }
 
-la_status check_io(const void* q, const void* k, const void* v, const void* y, const la_shape* s)
+// Pointer checks for q, y with rows_q rows and k, v with rows_k rows.
+la_status check_io_rows(const void* q, const void* k, const void* v, const void* y, const la_shape* s,
+                        size_t rows_q, size_t rows_k)
 {
     if (!q || !k || !v || !y) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and y must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, y must be 16-byte aligned");
-    const size_t rows = (size_t)s->B * s->H * s->N;
-    const size_t nq = rows * s->d_k * elem_size(s->in_dtype), nv = rows * s->d_v * elem_size(s->in_dtype);
-    const size_t ny = rows * s->d_v * elem_size(s->out_dtype);
-    if (overlaps(y, ny, q, nq) || overlaps(y, ny, k, nq) || overlaps(y, ny, v, nv))
+    const size_t es = elem_size(s->in_dtype);
+    const size_t nq = rows_q * s->d_k * es, nk = rows_k * s->d_k * es, nv = rows_k * s->d_v * es;
+    const size_t ny = rows_q * s->d_v * elem_size(s->out_dtype);
+    if (overlaps(y, ny, q, nq) || overlaps(y, ny, k, nk) || overlaps(y, ny, v, nv))
         return fail(LA_ERR_INVALID_ARGUMENT, "y must not alias q, k or v");
     return LA_OK;
+}
+
+la_status check_io(const void* q, const void* k, const void* v, const void* y, const la_shape* s)
+{
+    const size_t rows = (size_t)s->B * s->H * s->N;
+    return check_io_rows(q, k, v, y, s, rows, rows);
 }
 
 la_status check_eps(float eps)
@@ -405,10 +415,16 @@ size_t la_workspace_size(const la_shape* shape, const la_phi* phi, int32_t causa
     return make_plan(shape, F, e, causal != 0).ws_bytes;
 }
 
-la_status la_forward_causal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
-                            const la_phi* phi, const float* lambda_h, float eps, const float* S_in,
-                            const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
-                            la_stream_t stream)
+namespace {
+
+// Causal forward shared by the fixed-length, masked and packed entry points.
+// kpm: key padding mask [B][N] bytes or null.  cu: packed sequences (device
+// [B+1] offsets into head rows of N tokens) or null; max_len then plans the
+// segments (the longest sequence).
+la_status forward_causal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                         const la_phi* phi, const float* lambda_h, float eps, const uint8_t* kpm,
+                         const int32_t* cu, int64_t max_len, const float* S_in, const float* z_in, float* S_out,
+                         float* z_out, void* workspace, size_t workspace_bytes, la_stream_t stream)
 {
     int F = 0;
     const KernelEntry* ent = nullptr;
@@ -440,14 +456,22 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
         if (e != hipSuccess) return hip_fail(e, "la_forward_causal (N=0)");
         return ok();
     }
-    if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
-    const Plan plan = make_plan(shape, F, ent, true);
+    la_shape plan_shape = *shape;
+    if (cu) {
+        // packed rows: q, k, v, y hold H rows of N tokens
+        const size_t rows = (size_t)shape->H * shape->N;
+        if ((st = check_io_rows(q, k, v, y, shape, rows, rows)) != LA_OK) return st;
+        plan_shape.N = max_len;
+    } else {
+        if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
+    }
+    const Plan plan = make_plan(&plan_shape, F, ent, true, cu == nullptr);
     if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
 
     float* ws = static_cast<float*>(workspace);
     float* segs = ws;                                                     // [P][BH][SZ]
     float* carry = ws ? ws + (plan.Pmax > 1 ? (size_t)plan.Pmax * BH * plan.SZ : 0) : nullptr;  // [BH][SZ]
-    const int64_t NC = (shape->N + plan.C - 1) / plan.C;
+    const int64_t NC = (plan_shape.N + plan.C - 1) / plan.C;
 
     FwdArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -463,14 +487,22 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
     a.rf_sign = rf_sign(phi->kind);
     a.omega = phi->omega;
+    a.kpm = kpm;
+    a.kpm_stride = shape->N;
+    a.cu_seqlens = cu;
     a.lam = lam;
 
     for (int w = 0; w < plan.W; ++w) {
         const int64_t c0 = (int64_t)w * NC / plan.W, c1 = (int64_t)(w + 1) * NC / plan.W;
-        const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, shape->N) - n0;
+        const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, plan_shape.N) - n0;
         int P = 1;
         int64_t cps = 1;
-        cut_segments(c1 - c0, BH, &P, &cps);
+        if (cu) {
+            // every sequence is cut into the same P segments of its own length
+            P = plan.Pmax;
+        } else {
+            cut_segments(c1 - c0, BH, &P, &cps);
+        }
         // state entering and leaving this window
         const float* Si = nullptr;
         const float* zi = nullptr;
@@ -514,6 +546,9 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
             sa.n_len = n_len;
             sa.seg_len = cps * plan.C;
             sa.causal = 1;
+            sa.cu_seqlens = cu;
+            sa.N = shape->N;
+            sa.C = plan.C;
             sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
             sa.lam = lam;
@@ -538,6 +573,56 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
         }
     }
     return ok();
+}
+
+}  // namespace
+
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                            const la_phi* phi, const float* lambda_h, float eps, const float* S_in,
+                            const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                            la_stream_t stream)
+{
+    return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, nullptr, nullptr, 0, S_in, z_in, S_out, z_out,
+                          workspace, workspace_bytes, stream);
+}
+
+la_status la_forward_causal_masked(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                                   const la_phi* phi, const float* lambda_h, float eps,
+                                   const uint8_t* key_padding_mask, const float* S_in, const float* z_in,
+                                   float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                                   la_stream_t stream)
+{
+    if (!key_padding_mask) return fail(LA_ERR_INVALID_ARGUMENT, "key_padding_mask is NULL");
+    return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, key_padding_mask, nullptr, 0, S_in, z_in, S_out,
+                          z_out, workspace, workspace_bytes, stream);
+}
+
+size_t la_workspace_size_varlen(const la_shape* shape, int64_t max_seqlen, const la_phi* phi)
+{
+    int F = 0;
+    const KernelEntry* e = nullptr;
+    const std::string saved = g_last_error;
+    const la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &e);
+    g_last_error = saved;
+    if (st != LA_OK || shape->N == 0 || max_seqlen < 0 || max_seqlen > shape->N) return 0;
+    la_shape ps = *shape;
+    ps.N = max_seqlen;
+    return make_plan(&ps, F, e, true, false).ws_bytes;
+}
+
+la_status la_forward_causal_varlen(const void* q, const void* k, const void* v, void* y,
+                                   const int32_t* cu_seqlens, int64_t max_seqlen, const la_shape* shape,
+                                   const la_phi* phi, const float* lambda_h, float eps, const float* S_in,
+                                   const float* z_in, float* S_out, float* z_out, void* workspace,
+                                   size_t workspace_bytes, la_stream_t stream)
+{
+    if (!cu_seqlens) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+    if ((uintptr_t)cu_seqlens % 4) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+    if (shape && (max_seqlen < 0 || max_seqlen > shape->N))
+        return fail(LA_ERR_INVALID_ARGUMENT, "max_seqlen=%lld outside [0, N=%lld]", (long long)max_seqlen,
+                    (long long)shape->N);
+    return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, nullptr, cu_seqlens, max_seqlen, S_in, z_in, S_out,
+                          z_out, workspace, workspace_bytes, stream);
 }
 
 la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
@@ -610,6 +695,106 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     qa.src_seg_stride = 0;
     if ((e = launch(LA_KERNEL_FWD_QUERY, [&] { return ent->fwd(qa, MODE_QUERY, strm); })) != hipSuccess)
         return hip_fail(e, "query launch");
+    return ok();
+}
+
+size_t la_workspace_size_cross(const la_shape* shape, int64_t n_kv, const la_phi* phi)
+{
+    int F = 0;
+    const KernelEntry* e = nullptr;
+    const std::string saved = g_last_error;
+    const la_status st = check_shape(shape, phi, 1, INT64_MAX / 4, &F, &e);
+    g_last_error = saved;
+    if (st != LA_OK || n_kv < 1 || n_kv > INT64_MAX / 4) return 0;
+    la_shape ks = *shape;
+    ks.N = n_kv;
+    return make_plan(&ks, F, e, false).ws_bytes;
+}
+
+la_status la_forward_cross(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                           int64_t n_kv, const uint8_t* key_padding_mask, const la_phi* phi, float eps,
+                           void* workspace, size_t workspace_bytes, la_stream_t stream)
+{
+    int F = 0;
+    const KernelEntry* ent = nullptr;
+    la_status st = check_shape(shape, phi, 1, INT64_MAX / 4, &F, &ent);
+    if (st != LA_OK) return st;
+    if (n_kv < 1 || n_kv > INT64_MAX / 4) return fail(LA_ERR_INVALID_ARGUMENT, "n_kv=%lld must be >= 1", (long long)n_kv);
+    if ((st = check_eps(eps)) != LA_OK) return st;
+    const int64_t BH = shape->B * shape->H;
+    if (BH > 65535) return fail(LA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)BH);
+    if ((st = check_io_rows(q, k, v, y, shape, (size_t)BH * shape->N, (size_t)BH * n_kv)) != LA_OK) return st;
+    la_shape ks = *shape;
+    ks.N = n_kv;
+    const Plan plan = make_plan(&ks, F, ent, false);
+    if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+
+    FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.BH = (int32_t)BH;
+    a.H = (int32_t)shape->H;
+    a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
+    a.eps = eps;
+    a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
+    a.rf_sign = rf_sign(phi->kind);
+    a.omega = phi->omega;
+    make_lam(nullptr, shape->H, &a.lam);  // no decay in the non-causal form
+
+    // pass 1 over the n_kv keys: segment sums of phi(k) [v, 1]^T
+    int Pk = 1;
+    int64_t cpsk = 1;
+    cut_segments((n_kv + plan.C - 1) / plan.C, BH, &Pk, &cpsk);
+    FwdArgs l = a;
+    l.N = n_kv;
+    l.n_len = n_kv;
+    l.P = Pk;
+    l.cps = cpsk;
+    l.kpm = key_padding_mask;
+    l.kpm_stride = n_kv;
+    l.S_dst = ws;
+    l.z_dst = ws + (int64_t)F * shape->d_v;
+    l.dst_stride = plan.SZ;
+    l.dst_zstride = plan.SZ;
+    hipError_t e;
+    if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
+        return hip_fail(e, "cross state sum launch");
+    if (Pk > 1) {
+        ScanArgs sa;
+        std::memset(&sa, 0, sizeof(sa));
+        sa.ws = ws;
+        sa.P = Pk;
+        sa.BH = (int32_t)BH;
+        sa.H = (int32_t)shape->H;
+        sa.F = F;
+        sa.DV = shape->d_v;
+        sa.n_len = n_kv;
+        sa.seg_len = cpsk * plan.C;
+        sa.causal = 0;
+        if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+            return hip_fail(e, "cross state reduction launch");
+    }
+    // pass 2 over the N queries
+    int Pq = 1;
+    int64_t cpsq = 1;
+    cut_segments((shape->N + plan.C - 1) / plan.C, BH, &Pq, &cpsq);
+    FwdArgs qa = a;
+    qa.N = shape->N;
+    qa.n_len = shape->N;
+    qa.P = Pq;
+    qa.cps = cpsq;
+    qa.S_src = ws;
+    qa.z_src = ws + (int64_t)F * shape->d_v;
+    qa.src_stride = plan.SZ;
+    qa.src_zstride = plan.SZ;
+    qa.src_seg_stride = 0;
+    if ((e = launch(LA_KERNEL_FWD_QUERY, [&] { return ent->fwd(qa, MODE_QUERY, strm); })) != hipSuccess)
+        return hip_fail(e, "cross query launch");
     return ok();
 }
 

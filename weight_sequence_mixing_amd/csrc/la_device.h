@@ -184,6 +184,20 @@ template <int W> struct ColRead<float, W> {
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // lambda^k from log2(lambda), with lambda^0 = 1 also for lambda = 0.
+// Token range [s0, s1) of packed sequence b in a head row of N tokens, the
+// offsets clamped so that any values stay inside the row.
+__device__ __forceinline__ void varlen_range(const int32_t* cu, int b, int64_t N, int64_t* s0, int64_t* s1) {
+    const int64_t a = min(max((int64_t)cu[b], (int64_t)0), N);
+    *s0 = a;
+    *s1 = min(max((int64_t)cu[b + 1], a), N);
+}
+
+// Chunks per segment when n tokens are cut into P segments of whole C-token
+// chunks (0 for an empty sequence).
+__device__ __forceinline__ int64_t varlen_cps(int64_t n, int C, int P) {
+    return ((n + C - 1) / C + P - 1) / P;
+}
+
 __device__ __forceinline__ float lam_pow(float log2lam, int k) {
     return k == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)k * log2lam);
 }

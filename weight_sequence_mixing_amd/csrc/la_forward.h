@@ -165,11 +165,23 @@ la_fwd_kernel(const FwdArgs a)
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
     const float l2l = (MODE == MODE_QUERY) ? 0.f : a.lam.log2lam[h];
     const bool decay = l2l != 0.f;  // uniform over the workgroup
-    const int64_t NC = (a.n_len + C - 1) / C;
-    const int64_t c_beg = (int64_t)seg * a.cps, c_end = min(NC, c_beg + a.cps);
-    const T* qg = (const T*)a.q + ((int64_t)bh * a.N + a.n0) * DK;
-    const T* kg = (const T*)a.k + ((int64_t)bh * a.N + a.n0) * DK;
-    const T* vg = (const T*)a.v + ((int64_t)bh * a.N + a.n0) * DV;
+    // token range of this row: [n0, n0 + n_len) of row bh, or the packed
+    // sequence bh / H of head row h
+    int64_t row0 = (int64_t)bh * a.N + a.n0, n_len = a.n_len, cps = a.cps;
+    if (a.cu_seqlens) {
+        int64_t s0, s1;
+        varlen_range(a.cu_seqlens, bh / a.H, a.N, &s0, &s1);
+        row0 = (int64_t)h * a.N + s0;
+        n_len = s1 - s0;
+        cps = varlen_cps(n_len, C, a.P);
+    }
+    const int64_t NC = (n_len + C - 1) / C;
+    const int64_t c_beg = (int64_t)seg * cps, c_end = min(NC, c_beg + cps);
+    const T* qg = (const T*)a.q + row0 * DK;
+    const T* kg = (const T*)a.k + row0 * DK;
+    const T* vg = (const T*)a.v + row0 * DV;
+    // key padding mask of this row (keys only)
+    const uint8_t* kp = (Cfg::NEED_K && a.kpm) ? a.kpm + (int64_t)(bh / a.H) * a.kpm_stride + a.n0 : nullptr;
     const float qs = a.qk_scale;
     const Frag<T> ones = frag_ones<T>();
 
@@ -219,10 +231,11 @@ la_fwd_kernel(const FwdArgs a)
     // fixed per-thread offsets from a uniform base.  In a ragged last chunk,
     // rows past the end re-read the last valid row (always in bounds) and are
     // replaced by zeros in registers, so the loads stay unconditional.
-    const bool ragged = c_end > c_beg && c_end * C > a.n_len;
+    const bool ragged = c_end > c_beg && c_end * C > n_len;
     const int64_t c_full = ragged ? c_end - 1 : c_end;
-    const int n_tail = ragged ? (int)(a.n_len - c_full * C) : C;
+    const int n_tail = ragged ? (int)(n_len - c_full * C) : C;
     uint4 rq[Cfg::NEED_Q ? RQ : 1], rk[Cfg::NEED_K ? RQ : 1], rv[Cfg::NEED_K ? RV : 1];
+    int mk[Cfg::NEED_K ? RQ : 1];  // mask bytes of this thread's key rows
     auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const uint4 zero = {0u, 0u, 0u, 0u};
@@ -245,6 +258,11 @@ la_fwd_kernel(const FwdArgs a)
         if constexpr (Cfg::NEED_K) {
             load_rows(rk, kg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
             load_rows(rv, vg + t0 * DV, VPRV, DV, RV, n, tail_c);
+#pragma unroll
+            for (int r = 0; r < RQ; ++r) {
+                const int j = (tid + r * NT) / VPRQ;
+                mk[r] = kp ? (int)kp[t0 + (decltype(tail_c)::value ? min(j, n - 1) : j)] : 0;
+            }
         }
     };
 
@@ -379,12 +397,13 @@ la_fwd_kernel(const FwdArgs a)
                         s2 += x[e] * x[e] + x[e + 1] * x[e + 1] + x[e + 2] * x[e + 2] + x[e + 3] * x[e + 3];
                     }
                     s2 = wave_sum_xor(s2, 1, VPRQ / 2);
-                    if (cg == 0) sXn[C + j] = s2;
+                    // a padded key is marked by a negative norm
+                    if (cg == 0) sXn[C + j] = mk[r] ? -1.f : s2;
                 } else {
                     float p[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
-                    if (TAIL && j >= n) {
+                    if ((TAIL && j >= n) || mk[r]) {
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) p[e] = 0.f;
                     }
@@ -424,8 +443,9 @@ la_fwd_kernel(const FwdArgs a)
                 Frag<T> xf[KX];
 #pragma unroll
                 for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(sX, XLD, i, 32 * kb, g);
-                const float cfac = (i < n) ? exp_rf<T>(a.rf_sign * 0.5f * qs * qs * xn[i]) * cnorm : 0.f;
-                const float w = (i < n) ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
+                const bool use = i < n && (isq || !(xn[i] < 0.f));  // not past the end, not padded
+                const float cfac = use ? exp_rf<T>(a.rf_sign * 0.5f * qs * qs * xn[i]) * cnorm : 0.f;
+                const float w = use ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
 #pragma unroll
                 for (int u = 0; u < TPW; ++u) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -521,7 +541,7 @@ la_fwd_kernel(const FwdArgs a)
                 }
                 const float inv = fast_rcp(den + eps);
                 const float sc = (MODE == MODE_CAUSAL) ? lqi * dscale * inv : inv;
-                const int64_t yrow = (int64_t)bh * a.N + a.n0 + t0 + i;
+                const int64_t yrow = row0 + t0 + i;
 #pragma unroll
                 for (int t = 0; t < DBW; ++t) {
                     f32x4 o = {0.f, 0.f, 0.f, 0.f};

@@ -44,6 +44,15 @@ struct FwdArgs {
     // random features: sign s of the prefactor exp(s |x'|^2 / 2) / sqrt(m)
     float rf_sign;
     const float* omega;  // [m, d_k] fp32 (random features) or null
+    // key padding mask: byte kpm[b * kpm_stride + n0 + t] nonzero drops key t
+    // of batch b from every sum; null = no mask
+    const uint8_t* kpm;
+    int64_t kpm_stride;
+    // packed variable-length rows: sequence b = bh / H holds tokens
+    // [cu_seqlens[b], cu_seqlens[b+1]) of head row h = bh % H (N tokens per
+    // head row; offsets are clamped to [0, N]); each sequence is cut into the
+    // launch's P segments of its own length.  null = fixed [B,H,N] rows.
+    const int32_t* cu_seqlens;
     // initial state (MODE_CAUSAL, MODE_QUERY): S at
     // S_src + seg*src_seg_stride + bh*src_stride as [F][d_v], z at
     // z_src + seg*src_seg_stride + bh*src_zstride as [F]; null S_src = zero state.
@@ -68,6 +77,11 @@ struct ScanArgs {
     int64_t n_len;           // tokens covered by the P segments
     int64_t seg_len;         // tokens per segment (cps * C); the last may be shorter
     int32_t causal;          // 1: exclusive decayed scan; 0: plain sum into slot 0
+    // packed variable-length rows (as FwdArgs): per-sequence length from
+    // cu_seqlens (clamped to [0, N]) and segment length whole chunks of C
+    const int32_t* cu_seqlens;
+    int64_t N;
+    int32_t C;
     const float* S_init;     // initial state (causal), user layout or carry slot
     const float* z_init;
     int64_t init_stride, init_zstride;

@@ -46,6 +46,13 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
         return;
     }
     const float l2l = a.lam.log2lam[bh % a.H];
+    int64_t n_len = a.n_len, seg_len = a.seg_len;
+    if (a.cu_seqlens) {
+        int64_t s0, s1;
+        varlen_range(a.cu_seqlens, bh / a.H, a.N, &s0, &s1);
+        n_len = s1 - s0;
+        seg_len = varlen_cps(n_len, a.C, a.P) * a.C;
+    }
     f32x4 carry = zero;
     if (a.S_init)
         carry = isz ? *(const f32x4*)(a.z_init + bh * a.init_zstride + ez)
@@ -57,7 +64,8 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
         for (int b = 0; b < kScanBatch; ++b) {
             const int s = s0 + b;
             if (s < a.P) {
-                const int64_t L = min((int64_t)(s + 1) * a.seg_len, a.n_len) - (int64_t)s * a.seg_len;
+                // tokens of segment s (0 for segments past a short sequence's end)
+                const int64_t L = max(min((int64_t)(s + 1) * seg_len, n_len) - (int64_t)s * seg_len, (int64_t)0);
                 base[s * slot] = carry;
                 carry = lam_pow(l2l, (int)L) * carry + loc[b];
             }
