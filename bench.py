@@ -243,6 +243,125 @@ VARIANTS = (("relu_w2", 2, "relu", 0, 200), ("rf_softmax_w5", 5, "trig_rf_softma
             ("rf_m64_w5", 5, "trig_rf", 64, 25), ("rf_m32_w5", 5, "trig_rf", 32, 25))
 
 
+def bench_call(ctx, name, step, tokens, kernel_bytes, steps, warmup, launches_per_step=8):
+    """Time `step` (one call over the whole batch) and report its dominant
+    kernel against HBM with the algorithmic bytes kernel_bytes[kernel id]."""
+    la = ctx.la
+    ms = ctx.time_steps(step, steps=steps, warmup=warmup)
+    kt = ctx.kernel_times(step, steps=steps, launches_per_step=launches_per_step)
+    dom = max(kt.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
+    dom_ms = kt[dom][0]
+    alg = kernel_bytes.get(dom)
+    achieved = alg / (dom_ms * 1e-3) / 1e9 if alg else 0.0
+    return {
+        "workload": name, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 2),
+        "kernels": {la.la_kernel_name(k): {"mean_ms": round(t, 4), "launches_per_step": n} for k, (t, n) in kt.items()},
+        "dominant_kernel": la.la_kernel_name(dom),
+        "roofline": roofline(achieved, load_traffic(name, la.la_kernel_name(dom))),
+        "roofline_alg_bytes_per_launch": alg,
+        "dominant_mean_ms": round(dom_ms, 4),
+    }
+
+
+def _w2_inputs(ctx, B, H, N, seed=2):
+    import seeded_inputs as si
+    wl = si.workload(2)
+    g = ctx.torch.Generator(device=ctx.dev)
+    g.manual_seed(seed)
+    return wl, tuple(device_normal(ctx.torch, g, (B, H, N, wl.dk), wl.scale, ctx.dev) for _ in range(3))
+
+
+def masked_w2(ctx, steps=200):
+    """Causal forward at the headline shape over a padded batch: batch b keeps
+    its first L_b keys (L_0 = N, the others uniform), the rest are masked."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    wl, (q, k, v) = _w2_inputs(ctx, 4, 8, 4096)
+    B, H, N, d = wl.B, wl.H, wl.N, wl.dk
+    mask = torch.from_numpy(si.make_key_padding_mask(B, N, "right", seed=2)).to(ctx.dev)
+    y = torch.empty_like(q)
+    ws = torch.empty(max(la.la_workspace_size(B, H, N, d, d), 1), dtype=torch.uint8, device=ctx.dev)
+    P = max(1, -(-512 // (B * H)))
+    ids = la.KERNEL_IDS
+    SZ = d * d + d
+    kb = {ids["fwd_causal"]: B * H * N * 4 * d * 2 + B * N,
+          ids["fwd_local"]: B * H * N * 2 * d * 2 + B * N + P * B * H * SZ * 4,
+          ids["scan"]: 2 * P * B * H * SZ * 4}
+
+    def step():
+        la.la_forward_causal_masked(q, k, v, y, mask, eps=wl.eps, workspace=ws)
+
+    name = "elu1_causal_masked_right_B%d_H%d_N%d_d%d_bf16" % (B, H, N, d)
+    return bench_call(ctx, name, step, B * N, kb, steps, max(ctx.warmup, 5))
+
+
+def varlen_w2(ctx, steps=200):
+    """Packed causal forward: 32 sequences of mixed lengths (log-uniform in
+    [1, 4096], one of 4096) back to back in one row per head, 8 heads, d = 64."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    H, d = 8, 64
+    L = si.make_varlen_lengths(32, 4096, seed=2)
+    cu_np = si.cu_seqlens(L)
+    T = int(cu_np[-1])
+    wl, (q, k, v) = _w2_inputs(ctx, 1, H, T)
+    q, k, v = q[0], k[0], v[0]
+    cu = torch.from_numpy(cu_np).to(ctx.dev)
+    y = torch.empty_like(q)
+    mx = int(L.max())
+    ws_n = la.la_workspace_size_varlen(len(L), H, T, mx, d, d)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=ctx.dev)
+    SZ = d * d + d
+    P = max(1, int(round(ws_n / (len(L) * H * SZ * 4)))) if ws_n else 1
+    ids = la.KERNEL_IDS
+    kb = {ids["fwd_causal"]: H * T * 4 * d * 2,
+          ids["fwd_local"]: H * T * 2 * d * 2 + P * len(L) * H * SZ * 4,
+          ids["scan"]: 2 * P * len(L) * H * SZ * 4}
+
+    def step():
+        la.la_forward_causal_varlen(q, k, v, y, cu, mx, eps=wl.eps, workspace=ws)
+
+    name = "elu1_causal_varlen_S%d_T%d_H%d_d%d_bf16" % (len(L), T, H, d)
+    res = bench_call(ctx, name, step, T, kb, steps, max(ctx.warmup, 5))
+    res["sequences"] = int(len(L))
+    res["max_seqlen"] = mx
+    res["segments"] = P
+    return res
+
+
+def cross_w2(ctx, steps=200):
+    """Cross attention at the headline batch: 1024 queries against 4096 keys
+    and values per (batch, head), B = 4, H = 8, d = 64, keys right-padded."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    B, H, Nq, Nk, d = 4, 8, 1024, 4096, 64
+    wl, (k, v, _) = _w2_inputs(ctx, B, H, Nk)
+    _, (q, _, _) = _w2_inputs(ctx, B, H, Nq, seed=12)
+    mask = torch.from_numpy(si.make_key_padding_mask(B, Nk, "right", seed=2)).to(ctx.dev)
+    y = torch.empty_like(q)
+    ws_n = la.la_workspace_size_cross(B, H, Nq, Nk, d, d)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=ctx.dev)
+    SZ = d * d + d
+    P = max(1, int(round(ws_n / (B * H * SZ * 4)))) if ws_n else 1
+    ids = la.KERNEL_IDS
+    kb = {ids["fwd_local"]: B * H * Nk * 2 * d * 2 + B * Nk + P * B * H * SZ * 4,
+          ids["fwd_query"]: B * H * Nq * 2 * d * 2,
+          ids["scan"]: (P + 1) * B * H * SZ * 4}
+
+    def step():
+        la.la_forward_cross(q, k, v, y, mask, eps=wl.eps, workspace=ws)
+
+    name = "elu1_cross_masked_B%d_H%d_Nq%d_Nk%d_d%d_bf16" % (B, H, Nq, Nk, d)
+    res = bench_call(ctx, name, step, B * Nq, kb, steps, max(ctx.warmup, 5))
+    res["key_Mtokens_per_s"] = round(B * Nk / (res["ms_per_step"] * 1e-3) / 1e6, 2)
+    res["segments"] = P
+    return res
+
+
+# Mask / cross / packed lines measured beside the main workloads
+SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2))
+
+
 def workload4_decode(ctx, steps=1024):
     """Decode: prefix of 512 tokens through the causal forward, then `steps`
     single-token steps timed back to back.  Bytes per step: state read and
@@ -464,7 +583,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "copy"] + [v[0] for v in VARIANTS],
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "copy"] + [v[0] for v in VARIANTS] +
+                    [v[0] for v in SHAPE_VARIANTS],
                     help="run one workload (profiling)")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="host only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR into "
@@ -486,6 +606,7 @@ def main():
                "w4multi": workload4_multi}
         for key, base, phi, m, steps in VARIANTS:
             fns[key] = (lambda c, b=base, p=phi, mm=m, st=steps: feature_map_variant(c, b, p, mm, st))
+        fns.update(dict(SHAPE_VARIANTS))
         fn = fns[args.only]
         log("running", args.only)
         print(json.dumps({"only": args.only, "result": fn(ctx)}), flush=True)
@@ -505,6 +626,11 @@ def main():
         for key, base, phi, m, steps in VARIANTS:
             log(key, "...")
             extra[key] = feature_map_variant(ctx, base, phi, m, steps)
+            log(json.dumps(extra[key]))
+            ctx.torch.cuda.empty_cache()
+        for key, fn in SHAPE_VARIANTS:
+            log(key, "...")
+            extra[key] = fn(ctx)
             log(json.dumps(extra[key]))
             ctx.torch.cuda.empty_cache()
     log("workload 2 (headline) ...")

@@ -187,6 +187,8 @@ VARLEN = [
     (2, {}, 4, (12, 900, 2), "exact", False),
     (2, {}, 2, (5, 9000, 1), "exact", True),     # long sequences: many segments each
     (2, {}, 2, (7, 3000, 0), "zero", True),      # hint 0: one segment per sequence
+    (2, {}, 2, (5, 9000, 0), "half", False),     # understated hint: the last segment takes the rest
+    (2, {}, 4, (64, 2000, 8), "exact", True),    # many sequences, several empty
     (3, {}, 3, (6, 700, 1), "exact", True),      # d = 128, per-head decay
     (1, {}, 2, (9, 300, 2), "exact", False),     # fp32
     (5, {"m": 64}, 2, (6, 1200, 1), "exact", False),
@@ -213,7 +215,7 @@ def test_causal_varlen_parity(wi, over, H, lens, hint, with_state):
     y = torch.full((H, T, wl.dv), float("nan"), dtype=tdtype(wl.dtype), device=DEV)
     S = torch.full((n_seq, H, F, wl.dv), float("nan"), device=DEV)
     z = torch.full((n_seq, H, F), float("nan"), device=DEV)
-    mx = int(L.max()) if hint == "exact" else 0
+    mx = {"exact": int(L.max()), "half": int(L.max()) // 2, "zero": 0}[hint]
     la.la_forward_causal_varlen(q, k, v, y, torch.from_numpy(cu).to(DEV), mx, phi=phi_for(wl, inp.get("omega")),
                                 lambda_h=lam, eps=wl.eps, S_in=S_in, z_in=z_in, S_out=S, z_out=z)
     torch.cuda.synchronize()
@@ -233,3 +235,54 @@ def test_causal_varlen_parity(wi, over, H, lens, hint, with_state):
     tol = TOL[wl.dtype]
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=tol, atol=tol * np.abs(Sr).max())
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=tol, atol=tol * np.abs(zr).max())
+
+
+# ------------------------------------------- the benchmarked configurations, full size
+def test_full_size_masked_headline_shape():
+    # B=4 H=8 N=4096 d=64 bf16 with a right-padded batch, the benchmark's launch plan
+    wl = si.workload(2)
+    inp = si.make_inputs(wl)
+    mask = si.make_key_padding_mask(wl.B, wl.N, "right", seed=2)
+    q, k, v = (to_dev(inp, n, "bf16") for n in ("q", "k", "v"))
+    y = torch.empty(wl.B, wl.H, wl.N, wl.dv, dtype=torch.bfloat16, device=DEV)
+    la.la_forward_causal_masked(q, k, v, y, _dev_mask(mask), eps=wl.eps)
+    torch.cuda.synchronize()
+    ref = oracle.causal(inp["q"], inp["k"], inp["v"], None, wl.eps, key_padding_mask=mask)
+    err = rel_err(y, ref)
+    assert err < TOL["bf16"], err
+
+
+def test_full_size_varlen_32_sequences():
+    # 32 packed sequences (log-uniform lengths up to 4096), 8 heads, d = 64
+    wl = si.workload(2)
+    L = si.make_varlen_lengths(32, 4096, seed=2)
+    cu = si.cu_seqlens(L)
+    T = int(cu[-1])
+    inp = si.pack_heads(wl, T, H=8)
+    q, k, v = (to_dev(inp, n, "bf16")[0].contiguous() for n in ("q", "k", "v"))
+    y = torch.empty(8, T, 64, dtype=torch.bfloat16, device=DEV)
+    S = torch.empty(32, 8, 64, 64, device=DEV)
+    z = torch.empty(32, 8, 64, device=DEV)
+    la.la_forward_causal_varlen(q, k, v, y, torch.from_numpy(cu).to(DEV), int(L.max()), eps=wl.eps,
+                                S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    ref, Sr, zr = oracle.causal_varlen(inp["q"], inp["k"], inp["v"], cu, None, wl.eps)
+    err = rel_err(y[None], ref)
+    assert err < TOL["bf16"], err
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=TOL["bf16"])
+
+
+def test_full_size_cross_1024_by_4096():
+    # B=4 H=8, 1024 queries against 4096 right-padded keys, d = 64
+    wl = si.workload(2)
+    inp = si.make_inputs(wl, N=1024)
+    kv = si.make_kv(wl, 4096)
+    mask = si.make_key_padding_mask(wl.B, 4096, "right", seed=2)
+    q = to_dev(inp, "q", "bf16")
+    k, v = to_dev(kv, "k", "bf16"), to_dev(kv, "v", "bf16")
+    y = torch.empty(wl.B, wl.H, 1024, 64, dtype=torch.bfloat16, device=DEV)
+    la.la_forward_cross(q, k, v, y, _dev_mask(mask), eps=wl.eps)
+    torch.cuda.synchronize()
+    ref = oracle.cross(inp["q"], kv["k"], kv["v"], wl.eps, key_padding_mask=mask)
+    err = rel_err(y, ref)
+    assert err < TOL["bf16"], err

@@ -234,21 +234,41 @@ void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps)
     *P = (int)((NC + *cps - 1) / *cps);
 }
 
-// Plan of a forward over rows of N tokens (causal: may be cut into windows;
-// packed variable-length rows: N is the longest sequence, one window).
-Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, bool windows = true)
+// Segments of packed variable-length rows: one length of cps chunks for every
+// sequence, sized so that the head-sequences' segments number about
+// kTargetWorkgroups in all (total chunks per head row <= T/C + B), and P grid
+// segments to cover the longest sequence (the last one takes any remainder,
+// so an understated max_len costs speed, not correctness).
+void varlen_segments(int64_t T, int64_t B, int64_t H, int64_t max_len, int C, int* P, int64_t* cps)
+{
+    const int64_t chunks = ((T + C - 1) / C + B) * H;
+    int64_t c = (chunks + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    if (c < 1) c = 1;
+    int64_t p = ((max_len + C - 1) / C + c - 1) / c;
+    if (p < 1) p = 1;
+    if (p > 65535) {  // grid limit: longer segments instead
+        c = ((max_len + C - 1) / C + 65534) / 65535;
+        p = ((max_len + C - 1) / C + c - 1) / c;
+    }
+    *cps = c;
+    *P = (int)p;
+}
+
+// Plan of a forward over rows of N tokens (causal: may be cut into windows).
+// varlen_P > 0: packed variable-length rows cut into varlen_P segments, one window.
+Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, int varlen_P = 0)
 {
     Plan p;
     p.C = e->C;
     p.SZ = (int64_t)F * s->d_v + F;
     const int64_t BH = s->B * s->H;
     const int64_t NC = (s->N + p.C - 1) / p.C;
-    int W = (causal && windows) ? env_int("LA_WINDOWS", 1) : 1;
+    int W = (causal && varlen_P == 0) ? env_int("LA_WINDOWS", 1) : 1;
     if (W < 1) W = 1;
     if (W > NC) W = (int)(NC > 0 ? NC : 1);
     p.W = W;
     // every window has at most NC chunks, so it is cut into at most this many segments
-    p.Pmax = (int)target_segments(NC > 0 ? NC : 1, BH);
+    p.Pmax = varlen_P > 0 ? varlen_P : (int)target_segments(NC > 0 ? NC : 1, BH);
     size_t floats = 0;
     if (causal) {
         if (p.Pmax > 1) floats += (size_t)p.Pmax * BH * p.SZ;
@@ -456,22 +476,23 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
         if (e != hipSuccess) return hip_fail(e, "la_forward_causal (N=0)");
         return ok();
     }
-    la_shape plan_shape = *shape;
+    int vP = 0;
+    int64_t vcps = 1;
     if (cu) {
         // packed rows: q, k, v, y hold H rows of N tokens
         const size_t rows = (size_t)shape->H * shape->N;
         if ((st = check_io_rows(q, k, v, y, shape, rows, rows)) != LA_OK) return st;
-        plan_shape.N = max_len;
+        varlen_segments(shape->N, shape->B, shape->H, max_len, ent->C, &vP, &vcps);
     } else {
         if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
     }
-    const Plan plan = make_plan(&plan_shape, F, ent, true, cu == nullptr);
+    const Plan plan = make_plan(shape, F, ent, true, vP);
     if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
 
     float* ws = static_cast<float*>(workspace);
     float* segs = ws;                                                     // [P][BH][SZ]
     float* carry = ws ? ws + (plan.Pmax > 1 ? (size_t)plan.Pmax * BH * plan.SZ : 0) : nullptr;  // [BH][SZ]
-    const int64_t NC = (plan_shape.N + plan.C - 1) / plan.C;
+    const int64_t NC = (shape->N + plan.C - 1) / plan.C;
 
     FwdArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -494,12 +515,13 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
 
     for (int w = 0; w < plan.W; ++w) {
         const int64_t c0 = (int64_t)w * NC / plan.W, c1 = (int64_t)(w + 1) * NC / plan.W;
-        const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, plan_shape.N) - n0;
+        const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, shape->N) - n0;
         int P = 1;
         int64_t cps = 1;
         if (cu) {
-            // every sequence is cut into the same P segments of its own length
-            P = plan.Pmax;
+            // one segment length for every packed sequence (n0, n_len unused)
+            P = vP;
+            cps = vcps;
         } else {
             cut_segments(c1 - c0, BH, &P, &cps);
         }
@@ -548,7 +570,6 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             sa.causal = 1;
             sa.cu_seqlens = cu;
             sa.N = shape->N;
-            sa.C = plan.C;
             sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
             sa.lam = lam;
@@ -605,9 +626,10 @@ size_t la_workspace_size_varlen(const la_shape* shape, int64_t max_seqlen, const
     const la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &e);
     g_last_error = saved;
     if (st != LA_OK || shape->N == 0 || max_seqlen < 0 || max_seqlen > shape->N) return 0;
-    la_shape ps = *shape;
-    ps.N = max_seqlen;
-    return make_plan(&ps, F, e, true, false).ws_bytes;
+    int P = 1;
+    int64_t cps = 1;
+    varlen_segments(shape->N, shape->B, shape->H, max_seqlen, e->C, &P, &cps);
+    return make_plan(shape, F, e, true, P).ws_bytes;
 }
 
 la_status la_forward_causal_varlen(const void* q, const void* k, const void* v, void* y,

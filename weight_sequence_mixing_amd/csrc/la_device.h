@@ -192,12 +192,6 @@ __device__ __forceinline__ void varlen_range(const int32_t* cu, int b, int64_t N
     *s1 = min(max((int64_t)cu[b + 1], a), N);
 }
 
-// Chunks per segment when n tokens are cut into P segments of whole C-token
-// chunks (0 for an empty sequence).
-__device__ __forceinline__ int64_t varlen_cps(int64_t n, int C, int P) {
-    return ((n + C - 1) / C + P - 1) / P;
-}
-
 __device__ __forceinline__ float lam_pow(float log2lam, int k) {
     return k == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)k * log2lam);
 }

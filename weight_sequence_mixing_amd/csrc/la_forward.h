@@ -167,16 +167,22 @@ la_fwd_kernel(const FwdArgs a)
     const bool decay = l2l != 0.f;  // uniform over the workgroup
     // token range of this row: [n0, n0 + n_len) of row bh, or the packed
     // sequence bh / H of head row h
-    int64_t row0 = (int64_t)bh * a.N + a.n0, n_len = a.n_len, cps = a.cps;
+    int64_t row0 = (int64_t)bh * a.N + a.n0, n_len = a.n_len;
     if (a.cu_seqlens) {
         int64_t s0, s1;
         varlen_range(a.cu_seqlens, bh / a.H, a.N, &s0, &s1);
         row0 = (int64_t)h * a.N + s0;
         n_len = s1 - s0;
-        cps = varlen_cps(n_len, C, a.P);
     }
+    // segments of cps chunks; the last one takes whatever remains
     const int64_t NC = (n_len + C - 1) / C;
-    const int64_t c_beg = (int64_t)seg * cps, c_end = min(NC, c_beg + cps);
+    const int64_t c_beg = (int64_t)seg * a.cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + a.cps);
+    // an empty segment (past the end of a short packed sequence) has nothing
+    // to compute and nothing to store, unless it carries a state through
+    if (c_beg >= c_end) {
+        if constexpr (MODE != MODE_CAUSAL) return;
+        else if (!a.S_dst) return;
+    }
     const T* qg = (const T*)a.q + row0 * DK;
     const T* kg = (const T*)a.k + row0 * DK;
     const T* vg = (const T*)a.v + row0 * DV;

@@ -50,8 +50,9 @@ struct FwdArgs {
     int64_t kpm_stride;
     // packed variable-length rows: sequence b = bh / H holds tokens
     // [cu_seqlens[b], cu_seqlens[b+1]) of head row h = bh % H (N tokens per
-    // head row; offsets are clamped to [0, N]); each sequence is cut into the
-    // launch's P segments of its own length.  null = fixed [B,H,N] rows.
+    // head row; offsets are clamped to [0, N]).  Every sequence is cut into
+    // segments of cps chunks, the last grid segment taking the remainder; the
+    // segments past a short sequence's end are empty.  null = fixed rows.
     const int32_t* cu_seqlens;
     // initial state (MODE_CAUSAL, MODE_QUERY): S at
     // S_src + seg*src_seg_stride + bh*src_stride as [F][d_v], z at
@@ -78,10 +79,10 @@ struct ScanArgs {
     int64_t seg_len;         // tokens per segment (cps * C); the last may be shorter
     int32_t causal;          // 1: exclusive decayed scan; 0: plain sum into slot 0
     // packed variable-length rows (as FwdArgs): per-sequence length from
-    // cu_seqlens (clamped to [0, N]) and segment length whole chunks of C
+    // cu_seqlens (clamped to [0, N]); a sequence covers its first
+    // ceil(n / seg_len) segments (at most P), the others are empty and skipped
     const int32_t* cu_seqlens;
     int64_t N;
-    int32_t C;
     const float* S_init;     // initial state (causal), user layout or carry slot
     const float* z_init;
     int64_t init_stride, init_zstride;

@@ -46,26 +46,27 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
         return;
     }
     const float l2l = a.lam.log2lam[bh % a.H];
-    int64_t n_len = a.n_len, seg_len = a.seg_len;
+    int64_t n_len = a.n_len;
     if (a.cu_seqlens) {
         int64_t s0, s1;
         varlen_range(a.cu_seqlens, bh / a.H, a.N, &s0, &s1);
         n_len = s1 - s0;
-        seg_len = varlen_cps(n_len, a.C, a.P) * a.C;
     }
+    // segments holding tokens (the last of the P takes the remainder)
+    const int nseg = (int)min((n_len + a.seg_len - 1) / a.seg_len, (int64_t)a.P);
     f32x4 carry = zero;
     if (a.S_init)
         carry = isz ? *(const f32x4*)(a.z_init + bh * a.init_zstride + ez)
                     : *(const f32x4*)(a.S_init + bh * a.init_stride + e);
-    for (int s0 = 0; s0 < a.P; s0 += kScanBatch) {
+    for (int s0 = 0; s0 < nseg; s0 += kScanBatch) {
 #pragma unroll
-        for (int b = 0; b < kScanBatch; ++b) loc[b] = (s0 + b < a.P) ? base[(s0 + b) * slot] : zero;
+        for (int b = 0; b < kScanBatch; ++b) loc[b] = (s0 + b < nseg) ? base[(s0 + b) * slot] : zero;
 #pragma unroll
         for (int b = 0; b < kScanBatch; ++b) {
             const int s = s0 + b;
-            if (s < a.P) {
-                // tokens of segment s (0 for segments past a short sequence's end)
-                const int64_t L = max(min((int64_t)(s + 1) * seg_len, n_len) - (int64_t)s * seg_len, (int64_t)0);
+            if (s < nseg) {
+                const int64_t L = (s == a.P - 1 ? n_len : min((int64_t)(s + 1) * a.seg_len, n_len)) -
+                                  (int64_t)s * a.seg_len;
                 base[s * slot] = carry;
                 carry = lam_pow(l2l, (int)L) * carry + loc[b];
             }
