@@ -59,6 +59,11 @@ def _load():
     lib.orc_noncausal.restype = None
     lib.orc_cross.argtypes = [P, P, P, L, L, L, I, I, I, I, P, D, D, U, P]
     lib.orc_cross.restype = None
+    lib.orc_phi_vjp.argtypes = [I, P, I, I, P, D, P, P]
+    lib.orc_phi_vjp.restype = None
+    lib.orc_backward.argtypes = [P, P, P, P, L, L, I, I, I, I, P, D, P, D, U, P, P, P, P,
+                                 P, P, P, P, P, P]
+    lib.orc_backward.restype = None
     lib.orc_decode_step.argtypes = [P, P, P, L, I, I, I, I, P, D, P, D, P, P, P]
     lib.orc_decode_step.restype = None
     _lib = lib
@@ -274,6 +279,60 @@ def causal_varlen(q, k, v, cu_seqlens, lam=None, eps=1e-6, phi="elu1", omega=Non
         y[:, :, lo:hi] = yb
         S[b], z[b] = Sb[0], zb[0]
     return y, S, z
+
+
+def backward(q, k, v, gy, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0, S0=None, z0=None,
+             dS_out=None, dz_out=None, key_padding_mask=None, threads=None):
+    """Gradients of the causal forward for the loss sum(gy * y) +
+    <dS_out, S_final> + <dz_out, z_final>.
+
+    Returns a dict: dq, dk [B,H,N,dk], dv [B,H,N,dv], dS0 [B,H,F,dv],
+    dz0 [B,H,F] (gradient of the initial state) and dlam [B,H] (per row;
+    a per-head parameter's gradient is its sum over B).
+    """
+    lib = _load()
+    q, k, v, gy, om = _f64(q), _f64(k), _f64(v), _f64(gy), _f64(omega)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    m = 0 if om is None else om.shape[0]
+    F = feature_dim(phi, dk, om)
+    lam_r = _lam_rows(lam, B, H)
+    S0, z0, dS_out, dz_out = _f64(S0), _f64(z0), _f64(dS_out), _f64(dz_out)
+    kpm = _mask_rows(key_padding_mask, B, H, N)
+    out = {"dq": np.empty((B, H, N, dk)), "dk": np.empty((B, H, N, dk)), "dv": np.empty((B, H, N, dv)),
+           "dS0": np.empty((B, H, F, dv)), "dz0": np.empty((B, H, F)), "dlam": np.empty((B, H))}
+
+    def run(rng):
+        a, b = rng
+        lib.orc_backward(_ptr(q, a * N * dk), _ptr(k, a * N * dk), _ptr(v, a * N * dv), _ptr(gy, a * N * dv),
+                         b - a, N, dk, dv, PHI_KINDS[phi], m, _ptr(om), float(scale), _ptr(lam_r, a),
+                         float(eps), _uptr(kpm, a * N), _ptr(S0, a * F * dv), _ptr(z0, a * F),
+                         _ptr(dS_out, a * F * dv), _ptr(dz_out, a * F),
+                         _ptr(out["dq"], a * N * dk), _ptr(out["dk"], a * N * dk), _ptr(out["dv"], a * N * dv),
+                         _ptr(out["dS0"], a * F * dv), _ptr(out["dz0"], a * F), _ptr(out["dlam"], a))
+
+    parts = _split(B * H, threads or default_threads())
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return out
+
+
+def phi_vjp(x, dp, phi="elu1", omega=None, scale=1.0):
+    """J_phi(x)^T dp over the last axis (x [..., dk], dp [..., F])."""
+    lib = _load()
+    x, dp, om = _f64(x), _f64(dp), _f64(omega)
+    dk = x.shape[-1]
+    m = 0 if om is None else om.shape[0]
+    F = dp.shape[-1]
+    fx, fd = x.reshape(-1, dk), dp.reshape(-1, F)
+    out = np.empty_like(fx)
+    for r in range(fx.shape[0]):
+        lib.orc_phi_vjp(PHI_KINDS[phi], _ptr(fx, r * dk), dk, m, _ptr(om), float(scale), _ptr(fd, r * F),
+                        _ptr(out, r * dk))
+    return out.reshape(x.shape)
 
 
 def decode_step(q, k, v, S, z, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,

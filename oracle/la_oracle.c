@@ -274,3 +274,190 @@ void orc_decode_step(const double* q, const double* k, const double* v,
     }
     free(pk); free(pq);
 }
+
+/* Vector-Jacobian product of the feature map: dx = J_phi(x)^T dp for one
+ * vector x[dk] and a gradient dp[F] with respect to phi(x).
+ * ELU1: d phi_f / d x_f = 1 for x_f > 0, exp(x_f) otherwise.
+ * RELU: 1 for x_f > 0, 0 otherwise.
+ * TRIG_RF*: with x' = scale x, u_r = omega_r . x', phi = c [cos u, sin u] and
+ *   c = exp(s |x'|^2 / 2) / sqrt(m) (s = -1, 0, +1 by kind):
+ *   d phi / d x' = s x' phi^T + c [-sin u_r omega_r | cos u_r omega_r], so
+ *   dx = scale (s x' (phi . dp) + c sum_r omega_r (-sin u_r dp_r + cos u_r dp_{m+r})). */
+void orc_phi_vjp(int kind, const double* x, int dk, int m, const double* omega,
+                 double scale, const double* dp, double* dx)
+{
+    if (kind == ORC_PHI_ELU1) {
+        for (int f = 0; f < dk; ++f) dx[f] = dp[f] * (x[f] > 0.0 ? 1.0 : exp(x[f]));
+        return;
+    }
+    if (kind == ORC_PHI_RELU) {
+        for (int f = 0; f < dk; ++f) dx[f] = x[f] > 0.0 ? dp[f] : 0.0;
+        return;
+    }
+    const double s = kind == ORC_PHI_TRIG_RF ? -1.0 : (kind == ORC_PHI_TRIG_RF_SOFTMAX ? 1.0 : 0.0);
+    double* xs = (double*)malloc(sizeof(double) * (size_t)dk);
+    double nrm2 = 0.0;
+    for (int f = 0; f < dk; ++f) {
+        xs[f] = scale * x[f];
+        nrm2 += xs[f] * xs[f];
+        dx[f] = 0.0;
+    }
+    const double c = exp(0.5 * s * nrm2) / sqrt((double)m);
+    double phidp = 0.0;
+    for (int r = 0; r < m; ++r) {
+        double u = 0.0;
+        for (int f = 0; f < dk; ++f) u += omega[(size_t)r * dk + f] * xs[f];
+        const double cu = cos(u), su = sin(u);
+        phidp += c * cu * dp[r] + c * su * dp[m + r];
+        const double w = c * (-su * dp[r] + cu * dp[m + r]);
+        for (int f = 0; f < dk; ++f) dx[f] += w * omega[(size_t)r * dk + f];
+    }
+    for (int f = 0; f < dk; ++f) dx[f] = scale * (dx[f] + s * xs[f] * phidp);
+    free(xs);
+}
+
+/* Gradients of the causal forward (reverse mode of the recurrence of
+ * orc_causal), for the loss L = sum_i g_i . y_i + <dS_out, S_{N-1}> +
+ * <dz_out, z_{N-1}>.  Per (batch, head) row:
+ *   forward, token order: S_i, z_i, den_i = phi(q_i).z_i + eps, y_i;
+ *     dnum_i = g_i / den_i,  dden_i = -(g_i . y_i) / den_i,
+ *     d phi(q_i) = S_i dnum_i + z_i dden_i,  dq_i = J_phi(q_i)^T d phi(q_i);
+ *     and, forward mode in lambda, T_i = dS_i/dlambda = lambda T_{i-1} + S_{i-1}
+ *     (t_i likewise; T = 0 before token 0, S_{-1} = S0), so that
+ *     dlambda = sum_i [dnum_i . T_i^T phi(q_i) + dden_i t_i . phi(q_i)]
+ *             + <dS_out, T_{N-1}> + <dz_out, t_{N-1}>;
+ *   reverse, adjoint of the state: U_{N-1} = dS_out + phi(q_{N-1}) dnum_{N-1}^T,
+ *     U_i = lambda U_{i+1} + phi(q_i) dnum_i^T (u likewise with dden), then
+ *     d phi(k_i) = U_i v_i + u_i,  dv_i = U_i^T phi(k_i),
+ *     dk_i = J_phi(k_i)^T d phi(k_i);  dS0 = lambda U_0, dz0 = lambda u_0.
+ * kpm as in orc_causal (a padded key has phi(k) = 0 and gets dk = dv = 0).
+ * g [nbh][N][dv]; dS_out [nbh][F][dv] / dz_out [nbh][F] may be NULL (zero);
+ * outputs dq, dk [nbh][N][dk], dv [nbh][N][dv], dS0 [nbh][F][dv], dz0
+ * [nbh][F] (NULL = not written), dlam [nbh]. */
+void orc_backward(const double* q, const double* k, const double* v, const double* gy,
+                  long nbh, long N, int dk, int dv, int kind, int m,
+                  const double* omega, double scale, const double* lam, double eps,
+                  const unsigned char* kpm, const double* S0, const double* z0,
+                  const double* dS_out, const double* dz_out,
+                  double* dq, double* dkx, double* dvx, double* dS0, double* dz0, double* dlam)
+{
+    const int F = feat_dim(kind, dk, m);
+    const size_t FD = (size_t)F * dv;
+    double* S = (double*)malloc(sizeof(double) * FD);
+    double* z = (double*)malloc(sizeof(double) * (size_t)F);
+    double* T = (double*)malloc(sizeof(double) * FD);
+    double* t = (double*)malloc(sizeof(double) * (size_t)F);
+    double* Sp = (double*)malloc(sizeof(double) * FD);
+    double* zp = (double*)malloc(sizeof(double) * (size_t)F);
+    double* pq = (double*)malloc(sizeof(double) * (size_t)F * (N > 0 ? N : 1));
+    double* pk = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dnum = (double*)malloc(sizeof(double) * (size_t)dv * (N > 0 ? N : 1));
+    double* dden = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* y = (double*)malloc(sizeof(double) * (size_t)dv);
+    for (long bh = 0; bh < nbh; ++bh) {
+        const double L = lam[bh];
+        const double* qr = q + (size_t)bh * N * dk;
+        const double* kr = k + (size_t)bh * N * dk;
+        const double* vr = v + (size_t)bh * N * dv;
+        const double* gr = gy + (size_t)bh * N * dv;
+        const unsigned char* mr = kpm ? kpm + (size_t)bh * N : NULL;
+        if (S0) memcpy(S, S0 + (size_t)bh * FD, sizeof(double) * FD);
+        else memset(S, 0, sizeof(double) * FD);
+        if (z0) memcpy(z, z0 + (size_t)bh * F, sizeof(double) * (size_t)F);
+        else memset(z, 0, sizeof(double) * (size_t)F);
+        memset(T, 0, sizeof(double) * FD);
+        memset(t, 0, sizeof(double) * (size_t)F);
+        double dl = 0.0;
+        /* forward, token order */
+        for (long i = 0; i < N; ++i) {
+            memcpy(Sp, S, sizeof(double) * FD);
+            memcpy(zp, z, sizeof(double) * (size_t)F);
+            orc_phi(kind, kr + (size_t)i * dk, dk, m, omega, scale, pk);
+            if (mr && mr[i])
+                for (int f = 0; f < F; ++f) pk[f] = 0.0;
+            double* pqi = pq + (size_t)i * F;
+            orc_phi(kind, qr + (size_t)i * dk, dk, m, omega, scale, pqi);
+            const double* vi = vr + (size_t)i * dv;
+            for (int f = 0; f < F; ++f) {
+                for (int d = 0; d < dv; ++d) {
+                    const size_t e = (size_t)f * dv + d;
+                    T[e] = L * T[e] + Sp[e];
+                    S[e] = L * S[e] + pk[f] * vi[d];
+                }
+                t[f] = L * t[f] + zp[f];
+                z[f] = L * z[f] + pk[f];
+            }
+            double den = eps;
+            for (int f = 0; f < F; ++f) den += pqi[f] * z[f];
+            const double* gi = gr + (size_t)i * dv;
+            double gy_dot = 0.0;
+            for (int d = 0; d < dv; ++d) {
+                double num = 0.0;
+                for (int f = 0; f < F; ++f) num += pqi[f] * S[(size_t)f * dv + d];
+                y[d] = num / den;
+                gy_dot += gi[d] * y[d];
+            }
+            double* dni = dnum + (size_t)i * dv;
+            for (int d = 0; d < dv; ++d) dni[d] = gi[d] / den;
+            dden[i] = -gy_dot / den;
+            for (int f = 0; f < F; ++f) {
+                double a = z[f] * dden[i], b = t[f] * dden[i];
+                for (int d = 0; d < dv; ++d) {
+                    a += S[(size_t)f * dv + d] * dni[d];
+                    b += T[(size_t)f * dv + d] * dni[d];
+                }
+                dp[f] = a;
+                dl += pqi[f] * b;
+            }
+            orc_phi_vjp(kind, qr + (size_t)i * dk, dk, m, omega, scale, dp, dq + ((size_t)bh * N + i) * dk);
+        }
+        if (dS_out)
+            for (size_t e = 0; e < FD; ++e) dl += dS_out[(size_t)bh * FD + e] * T[e];
+        if (dz_out)
+            for (int f = 0; f < F; ++f) dl += dz_out[(size_t)bh * F + f] * t[f];
+        dlam[bh] = dl;
+        /* reverse: adjoint of the state (U, u reuse S, z) */
+        if (dS_out) memcpy(S, dS_out + (size_t)bh * FD, sizeof(double) * FD);
+        else memset(S, 0, sizeof(double) * FD);
+        if (dz_out) memcpy(z, dz_out + (size_t)bh * F, sizeof(double) * (size_t)F);
+        else memset(z, 0, sizeof(double) * (size_t)F);
+        for (long i = N - 1; i >= 0; --i) {
+            const double* pqi = pq + (size_t)i * F;
+            const double* dni = dnum + (size_t)i * dv;
+            const double w = (i < N - 1) ? L : 1.0;
+            for (int f = 0; f < F; ++f) {
+                for (int d = 0; d < dv; ++d) {
+                    const size_t e = (size_t)f * dv + d;
+                    S[e] = w * S[e] + pqi[f] * dni[d];
+                }
+                z[f] = w * z[f] + pqi[f] * dden[i];
+            }
+            orc_phi(kind, kr + (size_t)i * dk, dk, m, omega, scale, pk);
+            const int padded = mr && mr[i];
+            if (padded)
+                for (int f = 0; f < F; ++f) pk[f] = 0.0;
+            const double* vi = vr + (size_t)i * dv;
+            double* dvi = dvx + ((size_t)bh * N + i) * dv;
+            for (int d = 0; d < dv; ++d) {
+                double a = 0.0;
+                for (int f = 0; f < F; ++f) a += S[(size_t)f * dv + d] * pk[f];
+                dvi[d] = a;
+            }
+            for (int f = 0; f < F; ++f) {
+                double a = z[f];
+                for (int d = 0; d < dv; ++d) a += S[(size_t)f * dv + d] * vi[d];
+                dp[f] = padded ? 0.0 : a;
+            }
+            orc_phi_vjp(kind, kr + (size_t)i * dk, dk, m, omega, scale, dp, dkx + ((size_t)bh * N + i) * dk);
+        }
+        /* gradient of the initial state: S_0 = lambda S_{-1} + ... */
+        const double w0 = N > 0 ? L : 1.0;
+        if (dS0)
+            for (size_t e = 0; e < FD; ++e) dS0[(size_t)bh * FD + e] = w0 * S[e];
+        if (dz0)
+            for (int f = 0; f < F; ++f) dz0[(size_t)bh * F + f] = w0 * z[f];
+    }
+    free(S); free(z); free(T); free(t); free(Sp); free(zp); free(pq); free(pk); free(dp);
+    free(dnum); free(dden); free(y);
+}

@@ -535,3 +535,137 @@ def test_varlen_single_sequence_and_reordering(orc):
     np.testing.assert_allclose(yp[:, :, b:], ys[:, :, :a], rtol=1e-13)
     np.testing.assert_allclose(Sp[[1, 0]], Ss, rtol=1e-13)
     np.testing.assert_allclose(zp[[1, 0]], zs, rtol=1e-13)
+
+
+# ------------------------------------------------------------------ backward
+def _torch_quadratic_loss(q, k, v, g, lam, eps, phi, omega, scale, S0, z0, dS_out, dz_out, keep):
+    """The causal forward written as the O(N^2) quadratic form in torch fp64
+    (not the recurrence), plus the final-state terms, as a scalar loss."""
+    import torch
+    if phi == "elu1":
+        pq, pk = torch.nn.functional.elu(q) + 1.0, torch.nn.functional.elu(k) + 1.0
+    elif phi == "relu":
+        pq, pk = torch.relu(q), torch.relu(k)
+    else:
+        sgn = {"trig_rf": -1.0, "trig_rf_plain": 0.0, "trig_rf_softmax": 1.0}[phi]
+        m = omega.shape[0]
+
+        def rf(x):
+            xs = scale * x
+            u = xs @ omega.T
+            c = torch.exp(0.5 * sgn * (xs * xs).sum(-1, keepdim=True)) / math.sqrt(m)
+            return c * torch.cat([torch.cos(u), torch.sin(u)], -1)
+        pq, pk = rf(q), rf(k)
+    pk = pk * keep[:, None, :, None]
+    B, H, N, _ = q.shape
+    idx = torch.arange(N, dtype=torch.float64)
+    E = idx[:, None] - idx[None, :]
+    causal = (E >= 0).to(torch.float64)
+    lamh = lam.reshape(1, H, 1, 1)
+    W = torch.pow(lamh, E.clamp(min=0)) * causal                      # lambda^(i-j), j <= i
+    A = (pq @ pk.transpose(-1, -2)) * W
+    li = torch.pow(lamh.reshape(1, H, 1), idx + 1)                    # lambda^(i+1)
+    num = A @ v + li[..., None] * (pq @ S0)
+    den = A.sum(-1) + li * (pq * z0[:, :, None, :]).sum(-1) + eps
+    y = num / den[..., None]
+    wN = torch.pow(lamh.reshape(1, H, 1), (N - 1 - idx))              # lambda^(N-1-j)
+    S_fin = (pk * wN[..., None]).transpose(-1, -2) @ v + torch.pow(lam, N).reshape(1, H, 1, 1) * S0
+    z_fin = (pk * wN[..., None]).sum(2) + torch.pow(lam, N).reshape(1, H, 1) * z0
+    return (g * y).sum() + (dS_out * S_fin).sum() + (dz_out * z_fin).sum()
+
+
+@pytest.mark.parametrize("phi,dk,m,lams,masked", [
+    ("elu1", 4, 0, (0.9, 1.0), False), ("elu1", 6, 0, (0.3, 0.95), True),
+    ("relu", 4, 0, (0.8, 1.0), True), ("trig_rf", 4, 6, (0.9, 0.99), False),
+    ("trig_rf_softmax", 4, 4, (1.0, 0.7), False), ("trig_rf_plain", 6, 4, (0.6, 0.9), True)])
+def test_backward_matches_torch_autograd_of_quadratic_form(orc, phi, dk, m, lams, masked):
+    import torch
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd", phi, dk, lams)).encode()))
+    B, H, N, dv = 2, 2, 19, 3
+    q, k, v, g = (_rand(rng, B, H, N, d) for d in (dk, dk, dv, dv))
+    rf = phi.startswith("trig_rf")
+    om = make_omega(m, dk, seed=5) if rf else None
+    s = dk ** -0.25 if rf else 1.0
+    F = 2 * m if rf else dk
+    S0 = rng.standard_normal((B, H, F, dv)) * 0.2
+    z0 = rng.random((B, H, F)) + 0.5 if not rf else rng.standard_normal((B, H, F)) * 0.05
+    dS_out, dz_out = rng.standard_normal((B, H, F, dv)), rng.standard_normal((B, H, F))
+    mask = (rng.random((B, N)) < 0.3) if masked else None
+    got = orc.backward(q, k, v, g, np.array(lams), 1e-6, phi, om, s, S0, z0, dS_out, dz_out,
+                       key_padding_mask=mask)
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+         for n, a in (("q", q), ("k", k), ("v", v), ("S0", S0), ("z0", z0), ("lam", np.array(lams)))}
+    keep = torch.ones(B, N, dtype=torch.float64) if mask is None else torch.tensor(~mask, dtype=torch.float64)
+    loss = _torch_quadratic_loss(t["q"], t["k"], t["v"], torch.tensor(g), t["lam"], 1e-6, phi,
+                                 None if om is None else torch.tensor(om, dtype=torch.float64), s,
+                                 t["S0"], t["z0"], torch.tensor(dS_out), torch.tensor(dz_out), keep)
+    loss.backward()
+    for name, ref in (("dq", t["q"].grad), ("dk", t["k"].grad), ("dv", t["v"].grad),
+                      ("dS0", t["S0"].grad), ("dz0", t["z0"].grad)):
+        np.testing.assert_allclose(got[name], ref.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+    np.testing.assert_allclose(got["dlam"].sum(0), t["lam"].grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("lams,masked", [((0.0, 0.93), False), ((0.5, 1.0), True)])
+def test_backward_directional_finite_differences(orc, lams, masked):
+    # <grad, delta> against central differences of the forward oracle, for every
+    # input at once (step 1e-5: truncation ~1e-10, well inside the bound).
+    # lambda = 0 is included (the recurrence is a polynomial in lambda), but
+    # not with a mask: a padded key then leaves den = eps, where the loss is
+    # too curved for a finite difference.
+    rng = np.random.default_rng(31)
+    B, H, N, dk, dv = 1, 2, 40, 4, 3
+    q, k, v, g = (_rand(rng, B, H, N, d) for d in (dk, dk, dv, dv))
+    S0, z0 = rng.standard_normal((B, H, dk, dv)) * 0.2, rng.random((B, H, dk)) + 0.5
+    dS_out, dz_out = rng.standard_normal((B, H, dk, dv)), rng.standard_normal((B, H, dk))
+    lam = np.array(lams)
+    mask = (rng.random((B, N)) < 0.2) if masked else None
+    gr = orc.backward(q, k, v, g, lam, 1e-6, S0=S0, z0=z0, dS_out=dS_out, dz_out=dz_out,
+                      key_padding_mask=mask)
+    d = {n: rng.standard_normal(a.shape) for n, a in (("q", q), ("k", k), ("v", v), ("S0", S0),
+                                                      ("z0", z0), ("lam", lam))}
+
+    def loss(h):
+        y, S, z = orc.causal(q + h * d["q"], k + h * d["k"], v + h * d["v"], lam + h * d["lam"], 1e-6,
+                             S0=S0 + h * d["S0"], z0=z0 + h * d["z0"], want_state=True,
+                             key_padding_mask=mask)
+        return (g * y).sum() + (dS_out * S).sum() + (dz_out * z).sum()
+
+    hstep = 1e-5
+    fd = (loss(hstep) - loss(-hstep)) / (2 * hstep)
+    an = sum((gr[n] * d[x]).sum() for n, x in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dS0", "S0"),
+                                               ("dz0", "z0")))
+    an += (gr["dlam"].sum(0) * d["lam"]).sum()
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("phi,m", [("elu1", 0), ("relu", 0), ("trig_rf", 5), ("trig_rf_softmax", 3),
+                                   ("trig_rf_plain", 4)])
+def test_phi_vjp_finite_differences(orc, phi, m):
+    rng = np.random.default_rng(zlib.crc32(phi.encode()))
+    dk = 6
+    om = make_omega(m, dk, seed=2) if m else None
+    s = 0.7 if m else 1.0
+    x = rng.standard_normal((5, dk))
+    x[np.abs(x) < 1e-2] += 0.1  # keep ReLU away from its kink
+    F = 2 * m if m else dk
+    dp = rng.standard_normal((5, F))
+    got = orc.phi_vjp(x, dp, phi, om, s)
+    h = 1e-6
+    for c in range(dk):
+        e = np.zeros(dk)
+        e[c] = h
+        fd = ((orc.phi_map(x + e, phi, om, s) - orc.phi_map(x - e, phi, om, s)) / (2 * h) * dp).sum(-1)
+        np.testing.assert_allclose(got[:, c], fd, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_without_tokens_passes_state_gradient(orc):
+    rng = np.random.default_rng(32)
+    dS = rng.standard_normal((1, 1, 4, 3))
+    dz = rng.standard_normal((1, 1, 4))
+    q = np.zeros((1, 1, 0, 4))
+    v = np.zeros((1, 1, 0, 3))
+    gr = orc.backward(q, q, v, v, [0.5], dS_out=dS, dz_out=dz)
+    np.testing.assert_array_equal(gr["dS0"], dS)
+    np.testing.assert_array_equal(gr["dz0"], dz)
+    assert gr["dlam"][0, 0] == 0.0
