@@ -358,8 +358,43 @@ def cross_w2(ctx, steps=200):
     return res
 
 
-# Mask / cross / packed lines measured beside the main workloads
-SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2))
+def backward_w2(ctx, steps=100):
+    """Backward of the headline forward (B=4 H=8 N=4096 d=64 bf16, lambda = 1):
+    one la_backward_causal call -- forward segment states and scan, the dq
+    sweep, the adjoint segment sums and reverse scan, the dk/dv sweep."""
+    torch, la = ctx.torch, ctx.la
+    B, H, N, d = 4, 8, 4096, 64
+    wl, (q, k, v) = _w2_inputs(ctx, B, H, N)
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(22)
+    dy = device_normal(torch, g, (B, H, N, d), 0.5, ctx.dev)
+    y = torch.empty_like(q)
+    la.la_forward_causal(q, k, v, y, eps=wl.eps)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_n = la.la_workspace_size_backward(B, H, N, d, d)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=ctx.dev)
+    SZ = d * d + d
+    P = max(1, -(-512 // (B * H)))
+    rows = B * H * N
+    ids = la.KERNEL_IDS
+    kb = {ids["bwd_q"]: rows * (5 * d * 2 + d * 2 + 8) + P * B * H * SZ * 4,
+          ids["bwd_rlocal"]: rows * (2 * d * 2 + 8) + P * B * H * SZ * 4,
+          ids["bwd_kv"]: rows * (4 * d * 2 + 8 + 2 * d * 2) + P * B * H * SZ * 4,
+          ids["fwd_local"]: rows * 2 * d * 2 + P * B * H * SZ * 4,
+          ids["scan"]: 2 * P * B * H * SZ * 4}
+
+    def step():
+        la.la_backward_causal(q, k, v, y, dy, dq, dk, dv, eps=wl.eps, workspace=ws)
+
+    name = "elu1_backward_B%d_H%d_N%d_d%d_bf16" % (B, H, N, d)
+    res = bench_call(ctx, name, step, B * N, kb, steps, max(ctx.warmup, 5), launches_per_step=8)
+    res["segments"] = P
+    return res
+
+
+# Mask / cross / packed / backward lines measured beside the main workloads
+SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2),
+                  ("backward_w2", backward_w2))
 
 
 def workload4_decode(ctx, steps=1024):

@@ -213,6 +213,37 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
                            const uint8_t* key_padding_mask, const la_phi* phi, float eps,
                            void* workspace, size_t workspace_bytes, la_stream_t stream);
 
+/* Gradients of la_forward_causal (training: "Attention is also an FFN"
+ * sec. 4.1 and 5.2 train with the chunked form).  For the loss
+ *   L = sum_i dy_i . y_i + <dS_out, S_final> + <dz_out, z_final>
+ * writes dq, dk [B,H,N,d_k] and dv [B,H,N,d_v] (input type), and, if given,
+ * dS_in [B,H,F,d_v] / dz_in [B,H,F] fp32, the gradient of the initial state.
+ * q, k, v, y, dy: device inputs of shape->in_dtype; y is the forward's output
+ * for the same q, k, v, lambda_h, eps, key_padding_mask and S_in / z_in, and
+ * shape->out_dtype must equal shape->in_dtype.  dS_out / dz_out: optional
+ * gradient of the final state (both or none; NULL = 0).  Outputs must not
+ * alias inputs or each other.  Feature maps: LA_PHI_ELU1 and LA_PHI_RELU
+ * (others: LA_ERR_UNSUPPORTED).  The gradient of lambda is not computed.
+ * Method: with dnum_i = dy_i / den_i and dden_i = -(dy_i . y_i) / den_i,
+ * dq comes from a chunked sweep in token order that carries the forward
+ * state (d phi(q_i) = S_i dnum_i + z_i dden_i), dk and dv from a chunked
+ * sweep in reverse order that carries the adjoint
+ * U_j = sum_{i>=j} lambda^(i-j) phi(q_i) dnum_i^T (d phi(k_j) = U_j v_j + u_j,
+ * dv_j = U_j^T phi(k_j)); long rows are cut into segments joined by scans.
+ * Workspace: la_workspace_size_backward bytes (8 bytes per token plus the
+ * segment states). */
+size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi);
+la_status la_backward_causal(const void* q, const void* k, const void* v,
+                             const void* y, const void* dy,
+                             void* dq, void* dk, void* dv,
+                             const la_shape* shape, const la_phi* phi,
+                             const float* lambda_h, float eps,
+                             const uint8_t* key_padding_mask,
+                             const float* S_in, const float* z_in,
+                             const float* dS_out, const float* dz_out,
+                             float* dS_in, float* dz_in,
+                             void* workspace, size_t workspace_bytes, la_stream_t stream);
+
 /* Recurrent decode steps, in place ("From standard attention to linear
  * attention" sec. 6 autoregressive step, with the decay of "Attention is also
  * an FFN" sec. 3.2): per (b,h), for each of the N tokens in order
@@ -244,7 +275,10 @@ enum {
     LA_KERNEL_SCAN = 3,        /* segment state scan / reduction               */
     LA_KERNEL_DECODE = 4,      /* recurrent decode step                        */
     LA_KERNEL_FILL = 5,        /* zero fill (la_init_state, empty forward)     */
-    LA_KERNEL_COPY = 6         /* state copy (empty forward)                   */
+    LA_KERNEL_COPY = 6,        /* state copy (empty forward)                   */
+    LA_KERNEL_BWD_Q = 7,       /* backward: dq sweep                           */
+    LA_KERNEL_BWD_RLOCAL = 8,  /* backward: adjoint segment sums               */
+    LA_KERNEL_BWD_KV = 9       /* backward: dk, dv sweep                       */
 };
 la_status la_profile_begin(int32_t max_launches);
 la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);

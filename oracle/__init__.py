@@ -62,7 +62,7 @@ def _load():
     lib.orc_phi_vjp.argtypes = [I, P, I, I, P, D, P, P]
     lib.orc_phi_vjp.restype = None
     lib.orc_backward.argtypes = [P, P, P, P, L, L, I, I, I, I, P, D, P, D, U, P, P, P, P,
-                                 P, P, P, P, P, P]
+                                 P, P, P, P, P, P, P, P, P]
     lib.orc_backward.restype = None
     lib.orc_decode_step.argtypes = [P, P, P, L, I, I, I, I, P, D, P, D, P, P, P]
     lib.orc_decode_step.restype = None
@@ -282,13 +282,15 @@ def causal_varlen(q, k, v, cu_seqlens, lam=None, eps=1e-6, phi="elu1", omega=Non
 
 
 def backward(q, k, v, gy, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0, S0=None, z0=None,
-             dS_out=None, dz_out=None, key_padding_mask=None, threads=None):
+             dS_out=None, dz_out=None, key_padding_mask=None, threads=None, want_kappa=False):
     """Gradients of the causal forward for the loss sum(gy * y) +
     <dS_out, S_final> + <dz_out, z_final>.
 
     Returns a dict: dq, dk [B,H,N,dk], dv [B,H,N,dv], dS0 [B,H,F,dv],
     dz0 [B,H,F] (gradient of the initial state) and dlam [B,H] (per row;
-    a per-head parameter's gradient is its sum over B).
+    a per-head parameter's gradient is its sum over B); with want_kappa
+    (elementwise feature maps) also the rows' cancellation factors
+    kappa_dq, kappa_dk, kappa_dv [B,H,N].
     """
     lib = _load()
     q, k, v, gy, om = _f64(q), _f64(k), _f64(v), _f64(gy), _f64(omega)
@@ -301,6 +303,9 @@ def backward(q, k, v, gy, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
     kpm = _mask_rows(key_padding_mask, B, H, N)
     out = {"dq": np.empty((B, H, N, dk)), "dk": np.empty((B, H, N, dk)), "dv": np.empty((B, H, N, dv)),
            "dS0": np.empty((B, H, F, dv)), "dz0": np.empty((B, H, F)), "dlam": np.empty((B, H))}
+    if want_kappa:
+        for name in ("kappa_dq", "kappa_dk", "kappa_dv"):
+            out[name] = np.empty((B, H, N))
 
     def run(rng):
         a, b = rng
@@ -309,7 +314,9 @@ def backward(q, k, v, gy, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
                          float(eps), _uptr(kpm, a * N), _ptr(S0, a * F * dv), _ptr(z0, a * F),
                          _ptr(dS_out, a * F * dv), _ptr(dz_out, a * F),
                          _ptr(out["dq"], a * N * dk), _ptr(out["dk"], a * N * dk), _ptr(out["dv"], a * N * dv),
-                         _ptr(out["dS0"], a * F * dv), _ptr(out["dz0"], a * F), _ptr(out["dlam"], a))
+                         _ptr(out["dS0"], a * F * dv), _ptr(out["dz0"], a * F), _ptr(out["dlam"], a),
+                         _ptr(out.get("kappa_dq"), a * N), _ptr(out.get("kappa_dk"), a * N),
+                         _ptr(out.get("kappa_dv"), a * N))
 
     parts = _split(B * H, threads or default_threads())
     if len(parts) == 1:

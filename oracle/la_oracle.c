@@ -333,13 +333,21 @@ void orc_phi_vjp(int kind, const double* x, int dk, int m, const double* omega,
  * kpm as in orc_causal (a padded key has phi(k) = 0 and gets dk = dv = 0).
  * g [nbh][N][dv]; dS_out [nbh][F][dv] / dz_out [nbh][F] may be NULL (zero);
  * outputs dq, dk [nbh][N][dk], dv [nbh][N][dv], dS0 [nbh][F][dv], dz0
- * [nbh][F] (NULL = not written), dlam [nbh]. */
+ * [nbh][F] (NULL = not written), dlam [nbh].
+ * Cancellation factors (kq, kk, kv [nbh][N], NULL = not computed): for each
+ * gradient row, the largest sum of absolute values of the elementary terms
+ * it is made of (the recurrences above run on |.|, with |dden_i| replaced by
+ * sum_d |dnum_i,d y_i,d|, the terms of dden), over the row's largest |entry|;
+ * the rounding error of any evaluation order is bounded relative to the
+ * former, so kappa says how far the row's own size understates it
+ * (the elementwise feature maps only). */
 void orc_backward(const double* q, const double* k, const double* v, const double* gy,
                   long nbh, long N, int dk, int dv, int kind, int m,
                   const double* omega, double scale, const double* lam, double eps,
                   const unsigned char* kpm, const double* S0, const double* z0,
                   const double* dS_out, const double* dz_out,
-                  double* dq, double* dkx, double* dvx, double* dS0, double* dz0, double* dlam)
+                  double* dq, double* dkx, double* dvx, double* dS0, double* dz0, double* dlam,
+                  double* kq, double* kk, double* kv)
 {
     const int F = feat_dim(kind, dk, m);
     const size_t FD = (size_t)F * dv;
@@ -354,7 +362,12 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
     double* dp = (double*)malloc(sizeof(double) * (size_t)F);
     double* dnum = (double*)malloc(sizeof(double) * (size_t)dv * (N > 0 ? N : 1));
     double* dden = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* ddb = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     double* y = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* Sb = (double*)malloc(sizeof(double) * FD);
+    double* zb = (double*)malloc(sizeof(double) * (size_t)F);
+    double* xb = (double*)malloc(sizeof(double) * (size_t)(F > dv ? F : dv));
+    const int want_k = kq && kk && kv && (kind == ORC_PHI_ELU1 || kind == ORC_PHI_RELU);
     for (long bh = 0; bh < nbh; ++bh) {
         const double L = lam[bh];
         const double* qr = q + (size_t)bh * N * dk;
@@ -368,6 +381,8 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
         else memset(z, 0, sizeof(double) * (size_t)F);
         memset(T, 0, sizeof(double) * FD);
         memset(t, 0, sizeof(double) * (size_t)F);
+        for (size_t e = 0; e < FD; ++e) Sb[e] = S0 ? fabs(S0[(size_t)bh * FD + e]) : 0.0;
+        for (int f = 0; f < F; ++f) zb[f] = z0 ? fabs(z0[(size_t)bh * F + f]) : 0.0;
         double dl = 0.0;
         /* forward, token order */
         for (long i = 0; i < N; ++i) {
@@ -384,9 +399,11 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
                     const size_t e = (size_t)f * dv + d;
                     T[e] = L * T[e] + Sp[e];
                     S[e] = L * S[e] + pk[f] * vi[d];
+                    Sb[e] = L * Sb[e] + fabs(pk[f] * vi[d]);
                 }
                 t[f] = L * t[f] + zp[f];
                 z[f] = L * z[f] + pk[f];
+                zb[f] = L * zb[f] + fabs(pk[f]);
             }
             double den = eps;
             for (int f = 0; f < F; ++f) den += pqi[f] * z[f];
@@ -401,6 +418,8 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
             double* dni = dnum + (size_t)i * dv;
             for (int d = 0; d < dv; ++d) dni[d] = gi[d] / den;
             dden[i] = -gy_dot / den;
+            ddb[i] = 0.0;
+            for (int d = 0; d < dv; ++d) ddb[i] += fabs(dni[d] * y[d]);
             for (int f = 0; f < F; ++f) {
                 double a = z[f] * dden[i], b = t[f] * dden[i];
                 for (int d = 0; d < dv; ++d) {
@@ -411,6 +430,22 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
                 dl += pqi[f] * b;
             }
             orc_phi_vjp(kind, qr + (size_t)i * dk, dk, m, omega, scale, dp, dq + ((size_t)bh * N + i) * dk);
+            if (want_k) {
+                /* |terms| of d phi(q_i) = S_i dnum_i + z_i dden_i, through |phi'| */
+                for (int f = 0; f < F; ++f) {
+                    double a = zb[f] * ddb[i];
+                    for (int d = 0; d < dv; ++d) a += Sb[(size_t)f * dv + d] * fabs(dni[d]);
+                    dp[f] = a;
+                }
+                orc_phi_vjp(kind, qr + (size_t)i * dk, dk, m, omega, scale, dp, xb);
+                const double* dqi = dq + ((size_t)bh * N + i) * dk;
+                double num = 0.0, den2 = 0.0;
+                for (int f = 0; f < dk; ++f) {
+                    if (fabs(xb[f]) > num) num = fabs(xb[f]);
+                    if (fabs(dqi[f]) > den2) den2 = fabs(dqi[f]);
+                }
+                kq[(size_t)bh * N + i] = den2 > 0.0 ? num / den2 : (num > 0.0 ? INFINITY : 1.0);
+            }
         }
         if (dS_out)
             for (size_t e = 0; e < FD; ++e) dl += dS_out[(size_t)bh * FD + e] * T[e];
@@ -422,6 +457,8 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
         else memset(S, 0, sizeof(double) * FD);
         if (dz_out) memcpy(z, dz_out + (size_t)bh * F, sizeof(double) * (size_t)F);
         else memset(z, 0, sizeof(double) * (size_t)F);
+        for (size_t e = 0; e < FD; ++e) Sb[e] = fabs(S[e]);
+        for (int f = 0; f < F; ++f) zb[f] = fabs(z[f]);
         for (long i = N - 1; i >= 0; --i) {
             const double* pqi = pq + (size_t)i * F;
             const double* dni = dnum + (size_t)i * dv;
@@ -430,8 +467,10 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
                 for (int d = 0; d < dv; ++d) {
                     const size_t e = (size_t)f * dv + d;
                     S[e] = w * S[e] + pqi[f] * dni[d];
+                    Sb[e] = w * Sb[e] + fabs(pqi[f] * dni[d]);
                 }
                 z[f] = w * z[f] + pqi[f] * dden[i];
+                zb[f] = w * zb[f] + fabs(pqi[f]) * ddb[i];
             }
             orc_phi(kind, kr + (size_t)i * dk, dk, m, omega, scale, pk);
             const int padded = mr && mr[i];
@@ -450,6 +489,32 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
                 dp[f] = padded ? 0.0 : a;
             }
             orc_phi_vjp(kind, kr + (size_t)i * dk, dk, m, omega, scale, dp, dkx + ((size_t)bh * N + i) * dk);
+            if (want_k) {
+                /* dv_i = U_i^T phi(k_i): |U|^T |phi(k)| */
+                double num = 0.0, den2 = 0.0;
+                for (int d = 0; d < dv; ++d) {
+                    double a = 0.0;
+                    for (int f = 0; f < F; ++f) a += Sb[(size_t)f * dv + d] * fabs(pk[f]);
+                    if (a > num) num = a;
+                    if (fabs(dvi[d]) > den2) den2 = fabs(dvi[d]);
+                }
+                kv[(size_t)bh * N + i] = den2 > 0.0 ? num / den2 : (num > 0.0 ? INFINITY : 1.0);
+                /* d phi(k_i) = U_i v_i + u_i: |U| |v| + |u|, through |phi'| */
+                for (int f = 0; f < F; ++f) {
+                    double a = zb[f];
+                    for (int d = 0; d < dv; ++d) a += Sb[(size_t)f * dv + d] * fabs(vi[d]);
+                    dp[f] = padded ? 0.0 : a;
+                }
+                orc_phi_vjp(kind, kr + (size_t)i * dk, dk, m, omega, scale, dp, xb);
+                const double* dki = dkx + ((size_t)bh * N + i) * dk;
+                num = 0.0;
+                den2 = 0.0;
+                for (int f = 0; f < dk; ++f) {
+                    if (fabs(xb[f]) > num) num = fabs(xb[f]);
+                    if (fabs(dki[f]) > den2) den2 = fabs(dki[f]);
+                }
+                kk[(size_t)bh * N + i] = den2 > 0.0 ? num / den2 : (num > 0.0 ? INFINITY : 1.0);
+            }
         }
         /* gradient of the initial state: S_0 = lambda S_{-1} + ... */
         const double w0 = N > 0 ? L : 1.0;
@@ -459,5 +524,5 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
             for (int f = 0; f < F; ++f) dz0[(size_t)bh * F + f] = w0 * z[f];
     }
     free(S); free(z); free(T); free(t); free(Sp); free(zp); free(pq); free(pk); free(dp);
-    free(dnum); free(dden); free(y);
+    free(dnum); free(dden); free(ddb); free(y); free(Sb); free(zb); free(xb);
 }

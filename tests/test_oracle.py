@@ -669,3 +669,22 @@ def test_backward_without_tokens_passes_state_gradient(orc):
     np.testing.assert_array_equal(gr["dS0"], dS)
     np.testing.assert_array_equal(gr["dz0"], dz)
     assert gr["dlam"][0, 0] == 0.0
+
+
+def test_backward_kappa_bounds(orc):
+    # kappa >= 1 always; no cancellation (positive features, positive dy, and
+    # values making every term of dv positive) gives kappa_dv = 1; the first
+    # token's dq cancels exactly but for eps (kappa huge)
+    rng = np.random.default_rng(33)
+    B, H, N, dk, dv = 1, 2, 30, 4, 3
+    q, k = _rand(rng, B, H, N, dk), _rand(rng, B, H, N, dk)
+    v, g = _rand(rng, B, H, N, dv), np.abs(_rand(rng, B, H, N, dv)) + 0.1
+    r = orc.backward(q, k, v, g, [0.9, 1.0], want_kappa=True)
+    for n in ("kappa_dq", "kappa_dk", "kappa_dv"):
+        assert np.all(r[n] >= 1.0 - 1e-12), n
+    np.testing.assert_allclose(r["kappa_dv"], 1.0, rtol=1e-12)
+    assert np.all(r["kappa_dq"][:, :, 0] > 1e6)
+    # the gradients themselves are unchanged by asking for kappa
+    r0 = orc.backward(q, k, v, g, [0.9, 1.0])
+    for n in ("dq", "dk", "dv", "dS0", "dz0", "dlam"):
+        np.testing.assert_array_equal(r[n], r0[n])

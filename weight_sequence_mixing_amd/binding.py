@@ -29,10 +29,11 @@ LA_MAX_HEADS = 256
 # names declared in include/la.h
 EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
            "la_forward_causal_masked", "la_workspace_size_varlen", "la_forward_causal_varlen",
-           "la_workspace_size_cross", "la_forward_cross",
+           "la_workspace_size_cross", "la_forward_cross", "la_workspace_size_backward", "la_backward_causal",
            "la_decode_step", "la_status_string", "la_last_error", "la_profile_begin", "la_profile_end",
            "la_kernel_name")
-KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6}
+KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6,
+              "bwd_q": 7, "bwd_rlocal": 8, "bwd_kv": 9}
 
 
 class LaPhiC(ctypes.Structure):
@@ -92,6 +93,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.la_workspace_size_cross.restype = sz
     lib.la_forward_cross.argtypes = [vp, vp, vp, vp, SP, i64, vp, PP, f, vp, sz, vp]
     lib.la_forward_cross.restype = ctypes.c_int
+    lib.la_workspace_size_backward.argtypes = [SP, PP]
+    lib.la_workspace_size_backward.restype = sz
+    lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, sz, vp]
+    lib.la_backward_causal.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp]
     lib.la_decode_step.restype = ctypes.c_int
     lib.la_status_string.argtypes = [ctypes.c_int]
@@ -361,6 +367,33 @@ def la_forward_cross(q, k, v, y, key_padding_mask=None, phi: Optional[Phi] = Non
                                  _mask_ptr(key_padding_mask), ctypes.byref(pc), float(eps), _ptr(ws), ws_bytes,
                                  _stream(stream)))
     return y
+
+
+def la_workspace_size_backward(B, H, N, d_k, d_v, in_dtype=LA_BF16, phi: Optional[Phi] = None) -> int:
+    load_library()
+    phi = phi or Phi()
+    shape = LaShapeC(B, H, N, d_k, d_v, in_dtype, in_dtype)
+    pc = phi.c()
+    return int(_lib.la_workspace_size_backward(ctypes.byref(shape), ctypes.byref(pc)))
+
+
+def la_backward_causal(q, k, v, y, dy, dq, dk, dv, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6,
+                       key_padding_mask=None, S_in=None, z_in=None, dS_out=None, dz_out=None, dS_in=None,
+                       dz_in=None, workspace=None, stream=None):
+    """Gradients of la_forward_causal: writes dq, dk, dv (and dS_in, dz_in when given)."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    pc = phi.c()
+    need = int(_lib.la_workspace_size_backward(ctypes.byref(shape), ctypes.byref(pc)))
+    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
+    lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    _check(_lib.la_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   ctypes.byref(shape), ctypes.byref(pc), lam_ptr, float(eps),
+                                   _mask_ptr(key_padding_mask), _ptr(S_in), _ptr(z_in), _ptr(dS_out),
+                                   _ptr(dz_out), _ptr(dS_in), _ptr(dz_in), _ptr(ws), ws_bytes, _stream(stream)))
+    del lam_keep
+    return dq, dk, dv
 
 
 def la_decode_step(q, k, v, y, S, z, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6, stream=None):

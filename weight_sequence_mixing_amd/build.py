@@ -30,6 +30,8 @@ SOURCES = [
     "la_inst_f32.hip",
     "la_inst_bf16_relu.hip",
     "la_inst_f32_relu.hip",
+    "la_inst_bwd_bf16.hip",
+    "la_inst_bwd_f32.hip",
     "la_scan.hip",
     "la_api.cpp",
 ]

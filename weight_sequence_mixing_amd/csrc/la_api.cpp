@@ -396,6 +396,9 @@ const char* la_kernel_name(int32_t id)
     case LA_KERNEL_DECODE: return "la_decode_kernel";
     case LA_KERNEL_FILL: return "la_fill_zero_kernel";
     case LA_KERNEL_COPY: return "la_copy_kernel";
+    case LA_KERNEL_BWD_Q: return "la_bwd_q_kernel";
+    case LA_KERNEL_BWD_RLOCAL: return "la_bwd_kv_kernel (adjoint segment)";
+    case LA_KERNEL_BWD_KV: return "la_bwd_kv_kernel (dk dv)";
     }
     return "unknown";
 }
@@ -817,6 +820,237 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
     qa.src_seg_stride = 0;
     if ((e = launch(LA_KERNEL_FWD_QUERY, [&] { return ent->fwd(qa, MODE_QUERY, strm); })) != hipSuccess)
         return hip_fail(e, "cross query launch");
+    return ok();
+}
+
+namespace {
+
+const BwdEntry* find_bwd(int in_dtype, int phi, int dk, int F, int dv)
+{
+    const BwdEntry* tabs[] = {kBwdEntriesBf16, kBwdEntriesF32};
+    const int counts[] = {kNumBwdEntriesBf16, kNumBwdEntriesF32};
+    for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < counts[t]; ++i) {
+            const BwdEntry& e = tabs[t][i];
+            if (e.in_dtype == in_dtype && e.phi == phi && e.dk == dk && e.F == F && e.dv == dv) return &e;
+        }
+    return nullptr;
+}
+
+// Shape checks of the backward beyond the forward's; sets the segment plan.
+la_status check_backward(const la_shape* shape, const la_phi* phi, int* F, const KernelEntry** ent,
+                         const BwdEntry** bent)
+{
+    la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, F, ent);
+    if (st != LA_OK) return st;
+    if (phi->kind != LA_PHI_ELU1 && phi->kind != LA_PHI_RELU)
+        return fail(LA_ERR_UNSUPPORTED, "the backward supports the elementwise feature maps (elu+1, ReLU)");
+    if (shape->out_dtype != shape->in_dtype)
+        return fail(LA_ERR_UNSUPPORTED, "the backward takes y and dy in the input type (out_dtype == in_dtype)");
+    *bent = find_bwd(shape->in_dtype, phi->kind, shape->d_k, *F, shape->d_v);
+    if (!*bent) return fail(LA_ERR_UNSUPPORTED, "no backward kernel for this shape");
+    return LA_OK;
+}
+
+struct BwdPlan {
+    int P;
+    int64_t cps;
+    int64_t SZ;
+    size_t tok_floats, seg_floats, bytes;
+};
+
+BwdPlan bwd_plan(const la_shape* s, int F, int C)
+{
+    BwdPlan p;
+    const int64_t BH = s->B * s->H;
+    const int64_t NC = (s->N + C - 1) / C;
+    p.P = 1;
+    p.cps = 1;
+    if (NC > 0) cut_segments(NC, BH, &p.P, &p.cps);
+    p.SZ = (int64_t)F * s->d_v + F;
+    p.tok_floats = (size_t)BH * s->N * 2;
+    p.seg_floats = p.P > 1 ? (size_t)p.P * BH * p.SZ : 0;
+    const size_t tok_bytes = (p.tok_floats * sizeof(float) + 255) & ~size_t(255);
+    p.bytes = s->N > 0 ? tok_bytes + ((p.seg_floats * sizeof(float) + 255) & ~size_t(255)) : 0;
+    return p;
+}
+
+}  // namespace
+
+size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi)
+{
+    int F = 0;
+    const KernelEntry* e = nullptr;
+    const BwdEntry* be = nullptr;
+    const std::string saved = g_last_error;
+    const la_status st = check_backward(shape, phi, &F, &e, &be);
+    g_last_error = saved;
+    if (st != LA_OK) return 0;
+    return bwd_plan(shape, F, be->C).bytes;
+}
+
+la_status la_backward_causal(const void* q, const void* k, const void* v, const void* y, const void* dy,
+                             void* dq, void* dk, void* dv, const la_shape* shape, const la_phi* phi,
+                             const float* lambda_h, float eps, const uint8_t* key_padding_mask,
+                             const float* S_in, const float* z_in, const float* dS_out, const float* dz_out,
+                             float* dS_in, float* dz_in, void* workspace, size_t workspace_bytes,
+                             la_stream_t stream)
+{
+    int F = 0;
+    const KernelEntry* ent = nullptr;
+    const BwdEntry* bent = nullptr;
+    la_status st = check_backward(shape, phi, &F, &ent, &bent);
+    if (st != LA_OK) return st;
+    if ((S_in == nullptr) != (z_in == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_in and z_in must be given together");
+    if ((dS_out == nullptr) != (dz_out == nullptr))
+        return fail(LA_ERR_INVALID_ARGUMENT, "dS_out and dz_out must be given together");
+    if ((dS_in == nullptr) != (dz_in == nullptr))
+        return fail(LA_ERR_INVALID_ARGUMENT, "dS_in and dz_in must be given together");
+    const float* st_ptrs[] = {S_in, z_in, dS_out, dz_out, dS_in, dz_in};
+    for (const float* p : st_ptrs)
+        if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
+    if ((st = check_eps(eps)) != LA_OK) return st;
+    LamTable lam;
+    if ((st = make_lam(lambda_h, shape->H, &lam)) != LA_OK) return st;
+    const int64_t BH = shape->B * shape->H;
+    if (BH > 65535) return fail(LA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)BH);
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    const int64_t nS = BH * F * (int64_t)shape->d_v, nz = BH * F;
+
+    if (shape->N == 0) {
+        // no tokens: the initial state's gradient is the final state's
+        hipError_t e = hipSuccess;
+        if (dS_in) {
+            if (dS_out) {
+                e = launch(LA_KERNEL_COPY, [&] { return launch_copy(dS_in, dS_out, nS, strm); });
+                if (e == hipSuccess) e = launch(LA_KERNEL_COPY, [&] { return launch_copy(dz_in, dz_out, nz, strm); });
+            } else {
+                e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(dS_in, nS, strm); });
+                if (e == hipSuccess) e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(dz_in, nz, strm); });
+            }
+        }
+        if (e != hipSuccess) return hip_fail(e, "la_backward_causal (N=0)");
+        return ok();
+    }
+    const void* ins[] = {q, k, v, y, dy};
+    void* outs[] = {dq, dk, dv};
+    for (const void* p : ins)
+        if (!p || !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, y, dy must be non-NULL and 16-byte aligned");
+    for (const void* p : outs)
+        if (!p || !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must be non-NULL and 16-byte aligned");
+    const size_t es = elem_size(shape->in_dtype), rows = (size_t)BH * shape->N;
+    const size_t nk = rows * shape->d_k * es, nv = rows * shape->d_v * es;
+    const size_t in_sz[] = {nk, nk, nv, nv, nv};
+    const size_t out_sz[] = {nk, nk, nv};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 5; ++i)
+            if (overlaps(outs[o], out_sz[o], ins[i], in_sz[i]))
+                return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must not alias q, k, v, y or dy");
+        for (int o2 = 0; o2 < o; ++o2)
+            if (overlaps(outs[o], out_sz[o], outs[o2], out_sz[o2]))
+                return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must not overlap");
+    }
+    const BwdPlan plan = bwd_plan(shape, F, bent->C);
+    if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.bytes);
+    if (workspace_bytes < plan.bytes)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.bytes, workspace_bytes);
+    if (!aligned16(workspace)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    float* tok = static_cast<float*>(workspace);
+    float* segs = tok + (((plan.tok_floats * sizeof(float) + 255) & ~size_t(255)) / sizeof(float));
+
+    BwdArgs b;
+    std::memset(&b, 0, sizeof(b));
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.y = y;
+    b.gy = dy;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.tok = tok;
+    b.N = shape->N;
+    b.BH = (int32_t)BH;
+    b.H = (int32_t)shape->H;
+    b.P = plan.P;
+    b.cps = plan.cps;
+    b.eps = eps;
+    b.kpm = key_padding_mask;
+    b.lam = lam;
+    const int64_t FD = (int64_t)F * shape->d_v;
+    hipError_t e;
+    if (plan.P > 1) {
+        // forward state at each segment's start: segment sums, then the scan
+        FwdArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.N = shape->N;
+        a.n_len = shape->N;
+        a.BH = (int32_t)BH;
+        a.H = (int32_t)shape->H;
+        a.P = plan.P;
+        a.cps = plan.cps;
+        a.eps = eps;
+        a.qk_scale = 1.0f;
+        a.kpm = key_padding_mask;
+        a.kpm_stride = shape->N;
+        a.lam = lam;
+        a.S_dst = segs;
+        a.z_dst = segs + FD;
+        a.dst_stride = plan.SZ;
+        a.dst_zstride = plan.SZ;
+        if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(a, MODE_LOCAL, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: segment state launch");
+        ScanArgs sa;
+        std::memset(&sa, 0, sizeof(sa));
+        sa.ws = segs;
+        sa.P = plan.P;
+        sa.BH = (int32_t)BH;
+        sa.H = (int32_t)shape->H;
+        sa.F = F;
+        sa.DV = shape->d_v;
+        sa.n_len = shape->N;
+        sa.seg_len = plan.cps * bent->C;
+        sa.causal = 1;
+        sa.S_init = S_in; sa.z_init = z_in; sa.init_stride = FD; sa.init_zstride = F;
+        sa.lam = lam;
+        if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: segment scan launch");
+        BwdArgs bq = b;
+        bq.S_src = segs; bq.z_src = segs + FD;
+        bq.src_stride = plan.SZ; bq.src_zstride = plan.SZ; bq.src_seg_stride = BH * plan.SZ;
+        if ((e = launch(LA_KERNEL_BWD_Q, [&] { return bent->bwd(bq, BMODE_Q, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: dq launch");
+        // adjoint at each segment's end: reverse segment sums, then the reverse scan
+        BwdArgs br = b;
+        br.S_dst = segs; br.z_dst = segs + FD;
+        br.dst_stride = plan.SZ; br.dst_zstride = plan.SZ;
+        if ((e = launch(LA_KERNEL_BWD_RLOCAL, [&] { return bent->bwd(br, BMODE_RLOCAL, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: adjoint segment launch");
+        ScanArgs ra = sa;
+        ra.reverse = 1;
+        ra.S_init = dS_out; ra.z_init = dz_out;
+        ra.S_fin = dS_in; ra.z_fin = dz_in; ra.fin_stride = FD; ra.fin_zstride = F;
+        if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(ra, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: adjoint scan launch");
+        BwdArgs bk = b;
+        bk.S_src = segs; bk.z_src = segs + FD;
+        bk.src_stride = plan.SZ; bk.src_zstride = plan.SZ; bk.src_seg_stride = BH * plan.SZ;
+        if ((e = launch(LA_KERNEL_BWD_KV, [&] { return bent->bwd(bk, BMODE_KV, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: dk dv launch");
+    } else {
+        BwdArgs bq = b;
+        bq.S_src = S_in; bq.z_src = z_in; bq.src_stride = FD; bq.src_zstride = F;
+        if ((e = launch(LA_KERNEL_BWD_Q, [&] { return bent->bwd(bq, BMODE_Q, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: dq launch");
+        BwdArgs bk = b;
+        bk.S_src = dS_out; bk.z_src = dz_out; bk.src_stride = FD; bk.src_zstride = F;
+        bk.S_dst = dS_in; bk.z_dst = dz_in; bk.dst_stride = FD; bk.dst_zstride = F;
+        if ((e = launch(LA_KERNEL_BWD_KV, [&] { return bent->bwd(bk, BMODE_KV, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: dk dv launch");
+    }
     return ok();
 }
 

@@ -89,7 +89,48 @@ struct ScanArgs {
     float* S_fin;            // final state (causal) or null
     float* z_fin;
     int64_t fin_stride, fin_zstride;
+    // 1: visit the segments last to first (the adjoint state of the backward
+    // pass, carried from the end of the sequence towards its start)
+    int32_t reverse;
     LamTable lam;
+};
+
+// Backward passes of the causal forward.  One launch covers P segments of cps
+// chunks of every (batch, head) row of N tokens (grid: P x BH), like FwdArgs.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* y;    // forward output (dq pass)
+    const void* gy;   // gradient of y
+    void* dq;
+    void* dk;
+    void* dv;
+    float* tok;       // [BH][N][2]: 1/den and dden per token (written by the dq pass)
+    int64_t N;
+    int32_t BH, H, P;
+    int64_t cps;
+    float eps;
+    const uint8_t* kpm;  // key padding mask [B][N] or null
+    // carried-in state of each segment: forward state [S|z] (dq pass) or
+    // adjoint [U|u] at the segment's end (kv pass), at
+    // src + seg*src_seg_stride + bh*src_stride; null = zero
+    const float* S_src;
+    const float* z_src;
+    int64_t src_stride, src_zstride, src_seg_stride;
+    // reverse-local pass: segment sums at dst + (seg*BH + bh)*dst_stride;
+    // kv pass with one segment: the initial state's gradient at
+    // dst + bh*dst_stride, if set
+    float* S_dst;
+    float* z_dst;
+    int64_t dst_stride, dst_zstride;
+    LamTable lam;
+};
+
+enum BwdMode : int {
+    BMODE_Q = 0,       // dq, and 1/den, dden per token
+    BMODE_RLOCAL = 1,  // segment sums of lambda^(i-s0) phi(q_i) [dnum_i, dden_i]^T
+    BMODE_KV = 2,      // dk, dv from the carried adjoint
 };
 
 struct DecArgs {
@@ -112,6 +153,7 @@ struct DecArgs {
 
 typedef hipError_t (*fwd_launch_fn)(const FwdArgs&, int mode, hipStream_t);
 typedef hipError_t (*dec_launch_fn)(const DecArgs&, hipStream_t);
+typedef hipError_t (*bwd_launch_fn)(const BwdArgs&, int mode, hipStream_t);
 
 struct KernelEntry {
     int in_dtype;   // LA_F32 / LA_BF16
@@ -121,6 +163,16 @@ struct KernelEntry {
     fwd_launch_fn fwd;
     dec_launch_fn dec;
 };
+
+struct BwdEntry {
+    int in_dtype, phi, dk, F, dv;
+    int C;
+    bwd_launch_fn bwd;
+};
+extern BwdEntry kBwdEntriesBf16[];
+extern int kNumBwdEntriesBf16;
+extern BwdEntry kBwdEntriesF32[];
+extern int kNumBwdEntriesF32;
 
 // Tables defined by the instantiation units.
 extern KernelEntry kEntriesBf16Elu[];

@@ -58,13 +58,18 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
     if (a.S_init)
         carry = isz ? *(const f32x4*)(a.z_init + bh * a.init_zstride + ez)
                     : *(const f32x4*)(a.S_init + bh * a.init_stride + e);
+    // reverse: the segments are visited last to first (the carry enters a
+    // segment at its end)
     for (int s0 = 0; s0 < nseg; s0 += kScanBatch) {
 #pragma unroll
-        for (int b = 0; b < kScanBatch; ++b) loc[b] = (s0 + b < nseg) ? base[(s0 + b) * slot] : zero;
+        for (int b = 0; b < kScanBatch; ++b) {
+            const int s = a.reverse ? nseg - 1 - (s0 + b) : s0 + b;
+            loc[b] = (s0 + b < nseg) ? base[s * slot] : zero;
+        }
 #pragma unroll
         for (int b = 0; b < kScanBatch; ++b) {
-            const int s = s0 + b;
-            if (s < nseg) {
+            if (s0 + b < nseg) {
+                const int s = a.reverse ? nseg - 1 - (s0 + b) : s0 + b;
                 const int64_t L = (s == a.P - 1 ? n_len : min((int64_t)(s + 1) * a.seg_len, n_len)) -
                                   (int64_t)s * a.seg_len;
                 base[s * slot] = carry;
