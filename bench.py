@@ -374,10 +374,12 @@ def cross_w2(ctx, steps=200):
     return res
 
 
-def backward_w2(ctx, steps=100):
+def backward_w2(ctx, steps=100, with_dlam=False):
     """Backward of the headline forward (B=4 H=8 N=4096 d=64 bf16, lambda = 1):
     one la_backward_causal call -- forward segment states and scan, the dq
-    sweep, the adjoint segment sums and reverse scan, the dk/dv sweep."""
+    sweep, the adjoint segment sums and reverse scan, the dk/dv sweep (and,
+    with_dlam, the lambda gradient: dS/dlambda carried in the dq sweep and
+    the reduction over segments and batch)."""
     torch, la = ctx.torch, ctx.la
     B, H, N, d = 4, 8, 4096, 64
     wl, (q, k, v) = _w2_inputs(ctx, B, H, N)
@@ -399,10 +401,12 @@ def backward_w2(ctx, steps=100):
           ids["fwd_local"]: rows * 2 * d * 2 + P * B * H * SZ * 4,
           ids["scan"]: 2 * P * B * H * SZ * 4}
 
-    def step():
-        la.la_backward_causal(q, k, v, y, dy, dq, dk, dv, eps=wl.eps, workspace=ws)
+    dlam = torch.empty(H, device=ctx.dev) if with_dlam else None
 
-    name = "elu1_backward_B%d_H%d_N%d_d%d_bf16" % (B, H, N, d)
+    def step():
+        la.la_backward_causal(q, k, v, y, dy, dq, dk, dv, eps=wl.eps, dlambda=dlam, workspace=ws)
+
+    name = "elu1_backward%s_B%d_H%d_N%d_d%d_bf16" % ("_dlam" if with_dlam else "", B, H, N, d)
     res = bench_call(ctx, name, step, B * N, kb, steps, max(ctx.warmup, 5), launches_per_step=8)
     res["segments"] = P
     return res
@@ -410,7 +414,7 @@ def backward_w2(ctx, steps=100):
 
 # Mask / cross / packed / backward lines measured beside the main workloads
 SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2),
-                  ("backward_w2", backward_w2))
+                  ("backward_w2", backward_w2), ("backward_dlam_w2", lambda c: backward_w2(c, with_dlam=True)))
 
 
 def workload4_decode(ctx, steps=1024):

@@ -223,13 +223,17 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
  * shape->out_dtype must equal shape->in_dtype.  dS_out / dz_out: optional
  * gradient of the final state (both or none; NULL = 0).  Outputs must not
  * alias inputs or each other.  Feature maps: LA_PHI_ELU1 and LA_PHI_RELU
- * (others: LA_ERR_UNSUPPORTED).  The gradient of lambda is not computed.
+ * (others: LA_ERR_UNSUPPORTED).  dlambda: optional device fp32 [H], the
+ * gradient of lambda_h summed over the batch (NULL = not computed; not
+ * available for fp32 inputs with d_k = d_v = 128, LA_ERR_UNSUPPORTED).
  * Method: with dnum_i = dy_i / den_i and dden_i = -(dy_i . y_i) / den_i,
  * dq comes from a chunked sweep in token order that carries the forward
  * state (d phi(q_i) = S_i dnum_i + z_i dden_i), dk and dv from a chunked
  * sweep in reverse order that carries the adjoint
  * U_j = sum_{i>=j} lambda^(i-j) phi(q_i) dnum_i^T (d phi(k_j) = U_j v_j + u_j,
  * dv_j = U_j^T phi(k_j)); long rows are cut into segments joined by scans.
+ * dlambda follows the product rule through the chunks: the dq sweep also
+ * carries T = dS/dlambda, and a reduction joins the segments.
  * Workspace: la_workspace_size_backward bytes (8 bytes per token plus the
  * segment states). */
 size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi);
@@ -241,7 +245,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v,
                              const uint8_t* key_padding_mask,
                              const float* S_in, const float* z_in,
                              const float* dS_out, const float* dz_out,
-                             float* dS_in, float* dz_in,
+                             float* dS_in, float* dz_in, float* dlambda,
                              void* workspace, size_t workspace_bytes, la_stream_t stream);
 
 /* Recurrent decode steps, in place ("From standard attention to linear
@@ -278,7 +282,8 @@ enum {
     LA_KERNEL_COPY = 6,        /* state copy (empty forward)                   */
     LA_KERNEL_BWD_Q = 7,       /* backward: dq sweep                           */
     LA_KERNEL_BWD_RLOCAL = 8,  /* backward: adjoint segment sums               */
-    LA_KERNEL_BWD_KV = 9       /* backward: dk, dv sweep                       */
+    LA_KERNEL_BWD_KV = 9,      /* backward: dk, dv sweep                       */
+    LA_KERNEL_BWD_DLAM = 10    /* backward: lambda-gradient reduction          */
 };
 la_status la_profile_begin(int32_t max_launches);
 la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);

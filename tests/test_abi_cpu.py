@@ -185,9 +185,9 @@ def test_backward_validation(lib):
     P = [FAKE + i * 0x100000 for i in range(8)]  # q k v y dy dq dk dv
 
     def call(shape=s, phi=ELU, ptrs=P, S_in=None, z_in=None, dS_out=None, dz_out=None, dS_in=None,
-             dz_in=None, ws=None, ws_bytes=0):
+             dz_in=None, dlam=None, ws=None, ws_bytes=0):
         return lib.la_backward_causal(*ptrs, ctypes.byref(shape), ctypes.byref(phi), None, 1e-6, None, S_in, z_in,
-                                      dS_out, dz_out, dS_in, dz_in, ws, ws_bytes, None)
+                                      dS_out, dz_out, dS_in, dz_in, dlam, ws, ws_bytes, None)
 
     assert call(phi=LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35)) == U          # random features
     assert call(shape=_shape(ot=la.LA_F32)) == U                             # y in another type
@@ -196,6 +196,8 @@ def test_backward_validation(lib):
     assert call(ptrs=P[:5] + [P[0]] + P[6:]) == E                           # dq aliases q
     assert call(ptrs=P[:6] + [P[5]] + P[7:]) == E                           # dk overlaps dq
     assert call() == la.binding.LA_ERR_WORKSPACE                            # no workspace
+    big = _shape(it=la.LA_F32, dk=128, dv=128)
+    assert call(shape=big, dlam=FAKE) == U                                   # no lambda gradient for fp32 d=128
     n = lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(ELU))
     assert n >= 2 * 4 * s.B * s.H * s.N                                      # 8 bytes per token at least
     assert lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35))) == 0

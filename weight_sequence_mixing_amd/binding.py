@@ -33,7 +33,7 @@ EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_f
            "la_decode_step", "la_status_string", "la_last_error", "la_profile_begin", "la_profile_end",
            "la_kernel_name")
 KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6,
-              "bwd_q": 7, "bwd_rlocal": 8, "bwd_kv": 9}
+              "bwd_q": 7, "bwd_rlocal": 8, "bwd_kv": 9, "bwd_dlam": 10}
 
 
 class LaPhiC(ctypes.Structure):
@@ -96,7 +96,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.la_workspace_size_backward.argtypes = [SP, PP]
     lib.la_workspace_size_backward.restype = sz
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, sz, vp]
+                                       vp, vp, vp, sz, vp]
     lib.la_backward_causal.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp]
     lib.la_decode_step.restype = ctypes.c_int
@@ -379,8 +379,9 @@ def la_workspace_size_backward(B, H, N, d_k, d_v, in_dtype=LA_BF16, phi: Optiona
 
 def la_backward_causal(q, k, v, y, dy, dq, dk, dv, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6,
                        key_padding_mask=None, S_in=None, z_in=None, dS_out=None, dz_out=None, dS_in=None,
-                       dz_in=None, workspace=None, stream=None):
-    """Gradients of la_forward_causal: writes dq, dk, dv (and dS_in, dz_in when given)."""
+                       dz_in=None, dlambda=None, workspace=None, stream=None):
+    """Gradients of la_forward_causal: writes dq, dk, dv (and dS_in, dz_in,
+    dlambda [H] fp32 when given)."""
     load_library()
     phi = phi or Phi()
     shape = _shape(q, v, y)
@@ -391,7 +392,8 @@ def la_backward_causal(q, k, v, y, dy, dq, dk, dv, phi: Optional[Phi] = None, la
     _check(_lib.la_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
                                    ctypes.byref(shape), ctypes.byref(pc), lam_ptr, float(eps),
                                    _mask_ptr(key_padding_mask), _ptr(S_in), _ptr(z_in), _ptr(dS_out),
-                                   _ptr(dz_out), _ptr(dS_in), _ptr(dz_in), _ptr(ws), ws_bytes, _stream(stream)))
+                                   _ptr(dz_out), _ptr(dS_in), _ptr(dz_in), _ptr(dlambda), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
     del lam_keep
     return dq, dk, dv
 

@@ -399,6 +399,7 @@ const char* la_kernel_name(int32_t id)
     case LA_KERNEL_BWD_Q: return "la_bwd_q_kernel";
     case LA_KERNEL_BWD_RLOCAL: return "la_bwd_kv_kernel (adjoint segment)";
     case LA_KERNEL_BWD_KV: return "la_bwd_kv_kernel (dk dv)";
+    case LA_KERNEL_BWD_DLAM: return "la_dlam_rows_kernel";
     }
     return "unknown";
 }
@@ -856,8 +857,10 @@ struct BwdPlan {
     int P;
     int64_t cps;
     int64_t SZ;
-    size_t tok_floats, seg_floats, bytes;
+    size_t tok_floats, seg_floats, dlam_floats, bytes;
 };
+
+size_t round256(size_t floats) { return ((floats * sizeof(float) + 255) & ~size_t(255)) / sizeof(float); }
 
 BwdPlan bwd_plan(const la_shape* s, int F, int C)
 {
@@ -870,8 +873,9 @@ BwdPlan bwd_plan(const la_shape* s, int F, int C)
     p.SZ = (int64_t)F * s->d_v + F;
     p.tok_floats = (size_t)BH * s->N * 2;
     p.seg_floats = p.P > 1 ? (size_t)p.P * BH * p.SZ : 0;
-    const size_t tok_bytes = (p.tok_floats * sizeof(float) + 255) & ~size_t(255);
-    p.bytes = s->N > 0 ? tok_bytes + ((p.seg_floats * sizeof(float) + 255) & ~size_t(255)) : 0;
+    // lambda gradient: the segments' dT, their partials, one sum per row
+    p.dlam_floats = round256((size_t)p.P * BH * p.SZ) + round256((size_t)p.P * BH) + round256((size_t)BH);
+    p.bytes = s->N > 0 ? (round256(p.tok_floats) + round256(p.seg_floats) + p.dlam_floats) * sizeof(float) : 0;
     return p;
 }
 
@@ -893,7 +897,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
                              void* dq, void* dk, void* dv, const la_shape* shape, const la_phi* phi,
                              const float* lambda_h, float eps, const uint8_t* key_padding_mask,
                              const float* S_in, const float* z_in, const float* dS_out, const float* dz_out,
-                             float* dS_in, float* dz_in, void* workspace, size_t workspace_bytes,
+                             float* dS_in, float* dz_in, float* dlambda, void* workspace, size_t workspace_bytes,
                              la_stream_t stream)
 {
     int F = 0;
@@ -909,6 +913,9 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     const float* st_ptrs[] = {S_in, z_in, dS_out, dz_out, dS_in, dz_in};
     for (const float* p : st_ptrs)
         if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
+    if (dlambda && !bent->dlam)
+        return fail(LA_ERR_UNSUPPORTED, "the lambda gradient is not available for this type and head size");
+    if (dlambda && ((uintptr_t)dlambda % 4)) return fail(LA_ERR_INVALID_ARGUMENT, "dlambda must be 4-byte aligned");
     if ((st = check_eps(eps)) != LA_OK) return st;
     LamTable lam;
     if ((st = make_lam(lambda_h, shape->H, &lam)) != LA_OK) return st;
@@ -918,9 +925,11 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     const int64_t nS = BH * F * (int64_t)shape->d_v, nz = BH * F;
 
     if (shape->N == 0) {
-        // no tokens: the initial state's gradient is the final state's
+        // no tokens: the initial state's gradient is the final state's, and
+        // nothing depends on lambda
         hipError_t e = hipSuccess;
-        if (dS_in) {
+        if (dlambda) e = launch(LA_KERNEL_FILL, [&] { return launch_fill_zero(dlambda, shape->H, strm); });
+        if (dS_in && e == hipSuccess) {
             if (dS_out) {
                 e = launch(LA_KERNEL_COPY, [&] { return launch_copy(dS_in, dS_out, nS, strm); });
                 if (e == hipSuccess) e = launch(LA_KERNEL_COPY, [&] { return launch_copy(dz_in, dz_out, nz, strm); });
@@ -956,7 +965,25 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.bytes, workspace_bytes);
     if (!aligned16(workspace)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     float* tok = static_cast<float*>(workspace);
-    float* segs = tok + (((plan.tok_floats * sizeof(float) + 255) & ~size_t(255)) / sizeof(float));
+    float* segs = tok + round256(plan.tok_floats);
+    float* tseg = segs + round256(plan.seg_floats);
+    float* dlp = tseg + round256((size_t)plan.P * BH * plan.SZ);
+    float* drows = dlp + round256((size_t)plan.P * BH);
+    DlamArgs da;
+    std::memset(&da, 0, sizeof(da));
+    da.tseg = tseg;
+    da.dlp = dlp;
+    da.dS_out = dS_out;
+    da.dz_out = dz_out;
+    da.rows = drows;
+    da.dlam = dlambda;
+    da.P = plan.P;
+    da.BH = (int32_t)BH;
+    da.H = (int32_t)shape->H;
+    da.F = F;
+    da.DV = shape->d_v;
+    da.n_len = shape->N;
+    da.seg_len = plan.cps * bent->C;
 
     BwdArgs b;
     std::memset(&b, 0, sizeof(b));
@@ -977,6 +1004,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     b.eps = eps;
     b.kpm = key_padding_mask;
     b.lam = lam;
+    da.lam = lam;
     const int64_t FD = (int64_t)F * shape->d_v;
     hipError_t e;
     if (plan.P > 1) {
@@ -1021,6 +1049,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         BwdArgs bq = b;
         bq.S_src = segs; bq.z_src = segs + FD;
         bq.src_stride = plan.SZ; bq.src_zstride = plan.SZ; bq.src_seg_stride = BH * plan.SZ;
+        if (dlambda) { bq.tseg = tseg; bq.dlp = dlp; }
         if ((e = launch(LA_KERNEL_BWD_Q, [&] { return bent->bwd(bq, BMODE_Q, strm); })) != hipSuccess)
             return hip_fail(e, "backward: dq launch");
         // adjoint at each segment's end: reverse segment sums, then the reverse scan
@@ -1029,6 +1058,12 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         br.dst_stride = plan.SZ; br.dst_zstride = plan.SZ;
         if ((e = launch(LA_KERNEL_BWD_RLOCAL, [&] { return bent->bwd(br, BMODE_RLOCAL, strm); })) != hipSuccess)
             return hip_fail(e, "backward: adjoint segment launch");
+        if (dlambda) {
+            // before the reverse scan turns the adjoint segment sums into carries
+            da.wloc = segs;
+            if ((e = launch(LA_KERNEL_BWD_DLAM, [&] { return launch_dlam(da, strm); })) != hipSuccess)
+                return hip_fail(e, "backward: lambda gradient launch");
+        }
         ScanArgs ra = sa;
         ra.reverse = 1;
         ra.S_init = dS_out; ra.z_init = dz_out;
@@ -1043,8 +1078,11 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     } else {
         BwdArgs bq = b;
         bq.S_src = S_in; bq.z_src = z_in; bq.src_stride = FD; bq.src_zstride = F;
+        if (dlambda) { bq.tseg = tseg; bq.dlp = dlp; }
         if ((e = launch(LA_KERNEL_BWD_Q, [&] { return bent->bwd(bq, BMODE_Q, strm); })) != hipSuccess)
             return hip_fail(e, "backward: dq launch");
+        if (dlambda && (e = launch(LA_KERNEL_BWD_DLAM, [&] { return launch_dlam(da, strm); })) != hipSuccess)
+            return hip_fail(e, "backward: lambda gradient launch");
         BwdArgs bk = b;
         bk.S_src = dS_out; bk.z_src = dz_out; bk.src_stride = FD; bk.src_zstride = F;
         bk.S_dst = dS_in; bk.z_dst = dz_in; bk.dst_stride = FD; bk.dst_zstride = F;

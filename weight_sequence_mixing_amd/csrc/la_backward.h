@@ -76,7 +76,7 @@ template <class T, int PHI> __device__ __forceinline__ float phi_deriv_from_phi(
     else return p < 1.f ? p : 1.f;
 }
 
-template <class T, int DK, int F, int DV, int C, int NW, int MODE>
+template <class T, int DK, int F, int DV, int C, int NW, int MODE, bool DL = false>
 struct BwdCfg {
     static constexpr int NT = NW * 64;
     static constexpr int VEC = 16 / (int)sizeof(T);
@@ -101,22 +101,35 @@ struct BwdCfg {
     static constexpr size_t OFF_V1 = al(OFF_V0 + size_t(TV) * sizeof(T)); // G (dq) / dnum (kv)
     static constexpr size_t OFF_V2 = al(OFF_V1 + size_t(TV) * sizeof(T)); // Y (dq only)
     static constexpr size_t OFF_S = al(OFF_V2 + (KV ? 0 : size_t(TV) * sizeof(T)));  // published state
-    static constexpr size_t OFF_R = al(OFF_S + size_t(TS) * sizeof(T));   // per-token scalars
+    static constexpr size_t OFF_T = al(OFF_S + size_t(TS) * sizeof(T));   // published dS/dlambda (DL)
+    static constexpr size_t OFF_R = al(OFF_T + (DL ? size_t(TS) * sizeof(T) : 0));  // per-token scalars
     static constexpr size_t TOTAL = al(OFF_R + size_t(C) * sizeof(float));
 
     static_assert(C == 32, "one 32-token block per chunk");
     static_assert((C * (DK / VEC)) % NT == 0 && (C * (DV / VEC)) % NT == 0, "tile rows split evenly over the threads");
     static_assert(DK == F, "elementwise feature maps");
     static_assert(DBW >= 1 && FBW >= 1 && DB % NW == 0 && FB % NW == 0, "blocks must split over the waves");
-    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(DL || TOTAL <= 160 * 1024, "LDS budget");
 };
+
+// Whether the lambda-gradient variant of the dq sweep fits in LDS.
+template <class T, int DK, int F, int DV>
+constexpr bool bwd_dlam_fits() { return BwdCfg<T, DK, F, DV, 32, 4, BMODE_Q, true>::TOTAL <= 160 * 1024; }
 
 // ---------------------------------------------------------------------------
 // dq sweep (token order).
-template <class T, int PHI, int DK, int F, int DV, int C, int NW>
+// DL: also the lambda gradient.  T = d[S|z]/dlambda is carried beside the
+// state (zero at the segment's start, whose state is held fixed; the
+// segments are joined by the reduction kernel).  Per chunk of n tokens:
+//   dlambda += sum_i [ lambda^(i+1) phi(q_i).(T dnum_i + t dden_i)
+//                    + (i+1) lambda^i phi(q_i).(S dnum_i + z dden_i) ]
+//            + sum_{j<=i} (i-j) lambda^(i-j-1) A_ij B_ij
+//   T <- lambda^n T + n lambda^(n-1) S + sum_j (n-1-j) lambda^(n-2-j) phi(k_j) [v_j, 1]^T
+// (the product rule on the chunk's recurrence, with S, T before the chunk).
+template <class T, int PHI, int DK, int F, int DV, int C, int NW, bool DL>
 __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 {
-    using Cfg = BwdCfg<T, DK, F, DV, C, NW, BMODE_Q>;
+    using Cfg = BwdCfg<T, DK, F, DV, C, NW, BMODE_Q, DL>;
     using TF = TileL<T, F>;
     using TVL = TileL<T, DV>;
     constexpr int NT = Cfg::NT, VEC = Cfg::VEC, QB = Cfg::QB, CB = Cfg::CB, FB = Cfg::FB;
@@ -132,6 +145,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
     T* const sG = (T*)(smem + Cfg::OFF_V1);
     T* const sY = (T*)(smem + Cfg::OFF_V2);
     T* const sS = (T*)(smem + Cfg::OFF_S);
+    T* const sT = (T*)(smem + Cfg::OFF_T);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
@@ -180,6 +194,16 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
             for (int r = 0; r < 4; ++r) accZ[fb][r] = zb[16 * fb + 4 * g + r];
         }
     }
+    // dS/dlambda and dz/dlambda (DL), from zero at the segment's start
+    constexpr int TF1 = DL ? FB : 1, TD1 = DL ? DBW : 1;
+    f32x4 accT[TF1][TD1], accTz[TF1];
+#pragma unroll
+    for (int fb = 0; fb < TF1; ++fb) {
+        accTz[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < TD1; ++t) accT[fb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float dl = 0.f;  // this lane's share of the segment's lambda gradient
     // publish S (element type, row-major [F][DV]) for reads that contract over d
     auto publish = [&]() LA_BINLINE {
 #pragma unroll
@@ -191,6 +215,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                 for (int r = 0; r < 4; ++r) {
                     const int f = 16 * fb + 4 * g + r;
                     sS[TVL::off(f, d & ~3) + (d & 3)] = from_f32<T>(accS[fb][t][r]);
+                    if constexpr (DL) sT[TVL::off(f, d & ~3) + (d & 3)] = from_f32<T>(accT[fb][t][r]);
                 }
             }
     };
@@ -275,13 +300,14 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) mma(dz, zf[kb], qf[kb]);
             // A^T tiles (rows j, column i) for the normaliser
-            f32x4 pt[2 * CB];
+            f32x4 pt[2 * CB], praw[DL ? 2 * CB : 1];
 #pragma unroll
             for (int jb = 0; jb < 2 * CB; ++jb) {
                 pt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (jb <= ib) {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                    if constexpr (DL) praw[jb] = pt[jb];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) pt[jb][r] *= (jb == ib) ? m0[r] : m1[r] * lam_pow(l2l, 16 * (ib - jb - 1));
                 }
@@ -324,8 +350,15 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 #pragma unroll
                     for (int kb = 0; kb < VB; ++kb) mma(bt[jb], lds_frag_row<T, DV>(sV, 16 * jb + l16, kb, g), dn[kb]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        bt[jb][r] = (bt[jb][r] + dden) * ((jb == ib) ? m0[r] : m1[r] * lam_pow(l2l, 16 * (ib - jb - 1)));
+                    for (int r = 0; r < 4; ++r) {
+                        const float braw = bt[jb][r] + dden;
+                        if constexpr (DL) {
+                            // pairs inside the chunk: (i-j) lambda^(i-j-1) A_ij B_ij (one wave)
+                            const int e = 16 * (ib - jb) + l16 - 4 * g - r;
+                            if (wave == 0 && e >= 1) dl += (float)e * lam_pow(l2l, e - 1) * praw[jb][r] * braw;
+                        }
+                        bt[jb][r] = braw * ((jb == ib) ? m0[r] : m1[r] * lam_pow(l2l, 16 * (ib - jb - 1)));
+                    }
                 }
             }
             Frag<T> bf[CB];
@@ -340,6 +373,21 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                 for (int kb = 0; kb < VB; ++kb) mma(inter, lds_frag_row<T, DV>(sS, 16 * fb + l16, kb, g), dn[kb]);
 #pragma unroll
                 for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, F>::get(sK, 32 * kb, 16 * fb, lane), bf[kb]);
+                if constexpr (DL) {
+                    // phi(q_i).(S dnum_i + z dden_i) and phi(q_i).(T dnum_i + t dden_i) over
+                    // this wave's feature rows (phi(q) = 0 past the chunk's end)
+                    f32x4 tint = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < VB; ++kb) mma(tint, lds_frag_row<T, DV>(sT, 16 * fb + l16, kb, g), dn[kb]);
+                    float rs_ = 0.f, rt_ = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + r]);
+                        rs_ += p * (inter[r] + accZ[fb][r] * dden);
+                        rt_ += p * (tint[r] + accTz[fb][r] * dden);
+                    }
+                    dl += (float)(i + 1) * lam_pow(l2l, i) * rs_ + lqi * rt_;
+                }
                 if (i < n) {
                     const f32x4 ph = {to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 0]), to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 1]),
                                       to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 2]), to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 3])};
@@ -359,6 +407,38 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
             }
         }
 
+        // ---- dS/dlambda carry (before S changes): T <- lambda^n T + n lambda^(n-1) S
+        // + phi(K)^T (w' V), w'_j = (n-1-j) lambda^(n-2-j)
+        if constexpr (DL) {
+            const float ln_ = lam_pow(l2l, n), dn1 = (float)n * lam_pow(l2l, n - 1);
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) {
+                f32x4 wlo, whi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j0 = 32 * kb + 4 * g + e, j1 = j0 + 16;
+                    wlo[e] = j0 < n - 1 ? (float)(n - 1 - j0) * lam_pow(l2l, n - 2 - j0) : 0.f;
+                    whi[e] = j1 < n - 1 ? (float)(n - 1 - j1) * lam_pow(l2l, n - 2 - j1) : 0.f;
+                }
+                const Frag<T> dwf = frag_acc<T>(wlo, whi);
+                Frag<T> dwv[DBW];
+#pragma unroll
+                for (int t = 0; t < DBW; ++t)
+                    dwv[t] = frag_scale<T>(ColRead<T, DV>::get(sV, 32 * kb, 16 * (wave * DBW + t), lane), wlo, whi);
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb) {
+                    if (kb == 0) {
+                        accTz[fb] = accTz[fb] * ln_ + accZ[fb] * dn1;
+#pragma unroll
+                        for (int t = 0; t < DBW; ++t) accT[fb][t] = accT[fb][t] * ln_ + accS[fb][t] * dn1;
+                    }
+                    const Frag<T> kf = ColRead<T, F>::get(sK, 32 * kb, 16 * fb, lane);
+#pragma unroll
+                    for (int t = 0; t < DBW; ++t) mma(accT[fb][t], kf, dwv[t]);
+                    mma(accTz[fb], kf, dwf);
+                }
+            }
+        }
         // ---- state carry: S <- lambda^n S + phi(K)^T (w V), z <- lambda^n z + phi(K)^T w,
         // w_j = lambda^(n-1-j), applied to the V fragments in registers
         const float ln = lam_pow(l2l, n);
@@ -391,6 +471,33 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
             }
         }
         __syncthreads();  // every wave has read sS before it is republished
+    }
+
+    if constexpr (DL) {
+        // the segment's dT (start state held fixed) and its partial dlambda
+        const int64_t slot = (int64_t)seg * a.BH + bh;
+        constexpr int SZ = F * DV + F;
+        float* Td = a.tseg + slot * SZ;
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+            for (int t = 0; t < DBW; ++t) {
+                const int d = 16 * (wave * DBW + t) + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Td[(16 * fb + 4 * g + r) * DV + d] = accT[fb][t][r];
+            }
+            if (wave == 0 && l16 == 0) *(f32x4*)(Td + F * DV + 16 * fb + 4 * g) = accTz[fb];
+        }
+        dl = wave_sum_xor(dl, 1, 32);
+        float* red = (float*)(smem + Cfg::OFF_R);
+        if (lane == 0) red[wave] = dl;
+        __syncthreads();
+        if (tid == 0) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sum += red[w];
+            a.dlp[slot] = sum;
+        }
     }
 }
 
@@ -677,7 +784,13 @@ hipError_t bwd_launch(const BwdArgs& a, int mode, hipStream_t stream)
     const dim3 grid((unsigned)a.P, (unsigned)a.BH), block(NW * 64);
     switch (mode) {
     case BMODE_Q:
-        return launch_kernel(la_bwd_q_kernel<T, PHI, DK, F, DV, C, NW>, grid, block, stream, a);
+        if (a.tseg) {
+            if constexpr (BwdCfg<T, DK, F, DV, C, NW, BMODE_Q, true>::TOTAL <= 160 * 1024)
+                return launch_kernel(la_bwd_q_kernel<T, PHI, DK, F, DV, C, NW, true>, grid, block, stream, a);
+            else
+                return hipErrorInvalidConfiguration;
+        }
+        return launch_kernel(la_bwd_q_kernel<T, PHI, DK, F, DV, C, NW, false>, grid, block, stream, a);
     case BMODE_RLOCAL:
         return launch_kernel(la_bwd_kv_kernel<T, PHI, DK, F, DV, C, NW, BMODE_RLOCAL>, grid, block, stream, a);
     default:

@@ -2,7 +2,7 @@
 #include "la_backward.h"
 
 namespace la {
-#define LA_BWD_ENTRY(PHI, DK, DV) {LA_BF16, PHI, DK, DK, DV, 32, &bwd_launch<bf16, PHI, DK, DK, DV>}
+#define LA_BWD_ENTRY(PHI, DK, DV) {LA_BF16, PHI, DK, DK, DV, 32, &bwd_launch<bf16, PHI, DK, DK, DV>, bwd_dlam_fits<bf16, DK, DK, DV>()}
 
 BwdEntry kBwdEntriesBf16[] = {
     LA_BWD_ENTRY(LA_PHI_ELU1, 64, 64),

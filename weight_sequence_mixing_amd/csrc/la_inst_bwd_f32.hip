@@ -2,7 +2,7 @@
 #include "la_backward.h"
 
 namespace la {
-#define LA_BWD_ENTRY(PHI, DK, DV) {LA_F32, PHI, DK, DK, DV, 32, &bwd_launch<float, PHI, DK, DK, DV>}
+#define LA_BWD_ENTRY(PHI, DK, DV) {LA_F32, PHI, DK, DK, DV, 32, &bwd_launch<float, PHI, DK, DK, DV>, bwd_dlam_fits<float, DK, DK, DV>()}
 
 BwdEntry kBwdEntriesF32[] = {
     LA_BWD_ENTRY(LA_PHI_ELU1, 64, 64),

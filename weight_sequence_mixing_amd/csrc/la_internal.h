@@ -124,8 +124,31 @@ struct BwdArgs {
     float* S_dst;
     float* z_dst;
     int64_t dst_stride, dst_zstride;
+    // gradient of lambda (dq pass, optional): each workgroup writes its
+    // segment's dT = d[S|z]/dlambda with the segment's start state held fixed
+    // at tseg + (seg*BH + bh)*SZ, and its partial dlambda at dlp[seg*BH + bh]
+    float* tseg;
+    float* dlp;
     LamTable lam;
 };
+
+// Reduction of the lambda gradient: per (batch, head) row, the dq sweep's
+// partials, plus <T_in(s), W_loc(s)> over the segments (T_in: the scan of the
+// segments' dT; W_loc: the adjoint segment sums, or null with one segment),
+// plus <[dS_out|dz_out], T_final>; then the sum over the batch per head.
+struct DlamArgs {
+    const float* wloc;    // [P][BH][SZ] or null
+    const float* tseg;    // [P][BH][SZ]
+    const float* dlp;     // [P][BH]
+    const float* dS_out;  // [BH][F][DV] or null
+    const float* dz_out;  // [BH][F]
+    float* rows;          // [BH] scratch
+    float* dlam;          // [H] output
+    int32_t P, BH, H, F, DV;
+    int64_t n_len, seg_len;
+    LamTable lam;
+};
+hipError_t launch_dlam(const DlamArgs& a, hipStream_t stream);
 
 enum BwdMode : int {
     BMODE_Q = 0,       // dq, and 1/den, dden per token
@@ -153,7 +176,7 @@ struct DecArgs {
 
 typedef hipError_t (*fwd_launch_fn)(const FwdArgs&, int mode, hipStream_t);
 typedef hipError_t (*dec_launch_fn)(const DecArgs&, hipStream_t);
-typedef hipError_t (*bwd_launch_fn)(const BwdArgs&, int mode, hipStream_t);
+typedef hipError_t (*bwd_launch_fn)(const BwdArgs&, int mode, hipStream_t);  // BMODE_Q with a.tseg: the dlambda variant
 
 struct KernelEntry {
     int in_dtype;   // LA_F32 / LA_BF16
@@ -168,6 +191,7 @@ struct BwdEntry {
     int in_dtype, phi, dk, F, dv;
     int C;
     bwd_launch_fn bwd;
+    bool dlam;  // the lambda-gradient variant of the dq sweep fits in LDS
 };
 extern BwdEntry kBwdEntriesBf16[];
 extern int kNumBwdEntriesBf16;

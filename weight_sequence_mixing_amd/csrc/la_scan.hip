@@ -83,6 +83,59 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
     }
 }
 
+// Lambda gradient, per (batch, head) row (one workgroup each): the dq
+// sweep's partials, plus sum_s <T_in(s), W_loc(s)> with T_in(0) = 0 and
+// T_in(s+1) = lambda^(L_s) T_in(s) + dT(s) (the segments' own dT, their start
+// state held fixed), plus <[dS_out | dz_out], T_in(P)> -- the terms through
+// which each segment's start state and the final state depend on lambda.
+constexpr int kDlamThreads = 256;
+
+__global__ void __launch_bounds__(kDlamThreads) la_dlam_rows_kernel(const DlamArgs a)
+{
+    const int bh = blockIdx.x;
+    const int FD = a.F * a.DV, SZ = FD + a.F;
+    const float l2l = a.lam.log2lam[bh % a.H];
+    float part = 0.f;
+    for (int e = threadIdx.x; e < SZ; e += kDlamThreads) {
+        float t = 0.f;
+        for (int s = 0; s < a.P; ++s) {
+            const int64_t slot = (int64_t)s * a.BH + bh;
+            if (a.wloc && s > 0) part += t * a.wloc[slot * SZ + e];
+            const int64_t L = (s == a.P - 1 ? a.n_len : min((int64_t)(s + 1) * a.seg_len, a.n_len)) -
+                              (int64_t)s * a.seg_len;
+            t = lam_pow(l2l, (int)L) * t + a.tseg[slot * SZ + e];
+        }
+        if (a.dS_out) part += t * (e < FD ? a.dS_out[(int64_t)bh * FD + e] : a.dz_out[(int64_t)bh * a.F + (e - FD)]);
+    }
+    __shared__ float red[kDlamThreads / 64];
+    part = wave_sum_xor(part, 1, 32);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float sum = 0.f;
+        for (int w = 0; w < kDlamThreads / 64; ++w) sum += red[w];
+        for (int s = 0; s < a.P; ++s) sum += a.dlp[(int64_t)s * a.BH + bh];
+        a.rows[bh] = sum;
+    }
+}
+
+// dlambda[h] = sum over the batch of the rows' gradients
+__global__ void __launch_bounds__(256) la_dlam_heads_kernel(const DlamArgs a)
+{
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= a.H) return;
+    float sum = 0.f;
+    for (int b = 0; b < a.BH / a.H; ++b) sum += a.rows[b * a.H + h];
+    a.dlam[h] = sum;
+}
+
+hipError_t launch_dlam(const DlamArgs& a, hipStream_t stream)
+{
+    hipError_t e = launch_kernel(la_dlam_rows_kernel, dim3(a.BH), dim3(kDlamThreads), stream, a);
+    if (e != hipSuccess) return e;
+    return launch_kernel(la_dlam_heads_kernel, dim3((a.H + 255) / 256), dim3(256), stream, a);
+}
+
 __global__ void __launch_bounds__(256) la_fill_zero_kernel(float* p, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
