@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["la_forward.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h"]
+KERNEL_SOURCES = ["la_forward.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h", "la_backward.h"]
 
 
 def log(*a):
@@ -544,12 +544,23 @@ def state_copy(ctx, B=256, H=32, F=128, D=128, steps=50):
 # rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) runs of `bench.py --only TAG`
 # write <dir>/<counter>_<tag>/**/*_counter_collection.csv.  The counters are
 # scaled by what they read for the library's state copy, whose bytes are known.
-COUNTER_TAGS = {"copy": None, "w2": 2, "w3": 3, "w4": 4, "w5": 5}
+COUNTER_TAGS = {"copy": None, "w2": 2, "w3": 3, "w4": 4, "w5": 5,
+                "backward_w2": "elu1_backward_B4_H8_N4096_d64_bf16"}
 
 
 def _kernel_label(mangled):
     if "la_copy_kernel" in mangled:
         return "la_copy_kernel"
+    if "la_bwd_q_kernel" in mangled:
+        return "la_bwd_q_kernel"
+    if "la_bwd_kv_kernel" in mangled:
+        # the mode is the last int template argument
+        if "EEEvNS_7BwdArgsE" in mangled:
+            mode = mangled.split("EEEvNS_7BwdArgsE")[0].rsplit("ELi", 1)[-1]
+        else:
+            ints = [x.strip() for x in mangled.split(">(")[0].split(",") if x.strip().lstrip("-").isdigit()]
+            mode = ints[-1] if ints else ""
+        return {"1": "la_bwd_kv_kernel (adjoint segment)", "2": "la_bwd_kv_kernel (dk dv)"}.get(mode, "la_bwd_kv_kernel")
     if "la_decode_kernel" in mangled:
         return "la_decode_kernel"
     if "la_scan_kernel" in mangled:
@@ -600,7 +611,7 @@ def traffic_from(root):
     for tag, idx in COUNTER_TAGS.items():
         if idx is None:
             continue
-        name = si.workload(idx).name
+        name = idx if isinstance(idx, str) else si.workload(idx).name
         for label in sorted(set(fetch[tag]) & set(write[tag])):
             fr = float(np.mean(fetch[tag][label]))
             wr = float(np.mean(write[tag][label]))

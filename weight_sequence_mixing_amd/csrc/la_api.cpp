@@ -874,7 +874,8 @@ BwdPlan bwd_plan(const la_shape* s, int F, int C)
     p.tok_floats = (size_t)BH * s->N * 2;
     p.seg_floats = p.P > 1 ? (size_t)p.P * BH * p.SZ : 0;
     // lambda gradient: the segments' dT, their partials, one sum per row
-    p.dlam_floats = round256((size_t)p.P * BH * p.SZ) + round256((size_t)p.P * BH) + round256((size_t)BH);
+    p.dlam_floats = round256((size_t)p.P * BH * p.SZ) + round256((size_t)p.P * BH) +
+                    round256((size_t)BH * dlam_blocks(F, s->d_v));
     p.bytes = s->N > 0 ? (round256(p.tok_floats) + round256(p.seg_floats) + p.dlam_floats) * sizeof(float) : 0;
     return p;
 }

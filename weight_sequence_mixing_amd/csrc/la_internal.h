@@ -142,13 +142,14 @@ struct DlamArgs {
     const float* dlp;     // [P][BH]
     const float* dS_out;  // [BH][F][DV] or null
     const float* dz_out;  // [BH][F]
-    float* rows;          // [BH] scratch
+    float* rows;          // [BH][dlam_blocks(F, DV)] partial sums
     float* dlam;          // [H] output
     int32_t P, BH, H, F, DV;
     int64_t n_len, seg_len;
     LamTable lam;
 };
 hipError_t launch_dlam(const DlamArgs& a, hipStream_t stream);
+int dlam_blocks(int F, int DV);  // workgroups per row of the reduction
 
 enum BwdMode : int {
     BMODE_Q = 0,       // dq, and 1/den, dden per token

@@ -83,57 +83,88 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
     }
 }
 
-// Lambda gradient, per (batch, head) row (one workgroup each): the dq
-// sweep's partials, plus sum_s <T_in(s), W_loc(s)> with T_in(0) = 0 and
-// T_in(s+1) = lambda^(L_s) T_in(s) + dT(s) (the segments' own dT, their start
-// state held fixed), plus <[dS_out | dz_out], T_in(P)> -- the terms through
-// which each segment's start state and the final state depend on lambda.
-constexpr int kDlamThreads = 256;
-
-__global__ void __launch_bounds__(kDlamThreads) la_dlam_rows_kernel(const DlamArgs a)
+// Lambda gradient, per (batch, head) row: the dq sweep's partials, plus
+// sum_s <T_in(s), W_loc(s)> with T_in(0) = 0 and T_in(s+1) = lambda^(L_s)
+// T_in(s) + dT(s) (the segments' own dT, their start state held fixed), plus
+// <[dS_out | dz_out], T_in(P)> -- the terms through which each segment's start
+// state and the final state depend on lambda.  Like the scan, each thread owns
+// four elements of a row's [F x (d_v + 1)] state and walks the segments with
+// kScanBatch loads in flight; each workgroup writes one partial sum
+// (deterministic: no atomics), and the per-head kernel adds them up.
+__global__ void __launch_bounds__(kScanThreads) la_dlam_rows_kernel(const DlamArgs a)
 {
-    const int bh = blockIdx.x;
     const int FD = a.F * a.DV, SZ = FD + a.F;
+    const int e = 4 * (blockIdx.x * kScanThreads + threadIdx.x);
+    const int bh = blockIdx.y;
     const float l2l = a.lam.log2lam[bh % a.H];
-    float part = 0.f;
-    for (int e = threadIdx.x; e < SZ; e += kDlamThreads) {
-        float t = 0.f;
-        for (int s = 0; s < a.P; ++s) {
-            const int64_t slot = (int64_t)s * a.BH + bh;
-            if (a.wloc && s > 0) part += t * a.wloc[slot * SZ + e];
-            const int64_t L = (s == a.P - 1 ? a.n_len : min((int64_t)(s + 1) * a.seg_len, a.n_len)) -
-                              (int64_t)s * a.seg_len;
-            t = lam_pow(l2l, (int)L) * t + a.tseg[slot * SZ + e];
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = zero;
+    if (e < SZ) {
+        f32x4 t = zero;
+        f32x4 w[kScanBatch], d[kScanBatch];
+        for (int s0 = 0; s0 < a.P; s0 += kScanBatch) {
+#pragma unroll
+            for (int b = 0; b < kScanBatch; ++b) {
+                const int64_t slot = (int64_t)(s0 + b) * a.BH + bh;
+                const bool in = s0 + b < a.P;
+                d[b] = in ? *(const f32x4*)(a.tseg + slot * SZ + e) : zero;
+                w[b] = (in && a.wloc) ? *(const f32x4*)(a.wloc + slot * SZ + e) : zero;
+            }
+#pragma unroll
+            for (int b = 0; b < kScanBatch; ++b) {
+                const int s = s0 + b;
+                if (s < a.P) {
+                    acc += t * w[b];  // T_in(0) = 0, so segment 0 adds nothing
+                    const int64_t L = (s == a.P - 1 ? a.n_len : min((int64_t)(s + 1) * a.seg_len, a.n_len)) -
+                                      (int64_t)s * a.seg_len;
+                    t = lam_pow(l2l, (int)L) * t + d[b];
+                }
+            }
         }
-        if (a.dS_out) part += t * (e < FD ? a.dS_out[(int64_t)bh * FD + e] : a.dz_out[(int64_t)bh * a.F + (e - FD)]);
+        if (a.dS_out) {
+            const bool isz = e >= FD;
+            const f32x4 g = isz ? *(const f32x4*)(a.dz_out + (int64_t)bh * a.F + (e - FD))
+                                : *(const f32x4*)(a.dS_out + (int64_t)bh * FD + e);
+            acc += t * g;
+        }
     }
-    __shared__ float red[kDlamThreads / 64];
+    float part = acc[0] + acc[1] + acc[2] + acc[3];
+    __shared__ float red[kScanThreads / 64];
     part = wave_sum_xor(part, 1, 32);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
     __syncthreads();
     if (threadIdx.x == 0) {
         float sum = 0.f;
-        for (int w = 0; w < kDlamThreads / 64; ++w) sum += red[w];
-        for (int s = 0; s < a.P; ++s) sum += a.dlp[(int64_t)s * a.BH + bh];
-        a.rows[bh] = sum;
+        for (int w2 = 0; w2 < kScanThreads / 64; ++w2) sum += red[w2];
+        if (blockIdx.x == 0)
+            for (int s = 0; s < a.P; ++s) sum += a.dlp[(int64_t)s * a.BH + bh];
+        a.rows[(int64_t)bh * gridDim.x + blockIdx.x] = sum;
     }
 }
 
-// dlambda[h] = sum over the batch of the rows' gradients
-__global__ void __launch_bounds__(256) la_dlam_heads_kernel(const DlamArgs a)
+// dlambda[h] = sum over the batch of the rows' partial sums
+__global__ void __launch_bounds__(256) la_dlam_heads_kernel(const DlamArgs a, int nblk)
 {
     const int h = blockIdx.x * 256 + threadIdx.x;
     if (h >= a.H) return;
     float sum = 0.f;
-    for (int b = 0; b < a.BH / a.H; ++b) sum += a.rows[b * a.H + h];
+    for (int b = 0; b < a.BH / a.H; ++b)
+        for (int k = 0; k < nblk; ++k) sum += a.rows[(int64_t)(b * a.H + h) * nblk + k];
     a.dlam[h] = sum;
+}
+
+int dlam_blocks(int F, int DV)
+{
+    const int SZ4 = (F * DV + F) / 4;
+    return (SZ4 + kScanThreads - 1) / kScanThreads;
 }
 
 hipError_t launch_dlam(const DlamArgs& a, hipStream_t stream)
 {
-    hipError_t e = launch_kernel(la_dlam_rows_kernel, dim3(a.BH), dim3(kDlamThreads), stream, a);
+    const int nblk = dlam_blocks(a.F, a.DV);
+    hipError_t e = launch_kernel(la_dlam_rows_kernel, dim3(nblk, a.BH), dim3(kScanThreads), stream, a);
     if (e != hipSuccess) return e;
-    return launch_kernel(la_dlam_heads_kernel, dim3((a.H + 255) / 256), dim3(256), stream, a);
+    return launch_kernel(la_dlam_heads_kernel, dim3((a.H + 255) / 256), dim3(256), stream, a, nblk);
 }
 
 __global__ void __launch_bounds__(256) la_fill_zero_kernel(float* p, int64_t n)
