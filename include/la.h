@@ -189,7 +189,8 @@ la_status la_forward_causal_masked(const void* q, const void* k, const void* v, 
  * [B,H,F]; same rules as la_forward_causal).  Output rows outside every
  * sequence are not written.  max_seqlen (host, 0 <= max_seqlen <= T): the
  * longest sequence; it sizes the segment split and the workspace
- * (la_workspace_size_varlen) -- results do not depend on it, only speed. */
+ * (la_workspace_size_varlen, never 0 for T > 0: it holds the table of work
+ * items) -- results do not depend on it, only speed. */
 size_t la_workspace_size_varlen(const la_shape* shape, int64_t max_seqlen, const la_phi* phi);
 la_status la_forward_causal_varlen(const void* q, const void* k, const void* v, void* y,
                                    const int32_t* cu_seqlens, int64_t max_seqlen,
@@ -283,7 +284,8 @@ enum {
     LA_KERNEL_BWD_Q = 7,       /* backward: dq sweep                           */
     LA_KERNEL_BWD_RLOCAL = 8,  /* backward: adjoint segment sums               */
     LA_KERNEL_BWD_KV = 9,      /* backward: dk, dv sweep                       */
-    LA_KERNEL_BWD_DLAM = 10    /* backward: lambda-gradient reduction          */
+    LA_KERNEL_BWD_DLAM = 10,   /* backward: lambda-gradient reduction          */
+    LA_KERNEL_VARLEN_ITEMS = 11 /* packed sequences: table of work items       */
 };
 la_status la_profile_begin(int32_t max_launches);
 la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);

@@ -174,8 +174,10 @@ def test_cross_and_varlen_workspace_queries(lib):
     sv = _shape(B=2, H=1, N=1 << 16, dk=128, dv=128)
     assert lib.la_workspace_size_varlen(ctypes.byref(sv), 1 << 15, ctypes.byref(ELU)) >= 2 * (128 * 128 + 128) * 4
     assert lib.la_workspace_size_varlen(ctypes.byref(sv), (1 << 16) + 1, ctypes.byref(ELU)) == 0
+    # many head-sequences: one segment each, so only the table of work items
+    # (one int32 per sequence) remains
     wide = _shape(B=64, H=16, N=1 << 16)
-    assert lib.la_workspace_size_varlen(ctypes.byref(wide), 1024, ctypes.byref(ELU)) == 0
+    assert 64 * 4 <= lib.la_workspace_size_varlen(ctypes.byref(wide), 1024, ctypes.byref(ELU)) <= 1024
 
 
 def test_backward_validation(lib):

@@ -254,6 +254,16 @@ void varlen_segments(int64_t T, int64_t B, int64_t H, int64_t max_len, int C, in
     *P = (int)p;
 }
 
+// Work items per head of packed sequences: sum_b max(1, min(ceil(chunks_b /
+// cps), P)) <= ceil((ceil(T / C) + B) / cps) + B, and <= B * P.
+int64_t varlen_items_bound(int64_t T, int64_t B, int C, int64_t cps, int P)
+{
+    int64_t G = ((T + C - 1) / C + B + cps - 1) / cps + B;
+    return G < B * (int64_t)P ? G : B * (int64_t)P;
+}
+
+size_t bytes256(size_t n) { return (n + 255) & ~size_t(255); }
+
 // Plan of a forward over rows of N tokens (causal: may be cut into windows).
 // varlen_P > 0: packed variable-length rows cut into varlen_P segments, one window.
 Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, int varlen_P = 0)
@@ -400,6 +410,7 @@ const char* la_kernel_name(int32_t id)
     case LA_KERNEL_BWD_RLOCAL: return "la_bwd_kv_kernel (adjoint segment)";
     case LA_KERNEL_BWD_KV: return "la_bwd_kv_kernel (dk dv)";
     case LA_KERNEL_BWD_DLAM: return "la_dlam_rows_kernel";
+    case LA_KERNEL_VARLEN_ITEMS: return "la_varlen_items_kernel";
     }
     return "unknown";
 }
@@ -481,17 +492,22 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
         return ok();
     }
     int vP = 0;
-    int64_t vcps = 1;
+    int64_t vcps = 1, vG = 0;
     if (cu) {
         // packed rows: q, k, v, y hold H rows of N tokens
         const size_t rows = (size_t)shape->H * shape->N;
         if ((st = check_io_rows(q, k, v, y, shape, rows, rows)) != LA_OK) return st;
         varlen_segments(shape->N, shape->B, shape->H, max_len, ent->C, &vP, &vcps);
+        vG = varlen_items_bound(shape->N, shape->B, ent->C, vcps, vP);
+        if (vG > 65535) return fail(LA_ERR_UNSUPPORTED, "%lld work items per head exceed 65535", (long long)vG);
     } else {
         if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
     }
-    const Plan plan = make_plan(shape, F, ent, true, vP);
+    Plan plan = make_plan(shape, F, ent, true, vP);
+    const size_t seg_bytes = plan.ws_bytes;
+    if (cu) plan.ws_bytes = seg_bytes + bytes256((size_t)vG * sizeof(int32_t));  // + the item table
     if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
+    int32_t* items = cu ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + seg_bytes) : nullptr;
 
     float* ws = static_cast<float*>(workspace);
     float* segs = ws;                                                     // [P][BH][SZ]
@@ -526,6 +542,12 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             // one segment length for every packed sequence (n0, n_len unused)
             P = vP;
             cps = vcps;
+            a.G = (int32_t)vG;
+            a.items = items;
+            hipError_t ie = launch(LA_KERNEL_VARLEN_ITEMS, [&] {
+                return launch_varlen_items(cu, (int)shape->B, shape->N, plan.C, cps, P, (int)vG, items, strm);
+            });
+            if (ie != hipSuccess) return hip_fail(ie, "packed sequence items launch");
         } else {
             cut_segments(c1 - c0, BH, &P, &cps);
         }
@@ -633,7 +655,8 @@ size_t la_workspace_size_varlen(const la_shape* shape, int64_t max_seqlen, const
     int P = 1;
     int64_t cps = 1;
     varlen_segments(shape->N, shape->B, shape->H, max_seqlen, e->C, &P, &cps);
-    return make_plan(shape, F, e, true, P).ws_bytes;
+    const int64_t G = varlen_items_bound(shape->N, shape->B, e->C, cps, P);
+    return make_plan(shape, F, e, true, P).ws_bytes + bytes256((size_t)G * sizeof(int32_t));
 }
 
 la_status la_forward_causal_varlen(const void* q, const void* k, const void* v, void* y,

@@ -162,7 +162,17 @@ la_fwd_kernel(const FwdArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
-    const int seg = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
+    // fixed rows: blockIdx = (segment, batch*head); packed sequences:
+    // blockIdx = (work item of head blockIdx.y), mapped to (sequence, segment)
+    int seg = blockIdx.x, bh = blockIdx.y;
+    bool spare = false;  // a packed-sequence item past the last: no work, no stores
+    if (a.cu_seqlens) {
+        const int it = a.items[blockIdx.x];  // b * P + s, or -1
+        spare = it < 0;
+        seg = spare ? 0 : it % a.P;
+        bh = (spare ? 0 : it / a.P) * a.H + (int)blockIdx.y;
+    }
+    const int h = bh % a.H;
     const float l2l = (MODE == MODE_QUERY) ? 0.f : a.lam.log2lam[h];
     const bool decay = l2l != 0.f;  // uniform over the workgroup
     // token range of this row: [n0, n0 + n_len) of row bh, or the packed
@@ -175,13 +185,13 @@ la_fwd_kernel(const FwdArgs a)
         n_len = s1 - s0;
     }
     // segments of cps chunks; the last one takes whatever remains
-    const int64_t NC = (n_len + C - 1) / C;
+    const int64_t NC = spare ? 0 : (n_len + C - 1) / C;
     const int64_t c_beg = (int64_t)seg * a.cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + a.cps);
-    // an empty segment (past the end of a short packed sequence) has nothing
-    // to compute and nothing to store, unless it carries a state through
+    // an empty segment (an empty packed sequence) has nothing to compute and
+    // nothing to store, unless it carries a state through
     if (c_beg >= c_end) {
         if constexpr (MODE != MODE_CAUSAL) return;
-        else if (!a.S_dst) return;
+        else if (!a.S_dst || spare) return;
     }
     const T* qg = (const T*)a.q + row0 * DK;
     const T* kg = (const T*)a.k + row0 * DK;
@@ -716,7 +726,8 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
 {
     constexpr int C = chunk_len<T, PHI>(F);
     constexpr int NW = 4;
-    const dim3 grid((unsigned)a.P, (unsigned)a.BH), block(NW * 64);
+    const dim3 grid(a.cu_seqlens ? (unsigned)a.G : (unsigned)a.P, a.cu_seqlens ? (unsigned)a.H : (unsigned)a.BH),
+        block(NW * 64);
     // fp32 inputs always write fp32 outputs, so only bf16 needs both variants
     const bool o32 = sizeof(T) == 2 && a.out_f32;
     switch (mode) {

@@ -48,12 +48,16 @@ struct FwdArgs {
     // of batch b from every sum; null = no mask
     const uint8_t* kpm;
     int64_t kpm_stride;
-    // packed variable-length rows: sequence b = bh / H holds tokens
-    // [cu_seqlens[b], cu_seqlens[b+1]) of head row h = bh % H (N tokens per
-    // head row; offsets are clamped to [0, N]).  Every sequence is cut into
-    // segments of cps chunks, the last grid segment taking the remainder; the
-    // segments past a short sequence's end are empty.  null = fixed rows.
+    // packed variable-length rows: sequence b holds tokens
+    // [cu_seqlens[b], cu_seqlens[b+1]) of each head row h (N tokens per head
+    // row; offsets are clamped to [0, N]).  Every sequence is cut into
+    // segments of cps chunks, at most P (the last takes the remainder); the
+    // grid is (G work items, H heads), item w of a head being the w-th
+    // (sequence, segment) pair in order; items past the last exit.  The
+    // kernels address states as row bh = b*H + h, segment s.  null = fixed rows.
     const int32_t* cu_seqlens;
+    const int32_t* items;  // [G]: b * P + s of each work item in order, -1 past the last
+    int32_t G;             // work items per head (an upper bound of the segments' count)
     // initial state (MODE_CAUSAL, MODE_QUERY): S at
     // S_src + seg*src_seg_stride + bh*src_stride as [F][d_v], z at
     // z_src + seg*src_seg_stride + bh*src_zstride as [F]; null S_src = zero state.
@@ -232,6 +236,11 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Ar
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+// Work items of packed sequences: items[w] = b * P + s for the w-th
+// (sequence, segment) pair in order, -1 for w past the last (G entries).
+// Sequence b has max(1, min(ceil(chunks_b / cps), P)) segments.
+hipError_t launch_varlen_items(const int32_t* cu, int B, int64_t N, int C, int64_t cps, int P, int G,
+                               int32_t* items, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 // S[BH][F][DV] = alpha * I (f == d), z[BH][F] = alpha for f < min(F, DV)
 hipError_t launch_fill_identity(float* S, float* z, int64_t BH, int F, int DV, float alpha, hipStream_t stream);

@@ -83,6 +83,53 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
     }
 }
 
+// Work items of packed sequences (one workgroup): each thread counts the
+// segments of its sequences, a workgroup-wide exclusive scan gives their
+// first item, and the items are written in order; the rest of the table is -1.
+constexpr int kItemThreads = 1024;
+
+__global__ void __launch_bounds__(kItemThreads) la_varlen_items_kernel(const int32_t* cu, int B, int64_t N, int C,
+                                                                      int64_t cps, int P, int G, int32_t* items)
+{
+    __shared__ int part[kItemThreads];
+    __shared__ int carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = 0;
+    for (int w = tid; w < G; w += kItemThreads) items[w] = -1;
+    __syncthreads();
+    for (int b0 = 0; b0 < B; b0 += kItemThreads) {
+        const int b = b0 + tid;
+        int cnt = 0;
+        if (b < B) {
+            int64_t s0, s1;
+            varlen_range(cu, b, N, &s0, &s1);
+            const int64_t k = ((s1 - s0 + C - 1) / C + cps - 1) / cps;
+            cnt = (int)max((int64_t)1, min(k, (int64_t)P));
+        }
+        // inclusive scan over the workgroup (Hillis-Steele in LDS)
+        part[tid] = cnt;
+        __syncthreads();
+        for (int o = 1; o < kItemThreads; o <<= 1) {
+            const int t = tid >= o ? part[tid - o] : 0;
+            __syncthreads();
+            part[tid] += t;
+            __syncthreads();
+        }
+        const int first = carry + part[tid] - cnt;
+        for (int s = 0; s < cnt; ++s)
+            if (first + s < G) items[first + s] = b * P + s;
+        __syncthreads();
+        if (tid == kItemThreads - 1) carry += part[tid];
+        __syncthreads();
+    }
+}
+
+hipError_t launch_varlen_items(const int32_t* cu, int B, int64_t N, int C, int64_t cps, int P, int G,
+                               int32_t* items, hipStream_t stream)
+{
+    return launch_kernel(la_varlen_items_kernel, dim3(1), dim3(kItemThreads), stream, cu, B, N, C, cps, P, G, items);
+}
+
 // Lambda gradient, per (batch, head) row: the dq sweep's partials, plus
 // sum_s <T_in(s), W_loc(s)> with T_in(0) = 0 and T_in(s+1) = lambda^(L_s)
 // T_in(s) + dT(s) (the segments' own dT, their start state held fixed), plus
