@@ -71,6 +71,13 @@ template <> __device__ __forceinline__ Frag<float> frag_scale<float>(const Frag<
     return r;
 }
 
+// Four consecutive elements (one 8- or 16-byte LDS read) as floats.
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+    const bf16x4 v = ld4(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return ld4(p); }
+
 template <class T, int PHI> __device__ __forceinline__ float phi_deriv_from_phi(float p) {
     if constexpr (PHI == LA_PHI_RELU) return p > 0.f ? 1.f : 0.f;
     else return p < 1.f ? p : 1.f;
@@ -325,16 +332,16 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
             float gy = 0.f;
 #pragma unroll
             for (int kb = 0; kb < VB; ++kb) {
-                const T* p = sG + TVL::off(i, 32 * kb + 4 * g);
-                const T* p2 = sG + TVL::off(i, 32 * kb + 16 + 4 * g);
-                const T* py = sY + TVL::off(i, 32 * kb + 4 * g);
-                const T* py2 = sY + TVL::off(i, 32 * kb + 16 + 4 * g);
+                const f32x4 g0 = ld4f(sG + TVL::off(i, 32 * kb + 4 * g));
+                const f32x4 g1 = ld4f(sG + TVL::off(i, 32 * kb + 16 + 4 * g));
+                const f32x4 y0 = ld4f(sY + TVL::off(i, 32 * kb + 4 * g));
+                const f32x4 y1 = ld4f(sY + TVL::off(i, 32 * kb + 16 + 4 * g));
                 f32x4 lo, hi;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    lo[e] = to_f32(from_f32<T>(to_f32(p[e]) * rden));
-                    hi[e] = to_f32(from_f32<T>(to_f32(p2[e]) * rden));
-                    gy += lo[e] * to_f32(py[e]) + hi[e] * to_f32(py2[e]);
+                    lo[e] = to_f32(from_f32<T>(g0[e] * rden));
+                    hi[e] = to_f32(from_f32<T>(g1[e] * rden));
+                    gy += lo[e] * y0[e] + hi[e] * y1[e];
                 }
                 dn[kb] = frag_acc<T>(lo, hi);
             }
@@ -380,17 +387,17 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 #pragma unroll
                     for (int kb = 0; kb < VB; ++kb) mma(tint, lds_frag_row<T, DV>(sT, 16 * fb + l16, kb, g), dn[kb]);
                     float rs_ = 0.f, rt_ = 0.f;
+                    const f32x4 pq4 = ld4f(sQ + TF::off(i, 16 * fb + 4 * g));
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float p = to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + r]);
+                        const float p = pq4[r];
                         rs_ += p * (inter[r] + accZ[fb][r] * dden);
                         rt_ += p * (tint[r] + accTz[fb][r] * dden);
                     }
                     dl += (float)(i + 1) * lam_pow(l2l, i) * rs_ + lqi * rt_;
                 }
                 if (i < n) {
-                    const f32x4 ph = {to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 0]), to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 1]),
-                                      to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 2]), to_f32(sQ[TF::off(i, 16 * fb + 4 * g) + 3])};
+                    const f32x4 ph = ld4f(sQ + TF::off(i, 16 * fb + 4 * g));
                     float o[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -718,11 +725,11 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
                     for (int kb = 0; kb < VB; ++kb) mma(inter, lds_frag_row<T, DV>(sU, 16 * fb + l16, kb, g), vfr[kb]);
                     if (j < n) {
                         float o[4];
+                        const f32x4 ph = ld4f(sK + TF::off(j, 16 * fb + 4 * g));
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float ph = to_f32(sK[TF::off(j, 16 * fb + 4 * g) + r]);
                             const float dp = intra[r] + lj * (inter[r] + accu[fb][r]);
-                            o[r] = dp * phi_deriv_from_phi<T, PHI>(ph);
+                            o[r] = dp * phi_deriv_from_phi<T, PHI>(ph[r]);
                         }
                         st4((T*)a.dk + (row0 + t0 + j) * DK + 16 * fb + 4 * g, o[0], o[1], o[2], o[3]);
                     }
