@@ -64,6 +64,8 @@ def _load():
     lib.orc_backward.argtypes = [P, P, P, P, L, L, I, I, I, I, P, D, P, D, U, P, P, P, P,
                                  P, P, P, P, P, P, P, P, P]
     lib.orc_backward.restype = None
+    lib.orc_cross_backward.argtypes = [P, P, P, P, L, L, L, I, I, I, I, P, D, D, U, P, P, P]
+    lib.orc_cross_backward.restype = None
     lib.orc_decode_step.argtypes = [P, P, P, L, I, I, I, I, P, D, P, D, P, P, P]
     lib.orc_decode_step.restype = None
     _lib = lib
@@ -317,6 +319,35 @@ def backward(q, k, v, gy, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
                          _ptr(out["dS0"], a * F * dv), _ptr(out["dz0"], a * F), _ptr(out["dlam"], a),
                          _ptr(out.get("kappa_dq"), a * N), _ptr(out.get("kappa_dk"), a * N),
                          _ptr(out.get("kappa_dv"), a * N))
+
+    parts = _split(B * H, threads or default_threads())
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return out
+
+
+def cross_backward(q, k, v, gy, eps=1e-6, phi="elu1", omega=None, scale=1.0, key_padding_mask=None,
+                   threads=None):
+    """Gradients of cross() (non-causal; Nq may differ from Nk) for the loss
+    sum(gy * y).  Returns a dict: dq [B,H,Nq,dk], dk [B,H,Nk,dk], dv [B,H,Nk,dv]."""
+    lib = _load()
+    q, k, v, gy, om = _f64(q), _f64(k), _f64(v), _f64(gy), _f64(omega)
+    B, H, Nq, dk = q.shape
+    Nk = k.shape[2]
+    dv = v.shape[-1]
+    m = 0 if om is None else om.shape[0]
+    kpm = _mask_rows(key_padding_mask, B, H, Nk)
+    out = {"dq": np.empty((B, H, Nq, dk)), "dk": np.empty((B, H, Nk, dk)), "dv": np.empty((B, H, Nk, dv))}
+
+    def run(rng):
+        a, b = rng
+        lib.orc_cross_backward(_ptr(q, a * Nq * dk), _ptr(k, a * Nk * dk), _ptr(v, a * Nk * dv),
+                               _ptr(gy, a * Nq * dv), b - a, Nq, Nk, dk, dv, PHI_KINDS[phi], m, _ptr(om),
+                               float(scale), float(eps), _uptr(kpm, a * Nk), _ptr(out["dq"], a * Nq * dk),
+                               _ptr(out["dk"], a * Nk * dk), _ptr(out["dv"], a * Nk * dv))
 
     parts = _split(B * H, threads or default_threads())
     if len(parts) == 1:

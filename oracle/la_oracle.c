@@ -526,3 +526,88 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
     free(S); free(z); free(T); free(t); free(Sp); free(zp); free(pq); free(pk); free(dp);
     free(dnum); free(dden); free(ddb); free(y); free(Sb); free(zb); free(xb);
 }
+
+/* Gradients of orc_cross (non-causal; Nq queries, Nk keys) for the loss
+ * L = sum_i g_i . y_i.  With S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j)
+ * over the kept keys, den_i = phi(q_i).z + eps, y_i = phi(q_i)^T S / den_i,
+ * dnum_i = g_i / den_i, dden_i = -(g_i . y_i) / den_i:
+ *   d phi(q_i) = S dnum_i + z dden_i,  dq_i = J_phi(q_i)^T d phi(q_i);
+ *   U = sum_i phi(q_i) dnum_i^T, u = sum_i phi(q_i) dden_i (all queries);
+ *   d phi(k_j) = U v_j + u,  dv_j = U^T phi(k_j),  dk_j = J_phi(k_j)^T d phi(k_j)
+ * (a padded key gets dk = dv = 0).  g [nbh][Nq][dv]; outputs dq [nbh][Nq][dk],
+ * dk [nbh][Nk][dk], dv [nbh][Nk][dv]. */
+void orc_cross_backward(const double* q, const double* k, const double* v, const double* gy,
+                        long nbh, long Nq, long Nk, int dk, int dv, int kind, int m,
+                        const double* omega, double scale, double eps, const unsigned char* kpm,
+                        double* dq, double* dkx, double* dvx)
+{
+    const int F = feat_dim(kind, dk, m);
+    const size_t FD = (size_t)F * dv;
+    double* S = (double*)malloc(sizeof(double) * FD);
+    double* z = (double*)malloc(sizeof(double) * (size_t)F);
+    double* U = (double*)malloc(sizeof(double) * FD);
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* p = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dn = (double*)malloc(sizeof(double) * (size_t)dv);
+    for (long bh = 0; bh < nbh; ++bh) {
+        memset(S, 0, sizeof(double) * FD);
+        memset(z, 0, sizeof(double) * (size_t)F);
+        memset(U, 0, sizeof(double) * FD);
+        memset(u, 0, sizeof(double) * (size_t)F);
+        for (long j = 0; j < Nk; ++j) {
+            if (kpm && kpm[(size_t)bh * Nk + j]) continue;
+            orc_phi(kind, k + ((size_t)bh * Nk + j) * dk, dk, m, omega, scale, p);
+            const double* vj = v + ((size_t)bh * Nk + j) * dv;
+            for (int f = 0; f < F; ++f) {
+                for (int d = 0; d < dv; ++d) S[(size_t)f * dv + d] += p[f] * vj[d];
+                z[f] += p[f];
+            }
+        }
+        for (long i = 0; i < Nq; ++i) {
+            const double* qi = q + ((size_t)bh * Nq + i) * dk;
+            const double* gi = gy + ((size_t)bh * Nq + i) * dv;
+            orc_phi(kind, qi, dk, m, omega, scale, p);
+            double den = eps;
+            for (int f = 0; f < F; ++f) den += p[f] * z[f];
+            double gyd = 0.0;
+            for (int d = 0; d < dv; ++d) {
+                double num = 0.0;
+                for (int f = 0; f < F; ++f) num += p[f] * S[(size_t)f * dv + d];
+                gyd += gi[d] * num / den;
+                dn[d] = gi[d] / den;
+            }
+            const double dd = -gyd / den;
+            for (int f = 0; f < F; ++f) {
+                double a = z[f] * dd;
+                for (int d = 0; d < dv; ++d) {
+                    a += S[(size_t)f * dv + d] * dn[d];
+                    U[(size_t)f * dv + d] += p[f] * dn[d];
+                }
+                u[f] += p[f] * dd;
+                dp[f] = a;
+            }
+            orc_phi_vjp(kind, qi, dk, m, omega, scale, dp, dq + ((size_t)bh * Nq + i) * dk);
+        }
+        for (long j = 0; j < Nk; ++j) {
+            const double* kj = k + ((size_t)bh * Nk + j) * dk;
+            const double* vj = v + ((size_t)bh * Nk + j) * dv;
+            double* dvj = dvx + ((size_t)bh * Nk + j) * dv;
+            const int padded = kpm && kpm[(size_t)bh * Nk + j];
+            orc_phi(kind, kj, dk, m, omega, scale, p);
+            for (int d = 0; d < dv; ++d) {
+                double a = 0.0;
+                if (!padded)
+                    for (int f = 0; f < F; ++f) a += U[(size_t)f * dv + d] * p[f];
+                dvj[d] = a;
+            }
+            for (int f = 0; f < F; ++f) {
+                double a = u[f];
+                for (int d = 0; d < dv; ++d) a += U[(size_t)f * dv + d] * vj[d];
+                dp[f] = padded ? 0.0 : a;
+            }
+            orc_phi_vjp(kind, kj, dk, m, omega, scale, dp, dkx + ((size_t)bh * Nk + j) * dk);
+        }
+    }
+    free(S); free(z); free(U); free(u); free(p); free(dp); free(dn);
+}

@@ -688,3 +688,52 @@ def test_backward_kappa_bounds(orc):
     r0 = orc.backward(q, k, v, g, [0.9, 1.0])
     for n in ("dq", "dk", "dv", "dS0", "dz0", "dlam"):
         np.testing.assert_array_equal(r[n], r0[n])
+
+
+@pytest.mark.parametrize("phi,m,masked", [("elu1", 0, False), ("relu", 0, True), ("trig_rf", 6, True)])
+def test_cross_backward_matches_torch_autograd(orc, phi, m, masked):
+    # the non-causal closed form phi(Q)(phi(K)^T V) / (phi(Q) sum phi(k) + eps)
+    # in torch fp64, differentiated by autograd; Nq != Nk
+    import torch
+    rng = np.random.default_rng(zlib.crc32(repr(("xbwd", phi)).encode()))
+    B, H, Nq, Nk, dk, dv = 2, 2, 9, 14, 4, 3
+    q, k, v, g = _rand(rng, B, H, Nq, dk), _rand(rng, B, H, Nk, dk), _rand(rng, B, H, Nk, dv), _rand(rng, B, H, Nq, dv)
+    rf = phi.startswith("trig_rf")
+    om = make_omega(m, dk, seed=2) if rf else None
+    s = dk ** -0.25 if rf else 1.0
+    mask = (rng.random((B, Nk)) < 0.3) if masked else None
+    got = orc.cross_backward(q, k, v, g, 1e-6, phi, om, s, key_padding_mask=mask)
+    t = {n: torch.tensor(a, requires_grad=True) for n, a in (("q", q), ("k", k), ("v", v))}
+
+    def feat(x):
+        if phi == "elu1":
+            return torch.nn.functional.elu(x) + 1.0
+        if phi == "relu":
+            return torch.relu(x)
+        xs = s * x
+        uu = xs @ torch.tensor(om, dtype=torch.float64).T
+        c = torch.exp(-0.5 * (xs * xs).sum(-1, keepdim=True)) / math.sqrt(m)
+        return c * torch.cat([torch.cos(uu), torch.sin(uu)], -1)
+
+    pq, pk = feat(t["q"]), feat(t["k"])
+    if mask is not None:
+        pk = pk * torch.tensor(~mask, dtype=torch.float64)[:, None, :, None]
+    y = (pq @ (pk.transpose(-1, -2) @ t["v"])) / (pq @ pk.sum(2)[..., None] + 1e-6)
+    (torch.tensor(g) * y).sum().backward()
+    for n in ("q", "k", "v"):
+        np.testing.assert_allclose(got["d" + n], t[n].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=n)
+
+
+def test_cross_backward_finite_differences_and_noncausal_case(orc):
+    rng = np.random.default_rng(34)
+    B, H, Nq, Nk, dk, dv = 1, 2, 7, 11, 4, 3
+    q, k, v, g = _rand(rng, B, H, Nq, dk), _rand(rng, B, H, Nk, dk), _rand(rng, B, H, Nk, dv), _rand(rng, B, H, Nq, dv)
+    gr = orc.cross_backward(q, k, v, g)
+    d = {n: rng.standard_normal(a.shape) for n, a in (("q", q), ("k", k), ("v", v))}
+
+    def loss(h):
+        return (g * orc.cross(q + h * d["q"], k + h * d["k"], v + h * d["v"])).sum()
+
+    fd = (loss(1e-5) - loss(-1e-5)) / 2e-5
+    an = sum((gr["d" + n] * d[n]).sum() for n in ("q", "k", "v"))
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
