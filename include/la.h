@@ -249,6 +249,33 @@ la_status la_backward_causal(const void* q, const void* k, const void* v,
                              float* dS_in, float* dz_in, float* dlambda,
                              void* workspace, size_t workspace_bytes, la_stream_t stream);
 
+/* Gradients of la_forward_cross (and of la_forward_noncausal: n_kv = N with
+ * the same rows for keys and queries).  Training with the non-causal form:
+ * "From standard attention to linear attention" sec. 3 and 6 for the form,
+ * "Attention is also an FFN" sec. 4.1 and 5.2 for training it.  For the loss
+ * L = sum_i dy_i . y_i, with S, z the sums over the kept keys and
+ * dnum_i = dy_i / den_i, dden_i = -(dy_i . y_i) / den_i:
+ *   dq_i: J_phi(q_i)^T (S dnum_i + z dden_i),
+ *   U = sum_i phi(q_i) dnum_i^T, u = sum_i phi(q_i) dden_i over the queries,
+ *   dk_j: J_phi(k_j)^T (U v_j + u),  dv_j = U^T phi(k_j)
+ * (a padded key gets dk = dv = 0).  q, y, dy, dq: [B,H,N,d_*]; k, v, dk, dv:
+ * [B,H,n_kv,d_*]; all device, in shape->in_dtype (out_dtype must equal it);
+ * y is la_forward_cross's output for the same q, k, v, key_padding_mask and
+ * eps.  Outputs must not alias inputs or each other.  Feature maps:
+ * LA_PHI_ELU1 and LA_PHI_RELU (others: LA_ERR_UNSUPPORTED).  N >= 1,
+ * n_kv >= 1.  Method: three passes -- the state sums over the keys (as the
+ * forward), a sweep over the queries that writes dq and sums the adjoint per
+ * segment, a sweep over the keys that reads the total adjoint -- with two
+ * small reductions joining the segments.  Workspace:
+ * la_workspace_size_backward_cross bytes (segment states only). */
+size_t la_workspace_size_backward_cross(const la_shape* shape, int64_t n_kv, const la_phi* phi);
+la_status la_backward_cross(const void* q, const void* k, const void* v,
+                            const void* y, const void* dy,
+                            void* dq, void* dk, void* dv,
+                            const la_shape* shape, int64_t n_kv,
+                            const uint8_t* key_padding_mask, const la_phi* phi, float eps,
+                            void* workspace, size_t workspace_bytes, la_stream_t stream);
+
 /* Recurrent decode steps, in place ("From standard attention to linear
  * attention" sec. 6 autoregressive step, with the decay of "Attention is also
  * an FFN" sec. 3.2): per (b,h), for each of the N tokens in order
@@ -285,7 +312,9 @@ enum {
     LA_KERNEL_BWD_RLOCAL = 8,  /* backward: adjoint segment sums               */
     LA_KERNEL_BWD_KV = 9,      /* backward: dk, dv sweep                       */
     LA_KERNEL_BWD_DLAM = 10,   /* backward: lambda-gradient reduction          */
-    LA_KERNEL_VARLEN_ITEMS = 11 /* packed sequences: table of work items       */
+    LA_KERNEL_VARLEN_ITEMS = 11, /* packed sequences: table of work items      */
+    LA_KERNEL_BWD_NCQ = 12,    /* non-causal backward: dq and adjoint sums     */
+    LA_KERNEL_BWD_NCKV = 13    /* non-causal backward: dk, dv                  */
 };
 la_status la_profile_begin(int32_t max_launches);
 la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);

@@ -64,7 +64,7 @@ def _load():
     lib.orc_backward.argtypes = [P, P, P, P, L, L, I, I, I, I, P, D, P, D, U, P, P, P, P,
                                  P, P, P, P, P, P, P, P, P]
     lib.orc_backward.restype = None
-    lib.orc_cross_backward.argtypes = [P, P, P, P, L, L, L, I, I, I, I, P, D, D, U, P, P, P]
+    lib.orc_cross_backward.argtypes = [P, P, P, P, L, L, L, I, I, I, I, P, D, D, U, P, P, P, P, P, P]
     lib.orc_cross_backward.restype = None
     lib.orc_decode_step.argtypes = [P, P, P, L, I, I, I, I, P, D, P, D, P, P, P]
     lib.orc_decode_step.restype = None
@@ -330,9 +330,11 @@ def backward(q, k, v, gy, lam=None, eps=1e-6, phi="elu1", omega=None, scale=1.0,
 
 
 def cross_backward(q, k, v, gy, eps=1e-6, phi="elu1", omega=None, scale=1.0, key_padding_mask=None,
-                   threads=None):
+                   threads=None, want_kappa=False):
     """Gradients of cross() (non-causal; Nq may differ from Nk) for the loss
-    sum(gy * y).  Returns a dict: dq [B,H,Nq,dk], dk [B,H,Nk,dk], dv [B,H,Nk,dv]."""
+    sum(gy * y).  Returns a dict: dq [B,H,Nq,dk], dk [B,H,Nk,dk], dv [B,H,Nk,dv];
+    with want_kappa (elementwise feature maps) also the rows' cancellation
+    factors kappa_dq [B,H,Nq], kappa_dk, kappa_dv [B,H,Nk] (as backward())."""
     lib = _load()
     q, k, v, gy, om = _f64(q), _f64(k), _f64(v), _f64(gy), _f64(omega)
     B, H, Nq, dk = q.shape
@@ -341,13 +343,19 @@ def cross_backward(q, k, v, gy, eps=1e-6, phi="elu1", omega=None, scale=1.0, key
     m = 0 if om is None else om.shape[0]
     kpm = _mask_rows(key_padding_mask, B, H, Nk)
     out = {"dq": np.empty((B, H, Nq, dk)), "dk": np.empty((B, H, Nk, dk)), "dv": np.empty((B, H, Nk, dv))}
+    if want_kappa:
+        out["kappa_dq"] = np.empty((B, H, Nq))
+        out["kappa_dk"] = np.empty((B, H, Nk))
+        out["kappa_dv"] = np.empty((B, H, Nk))
 
     def run(rng):
         a, b = rng
         lib.orc_cross_backward(_ptr(q, a * Nq * dk), _ptr(k, a * Nk * dk), _ptr(v, a * Nk * dv),
                                _ptr(gy, a * Nq * dv), b - a, Nq, Nk, dk, dv, PHI_KINDS[phi], m, _ptr(om),
                                float(scale), float(eps), _uptr(kpm, a * Nk), _ptr(out["dq"], a * Nq * dk),
-                               _ptr(out["dk"], a * Nk * dk), _ptr(out["dv"], a * Nk * dv))
+                               _ptr(out["dk"], a * Nk * dk), _ptr(out["dv"], a * Nk * dv),
+                               _ptr(out.get("kappa_dq"), a * Nq), _ptr(out.get("kappa_dk"), a * Nk),
+                               _ptr(out.get("kappa_dv"), a * Nk))
 
     parts = _split(B * H, threads or default_threads())
     if len(parts) == 1:

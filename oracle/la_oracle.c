@@ -527,6 +527,19 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
     free(dnum); free(dden); free(ddb); free(y); free(Sb); free(zb); free(xb);
 }
 
+/* Largest |a_e| over largest |r_e| of one gradient row: its cancellation
+ * factor (a: the row's terms on |.|); a zero row is 1, or infinite if its
+ * terms are not zero. */
+static double row_kappa(const double* a, const double* r, int n)
+{
+    double num = 0.0, den = 0.0;
+    for (int e = 0; e < n; ++e) {
+        if (fabs(a[e]) > num) num = fabs(a[e]);
+        if (fabs(r[e]) > den) den = fabs(r[e]);
+    }
+    return den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 1.0);
+}
+
 /* Gradients of orc_cross (non-causal; Nq queries, Nk keys) for the loss
  * L = sum_i g_i . y_i.  With S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j)
  * over the kept keys, den_i = phi(q_i).z + eps, y_i = phi(q_i)^T S / den_i,
@@ -535,12 +548,17 @@ void orc_backward(const double* q, const double* k, const double* v, const doubl
  *   U = sum_i phi(q_i) dnum_i^T, u = sum_i phi(q_i) dden_i (all queries);
  *   d phi(k_j) = U v_j + u,  dv_j = U^T phi(k_j),  dk_j = J_phi(k_j)^T d phi(k_j)
  * (a padded key gets dk = dv = 0).  g [nbh][Nq][dv]; outputs dq [nbh][Nq][dk],
- * dk [nbh][Nk][dk], dv [nbh][Nk][dv]. */
+ * dk [nbh][Nk][dk], dv [nbh][Nk][dv].  Cancellation factors kq [nbh][Nq],
+ * kk, kv [nbh][Nk] (NULL = not computed; elementwise feature maps only), as
+ * in orc_backward: the sums above run on |.| (|dden_i| replaced by
+ * sum_d |dnum_i,d y_i,d|), and each row's largest such entry is divided by
+ * the row's largest |entry|. */
 void orc_cross_backward(const double* q, const double* k, const double* v, const double* gy,
                         long nbh, long Nq, long Nk, int dk, int dv, int kind, int m,
                         const double* omega, double scale, double eps, const unsigned char* kpm,
-                        double* dq, double* dkx, double* dvx)
+                        double* dq, double* dkx, double* dvx, double* kq, double* kk, double* kv)
 {
+    const int want_k = kq && kk && kv && (kind == ORC_PHI_ELU1 || kind == ORC_PHI_RELU);
     const int F = feat_dim(kind, dk, m);
     const size_t FD = (size_t)F * dv;
     double* S = (double*)malloc(sizeof(double) * FD);
@@ -550,18 +568,32 @@ void orc_cross_backward(const double* q, const double* k, const double* v, const
     double* p = (double*)malloc(sizeof(double) * (size_t)F);
     double* dp = (double*)malloc(sizeof(double) * (size_t)F);
     double* dn = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* yq = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* Sb = (double*)malloc(sizeof(double) * FD);  /* |.| companions (kappa) */
+    double* zb = (double*)malloc(sizeof(double) * (size_t)F);
+    double* Ub = (double*)malloc(sizeof(double) * FD);
+    double* ub = (double*)malloc(sizeof(double) * (size_t)F);
+    double* xb = (double*)malloc(sizeof(double) * (size_t)(F > dv ? F : dv));
     for (long bh = 0; bh < nbh; ++bh) {
         memset(S, 0, sizeof(double) * FD);
         memset(z, 0, sizeof(double) * (size_t)F);
         memset(U, 0, sizeof(double) * FD);
         memset(u, 0, sizeof(double) * (size_t)F);
+        memset(Sb, 0, sizeof(double) * FD);
+        memset(zb, 0, sizeof(double) * (size_t)F);
+        memset(Ub, 0, sizeof(double) * FD);
+        memset(ub, 0, sizeof(double) * (size_t)F);
         for (long j = 0; j < Nk; ++j) {
             if (kpm && kpm[(size_t)bh * Nk + j]) continue;
             orc_phi(kind, k + ((size_t)bh * Nk + j) * dk, dk, m, omega, scale, p);
             const double* vj = v + ((size_t)bh * Nk + j) * dv;
             for (int f = 0; f < F; ++f) {
-                for (int d = 0; d < dv; ++d) S[(size_t)f * dv + d] += p[f] * vj[d];
+                for (int d = 0; d < dv; ++d) {
+                    S[(size_t)f * dv + d] += p[f] * vj[d];
+                    Sb[(size_t)f * dv + d] += fabs(p[f] * vj[d]);
+                }
                 z[f] += p[f];
+                zb[f] += fabs(p[f]);
             }
         }
         for (long i = 0; i < Nq; ++i) {
@@ -574,20 +606,35 @@ void orc_cross_backward(const double* q, const double* k, const double* v, const
             for (int d = 0; d < dv; ++d) {
                 double num = 0.0;
                 for (int f = 0; f < F; ++f) num += p[f] * S[(size_t)f * dv + d];
-                gyd += gi[d] * num / den;
+                yq[d] = num / den;
+                gyd += gi[d] * yq[d];
                 dn[d] = gi[d] / den;
             }
             const double dd = -gyd / den;
+            double ddb = 0.0;
+            for (int d = 0; d < dv; ++d) ddb += fabs(dn[d] * yq[d]);
             for (int f = 0; f < F; ++f) {
                 double a = z[f] * dd;
                 for (int d = 0; d < dv; ++d) {
                     a += S[(size_t)f * dv + d] * dn[d];
                     U[(size_t)f * dv + d] += p[f] * dn[d];
+                    Ub[(size_t)f * dv + d] += fabs(p[f] * dn[d]);
                 }
                 u[f] += p[f] * dd;
+                ub[f] += fabs(p[f]) * ddb;
                 dp[f] = a;
             }
-            orc_phi_vjp(kind, qi, dk, m, omega, scale, dp, dq + ((size_t)bh * Nq + i) * dk);
+            double* dqi = dq + ((size_t)bh * Nq + i) * dk;
+            orc_phi_vjp(kind, qi, dk, m, omega, scale, dp, dqi);
+            if (want_k) {
+                for (int f = 0; f < F; ++f) {
+                    double a = zb[f] * ddb;
+                    for (int d = 0; d < dv; ++d) a += Sb[(size_t)f * dv + d] * fabs(dn[d]);
+                    dp[f] = a;
+                }
+                orc_phi_vjp(kind, qi, dk, m, omega, scale, dp, xb);
+                kq[(size_t)bh * Nq + i] = row_kappa(xb, dqi, dk);
+            }
         }
         for (long j = 0; j < Nk; ++j) {
             const double* kj = k + ((size_t)bh * Nk + j) * dk;
@@ -606,8 +653,28 @@ void orc_cross_backward(const double* q, const double* k, const double* v, const
                 for (int d = 0; d < dv; ++d) a += U[(size_t)f * dv + d] * vj[d];
                 dp[f] = padded ? 0.0 : a;
             }
-            orc_phi_vjp(kind, kj, dk, m, omega, scale, dp, dkx + ((size_t)bh * Nk + j) * dk);
+            double* dkj = dkx + ((size_t)bh * Nk + j) * dk;
+            orc_phi_vjp(kind, kj, dk, m, omega, scale, dp, dkj);
+            if (want_k) {
+                /* dv_j = U^T phi(k_j): |U|^T |phi(k_j)| */
+                for (int d = 0; d < dv; ++d) {
+                    double a = 0.0;
+                    if (!padded)
+                        for (int f = 0; f < F; ++f) a += Ub[(size_t)f * dv + d] * fabs(p[f]);
+                    xb[d] = a;
+                }
+                kv[(size_t)bh * Nk + j] = row_kappa(xb, dvj, dv);
+                /* d phi(k_j) = U v_j + u: |U| |v_j| + |u|, through |phi'| */
+                for (int f = 0; f < F; ++f) {
+                    double a = ub[f];
+                    for (int d = 0; d < dv; ++d) a += Ub[(size_t)f * dv + d] * fabs(vj[d]);
+                    dp[f] = padded ? 0.0 : a;
+                }
+                orc_phi_vjp(kind, kj, dk, m, omega, scale, dp, xb);
+                kk[(size_t)bh * Nk + j] = row_kappa(xb, dkj, dk);
+            }
         }
     }
     free(S); free(z); free(U); free(u); free(p); free(dp); free(dn);
+    free(yq); free(Sb); free(zb); free(Ub); free(ub); free(xb);
 }

@@ -203,3 +203,35 @@ def test_backward_validation(lib):
     n = lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(ELU))
     assert n >= 2 * 4 * s.B * s.H * s.N                                      # 8 bytes per token at least
     assert lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35))) == 0
+
+
+def test_cross_backward_validation(lib):
+    """Argument errors of la_backward_cross are caught on the host (no launch)."""
+    E, U, W = la.binding.LA_ERR_INVALID_ARGUMENT, la.binding.LA_ERR_UNSUPPORTED, la.binding.LA_ERR_WORKSPACE
+    s = _shape(N=64)
+    P = [FAKE + i * 0x100000 for i in range(8)]  # q k v y dy dq dk dv
+    RF = LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35)
+
+    def call(shape=s, n_kv=100, phi=ELU, ptrs=P, eps=1e-6, ws=None, ws_bytes=0):
+        return lib.la_backward_cross(*ptrs, ctypes.byref(shape), n_kv, None, ctypes.byref(phi), eps, ws, ws_bytes,
+                                     None)
+
+    assert call(phi=RF) == U                                    # random features
+    assert call(shape=_shape(ot=la.LA_F32)) == U                # y in another type
+    assert call(shape=_shape(N=0)) == E                         # no queries
+    assert call(n_kv=0) == E                                    # no keys
+    assert call(eps=-1.0) == E
+    assert call(ptrs=P[:5] + [P[0]] + P[6:]) == E              # dq aliases q
+    assert call(ptrs=P[:6] + [P[5] + 64] + P[7:]) == E         # dk overlaps dq
+    # dv runs over n_kv rows: with 4096 keys it reaches into the next buffer (dy)
+    assert call(n_kv=4096, ptrs=P[:7] + [P[4] - 0x40000]) == E
+    assert call() == W                                          # no workspace
+    n = lib.la_workspace_size_backward_cross(ctypes.byref(s), 100, ctypes.byref(ELU))
+    assert n > 0 and call(ws=FAKE, ws_bytes=n - 1) == W
+    assert lib.la_workspace_size_backward_cross(ctypes.byref(s), 100, ctypes.byref(RF)) == 0
+    assert lib.la_workspace_size_backward_cross(ctypes.byref(s), 0, ctypes.byref(ELU)) == 0
+    assert lib.la_workspace_size_backward_cross(ctypes.byref(_shape(N=0)), 100, ctypes.byref(ELU)) == 0
+    # segment states for the keys' and the queries' splits: grows with both lengths
+    big_k = lib.la_workspace_size_backward_cross(ctypes.byref(s), 1 << 16, ctypes.byref(ELU))
+    big_q = lib.la_workspace_size_backward_cross(ctypes.byref(_shape(N=1 << 16)), 100, ctypes.byref(ELU))
+    assert big_k > n and big_q > n

@@ -37,21 +37,24 @@ def head_scale(ref):
     return np.maximum(s, 0.1 * np.abs(ref).max())
 
 
-def _check(name, got, ref, kappa, dtype):
+def _check(name, got, ref, kappa, dtype, normwise=True):
     tol = TOL_BWD[dtype]
-    # every row within tol * kappa_r (rounding error against the row's terms)
     err = row_errors(got, ref)
-    bound = tol * np.maximum(1.0, kappa)
-    worst = int(np.argmax(err / bound))
-    assert np.all(err <= bound), (name, float(err.reshape(-1)[worst]), float(kappa.reshape(-1)[worst]))
+    if kappa is not None:
+        # every row within tol * kappa_r (rounding error against the row's terms)
+        bound = tol * np.maximum(1.0, kappa)
+        worst = int(np.argmax(err / bound))
+        assert np.all(err <= bound), (name, float(err.reshape(-1)[worst]), float(kappa.reshape(-1)[worst]))
     # normwise per head within tol, and rows of at least a tenth of their
     # head's scale within tol of their own size
     scale = head_scale(ref)
     he = np.abs(got - ref).reshape(got.shape[0], got.shape[1], -1).max(-1) / scale
     big = np.abs(ref).max(-1) >= 0.1 * scale[..., None]
     _record(float(he.max()))
-    print("%s head-normwise %.3e  large-row %.3e  kappa median %.1f" % (name, he.max(), err[big].max(),
-                                                                         float(np.median(kappa))))
+    print("%s head-normwise %.3e  large-row %.3e  kappa median %.1f" % (
+        name, he.max(), err[big].max(), float(np.median(kappa)) if kappa is not None else float("nan")))
+    if not normwise:
+        return  # every row cancels (the rows are no scale): the kappa bound alone
     assert float(he.max()) < tol, (name, float(he.max()))
     assert float(err[big].max()) < tol, (name, float(err[big].max()))
 
@@ -174,3 +177,80 @@ def test_backward_full_size_headline_shape():
     wl = si.workload(2)
     got, ref = run_backward(wl, wl.B, wl.H, wl.N, [1.0] * wl.H, seed=42)
     check_all(wl, got, ref)
+
+
+# ---------------------------------------------------------------------------
+# Non-causal / cross form (la_backward_cross): the same bar as the causal
+# form, with the oracle's kappa for this form.  With a single key the output
+# is that key's value whatever q and k are (but for eps), so every dq and dk
+# row cancels to the eps term: those rows are held to the kappa bound only.
+
+def run_cross_backward(wl, B, H, Nq, Nk, mask=None, seed=0, self_attention=False):
+    qi = si.make_inputs(wl, B=B, H=H, N=Nq)
+    kv = qi if self_attention else si.make_kv(wl, Nk, B=B, H=H, seed=seed)
+    q, k, v = to_dev(qi, "q", wl.dtype), to_dev(kv, "k", wl.dtype), to_dev(kv, "v", wl.dtype)
+    g_np, g = _grad_out(wl, B, H, Nq, seed + 1)
+    m = None if mask is None else si.make_key_padding_mask(B, Nk, mask, seed=seed + 3)
+    mt = None if m is None else _dev(m)
+    phi = la.Phi(wl.phi)
+    y = torch.empty(B, H, Nq, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    if self_attention:
+        la.la_forward_noncausal(q, k, v, y, phi=phi, eps=wl.eps)
+    else:
+        la.la_forward_cross(q, k, v, y, mt, phi=phi, eps=wl.eps)
+    dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    la.la_backward_cross(q, k, v, y, g, dq, dk, dv, mt, phi=phi, eps=wl.eps)
+    torch.cuda.synchronize()
+    ref = oracle.cross_backward(qi["q"], kv["k"], kv["v"], g_np, wl.eps, wl.phi, key_padding_mask=m,
+                                want_kappa=True)
+    got = {"dq": dq.float().cpu().numpy(), "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy()}
+    return got, ref, m
+
+
+CROSS_CASES = [
+    # workload, overrides, B, H, Nq, Nk, mask
+    (2, {}, 2, 2, 300, 777, None),
+    (2, {"phi": "relu"}, 2, 2, 1000, 513, "right"),
+    (1, {}, 2, 1, 257, 100, "random"),                  # fp32
+    (1, {"dk": 128, "dv": 128}, 1, 2, 64, 3000, None),  # many key segments
+    (2, {"dv": 128}, 1, 2, 5000, 200, "random"),        # many query segments: the adjoint reduction
+    (3, {"phi": "relu", "lam": "one"}, 1, 2, 33, 1, None),  # d = 128, one key
+    (2, {}, 1, 1, 1, 40, "random"),                     # one query
+]
+
+
+@pytest.mark.parametrize("wi,over,B,H,Nq,Nk,mask", CROSS_CASES)
+def test_cross_backward_parity(wi, over, B, H, Nq, Nk, mask):
+    wl = si.workload(wi).with_(**over)
+    got, ref, m = run_cross_backward(wl, B, H, Nq, Nk, mask, seed=wi * 100 + Nq)
+    for n in ("dq", "dk", "dv"):
+        _check(n, got[n], ref[n], ref["kappa_" + n], wl.dtype, normwise=Nk > 1 or n == "dv")
+    if m is not None:
+        padded = np.broadcast_to(m[:, None, :], (B, H, Nk))
+        assert float(np.abs(got["dk"][padded]).max(initial=0.0)) == 0.0
+        assert float(np.abs(got["dv"][padded]).max(initial=0.0)) == 0.0
+
+
+def test_noncausal_self_attention_backward():
+    # la_forward_noncausal's gradients: the same rows for keys and queries
+    wl = si.workload(2).with_(dk=128, dv=128)
+    got, ref, _ = run_cross_backward(wl, 1, 2, 4096, 4096, seed=7, self_attention=True)
+    for n in ("dq", "dk", "dv"):
+        _check(n, got[n], ref[n], ref["kappa_" + n], wl.dtype)
+
+
+def test_cross_backward_all_keys_padded_gives_zero():
+    # no key kept: S = z = 0, so y = 0 and every gradient vanishes
+    wl = si.workload(2)
+    got, _, _ = run_cross_backward(wl, 2, 2, 100, 70, mask="all", seed=3)
+    for n in ("dq", "dk", "dv"):
+        assert float(np.abs(got[n]).max()) == 0.0, n
+
+
+def test_cross_backward_full_size():
+    # B=4 H=8, 1024 queries against 4096 right-padded keys, d=64 bf16: the
+    # benchmarked cross-attention shape
+    wl = si.workload(2)
+    got, ref, _ = run_cross_backward(wl, 4, 8, 1024, 4096, mask="right", seed=11)
+    for n in ("dq", "dk", "dv"):
+        _check(n, got[n], ref[n], ref["kappa_" + n], wl.dtype)

@@ -79,7 +79,7 @@ def test_graph_forward_decode_backward():
     _replay_and_compare(graph, outs, eager, scramble)
 
 
-def test_graph_varlen_and_cross():
+def test_graph_varlen_and_cross():  # cross attention forward and backward
     wl = si.workload(2)
     H, d = 4, 64
     L = si.make_varlen_lengths(9, 700, seed=4, empty=1)
@@ -101,16 +101,20 @@ def test_graph_varlen_and_cross():
     mask = torch.from_numpy(si.make_key_padding_mask(B, Nk, "right", seed=4)).to(DEV)
     yc = torch.empty(B, H, Nq, d, dtype=torch.bfloat16, device=DEV)
     wsc = _ws(la.la_workspace_size_cross(B, H, Nq, Nk, d, d))
+    gc = torch.randn(B, H, Nq, d, device=DEV).to(torch.bfloat16)
+    dqc, dkc, dvc = torch.empty_like(cq), torch.empty_like(ck), torch.empty_like(cv)
+    wscb = _ws(la.la_workspace_size_backward_cross(B, H, Nq, Nk, d, d))
 
     def run():
         la.la_forward_causal_varlen(q, k, v, y, cu_t, mx, lambda_h=[0.9, 0.95, 0.99, 1.0], S_out=Sf, z_out=zf,
                                     workspace=wsv)
         la.la_forward_cross(cq, ck, cv, yc, mask, workspace=wsc)
+        la.la_backward_cross(cq, ck, cv, yc, gc, dqc, dkc, dvc, mask, workspace=wscb)
 
     y.fill_(0.0)  # rows after the last sequence are never written: same value in every run
     run()
     torch.cuda.synchronize()
-    outs = {"y": y, "S": Sf, "z": zf, "yc": yc}
+    outs = {"y": y, "S": Sf, "z": zf, "yc": yc, "dqc": dqc, "dkc": dkc, "dvc": dvc}
     eager = {n: t.clone() for n, t in outs.items()}
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -122,7 +126,7 @@ def test_graph_varlen_and_cross():
 
     def scramble():
         y[:, :T].fill_(float("nan"))  # only the rows the call writes
-        for t in (Sf, zf, yc):
+        for t in (Sf, zf, yc, dqc, dkc, dvc):
             t.fill_(float("nan"))
 
     _replay_and_compare(graph, outs, eager, scramble)

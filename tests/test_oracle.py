@@ -737,3 +737,22 @@ def test_cross_backward_finite_differences_and_noncausal_case(orc):
     fd = (loss(1e-5) - loss(-1e-5)) / 2e-5
     an = sum((gr["d" + n] * d[n]).sum() for n in ("q", "k", "v"))
     assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
+def test_cross_backward_kappa_bounds(orc):
+    # kappa >= 1; positive dy makes every term of dv positive (kappa_dv = 1);
+    # with a single key y_i = v (but for eps) whatever q_i and k are, so dq
+    # and dk cancel down to the eps term (kappa huge) while their terms do not
+    rng = np.random.default_rng(35)
+    B, H, Nq, Nk, dk, dv = 1, 2, 9, 13, 4, 3
+    q, k, v = _rand(rng, B, H, Nq, dk), _rand(rng, B, H, Nk, dk), _rand(rng, B, H, Nk, dv)
+    g = np.abs(_rand(rng, B, H, Nq, dv)) + 0.1
+    r = orc.cross_backward(q, k, v, g, want_kappa=True)
+    for n in ("kappa_dq", "kappa_dk", "kappa_dv"):
+        assert np.all(r[n] >= 1.0 - 1e-12), n
+    np.testing.assert_allclose(r["kappa_dv"], 1.0, rtol=1e-12)
+    r0 = orc.cross_backward(q, k, v, g)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(r[n], r0[n])
+    one = orc.cross_backward(q, k[:, :, :1], v[:, :, :1], g, want_kappa=True)
+    assert np.all(one["kappa_dq"] > 1e4) and np.all(one["kappa_dk"] > 1e4)

@@ -11,7 +11,8 @@ from .binding import (  # noqa: F401
     LA_PHI_TRIG_RF_PLAIN, LA_PHI_TRIG_RF_SOFTMAX, LaError, Phi,
     la_decode_step, la_forward_causal, la_forward_causal_masked, la_forward_causal_varlen, la_forward_cross,
     la_forward_noncausal, la_init_state, la_init_state_identity, la_kernel_name, la_workspace_size_cross,
-    la_workspace_size_varlen, la_backward_causal, la_workspace_size_backward,
+    la_workspace_size_varlen, la_backward_causal, la_workspace_size_backward, la_backward_cross,
+    la_workspace_size_backward_cross,
     la_last_error, la_profile_begin, la_profile_end, la_status_string, la_workspace_size,
     load_library, rf_scale,
 )

@@ -30,10 +30,12 @@ LA_MAX_HEADS = 256
 EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
            "la_forward_causal_masked", "la_workspace_size_varlen", "la_forward_causal_varlen",
            "la_workspace_size_cross", "la_forward_cross", "la_workspace_size_backward", "la_backward_causal",
+           "la_workspace_size_backward_cross", "la_backward_cross",
            "la_decode_step", "la_status_string", "la_last_error", "la_profile_begin", "la_profile_end",
            "la_kernel_name")
 KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6,
-              "bwd_q": 7, "bwd_rlocal": 8, "bwd_kv": 9, "bwd_dlam": 10, "varlen_items": 11}
+              "bwd_q": 7, "bwd_rlocal": 8, "bwd_kv": 9, "bwd_dlam": 10, "varlen_items": 11, "bwd_ncq": 12,
+              "bwd_nckv": 13}
 
 
 class LaPhiC(ctypes.Structure):
@@ -98,6 +100,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
     lib.la_backward_causal.restype = ctypes.c_int
+    lib.la_workspace_size_backward_cross.argtypes = [SP, i64, PP]
+    lib.la_workspace_size_backward_cross.restype = sz
+    lib.la_backward_cross.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, SP, i64, vp, PP, f, vp, sz, vp]
+    lib.la_backward_cross.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, SP, PP, vp, f, vp]
     lib.la_decode_step.restype = ctypes.c_int
     lib.la_status_string.argtypes = [ctypes.c_int]
@@ -395,6 +401,31 @@ def la_backward_causal(q, k, v, y, dy, dq, dk, dv, phi: Optional[Phi] = None, la
                                    _ptr(dz_out), _ptr(dS_in), _ptr(dz_in), _ptr(dlambda), _ptr(ws), ws_bytes,
                                    _stream(stream)))
     del lam_keep
+    return dq, dk, dv
+
+
+def la_workspace_size_backward_cross(B, H, N, n_kv, d_k, d_v, in_dtype=LA_BF16, phi: Optional[Phi] = None) -> int:
+    load_library()
+    phi = phi or Phi()
+    shape = LaShapeC(B, H, N, d_k, d_v, in_dtype, in_dtype)
+    pc = phi.c()
+    return int(_lib.la_workspace_size_backward_cross(ctypes.byref(shape), int(n_kv), ctypes.byref(pc)))
+
+
+def la_backward_cross(q, k, v, y, dy, dq, dk, dv, key_padding_mask=None, phi: Optional[Phi] = None,
+                      eps: float = 1e-6, workspace=None, stream=None):
+    """Gradients of la_forward_cross (q, y, dy, dq: [B,H,N,*]; k, v, dk, dv:
+    [B,H,M,*]): writes dq, dk, dv."""
+    load_library()
+    phi = phi or Phi()
+    shape = _shape(q, v, y)
+    n_kv = int(k.shape[2])
+    pc = phi.c()
+    need = int(_lib.la_workspace_size_backward_cross(ctypes.byref(shape), n_kv, ctypes.byref(pc)))
+    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
+    _check(_lib.la_backward_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  ctypes.byref(shape), n_kv, _mask_ptr(key_padding_mask), ctypes.byref(pc),
+                                  float(eps), _ptr(ws), ws_bytes, _stream(stream)))
     return dq, dk, dv
 
 

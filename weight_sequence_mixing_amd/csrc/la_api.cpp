@@ -411,6 +411,8 @@ const char* la_kernel_name(int32_t id)
     case LA_KERNEL_BWD_KV: return "la_bwd_kv_kernel (dk dv)";
     case LA_KERNEL_BWD_DLAM: return "la_dlam_rows_kernel";
     case LA_KERNEL_VARLEN_ITEMS: return "la_varlen_items_kernel";
+    case LA_KERNEL_BWD_NCQ: return "la_bwd_q_kernel (non-causal)";
+    case LA_KERNEL_BWD_NCKV: return "la_bwd_kv_kernel (non-causal dk dv)";
     }
     return "unknown";
 }
@@ -876,6 +878,34 @@ la_status check_backward(const la_shape* shape, const la_phi* phi, int* F, const
     return LA_OK;
 }
 
+// q, k, v, y, dy and dq, dk, dv: non-NULL and 16-byte aligned; the outputs
+// overlap no input and no other output.  q, y, dy, dq have rows_q rows,
+// k, v, dk, dv rows_k.
+la_status check_bwd_io(const void* q, const void* k, const void* v, const void* y, const void* dy, void* dq,
+                       void* dk, void* dv, const la_shape* s, size_t rows_q, size_t rows_k)
+{
+    const void* ins[] = {q, k, v, y, dy};
+    void* outs[] = {dq, dk, dv};
+    for (const void* p : ins)
+        if (!p || !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, y, dy must be non-NULL and 16-byte aligned");
+    for (const void* p : outs)
+        if (!p || !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must be non-NULL and 16-byte aligned");
+    const size_t es = elem_size(s->in_dtype);
+    const size_t nq = rows_q * s->d_k * es, nyq = rows_q * s->d_v * es;
+    const size_t nk = rows_k * s->d_k * es, nv = rows_k * s->d_v * es;
+    const size_t in_sz[] = {nq, nk, nv, nyq, nyq};
+    const size_t out_sz[] = {nq, nk, nv};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 5; ++i)
+            if (overlaps(outs[o], out_sz[o], ins[i], in_sz[i]))
+                return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must not alias q, k, v, y or dy");
+        for (int o2 = 0; o2 < o; ++o2)
+            if (overlaps(outs[o], out_sz[o], outs[o2], out_sz[o2]))
+                return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must not overlap");
+    }
+    return LA_OK;
+}
+
 struct BwdPlan {
     int P;
     int64_t cps;
@@ -965,24 +995,8 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         if (e != hipSuccess) return hip_fail(e, "la_backward_causal (N=0)");
         return ok();
     }
-    const void* ins[] = {q, k, v, y, dy};
-    void* outs[] = {dq, dk, dv};
-    for (const void* p : ins)
-        if (!p || !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, y, dy must be non-NULL and 16-byte aligned");
-    for (const void* p : outs)
-        if (!p || !aligned16(p)) return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must be non-NULL and 16-byte aligned");
-    const size_t es = elem_size(shape->in_dtype), rows = (size_t)BH * shape->N;
-    const size_t nk = rows * shape->d_k * es, nv = rows * shape->d_v * es;
-    const size_t in_sz[] = {nk, nk, nv, nv, nv};
-    const size_t out_sz[] = {nk, nk, nv};
-    for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 5; ++i)
-            if (overlaps(outs[o], out_sz[o], ins[i], in_sz[i]))
-                return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must not alias q, k, v, y or dy");
-        for (int o2 = 0; o2 < o; ++o2)
-            if (overlaps(outs[o], out_sz[o], outs[o2], out_sz[o2]))
-                return fail(LA_ERR_INVALID_ARGUMENT, "dq, dk, dv must not overlap");
-    }
+    const size_t rows = (size_t)BH * shape->N;
+    if ((st = check_bwd_io(q, k, v, y, dy, dq, dk, dv, shape, rows, rows)) != LA_OK) return st;
     const BwdPlan plan = bwd_plan(shape, F, bent->C);
     if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.bytes);
     if (workspace_bytes < plan.bytes)
@@ -1113,6 +1127,157 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         if ((e = launch(LA_KERNEL_BWD_KV, [&] { return bent->bwd(bk, BMODE_KV, strm); })) != hipSuccess)
             return hip_fail(e, "backward: dk dv launch");
     }
+    return ok();
+}
+
+namespace {
+
+// Segments of the non-causal backward: the keys' state sums (forward chunk
+// Cf), the query sweep and the key sweep (backward chunk Cb); the workspace
+// holds the state slots [Pk][BH][SZ] and the adjoint slots [Pq][BH][SZ]
+// (slot 0 of each ends as the total).
+struct CrossBwdPlan {
+    int Pk, Pq, Pv;
+    int64_t cpsk, cpsq, cpsv, SZ;
+    size_t state_floats, adj_floats, bytes;
+};
+
+CrossBwdPlan cross_bwd_plan(const la_shape* s, int64_t n_kv, int F, int Cf, int Cb)
+{
+    CrossBwdPlan p;
+    const int64_t BH = s->B * s->H;
+    cut_segments((n_kv + Cf - 1) / Cf, BH, &p.Pk, &p.cpsk);
+    cut_segments((s->N + Cb - 1) / Cb, BH, &p.Pq, &p.cpsq);
+    cut_segments((n_kv + Cb - 1) / Cb, BH, &p.Pv, &p.cpsv);
+    p.SZ = (int64_t)F * s->d_v + F;
+    p.state_floats = round256((size_t)p.Pk * BH * p.SZ);
+    p.adj_floats = round256((size_t)p.Pq * BH * p.SZ);
+    p.bytes = (p.state_floats + p.adj_floats) * sizeof(float);
+    return p;
+}
+
+}  // namespace
+
+size_t la_workspace_size_backward_cross(const la_shape* shape, int64_t n_kv, const la_phi* phi)
+{
+    int F = 0;
+    const KernelEntry* e = nullptr;
+    const BwdEntry* be = nullptr;
+    const std::string saved = g_last_error;
+    const la_status st = check_backward(shape, phi, &F, &e, &be);
+    g_last_error = saved;
+    if (st != LA_OK || shape->N < 1 || n_kv < 1 || n_kv > INT64_MAX / 4) return 0;
+    return cross_bwd_plan(shape, n_kv, F, e->C, be->C).bytes;
+}
+
+la_status la_backward_cross(const void* q, const void* k, const void* v, const void* y, const void* dy,
+                            void* dq, void* dk, void* dv, const la_shape* shape, int64_t n_kv,
+                            const uint8_t* key_padding_mask, const la_phi* phi, float eps,
+                            void* workspace, size_t workspace_bytes, la_stream_t stream)
+{
+    int F = 0;
+    const KernelEntry* ent = nullptr;
+    const BwdEntry* bent = nullptr;
+    la_status st = check_backward(shape, phi, &F, &ent, &bent);
+    if (st != LA_OK) return st;
+    if (shape->N < 1) return fail(LA_ERR_INVALID_ARGUMENT, "N must be >= 1");
+    if (n_kv < 1 || n_kv > INT64_MAX / 4) return fail(LA_ERR_INVALID_ARGUMENT, "n_kv=%lld must be >= 1", (long long)n_kv);
+    if ((st = check_eps(eps)) != LA_OK) return st;
+    const int64_t BH = shape->B * shape->H;
+    if (BH > 65535) return fail(LA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)BH);
+    if ((st = check_bwd_io(q, k, v, y, dy, dq, dk, dv, shape, (size_t)BH * shape->N, (size_t)BH * n_kv)) != LA_OK)
+        return st;
+    const CrossBwdPlan plan = cross_bwd_plan(shape, n_kv, F, ent->C, bent->C);
+    if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.bytes);
+    if (workspace_bytes < plan.bytes)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.bytes, workspace_bytes);
+    if (!aligned16(workspace)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    float* sws = static_cast<float*>(workspace);
+    float* aws = sws + plan.state_floats;
+    const int64_t FD = (int64_t)F * shape->d_v;
+    LamTable ones;
+    make_lam(nullptr, shape->H, &ones);  // no decay in the non-causal form
+    hipError_t e;
+
+    // total state over the kept keys: segment sums, then their sum into slot 0
+    FwdArgs l;
+    std::memset(&l, 0, sizeof(l));
+    l.q = q;
+    l.k = k;
+    l.v = v;
+    l.N = n_kv;
+    l.n_len = n_kv;
+    l.BH = (int32_t)BH;
+    l.H = (int32_t)shape->H;
+    l.P = plan.Pk;
+    l.cps = plan.cpsk;
+    l.eps = eps;
+    l.qk_scale = 1.0f;
+    l.kpm = key_padding_mask;
+    l.kpm_stride = n_kv;
+    l.lam = ones;
+    l.S_dst = sws;
+    l.z_dst = sws + FD;
+    l.dst_stride = plan.SZ;
+    l.dst_zstride = plan.SZ;
+    if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
+        return hip_fail(e, "cross backward: state sum launch");
+    ScanArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.BH = (int32_t)BH;
+    sa.H = (int32_t)shape->H;
+    sa.F = F;
+    sa.DV = shape->d_v;
+    sa.causal = 0;
+    sa.lam = ones;
+    if (plan.Pk > 1) {
+        sa.ws = sws;
+        sa.P = plan.Pk;
+        if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+            return hip_fail(e, "cross backward: state reduction launch");
+    }
+    // query sweep: dq, and the segments' adjoint sums
+    BwdArgs b;
+    std::memset(&b, 0, sizeof(b));
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.y = y;
+    b.gy = dy;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.BH = (int32_t)BH;
+    b.H = (int32_t)shape->H;
+    b.eps = eps;
+    b.lam = ones;
+    BwdArgs bq = b;
+    bq.N = shape->N;
+    bq.P = plan.Pq;
+    bq.cps = plan.cpsq;
+    bq.S_src = sws; bq.z_src = sws + FD;
+    bq.src_stride = plan.SZ; bq.src_zstride = plan.SZ; bq.src_seg_stride = 0;
+    bq.S_dst = aws; bq.z_dst = aws + FD;
+    bq.dst_stride = plan.SZ; bq.dst_zstride = plan.SZ;
+    if ((e = launch(LA_KERNEL_BWD_NCQ, [&] { return bent->bwd(bq, BMODE_NCQ, strm); })) != hipSuccess)
+        return hip_fail(e, "cross backward: dq launch");
+    if (plan.Pq > 1) {
+        sa.ws = aws;
+        sa.P = plan.Pq;
+        if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
+            return hip_fail(e, "cross backward: adjoint reduction launch");
+    }
+    // key sweep: dk, dv from the total adjoint
+    BwdArgs bk = b;
+    bk.N = n_kv;
+    bk.P = plan.Pv;
+    bk.cps = plan.cpsv;
+    bk.kpm = key_padding_mask;
+    bk.S_src = aws; bk.z_src = aws + FD;
+    bk.src_stride = plan.SZ; bk.src_zstride = plan.SZ; bk.src_seg_stride = 0;
+    if ((e = launch(LA_KERNEL_BWD_NCKV, [&] { return bent->bwd(bk, BMODE_NCKV, strm); })) != hipSuccess)
+        return hip_fail(e, "cross backward: dk dv launch");
     return ok();
 }
 

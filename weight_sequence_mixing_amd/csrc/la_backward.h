@@ -38,6 +38,15 @@
 // (dq, dk) or value blocks (dv).  The state is multiplied by lambda^n once a
 // chunk (no deferred scale: lambda <= 1, so nothing overflows).
 //
+// The non-causal form (cross attention: N queries against M keys, "From
+// standard attention to linear attention" sec. 2, 3 and 6) holds one state
+// S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j) for every query, so both sweeps
+// lose their score tiles and their carries: the query sweep reads the total
+// state (d phi(q_i) = S dnum_i + z dden_i) and sums the adjoint
+// U = sum_i phi(q_i) dnum_i^T, u = sum_i phi(q_i) dden_i over its segment;
+// the key sweep reads the total adjoint (d phi(k_j) = U v_j + u,
+// dv_j = U^T phi(k_j)).
+//
 // The feature maps' derivatives come from the staged features themselves:
 // elu+1: phi'(x) = 1 for x > 0 and e^x = phi(x) otherwise, i.e. min(phi(x), 1);
 // ReLU: phi'(x) = [phi(x) > 0].
@@ -133,9 +142,14 @@ constexpr bool bwd_dlam_fits() { return BwdCfg<T, DK, F, DV, 32, 4, BMODE_Q, tru
 //            + sum_{j<=i} (i-j) lambda^(i-j-1) A_ij B_ij
 //   T <- lambda^n T + n lambda^(n-1) S + sum_j (n-1-j) lambda^(n-2-j) phi(k_j) [v_j, 1]^T
 // (the product rule on the chunk's recurrence, with S, T before the chunk).
-template <class T, int PHI, int DK, int F, int DV, int C, int NW, bool DL>
+// NC: the non-causal form -- the state read at S_src is the total for every
+// query (no score tiles, no carry), and the adjoint sums
+// sum_i phi(q_i) [dnum_i, dden_i]^T over the segment go to S_dst / z_dst at
+// (seg*BH + bh)*dst_stride.
+template <class T, int PHI, int DK, int F, int DV, int C, int NW, bool DL, bool NC = false>
 __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 {
+    static_assert(!(DL && NC), "no decay in the non-causal form");
     using Cfg = BwdCfg<T, DK, F, DV, C, NW, BMODE_Q, DL>;
     using TF = TileL<T, F>;
     using TVL = TileL<T, DV>;
@@ -153,13 +167,15 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
     T* const sY = (T*)(smem + Cfg::OFF_V2);
     T* const sS = (T*)(smem + Cfg::OFF_S);
     T* const sT = (T*)(smem + Cfg::OFF_T);
+    T* const sDN = sV;  // NC: dnum rows (no values are staged)
+    float* const sDD = (float*)(smem + Cfg::OFF_R);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
-    const float l2l = a.lam.log2lam[h];
-    const int64_t NC = (a.N + C - 1) / C;
-    const int64_t c_beg = (int64_t)seg * a.cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + a.cps);
+    const float l2l = NC ? 0.f : a.lam.log2lam[h];
+    const int64_t nch = (a.N + C - 1) / C;
+    const int64_t c_beg = (int64_t)seg * a.cps, c_end = (seg == a.P - 1) ? nch : min(nch, c_beg + a.cps);
     const int64_t row0 = (int64_t)bh * a.N;
     const T* qg = (const T*)a.q + row0 * DK;
     const T* kg = (const T*)a.k + row0 * DK;
@@ -227,6 +243,18 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
             }
     };
 
+    // NC: the total state is published once; its registers then sum the adjoint
+    f32x4 accu[NC ? FB : 1];
+#pragma unroll
+    for (int fb = 0; fb < (NC ? FB : 1); ++fb) accu[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NC) {
+        publish();
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int t = 0; t < DBW; ++t) accS[fb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     uint4 rq[RQ], rk[RQ], rv[RV], rg[RV], ry[RV];
     int mk[RQ];
     for (int64_t c = c_beg; c < c_end; ++c) {
@@ -237,42 +265,45 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
         for (int r = 0; r < RQ; ++r) {
             const int idx = tid + r * NT, j = min(idx / VPRQ, n - 1), c4 = idx % VPRQ;
             rq[r] = *(const uint4*)(qg + (t0 + j) * DK + c4 * VEC);
-            rk[r] = *(const uint4*)(kg + (t0 + j) * DK + c4 * VEC);
-            mk[r] = kp ? (int)kp[t0 + j] : 0;
+            if constexpr (!NC) {
+                rk[r] = *(const uint4*)(kg + (t0 + j) * DK + c4 * VEC);
+                mk[r] = kp ? (int)kp[t0 + j] : 0;
+            }
         }
 #pragma unroll
         for (int r = 0; r < RV; ++r) {
             const int idx = tid + r * NT, j = min(idx / VPRV, n - 1), c4 = idx % VPRV;
-            rv[r] = *(const uint4*)(vg + (t0 + j) * DV + c4 * VEC);
+            if constexpr (!NC) rv[r] = *(const uint4*)(vg + (t0 + j) * DV + c4 * VEC);
             rg[r] = *(const uint4*)(gg + (t0 + j) * DV + c4 * VEC);
             ry[r] = *(const uint4*)(yg + (t0 + j) * DV + c4 * VEC);
         }
         // ---- publish the state and stage the chunk (the previous chunk's
         // reads of both ended at its closing barrier)
-        publish();
+        if constexpr (!NC) publish();
 #pragma unroll
         for (int r = 0; r < RQ; ++r) {
             const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
-            float xq[VEC], xk[VEC], pq[VEC], pk[VEC];
+            float xq[VEC], pq[VEC];
             unpack16(rq[r], xq, (const T*)nullptr);
-            unpack16(rk[r], xk, (const T*)nullptr);
-            const bool dead = j >= n || mk[r];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                pq[e] = j < n ? phi_elem<T, PHI>(xq[e]) : 0.f;
-                pk[e] = dead ? 0.f : phi_elem<T, PHI>(xk[e]);
-            }
+            for (int e = 0; e < VEC; ++e) pq[e] = j < n ? phi_elem<T, PHI>(xq[e]) : 0.f;
 #pragma unroll
-            for (int e = 0; e < VEC; e += 4) {
-                st4(sQ + TF::off(j, cg * VEC + e), pq[e], pq[e + 1], pq[e + 2], pq[e + 3]);
-                st4(sK + TF::off(j, cg * VEC + e), pk[e], pk[e + 1], pk[e + 2], pk[e + 3]);
+            for (int e = 0; e < VEC; e += 4) st4(sQ + TF::off(j, cg * VEC + e), pq[e], pq[e + 1], pq[e + 2], pq[e + 3]);
+            if constexpr (!NC) {
+                float xk[VEC], pk[VEC];
+                unpack16(rk[r], xk, (const T*)nullptr);
+                const bool dead = j >= n || mk[r];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) pk[e] = dead ? 0.f : phi_elem<T, PHI>(xk[e]);
+#pragma unroll
+                for (int e = 0; e < VEC; e += 4) st4(sK + TF::off(j, cg * VEC + e), pk[e], pk[e + 1], pk[e + 2], pk[e + 3]);
             }
         }
 #pragma unroll
         for (int r = 0; r < RV; ++r) {
             const int idx = tid + r * NT, j = idx / VPRV, cg = idx % VPRV;
             float xv[VEC], xg[VEC], xy[VEC];
-            unpack16(rv[r], xv, (const T*)nullptr);
+            if constexpr (!NC) unpack16(rv[r], xv, (const T*)nullptr);
             unpack16(rg[r], xg, (const T*)nullptr);
             unpack16(ry[r], xy, (const T*)nullptr);
 #pragma unroll
@@ -285,7 +316,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
             }
 #pragma unroll
             for (int e = 0; e < VEC; e += 4) {
-                st4(sV + TVL::off(j, cg * VEC + e), xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
+                if constexpr (!NC) st4(sV + TVL::off(j, cg * VEC + e), xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
                 st4(sG + TVL::off(j, cg * VEC + e), xg[e], xg[e + 1], xg[e + 2], xg[e + 3]);
                 st4(sY + TVL::off(j, cg * VEC + e), xy[e], xy[e + 1], xy[e + 2], xy[e + 3]);
             }
@@ -311,7 +342,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 #pragma unroll
             for (int jb = 0; jb < 2 * CB; ++jb) {
                 pt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (jb <= ib) {
+                if (!NC && jb <= ib) {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
                     if constexpr (DL) praw[jb] = pt[jb];
@@ -320,8 +351,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                 }
             }
             f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!NC) {
 #pragma unroll
-            for (int kb = 0; kb < CB; ++kb) mma(rs, ones, frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]));
+                for (int kb = 0; kb < CB; ++kb) mma(rs, ones, frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]));
+            }
             const float den = rs[0] + lqi * dz[0] + a.eps;
             const float rden = fast_rcp(den);
             // dnum_i as B operand fragments (k = value column, n = token i),
@@ -344,16 +377,21 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                     gy += lo[e] * y0[e] + hi[e] * y1[e];
                 }
                 dn[kb] = frag_acc<T>(lo, hi);
+                if (NC && wave == 0) {
+                    st4(sDN + TVL::off(i, 32 * kb + 4 * g), lo[0], lo[1], lo[2], lo[3]);
+                    st4(sDN + TVL::off(i, 32 * kb + 16 + 4 * g), hi[0], hi[1], hi[2], hi[3]);
+                }
             }
             gy += __shfl_xor(gy, 16, 64);
             gy += __shfl_xor(gy, 32, 64);
             const float dden = -gy;
+            if (NC && wave == 0 && g == 0) sDD[i] = dden;
             // B^T tiles (rows j, column i): v_j . dnum_i + dden_i, decayed
             f32x4 bt[2 * CB];
 #pragma unroll
             for (int jb = 0; jb < 2 * CB; ++jb) {
                 bt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (jb <= ib) {
+                if (!NC && jb <= ib) {
 #pragma unroll
                     for (int kb = 0; kb < VB; ++kb) mma(bt[jb], lds_frag_row<T, DV>(sV, 16 * jb + l16, kb, g), dn[kb]);
 #pragma unroll
@@ -378,8 +416,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                 f32x4 inter = {0.f, 0.f, 0.f, 0.f}, intra = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < VB; ++kb) mma(inter, lds_frag_row<T, DV>(sS, 16 * fb + l16, kb, g), dn[kb]);
+                if constexpr (!NC) {
 #pragma unroll
-                for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, F>::get(sK, 32 * kb, 16 * fb, lane), bf[kb]);
+                    for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, F>::get(sK, 32 * kb, 16 * fb, lane), bf[kb]);
+                }
                 if constexpr (DL) {
                     // phi(q_i).(S dnum_i + z dden_i) and phi(q_i).(T dnum_i + t dden_i) over
                     // this wave's feature rows (phi(q) = 0 past the chunk's end)
@@ -407,7 +447,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                     st4((T*)a.dq + (row0 + t0 + i) * DK + 16 * fb + 4 * g, o[0], o[1], o[2], o[3]);
                 }
             }
-            if (wave == 0 && g == 0 && i < n) {
+            if (!NC && wave == 0 && g == 0 && i < n) {
                 float* tp = a.tok + (row0 + t0 + i) * 2;
                 tp[0] = rden;
                 tp[1] = dden;
@@ -446,6 +486,27 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                 }
             }
         }
+        if constexpr (NC) {
+            // ---- adjoint sums: U += phi(Q)^T dnum, u += phi(Q)^T dden (rows of wave 0)
+            __syncthreads();
+            Frag<T> ddf[CB];
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb)
+                ddf[kb] = frag_acc<T>(*(const f32x4*)(sDD + 32 * kb + 4 * g), *(const f32x4*)(sDD + 32 * kb + 16 + 4 * g));
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) {
+                    const Frag<T> qf = ColRead<T, F>::get(sQ, 32 * kb, 16 * fb, lane);
+#pragma unroll
+                    for (int t = 0; t < DBW; ++t)
+                        mma(accS[fb][t], qf, ColRead<T, DV>::get(sDN, 32 * kb, 16 * (wave * DBW + t), lane));
+                    mma(accu[fb], qf, ddf[kb]);
+                }
+            }
+            __syncthreads();  // every wave has read the chunk's tiles
+            continue;
+        }
         // ---- state carry: S <- lambda^n S + phi(K)^T (w V), z <- lambda^n z + phi(K)^T w,
         // w_j = lambda^(n-1-j), applied to the V fragments in registers
         const float ln = lam_pow(l2l, n);
@@ -480,6 +541,20 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
         __syncthreads();  // every wave has read sS before it is republished
     }
 
+    if constexpr (NC) {
+        float* Sd = a.S_dst + ((int64_t)seg * a.BH + bh) * a.dst_stride;
+        float* zd = a.z_dst + ((int64_t)seg * a.BH + bh) * a.dst_zstride;
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+            for (int t = 0; t < DBW; ++t) {
+                const int d = 16 * (wave * DBW + t) + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sd[(16 * fb + 4 * g + r) * DV + d] = accS[fb][t][r];
+            }
+            if (wave == 0 && l16 == 0) *(f32x4*)(zd + 16 * fb + 4 * g) = accu[fb];
+        }
+    }
     if constexpr (DL) {
         // the segment's dT (start state held fixed) and its partial dlambda
         const int64_t slot = (int64_t)seg * a.BH + bh;
@@ -510,7 +585,8 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 
 // ---------------------------------------------------------------------------
 // Adjoint sweep (reverse chunk order): dk, dv (BMODE_KV) or the segment sums
-// of the adjoint (BMODE_RLOCAL).
+// of the adjoint (BMODE_RLOCAL); BMODE_NCKV: dk, dv of the non-causal form
+// from the total adjoint at S_src (keys only: no score tiles, no carry).
 template <class T, int PHI, int DK, int F, int DV, int C, int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
 {
@@ -518,6 +594,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
     using TF = TileL<T, F>;
     using TVL = TileL<T, DV>;
     constexpr bool RL = MODE == BMODE_RLOCAL;
+    constexpr bool NCK = MODE == BMODE_NCKV;
     constexpr int NT = Cfg::NT, VEC = Cfg::VEC, QB = Cfg::QB, CB = Cfg::CB, FB = Cfg::FB;
     constexpr int DBW = Cfg::DBW, FBW = Cfg::FBW;
     constexpr int KB = F / 32, VB = DV / 32;
@@ -536,7 +613,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
-    const float l2l = a.lam.log2lam[h];
+    const float l2l = NCK ? 0.f : a.lam.log2lam[h];
     const int64_t NC = (a.N + C - 1) / C;
     const int64_t c_beg = (int64_t)seg * a.cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + a.cps);
     const int64_t row0 = (int64_t)bh * a.N;
@@ -544,7 +621,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
     const T* kg = (const T*)a.k + row0 * DK;
     const T* vg = (const T*)a.v + row0 * DV;
     const T* gg = (const T*)a.gy + row0 * DV;
-    const float* tk = a.tok + row0 * 2;
+    const float* tk = NCK ? nullptr : a.tok + row0 * 2;
     const uint8_t* kp = a.kpm ? a.kpm + (int64_t)(bh / a.H) * a.N : nullptr;
 
     // decay of score element (i = 16 ib + 4 g + r, j = 16 jb + l16), i >= j
@@ -593,6 +670,8 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
             }
     };
 
+    if constexpr (NCK) publish();  // the total adjoint, read by every chunk
+
     uint4 rq[RQ], rk[RQ], rv[RV], rg[RV];
     int mk[RQ];
     for (int64_t c = c_end - 1; c >= c_beg; --c) {
@@ -601,7 +680,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
 #pragma unroll
         for (int r = 0; r < RQ; ++r) {
             const int idx = tid + r * NT, j = min(idx / VPRQ, n - 1), c4 = idx % VPRQ;
-            rq[r] = *(const uint4*)(qg + (t0 + j) * DK + c4 * VEC);
+            if constexpr (!NCK) rq[r] = *(const uint4*)(qg + (t0 + j) * DK + c4 * VEC);
             if constexpr (!RL) {
                 rk[r] = *(const uint4*)(kg + (t0 + j) * DK + c4 * VEC);
                 mk[r] = kp ? (int)kp[t0 + j] : 0;
@@ -612,26 +691,30 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
         for (int r = 0; r < RV; ++r) {
             const int idx = tid + r * NT, j = min(idx / VPRV, n - 1), c4 = idx % VPRV;
             if constexpr (!RL) rv[r] = *(const uint4*)(vg + (t0 + j) * DV + c4 * VEC);
-            rg[r] = *(const uint4*)(gg + (t0 + j) * DV + c4 * VEC);
-            rden_r[r] = tk[(t0 + j) * 2];
-            dd_r[r] = tk[(t0 + j) * 2 + 1];
+            if constexpr (!NCK) {
+                rg[r] = *(const uint4*)(gg + (t0 + j) * DV + c4 * VEC);
+                rden_r[r] = tk[(t0 + j) * 2];
+                dd_r[r] = tk[(t0 + j) * 2 + 1];
+            }
         }
-        if constexpr (!RL) publish();
+        if constexpr (!RL && !NCK) publish();
 #pragma unroll
         for (int r = 0; r < RQ; ++r) {
             const int idx = tid + r * NT, j = idx / VPRQ, cg = idx % VPRQ;
-            float xq[VEC], pq[VEC], pw[VEC];
-            unpack16(rq[r], xq, (const T*)nullptr);
-            const float w = j < n ? lam_pow(l2l, j + 1) : 0.f;
+            if constexpr (!NCK) {
+                float xq[VEC], pq[VEC], pw[VEC];
+                unpack16(rq[r], xq, (const T*)nullptr);
+                const float w = j < n ? lam_pow(l2l, j + 1) : 0.f;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                pq[e] = j < n ? phi_elem<T, PHI>(xq[e]) : 0.f;
-                pw[e] = pq[e] * w;
-            }
+                for (int e = 0; e < VEC; ++e) {
+                    pq[e] = j < n ? phi_elem<T, PHI>(xq[e]) : 0.f;
+                    pw[e] = pq[e] * w;
+                }
 #pragma unroll
-            for (int e = 0; e < VEC; e += 4) {
-                if constexpr (!RL) st4(sQ + TF::off(j, cg * VEC + e), pq[e], pq[e + 1], pq[e + 2], pq[e + 3]);
-                st4(sQw + TF::off(j, cg * VEC + e), pw[e], pw[e + 1], pw[e + 2], pw[e + 3]);
+                for (int e = 0; e < VEC; e += 4) {
+                    if constexpr (!RL) st4(sQ + TF::off(j, cg * VEC + e), pq[e], pq[e + 1], pq[e + 2], pq[e + 3]);
+                    st4(sQw + TF::off(j, cg * VEC + e), pw[e], pw[e + 1], pw[e + 2], pw[e + 3]);
+                }
             }
             if constexpr (!RL) {
                 float xk[VEC], pk[VEC];
@@ -646,12 +729,14 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
 #pragma unroll
         for (int r = 0; r < RV; ++r) {
             const int idx = tid + r * NT, j = idx / VPRV, cg = idx % VPRV;
-            float xg[VEC];
-            unpack16(rg[r], xg, (const T*)nullptr);
+            if constexpr (!NCK) {
+                float xg[VEC];
+                unpack16(rg[r], xg, (const T*)nullptr);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) xg[e] = j < n ? xg[e] * rden_r[r] : 0.f;
+                for (int e = 0; e < VEC; ++e) xg[e] = j < n ? xg[e] * rden_r[r] : 0.f;
 #pragma unroll
-            for (int e = 0; e < VEC; e += 4) st4(sDN + TVL::off(j, cg * VEC + e), xg[e], xg[e + 1], xg[e + 2], xg[e + 3]);
+                for (int e = 0; e < VEC; e += 4) st4(sDN + TVL::off(j, cg * VEC + e), xg[e], xg[e + 1], xg[e + 2], xg[e + 3]);
+            }
             if constexpr (!RL) {
                 float xv[VEC];
                 unpack16(rv[r], xv, (const T*)nullptr);
@@ -660,7 +745,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4) st4(sV + TVL::off(j, cg * VEC + e), xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
             }
-            if (cg == 0) sDD[j] = j < n ? dd_r[r] : 0.f;
+            if (!NCK && cg == 0) sDD[j] = j < n ? dd_r[r] : 0.f;
         }
         __syncthreads();
 
@@ -669,7 +754,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
 #pragma unroll
             for (int jb = 0; jb < QB; ++jb) {
                 const int j = 16 * jb + l16;
-                const float lj = lam_pow(l2l, max(n - 1 - j, 0));  // the carried adjoint's decay for key j
+                const float lj = NCK ? 1.f : lam_pow(l2l, max(n - 1 - j, 0));  // the carried adjoint's decay for key j
                 Frag<T> kf[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) kf[kb] = lds_frag_row<T, F>(sK, j, kb, g);
@@ -681,7 +766,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
                 for (int ib = 0; ib < 2 * CB; ++ib) {
                     at[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
                     bt[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (ib >= jb) {
+                    if (!NCK && ib >= jb) {
 #pragma unroll
                         for (int kb = 0; kb < KB; ++kb) mma(at[ib], lds_frag_row<T, F>(sQ, 16 * ib + l16, kb, g), kf[kb]);
 #pragma unroll
@@ -705,8 +790,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
                 for (int t = 0; t < DBW; ++t) {
                     const int d0 = 16 * (wave * DBW + t);
                     f32x4 intra = {0.f, 0.f, 0.f, 0.f}, inter = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!NCK) {
 #pragma unroll
-                    for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, DV>::get(sDN, 32 * kb, d0, lane), af[kb]);
+                        for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, DV>::get(sDN, 32 * kb, d0, lane), af[kb]);
+                    }
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) mma(inter, frag_acc<T>(accU[2 * kb][t], accU[2 * kb + 1][t]), kf[kb]);
                     if (j < n) {
@@ -719,8 +806,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
                 for (int u = 0; u < FBW; ++u) {
                     const int fb = wave * FBW + u;
                     f32x4 intra = {0.f, 0.f, 0.f, 0.f}, inter = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!NCK) {
 #pragma unroll
-                    for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, F>::get(sQ, 32 * kb, 16 * fb, lane), bf[kb]);
+                        for (int kb = 0; kb < CB; ++kb) mma(intra, ColRead<T, F>::get(sQ, 32 * kb, 16 * fb, lane), bf[kb]);
+                    }
 #pragma unroll
                     for (int kb = 0; kb < VB; ++kb) mma(inter, lds_frag_row<T, DV>(sU, 16 * fb + l16, kb, g), vfr[kb]);
                     if (j < n) {
@@ -737,6 +826,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
             }
         }
 
+        if constexpr (NCK) {
+            __syncthreads();  // every wave has read the chunk's tiles
+            continue;
+        }
         // ---- adjoint carry: W <- lambda^n W + (w phi(Q))^T dnum, w_i = lambda^(i+1); u likewise with dden
         const float ln = lam_pow(l2l, n);
         Frag<T> ddf[CB];
@@ -766,7 +859,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
     if constexpr (RL) {
         Sd = a.S_dst + ((int64_t)seg * a.BH + bh) * a.dst_stride;
         zd = a.z_dst + ((int64_t)seg * a.BH + bh) * a.dst_zstride;
-    } else if (a.S_dst) {
+    } else if (!NCK && a.S_dst) {
         Sd = a.S_dst + (int64_t)bh * a.dst_stride;
         zd = a.z_dst + (int64_t)bh * a.dst_zstride;
     }
@@ -800,6 +893,10 @@ hipError_t bwd_launch(const BwdArgs& a, int mode, hipStream_t stream)
         return launch_kernel(la_bwd_q_kernel<T, PHI, DK, F, DV, C, NW, false>, grid, block, stream, a);
     case BMODE_RLOCAL:
         return launch_kernel(la_bwd_kv_kernel<T, PHI, DK, F, DV, C, NW, BMODE_RLOCAL>, grid, block, stream, a);
+    case BMODE_NCQ:
+        return launch_kernel(la_bwd_q_kernel<T, PHI, DK, F, DV, C, NW, false, true>, grid, block, stream, a);
+    case BMODE_NCKV:
+        return launch_kernel(la_bwd_kv_kernel<T, PHI, DK, F, DV, C, NW, BMODE_NCKV>, grid, block, stream, a);
     default:
         return launch_kernel(la_bwd_kv_kernel<T, PHI, DK, F, DV, C, NW, BMODE_KV>, grid, block, stream, a);
     }

@@ -159,6 +159,8 @@ enum BwdMode : int {
     BMODE_Q = 0,       // dq, and 1/den, dden per token
     BMODE_RLOCAL = 1,  // segment sums of lambda^(i-s0) phi(q_i) [dnum_i, dden_i]^T
     BMODE_KV = 2,      // dk, dv from the carried adjoint
+    BMODE_NCQ = 3,     // non-causal: dq from the total state, segment sums of phi(q_i) [dnum_i, dden_i]^T
+    BMODE_NCKV = 4,    // non-causal: dk, dv from the total adjoint
 };
 
 struct DecArgs {
