@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -374,6 +375,43 @@ def cross_w2(ctx, steps=200):
     return res
 
 
+def cross_backward_w2(ctx, steps=100):
+    """Backward of the cross-attention line (1024 queries against 4096
+    right-padded keys per (batch, head), B = 4, H = 8, d = 64 bf16): one
+    la_backward_cross call -- the keys' state sums and their reduction, the
+    query sweep (dq and the adjoint's segment sums), the adjoint reduction,
+    the key sweep (dk, dv)."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    B, H, Nq, Nk, d = 4, 8, 1024, 4096, 64
+    wl, (k, v, _) = _w2_inputs(ctx, B, H, Nk)
+    _, (q, _, _) = _w2_inputs(ctx, B, H, Nq, seed=12)
+    mask = torch.from_numpy(si.make_key_padding_mask(B, Nk, "right", seed=2)).to(ctx.dev)
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(23)
+    dy = device_normal(torch, g, (B, H, Nq, d), 0.5, ctx.dev)
+    y = torch.empty_like(q)
+    la.la_forward_cross(q, k, v, y, mask, eps=wl.eps)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(la.la_workspace_size_backward_cross(B, H, Nq, Nk, d, d), dtype=torch.uint8, device=ctx.dev)
+    SZ = d * d + d
+    P = max(1, -(-512 // (B * H)))  # segments of every pass at this shape (>= P chunks each way)
+    ids = la.KERNEL_IDS
+    kb = {ids["fwd_local"]: B * H * Nk * 2 * d * 2 + B * Nk + P * B * H * SZ * 4,
+          ids["bwd_ncq"]: B * H * Nq * 4 * d * 2 + 2 * P * B * H * SZ * 4,
+          ids["bwd_nckv"]: B * H * Nk * 4 * d * 2 + B * Nk + P * B * H * SZ * 4,
+          ids["scan"]: (P + 1) * B * H * SZ * 4}
+
+    def step():
+        la.la_backward_cross(q, k, v, y, dy, dq, dk, dv, mask, eps=wl.eps, workspace=ws)
+
+    name = "elu1_cross_backward_masked_B%d_H%d_Nq%d_Nk%d_d%d_bf16" % (B, H, Nq, Nk, d)
+    res = bench_call(ctx, name, step, B * Nq, kb, steps, max(ctx.warmup, 5))
+    res["key_Mtokens_per_s"] = round(B * Nk / (res["ms_per_step"] * 1e-3) / 1e6, 2)
+    res["segments"] = P
+    return res
+
+
 def backward_w2(ctx, steps=100, with_dlam=False):
     """Backward of the headline forward (B=4 H=8 N=4096 d=64 bf16, lambda = 1):
     one la_backward_causal call -- forward segment states and scan, the dq
@@ -414,7 +452,8 @@ def backward_w2(ctx, steps=100, with_dlam=False):
 
 # Mask / cross / packed / backward lines measured beside the main workloads
 SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2),
-                  ("backward_w2", backward_w2), ("backward_dlam_w2", lambda c: backward_w2(c, with_dlam=True)))
+                  ("backward_w2", backward_w2), ("backward_dlam_w2", lambda c: backward_w2(c, with_dlam=True)),
+                  ("cross_backward_w2", cross_backward_w2))
 
 
 def workload4_decode(ctx, steps=1024):
@@ -552,6 +591,9 @@ def _kernel_label(mangled):
     if "la_copy_kernel" in mangled:
         return "la_copy_kernel"
     if "la_bwd_q_kernel" in mangled:
+        # the last bool template argument: the non-causal variant
+        if re.search(r"Lb1EE+vNS_7BwdArgsE", mangled) or mangled.split(">(")[0].rstrip().endswith("true"):
+            return "la_bwd_q_kernel (non-causal)"
         return "la_bwd_q_kernel"
     if "la_bwd_kv_kernel" in mangled:
         # the mode is the last int template argument
@@ -560,7 +602,8 @@ def _kernel_label(mangled):
         else:
             ints = [x.strip() for x in mangled.split(">(")[0].split(",") if x.strip().lstrip("-").isdigit()]
             mode = ints[-1] if ints else ""
-        return {"1": "la_bwd_kv_kernel (adjoint segment)", "2": "la_bwd_kv_kernel (dk dv)"}.get(mode, "la_bwd_kv_kernel")
+        return {"1": "la_bwd_kv_kernel (adjoint segment)", "2": "la_bwd_kv_kernel (dk dv)",
+                "4": "la_bwd_kv_kernel (non-causal dk dv)"}.get(mode, "la_bwd_kv_kernel")
     if "la_decode_kernel" in mangled:
         return "la_decode_kernel"
     if "la_scan_kernel" in mangled:
