@@ -108,10 +108,24 @@ struct FwdCfg {
     static constexpr size_t SZ_XK = (RF && NEED_K) ? size_t(C) * XLD * sizeof(T) : 0;
     static constexpr size_t OFF_XN = al(OFF_XK + SZ_XK);
     static constexpr size_t SZ_XN = RF ? size_t(2) * C * sizeof(float) : 0;
-    // the normaliser z after each chunk, double buffered (fp32, MODE_CAUSAL)
+    // Random features with bf16 inputs: omega enters the matrix cores as bf16
+    // high and low parts (SPLIT).  z is published after each chunk as bf16
+    // operand values and read where it is used (ZB16), and for F <= 128
+    // omega's operand fragments live in LDS instead of registers (OMLDS),
+    // which lets two workgroups share a compute unit.  At F = 256 the LDS
+    // tiles alone allow one workgroup per compute unit; there the fragments
+    // stay in registers (measured faster than LDS reads).
+    static constexpr bool SPLIT = RF && sizeof(T) == 2;
+    static constexpr bool OMLDS = SPLIT && F <= 128;
+    static constexpr bool ZB16 = SPLIT && NEED_Q && NEED_K;
+    // the normaliser z after each chunk, double buffered (MODE_CAUSAL; fp32,
+    // or bf16 with ZB16)
     static constexpr size_t OFF_Z = al(OFF_XN + SZ_XN);
-    static constexpr size_t SZ_Z = (NEED_Q && NEED_K) ? size_t(2) * F * sizeof(float) : 0;
-    static constexpr size_t TOTAL = al(OFF_Z + SZ_Z);
+    static constexpr size_t SZ_Z = (NEED_Q && NEED_K) ? size_t(2) * F * (ZB16 ? 2 : sizeof(float)) : 0;
+    // omega fragments: [row block][k block][high, low][lane], 16 bytes each
+    static constexpr size_t OFF_OM = al(OFF_Z + SZ_Z);
+    static constexpr size_t SZ_OM = OMLDS ? size_t(M / 16) * (DK / 32) * 2 * 64 * 16 : 0;
+    static constexpr size_t TOTAL = al(OFF_OM + SZ_OM);
     // random features: each wave computes the feature blocks of one 16-token
     // block (ib = wave % QB) for TPW 16-row blocks of omega, whose operand
     // fragments it keeps in registers
@@ -159,6 +173,8 @@ la_fwd_kernel(const FwdArgs a)
     T* const sXk = (T*)(smem + Cfg::OFF_XK);
     float* const sXn = (float*)(smem + Cfg::OFF_XN);
     float* const sZ = (float*)(smem + Cfg::OFF_Z);
+    bf16* const sZb = (bf16*)(smem + Cfg::OFF_Z);
+    Frag<T>* const sOm = (Frag<T>*)(smem + Cfg::OFF_OM);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
@@ -220,7 +236,12 @@ la_fwd_kernel(const FwdArgs a)
     // the whole workgroup: rows 16 rb.. of omega (rb = wave / QB + (NW / QB) u),
     // as bf16 high and low parts for bf16 inputs (omega = hi + lo to 16 bits)
     constexpr int TPW = Cfg::TPW, KX = Cfg::KX;
-    Frag<T> om_hi[TPW][KX], om_lo[sizeof(T) == 2 ? TPW : 1][KX];
+    // bf16 inputs: omega is scaled by qk_scale / (2 pi) before the split, so
+    // that the products are the angles in revolutions, the unit of the
+    // hardware sine and cosine; fp32 inputs keep radians for sincosf
+    constexpr bool REV = sizeof(T) == 2;
+    const float om_scale = REV ? qs * 0.159154943091895336f : 1.f;
+    Frag<T> om_hi[Cfg::OMLDS ? 1 : TPW][KX], om_lo[(Cfg::SPLIT && !Cfg::OMLDS) ? TPW : 1][KX];
     if constexpr (RF) {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
@@ -228,20 +249,43 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int kb = 0; kb < KX; ++kb) {
                 const float* p = a.omega + (int64_t)(16 * rb + l16) * DK + 32 * kb + 4 * g;
-                const f32x4 w0 = *(const f32x4*)p, w1 = *(const f32x4*)(p + 16);
-                om_hi[u][kb] = frag_acc<T>(w0, w1);
-                if constexpr (sizeof(T) == 2) {
+                const f32x4 w0 = *(const f32x4*)p * om_scale, w1 = *(const f32x4*)(p + 16) * om_scale;
+                const Frag<T> hi = frag_acc<T>(w0, w1);
+                if constexpr (Cfg::SPLIT) {
                     f32x4 r0, r1;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         r0[e] = w0[e] - (float)(bf16)w0[e];
                         r1[e] = w1[e] - (float)(bf16)w1[e];
                     }
-                    om_lo[u][kb] = frag_acc<T>(r0, r1);
+                    const Frag<T> lo = frag_acc<T>(r0, r1);
+                    if constexpr (Cfg::OMLDS) {
+                        // waves of the same row blocks hold the same
+                        // fragments; one of them stores (read after the
+                        // first barrier)
+                        if (wave % QB == 0) {
+                            sOm[((rb * KX + kb) * 2 + 0) * 64 + lane] = hi;
+                            sOm[((rb * KX + kb) * 2 + 1) * 64 + lane] = lo;
+                        }
+                    } else {
+                        om_hi[u][kb] = hi;
+                        om_lo[u][kb] = lo;
+                    }
+                } else {
+                    om_hi[u][kb] = hi;
                 }
             }
         }
     }
+    // operand fragment of omega rows 16 rb.. (high or low part)
+    auto omega_frag = [&](int u, int kb, int part) LA_INLINE {
+        if constexpr (Cfg::OMLDS) {
+            const int rb = wave / QB + (NW / QB) * u;
+            return sOm[((rb * KX + kb) * 2 + part) * 64 + lane];
+        } else {
+            return part ? om_lo[(Cfg::SPLIT && !Cfg::OMLDS) ? u : 0][kb] : om_hi[u][kb];
+        }
+    };
 
     // ---- global -> register prefetch of one chunk.  A full chunk is read at
     // fixed per-thread offsets from a uniform base.  In a ragged last chunk,
@@ -299,9 +343,9 @@ la_fwd_kernel(const FwdArgs a)
     for (int u = 0; u < ZB; ++u) accZ[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     // z as an operand fragment (A operand of z phi(Q)^T, z in every row)
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    Frag<T> zf[KB];
+    Frag<T> zf[Cfg::ZB16 ? 1 : KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) zf[kb] = frag_acc<T>(zero4, zero4);
+    for (int kb = 0; kb < (Cfg::ZB16 ? 1 : KB); ++kb) zf[kb] = frag_acc<T>(zero4, zero4);
     if constexpr (MODE != MODE_LOCAL) {
         if (a.S_src) {
             const float* Sb = a.S_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_stride;
@@ -317,13 +361,27 @@ la_fwd_kernel(const FwdArgs a)
             }
 #pragma unroll
             for (int u = 0; u < ZB; ++u) accZ[u] = *(const f32x4*)(zb + 16 * (ZB * wave + u) + 4 * g);
-            if constexpr (Cfg::NEED_Q) {
+            if constexpr (Cfg::NEED_Q && !Cfg::ZB16) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
                     zf[kb] = frag_acc<T>(*(const f32x4*)(zb + 32 * kb + 4 * g), *(const f32x4*)(zb + 32 * kb + 16 + 4 * g));
             }
         }
     }
+    // ZB16: the carried-in z goes to the slot the first chunk reads (1)
+    auto publish_z = [&](int par) LA_INLINE {
+        if (l16 == 0) {
+#pragma unroll
+            for (int u = 0; u < ZB; ++u) {
+                if constexpr (Cfg::ZB16) {
+                    st4(sZb + par * F + 16 * (ZB * wave + u) + 4 * g, accZ[u][0], accZ[u][1], accZ[u][2], accZ[u][3]);
+                } else {
+                    *(f32x4*)(sZ + par * F + 16 * (ZB * wave + u) + 4 * g) = accZ[u];
+                }
+            }
+        }
+    };
+    if constexpr (Cfg::ZB16) publish_z(1);
     // S as operand fragments (A operands of S^T phi(Q)^T)
     Frag<T> sf[KB][DBW];
     auto convert_state = [&]() LA_INLINE {
@@ -334,10 +392,12 @@ la_fwd_kernel(const FwdArgs a)
     };
     // z after the previous chunk, published in LDS by the waves that own it
     auto read_z = [&](int par) LA_INLINE {
-        const float* zs = sZ + par * F;
+        if constexpr (!Cfg::ZB16) {
+            const float* zs = sZ + par * F;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            zf[kb] = frag_acc<T>(*(const f32x4*)(zs + 32 * kb + 4 * g), *(const f32x4*)(zs + 32 * kb + 16 + 4 * g));
+            for (int kb = 0; kb < KB; ++kb)
+                zf[kb] = frag_acc<T>(*(const f32x4*)(zs + 32 * kb + 4 * g), *(const f32x4*)(zs + 32 * kb + 16 + 4 * g));
+        }
     };
     if constexpr (Cfg::NEED_Q) convert_state();
     float log2D = 0.f;  // the true state is 2^log2D times the accumulators
@@ -461,34 +521,39 @@ la_fwd_kernel(const FwdArgs a)
                 for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(sX, XLD, i, 32 * kb, g);
                 const bool use = i < n && (isq || !(xn[i] < 0.f));  // not past the end, not padded
                 const float cfac = use ? exp_rf<T>(a.rf_sign * 0.5f * qs * qs * xn[i]) * cnorm : 0.f;
-                const float w = use ? (decay ? key_weight(n - 1 - i, kw_l2) : 1.f) : 0.f;
+                // prefactor of the weighted keys (the key weight folded in)
+                const float cw = decay ? key_weight(n - 1 - i, kw_l2) * cfac : cfac;
 #pragma unroll
                 for (int u = 0; u < TPW; ++u) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < KX; ++kb) {
-                        mma(acc, om_hi[u][kb], xf[kb]);
-                        if constexpr (sizeof(T) == 2) mma(acc, om_lo[u][kb], xf[kb]);
+                        mma(acc, omega_frag(u, kb, 0), xf[kb]);
+                        if constexpr (Cfg::SPLIT) mma(acc, omega_frag(u, kb, 1), xf[kb]);
                     }
                     // acc[r] = (omega x_i)_{f0+r} with f0 = 16 rb + 4 g
                     const int f0 = 16 * (wave / QB + (NW / QB) * u) + 4 * g;
                     float cs[4], sn[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        sincos_rf<T>(qs * acc[r], &sn[r], &cs[r]);
-                        cs[r] *= cfac;
-                        sn[r] *= cfac;
-                    }
-                    if (isq) {
-                        st4(sQ0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
-                        st4(sQ0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
-                    } else {
-                        if constexpr (Cfg::NEED_KROW) {
-                            st4(sK0 + TF::off(i, f0), cs[0], cs[1], cs[2], cs[3]);
-                            st4(sK0 + TF::off(i, M + f0), sn[0], sn[1], sn[2], sn[3]);
+                        if constexpr (REV) {
+                            sn[r] = __builtin_amdgcn_sinf(acc[r]);
+                            cs[r] = __builtin_amdgcn_cosf(acc[r]);
+                        } else {
+                            sincos_rf<T>(qs * acc[r], &sn[r], &cs[r]);
                         }
-                        st4(sKw0 + TF::off(i, f0), w * cs[0], w * cs[1], w * cs[2], w * cs[3]);
-                        st4(sKw0 + TF::off(i, M + f0), w * sn[0], w * sn[1], w * sn[2], w * sn[3]);
+                    }
+                    auto put = [&](T* tile, float f) LA_INLINE {
+                        st4(tile + TF::off(i, f0), f * cs[0], f * cs[1], f * cs[2], f * cs[3]);
+                        st4(tile + TF::off(i, M + f0), f * sn[0], f * sn[1], f * sn[2], f * sn[3]);
+                    };
+                    if (isq) {
+                        put(sQ0, cfac);
+                    } else {
+                        // without decay the unweighted key tile serves both
+                        // the scores and the state update
+                        if constexpr (Cfg::NEED_KROW) put(sK0, cfac);
+                        if (!Cfg::NEED_KROW || decay) put(sKw0, cw);
                     }
                 }
             }
@@ -502,7 +567,7 @@ la_fwd_kernel(const FwdArgs a)
         constexpr bool TAIL = decltype(tail_c)::value;
         const T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         const T* const sK = sK0 + (RF ? 0 : buf * TQ);
-        const T* const sKw = (Cfg::NEED_KROW && !decay && !RF) ? sK : sKw0 + (RF ? 0 : buf * TQ);
+        const T* const sKw = (Cfg::NEED_KROW && !decay) ? sK : sKw0 + (RF ? 0 : buf * TQ);
         const T* const sV = sV0 + buf * TV;
         // V column fragments: A operand of V^T P^T and B operand of the state update
         Frag<T> vf[Cfg::NEED_K ? CB : 1][DBW];
@@ -524,7 +589,14 @@ la_fwd_kernel(const FwdArgs a)
                 // phi(q_i).z (every row of the tile holds it)
                 f32x4 dq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) mma(dq, zf[kb], qf[kb]);
+                for (int kb = 0; kb < KB; ++kb) {
+                    if constexpr (Cfg::ZB16) {
+                        const bf16* zs = sZb + (zpar ^ 1) * F + 32 * kb + 4 * g;
+                        mma(dq, frag2(zs, zs + 16), qf[kb]);
+                    } else {
+                        mma(dq, zf[kb], qf[kb]);
+                    }
+                }
                 float den = dq[0];
                 Frag<T> pf[CB];
                 if constexpr (MODE == MODE_CAUSAL) {
@@ -610,11 +682,7 @@ la_fwd_kernel(const FwdArgs a)
             if constexpr (Cfg::NEED_Q) {
                 convert_state();
                 // publish z for the next chunk (read after its barrier)
-                if (l16 == 0) {
-                    float* zs = sZ + zpar * F;
-#pragma unroll
-                    for (int u = 0; u < ZB; ++u) *(f32x4*)(zs + 16 * (ZB * wave + u) + 4 * g) = accZ[u];
-                }
+                publish_z(zpar);
             }
         }
     };
