@@ -450,10 +450,53 @@ def backward_w2(ctx, steps=100, with_dlam=False):
     return res
 
 
+def rf_backward_w5(ctx, steps=5):
+    """Backward of workload 5 (B=1 H=16 N=65536, m=128 random features, d=64
+    bf16, lambda = 1): one la_backward_causal call -- phi(q) and phi(k), the
+    backward sweeps on them at F = 256 with the identity map (d phi in fp32),
+    and the vector-Jacobian products through omega to dq and dk."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    wl = si.workload(5)
+    B, H, N, d, m = wl.B, wl.H, wl.N, wl.dk, wl.m
+    F = 2 * m
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(5)
+    q, k, v = (device_normal(torch, g, (B, H, N, d), wl.scale, ctx.dev) for _ in range(3))
+    omega = torch.from_numpy(si.make_omega(m, d, wl.index)).to(ctx.dev)
+    phi = la.Phi("trig_rf", omega, wl.qk_scale)
+    g.manual_seed(25)
+    dy = device_normal(torch, g, (B, H, N, d), 0.5, ctx.dev)
+    y = torch.empty_like(q)
+    la.la_forward_causal(q, k, v, y, phi=phi, eps=wl.eps)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(la.la_workspace_size_backward(B, H, N, d, d, phi=phi), dtype=torch.uint8, device=ctx.dev)
+    SZ = F * d + F
+    P = max(1, -(-512 // (B * H)))
+    rows = B * H * N
+    ids = la.KERNEL_IDS
+    # per launch: the feature pass and the gradient pass each cover q or k
+    kb = {ids["rf_features"]: rows * (d * 2 + F * 2),
+          ids["rf_vjp"]: rows * (d * 2 + F * 4 + d * 2),
+          ids["bwd_q"]: rows * (2 * F * 2 + 3 * d * 2 + F * 4 + 8) + P * B * H * SZ * 4,
+          ids["bwd_rlocal"]: rows * (F * 2 + d * 2 + 8) + P * B * H * SZ * 4,
+          ids["bwd_kv"]: rows * (2 * F * 2 + 2 * d * 2 + 8 + F * 4 + d * 2) + P * B * H * SZ * 4,
+          ids["fwd_local"]: rows * (F * 2 + d * 2) + P * B * H * SZ * 4,
+          ids["scan"]: 2 * P * B * H * SZ * 4}
+
+    def step():
+        la.la_backward_causal(q, k, v, y, dy, dq, dk, dv, phi=phi, eps=wl.eps, workspace=ws)
+
+    name = "trigrf_m%d_backward_B%d_H%d_N%d_d%d_bf16" % (m, B, H, N, d)
+    res = bench_call(ctx, name, step, B * N, kb, steps, max(ctx.warmup, 3), launches_per_step=12)
+    res["segments"] = P
+    return res
+
+
 # Mask / cross / packed / backward lines measured beside the main workloads
 SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2),
                   ("backward_w2", backward_w2), ("backward_dlam_w2", lambda c: backward_w2(c, with_dlam=True)),
-                  ("cross_backward_w2", cross_backward_w2))
+                  ("cross_backward_w2", cross_backward_w2), ("rf_backward_w5", rf_backward_w5))
 
 
 def workload4_decode(ctx, steps=1024):

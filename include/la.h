@@ -223,8 +223,14 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
  * for the same q, k, v, lambda_h, eps, key_padding_mask and S_in / z_in, and
  * shape->out_dtype must equal shape->in_dtype.  dS_out / dz_out: optional
  * gradient of the final state (both or none; NULL = 0).  Outputs must not
- * alias inputs or each other.  Feature maps: LA_PHI_ELU1 and LA_PHI_RELU
- * (others: LA_ERR_UNSUPPORTED).  dlambda: optional device fp32 [H], the
+ * alias inputs or each other.  Feature maps: all kinds.  The random-feature
+ * kinds ("From standard attention to linear attention" sec. 4.2) run the
+ * same sweeps on phi(q), phi(k) computed first (F = 2m in the role of d_k,
+ * supported for F * d_v <= 256 * 128 with bf16 inputs and F <= 128 with fp32
+ * inputs) and map the resulting d phi back through omega:
+ * dx = s (omega^T g + sigma x' (phi . d phi)), g_r = c (cos u_r d phi_{m+r} -
+ * sin u_r d phi_r), with x' = s x, u = omega x', c the prefactor and sigma its
+ * sign (-1, 0, +1 by kind).  dlambda: optional device fp32 [H], the
  * gradient of lambda_h summed over the batch (NULL = not computed; not
  * available for fp32 inputs with d_k = d_v = 128, LA_ERR_UNSUPPORTED).
  * Method: with dnum_i = dy_i / den_i and dden_i = -(dy_i . y_i) / den_i,
@@ -236,7 +242,8 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
  * dlambda follows the product rule through the chunks: the dq sweep also
  * carries T = dS/dlambda, and a reduction joins the segments.
  * Workspace: la_workspace_size_backward bytes (8 bytes per token plus the
- * segment states). */
+ * segment states; random features add phi(q), phi(k) in the input type and
+ * d phi(q), d phi(k) in fp32, B*H*N*2m values each). */
 size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi);
 la_status la_backward_causal(const void* q, const void* k, const void* v,
                              const void* y, const void* dy,
@@ -314,7 +321,9 @@ enum {
     LA_KERNEL_BWD_DLAM = 10,   /* backward: lambda-gradient reduction          */
     LA_KERNEL_VARLEN_ITEMS = 11, /* packed sequences: table of work items      */
     LA_KERNEL_BWD_NCQ = 12,    /* non-causal backward: dq and adjoint sums     */
-    LA_KERNEL_BWD_NCKV = 13    /* non-causal backward: dk, dv                  */
+    LA_KERNEL_BWD_NCKV = 13,   /* non-causal backward: dk, dv                  */
+    LA_KERNEL_RF_FEATURES = 14, /* random-feature backward: phi(q), phi(k)     */
+    LA_KERNEL_RF_VJP = 15      /* random-feature backward: dq, dk from d phi   */
 };
 la_status la_profile_begin(int32_t max_launches);
 la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);

@@ -191,7 +191,9 @@ def test_backward_validation(lib):
         return lib.la_backward_causal(*ptrs, ctypes.byref(shape), ctypes.byref(phi), None, 1e-6, None, S_in, z_in,
                                       dS_out, dz_out, dS_in, dz_in, dlam, ws, ws_bytes, None)
 
-    assert call(phi=LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35)) == U          # random features
+    RF = LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35)
+    assert call(phi=RF) == la.binding.LA_ERR_WORKSPACE                       # random features: supported
+    assert call(shape=_shape(it=la.LA_F32, ot=la.LA_F32), phi=LaPhiC(la.LA_PHI_TRIG_RF, 128, FAKE, 0.35)) == U
     assert call(shape=_shape(ot=la.LA_F32)) == U                             # y in another type
     assert call(S_in=FAKE) == E                                              # S_in without z_in
     assert call(dS_in=FAKE) == E
@@ -202,7 +204,13 @@ def test_backward_validation(lib):
     assert call(shape=big, dlam=FAKE) == U                                   # no lambda gradient for fp32 d=128
     n = lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(ELU))
     assert n >= 2 * 4 * s.B * s.H * s.N                                      # 8 bytes per token at least
-    assert lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(LaPhiC(la.LA_PHI_TRIG_RF, 64, FAKE, 0.35))) == 0
+    # random features add phi(q), phi(k) (input type) and d phi(q), d phi(k)
+    # (fp32) for every token: F = 2m = 128 values each
+    nrf = lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(RF))
+    rows = s.B * s.H * s.N
+    assert nrf >= n + rows * 128 * (2 + 2 + 4 + 4)
+    ws_rf = FAKE
+    assert call(phi=RF, ws=ws_rf, ws_bytes=nrf - 1) == la.binding.LA_ERR_WORKSPACE
 
 
 def test_cross_backward_validation(lib):

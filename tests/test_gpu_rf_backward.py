@@ -1,0 +1,140 @@
+"""GPU parity of the random-feature backward (la_backward_causal with the
+trigonometric feature maps) against the fp64 oracle's gradients, through the
+C ABI.
+
+The library computes phi(q), phi(k) in the input type, runs the backward
+sweeps on them (d phi in fp32) and maps d phi back through omega.
+
+Conditioning.  Random features are sign-indefinite, so a query's denominator
+phi(q_i)^T z_i can nearly cancel -- for the first tokens of a sequence started
+from a zero state, where it sums few terms, for small m, and now and then
+anywhere (the state after a 128-token prefix still leaves kappa up to ~4e4
+for some queries).  The forward's condition factor kappa_i = |phi q_i|^T
+zbar_i / |phi(q_i)^T z_i + eps| (the oracle's) bounds how far rounding of the
+operands moves row i, and every gradient depends on the queries through
+1 / den_i.  The bar is the elementwise backward's (tests/test_gpu_backward.py)
+scaled by it:
+  - dq, dk, dv, dS0, dz0 normwise per (batch, head), against the head's
+    largest entry: tol * max(1, K_h), K_h the head's largest kappa (keys and
+    the state gradient gather terms of every later query);
+  - dq rows of at least a tenth of their head's largest entry: tol *
+    max(1, kappa_i) each (smaller rows cancel -- the first token's dq is
+    eps-sized -- and are held by the normwise bound);
+  - cases whose every kappa is below 50: the flat tolerance, normwise.
+Measured: well-conditioned bf16 cases (m = 64, 128; K_h <= 32) at 4e-3 to
+1e-2, fp32 at 2e-4 with K_h ~ 4e4; ill-conditioned bf16 cases grow with K_h
+(0.12 at K_h = 272)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import weight_sequence_mixing_amd as la
+from gpu_util import DEV, phi_for, row_errors, tdtype, to_dev, _record
+from test_gpu_backward import TOL_BWD, _dev, _grad_out, head_scale
+
+pytestmark = pytest.mark.gpu
+
+
+def prefix_state(wl, B, H, lam, omega, seed, n=128):
+    """(S, z) after n tokens of the workload's distribution (oracle, fp32)."""
+    pre = si.make_inputs(wl, seed=seed, B=B, H=H, N=n)
+    _, S, z = oracle.causal(pre["q"], pre["k"], pre["v"], lam, wl.eps, wl.phi, omega, wl.qk_scale,
+                            want_state=True)
+    return S.astype(np.float32), z.astype(np.float32)
+
+
+def run_rf_backward(wl, B, H, N, lam, mask=None, state=False, dsout=False, seed=0):
+    inp = si.make_inputs(wl, B=B, H=H, N=N)
+    q, k, v = (to_dev(inp, n, wl.dtype) for n in ("q", "k", "v"))
+    g_np, g = _grad_out(wl, B, H, N, seed + 1)
+    rng = np.random.default_rng(seed + 2)
+    F = wl.F
+    S0 = z0 = dSo = dzo = None
+    if state:
+        S0, z0 = prefix_state(wl, B, H, lam, inp["omega"], seed + 4)
+    if dsout:
+        dSo = (rng.standard_normal((B, H, F, wl.dv)) * 0.01).astype(np.float32)
+        dzo = (rng.standard_normal((B, H, F)) * 0.01).astype(np.float32)
+    m = None if mask is None else si.make_key_padding_mask(B, N, mask, seed=seed + 3)
+    mt = None if m is None else _dev(m)
+    t = {n: (None if a is None else _dev(a)) for n, a in (("S0", S0), ("z0", z0), ("dSo", dSo), ("dzo", dzo))}
+    phi = phi_for(wl, inp["omega"])
+    y = torch.empty(B, H, N, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    if mt is None:
+        la.la_forward_causal(q, k, v, y, phi=phi, lambda_h=lam, eps=wl.eps, S_in=t["S0"], z_in=t["z0"])
+    else:
+        la.la_forward_causal_masked(q, k, v, y, mt, phi=phi, lambda_h=lam, eps=wl.eps, S_in=t["S0"], z_in=t["z0"])
+    dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    dSi = torch.full((B, H, F, wl.dv), float("nan"), device=DEV)
+    dzi = torch.full((B, H, F), float("nan"), device=DEV)
+    la.la_backward_causal(q, k, v, y, g, dq, dk, dv, phi=phi, lambda_h=lam, eps=wl.eps, key_padding_mask=mt,
+                          S_in=t["S0"], z_in=t["z0"], dS_out=t["dSo"], dz_out=t["dzo"], dS_in=dSi, dz_in=dzi)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], g_np, lam, wl.eps, wl.phi, inp["omega"], wl.qk_scale,
+                          S0, z0, dSo, dzo, key_padding_mask=m)
+    _, kap = oracle.causal(inp["q"], inp["k"], inp["v"], lam, wl.eps, wl.phi, inp["omega"], wl.qk_scale, S0, z0,
+                           want_kappa=True, key_padding_mask=m)
+    got = {"dq": dq.float().cpu().numpy(), "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy(),
+           "dS0": dSi.cpu().numpy(), "dz0": dzi.cpu().numpy()}
+    return got, ref, m, kap
+
+
+def check_rf(wl, got, ref, kap):
+    tol = TOL_BWD[wl.dtype]
+    B, H = kap.shape[:2]
+    K = np.maximum(1.0, kap.reshape(B, H, -1).max(-1))  # [B,H]
+    flat = float(K.max()) < 50
+    for n in ("dq", "dk", "dv", "dS0", "dz0"):
+        scale = head_scale(ref[n])
+        he = np.abs(got[n] - ref[n]).reshape(B, H, -1).max(-1) / scale
+        print("%s head-normwise %.3e  (K_h max %.1f)" % (n, float(he.max()), float(K.max())))
+        _record(float((he / K).max()))
+        assert np.all(he <= tol * K), (n, float(he.max()), float(K.max()))
+        if flat:
+            assert float(he.max()) < tol, (n, float(he.max()))
+    scale = head_scale(ref["dq"])
+    big = np.abs(ref["dq"]).max(-1) >= 0.1 * scale[..., None]
+    err = row_errors(got["dq"], ref["dq"])
+    bound = tol * np.maximum(1.0, kap)
+    worst = int(np.argmax(np.where(big, err / bound, 0.0)))
+    assert np.all(err[big] <= bound[big]), ("dq row", float(err.reshape(-1)[worst]), float(kap.reshape(-1)[worst]))
+
+
+CASES = [
+    # overrides of workload 5 (m=128, d=64, bf16, exp(-|x'|^2/2)), B, H, N, lambda, mask,
+    # initial state from a 128-token prefix, dS_out
+    ({}, 1, 2, 300, [0.95, 1.0], None, True, False),
+    ({"m": 32}, 2, 2, 777, [0.9, 1.0], "random", True, True),
+    ({"m": 64, "dv": 128}, 1, 2, 2100, [1.0, 0.99], "right", True, True),        # several segments
+    ({"m": 64, "dtype": "f32", "scale": 1.0}, 1, 2, 257, [0.97, 1.0], None, True, True),
+    ({"m": 32, "phi": "trig_rf_plain"}, 1, 2, 200, [0.9, 1.0], None, True, False),
+    ({"m": 32, "phi": "trig_rf_softmax"}, 1, 2, 200, [1.0, 0.95], "random", True, False),
+    ({"m": 64, "dk": 128}, 1, 2, 333, [0.97, 1.0], None, True, False),
+    ({"m": 32, "omega": "gaussian"}, 2, 1, 96, [0.8], None, True, False),
+    # from a zero state: the first tokens' denominators sum few terms
+    ({}, 1, 2, 300, [0.95, 1.0], None, False, False),
+    ({"m": 32, "dtype": "f32", "scale": 1.0}, 1, 2, 150, [1.0, 0.9], "random", False, True),
+]
+
+
+@pytest.mark.parametrize("over,B,H,N,lam,mask,state,dsout", CASES)
+def test_rf_backward_parity(over, B, H, N, lam, mask, state, dsout):
+    wl = si.workload(5).with_(**over)
+    got, ref, m, kap = run_rf_backward(wl, B, H, N, lam, mask, state, dsout, seed=500 + N)
+    check_rf(wl, got, ref, kap)
+    if m is not None:
+        padded = np.broadcast_to(m[:, None, :], (B, H, N))
+        assert float(np.abs(got["dk"][padded]).max(initial=0.0)) == 0.0
+        assert float(np.abs(got["dv"][padded]).max(initial=0.0)) == 0.0
+
+
+def test_rf_backward_unsupported_shape_is_refused():
+    # fp32 inputs with m = 128 (F = 256): the identity sweeps do not fit
+    wl = si.workload(5).with_(dtype="f32", scale=1.0)
+    inp = si.make_inputs(wl, B=1, H=1, N=64)
+    q = to_dev(inp, "q", "f32")
+    phi = phi_for(wl, inp["omega"])
+    with pytest.raises(la.LaError):
+        la.la_backward_causal(q, q, q, q, q, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), phi=phi)

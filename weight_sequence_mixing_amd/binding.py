@@ -35,7 +35,7 @@ EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_f
            "la_kernel_name")
 KERNEL_IDS = {"fwd_local": 0, "fwd_causal": 1, "fwd_query": 2, "scan": 3, "decode": 4, "fill": 5, "copy": 6,
               "bwd_q": 7, "bwd_rlocal": 8, "bwd_kv": 9, "bwd_dlam": 10, "varlen_items": 11, "bwd_ncq": 12,
-              "bwd_nckv": 13}
+              "bwd_nckv": 13, "rf_features": 14, "rf_vjp": 15}
 
 
 class LaPhiC(ctypes.Structure):

@@ -33,6 +33,9 @@ SOURCES = [
     "la_inst_bwd_bf16.hip",
     "la_inst_bwd_f32.hip",
     "la_scan.hip",
+    "la_inst_ident_bf16.hip",
+    "la_inst_ident_f32.hip",
+    "la_rf_grad.hip",
     "la_api.cpp",
 ]
 

@@ -108,10 +108,11 @@ float rf_sign(int kind)
 
 const KernelEntry* find_entry(int in_dtype, int phi, int dk, int F, int dv)
 {
-    const KernelEntry* tables[] = {kEntriesBf16Elu, kEntriesBf16Rf, kEntriesBf16Relu, kEntriesF32, kEntriesF32Relu};
+    const KernelEntry* tables[] = {kEntriesBf16Elu, kEntriesBf16Rf, kEntriesBf16Relu, kEntriesF32, kEntriesF32Relu,
+                                   kEntriesIdentBf16, kEntriesIdentF32};
     const int counts[] = {kNumEntriesBf16Elu, kNumEntriesBf16Rf, kNumEntriesBf16Relu, kNumEntriesF32,
-                          kNumEntriesF32Relu};
-    for (int t = 0; t < 5; ++t)
+                          kNumEntriesF32Relu, kNumEntriesIdentBf16, kNumEntriesIdentF32};
+    for (int t = 0; t < 7; ++t)
         for (int i = 0; i < counts[t]; ++i) {
             const KernelEntry& e = tables[t][i];
             if (e.in_dtype == in_dtype && e.phi == phi && e.dk == dk && e.F == F && e.dv == dv) return &e;
@@ -413,6 +414,8 @@ const char* la_kernel_name(int32_t id)
     case LA_KERNEL_VARLEN_ITEMS: return "la_varlen_items_kernel";
     case LA_KERNEL_BWD_NCQ: return "la_bwd_q_kernel (non-causal)";
     case LA_KERNEL_BWD_NCKV: return "la_bwd_kv_kernel (non-causal dk dv)";
+    case LA_KERNEL_RF_FEATURES: return "la_rf_features_kernel";
+    case LA_KERNEL_RF_VJP: return "la_rf_vjp_kernel";
     }
     return "unknown";
 }
@@ -853,9 +856,9 @@ namespace {
 
 const BwdEntry* find_bwd(int in_dtype, int phi, int dk, int F, int dv)
 {
-    const BwdEntry* tabs[] = {kBwdEntriesBf16, kBwdEntriesF32};
-    const int counts[] = {kNumBwdEntriesBf16, kNumBwdEntriesF32};
-    for (int t = 0; t < 2; ++t)
+    const BwdEntry* tabs[] = {kBwdEntriesBf16, kBwdEntriesF32, kBwdEntriesIdentBf16, kBwdEntriesIdentF32};
+    const int counts[] = {kNumBwdEntriesBf16, kNumBwdEntriesF32, kNumBwdEntriesIdentBf16, kNumBwdEntriesIdentF32};
+    for (int t = 0; t < 4; ++t)
         for (int i = 0; i < counts[t]; ++i) {
             const BwdEntry& e = tabs[t][i];
             if (e.in_dtype == in_dtype && e.phi == phi && e.dk == dk && e.F == F && e.dv == dv) return &e;
@@ -863,16 +866,29 @@ const BwdEntry* find_bwd(int in_dtype, int phi, int dk, int F, int dv)
     return nullptr;
 }
 
-// Shape checks of the backward beyond the forward's; sets the segment plan.
+// Shape checks of the backward beyond the forward's; sets F, the forward entry
+// that runs the segment-state pass and the entry of the backward sweeps.
+// Random features (allow_rf): both entries are those of the identity map at
+// d_k = F, run on phi(q), phi(k) computed beforehand.
 la_status check_backward(const la_shape* shape, const la_phi* phi, int* F, const KernelEntry** ent,
-                         const BwdEntry** bent)
+                         const BwdEntry** bent, bool allow_rf)
 {
     la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, F, ent);
     if (st != LA_OK) return st;
-    if (phi->kind != LA_PHI_ELU1 && phi->kind != LA_PHI_RELU)
-        return fail(LA_ERR_UNSUPPORTED, "the backward supports the elementwise feature maps (elu+1, ReLU)");
+    const bool rf = allow_rf && is_rf(phi->kind);
+    if (phi->kind != LA_PHI_ELU1 && phi->kind != LA_PHI_RELU && !rf)
+        return fail(LA_ERR_UNSUPPORTED, allow_rf ? "unsupported feature map for the backward"
+                                                 : "the non-causal backward supports the elementwise feature maps (elu+1, ReLU)");
     if (shape->out_dtype != shape->in_dtype)
         return fail(LA_ERR_UNSUPPORTED, "the backward takes y and dy in the input type (out_dtype == in_dtype)");
+    if (rf) {
+        *ent = find_entry(shape->in_dtype, kPhiIdentity, *F, *F, shape->d_v);
+        *bent = find_bwd(shape->in_dtype, kPhiIdentity, *F, *F, shape->d_v);
+        if (!*ent || !*bent)
+            return fail(LA_ERR_UNSUPPORTED, "no random-feature backward for dtype=%d F=%d d_v=%d", shape->in_dtype, *F,
+                        shape->d_v);
+        return LA_OK;
+    }
     *bent = find_bwd(shape->in_dtype, phi->kind, shape->d_k, *F, shape->d_v);
     if (!*bent) return fail(LA_ERR_UNSUPPORTED, "no backward kernel for this shape");
     return LA_OK;
@@ -914,6 +930,22 @@ struct BwdPlan {
 };
 
 size_t round256(size_t floats) { return ((floats * sizeof(float) + 255) & ~size_t(255)) / sizeof(float); }
+size_t round256b(size_t bytes) { return (bytes + 255) & ~size_t(255); }
+
+// Random-feature backward buffers after the plan's: phi(q), phi(k) in the
+// input type and d phi(q), d phi(k) in fp32, [B*H*N, F] each.
+struct RfBufs {
+    size_t feat_bytes, dphi_bytes, bytes;
+};
+RfBufs rf_bufs(const la_shape* s, int F)
+{
+    RfBufs b;
+    const size_t rows = (size_t)(s->B * s->H * s->N);
+    b.feat_bytes = round256b(rows * F * elem_size(s->in_dtype));
+    b.dphi_bytes = round256b(rows * F * sizeof(float));
+    b.bytes = 2 * b.feat_bytes + 2 * b.dphi_bytes;
+    return b;
+}
 
 BwdPlan bwd_plan(const la_shape* s, int F, int C)
 {
@@ -941,10 +973,11 @@ size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi)
     const KernelEntry* e = nullptr;
     const BwdEntry* be = nullptr;
     const std::string saved = g_last_error;
-    const la_status st = check_backward(shape, phi, &F, &e, &be);
+    const la_status st = check_backward(shape, phi, &F, &e, &be, true);
     g_last_error = saved;
     if (st != LA_OK) return 0;
-    return bwd_plan(shape, F, be->C).bytes;
+    const size_t base = bwd_plan(shape, F, be->C).bytes;
+    return is_rf(phi->kind) && shape->N > 0 ? base + rf_bufs(shape, F).bytes : base;
 }
 
 la_status la_backward_causal(const void* q, const void* k, const void* v, const void* y, const void* dy,
@@ -957,8 +990,9 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     int F = 0;
     const KernelEntry* ent = nullptr;
     const BwdEntry* bent = nullptr;
-    la_status st = check_backward(shape, phi, &F, &ent, &bent);
+    la_status st = check_backward(shape, phi, &F, &ent, &bent, true);
     if (st != LA_OK) return st;
+    const bool rf = is_rf(phi->kind);
     if ((S_in == nullptr) != (z_in == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_in and z_in must be given together");
     if ((dS_out == nullptr) != (dz_out == nullptr))
         return fail(LA_ERR_INVALID_ARGUMENT, "dS_out and dz_out must be given together");
@@ -998,11 +1032,52 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     const size_t rows = (size_t)BH * shape->N;
     if ((st = check_bwd_io(q, k, v, y, dy, dq, dk, dv, shape, rows, rows)) != LA_OK) return st;
     const BwdPlan plan = bwd_plan(shape, F, bent->C);
-    if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.bytes);
-    if (workspace_bytes < plan.bytes)
-        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.bytes, workspace_bytes);
+    const RfBufs rb = rf_bufs(shape, F);
+    const size_t need = plan.bytes + (rf ? rb.bytes : 0);
+    if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (workspace_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     float* tok = static_cast<float*>(workspace);
+    // random features: the sweeps run on phi(q), phi(k) (identity map) and
+    // write d phi in fp32; dq and dk follow from it through omega at the end
+    const void* q_in = q;
+    const void* k_in = k;
+    void* dq_out = dq;
+    void* dk_out = dk;
+    RfGradArgs rg;
+    std::memset(&rg, 0, sizeof(rg));
+    if (rf) {
+        char* base = static_cast<char*>(workspace) + plan.bytes;
+        void* fq = base;
+        void* fk = base + rb.feat_bytes;
+        float* dfq = reinterpret_cast<float*>(base + 2 * rb.feat_bytes);
+        float* dfk = reinterpret_cast<float*>(base + 2 * rb.feat_bytes + rb.dphi_bytes);
+        rg.omega = phi->omega;
+        rg.rows = (int64_t)rows;
+        rg.dk = shape->d_k;
+        rg.m = phi->m;
+        rg.scale = phi->qk_scale;
+        rg.sign = rf_sign(phi->kind);
+        rg.in_f32 = shape->in_dtype == LA_F32;
+        rg.N = shape->N;
+        rg.H = (int32_t)shape->H;
+        rg.kpm_stride = shape->N;
+        RfGradArgs fa = rg;
+        fa.x = q;
+        fa.out = fq;
+        hipError_t e = launch(LA_KERNEL_RF_FEATURES, [&] { return launch_rf_grad(fa, false, strm); });
+        if (e == hipSuccess) {
+            fa.x = k;
+            fa.out = fk;
+            e = launch(LA_KERNEL_RF_FEATURES, [&] { return launch_rf_grad(fa, false, strm); });
+        }
+        if (e != hipSuccess) return hip_fail(e, "backward: random-feature launch");
+        q_in = fq;
+        k_in = fk;
+        dq_out = dfq;
+        dk_out = dfk;
+    }
     float* segs = tok + round256(plan.tok_floats);
     float* tseg = segs + round256(plan.seg_floats);
     float* dlp = tseg + round256((size_t)plan.P * BH * plan.SZ);
@@ -1025,13 +1100,13 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
 
     BwdArgs b;
     std::memset(&b, 0, sizeof(b));
-    b.q = q;
-    b.k = k;
+    b.q = q_in;
+    b.k = k_in;
     b.v = v;
     b.y = y;
     b.gy = dy;
-    b.dq = dq;
-    b.dk = dk;
+    b.dq = dq_out;
+    b.dk = dk_out;
     b.dv = dv;
     b.tok = tok;
     b.N = shape->N;
@@ -1049,8 +1124,8 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         // forward state at each segment's start: segment sums, then the scan
         FwdArgs a;
         std::memset(&a, 0, sizeof(a));
-        a.q = q;
-        a.k = k;
+        a.q = q_in;
+        a.k = k_in;
         a.v = v;
         a.N = shape->N;
         a.n_len = shape->N;
@@ -1127,6 +1202,22 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         if ((e = launch(LA_KERNEL_BWD_KV, [&] { return bent->bwd(bk, BMODE_KV, strm); })) != hipSuccess)
             return hip_fail(e, "backward: dk dv launch");
     }
+    if (rf) {
+        // dq, dk = J_phi^T d phi (padded keys: 0)
+        RfGradArgs va = rg;
+        va.x = q;
+        va.dphi = static_cast<const float*>(dq_out);
+        va.out = dq;
+        e = launch(LA_KERNEL_RF_VJP, [&] { return launch_rf_grad(va, true, strm); });
+        if (e == hipSuccess) {
+            va.x = k;
+            va.dphi = static_cast<const float*>(dk_out);
+            va.out = dk;
+            va.kpm = key_padding_mask;
+            e = launch(LA_KERNEL_RF_VJP, [&] { return launch_rf_grad(va, true, strm); });
+        }
+        if (e != hipSuccess) return hip_fail(e, "backward: random-feature gradient launch");
+    }
     return ok();
 }
 
@@ -1164,7 +1255,7 @@ size_t la_workspace_size_backward_cross(const la_shape* shape, int64_t n_kv, con
     const KernelEntry* e = nullptr;
     const BwdEntry* be = nullptr;
     const std::string saved = g_last_error;
-    const la_status st = check_backward(shape, phi, &F, &e, &be);
+    const la_status st = check_backward(shape, phi, &F, &e, &be, false);
     g_last_error = saved;
     if (st != LA_OK || shape->N < 1 || n_kv < 1 || n_kv > INT64_MAX / 4) return 0;
     return cross_bwd_plan(shape, n_kv, F, e->C, be->C).bytes;
@@ -1178,7 +1269,7 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     int F = 0;
     const KernelEntry* ent = nullptr;
     const BwdEntry* bent = nullptr;
-    la_status st = check_backward(shape, phi, &F, &ent, &bent);
+    la_status st = check_backward(shape, phi, &F, &ent, &bent, false);
     if (st != LA_OK) return st;
     if (shape->N < 1) return fail(LA_ERR_INVALID_ARGUMENT, "N must be >= 1");
     if (n_kv < 1 || n_kv > INT64_MAX / 4) return fail(LA_ERR_INVALID_ARGUMENT, "n_kv=%lld must be >= 1", (long long)n_kv);

@@ -89,7 +89,16 @@ __device__ __forceinline__ f32x4 ld4f(const float* p) { return ld4(p); }
 
 template <class T, int PHI> __device__ __forceinline__ float phi_deriv_from_phi(float p) {
     if constexpr (PHI == LA_PHI_RELU) return p > 0.f ? 1.f : 0.f;
+    else if constexpr (PHI == kPhiIdentity) return 1.f;
     else return p < 1.f ? p : 1.f;
+}
+
+// dq / dk rows: the input type, or fp32 d phi for the identity map (the
+// random-feature backward maps it through omega afterwards)
+template <class T, int PHI>
+__device__ __forceinline__ void store_grad(void* base, int64_t off, const float* o) {
+    if constexpr (PHI == kPhiIdentity) st4((float*)base + off, o[0], o[1], o[2], o[3]);
+    else st4((T*)base + off, o[0], o[1], o[2], o[3]);
 }
 
 template <class T, int DK, int F, int DV, int C, int NW, int MODE, bool DL = false>
@@ -444,7 +453,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                         const float dp = lqi * (inter[r] + accZ[fb][r] * dden) + intra[r];
                         o[r] = dp * phi_deriv_from_phi<T, PHI>(ph[r]);
                     }
-                    st4((T*)a.dq + (row0 + t0 + i) * DK + 16 * fb + 4 * g, o[0], o[1], o[2], o[3]);
+                    store_grad<T, PHI>(a.dq, (row0 + t0 + i) * DK + 16 * fb + 4 * g, o);
                 }
             }
             if (!NC && wave == 0 && g == 0 && i < n) {
@@ -820,7 +829,7 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
                             const float dp = intra[r] + lj * (inter[r] + accu[fb][r]);
                             o[r] = dp * phi_deriv_from_phi<T, PHI>(ph[r]);
                         }
-                        st4((T*)a.dk + (row0 + t0 + j) * DK + 16 * fb + 4 * g, o[0], o[1], o[2], o[3]);
+                        store_grad<T, PHI>(a.dk, (row0 + t0 + j) * DK + 16 * fb + 4 * g, o);
                     }
                 }
             }

@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include "../../include/la.h"
+#include "la_internal.h"
 
 namespace la {
 
@@ -207,6 +208,7 @@ __device__ __forceinline__ float phi_relu(float x) { return x > 0.f ? x : 0.f; }
 // The elementwise feature maps (F = d_k) by kind.
 template <class T, int PHI> __device__ __forceinline__ float phi_elem(float x) {
     if constexpr (PHI == LA_PHI_RELU) return phi_relu(x);
+    else if constexpr (PHI == kPhiIdentity) return x;
     else return phi_elu1<T>(x);
 }
 

@@ -810,4 +810,16 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
     }
 }
 
+// The segment-state pass alone: the random-feature backward runs it on
+// features it has already computed (identity map), and needs no other mode.
+template <class T, int PHI, int DK, int F, int DV>
+hipError_t fwd_local_launch(const FwdArgs& a, int mode, hipStream_t stream)
+{
+    constexpr int C = chunk_len<T, PHI>(F);
+    constexpr int NW = 4;
+    if (mode != MODE_LOCAL || a.cu_seqlens) return hipErrorInvalidValue;
+    return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL, false>, dim3((unsigned)a.P, (unsigned)a.BH),
+                         dim3(NW * 64), stream, a);
+}
+
 }  // namespace la

@@ -10,6 +10,11 @@
 
 namespace la {
 
+// Internal feature-map kind: the inputs are already features (F = d_k).  The
+// random-feature backward runs the elementwise sweeps on phi(q), phi(k) with
+// it and maps their d phi back through omega itself.
+constexpr int kPhiIdentity = 100;
+
 // Per-head decay, passed by value in the kernel arguments so that a launch
 // never needs a host-to-device copy (and can be recorded into a graph).
 struct LamTable {
@@ -212,6 +217,15 @@ extern KernelEntry kEntriesBf16Rf[];
 extern int kNumEntriesBf16Rf;
 extern KernelEntry kEntriesF32[];
 extern int kNumEntriesF32;
+// identity-map entries of the random-feature backward (F = d_k = 2m)
+extern KernelEntry kEntriesIdentBf16[];
+extern int kNumEntriesIdentBf16;
+extern KernelEntry kEntriesIdentF32[];
+extern int kNumEntriesIdentF32;
+extern BwdEntry kBwdEntriesIdentBf16[];
+extern int kNumBwdEntriesIdentBf16;
+extern BwdEntry kBwdEntriesIdentF32[];
+extern int kNumBwdEntriesIdentF32;
 extern KernelEntry kEntriesBf16Relu[];
 extern int kNumEntriesBf16Relu;
 extern KernelEntry kEntriesF32Relu[];
@@ -244,6 +258,26 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_varlen_items(const int32_t* cu, int B, int64_t N, int C, int64_t cps, int P, int G,
                                int32_t* items, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
+// Random-feature backward, feature-map end (la_rf_grad.hip): phi(x) of `rows`
+// rows ([rows, d_k] in, [rows, 2m] out, input type), or the vector-Jacobian
+// product dx = J_phi(x)^T dphi (dphi fp32 [rows, 2m], dx [rows, d_k] input
+// type; rows of padded keys get 0 when kpm is set).
+struct RfGradArgs {
+    const void* x;
+    const float* omega;  // [m, d_k] fp32
+    const float* dphi;   // vjp only
+    void* out;
+    const uint8_t* kpm;  // vjp of keys: byte kpm[b * kpm_stride + n] of row (b*H + h)*N + n
+    int64_t kpm_stride;
+    int64_t N;
+    int32_t H;
+    int64_t rows;
+    int32_t dk, m;
+    float scale, sign;
+    int32_t in_f32;
+};
+hipError_t launch_rf_grad(const RfGradArgs& a, bool vjp, hipStream_t stream);
 // S[BH][F][DV] = alpha * I (f == d), z[BH][F] = alpha for f < min(F, DV)
 hipError_t launch_fill_identity(float* S, float* z, int64_t BH, int F, int DV, float alpha, hipStream_t stream);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream);
