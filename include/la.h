@@ -268,13 +268,15 @@ la_status la_backward_causal(const void* q, const void* k, const void* v,
  * (a padded key gets dk = dv = 0).  q, y, dy, dq: [B,H,N,d_*]; k, v, dk, dv:
  * [B,H,n_kv,d_*]; all device, in shape->in_dtype (out_dtype must equal it);
  * y is la_forward_cross's output for the same q, k, v, key_padding_mask and
- * eps.  Outputs must not alias inputs or each other.  Feature maps:
- * LA_PHI_ELU1 and LA_PHI_RELU (others: LA_ERR_UNSUPPORTED).  N >= 1,
- * n_kv >= 1.  Method: three passes -- the state sums over the keys (as the
- * forward), a sweep over the queries that writes dq and sums the adjoint per
- * segment, a sweep over the keys that reads the total adjoint -- with two
- * small reductions joining the segments.  Workspace:
- * la_workspace_size_backward_cross bytes (segment states only). */
+ * eps.  Outputs must not alias inputs or each other.  Feature maps: all
+ * kinds; the random-feature kinds as in la_backward_causal (the sweeps run on
+ * phi(q), phi(k), d phi returns through omega).  N >= 1, n_kv >= 1.
+ * Method: three passes -- the state sums over the keys (as the forward), a
+ * sweep over the queries that writes dq and sums the adjoint per segment, a
+ * sweep over the keys that reads the total adjoint -- with two small
+ * reductions joining the segments.  Workspace:
+ * la_workspace_size_backward_cross bytes (segment states; random features
+ * add phi and d phi of the queries and keys, as la_backward_causal). */
 size_t la_workspace_size_backward_cross(const la_shape* shape, int64_t n_kv, const la_phi* phi);
 la_status la_backward_cross(const void* q, const void* k, const void* v,
                             const void* y, const void* dy,

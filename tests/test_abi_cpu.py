@@ -224,7 +224,7 @@ def test_cross_backward_validation(lib):
         return lib.la_backward_cross(*ptrs, ctypes.byref(shape), n_kv, None, ctypes.byref(phi), eps, ws, ws_bytes,
                                      None)
 
-    assert call(phi=RF) == U                                    # random features
+    assert call(phi=RF) == W                                    # random features: supported
     assert call(shape=_shape(ot=la.LA_F32)) == U                # y in another type
     assert call(shape=_shape(N=0)) == E                         # no queries
     assert call(n_kv=0) == E                                    # no keys
@@ -236,7 +236,10 @@ def test_cross_backward_validation(lib):
     assert call() == W                                          # no workspace
     n = lib.la_workspace_size_backward_cross(ctypes.byref(s), 100, ctypes.byref(ELU))
     assert n > 0 and call(ws=FAKE, ws_bytes=n - 1) == W
-    assert lib.la_workspace_size_backward_cross(ctypes.byref(s), 100, ctypes.byref(RF)) == 0
+    # random features add phi and d phi of the 64 queries and 100 keys (F = 128)
+    nrf = lib.la_workspace_size_backward_cross(ctypes.byref(s), 100, ctypes.byref(RF))
+    assert nrf >= s.B * s.H * (64 + 100) * 128 * (2 + 4)
+    assert call(phi=RF, ws=FAKE, ws_bytes=nrf - 1) == W
     assert lib.la_workspace_size_backward_cross(ctypes.byref(s), 0, ctypes.byref(ELU)) == 0
     assert lib.la_workspace_size_backward_cross(ctypes.byref(_shape(N=0)), 100, ctypes.byref(ELU)) == 0
     # segment states for the keys' and the queries' splits: grows with both lengths

@@ -138,3 +138,70 @@ def test_rf_backward_unsupported_shape_is_refused():
     phi = phi_for(wl, inp["omega"])
     with pytest.raises(la.LaError):
         la.la_backward_causal(q, q, q, q, q, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), phi=phi)
+
+
+# ---------------------------------------------------------------------------
+# Non-causal / cross form (la_backward_cross): every query reads the one state
+# summed over the kept keys, so kappa_i = |phi q_i|^T zbar / |phi(q_i)^T z + eps|
+# with z, zbar the sums of phi(k_j), |phi(k_j)| over the kept keys (computed
+# here from the oracle's features).
+
+def cross_kappa(wl, qi, kv, m):
+    pq = oracle.phi_map(qi["q"], wl.phi, qi["omega"], wl.qk_scale)
+    pk = oracle.phi_map(kv["k"], wl.phi, qi["omega"], wl.qk_scale)
+    keep = np.ones((pk.shape[0], pk.shape[2])) if m is None else (~m).astype(np.float64)
+    w = keep[:, None, :, None]
+    z, zbar = (pk * w).sum(2), (np.abs(pk) * w).sum(2)
+    num = np.einsum("bhnf,bhf->bhn", np.abs(pq), zbar)
+    den = np.abs(np.einsum("bhnf,bhf->bhn", pq, z) + wl.eps)
+    return num / den
+
+
+def run_rf_cross_backward(wl, B, H, Nq, Nk, mask=None, seed=0):
+    qi = si.make_inputs(wl, B=B, H=H, N=Nq)
+    kv = si.make_kv(wl, Nk, B=B, H=H, seed=seed)
+    q, k, v = to_dev(qi, "q", wl.dtype), to_dev(kv, "k", wl.dtype), to_dev(kv, "v", wl.dtype)
+    g_np, g = _grad_out(wl, B, H, Nq, seed + 1)
+    m = None if mask is None else si.make_key_padding_mask(B, Nk, mask, seed=seed + 3)
+    mt = None if m is None else _dev(m)
+    phi = phi_for(wl, qi["omega"])
+    y = torch.empty(B, H, Nq, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_cross(q, k, v, y, mt, phi=phi, eps=wl.eps)
+    dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    la.la_backward_cross(q, k, v, y, g, dq, dk, dv, mt, phi=phi, eps=wl.eps)
+    torch.cuda.synchronize()
+    ref = oracle.cross_backward(qi["q"], kv["k"], kv["v"], g_np, wl.eps, wl.phi, qi["omega"], wl.qk_scale,
+                                key_padding_mask=m)
+    got = {"dq": dq.float().cpu().numpy(), "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy()}
+    return got, ref, m, cross_kappa(wl, qi, kv, m)
+
+
+CROSS_CASES = [
+    # overrides of workload 5, B, H, Nq, Nk, mask
+    ({}, 1, 2, 300, 700, None),
+    ({"m": 64}, 2, 2, 1000, 513, "right"),
+    ({"m": 32, "dtype": "f32", "scale": 1.0}, 2, 1, 257, 100, "random"),
+    ({"m": 64, "dk": 128, "dv": 128}, 1, 2, 64, 3000, None),          # many key segments
+    ({"m": 128, "phi": "trig_rf_softmax"}, 1, 2, 5000, 200, "random"),  # many query segments
+]
+
+
+@pytest.mark.parametrize("over,B,H,Nq,Nk,mask", CROSS_CASES)
+def test_rf_cross_backward_parity(over, B, H, Nq, Nk, mask):
+    wl = si.workload(5).with_(**over)
+    got, ref, m, kap = run_rf_cross_backward(wl, B, H, Nq, Nk, mask, seed=700 + Nq)
+    tol = TOL_BWD[wl.dtype]
+    K = np.maximum(1.0, kap.reshape(B, H, -1).max(-1))
+    flat = float(K.max()) < 50
+    for n in ("dq", "dk", "dv"):
+        scale = head_scale(ref[n])
+        he = np.abs(got[n] - ref[n]).reshape(B, H, -1).max(-1) / scale
+        print("%s head-normwise %.3e  (K_h max %.1f)" % (n, float(he.max()), float(K.max())))
+        _record(float((he / K).max()))
+        assert np.all(he <= tol * K), (n, float(he.max()), float(K.max()))
+        if flat:
+            assert float(he.max()) < tol, (n, float(he.max()))
+    if m is not None:
+        padded = np.broadcast_to(m[:, None, :], (B, H, Nk))
+        assert float(np.abs(got["dk"][padded]).max(initial=0.0)) == 0.0
+        assert float(np.abs(got["dv"][padded]).max(initial=0.0)) == 0.0

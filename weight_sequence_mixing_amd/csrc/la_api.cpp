@@ -868,17 +868,14 @@ const BwdEntry* find_bwd(int in_dtype, int phi, int dk, int F, int dv)
 
 // Shape checks of the backward beyond the forward's; sets F, the forward entry
 // that runs the segment-state pass and the entry of the backward sweeps.
-// Random features (allow_rf): both entries are those of the identity map at
-// d_k = F, run on phi(q), phi(k) computed beforehand.
+// Random features: both entries are those of the identity map at d_k = F,
+// run on phi(q), phi(k) computed beforehand.
 la_status check_backward(const la_shape* shape, const la_phi* phi, int* F, const KernelEntry** ent,
-                         const BwdEntry** bent, bool allow_rf)
+                         const BwdEntry** bent)
 {
     la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, F, ent);
     if (st != LA_OK) return st;
-    const bool rf = allow_rf && is_rf(phi->kind);
-    if (phi->kind != LA_PHI_ELU1 && phi->kind != LA_PHI_RELU && !rf)
-        return fail(LA_ERR_UNSUPPORTED, allow_rf ? "unsupported feature map for the backward"
-                                                 : "the non-causal backward supports the elementwise feature maps (elu+1, ReLU)");
+    const bool rf = is_rf(phi->kind);
     if (shape->out_dtype != shape->in_dtype)
         return fail(LA_ERR_UNSUPPORTED, "the backward takes y and dy in the input type (out_dtype == in_dtype)");
     if (rf) {
@@ -932,19 +929,78 @@ struct BwdPlan {
 size_t round256(size_t floats) { return ((floats * sizeof(float) + 255) & ~size_t(255)) / sizeof(float); }
 size_t round256b(size_t bytes) { return (bytes + 255) & ~size_t(255); }
 
-// Random-feature backward buffers after the plan's: phi(q), phi(k) in the
-// input type and d phi(q), d phi(k) in fp32, [B*H*N, F] each.
+// Random-feature backward buffers after the plan's: phi(q) [rows_q, F] and
+// phi(k) [rows_k, F] in the input type, d phi(q) and d phi(k) in fp32.
 struct RfBufs {
-    size_t feat_bytes, dphi_bytes, bytes;
+    size_t fq, fk, dfq, dfk, bytes;
 };
-RfBufs rf_bufs(const la_shape* s, int F)
+RfBufs rf_bufs(const la_shape* s, int F, size_t rows_q, size_t rows_k)
 {
     RfBufs b;
-    const size_t rows = (size_t)(s->B * s->H * s->N);
-    b.feat_bytes = round256b(rows * F * elem_size(s->in_dtype));
-    b.dphi_bytes = round256b(rows * F * sizeof(float));
-    b.bytes = 2 * b.feat_bytes + 2 * b.dphi_bytes;
+    const size_t es = elem_size(s->in_dtype);
+    b.fq = round256b(rows_q * F * es);
+    b.fk = round256b(rows_k * F * es);
+    b.dfq = round256b(rows_q * F * sizeof(float));
+    b.dfk = round256b(rows_k * F * sizeof(float));
+    b.bytes = b.fq + b.fk + b.dfq + b.dfk;
     return b;
+}
+
+// The feature-map end of the random-feature backward: phi(q), phi(k) into
+// the buffers at `base` (laid out as rf_bufs), the kernels' pointers then
+// redirected to them; rf_finish maps d phi back to dq, dk through omega.
+struct RfRoute {
+    RfGradArgs g;
+    void* fq;
+    void* fk;
+    float* dfq;
+    float* dfk;
+};
+hipError_t rf_begin(const la_phi* phi, const la_shape* s, int64_t rows_q, int64_t rows_k, const RfBufs& rb,
+                    char* base, const void* q, const void* k, RfRoute* r, hipStream_t strm)
+{
+    std::memset(&r->g, 0, sizeof(r->g));
+    r->fq = base;
+    r->fk = base + rb.fq;
+    r->dfq = reinterpret_cast<float*>(base + rb.fq + rb.fk);
+    r->dfk = reinterpret_cast<float*>(base + rb.fq + rb.fk + rb.dfq);
+    r->g.omega = phi->omega;
+    r->g.dk = s->d_k;
+    r->g.m = phi->m;
+    r->g.scale = phi->qk_scale;
+    r->g.sign = rf_sign(phi->kind);
+    r->g.in_f32 = s->in_dtype == LA_F32;
+    r->g.H = (int32_t)s->H;
+    RfGradArgs a = r->g;
+    a.x = q;
+    a.out = r->fq;
+    a.rows = rows_q;
+    hipError_t e = launch(LA_KERNEL_RF_FEATURES, [&] { return launch_rf_grad(a, false, strm); });
+    if (e != hipSuccess) return e;
+    a.x = k;
+    a.out = r->fk;
+    a.rows = rows_k;
+    return launch(LA_KERNEL_RF_FEATURES, [&] { return launch_rf_grad(a, false, strm); });
+}
+hipError_t rf_finish(const RfRoute& r, int64_t rows_q, int64_t rows_k, int64_t n_k, const uint8_t* kpm,
+                     const void* q, const void* k, void* dq, void* dk, hipStream_t strm)
+{
+    RfGradArgs a = r.g;
+    a.x = q;
+    a.dphi = r.dfq;
+    a.out = dq;
+    a.rows = rows_q;
+    hipError_t e = launch(LA_KERNEL_RF_VJP, [&] { return launch_rf_grad(a, true, strm); });
+    if (e != hipSuccess) return e;
+    // keys: rows (b*H + h)*n_k + n, padded keys get dk = 0
+    a.x = k;
+    a.dphi = r.dfk;
+    a.out = dk;
+    a.rows = rows_k;
+    a.kpm = kpm;
+    a.N = n_k;
+    a.kpm_stride = n_k;
+    return launch(LA_KERNEL_RF_VJP, [&] { return launch_rf_grad(a, true, strm); });
 }
 
 BwdPlan bwd_plan(const la_shape* s, int F, int C)
@@ -973,11 +1029,12 @@ size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi)
     const KernelEntry* e = nullptr;
     const BwdEntry* be = nullptr;
     const std::string saved = g_last_error;
-    const la_status st = check_backward(shape, phi, &F, &e, &be, true);
+    const la_status st = check_backward(shape, phi, &F, &e, &be);
     g_last_error = saved;
     if (st != LA_OK) return 0;
     const size_t base = bwd_plan(shape, F, be->C).bytes;
-    return is_rf(phi->kind) && shape->N > 0 ? base + rf_bufs(shape, F).bytes : base;
+    const size_t rows = (size_t)(shape->B * shape->H * shape->N);
+    return is_rf(phi->kind) && shape->N > 0 ? base + rf_bufs(shape, F, rows, rows).bytes : base;
 }
 
 la_status la_backward_causal(const void* q, const void* k, const void* v, const void* y, const void* dy,
@@ -990,7 +1047,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     int F = 0;
     const KernelEntry* ent = nullptr;
     const BwdEntry* bent = nullptr;
-    la_status st = check_backward(shape, phi, &F, &ent, &bent, true);
+    la_status st = check_backward(shape, phi, &F, &ent, &bent);
     if (st != LA_OK) return st;
     const bool rf = is_rf(phi->kind);
     if ((S_in == nullptr) != (z_in == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_in and z_in must be given together");
@@ -1032,56 +1089,33 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     const size_t rows = (size_t)BH * shape->N;
     if ((st = check_bwd_io(q, k, v, y, dy, dq, dk, dv, shape, rows, rows)) != LA_OK) return st;
     const BwdPlan plan = bwd_plan(shape, F, bent->C);
-    const RfBufs rb = rf_bufs(shape, F);
+    const RfBufs rb = rf_bufs(shape, F, rows, rows);
     const size_t need = plan.bytes + (rf ? rb.bytes : 0);
     if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (workspace_bytes < need)
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     float* tok = static_cast<float*>(workspace);
+    float* segs = tok + round256(plan.tok_floats);
+    float* tseg = segs + round256(plan.seg_floats);
+    float* dlp = tseg + round256((size_t)plan.P * BH * plan.SZ);
+    float* drows = dlp + round256((size_t)plan.P * BH);
     // random features: the sweeps run on phi(q), phi(k) (identity map) and
     // write d phi in fp32; dq and dk follow from it through omega at the end
     const void* q_in = q;
     const void* k_in = k;
     void* dq_out = dq;
     void* dk_out = dk;
-    RfGradArgs rg;
-    std::memset(&rg, 0, sizeof(rg));
+    RfRoute rr;
     if (rf) {
-        char* base = static_cast<char*>(workspace) + plan.bytes;
-        void* fq = base;
-        void* fk = base + rb.feat_bytes;
-        float* dfq = reinterpret_cast<float*>(base + 2 * rb.feat_bytes);
-        float* dfk = reinterpret_cast<float*>(base + 2 * rb.feat_bytes + rb.dphi_bytes);
-        rg.omega = phi->omega;
-        rg.rows = (int64_t)rows;
-        rg.dk = shape->d_k;
-        rg.m = phi->m;
-        rg.scale = phi->qk_scale;
-        rg.sign = rf_sign(phi->kind);
-        rg.in_f32 = shape->in_dtype == LA_F32;
-        rg.N = shape->N;
-        rg.H = (int32_t)shape->H;
-        rg.kpm_stride = shape->N;
-        RfGradArgs fa = rg;
-        fa.x = q;
-        fa.out = fq;
-        hipError_t e = launch(LA_KERNEL_RF_FEATURES, [&] { return launch_rf_grad(fa, false, strm); });
-        if (e == hipSuccess) {
-            fa.x = k;
-            fa.out = fk;
-            e = launch(LA_KERNEL_RF_FEATURES, [&] { return launch_rf_grad(fa, false, strm); });
-        }
+        hipError_t e = rf_begin(phi, shape, (int64_t)rows, (int64_t)rows, rb, static_cast<char*>(workspace) + plan.bytes,
+                                q, k, &rr, strm);
         if (e != hipSuccess) return hip_fail(e, "backward: random-feature launch");
-        q_in = fq;
-        k_in = fk;
-        dq_out = dfq;
-        dk_out = dfk;
+        q_in = rr.fq;
+        k_in = rr.fk;
+        dq_out = rr.dfq;
+        dk_out = rr.dfk;
     }
-    float* segs = tok + round256(plan.tok_floats);
-    float* tseg = segs + round256(plan.seg_floats);
-    float* dlp = tseg + round256((size_t)plan.P * BH * plan.SZ);
-    float* drows = dlp + round256((size_t)plan.P * BH);
     DlamArgs da;
     std::memset(&da, 0, sizeof(da));
     da.tseg = tseg;
@@ -1204,18 +1238,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     }
     if (rf) {
         // dq, dk = J_phi^T d phi (padded keys: 0)
-        RfGradArgs va = rg;
-        va.x = q;
-        va.dphi = static_cast<const float*>(dq_out);
-        va.out = dq;
-        e = launch(LA_KERNEL_RF_VJP, [&] { return launch_rf_grad(va, true, strm); });
-        if (e == hipSuccess) {
-            va.x = k;
-            va.dphi = static_cast<const float*>(dk_out);
-            va.out = dk;
-            va.kpm = key_padding_mask;
-            e = launch(LA_KERNEL_RF_VJP, [&] { return launch_rf_grad(va, true, strm); });
-        }
+        e = rf_finish(rr, (int64_t)rows, (int64_t)rows, shape->N, key_padding_mask, q, k, dq, dk, strm);
         if (e != hipSuccess) return hip_fail(e, "backward: random-feature gradient launch");
     }
     return ok();
@@ -1255,10 +1278,12 @@ size_t la_workspace_size_backward_cross(const la_shape* shape, int64_t n_kv, con
     const KernelEntry* e = nullptr;
     const BwdEntry* be = nullptr;
     const std::string saved = g_last_error;
-    const la_status st = check_backward(shape, phi, &F, &e, &be, false);
+    const la_status st = check_backward(shape, phi, &F, &e, &be);
     g_last_error = saved;
     if (st != LA_OK || shape->N < 1 || n_kv < 1 || n_kv > INT64_MAX / 4) return 0;
-    return cross_bwd_plan(shape, n_kv, F, e->C, be->C).bytes;
+    const size_t base = cross_bwd_plan(shape, n_kv, F, e->C, be->C).bytes;
+    const size_t BH = (size_t)(shape->B * shape->H);
+    return is_rf(phi->kind) ? base + rf_bufs(shape, F, BH * shape->N, BH * n_kv).bytes : base;
 }
 
 la_status la_backward_cross(const void* q, const void* k, const void* v, const void* y, const void* dy,
@@ -1269,8 +1294,9 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     int F = 0;
     const KernelEntry* ent = nullptr;
     const BwdEntry* bent = nullptr;
-    la_status st = check_backward(shape, phi, &F, &ent, &bent, false);
+    la_status st = check_backward(shape, phi, &F, &ent, &bent);
     if (st != LA_OK) return st;
+    const bool rf = is_rf(phi->kind);
     if (shape->N < 1) return fail(LA_ERR_INVALID_ARGUMENT, "N must be >= 1");
     if (n_kv < 1 || n_kv > INT64_MAX / 4) return fail(LA_ERR_INVALID_ARGUMENT, "n_kv=%lld must be >= 1", (long long)n_kv);
     if ((st = check_eps(eps)) != LA_OK) return st;
@@ -1279,11 +1305,30 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     if ((st = check_bwd_io(q, k, v, y, dy, dq, dk, dv, shape, (size_t)BH * shape->N, (size_t)BH * n_kv)) != LA_OK)
         return st;
     const CrossBwdPlan plan = cross_bwd_plan(shape, n_kv, F, ent->C, bent->C);
-    if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.bytes);
-    if (workspace_bytes < plan.bytes)
-        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.bytes, workspace_bytes);
+    const int64_t rows_q = BH * shape->N, rows_k = BH * n_kv;
+    const RfBufs rb = rf_bufs(shape, F, (size_t)rows_q, (size_t)rows_k);
+    const size_t need = plan.bytes + (rf ? rb.bytes : 0);
+    if (!workspace) return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (workspace_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    // random features: as the causal backward, the sweeps run on phi(q),
+    // phi(k) with the identity map and d phi returns through omega
+    const void* q_in = q;
+    const void* k_in = k;
+    void* dq_out = dq;
+    void* dk_out = dk;
+    RfRoute rr;
+    if (rf) {
+        hipError_t e0 = rf_begin(phi, shape, rows_q, rows_k, rb, static_cast<char*>(workspace) + plan.bytes, q, k, &rr,
+                                 strm);
+        if (e0 != hipSuccess) return hip_fail(e0, "cross backward: random-feature launch");
+        q_in = rr.fq;
+        k_in = rr.fk;
+        dq_out = rr.dfq;
+        dk_out = rr.dfk;
+    }
     float* sws = static_cast<float*>(workspace);
     float* aws = sws + plan.state_floats;
     const int64_t FD = (int64_t)F * shape->d_v;
@@ -1294,8 +1339,8 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     // total state over the kept keys: segment sums, then their sum into slot 0
     FwdArgs l;
     std::memset(&l, 0, sizeof(l));
-    l.q = q;
-    l.k = k;
+    l.q = q_in;
+    l.k = k_in;
     l.v = v;
     l.N = n_kv;
     l.n_len = n_kv;
@@ -1331,13 +1376,13 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     // query sweep: dq, and the segments' adjoint sums
     BwdArgs b;
     std::memset(&b, 0, sizeof(b));
-    b.q = q;
-    b.k = k;
+    b.q = q_in;
+    b.k = k_in;
     b.v = v;
     b.y = y;
     b.gy = dy;
-    b.dq = dq;
-    b.dk = dk;
+    b.dq = dq_out;
+    b.dk = dk_out;
     b.dv = dv;
     b.BH = (int32_t)BH;
     b.H = (int32_t)shape->H;
@@ -1369,6 +1414,10 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     bk.src_stride = plan.SZ; bk.src_zstride = plan.SZ; bk.src_seg_stride = 0;
     if ((e = launch(LA_KERNEL_BWD_NCKV, [&] { return bent->bwd(bk, BMODE_NCKV, strm); })) != hipSuccess)
         return hip_fail(e, "cross backward: dk dv launch");
+    if (rf) {
+        e = rf_finish(rr, rows_q, rows_k, n_kv, key_padding_mask, q, k, dq, dk, strm);
+        if (e != hipSuccess) return hip_fail(e, "cross backward: random-feature gradient launch");
+    }
     return ok();
 }
 
