@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["la_forward.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h", "la_backward.h"]
+KERNEL_SOURCES = ["la_forward.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h", "la_backward.h",
+                  "la_rf_grad.hip"]
 
 
 def log(*a):
@@ -627,7 +628,8 @@ def state_copy(ctx, B=256, H=32, F=128, D=128, steps=50):
 # write <dir>/<counter>_<tag>/**/*_counter_collection.csv.  The counters are
 # scaled by what they read for the library's state copy, whose bytes are known.
 COUNTER_TAGS = {"copy": None, "w2": 2, "w3": 3, "w4": 4, "w5": 5,
-                "backward_w2": "elu1_backward_B4_H8_N4096_d64_bf16"}
+                "backward_w2": "elu1_backward_B4_H8_N4096_d64_bf16",
+                "rf_backward_w5": "trigrf_m128_backward_B1_H16_N65536_d64_bf16"}
 
 
 def _kernel_label(mangled):
@@ -649,6 +651,10 @@ def _kernel_label(mangled):
                 "4": "la_bwd_kv_kernel (non-causal dk dv)"}.get(mode, "la_bwd_kv_kernel")
     if "la_decode_kernel" in mangled:
         return "la_decode_kernel"
+    if "la_rf_features_kernel" in mangled:
+        return "la_rf_features_kernel"
+    if "la_rf_vjp_kernel" in mangled:
+        return "la_rf_vjp_kernel"
     if "la_scan_kernel" in mangled:
         return "la_scan_kernel"
     if "la_fwd_kernel" in mangled:
