@@ -130,3 +130,51 @@ def test_graph_varlen_and_cross():  # cross attention forward and backward
             t.fill_(float("nan"))
 
     _replay_and_compare(graph, outs, eager, scramble)
+
+
+def test_graph_random_feature_forward_and_backward():
+    # m = 64 random features (F = 128), d = 64 bf16: forward, causal backward
+    # with a padded batch (feature pass, identity-map sweeps, vector-Jacobian
+    # products) and the cross backward
+    from gpu_util import phi_for
+    wl = si.workload(5).with_(m=64)
+    B, H, N, d = 2, 2, 700, 64
+    inp = si.make_inputs(wl, B=B, H=H, N=N)
+    q, k, v = (to_dev(inp, n, "bf16") for n in ("q", "k", "v"))
+    phi = phi_for(wl, inp["omega"])
+    lam = [0.97, 1.0]
+    mask = torch.from_numpy(si.make_key_padding_mask(B, N, "random", seed=6)).to(DEV)
+    g = torch.randn(B, H, N, d, device=DEV).to(torch.bfloat16)
+    y = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=DEV)
+    yc = torch.empty_like(y)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dqc, dkc, dvc = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsf = _ws(la.la_workspace_size(B, H, N, d, d, phi=phi))
+    wsb = _ws(la.la_workspace_size_backward(B, H, N, d, d, phi=phi))
+    wsc = _ws(la.la_workspace_size_cross(B, H, N, N, d, d, phi=phi))
+    wscb = _ws(la.la_workspace_size_backward_cross(B, H, N, N, d, d, phi=phi))
+
+    def run():
+        la.la_forward_causal_masked(q, k, v, y, mask, phi=phi, lambda_h=lam, workspace=wsf)
+        la.la_backward_causal(q, k, v, y, g, dq, dk, dv, phi=phi, lambda_h=lam, key_padding_mask=mask,
+                              workspace=wsb)
+        la.la_forward_cross(q, k, v, yc, mask, phi=phi, workspace=wsc)
+        la.la_backward_cross(q, k, v, yc, g, dqc, dkc, dvc, mask, phi=phi, workspace=wscb)
+
+    run()
+    torch.cuda.synchronize()
+    outs = {"y": y, "dq": dq, "dk": dk, "dv": dv, "yc": yc, "dqc": dqc, "dkc": dkc, "dvc": dvc}
+    eager = {n: t.clone() for n, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.synchronize()
+
+    def scramble():
+        for t in outs.values():
+            t.fill_(float("nan"))
+
+    _replay_and_compare(graph, outs, eager, scramble)
