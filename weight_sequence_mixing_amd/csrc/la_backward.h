@@ -93,6 +93,22 @@ template <class T, int PHI> __device__ __forceinline__ float phi_deriv_from_phi(
     else return p < 1.f ? p : 1.f;
 }
 
+// This wave's FBW blocks of a per-feature-block register array (blocks
+// wave * FBW + u), read with compile-time indices: a compare over the waves
+// replaces the run-time index, which for 16 blocks (F = 256) moved the whole
+// array to scratch memory.  Smaller arrays keep the run-time index (the
+// copies would cost registers, and occupancy, there).
+template <int NW, int FBW, int N>
+__device__ __forceinline__ void wave_blocks(const f32x4 (&src)[N], int wave, f32x4 (&dst)[FBW]) {
+#pragma unroll
+    for (int u = 0; u < FBW; ++u) {
+        dst[u] = src[u];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            if (w * FBW + u < N && wave == w) dst[u] = src[(w * FBW + u) % N];
+    }
+}
+
 // dq / dk rows: the input type, or fp32 d phi for the identity map (the
 // random-feature backward maps it through omega afterwards)
 template <class T, int PHI>
@@ -336,6 +352,13 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
         Frag<T> zf[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) zf[kb] = frag_acc<T>(accZ[2 * kb], accZ[2 * kb + 1]);
+        // this wave's z (and dz/dlambda) tiles for d phi(q)
+        constexpr bool WCOPY = FB >= 16;
+        f32x4 zw[WCOPY ? FBW : 1], tzw[(WCOPY && DL) ? FBW : 1];
+        if constexpr (WCOPY) {
+            wave_blocks<NW, FBW>(accZ, wave, zw);
+            if constexpr (DL) wave_blocks<NW, FBW>(accTz, wave, tzw);
+        }
 #pragma unroll
         for (int ib = 0; ib < QB; ++ib) {
             const int i = 16 * ib + l16;
@@ -440,8 +463,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float p = pq4[r];
-                        rs_ += p * (inter[r] + accZ[fb][r] * dden);
-                        rt_ += p * (tint[r] + accTz[fb][r] * dden);
+                        const float zr = WCOPY ? zw[WCOPY ? u : 0][r] : accZ[fb][r];
+                        const float tr = WCOPY ? tzw[WCOPY ? u : 0][r] : accTz[fb][r];
+                        rs_ += p * (inter[r] + zr * dden);
+                        rt_ += p * (tint[r] + tr * dden);
                     }
                     dl += (float)(i + 1) * lam_pow(l2l, i) * rs_ + lqi * rt_;
                 }
@@ -450,7 +475,8 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_q_kernel(const BwdArgs a)
                     float o[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float dp = lqi * (inter[r] + accZ[fb][r] * dden) + intra[r];
+                        const float zr = WCOPY ? zw[WCOPY ? u : 0][r] : accZ[fb][r];
+                        const float dp = lqi * (inter[r] + zr * dden) + intra[r];
                         o[r] = dp * phi_deriv_from_phi<T, PHI>(ph[r]);
                     }
                     store_grad<T, PHI>(a.dq, (row0 + t0 + i) * DK + 16 * fb + 4 * g, o);
@@ -759,6 +785,10 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
         __syncthreads();
 
         if constexpr (!RL) {
+            // this wave's carried u tiles for d phi(k)
+            constexpr bool WCOPY = FB >= 16;
+            f32x4 uw[WCOPY ? FBW : 1];
+            if constexpr (WCOPY) wave_blocks<NW, FBW>(accu, wave, uw);
             // per 16-key block: A and B score tiles (rows i, column j), dv, d phi(k)
 #pragma unroll
             for (int jb = 0; jb < QB; ++jb) {
@@ -826,7 +856,8 @@ __global__ void __launch_bounds__(NW * 64, 1) la_bwd_kv_kernel(const BwdArgs a)
                         const f32x4 ph = ld4f(sK + TF::off(j, 16 * fb + 4 * g));
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float dp = intra[r] + lj * (inter[r] + accu[fb][r]);
+                            const float ur = WCOPY ? uw[WCOPY ? u : 0][r] : accu[fb][r];
+                            const float dp = intra[r] + lj * (inter[r] + ur);
                             o[r] = dp * phi_deriv_from_phi<T, PHI>(ph[r]);
                         }
                         store_grad<T, PHI>(a.dk, (row0 + t0 + j) * DK + 16 * fb + 4 * g, o);
