@@ -5,20 +5,33 @@
 //   x' = s x,  u_r = omega_r . x'  (r < m),  c = exp(sigma |x'|^2 / 2) / sqrt(m),
 //   phi(x) = c [cos u_1 .. cos u_m, sin u_1 .. sin u_m]        (F = 2m)
 // with sigma = -1, 0 or +1 for the three kinds.  The backward computes phi(q),
-// phi(k) once (la_rf_features_kernel), runs the elementwise backward sweeps
-// on them as if they were the inputs (identity map), and maps the resulting
-// d phi back to the inputs with the vector-Jacobian product of the map
-// (la_rf_vjp_kernel):
+// phi(k) once (the features kernels), runs the elementwise backward sweeps on
+// them as if they were the inputs (identity map), and maps the resulting
+// d phi back to the inputs with the vector-Jacobian product of the map (the
+// vjp kernels):
 //   g_r   = c (-sin u_r dphi_r + cos u_r dphi_{m+r}),
 //   P     = sum_r c (cos u_r dphi_r + sin u_r dphi_{m+r})       (= phi . dphi),
 //   dx    = s (omega^T g + sigma x' P).
-// Both kernels recompute u in fp32 from the stored x and fp32 omega, one
-// workgroup per TB rows, the rows' scaled x' in LDS.  Phase A (u, sine,
-// cosine): thread j owns feature r = j % m and keeps omega's row r in
-// registers; the threads of one r step through the rows, reading each x'
-// row as 16-byte broadcasts.  Phase B (dx): thread j owns input column
-// d = j % d_k and keeps omega's column d in registers, reading g rows the
-// same way.
+//
+// bf16 inputs: both products run on the matrix cores, one wave per 16 rows.
+// U^T = omega' X^T with omega' = omega s / (2 pi) as bf16 high and low parts
+// (the angles come out in revolutions, the unit of the hardware sine and
+// cosine, and x is exact in bf16), then dX^T = omega^T G^T with omega and G
+// each split into high and low parts (three products: hi.hi, lo.hi, hi.lo).
+// In the accumulator of U^T a lane holds features 16 rb + 4 (l/16) + 0..3 of
+// token l%16; two such tiles are exactly the lane's B operand of the second
+// product (see la_device.h), so g never leaves registers, and the lane's x
+// fragment holds the x' entries of the dx^T tile it ends with.  omega's
+// operand fragments of both products are built once per workgroup in LDS.
+//
+// fp32 inputs: fp32 vector arithmetic, one workgroup per kRfRows rows with
+// the rows' x' in LDS.  Phase A (u, sine, cosine): thread j owns feature
+// r = j % m and keeps omega's row r in registers; the threads of one r step
+// through the rows, reading each x' row as 16-byte broadcasts.  Phase B (dx):
+// thread j owns input column d = j % d_k and keeps omega's column d in
+// registers, reading g rows the same way.
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -28,16 +41,6 @@ constexpr int kRfThreads = 256;
 constexpr int kRfRows = 64;        // rows (tokens) per workgroup
 constexpr int kRfMaxM = 128;       // largest m
 
-template <class T> __device__ __forceinline__ void rf_sincos(float u, float* s, float* c);
-template <> __device__ __forceinline__ void rf_sincos<bf16>(float u, float* s, float* c) {
-    *s = __sinf(u);
-    *c = __cosf(u);
-}
-template <> __device__ __forceinline__ void rf_sincos<float>(float u, float* s, float* c) { sincosf(u, s, c); }
-
-template <class T> __device__ __forceinline__ float rf_exp(float x);
-template <> __device__ __forceinline__ float rf_exp<bf16>(float x) { return __expf(x); }
-template <> __device__ __forceinline__ float rf_exp<float>(float x) { return expf(x); }
 
 // Shared set-up: the scaled rows x' of this workgroup in LDS ([TB][DK],
 // zero past the end) and each row's prefactor c.
@@ -54,7 +57,7 @@ __device__ __forceinline__ void rf_stage(const RfGradArgs& a, int64_t r0, int nt
     if (tid < kRfRows) {
         float s2 = 0.f;
         for (int d = 0; d < DK; ++d) s2 += sX[tid * DK + d] * sX[tid * DK + d];
-        sC[tid] = rf_exp<T>(0.5f * a.sign * s2) * rsqrtf((float)a.m);
+        sC[tid] = expf(0.5f * a.sign * s2) * rsqrtf((float)a.m);
     }
     __syncthreads();
 }
@@ -92,7 +95,7 @@ __global__ void __launch_bounds__(kRfThreads) la_rf_features_kernel(const RfGrad
     for (int t = tid / m; t < nt; t += G) {
         const float u = rf_dot<DK>(w, sX + t * DK);
         float sn, cs;
-        rf_sincos<T>(u, &sn, &cs);
+        sincosf(u, &sn, &cs);
         out[(r0 + t) * F + r] = from_f32<T>(sC[t] * cs);
         out[(r0 + t) * F + m + r] = from_f32<T>(sC[t] * sn);
     }
@@ -138,7 +141,7 @@ __global__ void __launch_bounds__(kRfThreads) la_rf_vjp_kernel(const RfGradArgs 
             if (t < nt) {
                 const float u = rf_dot<DK>(w, sX + t * DK);
                 float sn, cs;
-                rf_sincos<T>(u, &sn, &cs);
+                sincosf(u, &sn, &cs);
                 g = sC[t] * (cs * ds[j] - sn * dc[j]);
                 p = sC[t] * (cs * dc[j] + sn * ds[j]);
             }
@@ -182,6 +185,285 @@ __global__ void __launch_bounds__(kRfThreads) la_rf_vjp_kernel(const RfGradArgs 
     }
 }
 
+// ---- bf16 inputs: matrix-core kernels -----------------------------------
+
+constexpr int kMfWaves = 8;  // waves per workgroup; each wave takes 16-row tiles
+
+template <int DK, int M> struct RfMf {
+    static constexpr int KX = DK / 32;  // k blocks of the first product (over d)
+    static constexpr int RB = M / 16;   // 16-feature row blocks of U^T
+    static constexpr int DB = DK / 16;  // 16-column row blocks of dX^T
+    static constexpr int KF = M / 32;   // k blocks of the second product (over r)
+    // omega' fragments of U^T = omega' X^T: (rb, kb, part)
+    static constexpr int NA = RB * KX * 2;
+    // omega^T fragments of dX^T = omega^T G^T: (db, kf, part)
+    static constexpr int NB = DB * KF * 2;
+    __device__ static __forceinline__ int fa(int rb, int kb, int part) { return (rb * KX + kb) * 2 + part; }
+    __device__ static __forceinline__ int fb(int db, int kf, int part) { return NA + (db * KF + kf) * 2 + part; }
+};
+
+// High and low bf16 parts of 8 fp32 values (hi + lo = w to about 16 bits).
+__device__ __forceinline__ void rf_split(const float (&w)[8], Frag<bf16>& hi, Frag<bf16>& lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi.v[e] = (bf16)w[e];
+        lo.v[e] = (bf16)(w[e] - (float)hi.v[e]);
+    }
+}
+
+// Builds omega's operand fragments of the workgroup in LDS.  Lane L of a
+// fragment holds row L%16 of its 16-row block at the k positions K(L/16) of
+// its 32-wide k block: for U^T, row = feature, k = input column (omega
+// scaled into revolutions); for dX^T, row = input column, k = feature.
+template <int DK, int M, bool NEED_B>
+__device__ __forceinline__ void rf_build_frags(const RfGradArgs& a, Frag<bf16>* sOm)
+{
+    using P = RfMf<DK, M>;
+    const float om_scale = a.scale * 0.159154943091895336f;  // s / (2 pi)
+    constexpr int NPAIR = (P::NA + (NEED_B ? P::NB : 0)) / 2;
+    for (int i = threadIdx.x; i < NPAIR * 64; i += kMfWaves * 64) {
+        const int pr = i / 64, L = i % 64, r16 = L % 16, g = L / 16;
+        float w[8];
+        int idx;
+        if (pr < P::NA / 2) {
+            const int rb = pr / P::KX, kb = pr % P::KX;
+            const float* p = a.omega + (16 * rb + r16) * DK + 32 * kb + 4 * g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w[e] = p[e] * om_scale;
+                w[4 + e] = p[16 + e] * om_scale;
+            }
+            idx = P::fa(rb, kb, 0);
+        } else {
+            const int q = pr - P::NA / 2, db = q / P::KF, kf = q % P::KF;
+            const float* p = a.omega + (32 * kf + 4 * g) * DK + 16 * db + r16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w[e] = p[e * DK];
+                w[4 + e] = p[(16 + e) * DK];
+            }
+            idx = P::fb(db, kf, 0);
+        }
+        Frag<bf16> hi, lo;
+        rf_split(w, hi, lo);
+        sOm[idx * 64 + L] = hi;
+        sOm[(idx + 1) * 64 + L] = lo;
+    }
+    __syncthreads();
+}
+
+// Per-tile front end shared by both kernels: this lane's token row (clamped
+// into range for the loads), its x fragments, the prefactor c and the
+// accumulator tiles of U^T (angles in revolutions).
+template <int DK, int M>
+struct RfTile {
+    Frag<bf16> xf[DK / 32];
+    float c;
+};
+
+template <int DK, int M>
+__device__ __forceinline__ void rf_load_x(const RfGradArgs& a, int64_t tr, int g, RfTile<DK, M>& t)
+{
+    const bf16* x = (const bf16*)a.x + tr * DK;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) t.xf[kb] = frag_rm(x, 0, 0, 32 * kb, g);
+}
+
+template <int DK, int M>
+__device__ __forceinline__ void rf_prefactor(const RfGradArgs& a, RfTile<DK, M>& t)
+{
+    float s2 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = (float)t.xf[kb].v[e];
+            s2 += v * v;
+        }
+    s2 += __shfl_xor(s2, 16, 64);
+    s2 += __shfl_xor(s2, 32, 64);
+    t.c = __expf(0.5f * a.sign * a.scale * a.scale * s2) * rsqrtf((float)M);
+}
+
+// U^T block rb (features 16 rb..) against this lane's token, in revolutions.
+template <int DK, int M>
+__device__ __forceinline__ f32x4 rf_angles(const Frag<bf16>* sOm, const RfTile<DK, M>& t, int rb, int lane)
+{
+    using P = RfMf<DK, M>;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < P::KX; ++kb) {
+        mma(acc, sOm[P::fa(rb, kb, 0) * 64 + lane], t.xf[kb]);
+        mma(acc, sOm[P::fa(rb, kb, 1) * 64 + lane], t.xf[kb]);
+    }
+    return acc;
+}
+
+// Zero that the compiler cannot see through, taken once per tile: offsetting
+// the fragment base by it keeps the fragment reads inside the tile loop
+// instead of hoisted out of it into registers (all of omega's fragments at
+// once would not fit).
+__device__ __forceinline__ int rf_opaque_zero()
+{
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    return z;
+}
+
+// Persistent grid: as many workgroups as fit on the device at once; wave w
+// of workgroup b takes tiles 8 b + w, + 8 * gridDim.x, ...
+template <class K>
+hipError_t rf_mf_launch(K kernel, const RfGradArgs& a, hipStream_t stream)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kMfWaves * 64, 0);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = (a.rows + 15) / 16;
+    const int64_t want = (tiles + kMfWaves - 1) / kMfWaves;
+    const int64_t cap = (int64_t)cus * (per_cu > 1 ? per_cu : 1);
+    const dim3 grid((unsigned)(want < cap ? want : cap)), block(kMfWaves * 64);
+    return launch_kernel(kernel, grid, block, stream, a);
+}
+
+// phi(x) for a.rows rows ([rows, 2m] bf16).
+template <int DK, int M>
+__global__ void __launch_bounds__(kMfWaves * 64) la_rf_features_mfma_kernel(const RfGradArgs a)
+{
+    using P = RfMf<DK, M>;
+    __shared__ Frag<bf16> sOm[P::NA * 64];
+    rf_build_frags<DK, M, false>(a, sOm);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int64_t tiles = (a.rows + 15) / 16;
+    bf16* out = (bf16*)a.out;
+    for (int64_t tile = (int64_t)blockIdx.x * kMfWaves + wave; tile < tiles; tile += (int64_t)gridDim.x * kMfWaves) {
+        const int64_t row = tile * 16 + l16, tr = row < a.rows ? row : a.rows - 1;
+        const Frag<bf16>* om = sOm + rf_opaque_zero();
+        RfTile<DK, M> t;
+        rf_load_x(a, tr, g, t);
+        rf_prefactor(a, t);
+        bf16* o = out + tr * (2 * M) + 4 * g;
+#pragma unroll
+        for (int rb = 0; rb < P::RB; ++rb) {
+            const f32x4 u = rf_angles(om, t, rb, lane);
+            float cs[4], sn[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                cs[r] = t.c * __builtin_amdgcn_cosf(u[r]);
+                sn[r] = t.c * __builtin_amdgcn_sinf(u[r]);
+            }
+            if (row < a.rows) {
+                st4(o + 16 * rb, cs[0], cs[1], cs[2], cs[3]);
+                st4(o + M + 16 * rb, sn[0], sn[1], sn[2], sn[3]);
+            }
+        }
+    }
+}
+
+// dx = s (omega^T g + sigma x' P) from fp32 d phi ([rows, 2m]), bf16 out;
+// rows whose key is padded (a.kpm) get dx = 0.
+template <int DK, int M>
+__global__ void __launch_bounds__(kMfWaves * 64) la_rf_vjp_mfma_kernel(const RfGradArgs a)
+{
+    using P = RfMf<DK, M>;
+    __shared__ Frag<bf16> sOm[(P::NA + P::NB) * 64];
+    rf_build_frags<DK, M, true>(a, sOm);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int64_t tiles = (a.rows + 15) / 16;
+    bf16* out = (bf16*)a.out;
+    const float s = a.scale, ssig = a.sign * a.scale * a.scale;
+    for (int64_t tile = (int64_t)blockIdx.x * kMfWaves + wave; tile < tiles; tile += (int64_t)gridDim.x * kMfWaves) {
+        const int64_t row = tile * 16 + l16, tr = row < a.rows ? row : a.rows - 1;
+        // every load of the tile first: d phi of this lane's features, x
+        const float* dp = a.dphi + tr * (2 * M) + 4 * g;
+        f32x4 dc[P::RB], ds[P::RB];
+#pragma unroll
+        for (int rb = 0; rb < P::RB; ++rb) {
+            dc[rb] = *(const f32x4*)(dp + 16 * rb);
+            ds[rb] = *(const f32x4*)(dp + M + 16 * rb);
+        }
+        const Frag<bf16>* om = sOm + rf_opaque_zero();
+        RfTile<DK, M> t;
+        rf_load_x(a, tr, g, t);
+        rf_prefactor(a, t);
+        // g (the B operand of the second product, in accumulator layout) and
+        // this lane's terms of P
+        f32x4 gt[P::RB];
+        float p = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < P::RB; ++rb) {
+            const f32x4 u = rf_angles(om, t, rb, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float cs = __builtin_amdgcn_cosf(u[r]), sn = __builtin_amdgcn_sinf(u[r]);
+                gt[rb][r] = t.c * (cs * ds[rb][r] - sn * dc[rb][r]);
+                p += cs * dc[rb][r] + sn * ds[rb][r];
+            }
+        }
+        p += __shfl_xor(p, 16, 64);
+        p += __shfl_xor(p, 32, 64);
+        p *= t.c;
+        // dX^T: lane holds input columns 16 db + 4 g + 0..3 of its token
+        f32x4 dx[P::DB];
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db) dx[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kf = 0; kf < P::KF; ++kf) {
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w[e] = gt[2 * kf][e];
+                w[4 + e] = gt[2 * kf + 1][e];
+            }
+            Frag<bf16> ghi, glo;
+            rf_split(w, ghi, glo);
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db) {
+                const Frag<bf16> whi = om[P::fb(db, kf, 0) * 64 + lane];
+                mma(dx[db], whi, ghi);
+                mma(dx[db], om[P::fb(db, kf, 1) * 64 + lane], ghi);
+                mma(dx[db], whi, glo);
+            }
+        }
+        bool zero = false;
+        if (a.kpm) {
+            const int64_t bh = tr / a.N, n = tr % a.N;
+            zero = a.kpm[(bh / a.H) * a.kpm_stride + n] != 0;
+        }
+        if (row < a.rows) {
+            bf16* o = out + row * DK + 4 * g;
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float xd = (float)t.xf[db / 2].v[4 * (db % 2) + r];
+                    v[r] = zero ? 0.f : s * dx[db][r] + ssig * xd * p;
+                }
+                st4(o + 16 * db, v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+template <int DK>
+hipError_t rf_mf_dispatch(const RfGradArgs& a, bool vjp, hipStream_t stream)
+{
+    auto go = [&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        return vjp ? rf_mf_launch(la_rf_vjp_mfma_kernel<DK, M>, a, stream)
+                   : rf_mf_launch(la_rf_features_mfma_kernel<DK, M>, a, stream);
+    };
+    switch (a.m) {
+    case 32: return go(std::integral_constant<int, 32>());
+    case 64: return go(std::integral_constant<int, 64>());
+    case 128: return go(std::integral_constant<int, 128>());
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <class T, int DK>
 hipError_t rf_launch(const RfGradArgs& a, bool vjp, hipStream_t stream)
 {
@@ -200,7 +482,7 @@ hipError_t launch_rf_grad(const RfGradArgs& a, bool vjp, hipStream_t stream)
     if (a.rows <= 0) return hipSuccess;
     if (a.m < 1 || a.m > kRfMaxM || (a.dk != 64 && a.dk != 128)) return hipErrorInvalidValue;
     if (a.in_f32) return a.dk == 64 ? rf_launch<float, 64>(a, vjp, stream) : rf_launch<float, 128>(a, vjp, stream);
-    return a.dk == 64 ? rf_launch<bf16, 64>(a, vjp, stream) : rf_launch<bf16, 128>(a, vjp, stream);
+    return a.dk == 64 ? rf_mf_dispatch<64>(a, vjp, stream) : rf_mf_dispatch<128>(a, vjp, stream);
 }
 
 }  // namespace la
