@@ -18,9 +18,10 @@
 // (the angles come out in revolutions, the unit of the hardware sine and
 // cosine, and x is exact in bf16), then dX^T = omega^T G^T with omega and G
 // each split into high and low parts (three products: hi.hi, lo.hi, hi.lo).
-// In the accumulator of U^T a lane holds features 16 rb + 4 (l/16) + 0..3 of
-// token l%16; two such tiles are exactly the lane's B operand of the second
-// product (see la_device.h), so g never leaves registers, and the lane's x
+// In the accumulator of U^T a lane holds four features of token l%16 per
+// 16-row block; a pair of blocks gives the lane eight features, which are
+// its B operand of the second product once omega^T's fragments list the same
+// features in the same order, so g never leaves registers.  The lane's x
 // fragment holds the x' entries of the dx^T tile it ends with.  omega's
 // operand fragments of both products are built once per workgroup in LDS.
 //
@@ -198,6 +199,11 @@ template <int DK, int M> struct RfMf {
     static constexpr int NA = RB * KX * 2;
     // omega^T fragments of dX^T = omega^T G^T: (db, kf, part)
     static constexpr int NB = DB * KF * 2;
+    // Feature held in accumulator row j (= 4 (l/16) + r) of U^T block rb:
+    // the blocks pair up, and lane group g of pair p holds features
+    // 32 p + 8 g + 0..7, so a lane's eight values of a pair are adjacent in
+    // phi's row and the four groups cover 64 contiguous bytes of it.
+    __device__ static __forceinline__ int feat(int rb, int j) { return 32 * (rb / 2) + 8 * (j / 4) + 4 * (rb % 2) + j % 4; }
     __device__ static __forceinline__ int fa(int rb, int kb, int part) { return (rb * KX + kb) * 2 + part; }
     __device__ static __forceinline__ int fb(int db, int kf, int part) { return NA + (db * KF + kf) * 2 + part; }
 };
@@ -212,10 +218,13 @@ __device__ __forceinline__ void rf_split(const float (&w)[8], Frag<bf16>& hi, Fr
     }
 }
 
-// Builds omega's operand fragments of the workgroup in LDS.  Lane L of a
-// fragment holds row L%16 of its 16-row block at the k positions K(L/16) of
-// its 32-wide k block: for U^T, row = feature, k = input column (omega
-// scaled into revolutions); for dX^T, row = input column, k = feature.
+// Builds omega's operand fragments of the workgroup in LDS.  For U^T, lane L
+// of fragment (rb, kb) holds feature feat(rb, L%16) of omega (scaled into
+// revolutions) at the input columns K(L/16) of k block kb.  For dX^T, lane L
+// of fragment (db, kf) holds input column 16 db + L%16 of omega at the eight
+// features 32 kf + 8 (L/16) + 0..7 -- the features its lane holds of the
+// U^T block pair kf, in the same order, which is what makes the two
+// operands of the second product agree on the contraction index.
 template <int DK, int M, bool NEED_B>
 __device__ __forceinline__ void rf_build_frags(const RfGradArgs& a, Frag<bf16>* sOm)
 {
@@ -228,7 +237,7 @@ __device__ __forceinline__ void rf_build_frags(const RfGradArgs& a, Frag<bf16>* 
         int idx;
         if (pr < P::NA / 2) {
             const int rb = pr / P::KX, kb = pr % P::KX;
-            const float* p = a.omega + (16 * rb + r16) * DK + 32 * kb + 4 * g;
+            const float* p = a.omega + P::feat(rb, r16) * DK + 32 * kb + 4 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 w[e] = p[e] * om_scale;
@@ -237,12 +246,9 @@ __device__ __forceinline__ void rf_build_frags(const RfGradArgs& a, Frag<bf16>* 
             idx = P::fa(rb, kb, 0);
         } else {
             const int q = pr - P::NA / 2, db = q / P::KF, kf = q % P::KF;
-            const float* p = a.omega + (32 * kf + 4 * g) * DK + 16 * db + r16;
+            const float* p = a.omega + (32 * kf + 8 * g) * DK + 16 * db + r16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w[e] = p[e * DK];
-                w[4 + e] = p[(16 + e) * DK];
-            }
+            for (int e = 0; e < 8; ++e) w[e] = p[e * DK];
             idx = P::fb(db, kf, 0);
         }
         Frag<bf16> hi, lo;
@@ -286,7 +292,8 @@ __device__ __forceinline__ void rf_prefactor(const RfGradArgs& a, RfTile<DK, M>&
     t.c = __expf(0.5f * a.sign * a.scale * a.scale * s2) * rsqrtf((float)M);
 }
 
-// U^T block rb (features 16 rb..) against this lane's token, in revolutions.
+// U^T block rb against this lane's token (features feat(rb, 4 g + r)), in
+// revolutions.
 template <int DK, int M>
 __device__ __forceinline__ f32x4 rf_angles(const Frag<bf16>* sOm, const RfTile<DK, M>& t, int rb, int lane)
 {
@@ -344,19 +351,22 @@ __global__ void __launch_bounds__(kMfWaves * 64) la_rf_features_mfma_kernel(cons
         RfTile<DK, M> t;
         rf_load_x(a, tr, g, t);
         rf_prefactor(a, t);
-        bf16* o = out + tr * (2 * M) + 4 * g;
+        bf16* o = out + tr * (2 * M) + 8 * g;
 #pragma unroll
-        for (int rb = 0; rb < P::RB; ++rb) {
-            const f32x4 u = rf_angles(om, t, rb, lane);
-            float cs[4], sn[4];
+        for (int pr = 0; pr < P::RB / 2; ++pr) {
+            bf16x8 cs, sn;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                cs[r] = t.c * __builtin_amdgcn_cosf(u[r]);
-                sn[r] = t.c * __builtin_amdgcn_sinf(u[r]);
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 u = rf_angles(om, t, 2 * pr + h, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    cs[4 * h + r] = (bf16)(t.c * __builtin_amdgcn_cosf(u[r]));
+                    sn[4 * h + r] = (bf16)(t.c * __builtin_amdgcn_sinf(u[r]));
+                }
             }
             if (row < a.rows) {
-                st4(o + 16 * rb, cs[0], cs[1], cs[2], cs[3]);
-                st4(o + M + 16 * rb, sn[0], sn[1], sn[2], sn[3]);
+                *(bf16x8*)(o + 32 * pr) = cs;
+                *(bf16x8*)(o + M + 32 * pr) = sn;
             }
         }
     }
@@ -377,12 +387,12 @@ __global__ void __launch_bounds__(kMfWaves * 64) la_rf_vjp_mfma_kernel(const RfG
     for (int64_t tile = (int64_t)blockIdx.x * kMfWaves + wave; tile < tiles; tile += (int64_t)gridDim.x * kMfWaves) {
         const int64_t row = tile * 16 + l16, tr = row < a.rows ? row : a.rows - 1;
         // every load of the tile first: d phi of this lane's features, x
-        const float* dp = a.dphi + tr * (2 * M) + 4 * g;
+        const float* dp = a.dphi + tr * (2 * M) + 8 * g;
         f32x4 dc[P::RB], ds[P::RB];
 #pragma unroll
         for (int rb = 0; rb < P::RB; ++rb) {
-            dc[rb] = *(const f32x4*)(dp + 16 * rb);
-            ds[rb] = *(const f32x4*)(dp + M + 16 * rb);
+            dc[rb] = *(const f32x4*)(dp + 32 * (rb / 2) + 4 * (rb % 2));
+            ds[rb] = *(const f32x4*)(dp + M + 32 * (rb / 2) + 4 * (rb % 2));
         }
         const Frag<bf16>* om = sOm + rf_opaque_zero();
         RfTile<DK, M> t;
