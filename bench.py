@@ -454,7 +454,7 @@ def backward_w2(ctx, steps=100, with_dlam=False):
 def rf_backward_w5(ctx, steps=5):
     """Backward of workload 5 (B=1 H=16 N=65536, m=128 random features, d=64
     bf16, lambda = 1): one la_backward_causal call -- phi(q) and phi(k), the
-    backward sweeps on them at F = 256 with the identity map (d phi in fp32),
+    backward sweeps on them at F = 256 with the identity map (d phi in bf16),
     and the vector-Jacobian products through omega to dq and dk."""
     import seeded_inputs as si
     torch, la = ctx.torch, ctx.la
@@ -478,10 +478,10 @@ def rf_backward_w5(ctx, steps=5):
     ids = la.KERNEL_IDS
     # per launch: the feature pass and the gradient pass each cover q or k
     kb = {ids["rf_features"]: rows * (d * 2 + F * 2),
-          ids["rf_vjp"]: rows * (d * 2 + F * 4 + d * 2),
-          ids["bwd_q"]: rows * (2 * F * 2 + 3 * d * 2 + F * 4 + 8) + P * B * H * SZ * 4,
+          ids["rf_vjp"]: rows * (d * 2 + F * 2 + d * 2),
+          ids["bwd_q"]: rows * (2 * F * 2 + 3 * d * 2 + F * 2 + 8) + P * B * H * SZ * 4,
           ids["bwd_rlocal"]: rows * (F * 2 + d * 2 + 8) + P * B * H * SZ * 4,
-          ids["bwd_kv"]: rows * (2 * F * 2 + 2 * d * 2 + 8 + F * 4 + d * 2) + P * B * H * SZ * 4,
+          ids["bwd_kv"]: rows * (2 * F * 2 + 2 * d * 2 + 8 + F * 2 + d * 2) + P * B * H * SZ * 4,
           ids["fwd_local"]: rows * (F * 2 + d * 2) + P * B * H * SZ * 4,
           ids["scan"]: 2 * P * B * H * SZ * 4}
 
@@ -651,9 +651,10 @@ def _kernel_label(mangled):
                 "4": "la_bwd_kv_kernel (non-causal dk dv)"}.get(mode, "la_bwd_kv_kernel")
     if "la_decode_kernel" in mangled:
         return "la_decode_kernel"
-    if "la_rf_features_kernel" in mangled:
+    # fp32 (vector ALU) and bf16 (matrix-core) instances
+    if "la_rf_features" in mangled:
         return "la_rf_features_kernel"
-    if "la_rf_vjp_kernel" in mangled:
+    if "la_rf_vjp" in mangled:
         return "la_rf_vjp_kernel"
     if "la_scan_kernel" in mangled:
         return "la_scan_kernel"

@@ -242,8 +242,8 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
  * dlambda follows the product rule through the chunks: the dq sweep also
  * carries T = dS/dlambda, and a reduction joins the segments.
  * Workspace: la_workspace_size_backward bytes (8 bytes per token plus the
- * segment states; random features add phi(q), phi(k) in the input type and
- * d phi(q), d phi(k) in fp32, B*H*N*2m values each). */
+ * segment states; random features add phi(q), phi(k), d phi(q) and
+ * d phi(k) in the input type, B*H*N*2m values each). */
 size_t la_workspace_size_backward(const la_shape* shape, const la_phi* phi);
 la_status la_backward_causal(const void* q, const void* k, const void* v,
                              const void* y, const void* dy,

@@ -204,11 +204,11 @@ def test_backward_validation(lib):
     assert call(shape=big, dlam=FAKE) == U                                   # no lambda gradient for fp32 d=128
     n = lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(ELU))
     assert n >= 2 * 4 * s.B * s.H * s.N                                      # 8 bytes per token at least
-    # random features add phi(q), phi(k) (input type) and d phi(q), d phi(k)
-    # (fp32) for every token: F = 2m = 128 values each
+    # random features add phi(q), phi(k), d phi(q), d phi(k) (input type, bf16
+    # here) for every token: F = 2m = 128 values each
     nrf = lib.la_workspace_size_backward(ctypes.byref(s), ctypes.byref(RF))
     rows = s.B * s.H * s.N
-    assert nrf >= n + rows * 128 * (2 + 2 + 4 + 4)
+    assert nrf >= n + rows * 128 * (2 + 2 + 2 + 2)
     ws_rf = FAKE
     assert call(phi=RF, ws=ws_rf, ws_bytes=nrf - 1) == la.binding.LA_ERR_WORKSPACE
 

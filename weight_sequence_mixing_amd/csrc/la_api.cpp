@@ -940,8 +940,8 @@ RfBufs rf_bufs(const la_shape* s, int F, size_t rows_q, size_t rows_k)
     const size_t es = elem_size(s->in_dtype);
     b.fq = round256b(rows_q * F * es);
     b.fk = round256b(rows_k * F * es);
-    b.dfq = round256b(rows_q * F * sizeof(float));
-    b.dfk = round256b(rows_k * F * sizeof(float));
+    b.dfq = round256b(rows_q * F * es);
+    b.dfk = round256b(rows_k * F * es);
     b.bytes = b.fq + b.fk + b.dfq + b.dfk;
     return b;
 }
@@ -953,8 +953,8 @@ struct RfRoute {
     RfGradArgs g;
     void* fq;
     void* fk;
-    float* dfq;
-    float* dfk;
+    void* dfq;
+    void* dfk;
 };
 hipError_t rf_begin(const la_phi* phi, const la_shape* s, int64_t rows_q, int64_t rows_k, const RfBufs& rb,
                     char* base, const void* q, const void* k, RfRoute* r, hipStream_t strm)
@@ -962,8 +962,8 @@ hipError_t rf_begin(const la_phi* phi, const la_shape* s, int64_t rows_q, int64_
     std::memset(&r->g, 0, sizeof(r->g));
     r->fq = base;
     r->fk = base + rb.fq;
-    r->dfq = reinterpret_cast<float*>(base + rb.fq + rb.fk);
-    r->dfk = reinterpret_cast<float*>(base + rb.fq + rb.fk + rb.dfq);
+    r->dfq = base + rb.fq + rb.fk;
+    r->dfk = base + rb.fq + rb.fk + rb.dfq;
     r->g.omega = phi->omega;
     r->g.dk = s->d_k;
     r->g.m = phi->m;

@@ -109,12 +109,11 @@ __device__ __forceinline__ void wave_blocks(const f32x4 (&src)[N], int wave, f32
     }
 }
 
-// dq / dk rows: the input type, or fp32 d phi for the identity map (the
-// random-feature backward maps it through omega afterwards)
+// dq / dk rows in the input type (for the identity map these are d phi,
+// which the random-feature backward maps through omega afterwards)
 template <class T, int PHI>
 __device__ __forceinline__ void store_grad(void* base, int64_t off, const float* o) {
-    if constexpr (PHI == kPhiIdentity) st4((float*)base + off, o[0], o[1], o[2], o[3]);
-    else st4((T*)base + off, o[0], o[1], o[2], o[3]);
+    st4((T*)base + off, o[0], o[1], o[2], o[3]);
 }
 
 template <class T, int DK, int F, int DV, int C, int NW, int MODE, bool DL = false>

@@ -261,12 +261,12 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 // Random-feature backward, feature-map end (la_rf_grad.hip): phi(x) of `rows`
 // rows ([rows, d_k] in, [rows, 2m] out, input type), or the vector-Jacobian
-// product dx = J_phi(x)^T dphi (dphi fp32 [rows, 2m], dx [rows, d_k] input
+// product dx = J_phi(x)^T dphi (dphi [rows, 2m] input type, dx [rows, d_k] input
 // type; rows of padded keys get 0 when kpm is set).
 struct RfGradArgs {
     const void* x;
     const float* omega;  // [m, d_k] fp32
-    const float* dphi;   // vjp only
+    const void* dphi;    // vjp only
     void* out;
     const uint8_t* kpm;  // vjp of keys: byte kpm[b * kpm_stride + n] of row (b*H + h)*N + n
     int64_t kpm_stride;

@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(kRfThreads) la_rf_features_kernel(const RfGrad
     }
 }
 
-// dx = s (omega^T g + sigma x' P) from fp32 d phi ([rows, 2m]); rows whose
+// dx = s (omega^T g + sigma x' P) from d phi ([rows, 2m], input type); rows whose
 // key is padded (a.kpm) get dx = 0.
 template <class T, int DK, int M>
 __global__ void __launch_bounds__(kRfThreads) la_rf_vjp_kernel(const RfGradArgs a)
@@ -128,8 +128,8 @@ __global__ void __launch_bounds__(kRfThreads) la_rf_vjp_kernel(const RfGradArgs 
         for (int j = 0; j < NTH; ++j) {
             const int t = t0 + j * G;
             const int64_t row = r0 + min(t, nt - 1);  // in bounds; rows past the end unused
-            dc[j] = a.dphi[row * F + r];
-            ds[j] = a.dphi[row * F + m + r];
+            dc[j] = to_f32(((const T*)a.dphi)[row * F + r]);
+            ds[j] = to_f32(((const T*)a.dphi)[row * F + m + r]);
         }
         float w[DK];
 #pragma unroll
@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(kMfWaves * 64) la_rf_features_mfma_kernel(cons
     }
 }
 
-// dx = s (omega^T g + sigma x' P) from fp32 d phi ([rows, 2m]), bf16 out;
+// dx = s (omega^T g + sigma x' P) from bf16 d phi ([rows, 2m]), bf16 out;
 // rows whose key is padded (a.kpm) get dx = 0.
 template <int DK, int M>
 __global__ void __launch_bounds__(kMfWaves * 64) la_rf_vjp_mfma_kernel(const RfGradArgs a)
@@ -387,12 +387,12 @@ __global__ void __launch_bounds__(kMfWaves * 64) la_rf_vjp_mfma_kernel(const RfG
     for (int64_t tile = (int64_t)blockIdx.x * kMfWaves + wave; tile < tiles; tile += (int64_t)gridDim.x * kMfWaves) {
         const int64_t row = tile * 16 + l16, tr = row < a.rows ? row : a.rows - 1;
         // every load of the tile first: d phi of this lane's features, x
-        const float* dp = a.dphi + tr * (2 * M) + 8 * g;
-        f32x4 dc[P::RB], ds[P::RB];
+        const bf16* dp = (const bf16*)a.dphi + tr * (2 * M) + 8 * g;
+        bf16x8 dc[P::RB / 2], ds[P::RB / 2];
 #pragma unroll
-        for (int rb = 0; rb < P::RB; ++rb) {
-            dc[rb] = *(const f32x4*)(dp + 32 * (rb / 2) + 4 * (rb % 2));
-            ds[rb] = *(const f32x4*)(dp + M + 32 * (rb / 2) + 4 * (rb % 2));
+        for (int pr = 0; pr < P::RB / 2; ++pr) {
+            dc[pr] = *(const bf16x8*)(dp + 32 * pr);
+            ds[pr] = *(const bf16x8*)(dp + M + 32 * pr);
         }
         const Frag<bf16>* om = sOm + rf_opaque_zero();
         RfTile<DK, M> t;
@@ -408,8 +408,9 @@ __global__ void __launch_bounds__(kMfWaves * 64) la_rf_vjp_mfma_kernel(const RfG
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float cs = __builtin_amdgcn_cosf(u[r]), sn = __builtin_amdgcn_sinf(u[r]);
-                gt[rb][r] = t.c * (cs * ds[rb][r] - sn * dc[rb][r]);
-                p += cs * dc[rb][r] + sn * ds[rb][r];
+                const float c1 = (float)dc[rb / 2][4 * (rb % 2) + r], s1 = (float)ds[rb / 2][4 * (rb % 2) + r];
+                gt[rb][r] = t.c * (cs * s1 - sn * c1);
+                p += cs * c1 + sn * s1;
             }
         }
         p += __shfl_xor(p, 16, 64);
