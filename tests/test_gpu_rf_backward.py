@@ -3,7 +3,8 @@ trigonometric feature maps) against the fp64 oracle's gradients, through the
 C ABI.
 
 The library computes phi(q), phi(k) in the input type, runs the backward
-sweeps on them (d phi in fp32) and maps d phi back through omega.
+sweeps on them (d phi in the input type too) and maps d phi back through
+omega.
 
 Conditioning.  Random features are sign-indefinite, so a query's denominator
 phi(q_i)^T z_i can nearly cancel -- for the first tokens of a sequence started
@@ -81,12 +82,12 @@ def run_rf_backward(wl, B, H, N, lam, mask=None, state=False, dsout=False, seed=
     return got, ref, m, kap
 
 
-def check_rf(wl, got, ref, kap):
+def check_rf(wl, got, ref, kap, names=("dq", "dk", "dv", "dS0", "dz0")):
     tol = TOL_BWD[wl.dtype]
     B, H = kap.shape[:2]
     K = np.maximum(1.0, kap.reshape(B, H, -1).max(-1))  # [B,H]
     flat = float(K.max()) < 50
-    for n in ("dq", "dk", "dv", "dS0", "dz0"):
+    for n in names:
         scale = head_scale(ref[n])
         he = np.abs(got[n] - ref[n]).reshape(B, H, -1).max(-1) / scale
         print("%s head-normwise %.3e  (K_h max %.1f)" % (n, float(he.max()), float(K.max())))
@@ -128,6 +129,36 @@ def test_rf_backward_parity(over, B, H, N, lam, mask, state, dsout):
         padded = np.broadcast_to(m[:, None, :], (B, H, N))
         assert float(np.abs(got["dk"][padded]).max(initial=0.0)) == 0.0
         assert float(np.abs(got["dv"][padded]).max(initial=0.0)) == 0.0
+
+
+def test_rf_backward_full_size_sampled_head():
+    # the benchmarked configuration (B=1 H=16 N=65536, m=128, d=64, bf16,
+    # lambda = 1) in the launch configuration the bench times, where every
+    # wave of the persistent feature and chain-rule grids takes many 16-row
+    # tiles.  Every row of every head must be written and finite; head 5 is
+    # held to the oracle's gradients of that head alone (heads are
+    # independent).
+    wl = si.workload(5)
+    B, H, N, h = wl.B, wl.H, wl.N, 5
+    lam = [wl.lam_value] * H
+    inp = si.make_inputs(wl, B=B, H=H, N=N)
+    q, k, v = (to_dev(inp, n, wl.dtype) for n in ("q", "k", "v"))
+    g_np, g = _grad_out(wl, B, H, N, 91)
+    phi = phi_for(wl, inp["omega"])
+    y = torch.empty(B, H, N, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_causal(q, k, v, y, phi=phi, lambda_h=lam, eps=wl.eps)
+    dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    la.la_backward_causal(q, k, v, y, g, dq, dk, dv, phi=phi, lambda_h=lam, eps=wl.eps)
+    torch.cuda.synchronize()
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t.float()).all()), n
+    one = {n: np.ascontiguousarray(inp[n][:, h:h + 1]) for n in ("q", "k", "v")}
+    ref = oracle.backward(one["q"], one["k"], one["v"], np.ascontiguousarray(g_np[:, h:h + 1]), lam[:1], wl.eps,
+                          wl.phi, inp["omega"], wl.qk_scale)
+    _, kap = oracle.causal(one["q"], one["k"], one["v"], lam[:1], wl.eps, wl.phi, inp["omega"], wl.qk_scale,
+                           want_kappa=True)
+    got = {n: t[:, h:h + 1].float().cpu().numpy() for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    check_rf(wl, got, ref, kap, names=("dq", "dk", "dv"))
 
 
 def test_rf_backward_unsupported_shape_is_refused():
