@@ -17,7 +17,7 @@ namespace la {
 
 // Threads per workgroup of the scan, and segments whose loads are in flight
 // together (one memory round trip per batch, not one per segment).
-constexpr int kScanThreads = 128;
+constexpr int kScanThreads = 64;
 constexpr int kScanBatch = 16;
 
 __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
