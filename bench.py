@@ -754,8 +754,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path "
-            "(each GPU would run its own heads; see the sharding notes in DESIGN.md).")
+        log("bench.py measures one GPU: the library has no multi-GPU path "
+            "(the heads are independent, so each GPU would run its own share).")
         sys.exit(2)
 
     ctx = Ctx(args.steps, args.warmup)

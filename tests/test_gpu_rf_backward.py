@@ -113,6 +113,10 @@ CASES = [
     ({"m": 32, "phi": "trig_rf_plain"}, 1, 2, 200, [0.9, 1.0], None, True, False),
     ({"m": 32, "phi": "trig_rf_softmax"}, 1, 2, 200, [1.0, 0.95], "random", True, False),
     ({"m": 64, "dk": 128}, 1, 2, 333, [0.97, 1.0], None, True, False),
+    # d_k = 128 with the largest and the smallest m (omega's fragments of the
+    # chain-rule kernel fill 128 KB of LDS at m = 128)
+    ({"m": 128, "dk": 128}, 1, 2, 400, [0.97, 1.0], None, True, False),
+    ({"m": 32, "dk": 128}, 1, 2, 150, [1.0, 0.95], "random", True, False),
     ({"m": 32, "omega": "gaussian"}, 2, 1, 96, [0.8], None, True, False),
     # from a zero state: the first tokens' denominators sum few terms
     ({}, 1, 2, 300, [0.95, 1.0], None, False, False),
