@@ -113,9 +113,7 @@ CASES = [
     ({"m": 32, "phi": "trig_rf_plain"}, 1, 2, 200, [0.9, 1.0], None, True, False),
     ({"m": 32, "phi": "trig_rf_softmax"}, 1, 2, 200, [1.0, 0.95], "random", True, False),
     ({"m": 64, "dk": 128}, 1, 2, 333, [0.97, 1.0], None, True, False),
-    # d_k = 128 with the largest and the smallest m (omega's fragments of the
-    # chain-rule kernel fill 128 KB of LDS at m = 128)
-    ({"m": 128, "dk": 128}, 1, 2, 400, [0.97, 1.0], None, True, False),
+    # d_k = 128 with the smallest m (d_k * m <= 8192 for random features)
     ({"m": 32, "dk": 128}, 1, 2, 150, [1.0, 0.95], "random", True, False),
     ({"m": 32, "omega": "gaussian"}, 2, 1, 96, [0.8], None, True, False),
     # from a zero state: the first tokens' denominators sum few terms
@@ -165,11 +163,13 @@ def test_rf_backward_full_size_sampled_head():
     check_rf(wl, got, ref, kap, names=("dq", "dk", "dv"))
 
 
-def test_rf_backward_unsupported_shape_is_refused():
-    # fp32 inputs with m = 128 (F = 256): the identity sweeps do not fit
-    wl = si.workload(5).with_(dtype="f32", scale=1.0)
+@pytest.mark.parametrize("over", [{"dtype": "f32", "scale": 1.0}, {"dk": 128}])
+def test_rf_backward_unsupported_shape_is_refused(over):
+    # fp32 inputs with m = 128 (F = 256): the identity sweeps do not fit;
+    # d_k = 128 with m = 128: d_k * m above 8192, refused by the forward too
+    wl = si.workload(5).with_(**over)
     inp = si.make_inputs(wl, B=1, H=1, N=64)
-    q = to_dev(inp, "q", "f32")
+    q = to_dev(inp, "q", wl.dtype)
     phi = phi_for(wl, inp["omega"])
     with pytest.raises(la.LaError):
         la.la_backward_causal(q, q, q, q, q, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), phi=phi)

@@ -464,8 +464,13 @@ hipError_t rf_mf_dispatch(const RfGradArgs& a, bool vjp, hipStream_t stream)
 {
     auto go = [&](auto mc) {
         constexpr int M = decltype(mc)::value;
-        return vjp ? rf_mf_launch(la_rf_vjp_mfma_kernel<DK, M>, a, stream)
-                   : rf_mf_launch(la_rf_features_mfma_kernel<DK, M>, a, stream);
+        // random features need d_k * m <= 8192 (the forward's bound)
+        if constexpr (DK * M > 8192) {
+            return hipErrorInvalidValue;
+        } else {
+            return vjp ? rf_mf_launch(la_rf_vjp_mfma_kernel<DK, M>, a, stream)
+                       : rf_mf_launch(la_rf_features_mfma_kernel<DK, M>, a, stream);
+        }
     };
     switch (a.m) {
     case 32: return go(std::integral_constant<int, 32>());
