@@ -126,3 +126,37 @@ def test_decode_step_multi_token(phi, m, dk, k_tok):
     else:
         assert err < TOL["bf16"], err
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+
+
+@pytest.mark.parametrize("lam", [[0.3, 0.5, 0.97, 1.0], [0.0, 1e-4, 0.3, 1.0]])
+def test_decode_step_multi_token_decay_range(lam):
+    # 12 tokens per call over the whole decay range: small lambda (the state
+    # forgets within a few tokens), lambda = 0 (0^0 = 1: the state is the last
+    # key's term alone) and lambda = 1
+    wl = si.workload(4).with_(N=96)
+    B, H, calls, k_tok = 2, 4, 3, 12
+    pre = si.make_decode_prefix(wl, B=B, H=H)
+    S = torch.empty(B, H, wl.F, wl.dv, device=DEV)
+    z = torch.empty(B, H, wl.F, device=DEV)
+    q, k, v = (to_dev(pre, n, wl.dtype) for n in ("q", "k", "v"))
+    yp = torch.empty(B, H, wl.N, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_causal(q, k, v, yp, lambda_h=lam, eps=wl.eps, S_out=S, z_out=z)
+    rng = np.random.default_rng(77)
+    chunks, ys = [], []
+    for c in range(calls):
+        blk = {}
+        for n, d in (("q", wl.dk), ("k", wl.dk), ("v", wl.dv)):
+            bits, vals = si.round_to_bf16((rng.standard_normal((B, H, k_tok, d)) * wl.scale).astype(np.float32))
+            blk[n], blk[n + "_bits"] = vals, bits
+        chunks.append(blk)
+        qs, ks, vs = (to_dev(blk, n, wl.dtype) for n in ("q", "k", "v"))
+        y = torch.empty(B, H, k_tok, wl.dv, dtype=tdtype(wl.dtype), device=DEV)
+        la.la_decode_step(qs, ks, vs, y, S, z, lambda_h=lam, eps=wl.eps)
+        ys.append(y)
+    torch.cuda.synchronize()
+    cat = {n: np.concatenate([pre[n]] + [c[n] for c in chunks], axis=2) for n in ("q", "k", "v")}
+    ref, Sr, zr = oracle.causal(cat["q"], cat["k"], cat["v"], np.array(lam), wl.eps, want_state=True)
+    err = oracle.rowwise_rel_err(torch.cat(ys, dim=2).float().cpu().numpy(), ref[:, :, wl.N:])
+    assert err < TOL["bf16"], err
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=2e-2, atol=1e-6)
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
