@@ -38,7 +38,7 @@ namespace la {
 template <int DV>
 constexpr int decode_split() { return 1; }
 
-template <class T, int PHI, int DK, int F, int DV>
+template <class T, int PHI, int DK, int F, int DV, bool SCALED>
 __global__ void __launch_bounds__(256)
 la_decode_kernel(const DecArgs a)
 {
@@ -71,6 +71,18 @@ la_decode_kernel(const DecArgs a)
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = *(const f32x4*)(Sb + (rg + RG * i) * DV + 4 * cq);
     float zf = (tid < F) ? zb[tid] : 0.f;
+
+    // SCALED (several tokens per call, every lambda >= 2^-12): within blocks
+    // of at most kDecBlock tokens the registers hold s' = lambda^-e S (e
+    // tokens into the block), so that a token costs one fused multiply-add
+    // per state element for the update (s' += lambda^-e phi(k) v^T) and one
+    // for the query (phi(q)^T S = lambda^e phi(q)^T s'); s' returns to S at
+    // the block's end.  lambda^-e stays below 2^96.  Otherwise the plain
+    // update S <- lambda S + phi(k) v^T.
+    constexpr int kDecBlock = 8;
+    const float ilam = SCALED ? 1.0f / lam : 1.f;
+    float g = 1.f, pe = 1.f;  // lambda^-e and lambda^e of the current token
+    int e_blk = 0;
 
     for (int t = 0; t < a.ntok; ++t) {
         const int64_t row = (int64_t)bh * a.ntok + t;
@@ -117,17 +129,34 @@ la_decode_kernel(const DecArgs a)
         // S <- lambda S + phi(k) v^T ; partial phi(q)^T S
         const f32x4 v4 = {sV[4 * cq], sV[4 * cq + 1], sV[4 * cq + 2], sV[4 * cq + 3]};
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int f = rg + RG * i;
-            s[i] = lam * s[i] + sPk[f] * v4;
-            acc += sPq[f] * s[i];
-        }
-        // z <- lambda z + phi(k) ; partial phi(q)^T z
         float dz = 0.f;
-        if (tid < F) {
-            zf = lam * zf + sPk[tid];
-            dz = sPq[tid] * zf;
+        if constexpr (SCALED) {
+            ++e_blk;
+            g *= ilam;
+            pe *= lam;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int f = rg + RG * i;
+                s[i] += (g * sPk[f]) * v4;
+                acc += sPq[f] * s[i];
+            }
+            // z the same way ; partial phi(q)^T z
+            if (tid < F) {
+                zf += g * sPk[tid];
+                dz = sPq[tid] * zf;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int f = rg + RG * i;
+                s[i] = lam * s[i] + sPk[f] * v4;
+                acc += sPq[f] * s[i];
+            }
+            // z <- lambda z + phi(k) ; partial phi(q)^T z
+            if (tid < F) {
+                zf = lam * zf + sPk[tid];
+                dz = sPq[tid] * zf;
+            }
         }
         // reduce over row groups: lanes of one wave first, then waves
 #pragma unroll
@@ -147,6 +176,8 @@ la_decode_kernel(const DecArgs a)
                 num += sRed[w][tid];
                 den += sDen[w];
             }
+            num *= pe;  // 1 unless SCALED
+            den *= pe;
             const float inv = 1.0f / (den + a.eps);
             const int64_t yo = row * DV + d0 + 4 * tid;
             if (a.out_f32) {
@@ -155,6 +186,14 @@ la_decode_kernel(const DecArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ((T*)a.y)[yo + e] = from_f32<T>(num[e] * inv);
             }
+        }
+        // end of a scaled block: s' back to S
+        if (SCALED && (e_blk == kDecBlock || t == a.ntok - 1)) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) s[i] *= pe;
+            zf *= pe;
+            e_blk = 0;
+            g = pe = 1.f;
         }
     }
 
@@ -168,7 +207,10 @@ template <class T, int PHI, int DK, int F, int DV>
 hipError_t dec_launch(const DecArgs& a, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)a.BH * (unsigned)decode_split<DV>();
-    return launch_kernel(la_decode_kernel<T, PHI, DK, F, DV>, dim3(blocks), dim3(256), stream, a);
+    bool scaled = a.ntok > 1;
+    for (int h = 0; h < a.H && scaled; ++h) scaled = a.lam.lam[h] >= 0x1p-12f;
+    if (scaled) return launch_kernel(la_decode_kernel<T, PHI, DK, F, DV, true>, dim3(blocks), dim3(256), stream, a);
+    return launch_kernel(la_decode_kernel<T, PHI, DK, F, DV, false>, dim3(blocks), dim3(256), stream, a);
 }
 
 }  // namespace la
