@@ -193,7 +193,7 @@ constexpr int kMfWaves = 8;  // waves per workgroup; each wave takes 16-row tile
 template <int DK, int M> struct RfMf {
     static constexpr int KX = DK / 32;  // k blocks of the first product (over d)
     static constexpr int RB = M / 16;   // 16-feature row blocks of U^T
-    static constexpr int DB = DK / 16;  // 16-column row blocks of dX^T
+    static constexpr int DB = DK / 16;  // 16-row blocks of dX^T (input columns)
     static constexpr int KF = M / 32;   // k blocks of the second product (over r)
     // omega' fragments of U^T = omega' X^T: (rb, kb, part)
     static constexpr int NA = RB * KX * 2;
@@ -259,9 +259,8 @@ __device__ __forceinline__ void rf_build_frags(const RfGradArgs& a, Frag<bf16>* 
     __syncthreads();
 }
 
-// Per-tile front end shared by both kernels: this lane's token row (clamped
-// into range for the loads), its x fragments, the prefactor c and the
-// accumulator tiles of U^T (angles in revolutions).
+// Per-tile values shared by both kernels: this lane's x fragments (its token
+// row, clamped into range for the loads) and the row's prefactor c.
 template <int DK, int M>
 struct RfTile {
     Frag<bf16> xf[DK / 32];
