@@ -116,6 +116,10 @@ CASES = [
     # d_k = 128 with the smallest m (d_k * m <= 8192 for random features)
     ({"m": 32, "dk": 128}, 1, 2, 150, [1.0, 0.95], "random", True, False),
     ({"m": 32, "omega": "gaussian"}, 2, 1, 96, [0.8], None, True, False),
+    # fewer rows than one 16-row tile of the feature-map kernels, and one
+    # full tile plus one row
+    ({"m": 64}, 1, 1, 5, [0.9], None, True, False),
+    ({}, 1, 1, 17, [1.0], "random", True, True),
     # from a zero state: the first tokens' denominators sum few terms
     ({}, 1, 2, 300, [0.95, 1.0], None, False, False),
     ({"m": 32, "dtype": "f32", "scale": 1.0}, 1, 2, 150, [1.0, 0.9], "random", False, True),
@@ -218,6 +222,7 @@ CROSS_CASES = [
     ({"m": 32, "dtype": "f32", "scale": 1.0}, 2, 1, 257, 100, "random"),
     ({"m": 64, "dk": 128, "dv": 128}, 1, 2, 64, 3000, None),          # many key segments
     ({"m": 128, "phi": "trig_rf_softmax"}, 1, 2, 5000, 200, "random"),  # many query segments
+    ({"m": 32}, 1, 1, 3, 9, None),                                        # partial tiles on both sides
 ]
 
 
