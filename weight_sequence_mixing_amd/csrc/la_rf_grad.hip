@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(kRfThreads) la_rf_vjp_kernel(const RfGradArgs 
 
 // ---- bf16 inputs: matrix-core kernels -----------------------------------
 
-constexpr int kMfWaves = 8;  // waves per workgroup; each wave takes 16-row tiles
+constexpr int kMfWaves = 4;  // waves per workgroup; each wave takes 16-row tiles
 
 template <int DK, int M> struct RfMf {
     static constexpr int KX = DK / 32;  // k blocks of the first product (over d)
