@@ -100,11 +100,16 @@ def _uptr(a, offset=0):
 
 
 def default_threads() -> int:
+    """Host cores this process may use: its affinity set, capped by the CPU
+    share the environment grants through OMP_NUM_THREADS when that is set."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
 
 
 def feature_dim(phi: str, dk: int, omega) -> int:

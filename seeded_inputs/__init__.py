@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "bf16_bits_rne", "bf16_bits_to_f32",
     "round_to_bf16", "make_qkv", "make_lambda", "make_omega", "make_inputs",
-    "make_decode_step", "make_decode_prefix", "make_kv", "make_key_padding_mask",
+    "make_decode_step", "make_decode_steps", "make_decode_prefix", "make_kv", "make_key_padding_mask",
     "make_varlen_lengths", "cu_seqlens", "pack_heads",
 ]
 
@@ -45,15 +45,21 @@ def bf16_bits_rne(x) -> np.ndarray:
 
     NaN inputs map to a quiet NaN; infinities are preserved; values that
     round past the largest finite bf16 become infinity (IEEE behaviour).
+    The sum u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern u,
+    so the arithmetic runs in place on 32-bit words.
     """
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    u = a.view(np.uint32)
+    r = np.right_shift(u, np.uint32(16))
+    np.bitwise_and(r, np.uint32(1), out=r)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
-        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), r)
-    return r.astype(np.uint16)
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return out
 
 
 def bf16_bits_to_f32(bits) -> np.ndarray:
@@ -219,18 +225,38 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None
     return d
 
 
-def make_decode_prefix(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None):
-    """The prefix tokens that initialise the decode state: [B,H,N,d]."""
+def _pool_map(fn, items, threads):
+    """Map fn over items on `threads` threads (numpy's generators release the
+    GIL while they fill arrays, so independent streams draw in parallel)."""
+    items = list(items)
+    if threads <= 1 or len(items) <= 1:
+        return [fn(i) for i in items]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(threads, len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
+def make_decode_prefix(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None,
+                       threads: int = 1, values: bool = True):
+    """The prefix tokens that initialise the decode state: [B,H,N,d].
+
+    Each (tensor, batch row) pair draws from a sub-stream of its own, so a
+    smaller B keeps the first rows' values and rows can be drawn on several
+    threads.  values=False returns only the bf16 bit patterns."""
     seed = wl.index if seed is None else seed
     B = wl.B if B is None else B
     H = wl.H if H is None else H
     N = wl.N if N is None else N
     out = {}
     for j, (name, d) in enumerate((("q", wl.dk), ("k", wl.dk), ("v", wl.dv))):
-        bits, vals = _normal(_rng(seed, "prefix", j), (B, H, N, d), wl.scale, wl.dtype)
-        out[name] = vals
-        if bits is not None:
-            out[name + "_bits"] = bits
+        rows = _pool_map(lambda b: _normal(_rng(seed, "prefix", j, b), (1, H, N, d), wl.scale, wl.dtype),
+                         range(B), threads)
+        if wl.dtype == "bf16":
+            out[name + "_bits"] = np.concatenate([r[0] for r in rows], axis=0)
+            if values:
+                out[name] = bf16_bits_to_f32(out[name + "_bits"])
+        else:
+            out[name] = np.concatenate([r[1] for r in rows], axis=0)
     return out
 
 
@@ -247,6 +273,17 @@ def make_decode_step(wl: Workload, step: int, seed: Optional[int] = None, B=None
         if bits is not None:
             out[name + "_bits"] = bits
     return out
+
+
+def make_decode_steps(wl: Workload, t0: int, t1: int, seed: Optional[int] = None, B=None, H=None,
+                      threads: int = 1):
+    """Steps t0..t1-1 of make_decode_step stacked on a leading axis:
+    [t1-t0, B, H, 1, d] per tensor, bf16 bit patterns ('q_bits', ...) for
+    bf16 workloads, float32 values ('q', ...) otherwise.  The same values as
+    make_decode_step, drawn on `threads` threads."""
+    steps = _pool_map(lambda t: make_decode_step(wl, t, seed, B, H), range(t0, t1), threads)
+    key = "_bits" if wl.dtype == "bf16" else ""
+    return {n + key: np.stack([s[n + key] for s in steps]) for n in ("q", "k", "v")}
 
 
 # --------------------------------------------------------------------------

@@ -177,9 +177,87 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+# ---- argument checks: shapes, dtypes and devices of every tensor argument
+# (the library sees raw pointers and trusts the sizes it is given)
+def _one_device(*ts) -> torch.device:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on one device (got %s)" % sorted(map(str, devs)))
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device (got %s)" % dev)
+    return dev
+
+
+def _expect(t, name, shape, dtypes):
+    """t must have exactly `shape` and one of `dtypes` (None: not given)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype not in dtypes:
+        raise ValueError("%s must be %s (got %s)" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+_IO = (torch.bfloat16, torch.float32)
+_F32 = (torch.float32,)
+
+
+def _qkvy(q, k, v, y, n_kv=None):
+    """q [B,H,N,d_k], k [B,H,M,d_k], v [B,H,M,d_v], y [B,H,N,d_v] (M = N
+    unless n_kv is given); returns (B, H, N, d_k, d_v)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d_k] (got %s)" % (tuple(q.shape),))
+    B, H, N, dk = q.shape
+    M = N if n_kv is None else n_kv
+    if v.dim() != 4:
+        raise ValueError("v must be [B,H,N,d_v] (got %s)" % (tuple(v.shape),))
+    dv = v.shape[-1]
+    _expect(q, "q", (B, H, N, dk), _IO)
+    _expect(k, "k", (B, H, M, dk), (q.dtype,))
+    _expect(v, "v", (B, H, M, dv), (q.dtype,))
+    _expect(y, "y", (B, H, N, dv), (q.dtype, torch.float32))
+    return B, H, N, dk, dv
+
+
+def _state(S, z, B, H, F, dv, sname="S", zname="z"):
+    if (S is None) != (z is None):
+        raise ValueError("%s and %s must be given together" % (sname, zname))
+    _expect(S, sname, (B, H, F, dv), _F32)
+    _expect(z, zname, (B, H, F), _F32)
+
+
 def _shape(q: torch.Tensor, v: torch.Tensor, y: torch.Tensor) -> LaShapeC:
     B, H, N, dk = q.shape
     return LaShapeC(B, H, N, dk, v.shape[-1], _dt(q), _dt(y))
+
+
+def _phi_checked(phi: Optional["Phi"], d_k: int) -> "Phi":
+    phi = phi or Phi()
+    if phi.kind not in PHI_KINDS:
+        raise ValueError("unknown feature map %r" % (phi.kind,))
+    if phi.kind not in ELEMENTWISE:
+        om = phi.omega
+        if om is None:
+            raise ValueError("random features need omega [m, d_k]")
+        if om.dim() != 2 or om.shape[1] != d_k:
+            raise ValueError("omega must be [m, d_k=%d] (got %s)" % (d_k, tuple(om.shape)))
+    return phi
+
+
+def _omega(phi: "Phi"):
+    return None if phi.kind in ELEMENTWISE else phi.omega
+
+
+def _mask(mask, B, M):
+    if mask is None:
+        return
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("key_padding_mask must be bool or uint8")
+    if tuple(mask.shape) != (B, M):
+        raise ValueError("key_padding_mask must be [B, N_keys] = %s (got %s)" % ((B, M), tuple(mask.shape)))
 
 
 def _lam(lambda_h, H):
@@ -187,7 +265,10 @@ def _lam(lambda_h, H):
         return None, None
     if isinstance(lambda_h, torch.Tensor):
         lambda_h = lambda_h.detach().to("cpu", torch.float32).reshape(-1).tolist()
-    arr = (ctypes.c_float * H)(*[float(x) for x in lambda_h])
+    vals = [float(x) for x in lambda_h]
+    if len(vals) != H:
+        raise ValueError("lambda_h needs one value per head: %d given for H=%d" % (len(vals), H))
+    arr = (ctypes.c_float * H)(*vals)
     return arr, ctypes.cast(arr, ctypes.c_void_p)
 
 
@@ -220,10 +301,19 @@ def la_kernel_name(kernel_id: int) -> str:
     return load_library().la_kernel_name(int(kernel_id)).decode()
 
 
+def _state_shape(S, z):
+    if S.dim() != 4:
+        raise ValueError("S must be [B,H,F,d_v] (got %s)" % (tuple(S.shape),))
+    B, H, F, dv = S.shape
+    _state(S, z, B, H, F, dv)
+    _one_device(S, z)
+    return B, H, F, dv
+
+
 def la_init_state(S: torch.Tensor, z: torch.Tensor, stream=None) -> None:
     """S [B,H,F,d_v] = 0, z [B,H,F] = 0 (fp32 device tensors)."""
     load_library()
-    B, H, F, dv = S.shape
+    B, H, F, dv = _state_shape(S, z)
     _check(_lib.la_init_state(_ptr(S), _ptr(z), B, H, F, dv, _stream(stream)))
 
 
@@ -231,7 +321,7 @@ def la_init_state_identity(S: torch.Tensor, z: torch.Tensor, alpha: float = 1.0,
     """S [B,H,F,d_v] = alpha * I (rectangular), z [B,H,F] = alpha on the first
     min(F, d_v) features, 0 elsewhere (fp32 device tensors)."""
     load_library()
-    B, H, F, dv = S.shape
+    B, H, F, dv = _state_shape(S, z)
     _check(_lib.la_init_state_identity(_ptr(S), _ptr(z), B, H, F, dv, float(alpha), _stream(stream)))
 
 
@@ -244,24 +334,25 @@ def la_workspace_size(B, H, N, d_k, d_v, in_dtype=LA_BF16, out_dtype=None, phi: 
     return int(_lib.la_workspace_size(ctypes.byref(shape), ctypes.byref(pc), 1 if causal else 0))
 
 
-def _workspace(shape: LaShapeC, pc: LaPhiC, causal: bool, workspace, device):
-    need = int(_lib.la_workspace_size(ctypes.byref(shape), ctypes.byref(pc), 1 if causal else 0))
-    if workspace is None:
-        if need == 0:
-            return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+def _causal_args(q, k, v, y, phi, S_in, z_in, S_out, z_out, mask=None):
+    """Checks of the causal forwards' tensors; returns (device, phi, shape, LaPhiC)."""
+    B, H, N, dk, dv = _qkvy(q, k, v, y)
+    phi = _phi_checked(phi, dk)
+    F = phi.F(dk)
+    _state(S_in, z_in, B, H, F, dv, "S_in", "z_in")
+    _state(S_out, z_out, B, H, F, dv, "S_out", "z_out")
+    _mask(mask, B, N)
+    dev = _one_device(q, k, v, y, S_in, z_in, S_out, z_out, mask, _omega(phi))
+    return dev, phi, _shape(q, v, y), phi.c()
 
 
 def la_forward_causal(q, k, v, y, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6,
                       S_in=None, z_in=None, S_out=None, z_out=None, workspace=None, stream=None):
     """Causal forward; writes y [B,H,N,d_v] (and S_out, z_out when given)."""
     load_library()
-    phi = phi or Phi()
-    shape = _shape(q, v, y)
-    pc = phi.c()
-    ws, ws_bytes = _workspace(shape, pc, True, workspace, q.device)
     lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    dev, phi, shape, pc = _causal_args(q, k, v, y, phi, S_in, z_in, S_out, z_out)
+    ws, ws_bytes = _workspace(shape, pc, True, workspace, dev, stream)
     _check(_lib.la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
                                   lam_ptr, float(eps), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
                                   _ptr(ws), ws_bytes, _stream(stream)))
@@ -272,10 +363,8 @@ def la_forward_causal(q, k, v, y, phi: Optional[Phi] = None, lambda_h=None, eps:
 def la_forward_noncausal(q, k, v, y, phi: Optional[Phi] = None, eps: float = 1e-6, workspace=None, stream=None):
     """Non-causal forward; writes y [B,H,N,d_v]."""
     load_library()
-    phi = phi or Phi()
-    shape = _shape(q, v, y)
-    pc = phi.c()
-    ws, ws_bytes = _workspace(shape, pc, False, workspace, q.device)
+    dev, phi, shape, pc = _causal_args(q, k, v, y, phi, None, None, None, None)
+    ws, ws_bytes = _workspace(shape, pc, False, workspace, dev, stream)
     _check(_lib.la_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
                                      float(eps), _ptr(ws), ws_bytes, _stream(stream)))
     return y
@@ -289,25 +378,17 @@ def _mask_ptr(mask: Optional[torch.Tensor]):
     return _ptr(mask)  # bool is stored as one byte per element, 0 or 1
 
 
-def _alloc_ws(need: int, workspace, device):
-    if workspace is None:
-        if need == 0:
-            return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
-
-
 def la_forward_causal_masked(q, k, v, y, key_padding_mask, phi: Optional[Phi] = None, lambda_h=None,
                              eps: float = 1e-6, S_in=None, z_in=None, S_out=None, z_out=None, workspace=None,
                              stream=None):
     """Causal forward with a key padding mask [B,N] (bool / uint8 on the device,
     True = the key adds nothing)."""
     load_library()
-    phi = phi or Phi()
-    shape = _shape(q, v, y)
-    pc = phi.c()
-    ws, ws_bytes = _workspace(shape, pc, True, workspace, q.device)
+    if key_padding_mask is None:
+        raise ValueError("key_padding_mask is required")
     lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    dev, phi, shape, pc = _causal_args(q, k, v, y, phi, S_in, z_in, S_out, z_out, key_padding_mask)
+    ws, ws_bytes = _workspace(shape, pc, True, workspace, dev, stream)
     _check(_lib.la_forward_causal_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape),
                                          ctypes.byref(pc), lam_ptr, float(eps), _mask_ptr(key_padding_mask),
                                          _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out), _ptr(ws), ws_bytes,
@@ -331,16 +412,27 @@ def la_forward_causal_varlen(q, k, v, y, cu_seqlens, max_seqlen: int, phi: Optio
     """Causal forward over packed sequences: q, k [H,T,d_k], v, y [H,T,d_v];
     cu_seqlens: int32 device tensor [B+1]; states [B,H,F,d_v] / [B,H,F]."""
     load_library()
-    phi = phi or Phi()
-    if cu_seqlens.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be an int32 tensor [B+1] with B >= 1")
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed q, k, v, y must be [H,T,d]")
     H, T, dk = q.shape
+    dv = v.shape[-1]
     B = cu_seqlens.numel() - 1
-    shape = LaShapeC(B, H, T, dk, v.shape[-1], _dt(q), _dt(y))
+    _expect(q, "q", (H, T, dk), _IO)
+    _expect(k, "k", (H, T, dk), (q.dtype,))
+    _expect(v, "v", (H, T, dv), (q.dtype,))
+    _expect(y, "y", (H, T, dv), (q.dtype, torch.float32))
+    phi = _phi_checked(phi, dk)
+    F = phi.F(dk)
+    _state(S_in, z_in, B, H, F, dv, "S_in", "z_in")
+    _state(S_out, z_out, B, H, F, dv, "S_out", "z_out")
+    lam_keep, lam_ptr = _lam(lambda_h, H)
+    dev = _one_device(q, k, v, y, cu_seqlens, S_in, z_in, S_out, z_out, _omega(phi))
+    shape = LaShapeC(B, H, T, dk, dv, _dt(q), _dt(y))
     pc = phi.c()
     need = int(_lib.la_workspace_size_varlen(ctypes.byref(shape), int(max_seqlen), ctypes.byref(pc)))
-    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
-    lam_keep, lam_ptr = _lam(lambda_h, H)
+    ws, ws_bytes = _alloc_ws(need, workspace, dev, stream)
     _check(_lib.la_forward_causal_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(cu_seqlens), int(max_seqlen),
                                          ctypes.byref(shape), ctypes.byref(pc), lam_ptr, float(eps), _ptr(S_in),
                                          _ptr(z_in), _ptr(S_out), _ptr(z_out), _ptr(ws), ws_bytes,
@@ -358,17 +450,27 @@ def la_workspace_size_cross(B, H, N, n_kv, d_k, d_v, in_dtype=LA_BF16, out_dtype
     return int(_lib.la_workspace_size_cross(ctypes.byref(shape), int(n_kv), ctypes.byref(pc)))
 
 
+def _cross_args(q, k, v, y, phi, mask):
+    if k.dim() != 4:
+        raise ValueError("k must be [B,H,M,d_k] (got %s)" % (tuple(k.shape),))
+    n_kv = int(k.shape[2])
+    B, H, N, dk, dv = _qkvy(q, k, v, y, n_kv)
+    phi = _phi_checked(phi, dk)
+    _mask(mask, B, n_kv)
+    return phi, n_kv
+
+
 def la_forward_cross(q, k, v, y, key_padding_mask=None, phi: Optional[Phi] = None, eps: float = 1e-6,
                      workspace=None, stream=None):
     """Non-causal cross attention: q [B,H,N,d_k] against k [B,H,M,d_k] and
     v [B,H,M,d_v]; optional key_padding_mask [B,M]; writes y [B,H,N,d_v]."""
     load_library()
-    phi = phi or Phi()
+    phi, n_kv = _cross_args(q, k, v, y, phi, key_padding_mask)
+    dev = _one_device(q, k, v, y, key_padding_mask, _omega(phi))
     shape = _shape(q, v, y)
-    n_kv = int(k.shape[2])
     pc = phi.c()
     need = int(_lib.la_workspace_size_cross(ctypes.byref(shape), n_kv, ctypes.byref(pc)))
-    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
+    ws, ws_bytes = _alloc_ws(need, workspace, dev, stream)
     _check(_lib.la_forward_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), n_kv,
                                  _mask_ptr(key_padding_mask), ctypes.byref(pc), float(eps), _ptr(ws), ws_bytes,
                                  _stream(stream)))
@@ -383,18 +485,36 @@ def la_workspace_size_backward(B, H, N, d_k, d_v, in_dtype=LA_BF16, phi: Optiona
     return int(_lib.la_workspace_size_backward(ctypes.byref(shape), ctypes.byref(pc)))
 
 
+def _grads(q, k, v, y, dy, dq, dk, dv):
+    """dy like y (input type); dq, dk, dv like q, k, v."""
+    if y.dtype != q.dtype:
+        raise ValueError("the backward takes y in the input type (got %s for %s inputs)" % (y.dtype, q.dtype))
+    _expect(dy, "dy", tuple(y.shape), (q.dtype,))
+    _expect(dq, "dq", tuple(q.shape), (q.dtype,))
+    _expect(dk, "dk", tuple(k.shape), (q.dtype,))
+    _expect(dv, "dv", tuple(v.shape), (q.dtype,))
+
+
 def la_backward_causal(q, k, v, y, dy, dq, dk, dv, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6,
                        key_padding_mask=None, S_in=None, z_in=None, dS_out=None, dz_out=None, dS_in=None,
                        dz_in=None, dlambda=None, workspace=None, stream=None):
     """Gradients of la_forward_causal: writes dq, dk, dv (and dS_in, dz_in,
     dlambda [H] fp32 when given)."""
     load_library()
-    phi = phi or Phi()
-    shape = _shape(q, v, y)
-    pc = phi.c()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d_k] (got %s)" % (tuple(q.shape),))
+    B, H, N, dk_ = q.shape
+    _grads(q, k, v, y, dy, dq, dk, dv)
+    phi_c = _phi_checked(phi, dk_)
+    F, dv_ = phi_c.F(dk_), v.shape[-1]
+    _state(dS_out, dz_out, B, H, F, dv_, "dS_out", "dz_out")
+    _state(dS_in, dz_in, B, H, F, dv_, "dS_in", "dz_in")
+    _expect(dlambda, "dlambda", (H,), _F32)
+    lam_keep, lam_ptr = _lam(lambda_h, H)
+    dev, phi, shape, pc = _causal_args(q, k, v, y, phi, S_in, z_in, None, None, key_padding_mask)
+    _one_device(q, dy, dq, dk, dv, dS_out, dz_out, dS_in, dz_in, dlambda)
     need = int(_lib.la_workspace_size_backward(ctypes.byref(shape), ctypes.byref(pc)))
-    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
-    lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    ws, ws_bytes = _alloc_ws(need, workspace, dev, stream)
     _check(_lib.la_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
                                    ctypes.byref(shape), ctypes.byref(pc), lam_ptr, float(eps),
                                    _mask_ptr(key_padding_mask), _ptr(S_in), _ptr(z_in), _ptr(dS_out),
@@ -417,12 +537,13 @@ def la_backward_cross(q, k, v, y, dy, dq, dk, dv, key_padding_mask=None, phi: Op
     """Gradients of la_forward_cross (q, y, dy, dq: [B,H,N,*]; k, v, dk, dv:
     [B,H,M,*]): writes dq, dk, dv."""
     load_library()
-    phi = phi or Phi()
+    phi, n_kv = _cross_args(q, k, v, y, phi, key_padding_mask)
+    _grads(q, k, v, y, dy, dq, dk, dv)
+    dev = _one_device(q, k, v, y, dy, dq, dk, dv, key_padding_mask, _omega(phi))
     shape = _shape(q, v, y)
-    n_kv = int(k.shape[2])
     pc = phi.c()
     need = int(_lib.la_workspace_size_backward_cross(ctypes.byref(shape), n_kv, ctypes.byref(pc)))
-    ws, ws_bytes = _alloc_ws(need, workspace, q.device)
+    ws, ws_bytes = _alloc_ws(need, workspace, dev, stream)
     _check(_lib.la_backward_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv),
                                   ctypes.byref(shape), n_kv, _mask_ptr(key_padding_mask), ctypes.byref(pc),
                                   float(eps), _ptr(ws), ws_bytes, _stream(stream)))
@@ -433,10 +554,13 @@ def la_decode_step(q, k, v, y, S, z, phi: Optional[Phi] = None, lambda_h=None, e
     """Decode steps on [B,H,N,d] inputs (N tokens per head-state, in order, N <= 64);
     updates S [B,H,F,d_v] and z [B,H,F] in place."""
     load_library()
-    phi = phi or Phi()
-    shape = _shape(q, v, y)
-    pc = phi.c()
+    if S is None or z is None:
+        raise ValueError("S and z are required")
+    if q.dim() == 4 and v.dim() == 4:
+        B, H, _, dk_ = q.shape
+        _state(S, z, B, H, _phi_checked(phi, dk_).F(dk_), v.shape[-1])
     lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    dev, phi, shape, pc = _causal_args(q, k, v, y, phi, S, z, None, None)
     _check(_lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S), _ptr(z), ctypes.byref(shape),
                                ctypes.byref(pc), lam_ptr, float(eps), _stream(stream)))
     del lam_keep

@@ -5,7 +5,6 @@
 // allocates, frees or synchronises.  See include/la.h for the contract.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -1451,14 +1450,6 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
     a.rf_sign = rf_sign(phi->kind);
     a.omega = phi->omega;
-    // alternate the visiting order between calls (no effect on results; see
-    // la_decode.h); LA_DECODE_ORDER=plain keeps it ascending for measurements
-    static std::atomic<uint64_t> calls{0};
-    static const bool plain = [] {
-        const char* o = std::getenv("LA_DECODE_ORDER");
-        return o && std::strcmp(o, "plain") == 0;
-    }();
-    a.reverse = plain ? 0 : (int)(calls.fetch_add(1, std::memory_order_relaxed) & 1);
     hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = launch(LA_KERNEL_DECODE, [&] { return ent->dec(a, strm); });
     if (e != hipSuccess) return hip_fail(e, "decode launch");

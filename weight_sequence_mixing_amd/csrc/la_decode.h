@@ -19,12 +19,7 @@
 // reduced across lanes and then across waves through LDS.  Every workgroup
 // recomputes the new z for its denominator; the first column slice writes it
 // back.
-//
-// Head-states are visited in ascending order on even calls and descending
-// order on odd ones (DecArgs::reverse): when back-to-back steps run over a
-// state larger than the last-level cache, the part written last by one step
-// is read first by the next, while it may still be cached.  The order does
-// not change any result.
+
 #pragma once
 
 #include "la_device.h"
@@ -58,7 +53,7 @@ la_decode_kernel(const DecArgs a)
     __shared__ float sDen[NT / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int blk = a.reverse ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int blk = (int)blockIdx.x;
     const int bh = blk / DS, part = blk % DS, h = bh % a.H;
     const int d0 = part * DW;
     const float lam = a.lam.lam[h];

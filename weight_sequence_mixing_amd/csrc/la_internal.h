@@ -181,7 +181,6 @@ struct DecArgs {
     float qk_scale;
     float rf_sign;  // random features: sign of the prefactor's exponent
     const float* omega;
-    int32_t reverse;   // 1: visit head-states in descending order
     int32_t ntok;      // tokens per head-state, processed in order ([B,H,ntok,d] inputs)
     LamTable lam;
 };
