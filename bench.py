@@ -2,19 +2,23 @@
 """Benchmark of the causal kernelized linear attention hot path on one MI355X.
 
 One step = one la_forward_causal call over the whole batch of the headline
-workload (elu+1, B=4, H=8, N=4096, d_k=d_v=64, bf16 inputs, fp32 state): the
-segment-state pass, the segment scan and the chunked output pass.  Inputs are
-seeded synthetic tensors already resident in HBM when timing starts.
+workload (elu+1 with per-head decay, B=2, H=16, N=32768, d_k=d_v=128, bf16
+inputs, fp32 state): the segment-state pass, the segment scan and the chunked
+output pass.  Inputs are seeded synthetic tensors already resident in HBM
+when timing starts.
 
-Printed: ONE JSON line with the throughput (Mtokens/s, tokens = B*N), the
-roofline of the dominant kernel (algorithmic bytes per launch over its mean
-device time, from HIP events the library records around each of its launches
-on the launch stream), the secondary workloads (decode step on 256x32 state,
-long causal forwards with per-head decay and with random features) each with
-its own roofline, and the fp64 CPU oracle timed on the host as a baseline.
+Printed last, on stdout: ONE compact JSON line with the headline throughput
+(Mtokens/s, tokens = B*N), the roofline of its dominant kernel (algorithmic
+bytes per launch over its mean device time, from HIP events the library
+records around each of its launches on the launch stream), the whole step's
+HBM fraction, the matrix-core rate, the decode step (256x32 head-states,
+d=128, plain visiting order) against HBM, the throughput against sequence
+length, short figures of the other workloads and the fp64 CPU oracle timed
+on the host as a baseline.  Each line's full record goes to stderr as it is
+measured (and to --detail FILE as one JSON document).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-                       [--no-cpu-baseline] [--only NAME]
+                       [--no-cpu-baseline] [--only NAME] [--detail FILE]
 """
 import argparse
 import hashlib
@@ -163,13 +167,18 @@ def bench_causal(ctx, name, B, H, N, dk, dv, lam, phi, gen, steps=None, planned_
     achieved = alg / (dom_ms * 1e-3) / 1e9
     step_bytes = causal_bytes(B, H, N, dk, dv, 2, 2)
     flops_min = 4.0 * F * dv * B * H * N
+    C = 32  # tokens per chunk of every forward kernel
+    flops_exec = flops_min + 2.0 * C * (F + dv) * B * H * N
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
     res = {
         "workload": name, "ms_per_step": round(ms, 4), "Mtokens_per_s": round(tokens / (ms * 1e-3) / 1e6, 2),
         "head_tokens_per_s": round(B * H * N / (ms * 1e-3), 1),
-        "step_alg_bytes": step_bytes, "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_alg_bytes": step_bytes, "step_GBps": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "recurrent_TFLOPs": round(flops_min / (ms * 1e-3) / 1e12, 2),
         "recurrent_mfma_frac": round(flops_min / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "executed_TFLOPs": round(flops_exec / (ms * 1e-3) / 1e12, 2),
+        "executed_mfma_frac": round(flops_exec / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "segments": P,
         "kernels": {la.la_kernel_name(kid): {"mean_ms": round(t, 4), "launches_per_step": n}
                     for kid, (t, n) in kt.items()},
@@ -185,52 +194,77 @@ def device_normal(torch, gen, shape, scale, dev):
     return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * scale).to(torch.bfloat16)
 
 
-def workload2(ctx):
+def host_to_dev(ctx, inp, name):
+    """Seeded host inputs (bf16 bit patterns) on the device."""
+    return ctx.torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(ctx.torch.bfloat16).to(ctx.dev)
+
+
+def workload3_headline(ctx):
+    """The headline: the seeded inputs of the per-head-decay workload (the
+    same bytes the CPU baseline reads), timed for exactly --steps steps after
+    --warmup steps and half a second of clock warm-up."""
     import seeded_inputs as si
-    torch = ctx.torch
-    wl = si.workload(2)
+    wl = si.workload(3)
     inp = si.make_inputs(wl)
-
-    def t(name):
-        return torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16).to(ctx.dev)
-
-    gen = (t("q"), t("k"), t("v"))
-    # timed first in the run, after half a second of its own steps to bring
-    # the clocks up (a few milliseconds of work leave them still rising)
+    gen = tuple(host_to_dev(ctx, inp, n) for n in ("q", "k", "v"))
     res = bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, inp["lam"], ctx.la.Phi(), gen,
                        clock_warmup=0.5)
     return wl, inp, res
 
 
-# Timed steps of the secondary workloads: about 20 ms of device time each.
-SECONDARY_STEPS = {"w3": 50, "w5": 25}
+# Timed steps of the secondary workloads: about 10-20 ms of device time each.
+SECONDARY_STEPS = {"w2": 200, "w5": 25}
 
 
-def workload3(ctx):
+def workload2(ctx):
+    import seeded_inputs as si
+    wl = si.workload(2)
+    inp = si.make_inputs(wl)
+    gen = tuple(host_to_dev(ctx, inp, n) for n in ("q", "k", "v"))
+    return bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, inp["lam"], ctx.la.Phi(), gen,
+                        steps=SECONDARY_STEPS["w2"], warmup=max(ctx.warmup, 5), clock_warmup=0.2)
+
+
+def workload5(ctx, m=128):
     import seeded_inputs as si
     torch = ctx.torch
-    wl = si.workload(3)
-    g = torch.Generator(device=ctx.dev)
-    g.manual_seed(3)
-    shape = (wl.B, wl.H, wl.N, wl.dk)
-    gen = tuple(device_normal(torch, g, shape, wl.scale, ctx.dev) for _ in range(3))
-    lam = si.make_lambda(wl)
-    return bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, lam, ctx.la.Phi(), gen,
-                        steps=SECONDARY_STEPS["w3"], warmup=max(ctx.warmup, 5))
-
-
-def workload5(ctx):
-    import seeded_inputs as si
-    torch = ctx.torch
-    wl = si.workload(5)
+    wl = si.workload(5).with_(m=m)
     g = torch.Generator(device=ctx.dev)
     g.manual_seed(5)
     shape = (wl.B, wl.H, wl.N, wl.dk)
     gen = tuple(device_normal(torch, g, shape, wl.scale, ctx.dev) for _ in range(3))
     omega = torch.from_numpy(si.make_omega(wl.m, wl.dk, wl.index)).to(ctx.dev)
     phi = ctx.la.Phi("trig_rf", omega, wl.qk_scale)
-    return bench_causal(ctx, wl.name, wl.B, wl.H, wl.N, wl.dk, wl.dv, si.make_lambda(wl), phi, gen,
+    name = wl.name if m == 128 else wl.name.replace("m128", "m%d" % m)
+    return bench_causal(ctx, name, wl.B, wl.H, wl.N, wl.dk, wl.dv, si.make_lambda(wl), phi, gen,
                         steps=SECONDARY_STEPS["w5"], warmup=max(ctx.warmup, 5))
+
+
+def length_scaling(ctx, Ns=(1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)):
+    """Throughput against sequence length at the headline's heads (B=2, H=16,
+    d=128, per-head decay): one causal forward per step, about 10 ms of
+    device time per point.  Device bytes = q, k, v, y and the workspace."""
+    import seeded_inputs as si
+    torch, la = ctx.torch, ctx.la
+    wl = si.workload(3)
+    lam = si.make_lambda(wl)
+    g = torch.Generator(device=ctx.dev)
+    out = []
+    for N in Ns:
+        g.manual_seed(N)
+        shape = (wl.B, wl.H, N, wl.dk)
+        gen = tuple(device_normal(torch, g, shape, wl.scale, ctx.dev) for _ in range(3))
+        steps = max(5, int(10.0 / max(1e-3, 0.45 * N / 32768)))
+        r = bench_causal(ctx, "scaling_N%d" % N, wl.B, wl.H, N, wl.dk, wl.dv, lam, la.Phi(), gen, steps=steps,
+                         warmup=3)
+        ws = la.la_workspace_size(wl.B, wl.H, N, wl.dk, wl.dv)
+        out.append({"N": N, "ms": r["ms_per_step"], "Mtokens_per_s": r["Mtokens_per_s"],
+                    "step_hbm_frac": r["step_hbm_frac"], "out_pass_frac": r["roofline"]["frac"],
+                    "device_MB": round((r["step_alg_bytes"] + ws) / 1e6, 1)})
+        log(json.dumps(out[-1]))
+        del gen
+        torch.cuda.empty_cache()
+    return out
 
 
 def feature_map_variant(ctx, base, phi, m=0, steps=20):
@@ -502,7 +536,8 @@ SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2
 
 def workload4_decode(ctx, steps=1024):
     """Decode: prefix of 512 tokens through the causal forward, then `steps`
-    single-token steps timed back to back.  Bytes per step: state read and
+    single-token steps timed back to back (head-states visited in plain
+    ascending order on every step).  Bytes per step: the state read and
     written once, plus q, k, v, y."""
     import seeded_inputs as si
     torch, la = ctx.torch, ctx.la
@@ -535,8 +570,9 @@ def workload4_decode(ctx, steps=1024):
     per_step = state_bytes + io_bytes
     achieved = per_step / (dec_ms * 1e-3) / 1e9
     return {
-        "workload": wl.name, "ms_per_step": round(ms, 4), "steps_timed": steps,
+        "workload": wl.name, "ms_per_step": round(ms, 4), "steps_timed": steps, "order": "plain",
         "state_GBps": round(per_step / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(per_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "Mtokens_per_s": round(B / (ms * 1e-3) / 1e6, 4),
         "head_tokens_per_s": round(B * H / (ms * 1e-3), 1),
         "alg_bytes_per_step": per_step,
@@ -717,11 +753,27 @@ def traffic_from(root):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, inp, min_seconds=10.0, max_passes=400):
-    """The fp64 oracle, as it stands, on the host cores: whole passes over the
-    headline workload, repeated until at least `min_seconds` of CPU work."""
+    """The fp64 oracle, as it stands, on the host cores granted to this
+    process: whole passes over the headline workload, repeated until at least
+    `min_seconds` of CPU work."""
     import oracle
     threads = oracle.default_threads()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
     passes, t0 = 0, time.perf_counter()
     while True:
         oracle.causal(inp["q"], inp["k"], inp["v"], inp["lam"], wl.eps, threads=threads)
@@ -730,9 +782,19 @@ def cpu_baseline(wl, inp, min_seconds=10.0, max_passes=400):
         if dt >= min_seconds or passes >= max_passes:
             break
     return {"value": round(passes * wl.B * wl.N / dt / 1e6, 5), "unit": "Mtokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(), "affinity_cores": affinity,
             "sample": "%d whole passes over the workload (B=%d H=%d N=%d d=%d, fp64 per-token recurrence) "
                       "in %.2f s" % (passes, wl.B, wl.H, wl.N, wl.dk, dt)}
+
+
+def compact(r):
+    """Short figures of a secondary line for the printed JSON line."""
+    out = {"ms": r.get("ms_per_step", r.get("ms_per_call"))}
+    if "Mtokens_per_s" in r:
+        out["Mtok_s"] = r["Mtokens_per_s"]
+    if "roofline" in r:
+        out["frac"] = r["roofline"]["frac"]
+    return out
 
 
 def main():
@@ -742,7 +804,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "copy"] + [v[0] for v in VARIANTS] +
+    ap.add_argument("--detail", metavar="FILE", help="write every line's full record to FILE (JSON)")
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "copy", "scaling"] + [v[0] for v in VARIANTS] +
                     [v[0] for v in SHAPE_VARIANTS],
                     help="run one workload (profiling)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -759,10 +822,9 @@ def main():
         sys.exit(2)
 
     ctx = Ctx(args.steps, args.warmup)
-    import seeded_inputs as si
-    if args.only and args.only != "w2":
-        fns = {"w3": workload3, "w4": workload4_decode, "w5": workload5, "copy": state_copy,
-               "w4multi": workload4_multi}
+    if args.only:
+        fns = {"w2": workload2, "w3": lambda c: workload3_headline(c)[2], "w4": workload4_decode, "w5": workload5,
+               "copy": state_copy, "w4multi": workload4_multi, "scaling": length_scaling}
         for key, base, phi, m, steps in VARIANTS:
             fns[key] = (lambda c, b=base, p=phi, mm=m, st=steps: feature_map_variant(c, b, p, mm, st))
         fns.update(dict(SHAPE_VARIANTS))
@@ -771,16 +833,26 @@ def main():
         print(json.dumps({"only": args.only, "result": fn(ctx)}), flush=True)
         return
 
-    # the headline first (after its own clock warm-up), then the secondary lines
-    log("workload 2 (headline) ...")
-    wl, inp, res = workload2(ctx)
+    # the headline first (after its own clock warm-up), then the decode line
+    log("workload 3 (headline) ...")
+    wl, inp, res = workload3_headline(ctx)
     log(json.dumps(res))
     ctx.torch.cuda.empty_cache()
-    extra = {}
+    log("decode_w4 ...")
+    dec = workload4_decode(ctx)
+    log(json.dumps(dec))
+    ctx.torch.cuda.empty_cache()
+    log("state copy ...")
+    cp = state_copy(ctx)
+    log(json.dumps(cp))
+    detail = {"headline": res, "decode_w4": dec, "state_copy": cp}
+    scaling, extra = None, {}
     if not args.no_extra:
-        for key, fn in (("decode_w4", workload4_decode), ("decode_multi4_w4", workload4_multi),
-                        ("decode_multi16_w4", lambda c: workload4_multi(c, 16, 64)),
-                        ("causal_w3", workload3), ("causal_w5", workload5)):
+        log("length scaling ...")
+        scaling = length_scaling(ctx)
+        detail["length_scaling"] = scaling
+        for key, fn in (("w2", workload2), ("decode_multi4_w4", workload4_multi),
+                        ("decode_multi16_w4", lambda c: workload4_multi(c, 16, 64)), ("w5", workload5)):
             log(key, "...")
             extra[key] = fn(ctx)
             log(json.dumps(extra[key]))
@@ -795,10 +867,16 @@ def main():
             extra[key] = fn(ctx)
             log(json.dumps(extra[key]))
             ctx.torch.cuda.empty_cache()
+        detail["secondary"] = extra
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl, inp)
+        detail["cpu_baseline"] = cpu
+    if args.detail:
+        with open(args.detail, "w") as fh:
+            json.dump(detail, fh, indent=1)
+    step_bytes = res["step_alg_bytes"]
     line = {
         "metric": "causal linear-attn fwd Mtokens/s + MFMA util; decode-step state GB/s vs HBM",
         "value": res["Mtokens_per_s"],
@@ -813,16 +891,26 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)*0.5, rounded to bf16)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d_k": wl.dk, "d_v": wl.dv,
-                   "phi": wl.phi, "lambda": 1.0, "eps": wl.eps, "state": "fp32", "segments": res["segments"]},
+                   "phi": wl.phi, "lambda": "per head U[0.9,0.999]", "eps": wl.eps, "state": "fp32",
+                   "segments": res["segments"]},
         "roofline": res["roofline"],
         "dominant_kernel": res["dominant_kernel"],
-        "kernels": res["kernels"],
-        "step_hbm_frac": res["step_hbm_frac"],
-        "recurrent_mfma_frac": res["recurrent_mfma_frac"],
+        "step_roofline": {"bound": "hbm", "achieved": res["step_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": res["step_hbm_frac"], "alg_bytes": step_bytes},
+        "mfma": {"recurrent_TFLOPs": res["recurrent_TFLOPs"], "recurrent_frac": res["recurrent_mfma_frac"],
+                 "executed_TFLOPs": res["executed_TFLOPs"], "executed_frac": res["executed_mfma_frac"],
+                 "peak_TFLOPs": BF16_PEAK_TFLOPS},
+        "decode": {"workload": dec["workload"], "ms_per_step": dec["ms_per_step"], "state_GBps": dec["state_GBps"],
+                   "hbm_frac": dec["hbm_frac"], "kernel_frac": dec["roofline"]["frac"], "order": "plain",
+                   "copy_GBps": cp["device_GBps"]},
         "cpu_baseline": cpu,
-        "secondary": extra,
     }
-    print(json.dumps(line), flush=True)
+    if scaling:
+        line["length_scaling"] = [[p["N"], p["Mtokens_per_s"]] for p in scaling]
+    if extra:
+        line["secondary"] = {k: compact(v) for k, v in extra.items()}
+    sys.stderr.flush()
+    print(json.dumps(line, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":

@@ -146,13 +146,14 @@ def _rng(seed: int, stream: str, *extra: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(ss))
 
 
-def _normal(rng, shape, scale, dtype):
+def _normal(rng, shape, scale, dtype, values=True):
+    """scale * N(0,1) in fp32, then (bf16) rounded: (bits or None, values or None)."""
     x = rng.standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
-        x = (x * np.float32(scale)).astype(np.float32)
+        x *= np.float32(scale)
     if dtype == "bf16":
-        bits, vals = round_to_bf16(x)
-        return bits, vals
+        bits = bf16_bits_rne(x)
+        return bits, (bf16_bits_to_f32(bits) if values else None)
     return None, x
 
 
@@ -237,20 +238,23 @@ def _pool_map(fn, items, threads):
 
 
 def make_decode_prefix(wl: Workload, seed: Optional[int] = None, B=None, H=None, N=None,
-                       threads: int = 1, values: bool = True):
-    """The prefix tokens that initialise the decode state: [B,H,N,d].
+                       threads: int = 1, values: bool = True, b0: int = 0):
+    """The prefix tokens that initialise the decode state: [B,H,N,d], batch
+    rows b0 .. b0+B-1 of the workload.
 
     Each (tensor, batch row) pair draws from a sub-stream of its own, so a
-    smaller B keeps the first rows' values and rows can be drawn on several
-    threads.  values=False returns only the bf16 bit patterns."""
+    smaller B keeps the first rows' values, any block of rows can be drawn on
+    its own and rows can be drawn on several threads.  values=False returns
+    only the bf16 bit patterns."""
     seed = wl.index if seed is None else seed
     B = wl.B if B is None else B
     H = wl.H if H is None else H
     N = wl.N if N is None else N
     out = {}
     for j, (name, d) in enumerate((("q", wl.dk), ("k", wl.dk), ("v", wl.dv))):
-        rows = _pool_map(lambda b: _normal(_rng(seed, "prefix", j, b), (1, H, N, d), wl.scale, wl.dtype),
-                         range(B), threads)
+        rows = _pool_map(lambda b: _normal(_rng(seed, "prefix", j, b), (1, H, N, d), wl.scale, wl.dtype,
+                                           values=values or wl.dtype != "bf16"),
+                         range(b0, b0 + B), threads)
         if wl.dtype == "bf16":
             out[name + "_bits"] = np.concatenate([r[0] for r in rows], axis=0)
             if values:
@@ -260,16 +264,19 @@ def make_decode_prefix(wl: Workload, seed: Optional[int] = None, B=None, H=None,
     return out
 
 
-def make_decode_step(wl: Workload, step: int, seed: Optional[int] = None, B=None, H=None):
+def make_decode_step(wl: Workload, step: int, seed: Optional[int] = None, B=None, H=None, values: bool = True):
     """Single-token inputs of one decode step, [B,H,1,d]; regenerated from
-    (seed, step) so that no trajectory needs to be stored."""
+    (seed, step) so that no trajectory needs to be stored.  values=False
+    returns only the bf16 bit patterns of bf16 workloads."""
     seed = wl.index if seed is None else seed
     B = wl.B if B is None else B
     H = wl.H if H is None else H
     out = {}
     for j, (name, d) in enumerate((("q", wl.dk), ("k", wl.dk), ("v", wl.dv))):
-        bits, vals = _normal(_rng(seed, "steps", step, j), (B, H, 1, d), wl.scale, wl.dtype)
-        out[name] = vals
+        bits, vals = _normal(_rng(seed, "steps", step, j), (B, H, 1, d), wl.scale, wl.dtype,
+                             values=values or wl.dtype != "bf16")
+        if vals is not None:
+            out[name] = vals
         if bits is not None:
             out[name + "_bits"] = bits
     return out
@@ -281,9 +288,18 @@ def make_decode_steps(wl: Workload, t0: int, t1: int, seed: Optional[int] = None
     [t1-t0, B, H, 1, d] per tensor, bf16 bit patterns ('q_bits', ...) for
     bf16 workloads, float32 values ('q', ...) otherwise.  The same values as
     make_decode_step, drawn on `threads` threads."""
-    steps = _pool_map(lambda t: make_decode_step(wl, t, seed, B, H), range(t0, t1), threads)
-    key = "_bits" if wl.dtype == "bf16" else ""
-    return {n + key: np.stack([s[n + key] for s in steps]) for n in ("q", "k", "v")}
+    bf = wl.dtype == "bf16"
+    key = "_bits" if bf else ""
+    first = make_decode_step(wl, t0, seed, B, H, values=not bf)
+    out = {n + key: np.empty((t1 - t0,) + first[n + key].shape, dtype=first[n + key].dtype) for n in ("q", "k", "v")}
+
+    def fill(t):
+        st = first if t == t0 else make_decode_step(wl, t, seed, B, H, values=not bf)
+        for n in ("q", "k", "v"):
+            out[n + key][t - t0] = st[n + key]
+
+    _pool_map(fill, range(t0, t1), threads)
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -9,19 +9,15 @@ import torch
 import oracle
 import seeded_inputs as si
 import weight_sequence_mixing_amd as la
-from gpu_util import DEV, TOL, oracle_causal, phi_for, rel_err, row_errors, run_causal, tdtype, to_dev
+from gpu_util import DEV, TOL, check_kappa_rows, oracle_causal, phi_for, rel_err, run_causal, tdtype, to_dev
 
 pytestmark = pytest.mark.gpu
 
 
 def _check_rows(y, ref, kap, dtype):
-    """Every row within tol * max(1, kappa_r); well-conditioned rows within tol."""
-    err = row_errors(y, ref)
-    bound = TOL[dtype] * np.maximum(1.0, kap)
-    worst = int(np.argmax(err / bound))
-    assert np.all(err <= bound), (float(err.reshape(-1)[worst]), float(kap.reshape(-1)[worst]))
-    good = kap < 10
-    assert good.sum() > 0 and float(err[good].max()) < TOL[dtype]
+    """Every row within tol * max(1, kappa_r); well-conditioned rows within tol;
+    the rows a scaled bound leaves unchecked are a minority."""
+    check_kappa_rows(y, ref, kap, dtype)
 
 
 @pytest.mark.parametrize("dk,dv,dtype,N", [(64, 64, "bf16", 1000), (128, 128, "bf16", 777),

@@ -10,7 +10,7 @@ import torch
 import oracle
 import seeded_inputs as si
 import weight_sequence_mixing_amd as la
-from gpu_util import DEV, TOL, inputs, oracle_causal, phi_for, rel_err, row_errors, run_causal, tdtype, to_dev
+from gpu_util import DEV, TOL, check_kappa_rows, inputs, oracle_causal, phi_for, rel_err, run_causal, tdtype, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -61,34 +61,12 @@ def test_workload3_reduced_per_head_decay():
     assert err < TOL["bf16"], err
 
 
-def test_workload3_full_sampled_heads():
-    wl, inp = inputs(3)
-    y = run_causal(wl, inp)
-    for b, h in ((0, 0), (1, 15)):
-        ref = oracle.causal(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
-                            inp["v"][b:b + 1, h:h + 1], [inp["lam"][h]], wl.eps)
-        err = rel_err(y[b:b + 1, h:h + 1], ref)
-        assert err < TOL["bf16"], (b, h, err)
-    assert torch.isfinite(y.float()).all()
-
-
 def test_workload5_reduced_random_features():
     wl, inp = inputs(5, H=2, N=1000)
     y = run_causal(wl, inp)
     ref, kap = oracle_causal(wl, inp, want_kappa=True)
     err = rel_err(y, ref)
     assert err < TOL["bf16"], (err, float(kap.max()))
-
-
-def test_workload5_full_sampled_head():
-    wl, inp = inputs(5)
-    y = run_causal(wl, inp)
-    h = 3
-    ref = oracle.causal(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1], [1.0], wl.eps,
-                        "trig_rf", inp["omega"], wl.qk_scale)
-    err = rel_err(y[:, h:h + 1], ref)
-    assert err < TOL["bf16"], err
-    assert torch.isfinite(y.float()).all()
 
 
 @pytest.mark.parametrize("dk,m,dv,scale", [(64, 64, 128, 0.5), (128, 32, 64, 0.25), (128, 64, 128, 0.25)])
@@ -113,12 +91,7 @@ def test_random_features_ill_conditioned_rows(dk, m, dv, scale, dtype):
     y = run_causal(wl, inp, lam=[0.97, 1.0])
     ref, kap = oracle_causal(wl, inp, lam=[0.97, 1.0], want_kappa=True)
     assert float(kap.max()) > 1e3  # the case is what it claims to be
-    err = row_errors(y, ref)
-    bound = TOL[dtype] * np.maximum(1.0, kap)
-    worst = int(np.argmax(err / bound))
-    assert np.all(err <= bound), (float(err.reshape(-1)[worst]), float(kap.reshape(-1)[worst]))
-    good = kap < 10
-    assert good.sum() > 0 and float(err[good].max()) < TOL[dtype]
+    check_kappa_rows(y, ref, kap, dtype)
 
 
 @pytest.mark.parametrize("phi", ["elu1", "trig_rf"])
@@ -225,18 +198,6 @@ def test_decode_reduced_matches_forward_trajectory():
     assert rel_err(y, ref[:, :, wl.N:]) < TOL["bf16"]
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
-
-
-def test_decode_full_size_sampled():
-    wl = si.workload(4)
-    steps = 4
-    pre, lam, step_inp, y, S, z = _decode_run(wl, wl.B, wl.H, steps)
-    rng = np.random.default_rng(0)
-    for b, h in zip(rng.integers(0, wl.B, 6), rng.integers(0, wl.H, 6)):
-        cat = {n: np.concatenate([pre[n][b:b + 1, h:h + 1]] + [s[n][b:b + 1, h:h + 1] for s in step_inp], axis=2)
-               for n in ("q", "k", "v")}
-        ref = oracle.causal(cat["q"], cat["k"], cat["v"], [lam[h]], wl.eps)
-        assert rel_err(y[b:b + 1, h:h + 1], ref[:, :, wl.N:]) < TOL["bf16"], (b, h)
 
 
 def test_profile_hooks_record_launches():
