@@ -334,6 +334,27 @@ def la_workspace_size(B, H, N, d_k, d_v, in_dtype=LA_BF16, out_dtype=None, phi: 
     return int(_lib.la_workspace_size(ctypes.byref(shape), ctypes.byref(pc), 1 if causal else 0))
 
 
+def _alloc_ws(need: int, workspace, device, stream=None):
+    """The caller's workspace, or a new one.  A new block is marked as used on
+    the launch stream, so that the caching allocator does not hand it out
+    again before the kernels enqueued there have finished."""
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None:
+            s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+            workspace.record_stream(s)
+    elif not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _workspace(shape: LaShapeC, pc: LaPhiC, causal: bool, workspace, device, stream=None):
+    need = int(_lib.la_workspace_size(ctypes.byref(shape), ctypes.byref(pc), 1 if causal else 0))
+    return _alloc_ws(need, workspace, device, stream)
+
+
 def _causal_args(q, k, v, y, phi, S_in, z_in, S_out, z_out, mask=None):
     """Checks of the causal forwards' tensors; returns (device, phi, shape, LaPhiC)."""
     B, H, N, dk, dv = _qkvy(q, k, v, y)
