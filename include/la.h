@@ -151,6 +151,24 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
                             float* S_out, float* z_out,
                             void* workspace, size_t workspace_bytes, la_stream_t stream);
 
+/* la_forward_causal for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments without the workspace.  The
+ * segment states live in a static device array of LA_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every device it runs on until the process
+ * ends; the call allocates nothing.  The number of segments is capped so that
+ * their states fit it (fewer segments: less parallelism, the same result up
+ * to rounding order).  A window carry state (LA_WINDOWS > 1) that does not fit
+ * on its own is LA_ERR_WORKSPACE.  All calls on one device share its array:
+ * calls that overlap on one device (several streams or threads) race and must
+ * be serialised by the caller. */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+la_status la_forward_causal_noalloc(const void* q, const void* k, const void* v, void* y,
+                                    const la_shape* shape, const la_phi* phi,
+                                    const float* lambda_h, float eps,
+                                    const float* S_in, const float* z_in,
+                                    float* S_out, float* z_out, la_stream_t stream);
+
 /* Non-causal forward ("From standard attention to linear attention" sec. 3
  * and sec. 6): S = sum_j phi(k_j) v_j^T and z = sum_j phi(k_j) over the whole
  * sequence (no decay), then y_i = phi(q_i)^T S / (phi(q_i)^T z + eps).

@@ -246,3 +246,21 @@ def test_cross_backward_validation(lib):
     big_k = lib.la_workspace_size_backward_cross(ctypes.byref(s), 1 << 16, ctypes.byref(ELU))
     big_q = lib.la_workspace_size_backward_cross(ctypes.byref(_shape(N=1 << 16)), 100, ctypes.byref(ELU))
     assert big_k > n and big_q > n
+
+
+def test_noalloc_forward_host_validation(lib, monkeypatch):
+    """The static-scratch forward validates like la_forward_causal, and a
+    window carry larger than its scratch is refused on the host."""
+    def call(shape, lam=None, eps=1e-6):
+        lam_arr = (ctypes.c_float * len(lam))(*lam) if lam else None
+        return lib.la_forward_causal_noalloc(FAKE, FAKE + GAP, FAKE + 2 * GAP, FAKE + 3 * GAP, ctypes.byref(shape),
+                                             ctypes.byref(ELU), ctypes.cast(lam_arr, ctypes.c_void_p) if lam else None,
+                                             eps, None, None, None, None, None)
+    assert call(_shape(dk=96)) == la.binding.LA_ERR_UNSUPPORTED
+    assert call(_shape(), lam=[1.5, 1.0]) == la.binding.LA_ERR_INVALID_ARGUMENT
+    assert call(_shape(), eps=float("nan")) == la.binding.LA_ERR_INVALID_ARGUMENT
+    # 1024 heads of a 128 x 129 fp32 state: one carry slot is 67.6 MB > 64 MiB
+    monkeypatch.setenv("LA_WINDOWS", "2")
+    st = call(_shape(B=4, H=256, N=64, dk=128, dv=128))
+    assert st == la.binding.LA_ERR_WORKSPACE, la.la_last_error()
+    assert "static scratch" in la.la_last_error()

@@ -103,3 +103,9 @@ def test_cpu_tensors_are_rejected_last():
     one = t(B, H, 1, D)
     raises("GPU device", la.la_decode_step, one, one.clone(), one.clone(), one.clone(),
            t(B, H, D, D, dtype=torch.float32), t(B, H, D, dtype=torch.float32))
+
+
+def test_package_exports_every_entry_point():
+    for name in la.EXPORTS:
+        if name.startswith("la_") and name not in ("la_status_string", "la_last_error"):
+            assert hasattr(la, name), name

@@ -9,7 +9,7 @@ the current HIP stream.
 from .binding import (  # noqa: F401
     EXPORTS, KERNEL_IDS, LA_BF16, LA_F32, LA_MAX_HEADS, LA_PHI_ELU1, LA_PHI_RELU, LA_PHI_TRIG_RF,
     LA_PHI_TRIG_RF_PLAIN, LA_PHI_TRIG_RF_SOFTMAX, LaError, Phi,
-    la_decode_step, la_forward_causal, la_forward_causal_masked, la_forward_causal_varlen, la_forward_cross,
+    la_decode_step, la_forward_causal, la_forward_causal_noalloc, la_forward_causal_masked, la_forward_causal_varlen, la_forward_cross,
     la_forward_noncausal, la_init_state, la_init_state_identity, la_kernel_name, la_workspace_size_cross,
     la_workspace_size_varlen, la_backward_causal, la_workspace_size_backward, la_backward_cross,
     la_workspace_size_backward_cross,

@@ -27,7 +27,8 @@ ELEMENTWISE = ("elu1", "relu")
 LA_MAX_HEADS = 256
 
 # names declared in include/la.h
-EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_forward_causal", "la_forward_noncausal",
+EXPORTS = ("la_init_state", "la_init_state_identity", "la_workspace_size", "la_forward_causal",
+           "la_forward_causal_noalloc", "la_forward_noncausal",
            "la_forward_causal_masked", "la_workspace_size_varlen", "la_forward_causal_varlen",
            "la_workspace_size_cross", "la_forward_cross", "la_workspace_size_backward", "la_backward_causal",
            "la_workspace_size_backward_cross", "la_backward_cross",
@@ -83,6 +84,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.la_workspace_size.restype = sz
     lib.la_forward_causal.argtypes = [vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, sz, vp]
     lib.la_forward_causal.restype = ctypes.c_int
+    lib.la_forward_causal_noalloc.argtypes = [vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp]
+    lib.la_forward_causal_noalloc.restype = ctypes.c_int
     lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, SP, PP, f, vp, sz, vp]
     lib.la_forward_noncausal.restype = ctypes.c_int
     lib.la_forward_causal_masked.argtypes = [vp, vp, vp, vp, SP, PP, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -377,6 +380,23 @@ def la_forward_causal(q, k, v, y, phi: Optional[Phi] = None, lambda_h=None, eps:
     _check(_lib.la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
                                   lam_ptr, float(eps), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
                                   _ptr(ws), ws_bytes, _stream(stream)))
+    del lam_keep
+    return y
+
+
+LA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/la.h
+
+
+def la_forward_causal_noalloc(q, k, v, y, phi: Optional[Phi] = None, lambda_h=None, eps: float = 1e-6,
+                              S_in=None, z_in=None, S_out=None, z_out=None, stream=None):
+    """la_forward_causal without a workspace: the library's static device
+    scratch holds the segment states (nothing is allocated by the call)."""
+    load_library()
+    lam_keep, lam_ptr = _lam(lambda_h, q.shape[1])
+    dev, phi, shape, pc = _causal_args(q, k, v, y, phi, S_in, z_in, S_out, z_out)
+    _check(_lib.la_forward_causal_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(y), ctypes.byref(shape), ctypes.byref(pc),
+                                          lam_ptr, float(eps), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                          _stream(stream)))
     del lam_keep
     return y
 

@@ -36,6 +36,7 @@ SOURCES = [
     "la_inst_ident_bf16.hip",
     "la_inst_ident_f32.hip",
     "la_rf_grad.hip",
+    "la_scratch.hip",
     "la_api.cpp",
 ]
 

@@ -216,20 +216,23 @@ struct Plan {
 constexpr int kTargetWorkgroups = 512;
 
 // Segments wanted for a row of NC chunks (before rounding to whole chunks).
-int64_t target_segments(int64_t NC, int64_t BH)
+// max_P: an upper bound on the segments (the static-scratch forward caps them
+// so that their states fit its scratch).
+int64_t target_segments(int64_t NC, int64_t BH, int64_t max_P = INT64_MAX)
 {
     int64_t P = (kTargetWorkgroups + BH - 1) / BH;
     const int forced = env_int("LA_SEGMENTS", 0);
     if (forced > 0) P = forced;
+    if (P > max_P) P = max_P;
     if (P > NC) P = NC;
     if (P < 1) P = 1;
     return P;
 }
 
 // Cut NC chunks into segments of cps chunks: every segment but the last is full.
-void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps)
+void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps, int64_t max_P = INT64_MAX)
 {
-    const int64_t Pt = target_segments(NC, BH);
+    const int64_t Pt = target_segments(NC, BH, max_P);
     *cps = (NC + Pt - 1) / Pt;
     *P = (int)((NC + *cps - 1) / *cps);
 }
@@ -266,7 +269,8 @@ size_t bytes256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // Plan of a forward over rows of N tokens (causal: may be cut into windows).
 // varlen_P > 0: packed variable-length rows cut into varlen_P segments, one window.
-Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, int varlen_P = 0)
+Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, int varlen_P = 0,
+               int64_t max_P = INT64_MAX)
 {
     Plan p;
     p.C = e->C;
@@ -278,7 +282,7 @@ Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, int 
     if (W > NC) W = (int)(NC > 0 ? NC : 1);
     p.W = W;
     // every window has at most NC chunks, so it is cut into at most this many segments
-    p.Pmax = varlen_P > 0 ? varlen_P : (int)target_segments(NC > 0 ? NC : 1, BH);
+    p.Pmax = varlen_P > 0 ? varlen_P : (int)target_segments(NC > 0 ? NC : 1, BH, max_P);
     size_t floats = 0;
     if (causal) {
         if (p.Pmax > 1) floats += (size_t)p.Pmax * BH * p.SZ;
@@ -456,14 +460,17 @@ size_t la_workspace_size(const la_shape* shape, const la_phi* phi, int32_t causa
 
 namespace {
 
-// Causal forward shared by the fixed-length, masked and packed entry points.
-// kpm: key padding mask [B][N] bytes or null.  cu: packed sequences (device
-// [B+1] offsets into head rows of N tokens) or null; max_len then plans the
-// segments (the longest sequence).
+// Causal forward shared by the fixed-length, masked, packed and static-scratch
+// entry points.  kpm: key padding mask [B][N] bytes or null.  cu: packed
+// sequences (device [B+1] offsets into head rows of N tokens) or null; max_len
+// then plans the segments (the longest sequence).  use_scratch: the workspace
+// is the library's static device scratch (workspace arguments ignored); the
+// segments are capped so that their states fit it.
 la_status forward_causal(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
                          const la_phi* phi, const float* lambda_h, float eps, const uint8_t* kpm,
                          const int32_t* cu, int64_t max_len, const float* S_in, const float* z_in, float* S_out,
-                         float* z_out, void* workspace, size_t workspace_bytes, la_stream_t stream)
+                         float* z_out, void* workspace, size_t workspace_bytes, la_stream_t stream,
+                         bool use_scratch = false)
 {
     int F = 0;
     const KernelEntry* ent = nullptr;
@@ -507,7 +514,31 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
     } else {
         if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
     }
-    Plan plan = make_plan(shape, F, ent, true, vP);
+    int64_t max_P = INT64_MAX;
+    if (use_scratch) {
+        // segment states of P segments: P slots of BH states; a window carry
+        // (LA_WINDOWS > 1) one more slot that must fit on its own
+        const size_t slot = (size_t)BH * ((size_t)F * shape->d_v + F) * sizeof(float);
+        const Plan p1 = make_plan(shape, F, ent, true, 0, 1);
+        const size_t carry = p1.W > 1 ? slot : 0;
+        if (carry > kScratchBytes)
+            return fail(LA_ERR_WORKSPACE, "the window carry needs %zu bytes; the static scratch holds %zu", carry,
+                        kScratchBytes);
+        max_P = (int64_t)((kScratchBytes - carry) / slot);
+        if (max_P < 1) max_P = 1;
+    }
+    Plan plan = make_plan(shape, F, ent, true, vP, max_P);
+    if (use_scratch) {
+        if (plan.ws_bytes > kScratchBytes)
+            return fail(LA_ERR_WORKSPACE, "the plan needs %zu bytes; the static scratch holds %zu", plan.ws_bytes,
+                        kScratchBytes);
+        workspace = nullptr;
+        workspace_bytes = kScratchBytes;
+        if (plan.ws_bytes > 0) {
+            const hipError_t se = scratch_ptr(&workspace);
+            if (se != hipSuccess) return hip_fail(se, "static scratch address");
+        }
+    }
     const size_t seg_bytes = plan.ws_bytes;
     if (cu) plan.ws_bytes = seg_bytes + bytes256((size_t)vG * sizeof(int32_t));  // + the item table
     if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
@@ -553,7 +584,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             });
             if (ie != hipSuccess) return hip_fail(ie, "packed sequence items launch");
         } else {
-            cut_segments(c1 - c0, BH, &P, &cps);
+            cut_segments(c1 - c0, BH, &P, &cps, max_P);
         }
         // state entering and leaving this window
         const float* Si = nullptr;
@@ -635,6 +666,14 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* y
 {
     return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, nullptr, nullptr, 0, S_in, z_in, S_out, z_out,
                           workspace, workspace_bytes, stream);
+}
+
+la_status la_forward_causal_noalloc(const void* q, const void* k, const void* v, void* y, const la_shape* shape,
+                                    const la_phi* phi, const float* lambda_h, float eps, const float* S_in,
+                                    const float* z_in, float* S_out, float* z_out, la_stream_t stream)
+{
+    return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, nullptr, nullptr, 0, S_in, z_in, S_out, z_out,
+                          nullptr, 0, stream, true);
 }
 
 la_status la_forward_causal_masked(const void* q, const void* k, const void* v, void* y, const la_shape* shape,

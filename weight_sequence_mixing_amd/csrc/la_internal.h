@@ -281,4 +281,10 @@ hipError_t launch_rf_grad(const RfGradArgs& a, bool vjp, hipStream_t stream);
 hipError_t launch_fill_identity(float* S, float* z, int64_t BH, int F, int DV, float alpha, hipStream_t stream);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream);
 
+// Static device scratch of la_forward_causal_noalloc (la_scratch.hip): one
+// array of kScratchBytes per device, held until the process ends.  Its
+// address on the current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)LA_NOALLOC_SCRATCH_BYTES;
+hipError_t scratch_ptr(void** out);
+
 }  // namespace la
