@@ -261,6 +261,6 @@ def test_noalloc_forward_host_validation(lib, monkeypatch):
     assert call(_shape(), eps=float("nan")) == la.binding.LA_ERR_INVALID_ARGUMENT
     # 1024 heads of a 128 x 129 fp32 state: one carry slot is 67.6 MB > 64 MiB
     monkeypatch.setenv("LA_WINDOWS", "2")
-    st = call(_shape(B=4, H=256, N=64, dk=128, dv=128))
+    st = call(_shape(B=4, H=256, N=256, dk=128, dv=128))
     assert st == la.binding.LA_ERR_WORKSPACE, la.la_last_error()
     assert "static scratch" in la.la_last_error()

@@ -607,6 +607,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
         a.n_len = n_len;
         a.P = P;
         a.cps = cps;
+        a.chunk = plan.C;
         hipError_t e;
         if (P > 1) {
             // pass 1: segment-local states
@@ -749,6 +750,7 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     cut_segments((shape->N + plan.C - 1) / plan.C, BH, &P, &cps);
     a.P = P;
     a.cps = cps;
+    a.chunk = plan.C;
     a.out_f32 = shape->out_dtype == LA_F32 && shape->in_dtype != LA_F32;
     a.eps = eps;
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
@@ -837,6 +839,7 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
     a.rf_sign = rf_sign(phi->kind);
     a.omega = phi->omega;
     make_lam(nullptr, shape->H, &a.lam);  // no decay in the non-causal form
+    a.chunk = plan.C;
 
     // pass 1 over the n_kv keys: segment sums of phi(k) [v, 1]^T
     int Pk = 1;
@@ -1205,6 +1208,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         a.H = (int32_t)shape->H;
         a.P = plan.P;
         a.cps = plan.cps;
+        a.chunk = bent->C;
         a.eps = eps;
         a.qk_scale = 1.0f;
         a.kpm = key_padding_mask;
@@ -1386,6 +1390,7 @@ la_status la_backward_cross(const void* q, const void* k, const void* v, const v
     l.H = (int32_t)shape->H;
     l.P = plan.Pk;
     l.cps = plan.cpsk;
+    l.chunk = ent->C;
     l.eps = eps;
     l.qk_scale = 1.0f;
     l.kpm = key_padding_mask;

@@ -70,12 +70,47 @@ constexpr int chunk_len(int F) {
     return 32;
 }
 
+// Tokens per planning chunk (the unit in which a call cuts segments): 64 where
+// the causal output pass is la_out_kernel (bf16 inputs, elementwise maps),
+// whose chunks are 64 tokens; the kernel's own chunk length elsewhere.
+template <class T, int PHI>
+constexpr int plan_chunk(int F) {
+    return (sizeof(T) == 2 && (PHI == LA_PHI_ELU1 || PHI == LA_PHI_RELU)) ? 64 : chunk_len<T, PHI>(F);
+}
+
 // log2 of the smallest pending decay factor before the state is rescaled
 constexpr float kLog2MinScale = -60.f;
+
+// Chunks whose loads are in flight while one chunk is computed.  The d = 128
+// output pass needs more than 256 registers per lane, so one workgroup holds a
+// compute unit alone and its own prefetch is all that covers HBM latency:
+// one 24 KB chunk ahead leaves the pass latency-bound.  Deeper prefetch there
+// costs registers but no occupancy.
+#ifndef LA_PREFETCH_DEPTH_WIDE
+#define LA_PREFETCH_DEPTH_WIDE 1
+#endif
+template <int PHI, int F, int DV, int MODE>
+constexpr int prefetch_depth()
+{
+    return (MODE == MODE_CAUSAL && PHI != LA_PHI_TRIG_RF && F >= 128 && DV >= 128) ? LA_PREFETCH_DEPTH_WIDE : 1;
+}
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1 in order until one returns true.
+template <int I, int E, class Fn>
+__device__ __forceinline__ bool static_until(Fn&& f)
+{
+    if constexpr (I >= E) {
+        return false;
+    } else {
+        if (f(std::integral_constant<int, I>{})) return true;
+        return static_until<I + 1, E>(f);
+    }
+}
 
 template <class T, int PHI, int DK, int F, int DV, int C, int NW, int MODE>
 struct FwdCfg {
     static constexpr int NT = NW * 64;
+    static constexpr int PF = prefetch_depth<PHI, F, DV, MODE>();
     static constexpr int VEC = 16 / (int)sizeof(T);
     static constexpr bool RF = PHI == LA_PHI_TRIG_RF;
     static constexpr int M = RF ? F / 2 : 0;
@@ -200,9 +235,11 @@ la_fwd_kernel(const FwdArgs a)
         row0 = (int64_t)h * a.N + s0;
         n_len = s1 - s0;
     }
-    // segments of cps chunks; the last one takes whatever remains
+    // segments of cps units of a.chunk tokens (a multiple of C); the last one
+    // takes whatever remains
+    const int64_t cps = a.chunk > C ? a.cps * (a.chunk / C) : a.cps;
     const int64_t NC = spare ? 0 : (n_len + C - 1) / C;
-    const int64_t c_beg = (int64_t)seg * a.cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + a.cps);
+    const int64_t c_beg = (int64_t)seg * cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + cps);
     // an empty segment (an empty packed sequence) has nothing to compute and
     // nothing to store, unless it carries a state through
     if (c_beg >= c_end) {
@@ -294,8 +331,11 @@ la_fwd_kernel(const FwdArgs a)
     const bool ragged = c_end > c_beg && c_end * C > n_len;
     const int64_t c_full = ragged ? c_end - 1 : c_end;
     const int n_tail = ragged ? (int)(n_len - c_full * C) : C;
-    uint4 rq[Cfg::NEED_Q ? RQ : 1], rk[Cfg::NEED_K ? RQ : 1], rv[Cfg::NEED_K ? RV : 1];
-    int mk[Cfg::NEED_K ? RQ : 1];  // mask bytes of this thread's key rows
+    // PF register sets, each holding one chunk's loads (set s, chunk c: any
+    // chunk with c - c_beg = s mod PF)
+    constexpr int PF = Cfg::PF;
+    uint4 rq[PF][Cfg::NEED_Q ? RQ : 1], rk[PF][Cfg::NEED_K ? RQ : 1], rv[PF][Cfg::NEED_K ? RV : 1];
+    int mk[PF][Cfg::NEED_K ? RQ : 1];  // mask bytes of this thread's key rows
     auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const uint4 zero = {0u, 0u, 0u, 0u};
@@ -310,26 +350,37 @@ la_fwd_kernel(const FwdArgs a)
             }
         }
     };
-    // chunk c: a full one (c < c_full) or, with TAIL, the ragged last one
-    auto load_chunk = [&](int64_t c, auto tail_c) LA_INLINE {
+    // chunk c into register set `set_c`: a full one (c < c_full) or, with
+    // TAIL, the ragged last one
+    auto load_chunk = [&](auto set_c, int64_t c, auto tail_c) LA_INLINE {
+        constexpr int st = decltype(set_c)::value;
         const int64_t t0 = c * C;
         const int n = decltype(tail_c)::value ? n_tail : C;
-        if constexpr (Cfg::NEED_Q) load_rows(rq, qg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
+        if constexpr (Cfg::NEED_Q) load_rows(rq[st], qg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
         if constexpr (Cfg::NEED_K) {
-            load_rows(rk, kg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
-            load_rows(rv, vg + t0 * DV, VPRV, DV, RV, n, tail_c);
+            load_rows(rk[st], kg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
+            load_rows(rv[st], vg + t0 * DV, VPRV, DV, RV, n, tail_c);
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
                 const int j = (tid + r * NT) / VPRQ;
-                mk[r] = kp ? (int)kp[t0 + (decltype(tail_c)::value ? min(j, n - 1) : j)] : 0;
+                mk[st][r] = kp ? (int)kp[t0 + (decltype(tail_c)::value ? min(j, n - 1) : j)] : 0;
             }
         }
     };
 
-    // the first chunk's loads go out before the carried state is read, so
-    // that the two memory latencies overlap
-    if (c_beg < c_full) load_chunk(c_beg, std::false_type{});
-    else if (c_beg < c_end) load_chunk(c_beg, std::true_type{});
+    // the first chunks' loads go out before the carried state is read, so
+    // that the memory latencies overlap.  With PF > 1 the sets are filled
+    // with chunks c_beg .. c_beg + PF - 1; a chunk past the last full one is
+    // replaced by the last full one (loads that hit in the cache and are
+    // never used), so that every load of the chunk loop is unconditional.
+    if (c_beg < c_full) {
+        static_until<0, PF>([&](auto s_c) LA_INLINE {
+            load_chunk(s_c, min(c_beg + (int64_t)decltype(s_c)::value, c_full - 1), std::false_type{});
+            return false;
+        });
+    } else if (c_beg < c_end) {
+        load_chunk(std::integral_constant<int, 0>{}, c_beg, std::true_type{});
+    }
 
     // ---- carried state: S tiles (fb, this wave's d-blocks) and this wave's z
     // tiles fb = ZB * wave + u; lane (g, l16) of a z tile holds
@@ -429,7 +480,8 @@ la_fwd_kernel(const FwdArgs a)
     // TAIL (a std::bool_constant): the chunk is a ragged last chunk.  Query
     // rows past its end need no masking: each feeds only its own output row,
     // which is never stored.  Key rows past the end must not reach the state.
-    auto stage = [&](int buf, int n, float kw_l2, auto tail_c) LA_INLINE {
+    auto stage = [&](auto set_c, int buf, int n, float kw_l2, auto tail_c) LA_INLINE {
+        constexpr int st = decltype(set_c)::value;
         constexpr bool TAIL = decltype(tail_c)::value;
         T* const sQ = sQ0 + (RF ? 0 : buf * TQ);
         T* const sK = sK0 + (RF ? 0 : buf * TQ);
@@ -441,7 +493,7 @@ la_fwd_kernel(const FwdArgs a)
             for (int r = 0; r < RQ; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRQ;
                 float x[VEC];
-                unpack16(rq[r], x, (const T*)nullptr);
+                unpack16(rq[st][r], x, (const T*)nullptr);
                 if constexpr (RF) {
                     float s2 = 0.f;
 #pragma unroll
@@ -464,7 +516,7 @@ la_fwd_kernel(const FwdArgs a)
             for (int r = 0; r < RQ; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRQ;
                 float x[VEC];
-                unpack16(rk[r], x, (const T*)nullptr);
+                unpack16(rk[st][r], x, (const T*)nullptr);
                 if constexpr (RF) {
                     float s2 = 0.f;
 #pragma unroll
@@ -474,12 +526,12 @@ la_fwd_kernel(const FwdArgs a)
                     }
                     s2 = wave_sum_xor(s2, 1, VPRQ / 2);
                     // a padded key is marked by a negative norm
-                    if (cg == 0) sXn[C + j] = mk[r] ? -1.f : s2;
+                    if (cg == 0) sXn[C + j] = mk[st][r] ? -1.f : s2;
                 } else {
                     float p[VEC];
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
-                    if ((TAIL && j >= n) || mk[r]) {
+                    if ((TAIL && j >= n) || mk[st][r]) {
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) p[e] = 0.f;
                     }
@@ -499,7 +551,7 @@ la_fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int r = 0; r < RV; ++r) {
                 const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
-                put_raw(sV, j, c4 * VEC, rv[r]);
+                put_raw(sV, j, c4 * VEC, rv[st][r]);
             }
         }
     };
@@ -727,30 +779,52 @@ la_fwd_kernel(const FwdArgs a)
         compute(buf, n, c * C, d.dscale, d.do_rescale, d.rescale, buf, tail_c);
     };
 
+    using S0 = std::integral_constant<int, 0>;
     if (c_beg < c_end) {
         Dec d;
         if (c_beg < c_full) {
             d = book(C);
-            stage(0, C, d.kw_l2, std::false_type{});
+            stage(S0{}, 0, C, d.kw_l2, std::false_type{});
         } else {
             d = book(n_tail);
-            stage(0, n_tail, d.kw_l2, std::true_type{});
+            stage(S0{}, 0, n_tail, d.kw_l2, std::true_type{});
         }
-        for (int64_t c = c_beg; c < c_full; ++c) {
-            const int buf = (int)((c - c_beg) & 1);
-            const bool next_full = c + 1 < c_full;
-            if (next_full) load_chunk(c + 1, std::false_type{});
-            finish(c, C, d, std::false_type{});
-            if (next_full) {
+        if constexpr (PF == 1) {
+            for (int64_t c = c_beg; c < c_full; ++c) {
+                const int buf = (int)((c - c_beg) & 1);
+                const bool next_full = c + 1 < c_full;
+                if (next_full) load_chunk(S0{}, c + 1, std::false_type{});
+                finish(c, C, d, std::false_type{});
+                if (next_full) {
+                    d = book(C);
+                    stage(S0{}, buf ^ 1, C, d.kw_l2, std::false_type{});
+                }
+            }
+        } else if (c_beg < c_full) {
+            // unrolled PF times so that every register set has a fixed
+            // name: sub-step s computes the chunk held by set s, refills
+            // the set with the chunk PF ahead, and stages the next chunk
+            // from set s + 1
+            int64_t c = c_beg;
+            auto sub = [&](auto s_c) LA_INLINE {
+                constexpr int st = decltype(s_c)::value;
+                const int buf = (int)((c - c_beg) & 1);
+                load_chunk(s_c, min(c + PF, c_full - 1), std::false_type{});
+                finish(c, C, d, std::false_type{});
+                if (c + 1 >= c_full) return true;
                 d = book(C);
-                stage(buf ^ 1, C, d.kw_l2, std::false_type{});
+                stage(std::integral_constant<int, (st + 1) % PF>{}, buf ^ 1, C, d.kw_l2, std::false_type{});
+                ++c;
+                return false;
+            };
+            while (!static_until<0, PF>(sub)) {
             }
         }
         if (ragged) {
             if (c_full > c_beg) {
-                load_chunk(c_full, std::true_type{});
+                load_chunk(S0{}, c_full, std::true_type{});
                 d = book(n_tail);
-                stage((int)((c_full - c_beg) & 1), n_tail, d.kw_l2, std::true_type{});
+                stage(S0{}, (int)((c_full - c_beg) & 1), n_tail, d.kw_l2, std::true_type{});
             }
             finish(c_full, n_tail, d, std::true_type{});
         }
@@ -789,6 +863,12 @@ la_fwd_kernel(const FwdArgs a)
     }
 }
 
+}  // namespace la
+
+#include "la_output.h"
+
+namespace la {
+
 template <class T, int PHI, int DK, int F, int DV>
 hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
 {
@@ -802,6 +882,8 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
     case MODE_LOCAL:
         return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL, false>, grid, block, stream, a);
     case MODE_CAUSAL:
+        if constexpr (sizeof(T) == 2 && (PHI == LA_PHI_ELU1 || PHI == LA_PHI_RELU) && DK == F)
+            return out_launch<PHI, F, DV>(a, stream);
         return o32 ? launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL, true>, grid, block, stream, a)
                    : launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL, false>, grid, block, stream, a);
     default:

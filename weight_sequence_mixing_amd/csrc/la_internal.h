@@ -42,7 +42,8 @@ struct FwdArgs {
     int32_t BH;       // batch * heads
     int32_t H;
     int32_t P;        // segments
-    int64_t cps;      // chunks per segment
+    int64_t cps;      // units of `chunk` tokens per segment
+    int32_t chunk;    // tokens per unit of cps: the planning chunk, a multiple of every kernel's own
     int32_t out_f32;  // 1: y is fp32, 0: y has the input type
     float eps;
     float qk_scale;

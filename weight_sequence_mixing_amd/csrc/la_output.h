@@ -1,0 +1,463 @@
+// la_output.h -- the causal output pass for bf16 inputs and the elementwise
+// feature maps (elu+1, ReLU), with the work of a chunk split by query rows.
+//
+// What is computed is the chunked form of la_forward.h ("Attention is also an
+// FFN", kwkr.cn/news/587576, sec. 4.1 notes and sec. 5.2: parallel inside a
+// chunk, carried between chunks; decay sec. 3.2; normaliser sec. 4.2).  For
+// a chunk of n tokens after the state (S, z), local positions i, j:
+//
+//   num_i, den_i = lambda^(i+1) phi(q_i)^T [S, z]
+//                + sum_{j<=i} lambda^(i-j) (phi(q_i).phi(k_j)) [v_j, 1]
+//   y_i          = num_i / (den_i + eps)
+//   S            <- lambda^n S + sum_j lambda^(n-1-j) phi(k_j) v_j^T   (z likewise)
+//
+// Work split.  A chunk is C = 64 tokens, four 16-row query blocks.  Each wave
+// owns one query block (with 8 waves, half of its output columns): it forms
+// that block's decayed score tiles against the key blocks at or before it,
+// its row sums, the inter-chunk product S^T phi(Q)^T and the intra-chunk
+// product V^T P^T, and stores its outputs.  No score tile is formed twice in
+// a workgroup unless two waves share a query block.  The fp32 state is split
+// over the waves by feature rows (wave w owns FBW 16-row blocks); each wave
+// adds the chunk's keys to its rows with the matrix cores and writes them,
+// rounded to bf16, into a shared LDS copy of S^T, which every wave reads as
+// the A operand of the next chunk's inter-chunk product.
+//
+// Layouts.  phi(Q), phi(K), the weighted phi(K) and V are staged in LDS as in
+// la_forward.h (TileL, swizzled 8-byte units).  S^T is [DV][F] bf16 with the
+// feature order inside each 32-wide block permuted so that the 8 k positions
+// K(g) a lane needs (la_device.h) are contiguous: one 16-byte read per
+// fragment; the 16-byte units are XOR-swizzled with (row & 7).  z is kept
+// the same way ([F] bf16, permuted), so its fragment is one 16-byte read too.
+//
+// Per chunk there are two barriers: one after the chunk is staged (tiles,
+// S^T and z of the previous chunk visible), one after every wave has read the
+// tiles and S^T; the state's new S^T and z and the next chunk's tiles are
+// written after the second.  The next chunk's q, k, v are loaded into
+// registers while the current one is computed.
+#pragma once
+
+#include <type_traits>
+
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+template <int F, int DV>
+struct OutCfg {
+    static constexpr int C = 64;
+    static constexpr int QB = C / 16;
+    static constexpr int FB = F / 16, DB = DV / 16, KB = F / 32, CB = C / 32;
+    // eight waves (two per SIMD) where the state has at least eight feature
+    // blocks; otherwise four
+    static constexpr int NW = FB >= 8 ? 8 : 4;
+    static constexpr int NT = NW * 64;
+    static constexpr int QW = NW / QB;   // waves per query block
+    static constexpr int DBQ = DB / QW;  // output column tiles per wave
+    static constexpr int FBW = FB / NW;  // state feature blocks per wave
+    static constexpr int VEC = 8;        // bf16 per 16-byte vector
+    static constexpr int VPRQ = F / VEC, VPRV = DV / VEC;
+    static constexpr int RQ = C * VPRQ / NT, RV = C * VPRV / NT;
+    static constexpr int TQ = C * F, TV = C * DV;  // elements of a tile
+    static constexpr size_t OFF_Q = 0;
+    static constexpr size_t OFF_K = OFF_Q + size_t(TQ) * 2;
+    static constexpr size_t OFF_KW = OFF_K + size_t(TQ) * 2;
+    static constexpr size_t OFF_V = OFF_KW + size_t(TQ) * 2;
+    static constexpr size_t OFF_ST = OFF_V + size_t(TV) * 2;
+    static constexpr size_t OFF_Z = OFF_ST + size_t(DV) * F * 2;
+    static constexpr size_t TOTAL = OFF_Z + size_t(F) * 2;
+    static_assert(F % 64 == 0 && DV % 64 == 0, "head sizes");
+    static_assert(FBW >= 1 && FB % NW == 0 && NW % QB == 0 && DB % QW == 0, "wave split");
+    static_assert(RQ >= 1 && RV >= 1 && (C * VPRQ) % NT == 0 && (C * VPRV) % NT == 0, "loads per thread");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
+// Element offset in S^T ([DV][F] bf16) of 16-byte unit u of row r.
+template <int F>
+__device__ __forceinline__ int st_off(int r, int u)
+{
+    return r * F + ((u ^ (r & 7)) << 3);
+}
+
+template <int PHI, int F, int DV, bool OUTF32>
+__global__ void __launch_bounds__((OutCfg<F, DV>::NT), 2)
+la_out_kernel(const FwdArgs a)
+{
+    using Cfg = OutCfg<F, DV>;
+    using T = bf16;
+    constexpr int C = Cfg::C, NT = Cfg::NT, NW = Cfg::NW, QW = Cfg::QW, DBQ = Cfg::DBQ, FBW = Cfg::FBW;
+    constexpr int KB = Cfg::KB, CB = Cfg::CB, DB = Cfg::DB, VEC = Cfg::VEC;
+    constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
+    constexpr int DK = F;
+    using TF = TileL<T, F>;
+    using TVL = TileL<T, DV>;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    T* const sQ = (T*)(smem + Cfg::OFF_Q);
+    T* const sK = (T*)(smem + Cfg::OFF_K);
+    T* const sKw0 = (T*)(smem + Cfg::OFF_KW);
+    T* const sV = (T*)(smem + Cfg::OFF_V);
+    T* const sST = (T*)(smem + Cfg::OFF_ST);
+    T* const sZ = (T*)(smem + Cfg::OFF_Z);
+
+    // the wave index as a scalar: every branch on the query block below is
+    // uniform over the wave
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+    // query block of this wave; the two waves of a SIMD (w, w + 4) take
+    // blocks b and 3 - b, so that every SIMD forms the same number of score
+    // tiles; with two waves per block, w < 4 takes the first half of the
+    // output columns
+    const int ib = (wave < 4) ? wave : 3 - (wave - 4);
+    const int dq0 = (QW == 2 && wave >= 4) ? DBQ : 0;
+
+    int seg = blockIdx.x, bh = blockIdx.y;
+    bool spare = false;
+    if (a.cu_seqlens) {
+        const int it = a.items[blockIdx.x];
+        spare = it < 0;
+        seg = spare ? 0 : it % a.P;
+        bh = (spare ? 0 : it / a.P) * a.H + (int)blockIdx.y;
+    }
+    const int h = bh % a.H;
+    const float l2l = a.lam.log2lam[h];
+    const bool decay = l2l != 0.f;
+    int64_t row0 = (int64_t)bh * a.N + a.n0, n_len = a.n_len;
+    if (a.cu_seqlens) {
+        int64_t s0, s1;
+        varlen_range(a.cu_seqlens, bh / a.H, a.N, &s0, &s1);
+        row0 = (int64_t)h * a.N + s0;
+        n_len = s1 - s0;
+    }
+    // segments of cps units of a.chunk tokens (a multiple of C)
+    const int64_t cps = a.cps * (a.chunk / C);
+    const int64_t NC = spare ? 0 : (n_len + C - 1) / C;
+    const int64_t c_beg = (int64_t)seg * cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + cps);
+    if (c_beg >= c_end && (!a.S_dst || spare)) return;
+    const T* qg = (const T*)a.q + row0 * DK;
+    const T* kg = (const T*)a.k + row0 * DK;
+    const T* vg = (const T*)a.v + row0 * DV;
+    const uint8_t* kp = a.kpm ? a.kpm + (int64_t)(bh / a.H) * a.kpm_stride + a.n0 : nullptr;
+    const Frag<T> ones = frag_ones<T>();
+
+    // decay tables of this lane: score element (i = 16 ib + l16, j = 16 jb +
+    // 4 g + r) is weighted by lambda^(i-j): m0 on the diagonal block (zero
+    // above the diagonal, by selection so that a non-finite key cannot reach
+    // an earlier query through a zero weight), m1 * lambda^(16 (ib-jb-1))
+    // below it
+    float m0[4], m1[4];
+    bool above[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int e = l16 - 4 * g - r;
+        above[r] = e < 0;
+        m0[r] = e < 0 ? 0.f : (decay ? lam_pow(l2l, e) : 1.f);
+        m1[r] = decay ? lam_pow(l2l, 16 + e) : 1.f;
+    }
+    const float lq = decay ? lam_pow(l2l, 16 * ib + l16 + 1) : 1.f;  // lambda^(i+1)
+
+    // ---- loads of one chunk into registers (as la_forward.h: a ragged last
+    // chunk re-reads its last row and zeroes the rows past its end)
+    const bool ragged = c_end > c_beg && c_end * C > n_len;
+    const int64_t c_full = ragged ? c_end - 1 : c_end;
+    const int n_tail = ragged ? (int)(n_len - c_full * C) : C;
+    uint4 rq[RQ], rk[RQ], rv[RV];
+    int mk[RQ];
+    auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) LA_INLINE {
+        constexpr bool TAIL = decltype(tail_c)::value;
+        const uint4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int r = 0; r < nreg; ++r) {
+            const int idx = tid + r * NT, j = idx / vpr, c4 = idx % vpr;
+            if constexpr (!TAIL) {
+                dst[r] = *(const uint4*)(base + j * ld + c4 * VEC);
+            } else {
+                const uint4 val = *(const uint4*)(base + min(j, n - 1) * ld + c4 * VEC);
+                dst[r] = (j < n) ? val : zero;
+            }
+        }
+    };
+    auto load_chunk = [&](int64_t c, auto tail_c) LA_INLINE {
+        const int64_t t0 = c * C;
+        const int n = decltype(tail_c)::value ? n_tail : C;
+        load_rows(rq, qg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
+        load_rows(rk, kg + t0 * DK, VPRQ, DK, RQ, n, tail_c);
+        load_rows(rv, vg + t0 * DV, VPRV, DV, RV, n, tail_c);
+#pragma unroll
+        for (int r = 0; r < RQ; ++r) {
+            const int j = (tid + r * NT) / VPRQ;
+            mk[r] = kp ? (int)kp[t0 + (decltype(tail_c)::value ? min(j, n - 1) : j)] : 0;
+        }
+    };
+    if (c_beg < c_full) load_chunk(c_beg, std::false_type{});
+    else if (c_beg < c_end) load_chunk(c_beg, std::true_type{});
+
+    // ---- this wave's rows of the state: accS[u][t] holds S[16 fb + 4 g + r]
+    // [16 t + l16] with fb = FBW * wave + u; accZ[u] holds z[16 fb + 4 g + r]
+    // in every column
+    f32x4 accS[FBW][DB], accZ[FBW];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < FBW; ++u) {
+        accZ[u] = zero4;
+#pragma unroll
+        for (int t = 0; t < DB; ++t) accS[u][t] = zero4;
+    }
+    if (a.S_src) {
+        const float* Sb = a.S_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_stride;
+        const float* zb = a.z_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_zstride;
+#pragma unroll
+        for (int u = 0; u < FBW; ++u) {
+            const int f0 = 16 * (FBW * wave + u) + 4 * g;
+#pragma unroll
+            for (int t = 0; t < DB; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accS[u][t][r] = Sb[(int64_t)(f0 + r) * DV + 16 * t + l16];
+            accZ[u] = *(const f32x4*)(zb + f0);
+        }
+    }
+    // this wave's rows into the shared S^T and z (bf16, permuted features)
+    auto publish = [&]() LA_INLINE {
+#pragma unroll
+        for (int u = 0; u < FBW; ++u) {
+            const int fb = FBW * wave + u;
+            const int unit = 4 * (fb >> 1) + g, half = (fb & 1) * 4;
+#pragma unroll
+            for (int t = 0; t < DB; ++t) {
+                const int r = 16 * t + l16;
+                st4(sST + st_off<F>(r, unit) + half, accS[u][t][0], accS[u][t][1], accS[u][t][2], accS[u][t][3]);
+            }
+            if (l16 == 0) st4(sZ + unit * 8 + half, accZ[u][0], accZ[u][1], accZ[u][2], accZ[u][3]);
+        }
+    };
+    publish();
+    float log2D = 0.f;  // the true state is 2^log2D times the accumulators
+
+    // ---- staging of one chunk from the registers: phi(q), phi(k), the
+    // lambda-weighted phi(k) (decay only) and v.  kw_l2 as in la_forward.h.
+    auto key_weight = [&](int k, float kw_l2) LA_INLINE {
+        return k == 0 ? __builtin_amdgcn_exp2f(-kw_l2) : __builtin_amdgcn_exp2f((float)k * l2l - kw_l2);
+    };
+    auto put_feat = [&](T* tile, int row, int col, const float* p) LA_INLINE {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) st4(tile + TF::off(row, col + e), p[e], p[e + 1], p[e + 2], p[e + 3]);
+    };
+    auto stage = [&](int n, float kw_l2, auto tail_c) LA_INLINE {
+        constexpr bool TAIL = decltype(tail_c)::value;
+        const int cg = tid % VPRQ;
+#pragma unroll
+        for (int r = 0; r < RQ; ++r) {
+            const int j = (tid + r * NT) / VPRQ;
+            float x[VEC], p[VEC];
+            unpack16(rq[r], x, (const T*)nullptr);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
+            put_feat(sQ, j, cg * VEC, p);
+        }
+#pragma unroll
+        for (int r = 0; r < RQ; ++r) {
+            const int j = (tid + r * NT) / VPRQ;
+            float x[VEC], p[VEC];
+            unpack16(rk[r], x, (const T*)nullptr);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
+            if ((TAIL && j >= n) || mk[r]) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) p[e] = 0.f;
+            }
+            put_feat(sK, j, cg * VEC, p);
+            if (decay) {
+                const float w = (TAIL && j >= n) ? 0.f : key_weight(n - 1 - j, kw_l2);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) p[e] *= w;
+                put_feat(sKw0, j, cg * VEC, p);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+            const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
+            const uint4 u = rv[r];
+            *(uint2*)(sV + TVL::off(j, c4 * VEC)) = uint2{u.x, u.y};
+            *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
+        }
+    };
+
+    // ---- outputs of this wave's query block and the update of its state
+    // rows, for one staged chunk.  dscale: 2^log2D of the state in S^T;
+    // rescale: factor on the accumulators before the chunk's keys are added.
+    auto compute = [&](int n, int64_t t0, float dscale, bool do_rescale, float rescale, auto tail_c) LA_INLINE {
+        constexpr bool TAIL = decltype(tail_c)::value;
+        const T* const sKw = decay ? sKw0 : sK;
+        const int i = 16 * ib + l16;
+        Frag<T> qf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F>(sQ, i, kb, g);
+        // phi(q_i).z (every row holds it)
+        f32x4 dq = zero4;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            Frag<T> zf;
+            zf.v = *(const bf16x8*)(sZ + (4 * kb + g) * 8);
+            mma(dq, zf, qf[kb]);
+        }
+        // scores of this query block against all four key blocks, as P^T;
+        // blocks after the query block (jb > ib) and keys above the diagonal
+        // are set to zero by selection.  No branch depends on the wave.
+        f32x4 pt[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            pt[jb] = zero4;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
+            // lambda^(16 (ib-jb-1)) for blocks before the query block
+            const float dj = lam_pow(l2l, max(16 * (ib - jb - 1), 0));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float wgt = (jb == ib) ? m0[r] : m1[r] * dj;
+                const bool zero = jb > ib || (jb == ib && above[r]);
+                pt[jb][r] = zero ? 0.f : pt[jb][r] * wgt;
+            }
+        }
+        Frag<T> pf[CB];
+        f32x4 rs = zero4;
+#pragma unroll
+        for (int kb = 0; kb < CB; ++kb) {
+            pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
+            mma(rs, ones, pf[kb]);
+        }
+        const float lqd = lq * dscale;
+        const float inv = fast_rcp(rs[0] + lqd * dq[0] + a.eps);
+        const float sc = lqd * inv;
+        if (do_rescale) {
+#pragma unroll
+            for (int u = 0; u < FBW; ++u) {
+                accZ[u] *= rescale;
+#pragma unroll
+                for (int t = 0; t < DB; ++t) accS[u][t] *= rescale;
+            }
+        }
+        // weighted key fragments of this wave's feature blocks (A operands of
+        // the state update)
+        Frag<T> kwf[FBW][CB];
+#pragma unroll
+        for (int u = 0; u < FBW; ++u)
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) kwf[u][kb] = ColRead<T, F>::get(sKw, 32 * kb, 16 * (FBW * wave + u), lane);
+        // outputs of this wave's column tiles t = dq0 .. dq0 + DBQ - 1:
+        // O^T = S^T phi(Q)^T (scaled) + V^T P^T
+        const int64_t yrow = row0 + t0 + i;
+#pragma unroll
+        for (int tq = 0; tq < DBQ; ++tq) {
+            const int t = dq0 + tq;
+            f32x4 o = zero4, oi = zero4;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                Frag<T> sf;
+                sf.v = *(const bf16x8*)(sST + st_off<F>(16 * t + l16, 4 * kb + g));
+                mma(o, sf, qf[kb]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) mma(oi, ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane), pf[kb]);
+            const f32x4 y = o * sc + oi * inv;
+            if (!TAIL || i < n) {
+                const int64_t yo = yrow * DV + 16 * t + 4 * g;
+                if constexpr (OUTF32) st4((float*)a.y + yo, y[0], y[1], y[2], y[3]);
+                else st4((T*)a.y + yo, y[0], y[1], y[2], y[3]);
+            }
+        }
+        // state update of this wave's rows: S^ += (w phi(K))^T V
+#pragma unroll
+        for (int t = 0; t < DB; ++t) {
+            Frag<T> vf[CB];
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) vf[kb] = ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane);
+#pragma unroll
+            for (int u = 0; u < FBW; ++u)
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) mma(accS[u][t], kwf[u][kb], vf[kb]);
+        }
+#pragma unroll
+        for (int u = 0; u < FBW; ++u)
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) mma(accZ[u], kwf[u][kb], ones);
+    };
+
+    // decay bookkeeping, in chunk order (as la_forward.h)
+    struct Dec { float dscale, rescale, kw_l2; bool do_rescale; };
+    auto book = [&](int n) LA_INLINE {
+        Dec d = {decay ? exp2f(log2D) : 1.f, 1.f, 0.f, false};
+        if (decay) {
+            const float cand = log2D + (float)n * l2l;
+            if (cand >= kLog2MinScale) {
+                d.kw_l2 = cand;
+                log2D = cand;
+            } else {
+                d.do_rescale = true;
+                d.rescale = exp2f(cand);
+                log2D = 0.f;
+            }
+        }
+        return d;
+    };
+
+    if (c_beg < c_end) {
+        Dec d;
+        if (c_beg < c_full) {
+            d = book(C);
+            stage(C, d.kw_l2, std::false_type{});
+        } else {
+            d = book(n_tail);
+            stage(n_tail, d.kw_l2, std::true_type{});
+        }
+        for (int64_t c = c_beg; c < c_full; ++c) {
+            const bool next_full = c + 1 < c_full;
+            __syncthreads();
+            if (next_full) load_chunk(c + 1, std::false_type{});
+            compute(C, c * C, d.dscale, d.do_rescale, d.rescale, std::false_type{});
+            __syncthreads();
+            publish();
+            if (next_full) {
+                d = book(C);
+                stage(C, d.kw_l2, std::false_type{});
+            }
+        }
+        if (ragged) {
+            if (c_full > c_beg) {
+                load_chunk(c_full, std::true_type{});
+                d = book(n_tail);
+                stage(n_tail, d.kw_l2, std::true_type{});
+            }
+            __syncthreads();
+            compute(n_tail, c_full * C, d.dscale, d.do_rescale, d.rescale, std::true_type{});
+        }
+    }
+
+    // ---- final state (true scale), this wave's rows
+    if (a.S_dst) {
+        float* Sd = a.S_dst + (int64_t)bh * a.dst_stride;
+        float* zd = a.z_dst + (int64_t)bh * a.dst_zstride;
+        const float ds = decay ? exp2f(log2D) : 1.f;
+#pragma unroll
+        for (int u = 0; u < FBW; ++u) {
+            const int f0 = 16 * (FBW * wave + u) + 4 * g;
+#pragma unroll
+            for (int t = 0; t < DB; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sd[(int64_t)(f0 + r) * DV + 16 * t + l16] = ds * accS[u][t][r];
+            if (l16 == 0) *(f32x4*)(zd + f0) = accZ[u] * ds;
+        }
+    }
+}
+
+template <int PHI, int F, int DV>
+hipError_t out_launch(const FwdArgs& a, hipStream_t stream)
+{
+    using Cfg = OutCfg<F, DV>;
+    if (a.chunk % Cfg::C != 0) return hipErrorInvalidValue;  // segments must be whole chunks
+    const dim3 grid(a.cu_seqlens ? (unsigned)a.G : (unsigned)a.P, a.cu_seqlens ? (unsigned)a.H : (unsigned)a.BH),
+        block(Cfg::NT);
+    if (a.out_f32) return launch_kernel(la_out_kernel<PHI, F, DV, true>, grid, block, stream, a);
+    return launch_kernel(la_out_kernel<PHI, F, DV, false>, grid, block, stream, a);
+}
+
+}  // namespace la
