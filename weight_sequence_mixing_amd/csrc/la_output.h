@@ -17,8 +17,10 @@
 // its row sums, the inter-chunk product S^T phi(Q)^T and the intra-chunk
 // product V^T P^T, and stores its outputs.  No score tile is formed twice in
 // a workgroup unless two waves share a query block.  The fp32 state is split
-// over the waves by feature rows (wave w owns FBW 16-row blocks); each wave
-// adds the chunk's keys to its rows with the matrix cores and writes them,
+// over the waves in blocks of FBW feature blocks by the wave's own output
+// columns, so that the value fragments of a column tile serve both the
+// intra-chunk product and the state update; each wave adds the chunk's keys
+// to its part with the matrix cores and writes it,
 // rounded to bf16, into a shared LDS copy of S^T, which every wave reads as
 // the A operand of the next chunk's inter-chunk product.
 //
@@ -54,7 +56,9 @@ struct OutCfg {
     static constexpr int NT = NW * 64;
     static constexpr int QW = NW / QB;   // waves per query block
     static constexpr int DBQ = DB / QW;  // output column tiles per wave
-    static constexpr int FBW = FB / NW;  // state feature blocks per wave
+    // state tiles per wave: FBW feature blocks of the wave's own DBQ output
+    // column tiles (the QB waves of one column half split the feature rows)
+    static constexpr int FBW = FB / QB;
     static constexpr int VEC = 8;        // bf16 per 16-byte vector
     static constexpr int VPRQ = F / VEC, VPRV = DV / VEC;
     static constexpr int RQ = C * VPRQ / NT, RV = C * VPRV / NT;
@@ -67,7 +71,7 @@ struct OutCfg {
     static constexpr size_t OFF_Z = OFF_ST + size_t(DV) * F * 2;
     static constexpr size_t TOTAL = OFF_Z + size_t(F) * 2;
     static_assert(F % 64 == 0 && DV % 64 == 0, "head sizes");
-    static_assert(FBW >= 1 && FB % NW == 0 && NW % QB == 0 && DB % QW == 0, "wave split");
+    static_assert(FBW >= 1 && FB % QB == 0 && NW % QB == 0 && DB % QW == 0, "wave split");
     static_assert(RQ >= 1 && RV >= 1 && (C * VPRQ) % NT == 0 && (C * VPRV) % NT == 0, "loads per thread");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -192,27 +196,30 @@ la_out_kernel(const FwdArgs a)
     if (c_beg < c_full) load_chunk(c_beg, std::false_type{});
     else if (c_beg < c_end) load_chunk(c_beg, std::true_type{});
 
-    // ---- this wave's rows of the state: accS[u][t] holds S[16 fb + 4 g + r]
-    // [16 t + l16] with fb = FBW * wave + u; accZ[u] holds z[16 fb + 4 g + r]
-    // in every column
-    f32x4 accS[FBW][DB], accZ[FBW];
+    // ---- this wave's part of the state: accS[u][c] holds S[16 fb + 4 g + r]
+    // [16 (dq0 + c) + l16] with fb = FBW * qw + u (qw: the wave's index among
+    // the QB waves of its column half); accZ[u] holds z[16 fb + 4 g + r] in
+    // every column (the first column half publishes and stores z)
+    const int qw = wave % Cfg::QB;
+    const bool zowner = dq0 == 0;
+    f32x4 accS[FBW][DBQ], accZ[FBW];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < FBW; ++u) {
         accZ[u] = zero4;
 #pragma unroll
-        for (int t = 0; t < DB; ++t) accS[u][t] = zero4;
+        for (int c = 0; c < DBQ; ++c) accS[u][c] = zero4;
     }
     if (a.S_src) {
         const float* Sb = a.S_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_stride;
         const float* zb = a.z_src + (int64_t)seg * a.src_seg_stride + (int64_t)bh * a.src_zstride;
 #pragma unroll
         for (int u = 0; u < FBW; ++u) {
-            const int f0 = 16 * (FBW * wave + u) + 4 * g;
+            const int f0 = 16 * (FBW * qw + u) + 4 * g;
 #pragma unroll
-            for (int t = 0; t < DB; ++t)
+            for (int c = 0; c < DBQ; ++c)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) accS[u][t][r] = Sb[(int64_t)(f0 + r) * DV + 16 * t + l16];
+                for (int r = 0; r < 4; ++r) accS[u][c][r] = Sb[(int64_t)(f0 + r) * DV + 16 * (dq0 + c) + l16];
             accZ[u] = *(const f32x4*)(zb + f0);
         }
     }
@@ -220,14 +227,14 @@ la_out_kernel(const FwdArgs a)
     auto publish = [&]() LA_INLINE {
 #pragma unroll
         for (int u = 0; u < FBW; ++u) {
-            const int fb = FBW * wave + u;
+            const int fb = FBW * qw + u;
             const int unit = 4 * (fb >> 1) + g, half = (fb & 1) * 4;
 #pragma unroll
-            for (int t = 0; t < DB; ++t) {
-                const int r = 16 * t + l16;
-                st4(sST + st_off<F>(r, unit) + half, accS[u][t][0], accS[u][t][1], accS[u][t][2], accS[u][t][3]);
+            for (int c = 0; c < DBQ; ++c) {
+                const int r = 16 * (dq0 + c) + l16;
+                st4(sST + st_off<F>(r, unit) + half, accS[u][c][0], accS[u][c][1], accS[u][c][2], accS[u][c][3]);
             }
-            if (l16 == 0) st4(sZ + unit * 8 + half, accZ[u][0], accZ[u][1], accZ[u][2], accZ[u][3]);
+            if (zowner && l16 == 0) st4(sZ + unit * 8 + half, accZ[u][0], accZ[u][1], accZ[u][2], accZ[u][3]);
         }
     };
     publish();
@@ -333,7 +340,7 @@ la_out_kernel(const FwdArgs a)
             for (int u = 0; u < FBW; ++u) {
                 accZ[u] *= rescale;
 #pragma unroll
-                for (int t = 0; t < DB; ++t) accS[u][t] *= rescale;
+                for (int c = 0; c < DBQ; ++c) accS[u][c] *= rescale;
             }
         }
         // weighted key fragments of this wave's feature blocks (A operands of
@@ -342,13 +349,18 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
         for (int u = 0; u < FBW; ++u)
 #pragma unroll
-            for (int kb = 0; kb < CB; ++kb) kwf[u][kb] = ColRead<T, F>::get(sKw, 32 * kb, 16 * (FBW * wave + u), lane);
+            for (int kb = 0; kb < CB; ++kb) kwf[u][kb] = ColRead<T, F>::get(sKw, 32 * kb, 16 * (FBW * qw + u), lane);
         // outputs of this wave's column tiles t = dq0 .. dq0 + DBQ - 1:
         // O^T = S^T phi(Q)^T (scaled) + V^T P^T
         const int64_t yrow = row0 + t0 + i;
 #pragma unroll
         for (int tq = 0; tq < DBQ; ++tq) {
             const int t = dq0 + tq;
+            // value fragments of column tile t: A operands of V^T P^T and B
+            // operands of this wave's state update
+            Frag<T> vf[CB];
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) vf[kb] = ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane);
             f32x4 o = zero4, oi = zero4;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -357,24 +369,18 @@ la_out_kernel(const FwdArgs a)
                 mma(o, sf, qf[kb]);
             }
 #pragma unroll
-            for (int kb = 0; kb < CB; ++kb) mma(oi, ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane), pf[kb]);
+            for (int kb = 0; kb < CB; ++kb) mma(oi, vf[kb], pf[kb]);
             const f32x4 y = o * sc + oi * inv;
             if (!TAIL || i < n) {
                 const int64_t yo = yrow * DV + 16 * t + 4 * g;
                 if constexpr (OUTF32) st4((float*)a.y + yo, y[0], y[1], y[2], y[3]);
                 else st4((T*)a.y + yo, y[0], y[1], y[2], y[3]);
             }
-        }
-        // state update of this wave's rows: S^ += (w phi(K))^T V
-#pragma unroll
-        for (int t = 0; t < DB; ++t) {
-            Frag<T> vf[CB];
-#pragma unroll
-            for (int kb = 0; kb < CB; ++kb) vf[kb] = ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane);
+            // state update of this wave's part: S^ += (w phi(K))^T V
 #pragma unroll
             for (int u = 0; u < FBW; ++u)
 #pragma unroll
-                for (int kb = 0; kb < CB; ++kb) mma(accS[u][t], kwf[u][kb], vf[kb]);
+                for (int kb = 0; kb < CB; ++kb) mma(accS[u][tq], kwf[u][kb], vf[kb]);
         }
 #pragma unroll
         for (int u = 0; u < FBW; ++u)
@@ -439,12 +445,12 @@ la_out_kernel(const FwdArgs a)
         const float ds = decay ? exp2f(log2D) : 1.f;
 #pragma unroll
         for (int u = 0; u < FBW; ++u) {
-            const int f0 = 16 * (FBW * wave + u) + 4 * g;
+            const int f0 = 16 * (FBW * qw + u) + 4 * g;
 #pragma unroll
-            for (int t = 0; t < DB; ++t)
+            for (int c = 0; c < DBQ; ++c)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sd[(int64_t)(f0 + r) * DV + 16 * t + l16] = ds * accS[u][t][r];
-            if (l16 == 0) *(f32x4*)(zd + f0) = accZ[u] * ds;
+                for (int r = 0; r < 4; ++r) Sd[(int64_t)(f0 + r) * DV + 16 * (dq0 + c) + l16] = ds * accS[u][c][r];
+            if (zowner && l16 == 0) *(f32x4*)(zd + f0) = accZ[u] * ds;
         }
     }
 }
