@@ -70,12 +70,19 @@ constexpr int chunk_len(int F) {
     return 32;
 }
 
+// The causal output pass runs la_out_kernel (64-token chunks) for bf16 inputs
+// with elu+1, ReLU or random features.
+template <class T, int PHI>
+constexpr bool query_split_output() {
+    return sizeof(T) == 2 && (PHI == LA_PHI_ELU1 || PHI == LA_PHI_RELU || PHI == LA_PHI_TRIG_RF);
+}
+
 // Tokens per planning chunk (the unit in which a call cuts segments): 64 where
-// the causal output pass is la_out_kernel (bf16 inputs, elementwise maps),
-// whose chunks are 64 tokens; the kernel's own chunk length elsewhere.
+// the causal output pass is la_out_kernel; the kernel's own chunk length
+// elsewhere.
 template <class T, int PHI>
 constexpr int plan_chunk(int F) {
-    return (sizeof(T) == 2 && (PHI == LA_PHI_ELU1 || PHI == LA_PHI_RELU)) ? 64 : chunk_len<T, PHI>(F);
+    return query_split_output<T, PHI>() ? 64 : chunk_len<T, PHI>(F);
 }
 
 // log2 of the smallest pending decay factor before the state is rescaled
@@ -882,8 +889,8 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
     case MODE_LOCAL:
         return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL, false>, grid, block, stream, a);
     case MODE_CAUSAL:
-        if constexpr (sizeof(T) == 2 && (PHI == LA_PHI_ELU1 || PHI == LA_PHI_RELU) && DK == F)
-            return out_launch<PHI, F, DV>(a, stream);
+        if constexpr (query_split_output<T, PHI>() && OutCfg<PHI, DK, F, DV>::FITS)
+            return out_launch<PHI, DK, F, DV>(a, stream);
         return o32 ? launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL, true>, grid, block, stream, a)
                    : launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_CAUSAL, false>, grid, block, stream, a);
     default:

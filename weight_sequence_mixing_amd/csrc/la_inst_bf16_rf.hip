@@ -4,7 +4,7 @@
 
 namespace la {
 #define LA_ENTRY(T, TCODE, PHI, DK, F, DV) \
-    {TCODE, PHI, DK, F, DV, chunk_len<T, PHI>(F), &fwd_launch<T, PHI, DK, F, DV>, &dec_launch<T, PHI, DK, F, DV>}
+    {TCODE, PHI, DK, F, DV, plan_chunk<T, PHI>(F), &fwd_launch<T, PHI, DK, F, DV>, &dec_launch<T, PHI, DK, F, DV>}
 
 KernelEntry kEntriesBf16Rf[] = {
     LA_ENTRY(bf16, LA_BF16, LA_PHI_TRIG_RF, 64, 64, 64),

@@ -1,5 +1,6 @@
-// la_output.h -- the causal output pass for bf16 inputs and the elementwise
-// feature maps (elu+1, ReLU), with the work of a chunk split by query rows.
+// la_output.h -- the causal output pass for bf16 inputs (elu+1, ReLU and the
+// trigonometric random features), with the work of a chunk split by query
+// rows.
 //
 // What is computed is the chunked form of la_forward.h ("Attention is also an
 // FFN", kwkr.cn/news/587576, sec. 4.1 notes and sec. 5.2: parallel inside a
@@ -13,16 +14,30 @@
 //
 // Work split.  A chunk is C = 64 tokens, four 16-row query blocks.  Each wave
 // owns one query block (with 8 waves, half of its output columns): it forms
-// that block's decayed score tiles against the key blocks at or before it,
-// its row sums, the inter-chunk product S^T phi(Q)^T and the intra-chunk
-// product V^T P^T, and stores its outputs.  No score tile is formed twice in
-// a workgroup unless two waves share a query block.  The fp32 state is split
-// over the waves in blocks of FBW feature blocks by the wave's own output
-// columns, so that the value fragments of a column tile serve both the
-// intra-chunk product and the state update; each wave adds the chunk's keys
-// to its part with the matrix cores and writes it,
-// rounded to bf16, into a shared LDS copy of S^T, which every wave reads as
-// the A operand of the next chunk's inter-chunk product.
+// that block's decayed score tiles, its row sums, the inter-chunk product
+// S^T phi(Q)^T and the intra-chunk product V^T P^T, and stores its outputs.
+// The fp32 state is split over the waves in blocks of FBW feature blocks by
+// the wave's own output columns, so that the value fragments of a column tile
+// serve both the intra-chunk product and the state update; each wave adds the
+// chunk's keys to its part with the matrix cores and writes it, rounded to
+// bf16, into a shared LDS copy of S^T, which every wave reads as the A
+// operand of the next chunk's inter-chunk product.
+//
+// Random features ("From standard attention to linear attention", sec. 4.2:
+// phi(x) = c(x) [cos(omega x'), sin(omega x')] / sqrt(m), x' = qk_scale x).
+// The raw q and k rows of a chunk are staged in LDS with the prefactor of
+// each token; then every wave computes a share of the feature tiles on the
+// matrix cores (omega x^T from omega's row blocks, kept in LDS as bf16 high
+// and low parts, angles in revolutions for the hardware sine and cosine)
+// and writes them into the same tiles the elementwise maps use.  Half of the
+// waves take the queries, half the keys; a wave keeps RB row blocks of omega.
+//
+// Decay weights of the state update.  The elementwise maps stage the key
+// features a second time with the weight lambda^(n-1-j) (rescaled, see book);
+// the random features, whose feature rows are wider than the value rows, put
+// the weight on the value fragments instead, in registers (and the weights
+// themselves form the B operand of the z update), which halves the LDS tiles
+// of the keys.
 //
 // Layouts.  phi(Q), phi(K), the weighted phi(K) and V are staged in LDS as in
 // la_forward.h (TileL, swizzled 8-byte units).  S^T is [DV][F] bf16 with the
@@ -34,8 +49,9 @@
 // Per chunk there are two barriers: one after the chunk is staged (tiles,
 // S^T and z of the previous chunk visible), one after every wave has read the
 // tiles and S^T; the state's new S^T and z and the next chunk's tiles are
-// written after the second.  The next chunk's q, k, v are loaded into
-// registers while the current one is computed.
+// written after the second (for random features, the next chunk's raw rows
+// before it, as no wave reads them while computing).  The next chunk's q, k,
+// v are loaded into registers while the current one is computed.
 #pragma once
 
 #include <type_traits>
@@ -45,8 +61,11 @@
 
 namespace la {
 
-template <int F, int DV>
+template <int PHI, int DK, int F, int DV>
 struct OutCfg {
+    static constexpr bool RF = PHI == LA_PHI_TRIG_RF;
+    static constexpr bool VW = RF;       // decay weights on the values (else on the key features)
+    static constexpr int M = RF ? F / 2 : 0;
     static constexpr int C = 64;
     static constexpr int QB = C / 16;
     static constexpr int FB = F / 16, DB = DV / 16, KB = F / 32, CB = C / 32;
@@ -60,20 +79,36 @@ struct OutCfg {
     // column tiles (the QB waves of one column half split the feature rows)
     static constexpr int FBW = FB / QB;
     static constexpr int VEC = 8;        // bf16 per 16-byte vector
-    static constexpr int VPRQ = F / VEC, VPRV = DV / VEC;
+    static constexpr int VPRQ = DK / VEC, VPRV = DV / VEC;
     static constexpr int RQ = C * VPRQ / NT, RV = C * VPRV / NT;
+    // random features: raw rows of XLD elements (8 bytes of padding, so that
+    // the 16 rows of a fragment read start in different banks); omega row
+    // blocks per wave, each wave covering one of the two token matrices
+    static constexpr int XLD = DK + 4, KX = DK / 32;
+    static constexpr int RB = RF ? 2 * (M / 16) / NW : 0;
     static constexpr int TQ = C * F, TV = C * DV;  // elements of a tile
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t OFF_K = OFF_Q + size_t(TQ) * 2;
     static constexpr size_t OFF_KW = OFF_K + size_t(TQ) * 2;
-    static constexpr size_t OFF_V = OFF_KW + size_t(TQ) * 2;
+    static constexpr size_t OFF_V = OFF_KW + (VW ? 0 : size_t(TQ) * 2);
     static constexpr size_t OFF_ST = OFF_V + size_t(TV) * 2;
     static constexpr size_t OFF_Z = OFF_ST + size_t(DV) * F * 2;
-    static constexpr size_t TOTAL = OFF_Z + size_t(F) * 2;
-    static_assert(F % 64 == 0 && DV % 64 == 0, "head sizes");
+    static constexpr size_t OFF_X = OFF_Z + size_t(F) * 2;
+    static constexpr size_t OFF_CF = OFF_X + (RF ? size_t(2) * C * XLD * 2 : 0);
+    // omega's operand fragments: [row block][k block][high, low][lane], 16 bytes
+    static constexpr size_t OFF_OM = OFF_CF + (RF ? size_t(2) * C * 4 : 0);
+    static constexpr size_t OFF_W = OFF_OM + (RF ? size_t(M / 16) * KX * 2 * 64 * 16 : 0);
+    static constexpr size_t TOTAL = OFF_W + (VW ? size_t(C) * 4 : 0);
+    static_assert(F % 64 == 0 && DV % 64 == 0 && DK % 64 == 0, "head sizes");
+    static_assert(RF || DK == F, "elementwise maps keep the width");
     static_assert(FBW >= 1 && FB % QB == 0 && NW % QB == 0 && DB % QW == 0, "wave split");
     static_assert(RQ >= 1 && RV >= 1 && (C * VPRQ) % NT == 0 && (C * VPRV) % NT == 0, "loads per thread");
-    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(!RF || (RB >= 1 && RB * NW == 2 * (M / 16)), "feature tiles must split over the waves");
+    static_assert(OFF_X % 16 == 0 && OFF_CF % 16 == 0 && OFF_OM % 16 == 0 && OFF_W % 16 == 0, "alignment");
+    // the LDS of one workgroup (not met by m = 128 random features with
+    // d_v = 128, whose S^T alone is 64 KiB: the causal pass of la_forward.h
+    // serves that shape)
+    static constexpr bool FITS = TOTAL <= 160 * 1024;
 };
 
 // Element offset in S^T ([DV][F] bf16) of 16-byte unit u of row r.
@@ -83,16 +118,17 @@ __device__ __forceinline__ int st_off(int r, int u)
     return r * F + ((u ^ (r & 7)) << 3);
 }
 
-template <int PHI, int F, int DV, bool OUTF32>
-__global__ void __launch_bounds__((OutCfg<F, DV>::NT), 2)
+template <int PHI, int DK, int F, int DV, bool OUTF32>
+__global__ void __launch_bounds__((OutCfg<PHI, DK, F, DV>::NT), 2)
 la_out_kernel(const FwdArgs a)
 {
-    using Cfg = OutCfg<F, DV>;
+    using Cfg = OutCfg<PHI, DK, F, DV>;
     using T = bf16;
     constexpr int C = Cfg::C, NT = Cfg::NT, NW = Cfg::NW, QW = Cfg::QW, DBQ = Cfg::DBQ, FBW = Cfg::FBW;
     constexpr int KB = Cfg::KB, CB = Cfg::CB, DB = Cfg::DB, VEC = Cfg::VEC;
     constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
-    constexpr int DK = F;
+    constexpr bool RF = Cfg::RF, VW = Cfg::VW;
+    constexpr int M = Cfg::M, XLD = Cfg::XLD, KX = Cfg::KX, RB = Cfg::RB;
     using TF = TileL<T, F>;
     using TVL = TileL<T, DV>;
 
@@ -103,6 +139,10 @@ la_out_kernel(const FwdArgs a)
     T* const sV = (T*)(smem + Cfg::OFF_V);
     T* const sST = (T*)(smem + Cfg::OFF_ST);
     T* const sZ = (T*)(smem + Cfg::OFF_Z);
+    T* const sX = (T*)(smem + Cfg::OFF_X);        // raw q rows, then raw k rows ([C][XLD] each)
+    float* const sCF = (float*)(smem + Cfg::OFF_CF);  // prefactors of those rows; < 0: a dropped key
+    Frag<T>* const sOm = (Frag<T>*)(smem + Cfg::OFF_OM);
+    float* const sWt = (float*)(smem + Cfg::OFF_W);  // key weights of the chunk (decay, weights on V)
 
     // the wave index as a scalar: every branch on the query block below is
     // uniform over the wave
@@ -159,6 +199,29 @@ la_out_kernel(const FwdArgs a)
         m1[r] = decay ? lam_pow(l2l, 16 + e) : 1.f;
     }
     const float lq = decay ? lam_pow(l2l, 16 * ib + l16 + 1) : 1.f;  // lambda^(i+1)
+
+    // ---- random features: rows 16 rb + l16 of omega as A-operand fragments,
+    // scaled by qk_scale / (2 pi) so that the products are angles in
+    // revolutions, and split into bf16 high and low parts (omega = hi + lo to
+    // 16 bits), into LDS (read after the first barrier).  A wave of feature
+    // work takes row blocks rb = rbg + (NW / 2) u of the token matrix xpass.
+    const int rbg = wave % (NW / 2), xpass = wave / (NW / 2);
+    if constexpr (RF) {
+        const float om_scale = a.qk_scale * 0.159154943091895336f;
+        for (int fi = wave; fi < (M / 16) * KX; fi += NW) {
+            const int rb = fi / KX, kb = fi % KX;
+            const float* p = a.omega + (int64_t)(16 * rb + l16) * DK + 32 * kb + 4 * g;
+            const f32x4 w0 = *(const f32x4*)p * om_scale, w1 = *(const f32x4*)(p + 16) * om_scale;
+            f32x4 r0, r1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r0[e] = w0[e] - (float)(bf16)w0[e];
+                r1[e] = w1[e] - (float)(bf16)w1[e];
+            }
+            sOm[(fi * 2 + 0) * 64 + lane] = frag_acc<T>(w0, w1);
+            sOm[(fi * 2 + 1) * 64 + lane] = frag_acc<T>(r0, r1);
+        }
+    }
 
     // ---- loads of one chunk into registers (as la_forward.h: a ragged last
     // chunk re-reads its last row and zeroes the rows past its end)
@@ -240,8 +303,11 @@ la_out_kernel(const FwdArgs a)
     publish();
     float log2D = 0.f;  // the true state is 2^log2D times the accumulators
 
-    // ---- staging of one chunk from the registers: phi(q), phi(k), the
-    // lambda-weighted phi(k) (decay only) and v.  kw_l2 as in la_forward.h.
+    // ---- staging of one chunk from the registers.  Elementwise maps: phi(q),
+    // phi(k), the lambda-weighted phi(k) (decay only) and v.  Random features:
+    // v, and with decay the key weights; their q, k rows go in raw by stage_x
+    // and become features in features().  kw_l2 as in
+    // la_forward.h.
     auto key_weight = [&](int k, float kw_l2) LA_INLINE {
         return k == 0 ? __builtin_amdgcn_exp2f(-kw_l2) : __builtin_amdgcn_exp2f((float)k * l2l - kw_l2);
     };
@@ -252,32 +318,34 @@ la_out_kernel(const FwdArgs a)
     auto stage = [&](int n, float kw_l2, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const int cg = tid % VPRQ;
+        if constexpr (!RF) {
 #pragma unroll
-        for (int r = 0; r < RQ; ++r) {
-            const int j = (tid + r * NT) / VPRQ;
-            float x[VEC], p[VEC];
-            unpack16(rq[r], x, (const T*)nullptr);
+            for (int r = 0; r < RQ; ++r) {
+                const int j = (tid + r * NT) / VPRQ;
+                float x[VEC], p[VEC];
+                unpack16(rq[r], x, (const T*)nullptr);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
-            put_feat(sQ, j, cg * VEC, p);
-        }
-#pragma unroll
-        for (int r = 0; r < RQ; ++r) {
-            const int j = (tid + r * NT) / VPRQ;
-            float x[VEC], p[VEC];
-            unpack16(rk[r], x, (const T*)nullptr);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
-            if ((TAIL && j >= n) || mk[r]) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) p[e] = 0.f;
+                for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
+                put_feat(sQ, j, cg * VEC, p);
             }
-            put_feat(sK, j, cg * VEC, p);
-            if (decay) {
-                const float w = (TAIL && j >= n) ? 0.f : key_weight(n - 1 - j, kw_l2);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) p[e] *= w;
-                put_feat(sKw0, j, cg * VEC, p);
+            for (int r = 0; r < RQ; ++r) {
+                const int j = (tid + r * NT) / VPRQ;
+                float x[VEC], p[VEC];
+                unpack16(rk[r], x, (const T*)nullptr);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
+                if ((TAIL && j >= n) || mk[r]) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) p[e] = 0.f;
+                }
+                put_feat(sK, j, cg * VEC, p);
+                if (decay) {
+                    const float w = (TAIL && j >= n) ? 0.f : key_weight(n - 1 - j, kw_l2);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) p[e] *= w;
+                    put_feat(sKw0, j, cg * VEC, p);
+                }
             }
         }
 #pragma unroll
@@ -287,6 +355,92 @@ la_out_kernel(const FwdArgs a)
             *(uint2*)(sV + TVL::off(j, c4 * VEC)) = uint2{u.x, u.y};
             *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
         }
+        if constexpr (VW) {
+            if (decay && tid < C) sWt[tid] = (TAIL && tid >= n) ? 0.f : key_weight(n - 1 - tid, kw_l2);
+        }
+    };
+
+    // ---- random features, part 1: the raw q and k rows and the prefactor
+    // c(x) = exp(s |x'|^2 / 2) / sqrt(m) of each; a key that is past the end
+    // of the sequence or masked is marked by a negative prefactor
+    const float rf_cexp = 0.5f * a.rf_sign * a.qk_scale * a.qk_scale;
+    const float rf_cnorm = RF ? rsqrtf((float)M) : 0.f;
+    auto stage_x = [&](int n, auto tail_c) LA_INLINE {
+        if constexpr (RF) {
+            constexpr bool TAIL = decltype(tail_c)::value;
+            const int cg = tid % VPRQ;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+                for (int r = 0; r < RQ; ++r) {
+                    const int j = (tid + r * NT) / VPRQ;
+                    const uint4 u = pass ? rk[r] : rq[r];
+                    T* const row = sX + (pass * C + j) * XLD + cg * VEC;
+                    *(uint2*)row = uint2{u.x, u.y};
+                    *(uint2*)(row + 4) = uint2{u.z, u.w};
+                    float x[VEC];
+                    unpack16(u, x, (const T*)nullptr);
+                    float s2 = 0.f;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) s2 += x[e] * x[e];
+                    s2 = wave_sum_xor(s2, 1, VPRQ / 2);
+                    if (cg == 0) {
+                        float cf = exp_rf<T>(rf_cexp * s2) * rf_cnorm;
+                        if (pass == 1 && ((TAIL && j >= n) || mk[r])) cf = -1.f;
+                        sCF[pass * C + j] = cf;
+                    }
+                }
+        }
+    };
+
+    // ---- random features, part 2: U^T = omega x^T on the matrix cores for
+    // this wave's row blocks of omega and token matrix (queries or keys), all
+    // four token blocks; cos and sin times the prefactor, written row-major
+    // into phi(Q) or phi(K) (columns f and m + f).  A dropped key gets zeros
+    // by selection, so that no value of it reaches a sum.
+    auto features = [&]() LA_INLINE {
+        if constexpr (RF) {
+            const T* const xs = sX + xpass * C * XLD;
+            const float* const cfs = sCF + xpass * C;
+            T* const tile = xpass ? sK : sQ;
+            Frag<T> om_hi[RB][KX], om_lo[RB][KX];
+#pragma unroll
+            for (int u = 0; u < RB; ++u)
+#pragma unroll
+                for (int kb = 0; kb < KX; ++kb) {
+                    const int fi = (rbg + (NW / 2) * u) * KX + kb;
+                    om_hi[u][kb] = sOm[(fi * 2 + 0) * 64 + lane];
+                    om_lo[u][kb] = sOm[(fi * 2 + 1) * 64 + lane];
+                }
+#pragma unroll
+            for (int tb = 0; tb < Cfg::QB; ++tb) {
+                const int j = 16 * tb + l16;
+                Frag<T> xf[KX];
+#pragma unroll
+                for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(xs, XLD, j, 32 * kb, g);
+                const float cf = cfs[j];
+                const bool drop = cf < 0.f;
+#pragma unroll
+                for (int u = 0; u < RB; ++u) {
+                    f32x4 acc = zero4;
+#pragma unroll
+                    for (int kb = 0; kb < KX; ++kb) {
+                        mma(acc, om_hi[u][kb], xf[kb]);
+                        mma(acc, om_lo[u][kb], xf[kb]);
+                    }
+                    // acc[r]: angle of feature f0 + r for token j
+                    const int f0 = 16 * (rbg + (NW / 2) * u) + 4 * g;
+                    float cs[4], sn[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        cs[r] = drop ? 0.f : cf * __builtin_amdgcn_cosf(acc[r]);
+                        sn[r] = drop ? 0.f : cf * __builtin_amdgcn_sinf(acc[r]);
+                    }
+                    st4(tile + TF::off(j, f0), cs[0], cs[1], cs[2], cs[3]);
+                    st4(tile + TF::off(j, M + f0), sn[0], sn[1], sn[2], sn[3]);
+                }
+            }
+        }
     };
 
     // ---- outputs of this wave's query block and the update of its state
@@ -294,28 +448,56 @@ la_out_kernel(const FwdArgs a)
     // rescale: factor on the accumulators before the chunk's keys are added.
     auto compute = [&](int n, int64_t t0, float dscale, bool do_rescale, float rescale, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
-        const T* const sKw = decay ? sKw0 : sK;
         const int i = 16 * ib + l16;
-        Frag<T> qf[KB];
+        // products with phi(Q): phi(q_i).z (every row holds it), the scores
+        // of this query block against all four key blocks as P^T, and the
+        // inter-chunk part S^T phi(Q)^T of this wave's column tiles t = dq0 ..
+        // dq0 + DBQ - 1.  Where the feature row has no more k blocks than the
+        // wave has column tiles, the fragments of phi(q_i) are read first and
+        // the inter-chunk part follows per column tile; otherwise the
+        // products run one k block at a time into DBQ accumulators.
+        constexpr bool QF_ALL = KB <= DBQ;
+        f32x4 dq = zero4, pt[4], o[QF_ALL ? 1 : DBQ];
+        Frag<T> qf[QF_ALL ? KB : 1];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F>(sQ, i, kb, g);
-        // phi(q_i).z (every row holds it)
-        f32x4 dq = zero4;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int jb = 0; jb < 4; ++jb) pt[jb] = zero4;
+        auto sfrag = [&](int t, int kb) LA_INLINE {
+            Frag<T> sf;
+            sf.v = *(const bf16x8*)(sST + st_off<F>(16 * t + l16, 4 * kb + g));
+            return sf;
+        };
+        auto zfrag = [&](int kb) LA_INLINE {
             Frag<T> zf;
             zf.v = *(const bf16x8*)(sZ + (4 * kb + g) * 8);
-            mma(dq, zf, qf[kb]);
+            return zf;
+        };
+        if constexpr (QF_ALL) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F>(sQ, i, kb, g);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) mma(dq, zfrag(kb), qf[kb]);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
+        } else {
+#pragma unroll
+            for (int tq = 0; tq < DBQ; ++tq) o[tq] = zero4;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const Frag<T> q1 = lds_frag_row<T, F>(sQ, i, kb, g);
+                mma(dq, zfrag(kb), q1);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), q1);
+#pragma unroll
+                for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
+            }
         }
-        // scores of this query block against all four key blocks, as P^T;
-        // blocks after the query block (jb > ib) and keys above the diagonal
-        // are set to zero by selection.  No branch depends on the wave.
-        f32x4 pt[4];
+        // decay weights of the scores; blocks after the query block (jb > ib)
+        // and keys above the diagonal are set to zero by selection.  No branch
+        // depends on the wave.
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-            pt[jb] = zero4;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
             // lambda^(16 (ib-jb-1)) for blocks before the query block
             const float dj = lam_pow(l2l, max(16 * (ib - jb - 1), 0));
 #pragma unroll
@@ -335,6 +517,22 @@ la_out_kernel(const FwdArgs a)
         const float lqd = lq * dscale;
         const float inv = fast_rcp(rs[0] + lqd * dq[0] + a.eps);
         const float sc = lqd * inv;
+        // B operands of the z update: the chunk's key weights where they are
+        // not in the key features, else ones
+        Frag<T> wf[CB];
+        f32x4 wlo[VW ? CB : 1], whi[VW ? CB : 1];  // the weights of this lane's k positions
+#pragma unroll
+        for (int kb = 0; kb < CB; ++kb) wf[kb] = ones;
+        if constexpr (VW) {
+            if (decay) {
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) {
+                    wlo[kb] = *(const f32x4*)(sWt + 32 * kb + 4 * g);
+                    whi[kb] = *(const f32x4*)(sWt + 32 * kb + 16 + 4 * g);
+                    wf[kb] = frag_acc<T>(wlo[kb], whi[kb]);
+                }
+            }
+        }
         if (do_rescale) {
 #pragma unroll
             for (int u = 0; u < FBW; ++u) {
@@ -343,49 +541,96 @@ la_out_kernel(const FwdArgs a)
                 for (int c = 0; c < DBQ; ++c) accS[u][c] *= rescale;
             }
         }
-        // weighted key fragments of this wave's feature blocks (A operands of
-        // the state update)
-        Frag<T> kwf[FBW][CB];
+        // A operands of the state update: the weighted key features, or (the
+        // weights on the values, or no decay) the key features themselves.
+        // Where a wave has no more feature blocks than column tiles, their
+        // fragments are read first and each column tile's update follows its
+        // outputs; otherwise the (weighted) value fragments of every column
+        // tile are kept and the update runs one feature block at a time.
+        const T* const sKu = (VW || !decay) ? sK : sKw0;
+        constexpr bool KEYS_FIRST = FBW <= DBQ;
+        Frag<T> kwf[KEYS_FIRST ? FBW : 1][CB];
+        if constexpr (KEYS_FIRST) {
 #pragma unroll
-        for (int u = 0; u < FBW; ++u)
+            for (int u = 0; u < FBW; ++u)
 #pragma unroll
-            for (int kb = 0; kb < CB; ++kb) kwf[u][kb] = ColRead<T, F>::get(sKw, 32 * kb, 16 * (FBW * qw + u), lane);
-        // outputs of this wave's column tiles t = dq0 .. dq0 + DBQ - 1:
-        // O^T = S^T phi(Q)^T (scaled) + V^T P^T
+                for (int kb = 0; kb < CB; ++kb)
+                    kwf[u][kb] = ColRead<T, F>::get(sKu, 32 * kb, 16 * (FBW * qw + u), lane);
+        }
+        // outputs of this wave's column tiles: O^T = S^T phi(Q)^T (scaled) +
+        // V^T P^T; the value fragments of a column tile are the A operands of
+        // V^T P^T and (weighted where the weights are on the values) the B
+        // operands of the state update
         const int64_t yrow = row0 + t0 + i;
+        Frag<T> vwf[KEYS_FIRST ? 1 : DBQ][CB];
 #pragma unroll
         for (int tq = 0; tq < DBQ; ++tq) {
             const int t = dq0 + tq;
-            // value fragments of column tile t: A operands of V^T P^T and B
-            // operands of this wave's state update
             Frag<T> vf[CB];
 #pragma unroll
             for (int kb = 0; kb < CB; ++kb) vf[kb] = ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane);
-            f32x4 o = zero4, oi = zero4;
+            f32x4 ot, oi = zero4;
+            if constexpr (QF_ALL) {
+                ot = zero4;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                Frag<T> sf;
-                sf.v = *(const bf16x8*)(sST + st_off<F>(16 * t + l16, 4 * kb + g));
-                mma(o, sf, qf[kb]);
+                for (int kb = 0; kb < KB; ++kb) mma(ot, sfrag(t, kb), qf[kb]);
+            } else {
+                ot = o[tq];
             }
 #pragma unroll
             for (int kb = 0; kb < CB; ++kb) mma(oi, vf[kb], pf[kb]);
-            const f32x4 y = o * sc + oi * inv;
+            const f32x4 y = ot * sc + oi * inv;
             if (!TAIL || i < n) {
                 const int64_t yo = yrow * DV + 16 * t + 4 * g;
                 if constexpr (OUTF32) st4((float*)a.y + yo, y[0], y[1], y[2], y[3]);
                 else st4((T*)a.y + yo, y[0], y[1], y[2], y[3]);
             }
-            // state update of this wave's part: S^ += (w phi(K))^T V
+            const int vs = KEYS_FIRST ? 0 : tq;
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) vwf[vs][kb] = vf[kb];
+            if constexpr (VW) {
+                if (decay) {
+#pragma unroll
+                    for (int kb = 0; kb < CB; ++kb) {
+                        f32x4 lo, hi;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            lo[e] = (float)vf[kb].v[e] * wlo[kb][e];
+                            hi[e] = (float)vf[kb].v[4 + e] * whi[kb][e];
+                        }
+                        vwf[vs][kb] = frag_acc<T>(lo, hi);
+                    }
+                }
+            }
+            // state update of this column tile: S^ += (w phi(K))^T V, or
+            // phi(K)^T (w V)
+            if constexpr (KEYS_FIRST) {
+#pragma unroll
+                for (int u = 0; u < FBW; ++u)
+#pragma unroll
+                    for (int kb = 0; kb < CB; ++kb) mma(accS[u][tq], kwf[u][kb], vwf[0][kb]);
+            }
+        }
+        if constexpr (KEYS_FIRST) {
 #pragma unroll
             for (int u = 0; u < FBW; ++u)
 #pragma unroll
-                for (int kb = 0; kb < CB; ++kb) mma(accS[u][tq], kwf[u][kb], vf[kb]);
+                for (int kb = 0; kb < CB; ++kb) mma(accZ[u], kwf[u][kb], wf[kb]);
+        } else {
+            // state update one feature block at a time, z likewise
+#pragma unroll
+            for (int u = 0; u < FBW; ++u) {
+                Frag<T> kf[CB];
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) kf[kb] = ColRead<T, F>::get(sKu, 32 * kb, 16 * (FBW * qw + u), lane);
+#pragma unroll
+                for (int tq = 0; tq < DBQ; ++tq)
+#pragma unroll
+                    for (int kb = 0; kb < CB; ++kb) mma(accS[u][tq], kf[kb], vwf[tq][kb]);
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) mma(accZ[u], kf[kb], wf[kb]);
+            }
         }
-#pragma unroll
-        for (int u = 0; u < FBW; ++u)
-#pragma unroll
-            for (int kb = 0; kb < CB; ++kb) mma(accZ[u], kwf[u][kb], ones);
     };
 
     // decay bookkeeping, in chunk order (as la_forward.h)
@@ -410,28 +655,43 @@ la_out_kernel(const FwdArgs a)
         Dec d;
         if (c_beg < c_full) {
             d = book(C);
+            stage_x(C, std::false_type{});
             stage(C, d.kw_l2, std::false_type{});
         } else {
             d = book(n_tail);
+            stage_x(n_tail, std::true_type{});
             stage(n_tail, d.kw_l2, std::true_type{});
+        }
+        if constexpr (RF) {
+            __syncthreads();
+            features();
         }
         for (int64_t c = c_beg; c < c_full; ++c) {
             const bool next_full = c + 1 < c_full;
             __syncthreads();
             if (next_full) load_chunk(c + 1, std::false_type{});
             compute(C, c * C, d.dscale, d.do_rescale, d.rescale, std::false_type{});
+            // raw rows of the next chunk: features() of this chunk read them
+            // before the barrier above
+            if (next_full) stage_x(C, std::false_type{});
             __syncthreads();
             publish();
             if (next_full) {
                 d = book(C);
                 stage(C, d.kw_l2, std::false_type{});
+                features();
             }
         }
         if (ragged) {
             if (c_full > c_beg) {
                 load_chunk(c_full, std::true_type{});
                 d = book(n_tail);
+                stage_x(n_tail, std::true_type{});
                 stage(n_tail, d.kw_l2, std::true_type{});
+                if constexpr (RF) {
+                    __syncthreads();
+                    features();
+                }
             }
             __syncthreads();
             compute(n_tail, c_full * C, d.dscale, d.do_rescale, d.rescale, std::true_type{});
@@ -455,15 +715,16 @@ la_out_kernel(const FwdArgs a)
     }
 }
 
-template <int PHI, int F, int DV>
+template <int PHI, int DK, int F, int DV>
 hipError_t out_launch(const FwdArgs& a, hipStream_t stream)
 {
-    using Cfg = OutCfg<F, DV>;
+    using Cfg = OutCfg<PHI, DK, F, DV>;
+    static_assert(Cfg::FITS, "LDS budget");
     if (a.chunk % Cfg::C != 0) return hipErrorInvalidValue;  // segments must be whole chunks
     const dim3 grid(a.cu_seqlens ? (unsigned)a.G : (unsigned)a.P, a.cu_seqlens ? (unsigned)a.H : (unsigned)a.BH),
         block(Cfg::NT);
-    if (a.out_f32) return launch_kernel(la_out_kernel<PHI, F, DV, true>, grid, block, stream, a);
-    return launch_kernel(la_out_kernel<PHI, F, DV, false>, grid, block, stream, a);
+    if (a.out_f32) return launch_kernel(la_out_kernel<PHI, DK, F, DV, true>, grid, block, stream, a);
+    return launch_kernel(la_out_kernel<PHI, DK, F, DV, false>, grid, block, stream, a);
 }
 
 }  // namespace la
