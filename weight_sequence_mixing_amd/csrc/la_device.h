@@ -117,21 +117,48 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
 }
 
 // ---- LDS tiles ----------------------------------------------------------
+// Bank model of the gfx950 LDS (64 banks of 4 bytes), as measured with the
+// bank-conflict counter: a single 8-byte read is served 32 lanes at a time,
+// without conflict when their 8-byte slots differ modulo 256 bytes; an
+// 8-byte write, and each half of a two-address 8-byte read (ds_read2*), 16
+// lanes at a time, slots modulo 128 bytes; a 16-byte read 16 lanes at a time,
+// 16-byte slots modulo 256 bytes.
+//
 // A per-chunk operand tile holds `rows` tokens of W elements each, row-major.
 // bf16 tiles have no padding; their 8-byte units (4 elements) are XOR-swizzled
-// inside each aligned group of 16 units by swz(row).  With that permutation a
-// row-fragment read (16 consecutive rows, one unit each) and a transposing
-// read (4 consecutive rows x 4 consecutive units per 16 lanes) both touch 32
-// distinct banks.  fp32 tiles are padded by 4 elements per row instead.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
+// by the row.  Two layouts:
+//   TileL: u ^ (4 (r & 3) + bits2..3(r)), inside aligned groups of 16 units.
+//          A row-fragment read (16 consecutive rows, one unit each) is
+//          conflict-free in the two-address form the compiler makes of the
+//          reads of row blocks 16 rows apart, and so is an 8-byte write of
+//          one unit of 16 consecutive rows; single 8-byte reads (two units per
+//          32 lanes) and transposing reads pay one extra cycle per 32 lanes.
+//          Its address pattern repeats every 16 units, which keeps the
+//          number of address registers small.
+//   TileX: W >= 128: u ^ (4 (r & 7) + 2 bit3(r) + bit2(r)) ^ bit4(u);
+//          W == 64:  u ^ (4 bits1..2(r) + 2 bit3(r) + bit0(r)).
+//          Conflict-free for all of the above and for the two 8-byte halves
+//          of a staged 16-byte vector (consecutive threads along a row).
+// fp32 tiles are padded by 4 elements per row instead.
 template <class T, int W> struct TileL;
 template <int W> struct TileL<bf16, W> {
     static_assert(W % 64 == 0, "bf16 tiles need at least 16 units per row");
     static constexpr int STRIDE = W;
     // element offset of the 4-element unit holding column col (col % 4 == 0)
     __device__ static __forceinline__ int off(int row, int col) {
-        return row * W + ((((col >> 2) ^ swz(row))) << 2);
+        return row * W + ((((col >> 2) ^ (((row & 3) << 2) | ((row >> 2) & 3)))) << 2);
+    }
+};
+template <class T, int W> struct TileX;
+template <int W> struct TileX<bf16, W> {
+    static_assert(W == 64 || W % 128 == 0, "rows of 64 or a multiple of 128 elements");
+    static constexpr int STRIDE = W;
+    __device__ static __forceinline__ int off(int row, int col) {
+        const int u = col >> 2;
+        if constexpr (W >= 128)
+            return row * W + ((u ^ (((row & 7) << 2) | ((row >> 2) & 2) | ((row >> 2) & 1)) ^ ((u >> 4) & 1)) << 2);
+        else
+            return row * W + ((u ^ ((((row >> 1) & 3) << 2) | ((row >> 2) & 2) | (row & 1))) << 2);
     }
 };
 template <int W> struct TileL<float, W> {
@@ -140,9 +167,9 @@ template <int W> struct TileL<float, W> {
 };
 
 // Row fragment: lane (row, g) holds columns {32kb+4g..+3, 32kb+16+4g..+3}.
-template <class T, int W>
+template <class T, int W, class L = TileL<T, W>>
 __device__ __forceinline__ Frag<T> lds_frag_row(const T* t, int row, int kb, int g) {
-    return frag2(t + TileL<T, W>::off(row, 32 * kb + 4 * g), t + TileL<T, W>::off(row, 32 * kb + 16 + 4 * g));
+    return frag2(t + L::off(row, 32 * kb + 4 * g), t + L::off(row, 32 * kb + 16 + 4 * g));
 }
 
 // Column fragment of rows j0..j0+31 and columns m0..m0+15 (j0 % 32 == 0,
@@ -153,13 +180,13 @@ __device__ __forceinline__ Frag<T> lds_frag_row(const T* t, int row, int kb, int
 // instruction returns to lane i, slot e, element i%4 of the 8 bytes addressed
 // by lane 4e+i/4; lane 16g+l' therefore addresses row j0+4g+l'/4 at column
 // m0+4(l'%4).  fp32: eight scalar reads.
-template <class T, int W> struct ColRead;
-template <int W> struct ColRead<bf16, W> {
+template <class T, int W, class L = TileL<T, W>> struct ColRead;
+template <int W, class L> struct ColRead<bf16, W, L> {
     __device__ static __forceinline__ Frag<bf16> get(const bf16* t, int j0, int m0, int lane) {
         typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
         const int g = lane >> 4, lp = lane & 15;
         const int row = j0 + 4 * g + (lp >> 2), col = m0 + 4 * (lp & 3);
-        const bf16* p = t + TileL<bf16, W>::off(row, col);
+        const bf16* p = t + L::off(row, col);
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * W));
         Frag<bf16> f;
@@ -167,7 +194,7 @@ template <int W> struct ColRead<bf16, W> {
         return f;
     }
 };
-template <int W> struct ColRead<float, W> {
+template <int W, class L> struct ColRead<float, W, L> {
     __device__ static __forceinline__ Frag<float> get(const float* t, int j0, int m0, int lane) {
         const int g = lane >> 4, m = m0 + (lane & 15);
         constexpr int S = TileL<float, W>::STRIDE;

@@ -345,7 +345,6 @@ la_fwd_kernel(const FwdArgs a)
     int mk[PF][Cfg::NEED_K ? RQ : 1];  // mask bytes of this thread's key rows
     auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
-        const uint4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int r = 0; r < nreg; ++r) {
             const int idx = tid + r * NT, j = idx / vpr, c4 = idx % vpr;
@@ -353,7 +352,8 @@ la_fwd_kernel(const FwdArgs a)
                 dst[r] = *(const uint4*)(base + j * ld + c4 * VEC);
             } else {
                 const uint4 val = *(const uint4*)(base + min(j, n - 1) * ld + c4 * VEC);
-                dst[r] = (j < n) ? val : zero;
+                const bool in = j < n;  // per component: a select of the whole vector goes through memory
+                dst[r] = uint4{in ? val.x : 0u, in ? val.y : 0u, in ? val.z : 0u, in ? val.w : 0u};
             }
         }
     };

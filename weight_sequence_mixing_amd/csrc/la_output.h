@@ -29,21 +29,26 @@
 // each token; then every wave computes a share of the feature tiles on the
 // matrix cores (omega x^T from omega's row blocks, kept in LDS as bf16 high
 // and low parts, angles in revolutions for the hardware sine and cosine)
-// and writes them into the same tiles the elementwise maps use.  Half of the
-// waves take the queries, half the keys; a wave keeps RB row blocks of omega.
+// and writes cos and sin into the same tiles the elementwise maps use.  Half
+// of the waves take the queries, half the keys; a wave keeps RB row blocks of
+// omega.  The prefactors stay out of the tiles: a key's enters the score
+// weights and the value weights of the state update, a query's the
+// normaliser, since num_i and den_i are both linear in phi(q_i).
 //
 // Decay weights of the state update.  The elementwise maps stage the key
 // features a second time with the weight lambda^(n-1-j) (rescaled, see book);
 // the random features, whose feature rows are wider than the value rows, put
-// the weight on the value fragments instead, in registers (and the weights
-// themselves form the B operand of the z update), which halves the LDS tiles
-// of the keys.
+// the weight (times the key's prefactor) on the value fragments instead, in
+// registers (and the weights themselves form the B operand of the z update),
+// which halves the LDS tiles of the keys.
 //
-// Layouts.  phi(Q), phi(K), the weighted phi(K) and V are staged in LDS as in
-// la_forward.h (TileL, swizzled 8-byte units).  S^T is [DV][F] bf16 with the
+// Layouts.  phi(Q), phi(K) and the weighted phi(K) are staged in LDS as in
+// la_forward.h (TileL, swizzled 8-byte units); V and the raw q, k rows in
+// TileX, whose swizzle is conflict-free for transposing reads and staging
+// (la_device.h has the bank model).  S^T is [DV][F] bf16 with the
 // feature order inside each 32-wide block permuted so that the 8 k positions
 // K(g) a lane needs (la_device.h) are contiguous: one 16-byte read per
-// fragment; the 16-byte units are XOR-swizzled with (row & 7).  z is kept
+// fragment; the 16-byte units are XOR-swizzled by row (st_off).  z is kept
 // the same way ([F] bf16, permuted), so its fragment is one 16-byte read too.
 //
 // Per chunk there are two barriers: one after the chunk is staged (tiles,
@@ -81,10 +86,9 @@ struct OutCfg {
     static constexpr int VEC = 8;        // bf16 per 16-byte vector
     static constexpr int VPRQ = DK / VEC, VPRV = DV / VEC;
     static constexpr int RQ = C * VPRQ / NT, RV = C * VPRV / NT;
-    // random features: raw rows of XLD elements (8 bytes of padding, so that
-    // the 16 rows of a fragment read start in different banks); omega row
+    // random features: raw q, k rows (TileL layout of width DK); omega row
     // blocks per wave, each wave covering one of the two token matrices
-    static constexpr int XLD = DK + 4, KX = DK / 32;
+    static constexpr int KX = DK / 32;
     static constexpr int RB = RF ? 2 * (M / 16) / NW : 0;
     static constexpr int TQ = C * F, TV = C * DV;  // elements of a tile
     static constexpr size_t OFF_Q = 0;
@@ -94,9 +98,9 @@ struct OutCfg {
     static constexpr size_t OFF_ST = OFF_V + size_t(TV) * 2;
     static constexpr size_t OFF_Z = OFF_ST + size_t(DV) * F * 2;
     static constexpr size_t OFF_X = OFF_Z + size_t(F) * 2;
-    static constexpr size_t OFF_CF = OFF_X + (RF ? size_t(2) * C * XLD * 2 : 0);
+    static constexpr size_t OFF_CF = OFF_X + (RF ? size_t(2) * C * DK * 2 : 0);
     // omega's operand fragments: [row block][k block][high, low][lane], 16 bytes
-    static constexpr size_t OFF_OM = OFF_CF + (RF ? size_t(2) * C * 4 : 0);
+    static constexpr size_t OFF_OM = OFF_CF + (RF ? size_t(4) * C * 4 : 0);
     static constexpr size_t OFF_W = OFF_OM + (RF ? size_t(M / 16) * KX * 2 * 64 * 16 : 0);
     static constexpr size_t TOTAL = OFF_W + (VW ? size_t(C) * 4 : 0);
     static_assert(F % 64 == 0 && DV % 64 == 0 && DK % 64 == 0, "head sizes");
@@ -111,11 +115,15 @@ struct OutCfg {
     static constexpr bool FITS = TOTAL <= 160 * 1024;
 };
 
-// Element offset in S^T ([DV][F] bf16) of 16-byte unit u of row r.
+// Element offset in S^T ([DV][F] bf16) of 16-byte unit u of row r: the units
+// are XOR-swizzled by row, so that the 16 rows of a fragment read fall in
+// distinct 16-byte slots of the 64 banks (rows of F = 64 share a 256-byte
+// window two by two).
 template <int F>
 __device__ __forceinline__ int st_off(int r, int u)
 {
-    return r * F + ((u ^ (r & 7)) << 3);
+    if constexpr (F >= 128) return r * F + ((u ^ (r & 15)) << 3);
+    else return r * F + ((u ^ ((r >> 1) & 7)) << 3);
 }
 
 template <int PHI, int DK, int F, int DV, bool OUTF32>
@@ -128,9 +136,12 @@ la_out_kernel(const FwdArgs a)
     constexpr int KB = Cfg::KB, CB = Cfg::CB, DB = Cfg::DB, VEC = Cfg::VEC;
     constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
     constexpr bool RF = Cfg::RF, VW = Cfg::VW;
-    constexpr int M = Cfg::M, XLD = Cfg::XLD, KX = Cfg::KX, RB = Cfg::RB;
+    constexpr int M = Cfg::M, KX = Cfg::KX, RB = Cfg::RB;
+    // phi(Q), phi(K) and the weighted phi(K) in TileL (row reads in the
+    // two-address form, 8-byte feature writes); V and the raw rows in TileX
     using TF = TileL<T, F>;
-    using TVL = TileL<T, DV>;
+    using TVL = TileX<T, DV>;
+    using TXL = TileX<T, DK>;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
     T* const sQ = (T*)(smem + Cfg::OFF_Q);
@@ -139,8 +150,11 @@ la_out_kernel(const FwdArgs a)
     T* const sV = (T*)(smem + Cfg::OFF_V);
     T* const sST = (T*)(smem + Cfg::OFF_ST);
     T* const sZ = (T*)(smem + Cfg::OFF_Z);
-    T* const sX = (T*)(smem + Cfg::OFF_X);        // raw q rows, then raw k rows ([C][XLD] each)
-    float* const sCF = (float*)(smem + Cfg::OFF_CF);  // prefactors of those rows; < 0: a dropped key
+    T* const sX = (T*)(smem + Cfg::OFF_X);        // raw q rows, then raw k rows (C x DK tiles)
+    // prefactors of those rows, two buffers by chunk parity: the next
+    // chunk's are written while the current chunk's are still read
+    float* const sCF0 = (float*)(smem + Cfg::OFF_CF);
+    int cb = 0;  // buffer of the chunk being staged and computed
     Frag<T>* const sOm = (Frag<T>*)(smem + Cfg::OFF_OM);
     float* const sWt = (float*)(smem + Cfg::OFF_W);  // key weights of the chunk (decay, weights on V)
 
@@ -232,7 +246,6 @@ la_out_kernel(const FwdArgs a)
     int mk[RQ];
     auto load_rows = [&](uint4* dst, const T* base, int vpr, int ld, int nreg, int n, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
-        const uint4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int r = 0; r < nreg; ++r) {
             const int idx = tid + r * NT, j = idx / vpr, c4 = idx % vpr;
@@ -240,7 +253,8 @@ la_out_kernel(const FwdArgs a)
                 dst[r] = *(const uint4*)(base + j * ld + c4 * VEC);
             } else {
                 const uint4 val = *(const uint4*)(base + min(j, n - 1) * ld + c4 * VEC);
-                dst[r] = (j < n) ? val : zero;
+                const bool in = j < n;  // per component: a select of the whole vector goes through memory
+                dst[r] = uint4{in ? val.x : 0u, in ? val.y : 0u, in ? val.z : 0u, in ? val.w : 0u};
             }
         }
     };
@@ -288,16 +302,37 @@ la_out_kernel(const FwdArgs a)
     }
     // this wave's rows into the shared S^T and z (bf16, permuted features)
     auto publish = [&]() LA_INLINE {
+        if constexpr (FBW % 2 == 0) {
+            // feature blocks fb (even) and fb + 1 fill the two halves of one
+            // 16-byte unit: one store each
 #pragma unroll
-        for (int u = 0; u < FBW; ++u) {
-            const int fb = FBW * qw + u;
-            const int unit = 4 * (fb >> 1) + g, half = (fb & 1) * 4;
+            for (int u = 0; u < FBW; u += 2) {
+                const int unit = 4 * ((FBW * qw + u) >> 1) + g;
 #pragma unroll
-            for (int c = 0; c < DBQ; ++c) {
-                const int r = 16 * (dq0 + c) + l16;
-                st4(sST + st_off<F>(r, unit) + half, accS[u][c][0], accS[u][c][1], accS[u][c][2], accS[u][c][3]);
+                for (int c = 0; c < DBQ; ++c) {
+                    const int r = 16 * (dq0 + c) + l16;
+                    const f32x4 a0 = accS[u][c], a1 = accS[u + 1][c];
+                    *(bf16x8*)(sST + st_off<F>(r, unit)) = bf16x8{(T)a0[0], (T)a0[1], (T)a0[2], (T)a0[3],
+                                                                   (T)a1[0], (T)a1[1], (T)a1[2], (T)a1[3]};
+                }
+                if (zowner && l16 == 0) {
+                    const f32x4 z0 = accZ[u], z1 = accZ[u + 1];
+                    *(bf16x8*)(sZ + unit * 8) = bf16x8{(T)z0[0], (T)z0[1], (T)z0[2], (T)z0[3],
+                                                       (T)z1[0], (T)z1[1], (T)z1[2], (T)z1[3]};
+                }
             }
-            if (zowner && l16 == 0) st4(sZ + unit * 8 + half, accZ[u][0], accZ[u][1], accZ[u][2], accZ[u][3]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < FBW; ++u) {
+                const int fb = FBW * qw + u;
+                const int unit = 4 * (fb >> 1) + g, half = (fb & 1) * 4;
+#pragma unroll
+                for (int c = 0; c < DBQ; ++c) {
+                    const int r = 16 * (dq0 + c) + l16;
+                    st4(sST + st_off<F>(r, unit) + half, accS[u][c][0], accS[u][c][1], accS[u][c][2], accS[u][c][3]);
+                }
+                if (zowner && l16 == 0) st4(sZ + unit * 8 + half, accZ[u][0], accZ[u][1], accZ[u][2], accZ[u][3]);
+            }
         }
     };
     publish();
@@ -305,15 +340,15 @@ la_out_kernel(const FwdArgs a)
 
     // ---- staging of one chunk from the registers.  Elementwise maps: phi(q),
     // phi(k), the lambda-weighted phi(k) (decay only) and v.  Random features:
-    // v, and with decay the key weights; their q, k rows go in raw by stage_x
-    // and become features in features().  kw_l2 as in
+    // v and the key weights; their q, k rows go in raw by stage_x and become
+    // features in features().  kw_l2 as in
     // la_forward.h.
     auto key_weight = [&](int k, float kw_l2) LA_INLINE {
         return k == 0 ? __builtin_amdgcn_exp2f(-kw_l2) : __builtin_amdgcn_exp2f((float)k * l2l - kw_l2);
     };
     auto put_feat = [&](T* tile, int row, int col, const float* p) LA_INLINE {
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) st4(tile + TF::off(row, col + e), p[e], p[e + 1], p[e + 2], p[e + 3]);
+        st4(tile + TF::off(row, col), p[0], p[1], p[2], p[3]);
+        st4(tile + TF::off(row, col + 4), p[4], p[5], p[6], p[7]);
     };
     auto stage = [&](int n, float kw_l2, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
@@ -356,16 +391,20 @@ la_out_kernel(const FwdArgs a)
             *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
         }
         if constexpr (VW) {
-            if (decay && tid < C) sWt[tid] = (TAIL && tid >= n) ? 0.f : key_weight(n - 1 - tid, kw_l2);
+            // weight of key tid in the state update: its decay weight times
+            // its prefactor (zero for a dropped key)
+            if (tid < C)
+                sWt[tid] = (TAIL && tid >= n) ? 0.f : (decay ? key_weight(n - 1 - tid, kw_l2) : 1.f) * sCF0[cb * 2 * C + C + tid];
         }
     };
 
     // ---- random features, part 1: the raw q and k rows and the prefactor
-    // c(x) = exp(s |x'|^2 / 2) / sqrt(m) of each; a key that is past the end
-    // of the sequence or masked is marked by a negative prefactor
+    // c(x) = exp(s |x'|^2 / 2) / sqrt(m) of each.  A key that is past the end
+    // of the sequence or masked is dropped: its row is staged as zeros (finite
+    // features whatever its values) and its prefactor is zero.
     const float rf_cexp = 0.5f * a.rf_sign * a.qk_scale * a.qk_scale;
     const float rf_cnorm = RF ? rsqrtf((float)M) : 0.f;
-    auto stage_x = [&](int n, auto tail_c) LA_INLINE {
+    auto stage_x = [&](int n, int buf, auto tail_c) LA_INLINE {
         if constexpr (RF) {
             constexpr bool TAIL = decltype(tail_c)::value;
             const int cg = tid % VPRQ;
@@ -374,34 +413,29 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
                 for (int r = 0; r < RQ; ++r) {
                     const int j = (tid + r * NT) / VPRQ;
-                    const uint4 u = pass ? rk[r] : rq[r];
-                    T* const row = sX + (pass * C + j) * XLD + cg * VEC;
-                    *(uint2*)row = uint2{u.x, u.y};
-                    *(uint2*)(row + 4) = uint2{u.z, u.w};
+                    const bool drop = pass == 1 && ((TAIL && j >= n) || mk[r]);
+                    const uint4 u = drop ? uint4{0u, 0u, 0u, 0u} : (pass ? rk[r] : rq[r]);
+                    T* const xt = sX + pass * C * DK;
+                    *(uint2*)(xt + TXL::off(j, cg * VEC)) = uint2{u.x, u.y};
+                    *(uint2*)(xt + TXL::off(j, cg * VEC + 4)) = uint2{u.z, u.w};
                     float x[VEC];
                     unpack16(u, x, (const T*)nullptr);
                     float s2 = 0.f;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) s2 += x[e] * x[e];
                     s2 = wave_sum_xor(s2, 1, VPRQ / 2);
-                    if (cg == 0) {
-                        float cf = exp_rf<T>(rf_cexp * s2) * rf_cnorm;
-                        if (pass == 1 && ((TAIL && j >= n) || mk[r])) cf = -1.f;
-                        sCF[pass * C + j] = cf;
-                    }
+                    if (cg == 0) sCF0[buf * 2 * C + pass * C + j] = drop ? 0.f : exp_rf<T>(rf_cexp * s2) * rf_cnorm;
                 }
         }
     };
 
     // ---- random features, part 2: U^T = omega x^T on the matrix cores for
     // this wave's row blocks of omega and token matrix (queries or keys), all
-    // four token blocks; cos and sin times the prefactor, written row-major
-    // into phi(Q) or phi(K) (columns f and m + f).  A dropped key gets zeros
-    // by selection, so that no value of it reaches a sum.
+    // four token blocks; cos and sin (without the prefactor) written
+    // row-major into phi(Q) or phi(K) (columns f and m + f)
     auto features = [&]() LA_INLINE {
         if constexpr (RF) {
-            const T* const xs = sX + xpass * C * XLD;
-            const float* const cfs = sCF + xpass * C;
+            const T* const xs = sX + xpass * C * DK;
             T* const tile = xpass ? sK : sQ;
             Frag<T> om_hi[RB][KX], om_lo[RB][KX];
 #pragma unroll
@@ -417,9 +451,7 @@ la_out_kernel(const FwdArgs a)
                 const int j = 16 * tb + l16;
                 Frag<T> xf[KX];
 #pragma unroll
-                for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(xs, XLD, j, 32 * kb, g);
-                const float cf = cfs[j];
-                const bool drop = cf < 0.f;
+                for (int kb = 0; kb < KX; ++kb) xf[kb] = lds_frag_row<T, DK, TXL>(xs, j, kb, g);
 #pragma unroll
                 for (int u = 0; u < RB; ++u) {
                     f32x4 acc = zero4;
@@ -433,8 +465,8 @@ la_out_kernel(const FwdArgs a)
                     float cs[4], sn[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        cs[r] = drop ? 0.f : cf * __builtin_amdgcn_cosf(acc[r]);
-                        sn[r] = drop ? 0.f : cf * __builtin_amdgcn_sinf(acc[r]);
+                        cs[r] = __builtin_amdgcn_cosf(acc[r]);
+                        sn[r] = __builtin_amdgcn_sinf(acc[r]);
                     }
                     st4(tile + TF::off(j, f0), cs[0], cs[1], cs[2], cs[3]);
                     st4(tile + TF::off(j, M + f0), sn[0], sn[1], sn[2], sn[3]);
@@ -493,18 +525,21 @@ la_out_kernel(const FwdArgs a)
                 for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
             }
         }
-        // decay weights of the scores; blocks after the query block (jb > ib)
-        // and keys above the diagonal are set to zero by selection.  No branch
-        // depends on the wave.
+        // decay weights of the scores (random features: times the key's
+        // prefactor); blocks after the query block (jb > ib) and keys above
+        // the diagonal are set to zero by selection.  No branch depends on the
+        // wave.
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             // lambda^(16 (ib-jb-1)) for blocks before the query block
             const float dj = lam_pow(l2l, max(16 * (ib - jb - 1), 0));
+            f32x4 ck = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * jb + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float wgt = (jb == ib) ? m0[r] : m1[r] * dj;
                 const bool zero = jb > ib || (jb == ib && above[r]);
-                pt[jb][r] = zero ? 0.f : pt[jb][r] * wgt;
+                pt[jb][r] = zero ? 0.f : pt[jb][r] * (RF ? wgt * ck[r] : wgt);
             }
         }
         Frag<T> pf[CB];
@@ -514,23 +549,25 @@ la_out_kernel(const FwdArgs a)
             pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
             mma(rs, ones, pf[kb]);
         }
+        // y_i = c_i (o + o_i) / (c_i den + eps) with c_i the query's
+        // prefactor (random features), else y_i = (o + o_i) / (den + eps)
         const float lqd = lq * dscale;
-        const float inv = fast_rcp(rs[0] + lqd * dq[0] + a.eps);
+        const float cq = RF ? sCF0[cb * 2 * C + i] : 1.f;
+        const float inv0 = fast_rcp(cq * (rs[0] + lqd * dq[0]) + a.eps);
+        const float inv = RF ? cq * inv0 : inv0;
         const float sc = lqd * inv;
         // B operands of the z update: the chunk's key weights where they are
         // not in the key features, else ones
         Frag<T> wf[CB];
         f32x4 wlo[VW ? CB : 1], whi[VW ? CB : 1];  // the weights of this lane's k positions
 #pragma unroll
-        for (int kb = 0; kb < CB; ++kb) wf[kb] = ones;
-        if constexpr (VW) {
-            if (decay) {
-#pragma unroll
-                for (int kb = 0; kb < CB; ++kb) {
-                    wlo[kb] = *(const f32x4*)(sWt + 32 * kb + 4 * g);
-                    whi[kb] = *(const f32x4*)(sWt + 32 * kb + 16 + 4 * g);
-                    wf[kb] = frag_acc<T>(wlo[kb], whi[kb]);
-                }
+        for (int kb = 0; kb < CB; ++kb) {
+            if constexpr (VW) {
+                wlo[kb] = *(const f32x4*)(sWt + 32 * kb + 4 * g);
+                whi[kb] = *(const f32x4*)(sWt + 32 * kb + 16 + 4 * g);
+                wf[kb] = frag_acc<T>(wlo[kb], whi[kb]);
+            } else {
+                wf[kb] = ones;
             }
         }
         if (do_rescale) {
@@ -568,7 +605,7 @@ la_out_kernel(const FwdArgs a)
             const int t = dq0 + tq;
             Frag<T> vf[CB];
 #pragma unroll
-            for (int kb = 0; kb < CB; ++kb) vf[kb] = ColRead<T, DV>::get(sV, 32 * kb, 16 * t, lane);
+            for (int kb = 0; kb < CB; ++kb) vf[kb] = ColRead<T, DV, TVL>::get(sV, 32 * kb, 16 * t, lane);
             f32x4 ot, oi = zero4;
             if constexpr (QF_ALL) {
                 ot = zero4;
@@ -589,17 +626,15 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
             for (int kb = 0; kb < CB; ++kb) vwf[vs][kb] = vf[kb];
             if constexpr (VW) {
-                if (decay) {
 #pragma unroll
-                    for (int kb = 0; kb < CB; ++kb) {
-                        f32x4 lo, hi;
+                for (int kb = 0; kb < CB; ++kb) {
+                    f32x4 lo, hi;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            lo[e] = (float)vf[kb].v[e] * wlo[kb][e];
-                            hi[e] = (float)vf[kb].v[4 + e] * whi[kb][e];
-                        }
-                        vwf[vs][kb] = frag_acc<T>(lo, hi);
+                    for (int e = 0; e < 4; ++e) {
+                        lo[e] = (float)vf[kb].v[e] * wlo[kb][e];
+                        hi[e] = (float)vf[kb].v[4 + e] * whi[kb][e];
                     }
+                    vwf[vs][kb] = frag_acc<T>(lo, hi);
                 }
             }
             // state update of this column tile: S^ += (w phi(K))^T V, or
@@ -653,19 +688,21 @@ la_out_kernel(const FwdArgs a)
 
     if (c_beg < c_end) {
         Dec d;
+        // (random features: the key weights of stage() need the prefactors
+        // of stage_x(), and features() the raw rows, so a barrier follows
+        // stage_x() where no other one does)
         if (c_beg < c_full) {
             d = book(C);
-            stage_x(C, std::false_type{});
+            stage_x(C, cb, std::false_type{});
+            if constexpr (RF) __syncthreads();
             stage(C, d.kw_l2, std::false_type{});
         } else {
             d = book(n_tail);
-            stage_x(n_tail, std::true_type{});
+            stage_x(n_tail, cb, std::true_type{});
+            if constexpr (RF) __syncthreads();
             stage(n_tail, d.kw_l2, std::true_type{});
         }
-        if constexpr (RF) {
-            __syncthreads();
-            features();
-        }
+        features();
         for (int64_t c = c_beg; c < c_full; ++c) {
             const bool next_full = c + 1 < c_full;
             __syncthreads();
@@ -673,10 +710,11 @@ la_out_kernel(const FwdArgs a)
             compute(C, c * C, d.dscale, d.do_rescale, d.rescale, std::false_type{});
             // raw rows of the next chunk: features() of this chunk read them
             // before the barrier above
-            if (next_full) stage_x(C, std::false_type{});
+            if (next_full) stage_x(C, cb ^ 1, std::false_type{});
             __syncthreads();
             publish();
             if (next_full) {
+                cb ^= 1;
                 d = book(C);
                 stage(C, d.kw_l2, std::false_type{});
                 features();
@@ -685,13 +723,12 @@ la_out_kernel(const FwdArgs a)
         if (ragged) {
             if (c_full > c_beg) {
                 load_chunk(c_full, std::true_type{});
+                cb ^= 1;
                 d = book(n_tail);
-                stage_x(n_tail, std::true_type{});
+                stage_x(n_tail, cb, std::true_type{});
+                if constexpr (RF) __syncthreads();
                 stage(n_tail, d.kw_l2, std::true_type{});
-                if constexpr (RF) {
-                    __syncthreads();
-                    features();
-                }
+                features();
             }
             __syncthreads();
             compute(n_tail, c_full * C, d.dscale, d.do_rescale, d.rescale, std::true_type{});
