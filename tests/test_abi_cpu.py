@@ -264,3 +264,31 @@ def test_noalloc_forward_host_validation(lib, monkeypatch):
     st = call(_shape(B=4, H=256, N=256, dk=128, dv=128))
     assert st == la.binding.LA_ERR_WORKSPACE, la.la_last_error()
     assert "static scratch" in la.la_last_error()
+
+
+def test_random_features_m256_scope(lib):
+    """m = 256 (F = 512) runs the causal forward as two halves of 256 features:
+    its workspace holds one half's segment states plus one float per output
+    element and per row for the numerators and denominators handed from the
+    first half to the second.  Every other entry point, and fp32 inputs or
+    heads other than d_k = d_v = 64, refuse it on the host."""
+    rf256 = LaPhiC(la.LA_PHI_TRIG_RF, 256, FAKE, 0.125)
+    rf128 = LaPhiC(la.LA_PHI_TRIG_RF, 128, FAKE, 0.125)
+    s = _shape(B=1, H=2, N=4096)
+    ws256 = lib.la_workspace_size(ctypes.byref(s), ctypes.byref(rf256), 1)
+    ws128 = lib.la_workspace_size(ctypes.byref(s), ctypes.byref(rf128), 1)
+    assert ws256 >= ws128 + 2 * 4096 * (64 + 1) * 4
+    sv = _shape(B=2, H=2, N=4096)
+    assert lib.la_workspace_size_varlen(ctypes.byref(sv), 2048, ctypes.byref(rf256)) >= 2 * 4096 * (64 + 1) * 4
+    assert lib.la_workspace_size(ctypes.byref(s), ctypes.byref(rf256), 0) == 0          # non-causal
+    assert lib.la_workspace_size(ctypes.byref(_shape(dk=128, dv=128)), ctypes.byref(rf256), 1) == 0
+    assert lib.la_workspace_size(ctypes.byref(_shape(dv=128)), ctypes.byref(rf256), 1) == 0
+    assert lib.la_workspace_size(ctypes.byref(_shape(it=la.LA_F32)), ctypes.byref(rf256), 1) == 0
+    U = la.binding.LA_ERR_UNSUPPORTED
+    s1 = _shape(N=1)
+    st = lib.la_decode_step(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                            FAKE + 0x500000, ctypes.byref(s1), ctypes.byref(rf256), None, 1e-6, None)
+    assert st == U
+    st = lib.la_forward_noncausal(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, ctypes.byref(s),
+                                  ctypes.byref(rf256), 1e-6, None, 0, None)
+    assert st == U

@@ -130,3 +130,45 @@ def test_feature_map_decode_matches_forward_trajectory(phi, m, dk):
     ref, kap = oracle.causal(cat["q"], cat["k"], cat["v"], lam, wl.eps, phi, omega, wl.qk_scale,
                              want_kappa=True)
     _check_rows(y, ref[:, :, wl.N:], kap[:, :, wl.N:], "bf16")
+
+
+@pytest.mark.parametrize("phi,dv,N,out_f32", [("trig_rf", 64, 700, False), ("trig_rf_softmax", 64, 333, False),
+                                             ("trig_rf", 64, 4133, True)])
+def test_random_features_m256_causal(phi, dv, N, out_f32):
+    # m = 256 (F = 512) runs as two halves of 128 directions; the second adds
+    # the first's numerators and denominators.  Several segments at N = 4133.
+    wl = si.workload(5).with_(phi=phi, m=256, dv=dv)
+    inp = si.make_inputs(wl, B=1, H=2, N=N)
+    lam = [0.97, 1.0]
+    y, S, z = run_causal(wl, inp, lam=lam, out_f32=out_f32, want_state=True)
+    ref, kap = oracle_causal(wl, inp, lam=lam, want_kappa=True)
+    _check_rows(y, ref, kap, "bf16")
+    _, Sr, zr = oracle_causal(wl, inp, lam=lam, want_state=True)
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(zr).max())
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(Sr).max())
+
+
+def test_random_features_m256_state_in_and_varlen():
+    # carried-in state (both halves read their rows of S_in, z_in) and packed
+    # sequences (the stored numerators are indexed by packed row)
+    wl = si.workload(5).with_(m=256)
+    inp = si.make_inputs(wl, B=1, H=2, N=600)
+    lam = [0.99, 0.9]
+    cut = lambda sl: {n: (np.ascontiguousarray(x[:, :, sl]) if n in ("q", "k", "v", "q_bits", "k_bits", "v_bits")
+                          else x) for n, x in inp.items()}
+    _, S0, z0 = run_causal(wl, cut(slice(0, 200)), lam=lam, want_state=True)
+    rest = cut(slice(200, None))
+    y = run_causal(wl, rest, lam=lam, S_in=S0, z_in=z0)
+    ref, kap = oracle_causal(wl, inp, lam=lam, want_kappa=True)
+    _check_rows(y, ref[:, :, 200:], kap[:, :, 200:], "bf16")
+    # packed: two sequences of 250 and 350 tokens in head rows of 600
+    q, k, v = (to_dev(inp, n, "bf16")[0] for n in ("q", "k", "v"))
+    cu = torch.tensor([0, 250, 600], dtype=torch.int32, device=DEV)
+    yv = torch.empty(2, 600, wl.dv, dtype=torch.bfloat16, device=DEV)
+    la.la_forward_causal_varlen(q, k, v, yv, cu, 350, phi=phi_for(wl, inp["omega"]), lambda_h=lam, eps=wl.eps)
+    torch.cuda.synchronize()
+    for s0, s1 in ((0, 250), (250, 600)):
+        part = {n: inp[n][:, :, s0:s1] for n in ("q", "k", "v")}
+        refp, kapp = oracle.causal(part["q"], part["k"], part["v"], np.asarray(lam), wl.eps, wl.phi, inp["omega"],
+                                   wl.qk_scale, want_kappa=True)
+        _check_rows(yv[None, :, s0:s1], refp, kapp, "bf16")

@@ -24,7 +24,7 @@ import torch
 import oracle
 import seeded_inputs as si
 import weight_sequence_mixing_amd as la
-from gpu_util import DEV, TOL, oracle_causal, rel_err, row_errors, run_causal
+from gpu_util import DEV, TOL, check_kappa_rows, oracle_causal, rel_err, row_errors, run_causal
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,22 @@ def test_workload5_full_every_head():
     print("largest kappa %.1f; per-head max:" % float(kap.max()),
           " ".join("%.2e" % e for e in err.reshape(wl.H, -1).max(axis=1)), flush=True)
     assert np.isfinite(err).all()
-    assert float(err.max()) < TOL["bf16"], float(err.max())
-    rel_err(y, ref)
+    check_kappa_rows(y, ref, kap, "bf16")
+
+
+def test_workload5_m256_full_sampled_heads():
+    # the m sweep's last point at workload 5's size (two halves of 128
+    # directions); all 16 heads run, four are compared (every row of each)
+    wl = si.workload(5).with_(m=256)
+    inp = si.make_inputs(wl)
+    y = run_causal(wl, inp).float().cpu().numpy()
+    heads = [0, 5, 10, 15]
+    sub = dict(inp, q=inp["q"][:, heads], k=inp["k"][:, heads], v=inp["v"][:, heads], lam=inp["lam"][heads])
+    ref, kap = oracle_causal(wl, sub, want_kappa=True)
+    err = row_errors(y[:, heads], ref)
+    _report(wl.name + "_m256_heads0-5-10-15", err)
+    assert np.isfinite(err).all()
+    check_kappa_rows(y[:, heads], ref, kap, "bf16")
 
 
 def _bits_to_dev(bits):

@@ -136,9 +136,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 }
 
 // Shape and feature-map checks shared by every entry point.  On success sets
-// F and the kernel table entry.
+// F and the kernel table entry.  split_ok: the caller runs a map of F = 512
+// (m = 256 random features, bf16, d_k = 64) as two halves of 256 features;
+// the entry is then that of one half.
 la_status check_shape(const la_shape* s, const la_phi* phi, int64_t min_n, int64_t max_n,
-                      int* F_out, const KernelEntry** entry_out)
+                      int* F_out, const KernelEntry** entry_out, bool split_ok = false)
 {
     if (!s) return fail(LA_ERR_INVALID_ARGUMENT, "shape is NULL");
     if (!phi) return fail(LA_ERR_INVALID_ARGUMENT, "phi is NULL");
@@ -167,8 +169,19 @@ la_status check_shape(const la_shape* s, const la_phi* phi, int64_t min_n, int64
         if (!aligned16(phi->omega)) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be 16-byte aligned");
         if (!std::isfinite(phi->qk_scale) || phi->qk_scale <= 0.f)
             return fail(LA_ERR_INVALID_ARGUMENT, "qk_scale must be finite and > 0");
+        if (phi->m == 256) {
+            if (!split_ok || s->in_dtype != LA_BF16 || s->d_k != 64 || s->d_v != 64)
+                return fail(LA_ERR_UNSUPPORTED,
+                            "m=256 random features are supported by the causal forward with bf16 inputs and "
+                            "d_k = d_v = 64");
+            const KernelEntry* e = find_entry(s->in_dtype, LA_PHI_TRIG_RF, s->d_k, 256, s->d_v);
+            if (!e) return fail(LA_ERR_UNSUPPORTED, "no kernel for m=256 halves with d_v=%d", s->d_v);
+            *F_out = 512;
+            *entry_out = e;
+            return LA_OK;
+        }
         if (phi->m != 32 && phi->m != 64 && phi->m != 128)
-            return fail(LA_ERR_UNSUPPORTED, "m=%d: supported random-feature counts are 32, 64, 128", phi->m);
+            return fail(LA_ERR_UNSUPPORTED, "m=%d: supported random-feature counts are 32, 64, 128, 256", phi->m);
         if ((int64_t)s->d_k * phi->m > 8192) return fail(LA_ERR_UNSUPPORTED, "d_k * m must be <= 8192");
         F = 2 * phi->m;
     } else {
@@ -447,15 +460,26 @@ la_status la_init_state_identity(float* S, float* z, int64_t B, int64_t H, int32
     return ok();
 }
 
+// Features per launch: a map of F > 256 runs as two halves.
+int half_features(int F) { return F > 256 ? F / 2 : F; }
+
+// Bytes of the numerators and denominators one half of a split map leaves
+// for the other: `rows` rows of d_v + 1 floats.
+size_t split_bytes(const la_shape* s, int F, int64_t rows)
+{
+    return F > 256 ? bytes256((size_t)rows * (s->d_v + 1) * sizeof(float)) : 0;
+}
+
 size_t la_workspace_size(const la_shape* shape, const la_phi* phi, int32_t causal)
 {
     int F = 0;
     const KernelEntry* e = nullptr;
     const std::string saved = g_last_error;
-    const la_status st = check_shape(shape, phi, causal ? 0 : 1, INT64_MAX / 4, &F, &e);
+    const la_status st = check_shape(shape, phi, causal ? 0 : 1, INT64_MAX / 4, &F, &e, causal != 0);
     g_last_error = saved;
     if (st != LA_OK || shape->N == 0) return 0;
-    return make_plan(shape, F, e, causal != 0).ws_bytes;
+    return make_plan(shape, half_features(F), e, causal != 0).ws_bytes +
+           split_bytes(shape, F, shape->B * shape->H * shape->N);
 }
 
 namespace {
@@ -474,8 +498,11 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
 {
     int F = 0;
     const KernelEntry* ent = nullptr;
-    la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &ent);
+    la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &ent, true);
     if (st != LA_OK) return st;
+    // a map of F = 512 runs as two halves of Fh features; the first leaves its
+    // numerators and denominators, the second adds them in
+    const int Fh = half_features(F), nhalf = F / Fh;
     if ((S_in == nullptr) != (z_in == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_in and z_in must be given together");
     if ((S_out == nullptr) != (z_out == nullptr)) return fail(LA_ERR_INVALID_ARGUMENT, "S_out and z_out must be given together");
     if ((S_in && (!aligned16(S_in) || !aligned16(z_in))) || (S_out && (!aligned16(S_out) || !aligned16(z_out))))
@@ -518,7 +545,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
     if (use_scratch) {
         // segment states of P segments: P slots of BH states; a window carry
         // (LA_WINDOWS > 1) one more slot that must fit on its own
-        const size_t slot = (size_t)BH * ((size_t)F * shape->d_v + F) * sizeof(float);
+        const size_t slot = (size_t)BH * ((size_t)Fh * shape->d_v + Fh) * sizeof(float);
         const Plan p1 = make_plan(shape, F, ent, true, 0, 1);
         const size_t carry = p1.W > 1 ? slot : 0;
         if (carry > kScratchBytes)
@@ -527,7 +554,11 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
         max_P = (int64_t)((kScratchBytes - carry) / slot);
         if (max_P < 1) max_P = 1;
     }
-    Plan plan = make_plan(shape, F, ent, true, vP, max_P);
+    Plan plan = make_plan(shape, Fh, ent, true, vP, max_P);
+    const size_t seg_bytes = plan.ws_bytes;
+    const size_t item_bytes = cu ? bytes256((size_t)vG * sizeof(int32_t)) : 0;
+    const int64_t rows = cu ? shape->H * shape->N : BH * shape->N;  // rows of y
+    plan.ws_bytes = seg_bytes + item_bytes + split_bytes(shape, F, rows);
     if (use_scratch) {
         if (plan.ws_bytes > kScratchBytes)
             return fail(LA_ERR_WORKSPACE, "the plan needs %zu bytes; the static scratch holds %zu", plan.ws_bytes,
@@ -539,10 +570,10 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             if (se != hipSuccess) return hip_fail(se, "static scratch address");
         }
     }
-    const size_t seg_bytes = plan.ws_bytes;
-    if (cu) plan.ws_bytes = seg_bytes + bytes256((size_t)vG * sizeof(int32_t));  // + the item table
     if ((st = check_ws(plan, workspace, workspace_bytes)) != LA_OK) return st;
     int32_t* items = cu ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + seg_bytes) : nullptr;
+    float* part_num = nhalf > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + seg_bytes + item_bytes)
+                                : nullptr;
 
     float* ws = static_cast<float*>(workspace);
     float* segs = ws;                                                     // [P][BH][SZ]
@@ -562,12 +593,26 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
     a.eps = eps;
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
     a.rf_sign = rf_sign(phi->kind);
-    a.omega = phi->omega;
+    a.rf_scale = is_rf(phi->kind) ? 1.f / std::sqrt((float)phi->m) : 0.f;
+    a.part_num = part_num;
+    a.part_den = part_num ? part_num + rows * shape->d_v : nullptr;
     a.kpm = kpm;
     a.kpm_stride = shape->N;
     a.cu_seqlens = cu;
     a.lam = lam;
 
+    for (int half = 0; half < nhalf; ++half) {
+    // this half's rows of omega and of the caller's states
+    a.omega = phi->omega ? phi->omega + (size_t)half * (Fh / 2) * shape->d_k : nullptr;
+    a.part_mode = nhalf > 1 ? 1 + half : 0;
+    // the caller's rows of a half: its cos rows at (Fh/2) half, its sin rows
+    // F/2 further (a gap of Fh/2 rows after the half's first Fh/2)
+    const size_t sh = (size_t)half * (Fh / 2) * shape->d_v, zh = (size_t)half * (Fh / 2);
+    const int32_t gap = nhalf > 1 ? Fh / 2 : 0;
+    const float* S_in_h = S_in ? S_in + sh : nullptr;
+    const float* z_in_h = z_in ? z_in + zh : nullptr;
+    float* S_out_h = S_out ? S_out + sh : nullptr;
+    float* z_out_h = z_out ? z_out + zh : nullptr;
     for (int w = 0; w < plan.W; ++w) {
         const int64_t c0 = (int64_t)w * NC / plan.W, c1 = (int64_t)(w + 1) * NC / plan.W;
         const int64_t n0 = c0 * plan.C, n_len = std::min(c1 * plan.C, shape->N) - n0;
@@ -590,18 +635,19 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
         const float* Si = nullptr;
         const float* zi = nullptr;
         int64_t si_stride = 0, zi_stride = 0;
+        int32_t si_gap = 0, so_gap = 0;
         if (w == 0) {
-            Si = S_in; zi = z_in; si_stride = (int64_t)F * shape->d_v; zi_stride = F;
+            Si = S_in_h; zi = z_in_h; si_stride = (int64_t)F * shape->d_v; zi_stride = F; si_gap = gap;
         } else {
-            Si = carry; zi = carry + (int64_t)F * shape->d_v; si_stride = plan.SZ; zi_stride = plan.SZ;
+            Si = carry; zi = carry + (int64_t)Fh * shape->d_v; si_stride = plan.SZ; zi_stride = plan.SZ;
         }
         float* So = nullptr;
         float* zo = nullptr;
         int64_t so_stride = 0, zo_stride = 0;
         if (w == plan.W - 1) {
-            So = S_out; zo = z_out; so_stride = (int64_t)F * shape->d_v; zo_stride = F;
+            So = S_out_h; zo = z_out_h; so_stride = (int64_t)F * shape->d_v; zo_stride = F; so_gap = gap;
         } else {
-            So = carry; zo = carry + (int64_t)F * shape->d_v; so_stride = plan.SZ; zo_stride = plan.SZ;
+            So = carry; zo = carry + (int64_t)Fh * shape->d_v; so_stride = plan.SZ; zo_stride = plan.SZ;
         }
         a.n0 = n0;
         a.n_len = n_len;
@@ -613,7 +659,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             // pass 1: segment-local states
             FwdArgs l = a;
             l.S_dst = segs;
-            l.z_dst = segs + (int64_t)F * shape->d_v;
+            l.z_dst = segs + (int64_t)Fh * shape->d_v;
             l.dst_stride = plan.SZ;
             l.dst_zstride = plan.SZ;
             if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
@@ -625,7 +671,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             sa.P = P;
             sa.BH = (int32_t)BH;
             sa.H = (int32_t)shape->H;
-            sa.F = F;
+            sa.F = Fh;
             sa.DV = shape->d_v;
             sa.n_len = n_len;
             sa.seg_len = cps * plan.C;
@@ -634,13 +680,15 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             sa.N = shape->N;
             sa.S_init = Si; sa.z_init = zi; sa.init_stride = si_stride; sa.init_zstride = zi_stride;
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
+            sa.init_gap = si_gap;
+            sa.fin_gap = so_gap;
             sa.lam = lam;
             if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
                 return hip_fail(e, "segment scan launch");
             // pass 3: outputs from the carried-in state of each segment
             FwdArgs c = a;
             c.S_src = segs;
-            c.z_src = segs + (int64_t)F * shape->d_v;
+            c.z_src = segs + (int64_t)Fh * shape->d_v;
             c.src_stride = plan.SZ;
             c.src_zstride = plan.SZ;
             c.src_seg_stride = BH * plan.SZ;
@@ -650,10 +698,13 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             FwdArgs c = a;
             c.S_src = Si; c.z_src = zi; c.src_stride = si_stride; c.src_zstride = zi_stride;
             c.src_seg_stride = 0;
+            c.src_gap = si_gap;
             c.S_dst = So; c.z_dst = zo; c.dst_stride = so_stride; c.dst_zstride = zo_stride;
+            c.dst_gap = so_gap;
             if ((e = launch(LA_KERNEL_FWD_CAUSAL, [&] { return ent->fwd(c, MODE_CAUSAL, strm); })) != hipSuccess)
                 return hip_fail(e, "causal launch");
         }
+    }
     }
     return ok();
 }
@@ -693,14 +744,15 @@ size_t la_workspace_size_varlen(const la_shape* shape, int64_t max_seqlen, const
     int F = 0;
     const KernelEntry* e = nullptr;
     const std::string saved = g_last_error;
-    const la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &e);
+    const la_status st = check_shape(shape, phi, 0, INT64_MAX / 4, &F, &e, true);
     g_last_error = saved;
     if (st != LA_OK || shape->N == 0 || max_seqlen < 0 || max_seqlen > shape->N) return 0;
     int P = 1;
     int64_t cps = 1;
     varlen_segments(shape->N, shape->B, shape->H, max_seqlen, e->C, &P, &cps);
     const int64_t G = varlen_items_bound(shape->N, shape->B, e->C, cps, P);
-    return make_plan(shape, F, e, true, P).ws_bytes + bytes256((size_t)G * sizeof(int32_t));
+    return make_plan(shape, half_features(F), e, true, P).ws_bytes + bytes256((size_t)G * sizeof(int32_t)) +
+           split_bytes(shape, F, shape->H * shape->N);
 }
 
 la_status la_forward_causal_varlen(const void* q, const void* k, const void* v, void* y,
@@ -755,6 +807,7 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     a.eps = eps;
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
     a.rf_sign = rf_sign(phi->kind);
+    a.rf_scale = is_rf(phi->kind) ? 1.f / std::sqrt((float)phi->m) : 0.f;
     a.omega = phi->omega;
     make_lam(nullptr, shape->H, &a.lam);  // no decay in the non-causal form
 
@@ -837,6 +890,7 @@ la_status la_forward_cross(const void* q, const void* k, const void* v, void* y,
     a.eps = eps;
     a.qk_scale = is_rf(phi->kind) ? phi->qk_scale : 1.0f;
     a.rf_sign = rf_sign(phi->kind);
+    a.rf_scale = is_rf(phi->kind) ? 1.f / std::sqrt((float)phi->m) : 0.f;
     a.omega = phi->omega;
     make_lam(nullptr, shape->H, &a.lam);  // no decay in the non-causal form
     a.chunk = plan.C;

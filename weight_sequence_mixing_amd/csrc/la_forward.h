@@ -567,7 +567,7 @@ la_fwd_kernel(const FwdArgs a)
     // written row-major into the feature tiles
     auto rf_features = [&](int n, float kw_l2) LA_INLINE {
         if constexpr (RF) {
-            const float cnorm = rsqrtf((float)M);
+            const float cnorm = a.rf_scale;
             constexpr int NPASS = (Cfg::NEED_Q ? 1 : 0) + (Cfg::NEED_K ? 1 : 0);
             const int i = 16 * (wave % QB) + l16;  // this lane's token
 #pragma unroll

@@ -47,8 +47,18 @@ struct FwdArgs {
     int32_t out_f32;  // 1: y is fp32, 0: y has the input type
     float eps;
     float qk_scale;
-    // random features: sign s of the prefactor exp(s |x'|^2 / 2) / sqrt(m)
+    // random features: sign s of the prefactor exp(s |x'|^2 / 2) / sqrt(m),
+    // and its scale 1 / sqrt(m) (m of the whole map: a launch may cover half
+    // of the features)
     float rf_sign;
+    float rf_scale;
+    // causal output over one half of the features (random features with
+    // m = 256): 1 stores each row's numerator and denominator (fp32, at
+    // part_num + row * d_v and part_den + row, rows indexed as y), 2 adds the
+    // stored ones to its own before the division; 0 = a whole map
+    int32_t part_mode;
+    float* part_num;
+    float* part_den;
     const float* omega;  // [m, d_k] fp32 (random features) or null
     // key padding mask: byte kpm[b * kpm_stride + n0 + t] nonzero drops key t
     // of batch b from every sum; null = no mask
@@ -72,6 +82,10 @@ struct FwdArgs {
     int64_t src_stride;
     int64_t src_zstride;
     int64_t src_seg_stride;
+    // rows f >= F/2 of S_src, z_src (S_dst, z_dst) sit src_gap (dst_gap) rows
+    // further: one half of a split random-feature map in the caller's layout
+    // (its cos and its sin rows); 0 elsewhere
+    int32_t src_gap, dst_gap;
     // final state (MODE_CAUSAL, optional) or segment-local state (MODE_LOCAL):
     // written at S_dst + (seg*BH + bh)*dst_stride (MODE_LOCAL) or
     // S_dst + bh*dst_stride (MODE_CAUSAL), z likewise.
@@ -99,6 +113,9 @@ struct ScanArgs {
     float* S_fin;            // final state (causal) or null
     float* z_fin;
     int64_t fin_stride, fin_zstride;
+    // rows f >= F/2 of S_init, z_init (S_fin, z_fin) sit init_gap (fin_gap)
+    // rows further (as FwdArgs src_gap)
+    int32_t init_gap, fin_gap;
     // 1: visit the segments last to first (the adjoint state of the backward
     // pass, carried from the end of the sequence towards its start)
     int32_t reverse;

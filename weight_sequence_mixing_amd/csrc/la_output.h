@@ -293,11 +293,12 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
         for (int u = 0; u < FBW; ++u) {
             const int f0 = 16 * (FBW * qw + u) + 4 * g;
+            const int fr = f0 + (f0 >= F / 2 ? a.src_gap : 0);  // row in the source's layout
 #pragma unroll
             for (int c = 0; c < DBQ; ++c)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) accS[u][c][r] = Sb[(int64_t)(f0 + r) * DV + 16 * (dq0 + c) + l16];
-            accZ[u] = *(const f32x4*)(zb + f0);
+                for (int r = 0; r < 4; ++r) accS[u][c][r] = Sb[(int64_t)(fr + r) * DV + 16 * (dq0 + c) + l16];
+            accZ[u] = *(const f32x4*)(zb + fr);
         }
     }
     // this wave's rows into the shared S^T and z (bf16, permuted features)
@@ -403,7 +404,7 @@ la_out_kernel(const FwdArgs a)
     // of the sequence or masked is dropped: its row is staged as zeros (finite
     // features whatever its values) and its prefactor is zero.
     const float rf_cexp = 0.5f * a.rf_sign * a.qk_scale * a.qk_scale;
-    const float rf_cnorm = RF ? rsqrtf((float)M) : 0.f;
+    const float rf_cnorm = a.rf_scale;
     auto stage_x = [&](int n, int buf, auto tail_c) LA_INLINE {
         if constexpr (RF) {
             constexpr bool TAIL = decltype(tail_c)::value;
@@ -550,12 +551,20 @@ la_out_kernel(const FwdArgs a)
             mma(rs, ones, pf[kb]);
         }
         // y_i = c_i (o + o_i) / (c_i den + eps) with c_i the query's
-        // prefactor (random features), else y_i = (o + o_i) / (den + eps)
+        // prefactor (random features), else y_i = (o + o_i) / (den + eps).
+        // Over half of the features (part_mode 1, 2) the numerator and the
+        // denominator of the other half are stored, or added in.
         const float lqd = lq * dscale;
         const float cq = RF ? sCF0[cb * 2 * C + i] : 1.f;
-        const float inv0 = fast_rcp(cq * (rs[0] + lqd * dq[0]) + a.eps);
+        const int64_t yrow = row0 + t0 + i;
+        const bool live = !TAIL || i < n;  // rows past the end are neither read nor stored
+        const int pmode = RF ? a.part_mode : 0;
+        const float den = cq * (rs[0] + lqd * dq[0]);
+        const float den1 = (pmode == 2 && live) ? a.part_den[yrow] : 0.f;
+        const float inv0 = pmode == 1 ? 1.f : fast_rcp(den + den1 + a.eps);
         const float inv = RF ? cq * inv0 : inv0;
         const float sc = lqd * inv;
+        if (pmode == 1 && live && dq0 == 0 && g == 0) a.part_den[yrow] = den;
         // B operands of the z update: the chunk's key weights where they are
         // not in the key features, else ones
         Frag<T> wf[CB];
@@ -598,7 +607,6 @@ la_out_kernel(const FwdArgs a)
         // V^T P^T; the value fragments of a column tile are the A operands of
         // V^T P^T and (weighted where the weights are on the values) the B
         // operands of the state update
-        const int64_t yrow = row0 + t0 + i;
         Frag<T> vwf[KEYS_FIRST ? 1 : DBQ][CB];
 #pragma unroll
         for (int tq = 0; tq < DBQ; ++tq) {
@@ -616,11 +624,16 @@ la_out_kernel(const FwdArgs a)
             }
 #pragma unroll
             for (int kb = 0; kb < CB; ++kb) mma(oi, vf[kb], pf[kb]);
-            const f32x4 y = ot * sc + oi * inv;
-            if (!TAIL || i < n) {
+            f32x4 y = ot * sc + oi * inv;
+            if (live) {
                 const int64_t yo = yrow * DV + 16 * t + 4 * g;
-                if constexpr (OUTF32) st4((float*)a.y + yo, y[0], y[1], y[2], y[3]);
-                else st4((T*)a.y + yo, y[0], y[1], y[2], y[3]);
+                if (pmode == 1) {
+                    st4(a.part_num + yo, y[0], y[1], y[2], y[3]);
+                } else {
+                    if (pmode == 2) y += *(const f32x4*)(a.part_num + yo) * inv0;
+                    if constexpr (OUTF32) st4((float*)a.y + yo, y[0], y[1], y[2], y[3]);
+                    else st4((T*)a.y + yo, y[0], y[1], y[2], y[3]);
+                }
             }
             const int vs = KEYS_FIRST ? 0 : tq;
 #pragma unroll
@@ -743,11 +756,12 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
         for (int u = 0; u < FBW; ++u) {
             const int f0 = 16 * (FBW * qw + u) + 4 * g;
+            const int fr = f0 + (f0 >= F / 2 ? a.dst_gap : 0);  // row in the destination's layout
 #pragma unroll
             for (int c = 0; c < DBQ; ++c)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sd[(int64_t)(f0 + r) * DV + 16 * (dq0 + c) + l16] = ds * accS[u][c][r];
-            if (zowner && l16 == 0) *(f32x4*)(zd + f0) = accZ[u] * ds;
+                for (int r = 0; r < 4; ++r) Sd[(int64_t)(fr + r) * DV + 16 * (dq0 + c) + l16] = ds * accS[u][c][r];
+            if (zowner && l16 == 0) *(f32x4*)(zd + fr) = accZ[u] * ds;
         }
     }
 }

@@ -55,9 +55,15 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
     // segments holding tokens (the last of the P takes the remainder)
     const int nseg = (int)min((n_len + a.seg_len - 1) / a.seg_len, (int64_t)a.P);
     f32x4 carry = zero;
+    // the caller's layout may hold the upper half of the rows further on
+    const int half_rows = a.F / 2;
+    const int ei = isz ? ez + (ez >= half_rows ? a.init_gap : 0)
+                       : e + (e >= half_rows * a.DV ? a.init_gap * a.DV : 0);
+    const int ef = isz ? ez + (ez >= half_rows ? a.fin_gap : 0)
+                       : e + (e >= half_rows * a.DV ? a.fin_gap * a.DV : 0);
     if (a.S_init)
-        carry = isz ? *(const f32x4*)(a.z_init + bh * a.init_zstride + ez)
-                    : *(const f32x4*)(a.S_init + bh * a.init_stride + e);
+        carry = isz ? *(const f32x4*)(a.z_init + bh * a.init_zstride + ei)
+                    : *(const f32x4*)(a.S_init + bh * a.init_stride + ei);
     // reverse: the segments are visited last to first (the carry enters a
     // segment at its end)
     for (int s0 = 0; s0 < nseg; s0 += kScanBatch) {
@@ -78,8 +84,8 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
         }
     }
     if (a.S_fin) {
-        if (isz) *(f32x4*)(a.z_fin + bh * a.fin_zstride + ez) = carry;
-        else *(f32x4*)(a.S_fin + bh * a.fin_stride + e) = carry;
+        if (isz) *(f32x4*)(a.z_fin + bh * a.fin_zstride + ef) = carry;
+        else *(f32x4*)(a.S_fin + bh * a.fin_stride + ef) = carry;
     }
 }
 
