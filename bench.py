@@ -125,10 +125,18 @@ def causal_bytes(B, H, N, dk, dv, in_bytes, out_bytes):
 
 
 def kernel_alg_bytes(kid, la, B, H, N, dk, dv, F, P, in_bytes=2, out_bytes=2):
+    """Algorithmic bytes of one launch.  A map of F > 256 features runs each
+    pass twice, over halves of F: the output launches also hand d_v + 1 fp32
+    values per row from the first half to the second (the mean of the two
+    launches is returned)."""
     ids = la.KERNEL_IDS
     rows = B * H * N
+    split = F > 256
+    F = F // 2 if split else F
     SZ = F * dv + F
     if kid == ids["fwd_causal"]:
+        if split:
+            return rows * ((2 * dk + dv) * in_bytes + (dv + 1) * 4 + dv * out_bytes / 2)
         return rows * ((2 * dk + dv) * in_bytes + dv * out_bytes)
     if kid == ids["fwd_local"]:
         return rows * (dk + dv) * in_bytes + P * B * H * SZ * 4
@@ -160,14 +168,17 @@ def bench_causal(ctx, name, B, H, N, dk, dv, lam, phi, gen, steps=None, planned_
     # dominant kernel by total device time per step
     dom = max(kt.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
     dom_ms = kt[dom][0]
-    # segments actually used: infer from the workspace (states of P segments)
+    # segments actually used: infer from the workspace (states of P segments
+    # of one half of F for F > 256, beside the rows handed between halves)
     if ws_n:
-        P = max(1, int(round(ws_n / (B * H * (F * dv + F) * 4))))
+        Fh = F // 2 if F > 256 else F
+        hand = B * H * N * (dv + 1) * 4 if F > 256 else 0
+        P = max(1, int(round((ws_n - hand) / (B * H * (Fh * dv + Fh) * 4))))
     alg = kernel_alg_bytes(dom, la, B, H, N, dk, dv, F, P)
     achieved = alg / (dom_ms * 1e-3) / 1e9
     step_bytes = causal_bytes(B, H, N, dk, dv, 2, 2)
     flops_min = 4.0 * F * dv * B * H * N
-    C = 32  # tokens per chunk of every forward kernel
+    C = 64  # tokens per chunk of the bf16 causal output kernels (every score tile formed)
     flops_exec = flops_min + 2.0 * C * (F + dv) * B * H * N
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
     res = {
@@ -665,7 +676,8 @@ def state_copy(ctx, B=256, H=32, F=128, D=128, steps=50):
 # scaled by what they read for the library's state copy, whose bytes are known.
 COUNTER_TAGS = {"copy": None, "w2": 2, "w3": 3, "w4": 4, "w5": 5,
                 "backward_w2": "elu1_backward_B4_H8_N4096_d64_bf16",
-                "rf_backward_w5": "trigrf_m128_backward_B1_H16_N65536_d64_bf16"}
+                "rf_backward_w5": "trigrf_m128_backward_B1_H16_N65536_d64_bf16",
+                "w5m256": "trigrf_m256_causal_B1_H16_N65536_d64_bf16"}
 
 
 def _kernel_label(mangled):
@@ -694,6 +706,8 @@ def _kernel_label(mangled):
         return "la_rf_vjp_kernel"
     if "la_scan_kernel" in mangled:
         return "la_scan_kernel"
+    if "la_out_kernel" in mangled:
+        return "causal output pass"
     if "la_fwd_kernel" in mangled:
         # the mode is the last int template argument (a bool, the output type,
         # follows it), mangled (...ELi1ELb0EEEvNS_7FwdArgsE) or demangled
@@ -704,8 +718,8 @@ def _kernel_label(mangled):
             args = [x.strip() for x in mangled.split(">(")[0].split(",")]
             ints = [x for x in args if x.lstrip("-").isdigit()]
             mode = ints[-1] if ints else ""
-        return {"0": "la_fwd_kernel (segment state)", "1": "la_fwd_kernel (causal output)",
-                "2": "la_fwd_kernel (non-causal output)"}.get(mode, "la_fwd_kernel")
+        return {"0": "segment state pass", "1": "causal output pass",
+                "2": "non-causal output pass"}.get(mode, "la_fwd_kernel")
     return None
 
 
@@ -805,7 +819,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", metavar="FILE", help="write every line's full record to FILE (JSON)")
-    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "copy", "scaling"] + [v[0] for v in VARIANTS] +
+    ap.add_argument("--only", choices=["w2", "w3", "w4", "w4multi", "w5", "w5m256", "copy", "scaling"] +
+                    [v[0] for v in VARIANTS] +
                     [v[0] for v in SHAPE_VARIANTS],
                     help="run one workload (profiling)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -824,6 +839,7 @@ def main():
     ctx = Ctx(args.steps, args.warmup)
     if args.only:
         fns = {"w2": workload2, "w3": lambda c: workload3_headline(c)[2], "w4": workload4_decode, "w5": workload5,
+               "w5m256": lambda c: workload5(c, m=256),
                "copy": state_copy, "w4multi": workload4_multi, "scaling": length_scaling}
         for key, base, phi, m, steps in VARIANTS:
             fns[key] = (lambda c, b=base, p=phi, mm=m, st=steps: feature_map_variant(c, b, p, mm, st))
@@ -852,7 +868,8 @@ def main():
         scaling = length_scaling(ctx)
         detail["length_scaling"] = scaling
         for key, fn in (("w2", workload2), ("decode_multi4_w4", workload4_multi),
-                        ("decode_multi16_w4", lambda c: workload4_multi(c, 16, 64)), ("w5", workload5)):
+                        ("decode_multi16_w4", lambda c: workload4_multi(c, 16, 64)), ("w5", workload5),
+                        ("rf_m256_w5", lambda c: workload5(c, m=256))):
             log(key, "...")
             extra[key] = fn(ctx)
             log(json.dumps(extra[key]))

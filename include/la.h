@@ -34,7 +34,12 @@
  *    surface at the caller's next synchronisation.
  *  - Support matrix: d_k, d_v in {64, 128}; random features with m in {32, 64,
  *    128} (F = 2m) and d_k * m <= 8192; in_dtype LA_BF16 or LA_F32; out_dtype
- *    equal to in_dtype or LA_F32.  Other valid shapes return LA_ERR_UNSUPPORTED.
+ *    equal to in_dtype or LA_F32.  m = 256 (F = 512, the last point of the
+ *    m sweep in "From standard attention to linear attention" sec. 7) is
+ *    supported by the causal forward entry points (fixed, masked, packed and
+ *    no-allocation) for bf16 inputs with d_k = d_v = 64: the library runs it as
+ *    two halves of 128 directions and the workspace also holds d_v + 1 floats
+ *    per output row.  Other valid shapes return LA_ERR_UNSUPPORTED.
  *  - H <= LA_MAX_HEADS; lambda_h values must lie in [0, 1] (0^0 is taken as 1);
  *    eps must be finite and >= 0.
  */
@@ -347,7 +352,9 @@ enum {
 };
 la_status la_profile_begin(int32_t max_launches);
 la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32_t* count);
-/* Name of a kernel id: the prefix of the device function's symbol. */
+/* Name of a kernel id: the device function's symbol prefix, or for the three
+ * forward passes, which run different kernels by shape, the pass ("segment
+ * state pass", "causal output pass", "non-causal output pass"). */
 const char* la_kernel_name(int32_t kernel_id);
 
 /* Static description of a status code. */

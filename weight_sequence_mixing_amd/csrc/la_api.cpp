@@ -416,9 +416,9 @@ la_status la_profile_end(int32_t* kernel_ids, float* ms, int32_t capacity, int32
 const char* la_kernel_name(int32_t id)
 {
     switch (id) {
-    case LA_KERNEL_FWD_LOCAL: return "la_fwd_kernel (segment state)";
-    case LA_KERNEL_FWD_CAUSAL: return "la_fwd_kernel (causal output)";
-    case LA_KERNEL_FWD_QUERY: return "la_fwd_kernel (non-causal output)";
+    case LA_KERNEL_FWD_LOCAL: return "segment state pass";
+    case LA_KERNEL_FWD_CAUSAL: return "causal output pass";
+    case LA_KERNEL_FWD_QUERY: return "non-causal output pass";
     case LA_KERNEL_SCAN: return "la_scan_kernel";
     case LA_KERNEL_DECODE: return "la_decode_kernel";
     case LA_KERNEL_FILL: return "la_fill_zero_kernel";
