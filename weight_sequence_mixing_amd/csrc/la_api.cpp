@@ -10,7 +10,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "la_internal.h"
@@ -79,6 +82,25 @@ hipError_t launch(int id, Fn&& fn)
 }
 
 }  // namespace
+
+int la::device_slots(const void* kernel, int threads)
+{
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cache;  // (kernel, device) -> slots
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(kernel, dev);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+        return 0;
+    const int slots = cus * (per_cu > 0 ? per_cu : 1);
+    cache[key] = slots;
+    return slots;
+}
 
 LaunchEvents& la::launch_events()
 {

@@ -268,6 +268,16 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Ar
     return hipGetLastError();
 }
 
+// Workgroups of `threads` threads of `kernel` resident at once on the current
+// device (compute units x workgroups per unit); 0 if the runtime cannot say.
+// Cached per kernel and device.
+int device_slots(const void* kernel, int threads);
+template <class K>
+int device_slots(K kernel, int threads)
+{
+    return device_slots(reinterpret_cast<const void*>(kernel), threads);
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // Work items of packed sequences: items[w] = b * P + s for the w-th
 // (sequence, segment) pair in order, -1 for w past the last (G entries).

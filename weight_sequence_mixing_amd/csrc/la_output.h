@@ -43,9 +43,9 @@
 // which halves the LDS tiles of the keys.
 //
 // Layouts.  phi(Q), phi(K) and the weighted phi(K) are staged in LDS as in
-// la_forward.h (TileL, swizzled 8-byte units); V and the raw q, k rows in
-// TileX, whose swizzle is conflict-free for transposing reads and staging
-// (la_device.h has the bank model).  S^T is [DV][F] bf16 with the
+// la_forward.h (TileL, swizzled 8-byte units); V in TileX, whose swizzle is
+// conflict-free for transposing reads and staging (la_device.h has the bank
+// model); the raw q, k rows padded by 16 bytes.  S^T is [DV][F] bf16 with the
 // feature order inside each 32-wide block permuted so that the 8 k positions
 // K(g) a lane needs (la_device.h) are contiguous: one 16-byte read per
 // fragment; the 16-byte units are XOR-swizzled by row (st_off).  z is kept
@@ -86,9 +86,11 @@ struct OutCfg {
     static constexpr int VEC = 8;        // bf16 per 16-byte vector
     static constexpr int VPRQ = DK / VEC, VPRV = DV / VEC;
     static constexpr int RQ = C * VPRQ / NT, RV = C * VPRV / NT;
-    // random features: raw q, k rows (TileL layout of width DK); omega row
-    // blocks per wave, each wave covering one of the two token matrices
-    static constexpr int KX = DK / 32;
+    // random features: raw q, k rows of XLD elements (16 bytes of padding:
+    // a row-fragment read of 16 rows is then conflict-free as a single 8-byte
+    // read); omega row blocks per wave, each wave covering one of the two
+    // token matrices
+    static constexpr int KX = DK / 32, XLD = DK + 8;
     static constexpr int RB = RF ? 2 * (M / 16) / NW : 0;
     static constexpr int TQ = C * F, TV = C * DV;  // elements of a tile
     static constexpr size_t OFF_Q = 0;
@@ -98,7 +100,7 @@ struct OutCfg {
     static constexpr size_t OFF_ST = OFF_V + size_t(TV) * 2;
     static constexpr size_t OFF_Z = OFF_ST + size_t(DV) * F * 2;
     static constexpr size_t OFF_X = OFF_Z + size_t(F) * 2;
-    static constexpr size_t OFF_CF = OFF_X + (RF ? size_t(2) * C * DK * 2 : 0);
+    static constexpr size_t OFF_CF = OFF_X + (RF ? size_t(2) * C * XLD * 2 : 0);
     // omega's operand fragments: [row block][k block][high, low][lane], 16 bytes
     static constexpr size_t OFF_OM = OFF_CF + (RF ? size_t(4) * C * 4 : 0);
     static constexpr size_t OFF_W = OFF_OM + (RF ? size_t(M / 16) * KX * 2 * 64 * 16 : 0);
@@ -126,7 +128,9 @@ __device__ __forceinline__ int st_off(int r, int u)
     else return r * F + ((u ^ ((r >> 1) & 7)) << 3);
 }
 
-template <int PHI, int DK, int F, int DV, bool OUTF32>
+// PART: 0 for a whole map; 1, 2 for the first and second half of a split
+// random-feature map (FwdArgs part_mode).
+template <int PHI, int DK, int F, int DV, bool OUTF32, int PART>
 __global__ void __launch_bounds__((OutCfg<PHI, DK, F, DV>::NT), 2)
 la_out_kernel(const FwdArgs a)
 {
@@ -136,12 +140,11 @@ la_out_kernel(const FwdArgs a)
     constexpr int KB = Cfg::KB, CB = Cfg::CB, DB = Cfg::DB, VEC = Cfg::VEC;
     constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
     constexpr bool RF = Cfg::RF, VW = Cfg::VW;
-    constexpr int M = Cfg::M, KX = Cfg::KX, RB = Cfg::RB;
+    constexpr int M = Cfg::M, KX = Cfg::KX, RB = Cfg::RB, XLD = Cfg::XLD;
     // phi(Q), phi(K) and the weighted phi(K) in TileL (row reads in the
-    // two-address form, 8-byte feature writes); V and the raw rows in TileX
+    // two-address form, 8-byte feature writes); V in TileX
     using TF = TileL<T, F>;
     using TVL = TileX<T, DV>;
-    using TXL = TileX<T, DK>;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
     T* const sQ = (T*)(smem + Cfg::OFF_Q);
@@ -150,7 +153,7 @@ la_out_kernel(const FwdArgs a)
     T* const sV = (T*)(smem + Cfg::OFF_V);
     T* const sST = (T*)(smem + Cfg::OFF_ST);
     T* const sZ = (T*)(smem + Cfg::OFF_Z);
-    T* const sX = (T*)(smem + Cfg::OFF_X);        // raw q rows, then raw k rows (C x DK tiles)
+    T* const sX = (T*)(smem + Cfg::OFF_X);        // raw q rows, then raw k rows ([C][XLD] each)
     // prefactors of those rows, two buffers by chunk parity: the next
     // chunk's are written while the current chunk's are still read
     float* const sCF0 = (float*)(smem + Cfg::OFF_CF);
@@ -416,9 +419,7 @@ la_out_kernel(const FwdArgs a)
                     const int j = (tid + r * NT) / VPRQ;
                     const bool drop = pass == 1 && ((TAIL && j >= n) || mk[r]);
                     const uint4 u = drop ? uint4{0u, 0u, 0u, 0u} : (pass ? rk[r] : rq[r]);
-                    T* const xt = sX + pass * C * DK;
-                    *(uint2*)(xt + TXL::off(j, cg * VEC)) = uint2{u.x, u.y};
-                    *(uint2*)(xt + TXL::off(j, cg * VEC + 4)) = uint2{u.z, u.w};
+                    *(uint4*)(sX + (pass * C + j) * XLD + cg * VEC) = u;
                     float x[VEC];
                     unpack16(u, x, (const T*)nullptr);
                     float s2 = 0.f;
@@ -436,7 +437,7 @@ la_out_kernel(const FwdArgs a)
     // row-major into phi(Q) or phi(K) (columns f and m + f)
     auto features = [&]() LA_INLINE {
         if constexpr (RF) {
-            const T* const xs = sX + xpass * C * DK;
+            const T* const xs = sX + xpass * C * XLD;
             T* const tile = xpass ? sK : sQ;
             Frag<T> om_hi[RB][KX], om_lo[RB][KX];
 #pragma unroll
@@ -452,7 +453,7 @@ la_out_kernel(const FwdArgs a)
                 const int j = 16 * tb + l16;
                 Frag<T> xf[KX];
 #pragma unroll
-                for (int kb = 0; kb < KX; ++kb) xf[kb] = lds_frag_row<T, DK, TXL>(xs, j, kb, g);
+                for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(xs, XLD, j, 32 * kb, g);
 #pragma unroll
                 for (int u = 0; u < RB; ++u) {
                     f32x4 acc = zero4;
@@ -558,7 +559,7 @@ la_out_kernel(const FwdArgs a)
         const float cq = RF ? sCF0[cb * 2 * C + i] : 1.f;
         const int64_t yrow = row0 + t0 + i;
         const bool live = !TAIL || i < n;  // rows past the end are neither read nor stored
-        const int pmode = RF ? a.part_mode : 0;
+        constexpr int pmode = PART;
         const float den = cq * (rs[0] + lqd * dq[0]);
         const float den1 = (pmode == 2 && live) ? a.part_den[yrow] : 0.f;
         const float inv0 = pmode == 1 ? 1.f : fast_rcp(den + den1 + a.eps);
@@ -772,10 +773,35 @@ hipError_t out_launch(const FwdArgs& a, hipStream_t stream)
     using Cfg = OutCfg<PHI, DK, F, DV>;
     static_assert(Cfg::FITS, "LDS budget");
     if (a.chunk % Cfg::C != 0) return hipErrorInvalidValue;  // segments must be whole chunks
-    const dim3 grid(a.cu_seqlens ? (unsigned)a.G : (unsigned)a.P, a.cu_seqlens ? (unsigned)a.H : (unsigned)a.BH),
+    // the halves of a split map: only the instance that can be one (m = 128
+    // directions per half, d_k = d_v = 64) has them
+    constexpr bool SPLIT = PHI == LA_PHI_TRIG_RF && F == 256 && DK == 64 && DV == 64;
+    auto kernel = a.out_f32 ? la_out_kernel<PHI, DK, F, DV, true, 0> : la_out_kernel<PHI, DK, F, DV, false, 0>;
+    if (a.part_mode != 0) {
+        if constexpr (SPLIT) {
+            if (a.part_mode == 1) kernel = la_out_kernel<PHI, DK, F, DV, false, 1>;
+            else kernel = a.out_f32 ? la_out_kernel<PHI, DK, F, DV, true, 2> : la_out_kernel<PHI, DK, F, DV, false, 2>;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    // More segments than workgroups resident at once: each workgroup takes k
+    // consecutive segments (their carried-in state is the first one's), so
+    // that the pass runs in one round of workgroups.
+    FwdArgs b = a;
+    if (!a.cu_seqlens && a.P > 1) {
+        const int slots = device_slots(kernel, Cfg::NT);
+        const int64_t wgs = (int64_t)a.P * a.BH;
+        const int k = slots > 0 ? (int)((wgs + slots - 1) / slots) : 1;
+        if (k > 1) {
+            b.P = (a.P + k - 1) / k;
+            b.cps = a.cps * k;
+            b.src_seg_stride = a.src_seg_stride * k;
+        }
+    }
+    const dim3 grid(b.cu_seqlens ? (unsigned)b.G : (unsigned)b.P, b.cu_seqlens ? (unsigned)b.H : (unsigned)b.BH),
         block(Cfg::NT);
-    if (a.out_f32) return launch_kernel(la_out_kernel<PHI, DK, F, DV, true>, grid, block, stream, a);
-    return launch_kernel(la_out_kernel<PHI, DK, F, DV, false>, grid, block, stream, a);
+    return launch_kernel(kernel, grid, block, stream, b);
 }
 
 }  // namespace la

@@ -322,14 +322,11 @@ __device__ __forceinline__ int rf_opaque_zero()
 template <class K>
 hipError_t rf_mf_launch(K kernel, const RfGradArgs& a, hipStream_t stream)
 {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kMfWaves * 64, 0);
-    if (e != hipSuccess) return e;
+    const int slots = device_slots(kernel, kMfWaves * 64);
+    if (slots <= 0) return hipErrorInvalidDevice;
     const int64_t tiles = (a.rows + 15) / 16;
     const int64_t want = (tiles + kMfWaves - 1) / kMfWaves;
-    const int64_t cap = (int64_t)cus * (per_cu > 1 ? per_cu : 1);
+    const int64_t cap = slots;
     const dim3 grid((unsigned)(want < cap ? want : cap)), block(kMfWaves * 64);
     return launch_kernel(kernel, grid, block, stream, a);
 }
