@@ -31,7 +31,7 @@ def test_profile_hooks_host_side(lib):
         la.la_profile_end()
     with pytest.raises(la.LaError):
         la.la_profile_begin(0)
-    assert la.la_kernel_name(1).startswith("la_fwd_kernel")
+    assert la.la_kernel_name(1) == "causal output pass"
     assert la.la_kernel_name(4) == "la_decode_kernel"
 
 
