@@ -56,7 +56,9 @@
 // tiles and S^T; the state's new S^T and z and the next chunk's tiles are
 // written after the second (for random features, the next chunk's raw rows
 // before it, as no wave reads them while computing).  The next chunk's q, k,
-// v are loaded into registers while the current one is computed.
+// v are loaded into registers while the current one is computed (for the
+// elementwise maps issued right after the previous staging, so that they
+// have the first barrier's wait too).
 #pragma once
 
 #include <type_traits>
@@ -717,10 +719,15 @@ la_out_kernel(const FwdArgs a)
             stage(n_tail, d.kw_l2, std::true_type{});
         }
         features();
+        // elementwise maps: the next chunk's loads go out as soon as this
+        // one is staged, before the barrier (random features keep them after
+        // it: their staging registers are live until the raw rows are staged)
+        constexpr bool EARLY = !RF;
+        if (EARLY && c_beg + 1 < c_full) load_chunk(c_beg + 1, std::false_type{});
         for (int64_t c = c_beg; c < c_full; ++c) {
             const bool next_full = c + 1 < c_full;
             __syncthreads();
-            if (next_full) load_chunk(c + 1, std::false_type{});
+            if (!EARLY && next_full) load_chunk(c + 1, std::false_type{});
             compute(C, c * C, d.dscale, d.do_rescale, d.rescale, std::false_type{});
             // raw rows of the next chunk: features() of this chunk read them
             // before the barrier above
@@ -732,6 +739,7 @@ la_out_kernel(const FwdArgs a)
                 d = book(C);
                 stage(C, d.kw_l2, std::false_type{});
                 features();
+                if (EARLY && c + 2 < c_full) load_chunk(c + 2, std::false_type{});
             }
         }
         if (ragged) {
