@@ -115,6 +115,8 @@ MASKED = [
     (1, {}, 2, 2, 300, "random", False),      # fp32
     (1, {"phi": "relu"}, 1, 2, 257, "random", True),
     (5, {"m": 64}, 1, 4, 700, "random", False),
+    (5, {"m": 128}, 1, 2, 1500, "random", True),   # F = 256: features in the output kernel
+    (5, {"m": 256}, 1, 2, 900, "right", True),     # two halves of 128 directions
 ]
 
 
@@ -192,6 +194,7 @@ VARLEN = [
     (3, {}, 3, (6, 700, 1), "exact", True),      # d = 128, per-head decay
     (1, {}, 2, (9, 300, 2), "exact", False),     # fp32
     (5, {"m": 64}, 2, (6, 1200, 1), "exact", False),
+    (5, {"m": 256}, 2, (5, 1500, 1), "exact", True),
 ]
 
 

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import weight_sequence_mixing_amd as la
-from gpu_util import DEV, TOL, inputs, oracle_causal, rel_err, to_dev
+from gpu_util import DEV, TOL, check_kappa_rows, inputs, oracle_causal, phi_for, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,12 +23,13 @@ def _both(wl, inp):
     q, k, v = (to_dev(inp, n, wl.dtype) for n in ("q", "k", "v"))
     B, H, N, _ = q.shape
     lam = list(map(float, inp["lam"]))
+    phi = phi_for(wl, inp.get("omega"))
     outs = []
     for fn in (la.la_forward_causal, la.la_forward_causal_noalloc):
         y = torch.full((B, H, N, wl.dv), float("nan"), dtype=torch.bfloat16, device=DEV)
         S = torch.full((B, H, wl.F, wl.dv), float("nan"), device=DEV)
         z = torch.full((B, H, wl.F), float("nan"), device=DEV)
-        fn(q, k, v, y, lambda_h=lam, eps=wl.eps, S_out=S, z_out=z)
+        fn(q, k, v, y, phi=phi, lambda_h=lam, eps=wl.eps, S_out=S, z_out=z)
         torch.cuda.synchronize()
         outs.append((y, S, z))
     return outs
@@ -56,3 +57,16 @@ def test_noalloc_caps_segments_to_its_scratch(monkeypatch):
     assert e0 < TOL["bf16"] and e1 < TOL["bf16"]
     s_err = float((np.abs(S1.cpu().numpy() - Sr).max(axis=-1) / np.abs(Sr).max(axis=-1)).max())
     assert s_err < TOL["bf16"]
+
+
+def test_noalloc_random_features():
+    # m = 128 (features inside the output kernel) and m = 256 (the numerators
+    # and denominators handed between halves sit in the static scratch too),
+    # two calls in a row each, the second smaller
+    for m in (128, 256):
+        for over in (dict(B=1, H=4, N=3000), dict(B=1, H=2, N=555)):
+            wl, inp = inputs(5, m=m, **over)
+            (y0, S0, z0), (y1, S1, z1) = _both(wl, inp)
+            assert torch.equal(y1, y0) and torch.equal(S1, S0) and torch.equal(z1, z0), (m, over)
+            ref, kap = oracle_causal(wl, inp, want_kappa=True)
+            check_kappa_rows(y1, ref, kap, "bf16")
