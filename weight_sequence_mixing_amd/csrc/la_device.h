@@ -139,6 +139,14 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
 //          W == 64:  u ^ (4 bits1..2(r) + 2 bit3(r) + bit0(r)).
 //          Conflict-free for all of the above and for the two 8-byte halves
 //          of a staged 16-byte vector (consecutive threads along a row).
+//   TileP: the features of each 32-wide block permuted so that the 8 k
+//          positions K(g) of a row fragment are one 16-byte unit (unit
+//          4 kb + g holds features 32 kb + 4 g .. + 3, then 32 kb + 16 + 4 g
+//          .. + 3), units XOR-swizzled by row & 15 (W >= 128) or
+//          bits 1..3 of the row (W == 64, two rows per 256 B): a row fragment
+//          is one conflict-free 16-byte read straight into the operand's
+//          registers.  A 4-feature group is one 8-byte half of a unit, so
+//          transposing reads and 4-element writes work as on the others.
 // fp32 tiles are padded by 4 elements per row instead.
 template <class T, int W> struct TileL;
 template <int W> struct TileL<bf16, W> {
@@ -147,6 +155,22 @@ template <int W> struct TileL<bf16, W> {
     // element offset of the 4-element unit holding column col (col % 4 == 0)
     __device__ static __forceinline__ int off(int row, int col) {
         return row * W + ((((col >> 2) ^ (((row & 3) << 2) | ((row >> 2) & 3)))) << 2);
+    }
+};
+template <class T, int W> struct TileP;
+template <int W> struct TileP<bf16, W> {
+    static_assert(W == 64 || W % 128 == 0, "rows of 64 or a multiple of 128 elements");
+    static constexpr int STRIDE = W;
+    static constexpr bool kRowUnits = true;  // a row fragment is one unit
+    // element offset of 16-byte unit u (u = 4 kb + g) of row `row`
+    __device__ static __forceinline__ int unit_off(int row, int u) {
+        if constexpr (W >= 128) return row * W + ((u ^ (row & 15)) << 3);
+        else return row * W + ((u ^ ((row >> 1) & 7)) << 3);
+    }
+    // element offset of the 4-element group holding feature col (col % 4 == 0)
+    __device__ static __forceinline__ int off(int row, int col) {
+        const int w = col & 31;
+        return unit_off(row, 4 * (col >> 5) + ((w & 15) >> 2)) + ((w >> 4) << 2);
     }
 };
 template <class T, int W> struct TileX;
@@ -167,9 +191,18 @@ template <int W> struct TileL<float, W> {
 };
 
 // Row fragment: lane (row, g) holds columns {32kb+4g..+3, 32kb+16+4g..+3}.
+template <class L, class = void> struct RowUnits { static constexpr bool value = false; };
+template <class L> struct RowUnits<L, decltype(void(L::kRowUnits))> { static constexpr bool value = L::kRowUnits; };
+
 template <class T, int W, class L = TileL<T, W>>
 __device__ __forceinline__ Frag<T> lds_frag_row(const T* t, int row, int kb, int g) {
-    return frag2(t + L::off(row, 32 * kb + 4 * g), t + L::off(row, 32 * kb + 16 + 4 * g));
+    if constexpr (RowUnits<L>::value) {
+        Frag<T> f;
+        f.v = *(const bf16x8*)(t + L::unit_off(row, 4 * kb + g));
+        return f;
+    } else {
+        return frag2(t + L::off(row, 32 * kb + 4 * g), t + L::off(row, 32 * kb + 16 + 4 * g));
+    }
 }
 
 // Column fragment of rows j0..j0+31 and columns m0..m0+15 (j0 % 32 == 0,

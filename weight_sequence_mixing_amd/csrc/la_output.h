@@ -143,9 +143,9 @@ la_out_kernel(const FwdArgs a)
     constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
     constexpr bool RF = Cfg::RF, VW = Cfg::VW;
     constexpr int M = Cfg::M, KX = Cfg::KX, RB = Cfg::RB, XLD = Cfg::XLD;
-    // phi(Q), phi(K) and the weighted phi(K) in TileL (row reads in the
-    // two-address form, 8-byte feature writes); V in TileX
-    using TF = TileL<T, F>;
+    // phi(Q), phi(K) and the weighted phi(K) in TileP (a row fragment is one
+    // 16-byte read); V in TileX
+    using TF = TileP<T, F>;
     using TVL = TileX<T, DV>;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
@@ -509,22 +509,22 @@ la_out_kernel(const FwdArgs a)
         };
         if constexpr (QF_ALL) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F>(sQ, i, kb, g);
+            for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F, TF>(sQ, i, kb, g);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) mma(dq, zfrag(kb), qf[kb]);
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), qf[kb]);
         } else {
 #pragma unroll
             for (int tq = 0; tq < DBQ; ++tq) o[tq] = zero4;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const Frag<T> q1 = lds_frag_row<T, F>(sQ, i, kb, g);
+                const Frag<T> q1 = lds_frag_row<T, F, TF>(sQ, i, kb, g);
                 mma(dq, zfrag(kb), q1);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) mma(pt[jb], lds_frag_row<T, F>(sK, 16 * jb + l16, kb, g), q1);
+                for (int jb = 0; jb < 4; ++jb) mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), q1);
 #pragma unroll
                 for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
             }
@@ -604,7 +604,7 @@ la_out_kernel(const FwdArgs a)
             for (int u = 0; u < FBW; ++u)
 #pragma unroll
                 for (int kb = 0; kb < CB; ++kb)
-                    kwf[u][kb] = ColRead<T, F>::get(sKu, 32 * kb, 16 * (FBW * qw + u), lane);
+                    kwf[u][kb] = ColRead<T, F, TF>::get(sKu, 32 * kb, 16 * (FBW * qw + u), lane);
         }
         // outputs of this wave's column tiles: O^T = S^T phi(Q)^T (scaled) +
         // V^T P^T; the value fragments of a column tile are the A operands of
@@ -673,7 +673,7 @@ la_out_kernel(const FwdArgs a)
             for (int u = 0; u < FBW; ++u) {
                 Frag<T> kf[CB];
 #pragma unroll
-                for (int kb = 0; kb < CB; ++kb) kf[kb] = ColRead<T, F>::get(sKu, 32 * kb, 16 * (FBW * qw + u), lane);
+                for (int kb = 0; kb < CB; ++kb) kf[kb] = ColRead<T, F, TF>::get(sKu, 32 * kb, 16 * (FBW * qw + u), lane);
 #pragma unroll
                 for (int tq = 0; tq < DBQ; ++tq)
 #pragma unroll
