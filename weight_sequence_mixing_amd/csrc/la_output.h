@@ -513,9 +513,16 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) mma(dq, zfrag(kb), qf[kb]);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
+            for (int jb = 0; jb < 4; ++jb) {
+                // key blocks after the query block are skipped (ib is the
+                // same in every lane of the wave); the selection below zeroes
+                // them either way
+                if (jb <= ib) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                    for (int kb = 0; kb < KB; ++kb)
+                        mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                }
+            }
         } else {
 #pragma unroll
             for (int tq = 0; tq < DBQ; ++tq) o[tq] = zero4;
@@ -531,8 +538,7 @@ la_out_kernel(const FwdArgs a)
         }
         // decay weights of the scores (random features: times the key's
         // prefactor); blocks after the query block (jb > ib) and keys above
-        // the diagonal are set to zero by selection.  No branch depends on the
-        // wave.
+        // the diagonal are set to zero by selection.
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             // lambda^(16 (ib-jb-1)) for blocks before the query block
