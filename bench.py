@@ -36,8 +36,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["la_forward.h", "la_output.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h", "la_backward.h",
-                  "la_rf_grad.hip", "la_api.cpp"]
+KERNEL_SOURCES = ["la_forward.h", "la_output.h", "la_state.h", "la_decode.h", "la_device.h", "la_scan.hip", "la_internal.h",
+                  "la_backward.h", "la_rf_grad.hip", "la_api.cpp"]
 
 
 def log(*a):
@@ -708,6 +708,8 @@ def _kernel_label(mangled):
         return "la_scan_kernel"
     if "la_out_kernel" in mangled:
         return "causal output pass"
+    if "la_state_kernel" in mangled:
+        return "segment state pass"
     if "la_fwd_kernel" in mangled:
         # the mode is the last int template argument (a bool, the output type,
         # follows it), mangled (...ELi1ELb0EEEvNS_7FwdArgsE) or demangled

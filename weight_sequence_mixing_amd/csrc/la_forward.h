@@ -873,6 +873,7 @@ la_fwd_kernel(const FwdArgs a)
 }  // namespace la
 
 #include "la_output.h"
+#include "la_state.h"
 
 namespace la {
 
@@ -887,6 +888,11 @@ hipError_t fwd_launch(const FwdArgs& a, int mode, hipStream_t stream)
     const bool o32 = sizeof(T) == 2 && a.out_f32;
     switch (mode) {
     case MODE_LOCAL:
+        // la_state_kernel for the maps of the query-split output pass, where
+        // the segments are whole 64-token chunks (the backward cuts its
+        // segments in its own chunks)
+        if constexpr (query_split_output<T, PHI>())
+            if (a.chunk % StateCfg<PHI, DK, F, DV>::C == 0) return state_launch<PHI, DK, F, DV>(a, stream);
         return launch_kernel(la_fwd_kernel<T, PHI, DK, F, DV, C, NW, MODE_LOCAL, false>, grid, block, stream, a);
     case MODE_CAUSAL:
         if constexpr (query_split_output<T, PHI>() && OutCfg<PHI, DK, F, DV>::FITS)
