@@ -61,6 +61,23 @@ def test_random_feature_prefactors_causal(phi, m):
     _check_rows(y, ref, kap, "bf16")
 
 
+@pytest.mark.parametrize("m,dk,dv", [(32, 128, 128), (64, 128, 64), (128, 64, 128), (64, 64, 128)])
+def test_random_features_head_sizes(m, dk, dv, monkeypatch):
+    # random features beyond d_k = d_v = 64: four k blocks of omega per
+    # feature tile, eight value tiles per wave in the segment states, two
+    # waves per omega row block for m <= 64; three segments of six 64-token
+    # chunks, the last one ragged
+    monkeypatch.setenv("LA_SEGMENTS", "3")
+    wl = si.workload(5).with_(m=m, dk=dk, dv=dv)
+    inp = si.make_inputs(wl, B=1, H=2, N=1100)
+    lam = [0.98, 1.0]
+    y, S, z = run_causal(wl, inp, lam=lam, want_state=True)
+    ref, Sr, zr, kap = oracle_causal(wl, inp, lam=lam, want_state=True, want_kappa=True)
+    _check_rows(y, ref, kap, "bf16")
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(zr).max())
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(Sr).max())
+
+
 @pytest.mark.parametrize("phi", ["trig_rf", "trig_rf_softmax"])
 def test_random_features_gaussian_omega(phi):
     # rows of omega drawn independently from N(0, I), no orthogonal blocks
