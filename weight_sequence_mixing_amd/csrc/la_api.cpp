@@ -684,6 +684,9 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             l.z_dst = segs + (int64_t)Fh * shape->d_v;
             l.dst_stride = plan.SZ;
             l.dst_zstride = plan.SZ;
+            // with no state leaving this window, no segment reads the local
+            // state of a row's last segment
+            l.skip_last = So == nullptr;
             if ((e = launch(LA_KERNEL_FWD_LOCAL, [&] { return ent->fwd(l, MODE_LOCAL, strm); })) != hipSuccess)
                 return hip_fail(e, "segment state launch");
             // pass 2: decayed exclusive scan over segments
@@ -704,6 +707,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             sa.S_fin = So; sa.z_fin = zo; sa.fin_stride = so_stride; sa.fin_zstride = zo_stride;
             sa.init_gap = si_gap;
             sa.fin_gap = so_gap;
+            sa.skip_last = l.skip_last;
             sa.lam = lam;
             if ((e = launch(LA_KERNEL_SCAN, [&] { return launch_scan(sa, strm); })) != hipSuccess)
                 return hip_fail(e, "segment scan launch");

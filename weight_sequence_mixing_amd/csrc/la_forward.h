@@ -253,6 +253,10 @@ la_fwd_kernel(const FwdArgs a)
         if constexpr (MODE != MODE_CAUSAL) return;
         else if (!a.S_dst || spare) return;
     }
+    // with skip_last, the segment that reaches the row's end (whose local
+    // state only a final state would read)
+    if constexpr (MODE == MODE_LOCAL)
+        if (a.skip_last && c_end == NC) return;
     const T* qg = (const T*)a.q + row0 * DK;
     const T* kg = (const T*)a.k + row0 * DK;
     const T* vg = (const T*)a.v + row0 * DV;

@@ -93,6 +93,9 @@ struct FwdArgs {
     float* z_dst;
     int64_t dst_stride;
     int64_t dst_zstride;
+    // MODE_LOCAL: 1 when no final state is wanted, so that the segment that
+    // reaches the end of its row is not computed (no later segment reads it)
+    int32_t skip_last;
     LamTable lam;
 };
 
@@ -119,6 +122,9 @@ struct ScanArgs {
     // 1: visit the segments last to first (the adjoint state of the backward
     // pass, carried from the end of the sequence towards its start)
     int32_t reverse;
+    // causal, forward order, no final state: the local state of the last
+    // segment holding tokens is neither read nor needed (FwdArgs skip_last)
+    int32_t skip_last;
     LamTable lam;
 };
 

@@ -70,7 +70,8 @@ __global__ void __launch_bounds__(kScanThreads) la_scan_kernel(const ScanArgs a)
 #pragma unroll
         for (int b = 0; b < kScanBatch; ++b) {
             const int s = a.reverse ? nseg - 1 - (s0 + b) : s0 + b;
-            loc[b] = (s0 + b < nseg) ? base[s * slot] : zero;
+            const bool skipped = a.skip_last && s == nseg - 1;  // never computed
+            loc[b] = (s0 + b < nseg && !skipped) ? base[s * slot] : zero;
         }
 #pragma unroll
         for (int b = 0; b < kScanBatch; ++b) {

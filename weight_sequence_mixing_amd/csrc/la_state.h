@@ -154,11 +154,12 @@ la_state_kernel(const FwdArgs a)
     }
     // segments of cps units of a.chunk tokens (a multiple of C); the last one
     // takes whatever remains.  An empty segment stores nothing (the scan
-    // reads only the segments a row has).
+    // reads only the segments a row has), nor, with skip_last, the one that
+    // reaches the row's end (only a final state would read it).
     const int64_t cps = a.cps * (a.chunk / C);
     const int64_t NC = spare ? 0 : (n_len + C - 1) / C;
     const int64_t c_beg = (int64_t)seg * cps, c_end = (seg == a.P - 1) ? NC : min(NC, c_beg + cps);
-    if (c_beg >= c_end) return;
+    if (c_beg >= c_end || (a.skip_last && c_end == NC)) return;
     const T* kg = (const T*)a.k + row0 * DK;
     const T* vg = (const T*)a.v + row0 * DV;
     const uint8_t* kp = a.kpm ? a.kpm + (int64_t)(bh / a.H) * a.kpm_stride + a.n0 : nullptr;
