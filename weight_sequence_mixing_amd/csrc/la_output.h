@@ -495,8 +495,10 @@ la_out_kernel(const FwdArgs a)
         constexpr bool QF_ALL = KB <= DBQ;
         f32x4 dq = zero4, pt[4], o[QF_ALL ? 1 : DBQ];
         Frag<T> qf[QF_ALL ? KB : 1];
+        if constexpr (!QF_ALL) {
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) pt[jb] = zero4;
+            for (int jb = 0; jb < 4; ++jb) pt[jb] = zero4;
+        }
         auto sfrag = [&](int t, int kb) LA_INLINE {
             Frag<T> sf;
             sf.v = *(const bf16x8*)(sST + st_off<F>(16 * t + l16, 4 * kb + g));
@@ -516,11 +518,16 @@ la_out_kernel(const FwdArgs a)
             for (int jb = 0; jb < 4; ++jb) {
                 // key blocks after the query block are skipped (ib is the
                 // same in every lane of the wave); the selection below zeroes
-                // them either way
+                // them, so their tiles are left undetermined rather than set
+                // to zero (which would cost register moves around the branch)
                 if (jb <= ib) {
+                    f32x4 acc = zero4;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
-                        mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                        mma(acc, lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), qf[kb]);
+                    pt[jb] = acc;
+                } else {
+                    pt[jb] = __builtin_nondeterministic_value(zero4);
                 }
             }
         } else {
