@@ -301,6 +301,17 @@ __device__ __forceinline__ void unpack16(const uint4& u, float* out, const float
     out[3] = __uint_as_float(u.w);
 }
 
+// 16 bytes at byte offset voff (per lane) from a base address that is the
+// same in every lane, through a raw buffer resource: the lane's offset is a
+// 32-bit register that stays fixed from chunk to chunk, so the loads of a
+// chunk need no 64-bit address arithmetic per load.  voff must stay below
+// 2^31 (the resource's range).
+__device__ __forceinline__ uint4 load16(const void* base, uint32_t voff) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                                                        0x00020000);
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
+
 __device__ __forceinline__ float wave_sum_xor(float v, int mask_lo, int mask_hi) {
     for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, 64);
     return v;

@@ -255,7 +255,7 @@ la_out_kernel(const FwdArgs a)
         for (int r = 0; r < nreg; ++r) {
             const int idx = tid + r * NT, j = idx / vpr, c4 = idx % vpr;
             if constexpr (!TAIL) {
-                dst[r] = *(const uint4*)(base + j * ld + c4 * VEC);
+                dst[r] = load16(base, (uint32_t)((j * ld + c4 * VEC) * sizeof(T)));
             } else {
                 const uint4 val = *(const uint4*)(base + min(j, n - 1) * ld + c4 * VEC);
                 const bool in = j < n;  // per component: a select of the whole vector goes through memory
