@@ -250,12 +250,24 @@ struct Plan {
 // an MI355X (256 CUs).
 constexpr int kTargetWorkgroups = 512;
 
+// Workgroups a causal forward over fixed rows aims for: one per compute unit
+// where the segment-state pass streams elementwise bf16 features of width 128
+// or more (it is bound by its stream of loads, and fewer, longer segments
+// write and scan fewer states; the causal output kernel of that width holds
+// one workgroup per unit anyway), two elsewhere (the random-feature state
+// pass is bound by its arithmetic and gains from the second workgroup).
+int64_t causal_target_workgroups(const KernelEntry* e, int F)
+{
+    return (e->in_dtype == LA_BF16 && e->phi != LA_PHI_TRIG_RF && F >= 128) ? kTargetWorkgroups / 2
+                                                                            : kTargetWorkgroups;
+}
+
 // Segments wanted for a row of NC chunks (before rounding to whole chunks).
 // max_P: an upper bound on the segments (the static-scratch forward caps them
 // so that their states fit its scratch).
-int64_t target_segments(int64_t NC, int64_t BH, int64_t max_P = INT64_MAX)
+int64_t target_segments(int64_t NC, int64_t BH, int64_t max_P = INT64_MAX, int64_t target = kTargetWorkgroups)
 {
-    int64_t P = (kTargetWorkgroups + BH - 1) / BH;
+    int64_t P = (target + BH - 1) / BH;
     const int forced = env_int("LA_SEGMENTS", 0);
     if (forced > 0) P = forced;
     if (P > max_P) P = max_P;
@@ -265,9 +277,10 @@ int64_t target_segments(int64_t NC, int64_t BH, int64_t max_P = INT64_MAX)
 }
 
 // Cut NC chunks into segments of cps chunks: every segment but the last is full.
-void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps, int64_t max_P = INT64_MAX)
+void cut_segments(int64_t NC, int64_t BH, int* P, int64_t* cps, int64_t max_P = INT64_MAX,
+                  int64_t target = kTargetWorkgroups)
 {
-    const int64_t Pt = target_segments(NC, BH, max_P);
+    const int64_t Pt = target_segments(NC, BH, max_P, target);
     *cps = (NC + Pt - 1) / Pt;
     *P = (int)((NC + *cps - 1) / *cps);
 }
@@ -317,7 +330,9 @@ Plan make_plan(const la_shape* s, int F, const KernelEntry* e, bool causal, int 
     if (W > NC) W = (int)(NC > 0 ? NC : 1);
     p.W = W;
     // every window has at most NC chunks, so it is cut into at most this many segments
-    p.Pmax = varlen_P > 0 ? varlen_P : (int)target_segments(NC > 0 ? NC : 1, BH, max_P);
+    p.Pmax = varlen_P > 0 ? varlen_P
+                          : (int)target_segments(NC > 0 ? NC : 1, BH, max_P,
+                                                 causal ? causal_target_workgroups(e, F) : kTargetWorkgroups);
     size_t floats = 0;
     if (causal) {
         if (p.Pmax > 1) floats += (size_t)p.Pmax * BH * p.SZ;
@@ -651,7 +666,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* y, c
             });
             if (ie != hipSuccess) return hip_fail(ie, "packed sequence items launch");
         } else {
-            cut_segments(c1 - c0, BH, &P, &cps, max_P);
+            cut_segments(c1 - c0, BH, &P, &cps, max_P, causal_target_workgroups(ent, Fh));
         }
         // state entering and leaving this window
         const float* Si = nullptr;
