@@ -9,16 +9,16 @@
 // only).  The scan of la_scan.hip turns these into each segment's carried-in
 // state.
 //
-// Work split.  A workgroup takes one segment in 64-token chunks; the chunk's
-// loads for the next chunk are issued as soon as the current one is staged,
-// and the LDS buffers are doubled, so a chunk needs one barrier.
+// Work split.  A workgroup takes one segment in 64-token chunks; the next
+// chunk's loads are issued as soon as the current one is staged, and the
+// LDS buffers are doubled, so a chunk needs one barrier.
 //
 // Elementwise maps: the weighted key features w_j phi(k_j) (w_j the decay
 // weight, zero for a dropped key) and the values are staged in TileX, whose
 // staging writes and transposing reads are both conflict-free.  The state's
-// 16 x 16 tiles are split over a 4 x 2 grid of waves (feature blocks x value
-// columns); each wave reads the (w phi(K))^T and V fragments of its tiles and
-// adds their product.
+// 16 x 16 tiles are split over a 4 x 2 grid of eight waves, or 4 x 4 of
+// sixteen where d_k = d_v = 128 (feature blocks x value columns); each wave
+// reads the (w phi(K))^T and V fragments of its tiles and adds their product.
 //
 // Random features ("From standard attention to linear attention", sec. 4.2:
 // phi(x) = c(x) [cos(omega x'), sin(omega x')] / sqrt(m), x' = qk_scale x):
@@ -50,8 +50,9 @@ struct StateCfg {
     // random features: row blocks of omega, one per wave (two waves each
     // where there are fewer than eight: TS token splits)
     static constexpr int RBN = RF ? M / 16 : 1;
-    // elementwise maps: a 4 x (NWE / 4) grid of waves
-    static constexpr int NWE = 8;
+    // elementwise maps: a 4 x (NWE / 4) grid of waves; 16 waves where both
+    // widths are 128 (the plan then gives one workgroup per compute unit)
+    static constexpr int NWE = (DK >= 128 && DV >= 128) ? 16 : 8;
     static constexpr int NW = RF ? (2 * RBN < 8 ? 2 * RBN : 8) : NWE;
     static constexpr int NT = NW * 64;
     static constexpr int TS = RF ? NW / RBN : 1;
@@ -76,10 +77,11 @@ struct StateCfg {
     static constexpr int TPW = FBW * DBW + FBW;
     static constexpr size_t RED = TS > 1 ? size_t(RBN) * TPW * 64 * 16 : 0;
     static constexpr size_t TOTAL = 2 * BUF > RED ? 2 * BUF : RED;
-    // waves per SIMD asked of the register allocator: two workgroups per
-    // compute unit (128 registers), one for the random features beyond
-    // d_k = d_v = 64, whose omega fragments and value tiles need more
-    static constexpr int WPE = (RF && (DK > 64 || DV > 64)) ? NW / 4 : 2 * NW / 4;
+    // waves per SIMD asked of the register allocator: four (128 registers:
+    // two workgroups of eight waves, or one of sixteen, per compute unit);
+    // for the random features beyond d_k = d_v = 64, whose omega fragments
+    // and value tiles need more, one workgroup per compute unit
+    static constexpr int WPE = RF ? ((DK > 64 || DV > 64) ? NW / 4 : 2 * NW / 4) : 4;
     static_assert(F % 64 == 0 && DV % 64 == 0 && DK % 64 == 0, "head sizes");
     static_assert(RF || DK == F, "elementwise maps keep the width");
     static_assert(!RF || (RBN >= 2 && TS <= 2 && RBN * TS == NW), "omega row blocks over the waves");
