@@ -160,6 +160,31 @@ def test_causal_masked_parity(wi, over, B, H, N, kind, with_state):
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=tol, atol=tol * np.abs(zr).max())
 
 
+@pytest.mark.parametrize("wi,over,kind", [(3, {}, "random"), (5, {"m": 64}, "random"),
+                                         (2, {"phi": "relu", "dk": 128, "dv": 128}, "right")])
+def test_causal_masked_multichunk_segments(wi, over, kind, monkeypatch):
+    # three segments of several 64-token chunks each and no final state asked
+    # for, so the segment-state pass leaves out each row's last segment
+    monkeypatch.setenv("LA_SEGMENTS", "3")
+    wl = si.workload(wi).with_(**over)
+    B, H, N = 2, 2, 1500
+    inp = si.make_inputs(wl, B=B, H=H, N=N)
+    lam = [0.95, 1.0]
+    mask = si.make_key_padding_mask(B, N, kind, seed=wi + N + 1)
+    q, k, v = (to_dev(inp, n, wl.dtype) for n in ("q", "k", "v"))
+    y = torch.full((B, H, N, wl.dv), float("nan"), dtype=tdtype(wl.dtype), device=DEV)
+    la.la_forward_causal_masked(q, k, v, y, _dev_mask(mask), phi=phi_for(wl, inp.get("omega")), lambda_h=lam,
+                                eps=wl.eps)
+    torch.cuda.synchronize()
+    ref, kap = oracle.causal(inp["q"], inp["k"], inp["v"], lam, wl.eps, wl.phi, inp.get("omega"), wl.qk_scale,
+                             want_kappa=True, key_padding_mask=mask)
+    if wl.random_features:
+        _check_rows(y, ref, kap, wl.dtype)
+    else:
+        err = rel_err(y, ref)
+        assert err < TOL[wl.dtype], err
+
+
 def test_causal_mask_all_padded_and_none():
     wl = si.workload(2)
     B, H, N = 2, 2, 300
