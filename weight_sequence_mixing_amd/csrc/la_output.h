@@ -275,6 +275,20 @@ la_out_kernel(const FwdArgs a)
             mk[r] = kp ? (int)kp[t0 + (decltype(tail_c)::value ? min(j, n - 1) : j)] : 0;
         }
     };
+    // one tensor of a full chunk (0: v, 1: q, 2: k and its mask bytes), so
+    // that each tensor's next loads go out as soon as its registers are staged
+    auto load_part = [&](int part, int64_t c) LA_INLINE {
+        const int64_t t0 = c * C;
+        if (part == 0) {
+            load_rows(rv, vg + t0 * DV, VPRV, DV, RV, C, std::false_type{});
+        } else if (part == 1) {
+            load_rows(rq, qg + t0 * DK, VPRQ, DK, RQ, C, std::false_type{});
+        } else {
+            load_rows(rk, kg + t0 * DK, VPRQ, DK, RQ, C, std::false_type{});
+#pragma unroll
+            for (int r = 0; r < RQ; ++r) mk[r] = kp ? (int)kp[t0 + (tid + r * NT) / VPRQ] : 0;
+        }
+    };
     if (c_beg < c_full) load_chunk(c_beg, std::false_type{});
     else if (c_beg < c_end) load_chunk(c_beg, std::true_type{});
 
@@ -356,9 +370,18 @@ la_out_kernel(const FwdArgs a)
         st4(tile + TF::off(row, col), p[0], p[1], p[2], p[3]);
         st4(tile + TF::off(row, col + 4), p[4], p[5], p[6], p[7]);
     };
-    auto stage = [&](int n, float kw_l2, auto tail_c) LA_INLINE {
+    // after_part(p) runs once tensor p (0: v, 1: q, 2: k) is staged
+    auto stage = [&](int n, float kw_l2, auto tail_c, auto&& after_part) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const int cg = tid % VPRQ;
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+            const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
+            const uint4 u = rv[r];
+            *(uint2*)(sV + TVL::off(j, c4 * VEC)) = uint2{u.x, u.y};
+            *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
+        }
+        after_part(0);
         if constexpr (!RF) {
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
@@ -369,6 +392,7 @@ la_out_kernel(const FwdArgs a)
                 for (int e = 0; e < VEC; ++e) p[e] = phi_elem<T, PHI>(x[e]);
                 put_feat(sQ, j, cg * VEC, p);
             }
+            after_part(1);
 #pragma unroll
             for (int r = 0; r < RQ; ++r) {
                 const int j = (tid + r * NT) / VPRQ;
@@ -388,13 +412,7 @@ la_out_kernel(const FwdArgs a)
                     put_feat(sKw0, j, cg * VEC, p);
                 }
             }
-        }
-#pragma unroll
-        for (int r = 0; r < RV; ++r) {
-            const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
-            const uint4 u = rv[r];
-            *(uint2*)(sV + TVL::off(j, c4 * VEC)) = uint2{u.x, u.y};
-            *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
+            after_part(2);
         }
         if constexpr (VW) {
             // weight of key tid in the state update: its decay weight times
@@ -403,6 +421,7 @@ la_out_kernel(const FwdArgs a)
                 sWt[tid] = (TAIL && tid >= n) ? 0.f : (decay ? key_weight(n - 1 - tid, kw_l2) : 1.f) * sCF0[cb * 2 * C + C + tid];
         }
     };
+    const auto no_loads = [](int) {};
 
     // ---- random features, part 1: the raw q and k rows and the prefactor
     // c(x) = exp(s |x'|^2 / 2) / sqrt(m) of each.  A key that is past the end
@@ -720,23 +739,26 @@ la_out_kernel(const FwdArgs a)
         // (random features: the key weights of stage() need the prefactors
         // of stage_x(), and features() the raw rows, so a barrier follows
         // stage_x() where no other one does)
+        // elementwise maps: the next chunk's loads go out as soon as this
+        // one's tensors are staged, before the barrier (random features keep
+        // them after it: their staging registers are live until the raw rows
+        // are staged)
+        constexpr bool EARLY = !RF;
         if (c_beg < c_full) {
             d = book(C);
             stage_x(C, cb, std::false_type{});
             if constexpr (RF) __syncthreads();
-            stage(C, d.kw_l2, std::false_type{});
+            const bool load1 = EARLY && c_beg + 1 < c_full;
+            stage(C, d.kw_l2, std::false_type{}, [&](int part) LA_INLINE {
+                if (load1) load_part(part, c_beg + 1);
+            });
         } else {
             d = book(n_tail);
             stage_x(n_tail, cb, std::true_type{});
             if constexpr (RF) __syncthreads();
-            stage(n_tail, d.kw_l2, std::true_type{});
+            stage(n_tail, d.kw_l2, std::true_type{}, no_loads);
         }
         features();
-        // elementwise maps: the next chunk's loads go out as soon as this
-        // one is staged, before the barrier (random features keep them after
-        // it: their staging registers are live until the raw rows are staged)
-        constexpr bool EARLY = !RF;
-        if (EARLY && c_beg + 1 < c_full) load_chunk(c_beg + 1, std::false_type{});
         for (int64_t c = c_beg; c < c_full; ++c) {
             const bool next_full = c + 1 < c_full;
             __syncthreads();
@@ -750,9 +772,13 @@ la_out_kernel(const FwdArgs a)
             if (next_full) {
                 cb ^= 1;
                 d = book(C);
-                stage(C, d.kw_l2, std::false_type{});
+                // elementwise maps: each tensor's loads for chunk c + 2 go
+                // out right after the tensor is staged
+                const bool load2 = EARLY && c + 2 < c_full;
+                stage(C, d.kw_l2, std::false_type{}, [&](int part) LA_INLINE {
+                    if (load2) load_part(part, c + 2);
+                });
                 features();
-                if (EARLY && c + 2 < c_full) load_chunk(c + 2, std::false_type{});
             }
         }
         if (ragged) {
@@ -762,7 +788,7 @@ la_out_kernel(const FwdArgs a)
                 d = book(n_tail);
                 stage_x(n_tail, cb, std::true_type{});
                 if constexpr (RF) __syncthreads();
-                stage(n_tail, d.kw_l2, std::true_type{});
+                stage(n_tail, d.kw_l2, std::true_type{}, no_loads);
                 features();
             }
             __syncthreads();
