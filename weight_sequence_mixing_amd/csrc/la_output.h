@@ -512,7 +512,7 @@ la_out_kernel(const FwdArgs a)
         // the inter-chunk part follows per column tile; otherwise the
         // products run one k block at a time into DBQ accumulators.
         constexpr bool QF_ALL = KB <= DBQ;
-        f32x4 dq = zero4, pt[4], o[QF_ALL ? 1 : DBQ];
+        f32x4 dq = zero4, pt[QF_ALL ? 1 : 4], o[QF_ALL ? 1 : DBQ];
         Frag<T> qf[QF_ALL ? KB : 1];
         if constexpr (!QF_ALL) {
 #pragma unroll
@@ -528,26 +528,57 @@ la_out_kernel(const FwdArgs a)
             zf.v = *(const bf16x8*)(sZ + (4 * kb + g) * 8);
             return zf;
         };
+        Frag<T> pf[CB];
+        f32x4 rs = zero4;
         if constexpr (QF_ALL) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) qf[kb] = lds_frag_row<T, F, TF>(sQ, i, kb, g);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) mma(dq, zfrag(kb), qf[kb]);
+            // one version per query block (ib is the same in every lane of
+            // the wave): the score tiles of key blocks 0 .. ib are formed and
+            // given their decay weights (random features: times the key's
+            // prefactor), those after it are zero; only the diagonal block
+            // needs a selection, which zeroes its keys above the diagonal
+            // (by selection, so that a non-finite key cannot reach an
+            // earlier query through a zero weight)
+            auto scores = [&](auto ib_c) LA_INLINE {
+                constexpr int IB = decltype(ib_c)::value;
+                f32x4 p4[4];
+                static_until<0, 4>([&](auto jb_c) LA_INLINE {
+                    constexpr int JB = decltype(jb_c)::value;
+                    if constexpr (JB <= IB) {
+                        f32x4 acc = zero4;
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                // key blocks after the query block are skipped (ib is the
-                // same in every lane of the wave); the selection below zeroes
-                // them, so their tiles are left undetermined rather than set
-                // to zero (which would cost register moves around the branch)
-                if (jb <= ib) {
-                    f32x4 acc = zero4;
+                        for (int kb = 0; kb < KB; ++kb)
+                            mma(acc, lds_frag_row<T, F, TF>(sK, 16 * JB + l16, kb, g), qf[kb]);
+                        f32x4 ck = {1.f, 1.f, 1.f, 1.f};
+                        if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * JB + 4 * g);
+                        if constexpr (JB == IB) {
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        mma(acc, lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), qf[kb]);
-                    pt[jb] = acc;
-                } else {
-                    pt[jb] = __builtin_nondeterministic_value(zero4);
+                            for (int r = 0; r < 4; ++r) p4[JB][r] = above[r] ? 0.f : acc[r] * (m0[r] * ck[r]);
+                        } else {
+                            // lambda^(16 (ib-jb-1)) for blocks before the query block
+                            const float dj = lam_pow(l2l, 16 * (IB - JB - 1));
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) p4[JB][r] = acc[r] * (m1[r] * dj * ck[r]);
+                        }
+                    } else {
+                        p4[JB] = zero4;
+                    }
+                    return false;
+                });
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) {
+                    pf[kb] = frag_acc<T>(p4[2 * kb], p4[2 * kb + 1]);
+                    if (2 * kb <= IB) mma(rs, ones, pf[kb]);
                 }
+            };
+            switch (ib) {
+            case 0: scores(std::integral_constant<int, 0>{}); break;
+            case 1: scores(std::integral_constant<int, 1>{}); break;
+            case 2: scores(std::integral_constant<int, 2>{}); break;
+            default: scores(std::integral_constant<int, 3>{}); break;
             }
         } else {
 #pragma unroll
@@ -561,29 +592,27 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
                 for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
             }
-        }
-        // decay weights of the scores (random features: times the key's
-        // prefactor); blocks after the query block (jb > ib) and keys above
-        // the diagonal are set to zero by selection.
+            // decay weights of the scores (random features: times the key's
+            // prefactor); blocks after the query block (jb > ib) and keys
+            // above the diagonal are set to zero by selection.
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            // lambda^(16 (ib-jb-1)) for blocks before the query block
-            const float dj = lam_pow(l2l, max(16 * (ib - jb - 1), 0));
-            f32x4 ck = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * jb + 4 * g);
+            for (int jb = 0; jb < 4; ++jb) {
+                // lambda^(16 (ib-jb-1)) for blocks before the query block
+                const float dj = lam_pow(l2l, max(16 * (ib - jb - 1), 0));
+                f32x4 ck = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * jb + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float wgt = (jb == ib) ? m0[r] : m1[r] * dj;
-                const bool zero = jb > ib || (jb == ib && above[r]);
-                pt[jb][r] = zero ? 0.f : pt[jb][r] * (RF ? wgt * ck[r] : wgt);
+                for (int r = 0; r < 4; ++r) {
+                    const float wgt = (jb == ib) ? m0[r] : m1[r] * dj;
+                    const bool zero = jb > ib || (jb == ib && above[r]);
+                    pt[jb][r] = zero ? 0.f : pt[jb][r] * (RF ? wgt * ck[r] : wgt);
+                }
             }
-        }
-        Frag<T> pf[CB];
-        f32x4 rs = zero4;
 #pragma unroll
-        for (int kb = 0; kb < CB; ++kb) {
-            pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
-            mma(rs, ones, pf[kb]);
+            for (int kb = 0; kb < CB; ++kb) {
+                pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
+                mma(rs, ones, pf[kb]);
+            }
         }
         // y_i = c_i (o + o_i) / (c_i den + eps) with c_i the query's
         // prefactor (random features), else y_i = (o + o_i) / (den + eps).
