@@ -593,25 +593,41 @@ la_out_kernel(const FwdArgs a)
                 for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
             }
             // decay weights of the scores (random features: times the key's
-            // prefactor); blocks after the query block (jb > ib) and keys
-            // above the diagonal are set to zero by selection.
+            // prefactor), in one version per query block as above: blocks
+            // after the query block are zero, keys above the diagonal are
+            // zeroed by selection
+            auto weigh = [&](auto ib_c) LA_INLINE {
+                constexpr int IB = decltype(ib_c)::value;
+                f32x4 p4[4];
+                static_until<0, 4>([&](auto jb_c) LA_INLINE {
+                    constexpr int JB = decltype(jb_c)::value;
+                    if constexpr (JB <= IB) {
+                        f32x4 ck = {1.f, 1.f, 1.f, 1.f};
+                        if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * JB + 4 * g);
+                        if constexpr (JB == IB) {
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                // lambda^(16 (ib-jb-1)) for blocks before the query block
-                const float dj = lam_pow(l2l, max(16 * (ib - jb - 1), 0));
-                f32x4 ck = {1.f, 1.f, 1.f, 1.f};
-                if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * jb + 4 * g);
+                            for (int r = 0; r < 4; ++r) p4[JB][r] = above[r] ? 0.f : pt[JB][r] * (m0[r] * ck[r]);
+                        } else {
+                            const float dj = lam_pow(l2l, 16 * (IB - JB - 1));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float wgt = (jb == ib) ? m0[r] : m1[r] * dj;
-                    const bool zero = jb > ib || (jb == ib && above[r]);
-                    pt[jb][r] = zero ? 0.f : pt[jb][r] * (RF ? wgt * ck[r] : wgt);
+                            for (int r = 0; r < 4; ++r) p4[JB][r] = pt[JB][r] * (m1[r] * dj * ck[r]);
+                        }
+                    } else {
+                        p4[JB] = zero4;
+                    }
+                    return false;
+                });
+#pragma unroll
+                for (int kb = 0; kb < CB; ++kb) {
+                    pf[kb] = frag_acc<T>(p4[2 * kb], p4[2 * kb + 1]);
+                    if (2 * kb <= IB) mma(rs, ones, pf[kb]);
                 }
-            }
-#pragma unroll
-            for (int kb = 0; kb < CB; ++kb) {
-                pf[kb] = frag_acc<T>(pt[2 * kb], pt[2 * kb + 1]);
-                mma(rs, ones, pf[kb]);
+            };
+            switch (ib) {
+            case 0: weigh(std::integral_constant<int, 0>{}); break;
+            case 1: weigh(std::integral_constant<int, 1>{}); break;
+            case 2: weigh(std::integral_constant<int, 2>{}); break;
+            default: weigh(std::integral_constant<int, 3>{}); break;
             }
         }
         // y_i = c_i (o + o_i) / (c_i den + eps) with c_i the query's
