@@ -60,7 +60,7 @@ struct StateCfg {
     static constexpr int WD = RF ? 1 : NW / 4;
     static constexpr int FBW = RF ? 2 : FB / 4;
     static constexpr int DBW = RF ? DB : DB / WD;
-    // chunks whose loads are in flight (register sets)
+    // register sets of loads in flight (one chunk ahead)
     static constexpr int PF = 1;
     static constexpr int VEC = 8, VPRK = DK / VEC, VPRV = DV / VEC;
     static constexpr int RK = C * VPRK / NT, RV = C * VPRV / NT;
@@ -223,38 +223,22 @@ la_state_kernel(const FwdArgs a)
             mk[st][r] = kp ? (int)kp[t0 + (decltype(tail_c)::value ? min(j, n - 1) : j)] : 0;
         }
     };
-    // ---- decay bookkeeping (as the output pass): the accumulators hold
-    // S / 2^log2D; a chunk of n keys is added with the weights
-    // lambda^(n-1-j) / 2^log2D' (kw_l2 = log2D'), or, once 2^log2D' would
-    // fall below 2^kLog2MinScale, the accumulators are rescaled to the true
-    // scale first
-    float log2D = 0.f;
-    struct Dec { float rescale, kw_l2; bool do_rescale; };
-    auto book = [&](int n) LA_INLINE {
-        Dec d = {1.f, 0.f, false};
-        if (decay) {
-            const float cand = log2D + (float)n * l2l;
-            if (cand >= kLog2MinScale) {
-                d.kw_l2 = cand;
-                log2D = cand;
-            } else {
-                d.do_rescale = true;
-                d.rescale = exp2f(cand);
-                log2D = 0.f;
-            }
-        }
-        return d;
-    };
-    // log2 of a key's weight lambda^k / 2^kw_l2 (lambda^0 = 1 also for
-    // lambda = 0)
-    auto key_lw = [&](int k, float kw_l2) LA_INLINE { return (k == 0 ? 0.f : (float)k * l2l) - kw_l2; };
+    // ---- decay weights.  The chunks are visited from the segment's end to
+    // its start, so that the last ones read (the segment's first chunks)
+    // are the first the causal output pass reads.  Key t of the segment
+    // enters with lambda^(t_last - t) (lambda^0 = 1 also for lambda = 0),
+    // t_last its last token: weights only shrink along the visit, so the
+    // accumulators hold the true state and the smallest weights underflow
+    // to zero harmlessly.  dbase: t_last - t for the chunk's first key.
+    const int64_t t_last = min(c_end * C, n_len) - 1;
+    auto key_lw = [&](int64_t dist) LA_INLINE { return dist == 0 ? 0.f : (float)dist * l2l; };
 
     // ---- staging of one chunk into buffer b.  A key past the end of the
     // sequence or masked is dropped: its row enters as zeros (so that no
     // non-finite value of it survives) with a zero weight.
     const float rf_cexp = 0.5f * a.rf_sign * a.qk_scale * a.qk_scale;
     const float rf_cnorm = a.rf_scale;
-    auto stage = [&](auto set_c, int b, int n, float kw_l2, auto tail_c) LA_INLINE {
+    auto stage = [&](auto set_c, int b, int n, int64_t dbase, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         constexpr int st = decltype(set_c)::value;
         const int cg = tid % VPRK;
@@ -262,7 +246,7 @@ la_state_kernel(const FwdArgs a)
         for (int r = 0; r < RK; ++r) {
             const int j = (tid + r * NT) / VPRK;
             const bool drop = (TAIL && j >= n) || mk[st][r];
-            const float lw = drop ? -INFINITY : (decay ? key_lw(n - 1 - j, kw_l2) : 0.f);
+            const float lw = drop ? -INFINITY : (decay ? key_lw(dbase - j) : 0.f);
             const float w = __builtin_amdgcn_exp2f(lw);
             // a dropped key's row is replaced by zeros: its features are then
             // finite whatever it held, and its weight zeroes them
@@ -308,15 +292,7 @@ la_state_kernel(const FwdArgs a)
     }
 
     // ---- the chunk in buffer b into this wave's tiles
-    auto update = [&](int b, const Dec& d) LA_INLINE {
-        if (d.do_rescale) {
-#pragma unroll
-            for (int u = 0; u < FBW; ++u) {
-                accZ[u] *= d.rescale;
-#pragma unroll
-                for (int c = 0; c < DBW; ++c) accS[u][c] *= d.rescale;
-            }
-        }
+    auto update = [&](int b) LA_INLINE {
         const T* const sV = sVb(b);
         if constexpr (!RF) {
             const T* const sK = sKb(b);
@@ -384,45 +360,32 @@ la_state_kernel(const FwdArgs a)
         }
     };
 
-    // ---- the segment, one barrier per chunk: staging chunk c into buffer
-    // c & 1 follows the barrier after which every wave has finished reading
-    // that buffer for chunk c - 2.  The loads of chunk c + PF go out as soon
-    // as chunk c is staged from its register set; inside the loop they are
-    // always full-chunk loads (past the last full chunk they re-read it, in
-    // bounds and unused), so that the compiler cannot merge them with the
-    // ragged chunk's zeroing, which would wait for them on the spot.  The
-    // ragged chunk is loaded after the loop.
-    static_until<0, PF>([&](auto s_c) LA_INLINE {
-        if (c_beg + decltype(s_c)::value < c_full) load_chunk(s_c, c_beg + decltype(s_c)::value, std::false_type{});
-        return false;
-    });
+    // ---- the segment, last chunk first, one barrier per chunk: staging a
+    // chunk into buffer b follows the barrier after which every wave has
+    // finished reading b for the chunk before the previous one.  The next
+    // chunk's loads go out as soon as the current one is staged; inside the
+    // loop they are always full-chunk loads (at the segment's first chunk
+    // they re-read it, in bounds and unused), so that the compiler cannot
+    // merge them with the ragged chunk's zeroing, which would wait for them
+    // on the spot.  A ragged chunk (the row's last) comes first.
+    const std::integral_constant<int, 0> s0;
     int buf = 0;
-    auto step = [&](auto s_c, int64_t c) LA_INLINE {
-        const Dec d = book(C);
-        stage(s_c, buf, C, d.kw_l2, std::false_type{});
-        load_chunk(s_c, min(c + PF, c_full - 1), std::false_type{});
-        __syncthreads();
-        update(buf, d);
-        buf ^= 1;
-    };
-    int64_t c = c_beg;
-    for (; c + PF <= c_full; c += PF)
-        static_until<0, PF>([&](auto s_c) LA_INLINE {
-            step(s_c, c + decltype(s_c)::value);
-            return false;
-        });
-    static_until<0, PF>([&](auto s_c) LA_INLINE {
-        if (c + decltype(s_c)::value >= c_full) return true;
-        step(s_c, c + decltype(s_c)::value);
-        return false;
-    });
     if (ragged) {
-        const std::integral_constant<int, 0> s0;
         load_chunk(s0, c_full, std::true_type{});
-        const Dec d = book(n_tail);
-        stage(s0, buf, n_tail, d.kw_l2, std::true_type{});
+        stage(s0, buf, n_tail, t_last - c_full * C, std::true_type{});
+        if (c_full > c_beg) load_chunk(s0, c_full - 1, std::false_type{});
         __syncthreads();
-        update(buf, d);
+        update(buf);
+        buf ^= 1;
+    } else {
+        load_chunk(s0, c_full - 1, std::false_type{});
+    }
+    for (int64_t c = c_full - 1; c >= c_beg; --c) {
+        stage(s0, buf, C, t_last - c * C, std::false_type{});
+        load_chunk(s0, max(c - 1, c_beg), std::false_type{});
+        __syncthreads();
+        update(buf);
+        buf ^= 1;
     }
 
     // ---- two token splits: the second hands its tiles to the first
@@ -450,15 +413,14 @@ la_state_kernel(const FwdArgs a)
     // ---- the segment's state (true scale)
     float* const Sd = a.S_dst + ((int64_t)seg * a.BH + bh) * a.dst_stride;
     float* const zd = a.z_dst + ((int64_t)seg * a.BH + bh) * a.dst_zstride;
-    const float ds = decay ? exp2f(log2D) : 1.f;
 #pragma unroll
     for (int u = 0; u < FBW; ++u) {
         const int f0 = 16 * fblock(u) + 4 * g;
 #pragma unroll
         for (int c = 0; c < DBW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sd[(int64_t)(f0 + r) * DV + 16 * (DBW * wd + c) + l16] = ds * accS[u][c][r];
-        if (wd == 0 && l16 == 0) *(f32x4*)(zd + f0) = accZ[u] * ds;
+            for (int r = 0; r < 4; ++r) Sd[(int64_t)(f0 + r) * DV + 16 * (DBW * wd + c) + l16] = accS[u][c][r];
+        if (wd == 0 && l16 == 0) *(f32x4*)(zd + f0) = accZ[u];
     }
 }
 
