@@ -78,6 +78,24 @@ def test_random_features_head_sizes(m, dk, dv, monkeypatch):
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(Sr).max())
 
 
+@pytest.mark.parametrize("m", [32, 64, 128, 256])
+@pytest.mark.parametrize("lam", [[0.5, 0.0, 0.3, 1.0], [0.71, 0.75, 1.0, 0.999]], ids=["small", "edge"])
+def test_random_features_decay_range(m, lam, monkeypatch):
+    # the causal output pass stages the values with their key weights only
+    # where every head has lambda = 1 or lambda >= 2^-1/2; "small" takes the
+    # other form (lambda = 0 among the heads), "edge" the weighted one near
+    # its limit, where a chunk's weights span lambda^63 ~ 2^-31; four
+    # segments of 64-token chunks, the last one ragged
+    monkeypatch.setenv("LA_SEGMENTS", "4")
+    wl = si.workload(5).with_(m=m)
+    inp = si.make_inputs(wl, B=1, H=4, N=1500)
+    y, S, z = run_causal(wl, inp, lam=lam, want_state=True)
+    ref, Sr, zr, kap = oracle_causal(wl, inp, lam=lam, want_state=True, want_kappa=True)
+    _check_rows(y, ref, kap, "bf16")
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(zr).max())
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=TOL["bf16"], atol=TOL["bf16"] * np.abs(Sr).max())
+
+
 @pytest.mark.parametrize("phi", ["trig_rf", "trig_rf_softmax"])
 def test_random_features_gaussian_omega(phi):
     # rows of omega drawn independently from N(0, I), no orthogonal blocks

@@ -38,9 +38,18 @@
 // Decay weights of the state update.  The elementwise maps stage the key
 // features a second time with the weight lambda^(n-1-j) (rescaled, see book);
 // the random features, whose feature rows are wider than the value rows, put
-// the weight (times the key's prefactor) on the value fragments instead, in
-// registers (and the weights themselves form the B operand of the z update),
-// which halves the LDS tiles of the keys.
+// the weight (times the key's prefactor) on the values instead (and the
+// weights themselves form the B operand of the z update), which halves the
+// LDS tiles of the keys.  With WV the values are staged already weighted, so
+// that one value fragment serves both the state update and V^T P^T: for a
+// query i of the chunk, lambda^(i-j) c_j = r_i w_j with w_j the key's weight
+// in the update and r_i = lambda^(i-n+1) times the pending scale, a factor of
+// the query alone, so the score tiles need only the causal selection, the row
+// sums take the weights as their A operand, and r_i multiplies the query's
+// intra-chunk numerator and denominator.  w_j spans lambda^(C-1) inside a
+// chunk, which the host allows only for lambda = 1 or lambda >= 2^-1/2 (the
+// smallest weight then stays above 2^-32 of the largest); other heads run
+// without WV.
 //
 // Layouts.  phi(Q), phi(K) and the weighted phi(K) are staged in LDS as in
 // la_forward.h (TileL, swizzled 8-byte units); V in TileX, whose swizzle is
@@ -131,8 +140,9 @@ __device__ __forceinline__ int st_off(int r, int u)
 }
 
 // PART: 0 for a whole map; 1, 2 for the first and second half of a split
-// random-feature map (FwdArgs part_mode).
-template <int PHI, int DK, int F, int DV, bool OUTF32, int PART>
+// random-feature map (FwdArgs part_mode).  WV (random features): the values
+// are staged with their key weights.
+template <int PHI, int DK, int F, int DV, bool OUTF32, int PART, bool WV>
 __global__ void __launch_bounds__((OutCfg<PHI, DK, F, DV>::NT), 2)
 la_out_kernel(const FwdArgs a)
 {
@@ -142,6 +152,7 @@ la_out_kernel(const FwdArgs a)
     constexpr int KB = Cfg::KB, CB = Cfg::CB, DB = Cfg::DB, VEC = Cfg::VEC;
     constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
     constexpr bool RF = Cfg::RF, VW = Cfg::VW;
+    static_assert(!WV || VW, "weighted values only where the weights are on the values");
     constexpr int M = Cfg::M, KX = Cfg::KX, RB = Cfg::RB, XLD = Cfg::XLD;
     // phi(Q), phi(K) and the weighted phi(K) in TileP (a row fragment is one
     // 16-byte read); V in TileX
@@ -378,8 +389,21 @@ la_out_kernel(const FwdArgs a)
         for (int r = 0; r < RV; ++r) {
             const int idx = tid + r * NT, j = idx / VPRV, c4 = idx % VPRV;
             const uint4 u = rv[r];
-            *(uint2*)(sV + TVL::off(j, c4 * VEC)) = uint2{u.x, u.y};
-            *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
+            if constexpr (WV) {
+                // v_j times its key weight; a dropped key's row is zeroed by
+                // selection, whatever its values
+                const float w = (TAIL && j >= n) ? 0.f
+                                                 : (decay ? key_weight(n - 1 - j, kw_l2) : 1.f) * sCF0[cb * 2 * C + C + j];
+                float x[VEC];
+                unpack16(u, x, (const T*)nullptr);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) x[e] = w == 0.f ? 0.f : x[e] * w;
+                st4(sV + TVL::off(j, c4 * VEC), x[0], x[1], x[2], x[3]);
+                st4(sV + TVL::off(j, c4 * VEC + 4), x[4], x[5], x[6], x[7]);
+            } else {
+                *(uint2*)(sV + TVL::off(j, c4 * VEC)) = uint2{u.x, u.y};
+                *(uint2*)(sV + TVL::off(j, c4 * VEC + 4)) = uint2{u.z, u.w};
+            }
         }
         after_part(0);
         if constexpr (!RF) {
@@ -501,7 +525,7 @@ la_out_kernel(const FwdArgs a)
     // ---- outputs of this wave's query block and the update of its state
     // rows, for one staged chunk.  dscale: 2^log2D of the state in S^T;
     // rescale: factor on the accumulators before the chunk's keys are added.
-    auto compute = [&](int n, int64_t t0, float dscale, bool do_rescale, float rescale, auto tail_c) LA_INLINE {
+    auto compute = [&](int n, int64_t t0, float dscale, bool do_rescale, float rescale, float kw_l2, auto tail_c) LA_INLINE {
         constexpr bool TAIL = decltype(tail_c)::value;
         const int i = 16 * ib + l16;
         // products with phi(Q): phi(q_i).z (every row holds it), the scores
@@ -528,6 +552,24 @@ la_out_kernel(const FwdArgs a)
             zf.v = *(const bf16x8*)(sZ + (4 * kb + g) * 8);
             return zf;
         };
+        // B operands of the z update (with WV also the A operands of the row
+        // sums): the chunk's key weights where they are not in the key
+        // features, else ones
+        Frag<T> wf[CB];
+        f32x4 wlo[VW ? CB : 1], whi[VW ? CB : 1];  // the weights of this lane's k positions
+        auto load_weights = [&]() LA_INLINE {
+#pragma unroll
+            for (int kb = 0; kb < CB; ++kb) {
+                if constexpr (VW) {
+                    wlo[kb] = *(const f32x4*)(sWt + 32 * kb + 4 * g);
+                    whi[kb] = *(const f32x4*)(sWt + 32 * kb + 16 + 4 * g);
+                    wf[kb] = frag_acc<T>(wlo[kb], whi[kb]);
+                } else {
+                    wf[kb] = ones;
+                }
+            }
+        };
+        if constexpr (WV) load_weights();
         Frag<T> pf[CB];
         f32x4 rs = zero4;
         if constexpr (QF_ALL) {
@@ -553,10 +595,12 @@ la_out_kernel(const FwdArgs a)
                         for (int kb = 0; kb < KB; ++kb)
                             mma(acc, lds_frag_row<T, F, TF>(sK, 16 * JB + l16, kb, g), qf[kb]);
                         f32x4 ck = {1.f, 1.f, 1.f, 1.f};
-                        if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * JB + 4 * g);
+                        if constexpr (RF && !WV) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * JB + 4 * g);
                         if constexpr (JB == IB) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) p4[JB][r] = above[r] ? 0.f : acc[r] * (m0[r] * ck[r]);
+                            for (int r = 0; r < 4; ++r) p4[JB][r] = above[r] ? 0.f : (WV ? acc[r] : acc[r] * (m0[r] * ck[r]));
+                        } else if constexpr (WV) {
+                            p4[JB] = acc;
                         } else {
                             // lambda^(16 (ib-jb-1)) for blocks before the query block
                             const float dj = lam_pow(l2l, 16 * (IB - JB - 1));
@@ -571,7 +615,7 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
                 for (int kb = 0; kb < CB; ++kb) {
                     pf[kb] = frag_acc<T>(p4[2 * kb], p4[2 * kb + 1]);
-                    if (2 * kb <= IB) mma(rs, ones, pf[kb]);
+                    if (2 * kb <= IB) mma(rs, WV ? wf[kb] : ones, pf[kb]);
                 }
             };
             switch (ib) {
@@ -603,10 +647,12 @@ la_out_kernel(const FwdArgs a)
                     constexpr int JB = decltype(jb_c)::value;
                     if constexpr (JB <= IB) {
                         f32x4 ck = {1.f, 1.f, 1.f, 1.f};
-                        if constexpr (RF) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * JB + 4 * g);
+                        if constexpr (RF && !WV) ck = *(const f32x4*)(sCF0 + cb * 2 * C + C + 16 * JB + 4 * g);
                         if constexpr (JB == IB) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) p4[JB][r] = above[r] ? 0.f : pt[JB][r] * (m0[r] * ck[r]);
+                            for (int r = 0; r < 4; ++r) p4[JB][r] = above[r] ? 0.f : (WV ? pt[JB][r] : pt[JB][r] * (m0[r] * ck[r]));
+                        } else if constexpr (WV) {
+                            p4[JB] = pt[JB];
                         } else {
                             const float dj = lam_pow(l2l, 16 * (IB - JB - 1));
 #pragma unroll
@@ -620,7 +666,7 @@ la_out_kernel(const FwdArgs a)
 #pragma unroll
                 for (int kb = 0; kb < CB; ++kb) {
                     pf[kb] = frag_acc<T>(p4[2 * kb], p4[2 * kb + 1]);
-                    if (2 * kb <= IB) mma(rs, ones, pf[kb]);
+                    if (2 * kb <= IB) mma(rs, WV ? wf[kb] : ones, pf[kb]);
                 }
             };
             switch (ib) {
@@ -639,26 +685,16 @@ la_out_kernel(const FwdArgs a)
         const int64_t yrow = row0 + t0 + i;
         const bool live = !TAIL || i < n;  // rows past the end are neither read nor stored
         constexpr int pmode = PART;
-        const float den = cq * (rs[0] + lqd * dq[0]);
+        // WV: the query's factor on its intra-chunk parts, lambda^(i-n+1)
+        // times the pending scale
+        const float ri = (WV && decay) ? __builtin_amdgcn_exp2f((float)(i - (n - 1)) * l2l + kw_l2) : 1.f;
+        const float den = cq * (rs[0] * ri + lqd * dq[0]);
         const float den1 = (pmode == 2 && live) ? a.part_den[yrow] : 0.f;
         const float inv0 = pmode == 1 ? 1.f : fast_rcp(den + den1 + a.eps);
         const float inv = RF ? cq * inv0 : inv0;
-        const float sc = lqd * inv;
+        const float sc = lqd * inv, si = inv * ri;
         if (pmode == 1 && live && dq0 == 0 && g == 0) a.part_den[yrow] = den;
-        // B operands of the z update: the chunk's key weights where they are
-        // not in the key features, else ones
-        Frag<T> wf[CB];
-        f32x4 wlo[VW ? CB : 1], whi[VW ? CB : 1];  // the weights of this lane's k positions
-#pragma unroll
-        for (int kb = 0; kb < CB; ++kb) {
-            if constexpr (VW) {
-                wlo[kb] = *(const f32x4*)(sWt + 32 * kb + 4 * g);
-                whi[kb] = *(const f32x4*)(sWt + 32 * kb + 16 + 4 * g);
-                wf[kb] = frag_acc<T>(wlo[kb], whi[kb]);
-            } else {
-                wf[kb] = ones;
-            }
-        }
+        if constexpr (!WV) load_weights();
         if (do_rescale) {
 #pragma unroll
             for (int u = 0; u < FBW; ++u) {
@@ -704,7 +740,7 @@ la_out_kernel(const FwdArgs a)
             }
 #pragma unroll
             for (int kb = 0; kb < CB; ++kb) mma(oi, vf[kb], pf[kb]);
-            f32x4 y = ot * sc + oi * inv;
+            f32x4 y = ot * sc + oi * si;
             if (live) {
                 const int64_t yo = yrow * DV + 16 * t + 4 * g;
                 if (pmode == 1) {
@@ -718,7 +754,7 @@ la_out_kernel(const FwdArgs a)
             const int vs = KEYS_FIRST ? 0 : tq;
 #pragma unroll
             for (int kb = 0; kb < CB; ++kb) vwf[vs][kb] = vf[kb];
-            if constexpr (VW) {
+            if constexpr (VW && !WV) {
 #pragma unroll
                 for (int kb = 0; kb < CB; ++kb) {
                     f32x4 lo, hi;
@@ -808,7 +844,7 @@ la_out_kernel(const FwdArgs a)
             const bool next_full = c + 1 < c_full;
             __syncthreads();
             if (!EARLY && next_full) load_chunk(c + 1, std::false_type{});
-            compute(C, c * C, d.dscale, d.do_rescale, d.rescale, std::false_type{});
+            compute(C, c * C, d.dscale, d.do_rescale, d.rescale, d.kw_l2, std::false_type{});
             // raw rows of the next chunk: features() of this chunk read them
             // before the barrier above
             if (next_full) stage_x(C, cb ^ 1, std::false_type{});
@@ -837,7 +873,7 @@ la_out_kernel(const FwdArgs a)
                 features();
             }
             __syncthreads();
-            compute(n_tail, c_full * C, d.dscale, d.do_rescale, d.rescale, std::true_type{});
+            compute(n_tail, c_full * C, d.dscale, d.do_rescale, d.rescale, d.kw_l2, std::true_type{});
         }
     }
 
@@ -868,15 +904,31 @@ hipError_t out_launch(const FwdArgs& a, hipStream_t stream)
     // the halves of a split map: only the instance that can be one (m = 128
     // directions per half, d_k = d_v = 64) has them
     constexpr bool SPLIT = PHI == LA_PHI_TRIG_RF && F == 256 && DK == 64 && DV == 64;
-    auto kernel = a.out_f32 ? la_out_kernel<PHI, DK, F, DV, true, 0> : la_out_kernel<PHI, DK, F, DV, false, 0>;
-    if (a.part_mode != 0) {
-        if constexpr (SPLIT) {
-            if (a.part_mode == 1) kernel = la_out_kernel<PHI, DK, F, DV, false, 1>;
-            else kernel = a.out_f32 ? la_out_kernel<PHI, DK, F, DV, true, 2> : la_out_kernel<PHI, DK, F, DV, false, 2>;
-        } else {
-            return hipErrorInvalidValue;
+    if (a.part_mode != 0 && !SPLIT) return hipErrorInvalidValue;
+    // random features: the values are staged with their key weights where
+    // every head has lambda = 1 or lambda >= 2^-1/2 (the range of the weights
+    // inside a chunk, lambda^(C-1), stays within 2^-32)
+    bool wv = false;
+    if constexpr (Cfg::VW) {
+        wv = true;
+        for (int h = 0; h < a.H; ++h) {
+            const float l2 = a.lam.log2lam[h];
+            if (!(l2 == 0.f || l2 >= -0.5f)) wv = false;
         }
     }
+    auto pick = [&](auto wv_c) {
+        constexpr bool W = decltype(wv_c)::value;
+        auto k = a.out_f32 ? la_out_kernel<PHI, DK, F, DV, true, 0, W> : la_out_kernel<PHI, DK, F, DV, false, 0, W>;
+        if constexpr (SPLIT) {
+            if (a.part_mode == 1) k = la_out_kernel<PHI, DK, F, DV, false, 1, W>;
+            else if (a.part_mode == 2)
+                k = a.out_f32 ? la_out_kernel<PHI, DK, F, DV, true, 2, W> : la_out_kernel<PHI, DK, F, DV, false, 2, W>;
+        }
+        return k;
+    };
+    auto kernel = pick(std::false_type{});
+    if constexpr (Cfg::VW)
+        if (wv) kernel = pick(std::true_type{});
     // More segments than workgroups resident at once: each workgroup takes k
     // consecutive segments (their carried-in state is the first one's), so
     // that the pass runs in one round of workgroups.
