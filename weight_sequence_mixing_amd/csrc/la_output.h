@@ -625,16 +625,38 @@ la_out_kernel(const FwdArgs a)
             default: scores(std::integral_constant<int, 3>{}); break;
             }
         } else {
+            // the products one k block at a time: where the feature row has
+            // at most 128 features, in one version per query block that
+            // forms key blocks 0 .. ib only (kloop below); wider rows form all
+            // four blocks in one version of the loop (four versions spill
+            // there)
+            constexpr bool KLOOP_IB = F <= 128;
+            auto kloop = [&](auto ib_c) LA_INLINE {
+                constexpr int IB = decltype(ib_c)::value;
 #pragma unroll
-            for (int tq = 0; tq < DBQ; ++tq) o[tq] = zero4;
+                for (int tq = 0; tq < DBQ; ++tq) o[tq] = zero4;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const Frag<T> q1 = lds_frag_row<T, F, TF>(sQ, i, kb, g);
-                mma(dq, zfrag(kb), q1);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const Frag<T> q1 = lds_frag_row<T, F, TF>(sQ, i, kb, g);
+                    mma(dq, zfrag(kb), q1);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), q1);
+                    for (int jb = 0; jb <= IB; ++jb) mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), q1);
 #pragma unroll
-                for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
+                    for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
+                }
+            };
+            if constexpr (!KLOOP_IB) {
+#pragma unroll
+                for (int tq = 0; tq < DBQ; ++tq) o[tq] = zero4;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const Frag<T> q1 = lds_frag_row<T, F, TF>(sQ, i, kb, g);
+                    mma(dq, zfrag(kb), q1);
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) mma(pt[jb], lds_frag_row<T, F, TF>(sK, 16 * jb + l16, kb, g), q1);
+#pragma unroll
+                    for (int tq = 0; tq < DBQ; ++tq) mma(o[tq], sfrag(dq0 + tq, kb), q1);
+                }
             }
             // decay weights of the scores (random features: times the key's
             // prefactor), in one version per query block as above: blocks
@@ -669,11 +691,15 @@ la_out_kernel(const FwdArgs a)
                     if (2 * kb <= IB) mma(rs, WV ? wf[kb] : ones, pf[kb]);
                 }
             };
+            auto both = [&](auto ib_c) LA_INLINE {
+                if constexpr (KLOOP_IB) kloop(ib_c);
+                weigh(ib_c);
+            };
             switch (ib) {
-            case 0: weigh(std::integral_constant<int, 0>{}); break;
-            case 1: weigh(std::integral_constant<int, 1>{}); break;
-            case 2: weigh(std::integral_constant<int, 2>{}); break;
-            default: weigh(std::integral_constant<int, 3>{}); break;
+            case 0: both(std::integral_constant<int, 0>{}); break;
+            case 1: both(std::integral_constant<int, 1>{}); break;
+            case 2: both(std::integral_constant<int, 2>{}); break;
+            default: both(std::integral_constant<int, 3>{}); break;
             }
         }
         // y_i = c_i (o + o_i) / (c_i den + eps) with c_i the query's
