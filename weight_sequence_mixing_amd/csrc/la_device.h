@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/la.h"
 #include "la_internal.h"
 
@@ -314,6 +316,26 @@ __device__ __forceinline__ uint4 load16(const void* base, uint32_t voff) {
 
 __device__ __forceinline__ float wave_sum_xor(float v, int mask_lo, int mask_hi) {
     for (int m = mask_lo; m <= mask_hi; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8 or 16), the result in
+// every lane of the group, with DPP lane moves in the vector unit instead of
+// LDS permutes: quad_perm swaps for lanes 1 and 2 apart, then the mirror of
+// the half row (lane i of 8 takes lane 7 - i, which lies in the other quad)
+// and of the row (i of 16 takes 15 - i, in the other half row); each step
+// adds a lane that holds the sum of a disjoint group of the same size.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2 to 16 lanes");
+    auto dpp = [](float x, auto ctrl_c) {
+        constexpr int CTRL = decltype(ctrl_c)::value;
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+    };
+    v += dpp(v, std::integral_constant<int, 0xB1>{});  // quad_perm(1, 0, 3, 2)
+    if constexpr (N >= 4) v += dpp(v, std::integral_constant<int, 0x4E>{});  // quad_perm(2, 3, 0, 1)
+    if constexpr (N >= 8) v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (N >= 16) v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
     return v;
 }
 

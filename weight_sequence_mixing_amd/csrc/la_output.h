@@ -470,7 +470,7 @@ la_out_kernel(const FwdArgs a)
                     float s2 = 0.f;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) s2 += x[e] * x[e];
-                    s2 = wave_sum_xor(s2, 1, VPRQ / 2);
+                    s2 = group_sum<VPRQ>(s2);
                     if (cg == 0) sCF0[buf * 2 * C + pass * C + j] = drop ? 0.f : exp_rf<T>(rf_cexp * s2) * rf_cnorm;
                 }
         }
