@@ -539,8 +539,39 @@ def rf_backward_w5(ctx, steps=5):
     return res
 
 
-# Mask / cross / packed / backward lines measured beside the main workloads
+def noncausal(ctx, B, H, N, d, steps=100):
+    """Non-causal forward (every query against the whole sequence, no decay):
+    the state sums over segments of the sequence, their reduction, the query
+    pass.  Bytes: the state sums read k, v and write P partial states; the
+    query pass reads q and the state and writes y."""
+    torch, la = ctx.torch, ctx.la
+    g = torch.Generator(device=ctx.dev)
+    g.manual_seed(31)
+    q, k, v = (device_normal(torch, g, (B, H, N, d), 0.5, ctx.dev) for _ in range(3))
+    y = torch.empty_like(q)
+    ws_n = la.la_workspace_size(B, H, N, d, d, causal=False)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=ctx.dev)
+    SZ = d * d + d
+    P = max(1, int(round(ws_n / (B * H * SZ * 4)))) if ws_n else 1
+    ids = la.KERNEL_IDS
+    kb = {ids["fwd_local"]: B * H * N * 2 * d * 2 + P * B * H * SZ * 4,
+          ids["fwd_query"]: B * H * N * 2 * d * 2 + B * H * SZ * 4,
+          ids["scan"]: (P + 1) * B * H * SZ * 4}
+
+    def step():
+        la.la_forward_noncausal(q, k, v, y, eps=1e-6, workspace=ws)
+
+    name = "elu1_noncausal_B%d_H%d_N%d_d%d_bf16" % (B, H, N, d)
+    res = bench_call(ctx, name, step, B * N, kb, steps, max(ctx.warmup, 5))
+    res["segments"] = P
+    return res
+
+
+# Mask / cross / packed / non-causal / backward lines measured beside the
+# main workloads
 SHAPE_VARIANTS = (("masked_w2", masked_w2), ("varlen_w2", varlen_w2), ("cross_w2", cross_w2),
+                  ("noncausal_w2", lambda c: noncausal(c, 4, 8, 4096, 64)),
+                  ("noncausal_w3", lambda c: noncausal(c, 2, 16, 32768, 128, steps=50)),
                   ("backward_w2", backward_w2), ("backward_dlam_w2", lambda c: backward_w2(c, with_dlam=True)),
                   ("cross_backward_w2", cross_backward_w2), ("rf_backward_w5", rf_backward_w5))
 
