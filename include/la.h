@@ -315,7 +315,13 @@ la_status la_backward_cross(const void* q, const void* k, const void* v,
  *   y  = phi(q)^T S / (phi(q)^T z + eps).
  * q, k: [B,H,N,d_k]; v: [B,H,N,d_v]; y: [B,H,N,d_v]; S [B,H,F,d_v] and
  * z [B,H,F] fp32 are read once and overwritten once.  1 <= shape->N <=
- * LA_DECODE_MAX_TOKENS (longer runs: la_forward_causal with S_in = S_out). */
+ * LA_DECODE_MAX_TOKENS (longer runs: la_forward_causal with S_in = S_out).
+ * With bf16 inputs, an elementwise map and at least 10 tokens (11 where
+ * F * d_v >= 128 * 128) the call runs the causal forward's kernels over its
+ * tokens from S back into S (the same result up to rounding: the state's
+ * contribution to the outputs is then read from a bf16 copy, as in
+ * la_forward_causal); other calls run the recurrent decode kernel, whose
+ * state stays fp32 throughout. */
 la_status la_decode_step(const void* q, const void* k, const void* v, void* y,
                          float* S, float* z, const la_shape* shape, const la_phi* phi,
                          const float* lambda_h, float eps, la_stream_t stream);

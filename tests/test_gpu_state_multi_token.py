@@ -86,10 +86,15 @@ def test_multi_token_decode_in_place(k_tok):
 
 
 @pytest.mark.parametrize("phi,m,dk,k_tok", [("elu1", 0, 128, 3), ("elu1", 0, 128, 16), ("elu1", 0, 64, 64),
-                                            ("relu", 0, 128, 5), ("trig_rf", 32, 64, 7)])
+                                            ("relu", 0, 128, 5), ("trig_rf", 32, 64, 7),
+                                            ("elu1", 0, 128, 10), ("elu1", 0, 128, 11), ("elu1", 0, 64, 9),
+                                            ("relu", 0, 64, 10), ("trig_rf", 32, 64, 20)])
 def test_decode_step_multi_token(phi, m, dk, k_tok):
     # la_decode_step with k_tok tokens per head-state per call (state held on
-    # chip across them), three calls after a 96-token prefix
+    # chip across them), three calls after a 96-token prefix; with bf16
+    # inputs and an elementwise map, calls from 10 tokens (11 at d = 128) run
+    # the causal forward's kernels from S back into S, shorter ones and the
+    # random features the decode kernel: both sides of each threshold
     wl = si.workload(4).with_(N=96, phi=phi, m=m, dk=dk, dv=dk)
     B, H, calls = 2, 4, 3
     omega = si.make_omega(m, dk, 4) if m else None

@@ -1572,6 +1572,17 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     if ((st = check_io(q, k, v, y, shape)) != LA_OK) return st;
     const int64_t BH = shape->B * shape->H;
     if (BH > 0x7fffffff) return fail(LA_ERR_UNSUPPORTED, "B*H too large");
+    // Several tokens per call with an elementwise map on bf16 inputs: the
+    // causal forward over the call's tokens, from S back into S, is faster
+    // from about ten tokens on (its output kernel does the per-token products
+    // on the matrix cores, while the decode kernel's fp32 arithmetic grows
+    // with the tokens; measured at B = 256, H = 32: d = 128 ties at 10 tokens
+    // and wins from 12, d = 64 wins from 10).  At most 64 tokens are one
+    // chunk, one segment per row, so it needs no workspace.
+    if (shape->in_dtype == LA_BF16 && (phi->kind == LA_PHI_ELU1 || phi->kind == LA_PHI_RELU) &&
+        shape->N >= ((int64_t)F * shape->d_v >= 128 * 128 ? 11 : 10) && shape->N <= 64)
+        return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, nullptr, nullptr, 0, S, z, S, z, nullptr, 0,
+                              stream);
     DecArgs a;
     std::memset(&a, 0, sizeof(a));
     if ((st = make_lam(lambda_h, shape->H, &a.lam)) != LA_OK) return st;
