@@ -30,8 +30,11 @@
 // matrix cores (omega x^T from omega's row blocks, kept in LDS as bf16 high
 // and low parts, angles in revolutions for the hardware sine and cosine)
 // and writes cos and sin into the same tiles the elementwise maps use.  Half
-// of the waves take the queries, half the keys; a wave keeps RB row blocks of
-// omega.  The prefactors stay out of the tiles: a key's enters the score
+// of the waves take the queries, half the keys; a wave takes one pair of
+// omega's 16-row blocks, whose features are the two halves of the tiles'
+// 16-byte units, so that a lane writes its cosines (and its sines) of a token
+// as one 16-byte unit (8-byte halves from 16 rows at once would meet in the
+// banks two by two).  The prefactors stay out of the tiles: a key's enters the score
 // weights and the value weights of the state update, a query's the
 // normaliser, since num_i and den_i are both linear in phi(q_i).
 //
@@ -102,7 +105,11 @@ struct OutCfg {
     // read); omega row blocks per wave, each wave covering one of the two
     // token matrices
     static constexpr int KX = DK / 32, XLD = DK + 8;
-    static constexpr int RB = RF ? 2 * (M / 16) / NW : 0;
+    // random features: a wave of feature work takes one pair of omega's
+    // 16-row blocks (2 p, 2 p + 1: the two halves of each 16-byte TileP unit)
+    // and FTB of the four token blocks of its token matrix
+    static constexpr int RBP = RF ? M / 32 : 0;
+    static constexpr int FTB = RF ? RBP * (C / 16) / (NW / 2) : 0;
     static constexpr int TQ = C * F, TV = C * DV;  // elements of a tile
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t OFF_K = OFF_Q + size_t(TQ) * 2;
@@ -120,7 +127,8 @@ struct OutCfg {
     static_assert(RF || DK == F, "elementwise maps keep the width");
     static_assert(FBW >= 1 && FB % QB == 0 && NW % QB == 0 && DB % QW == 0, "wave split");
     static_assert(RQ >= 1 && RV >= 1 && (C * VPRQ) % NT == 0 && (C * VPRV) % NT == 0, "loads per thread");
-    static_assert(!RF || (RB >= 1 && RB * NW == 2 * (M / 16)), "feature tiles must split over the waves");
+    static_assert(!RF || (FTB >= 1 && FTB <= C / 16 && (C / 16) % FTB == 0 && FTB * (NW / 2) == RBP * (C / 16)),
+                  "feature tiles must split over the waves");
     static_assert(OFF_X % 16 == 0 && OFF_CF % 16 == 0 && OFF_OM % 16 == 0 && OFF_W % 16 == 0, "alignment");
     // the LDS of one workgroup (not met by m = 128 random features with
     // d_v = 128, whose S^T alone is 64 KiB: the causal pass of la_forward.h
@@ -153,7 +161,7 @@ la_out_kernel(const FwdArgs a)
     constexpr int VPRQ = Cfg::VPRQ, VPRV = Cfg::VPRV, RQ = Cfg::RQ, RV = Cfg::RV;
     constexpr bool RF = Cfg::RF, VW = Cfg::VW;
     static_assert(!WV || VW, "weighted values only where the weights are on the values");
-    constexpr int M = Cfg::M, KX = Cfg::KX, RB = Cfg::RB, XLD = Cfg::XLD;
+    constexpr int M = Cfg::M, KX = Cfg::KX, FTB = Cfg::FTB, XLD = Cfg::XLD;
     // phi(Q), phi(K) and the weighted phi(K) in TileP (a row fragment is one
     // 16-byte read); V in TileX
     using TF = TileP<T, F>;
@@ -233,8 +241,9 @@ la_out_kernel(const FwdArgs a)
     // ---- random features: rows 16 rb + l16 of omega as A-operand fragments,
     // scaled by qk_scale / (2 pi) so that the products are angles in
     // revolutions, and split into bf16 high and low parts (omega = hi + lo to
-    // 16 bits), into LDS (read after the first barrier).  A wave of feature
-    // work takes row blocks rb = rbg + (NW / 2) u of the token matrix xpass.
+    // 16 bits), into LDS (read after the first barrier).  Wave rbg of token
+    // matrix xpass takes items rbg FTB .. rbg FTB + FTB - 1 of that matrix's
+    // (row-block pair, token block) items, all of one pair.
     const int rbg = wave % (NW / 2), xpass = wave / (NW / 2);
     if constexpr (RF) {
         const float om_scale = a.qk_scale * 0.159154943091895336f;
@@ -484,40 +493,48 @@ la_out_kernel(const FwdArgs a)
         if constexpr (RF) {
             const T* const xs = sX + xpass * C * XLD;
             T* const tile = xpass ? sK : sQ;
-            Frag<T> om_hi[RB][KX], om_lo[RB][KX];
+            const int it0 = rbg * FTB, pr = it0 / Cfg::QB;  // first item, row-block pair
+            Frag<T> om_hi[2][KX], om_lo[2][KX];
 #pragma unroll
-            for (int u = 0; u < RB; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int kb = 0; kb < KX; ++kb) {
-                    const int fi = (rbg + (NW / 2) * u) * KX + kb;
+                    const int fi = (2 * pr + u) * KX + kb;
                     om_hi[u][kb] = sOm[(fi * 2 + 0) * 64 + lane];
                     om_lo[u][kb] = sOm[(fi * 2 + 1) * 64 + lane];
                 }
 #pragma unroll
-            for (int tb = 0; tb < Cfg::QB; ++tb) {
-                const int j = 16 * tb + l16;
+            for (int t = 0; t < FTB; ++t) {
+                const int j = 16 * ((it0 + t) % Cfg::QB) + l16;
                 Frag<T> xf[KX];
 #pragma unroll
                 for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(xs, XLD, j, 32 * kb, g);
+                // acc[u][r]: angle of feature 16 (2 pr + u) + 4 g + r for token j
+                f32x4 acc[2];
 #pragma unroll
-                for (int u = 0; u < RB; ++u) {
-                    f32x4 acc = zero4;
+                for (int u = 0; u < 2; ++u) {
+                    acc[u] = zero4;
 #pragma unroll
                     for (int kb = 0; kb < KX; ++kb) {
-                        mma(acc, om_hi[u][kb], xf[kb]);
-                        mma(acc, om_lo[u][kb], xf[kb]);
+                        mma(acc[u], om_hi[u][kb], xf[kb]);
+                        mma(acc[u], om_lo[u][kb], xf[kb]);
                     }
-                    // acc[r]: angle of feature f0 + r for token j
-                    const int f0 = 16 * (rbg + (NW / 2) * u) + 4 * g;
-                    float cs[4], sn[4];
+                }
+                float cs[2][4], sn[2][4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        cs[r] = __builtin_amdgcn_cosf(acc[r]);
-                        sn[r] = __builtin_amdgcn_sinf(acc[r]);
+                        cs[u][r] = __builtin_amdgcn_cosf(acc[u][r]);
+                        sn[u][r] = __builtin_amdgcn_sinf(acc[u][r]);
                     }
-                    st4(tile + TF::off(j, f0), cs[0], cs[1], cs[2], cs[3]);
-                    st4(tile + TF::off(j, M + f0), sn[0], sn[1], sn[2], sn[3]);
-                }
+                // the pair's features 32 pr + 4 g .. + 3 and 32 pr + 16 + 4 g
+                // .. + 3 fill TileP unit 4 pr + g: one 16-byte write for the
+                // cosines, one for the sines (columns m + f)
+                *(bf16x8*)(tile + TF::unit_off(j, 4 * pr + g)) =
+                    bf16x8{(T)cs[0][0], (T)cs[0][1], (T)cs[0][2], (T)cs[0][3], (T)cs[1][0], (T)cs[1][1], (T)cs[1][2], (T)cs[1][3]};
+                *(bf16x8*)(tile + TF::unit_off(j, 4 * (M / 32 + pr) + g)) =
+                    bf16x8{(T)sn[0][0], (T)sn[0][1], (T)sn[0][2], (T)sn[0][3], (T)sn[1][0], (T)sn[1][1], (T)sn[1][2], (T)sn[1][3]};
             }
         }
     };
