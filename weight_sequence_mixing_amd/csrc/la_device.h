@@ -75,6 +75,18 @@ __device__ __forceinline__ Frag<T> frag_rm(const T* base, int ld, int row, int k
     return frag2(p, p + 16);
 }
 
+// Fragment of a row-major bf16 [rows][ld] buffer holding the 8 consecutive
+// elements k0 + 8 g .. + 7 of row `row`, one 16-byte read (k positions in
+// natural order: pair it only with operands built in the same order).  With
+// ld = 72 (144-byte rows) the 16 rows of a read fall in distinct 16-byte
+// slots of the banks, where the two 8-byte halves of frag_rm meet two by two
+// once the compiler pairs them into one two-address read.
+__device__ __forceinline__ Frag<bf16> frag_row16(const bf16* base, int ld, int row, int k0, int g) {
+    Frag<bf16> f;
+    f.v = *(const bf16x8*)(base + row * ld + k0 + 8 * g);
+    return f;
+}
+
 // Fragment from two accumulator tiles (rows 0..15 then 16..31 of the k block).
 template <class T> __device__ __forceinline__ Frag<T> frag_acc(const f32x4& a, const f32x4& b);
 template <> __device__ __forceinline__ Frag<bf16> frag_acc<bf16>(const f32x4& a, const f32x4& b) {

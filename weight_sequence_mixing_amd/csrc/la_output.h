@@ -249,8 +249,10 @@ la_out_kernel(const FwdArgs a)
         const float om_scale = a.qk_scale * 0.159154943091895336f;
         for (int fi = wave; fi < (M / 16) * KX; fi += NW) {
             const int rb = fi / KX, kb = fi % KX;
-            const float* p = a.omega + (int64_t)(16 * rb + l16) * DK + 32 * kb + 4 * g;
-            const f32x4 w0 = *(const f32x4*)p * om_scale, w1 = *(const f32x4*)(p + 16) * om_scale;
+            // k positions in natural order (8 g .. 8 g + 7), as the raw rows
+            // are read in features()
+            const float* p = a.omega + (int64_t)(16 * rb + l16) * DK + 32 * kb + 8 * g;
+            const f32x4 w0 = *(const f32x4*)p * om_scale, w1 = *(const f32x4*)(p + 4) * om_scale;
             f32x4 r0, r1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -508,7 +510,7 @@ la_out_kernel(const FwdArgs a)
                 const int j = 16 * ((it0 + t) % Cfg::QB) + l16;
                 Frag<T> xf[KX];
 #pragma unroll
-                for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_rm(xs, XLD, j, 32 * kb, g);
+                for (int kb = 0; kb < KX; ++kb) xf[kb] = frag_row16(xs, XLD, j, 32 * kb, g);
                 // acc[u][r]: angle of feature 16 (2 pr + u) + 4 g + r for token j
                 f32x4 acc[2];
 #pragma unroll

@@ -176,8 +176,10 @@ la_state_kernel(const FwdArgs a)
         const float om_scale = a.qk_scale * 0.159154943091895336f;
 #pragma unroll
         for (int kx = 0; kx < KX; ++kx) {
-            const float* p = a.omega + (int64_t)(16 * wf + l16) * DK + 32 * kx + 4 * g;
-            const f32x4 w0 = *(const f32x4*)p * om_scale, w1 = *(const f32x4*)(p + 16) * om_scale;
+            // k positions in natural order (8 g .. 8 g + 7), as the raw rows
+            // are read below
+            const float* p = a.omega + (int64_t)(16 * wf + l16) * DK + 32 * kx + 8 * g;
+            const f32x4 w0 = *(const f32x4*)p * om_scale, w1 = *(const f32x4*)(p + 4) * om_scale;
             f32x4 r0, r1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -330,7 +332,7 @@ la_state_kernel(const FwdArgs a)
                     ang[hh] = zero4;
 #pragma unroll
                     for (int kx = 0; kx < KX; ++kx) {
-                        const Frag<T> xf = frag_rm(sX, XLD, j, 32 * kx, g);
+                        const Frag<T> xf = frag_row16(sX, XLD, j, 32 * kx, g);
                         mma(ang[hh], xf, om_hi[kx]);
                         mma(ang[hh], xf, om_lo[kx]);
                     }
