@@ -165,3 +165,28 @@ def test_decode_step_multi_token_decay_range(lam):
     assert err < TOL["bf16"], err
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=2e-2, atol=1e-6)
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+
+
+def test_decode_step_many_head_states_multi_token():
+    # more head-states than one grid dimension takes (B*H = 70400 > 65535): a
+    # 12-token call, which with fewer head-states would run the causal
+    # forward's kernels, stays on the decode kernel; sampled head-states
+    # against the oracle from an identity initial state
+    B, H, d, n = 1100, 64, 64, 12
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    q, k, v = (torch.randn(B, H, n, d, generator=g, device=DEV).mul_(0.5).to(torch.bfloat16) for _ in range(3))
+    S = torch.empty(B, H, d, d, device=DEV)
+    z = torch.empty(B, H, d, device=DEV)
+    la.la_init_state_identity(S, z, 0.5)
+    y = torch.empty_like(q)
+    lam = 0.97
+    la.la_decode_step(q, k, v, y, S, z, lambda_h=[lam] * H, eps=1e-6)
+    torch.cuda.synchronize()
+    S0, z0 = _identity(1, 1, d, d, 0.5)
+    for b, h in ((0, 0), (B - 1, H - 1), (550, 31), (1023, 1)):
+        one = lambda t: t[b, h].float().cpu().numpy()[None, None]
+        ref, Sr, zr = oracle.causal(one(q), one(k), one(v), np.array([lam]), 1e-6, S0=S0, z0=z0, want_state=True)
+        assert oracle.rowwise_rel_err(y[b, h].float().cpu().numpy()[None, None], ref) < TOL["bf16"], (b, h)
+        np.testing.assert_allclose(S[b, h].cpu().numpy(), Sr[0, 0], rtol=2e-2, atol=2e-2 * np.abs(Sr).max())
+        np.testing.assert_allclose(z[b, h].cpu().numpy(), zr[0, 0], rtol=2e-2, atol=2e-2 * np.abs(zr).max())

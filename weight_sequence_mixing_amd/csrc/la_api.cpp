@@ -1578,9 +1578,10 @@ la_status la_decode_step(const void* q, const void* k, const void* v, void* y, f
     // on the matrix cores, while the decode kernel's fp32 arithmetic grows
     // with the tokens; measured at B = 256, H = 32: d = 128 ties at 10 tokens
     // and wins from 12, d = 64 wins from 10).  At most 64 tokens are one
-    // chunk, one segment per row, so it needs no workspace.
+    // chunk, one segment per row, so it needs no workspace; its grid takes at
+    // most 65535 head-states (more stay on the decode kernel).
     if (shape->in_dtype == LA_BF16 && (phi->kind == LA_PHI_ELU1 || phi->kind == LA_PHI_RELU) &&
-        shape->N >= ((int64_t)F * shape->d_v >= 128 * 128 ? 11 : 10) && shape->N <= 64)
+        shape->N >= ((int64_t)F * shape->d_v >= 128 * 128 ? 11 : 10) && shape->N <= 64 && BH <= 65535)
         return forward_causal(q, k, v, y, shape, phi, lambda_h, eps, nullptr, nullptr, 0, S, z, S, z, nullptr, 0,
                               stream);
     DecArgs a;
